@@ -1,0 +1,17 @@
+"""fp64 CPU oracle for the BRA forward pass -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
+leg may import it.  It shares no code with the HIP library.
+"""
+
+from .bra_oracle import (  # noqa: F401
+    bra_forward,
+    lepe,
+    region_affinity,
+    region_mean,
+    region_shape,
+    region_token_maps,
+    region_tokens,
+    routed_attention,
+    topk_route,
+)

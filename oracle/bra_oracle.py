@@ -1,0 +1,247 @@
+"""fp64 CPU oracle for the Bi-Level Routing Attention (BRA) forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, helper,
+constant or table with the HIP library; the only thing both sides share is the
+seeded input generator (``vision_transformer_dynamic_region_amd.workloads``),
+which holds none of the method's arithmetic.
+
+Everything here is plain NumPy in float64, written as the definitions the
+pages give, step by step, with no blocking, fusion or reordering.
+
+Sources (the pages, cited by key, page title and section):
+
+  p1  "CVPR2023: BiFormer中的双层路由注意力机制解析" (cybasar.com news 187266)
+      §2 (the core design: region-level routing, then token-level attention),
+      §3 (the implementation walk-through with a PyTorch-style sketch),
+      §4 (architecture: per-stage top-k), §5 (tuning: S per task).
+  p2  "从静态到动态：BRA双层路由注意力如何革新视觉Transformer的计算范式"
+      (snabindia.com news 101103)
+      §2 (region mean pooling over the region-internal axes),
+      §4 (TopkRouting: scaled region affinity, top-k; the LePE depthwise conv),
+      §5 (routing index held fixed at deployment).
+  p4  "Biformer注意力机制的原理及数学公式推导" (un.csdn.net) -- a different
+      method; only its local-window softmax(QK^T/sqrt(d_k))V formula is used,
+      as a special case in the tests.
+  p5  "BiFormer: Vision Transformer mit Bi-Level-Routing-Attention"
+      (hyper.ai, arXiv 2303.08810 abstract): filter irrelevant key/value pairs
+      at region level, then token-to-token attention over the union of the
+      routed regions.
+
+Readings taken where the pages are silent or garbled (each one is listed with
+its reason in the design notes of the repository):
+
+  R1  The sketch in p1 §3 lost its '=', '@' and '+=' operators in extraction;
+      it is read with them restored.
+  R2  Regions are row-major over the S x S grid; tokens are row-major inside a
+      region (p1 §3: reshape to (S, H/S, S, W/S, C), swap axes 1 and 2).
+  R3  H and W must be divisible by S; nothing is padded.
+  R4  Routing is per image over all C channels and is shared by every head
+      (the region affinity in p1 §3 has no head axis).
+  R5  Routing scale: p1 §3 has none, p2 §4 multiplies by a scale; it is a
+      caller-chosen positive number (default C**-0.5).  A positive scale never
+      changes the order of the affinities.
+  R6  Top-k order: descending affinity, ties go to the lower region index.
+      A region's own index is not forced into its route.
+  R7  Region descriptor is the mean (both sketches use a mean).
+  R8  Heads are contiguous d-channel slices, d = C / heads; attention scale is
+      a caller-chosen number (default d**-0.5).
+  R9  LePE is a depthwise ks x ks cross-correlation (PyTorch Conv2d
+      convention) of V over the whole image, zero padding ks // 2, stride 1,
+      optional per-channel bias, added to the attention output (p2 §4, p1 §3).
+  R10 Softmax is max-subtracted, with no dropout and no mask other than the
+      routing.
+  R11 Output of the method is (out, idx); no Q/K/V or output projection.
+
+Parity pins for every function live in ``tests/test_oracle_pins.py``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "region_shape",
+    "region_token_maps",
+    "region_mean",
+    "region_affinity",
+    "topk_route",
+    "region_tokens",
+    "routed_attention",
+    "lepe",
+    "bra_forward",
+]
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def region_shape(H: int, W: int, S: int) -> tuple[int, int]:
+    """Region height and width for an S x S grid (p1 §2, §3; reading R3)."""
+    if S < 1 or H % S or W % S:
+        raise ValueError(f"S={S} must divide H={H} and W={W}")
+    return H // S, W // S
+
+
+def region_token_maps(H: int, W: int, S: int) -> tuple[np.ndarray, np.ndarray]:
+    """Partition step (p1 §3, reading R2).
+
+    Returns two int arrays of shape [H, W]: the region index of each pixel
+    (row-major over the S x S grid) and its token index inside its region
+    (row-major over the hs x ws region).
+    """
+    hs, ws = region_shape(H, W, S)
+    y = np.arange(H)[:, None]
+    x = np.arange(W)[None, :]
+    region = (y // hs) * S + (x // ws)
+    token = (y % hs) * ws + (x % ws)
+    return region.astype(np.int64), token.astype(np.int64)
+
+
+def region_tokens(H: int, W: int, S: int, r: int) -> tuple[np.ndarray, np.ndarray]:
+    """(ys, xs) pixel coordinates of region r's tokens in token order (R2)."""
+    hs, ws = region_shape(H, W, S)
+    ry, rx = divmod(int(r), S)
+    t = np.arange(hs * ws)
+    return ry * hs + t // ws, rx * ws + t % ws
+
+
+def region_mean(X, S: int) -> np.ndarray:
+    """Region pooling (p1 §3 region-mean step; p2 §2 mean over the region axes).
+
+    X: [B, H, W, C].  Returns [B, S*S, C]: the mean of each region's tokens,
+    regions row-major (R2, R7).
+    """
+    X = _f64(X)
+    B, H, W, C = X.shape
+    hs, ws = region_shape(H, W, S)
+    out = np.empty((B, S * S, C), dtype=np.float64)
+    for i in range(S):
+        for j in range(S):
+            block = X[:, i * hs:(i + 1) * hs, j * ws:(j + 1) * ws, :]
+            out[:, i * S + j, :] = block.reshape(B, hs * ws, C).mean(axis=1)
+    return out
+
+
+def region_affinity(q_r, k_r, route_scale: float) -> np.ndarray:
+    """Region-to-region affinity (p1 §3; p2 §4 with its scale; R4, R5).
+
+    q_r, k_r: [B, S*S, C] region means.  Returns [B, S*S, S*S] with entry
+    [b, r, s] = route_scale * <q_r[b, r], k_r[b, s]>.
+    """
+    q_r = _f64(q_r)
+    k_r = _f64(k_r)
+    return float(route_scale) * np.matmul(q_r, np.swapaxes(k_r, -1, -2))
+
+
+def topk_route(A, topk: int) -> np.ndarray:
+    """Top-k routing index (p1 §3 top-k over the affinity rows; p2 §4; R6).
+
+    A: [B, R, R].  Returns int32 [B, R, topk]: per row, the column indices of
+    the topk largest entries, largest first, equal values by lower index.
+    """
+    A = _f64(A)
+    R = A.shape[-1]
+    if not 1 <= topk <= R:
+        raise ValueError(f"topk={topk} must be in [1, {R}]")
+    # A stable sort of the negated values keeps equal values in index order.
+    order = np.argsort(-A, axis=-1, kind="stable")
+    return order[..., :topk].astype(np.int32)
+
+
+def routed_attention(Q, K, V, idx, heads: int, S: int, attn_scale: float) -> np.ndarray:
+    """Token-to-token attention over the routed regions (p1 §3 gather and
+    attention; p5: attention over the union of the routed regions; R8, R10).
+
+    Q, K, V: [B, H, W, C]; idx: [B, S*S, topk] region indices.
+    For query pixel p in region r, the keys are all tokens of the regions
+    idx[b, r, 0..topk-1] (region order, then token order; the order does not
+    change the result).  Per head m (channels m*d .. m*d+d-1):
+        O_p = sum_t softmax_t(attn_scale * <Q_p, K_t>) V_t.
+    Returns O: [B, H, W, C] float64.
+    """
+    Q = _f64(Q)
+    K = _f64(K)
+    V = _f64(V)
+    idx = np.asarray(idx)
+    B, H, W, C = Q.shape
+    if C % heads:
+        raise ValueError("heads must divide C")
+    d = C // heads
+    n_reg = S * S
+    coords = [region_tokens(H, W, S, r) for r in range(n_reg)]
+    O = np.zeros_like(Q)
+    for b in range(B):
+        for r in range(n_reg):
+            ys, xs = coords[r]
+            q = Q[b, ys, xs, :].reshape(-1, heads, d)            # [n, h, d]
+            key_y = np.concatenate([coords[s][0] for s in idx[b, r]])
+            key_x = np.concatenate([coords[s][1] for s in idx[b, r]])
+            k = K[b, key_y, key_x, :].reshape(-1, heads, d)      # [m, h, d]
+            v = V[b, key_y, key_x, :].reshape(-1, heads, d)
+            logits = attn_scale * np.einsum("nhd,mhd->hnm", q, k)
+            logits = logits - logits.max(axis=-1, keepdims=True)
+            p = np.exp(logits)
+            p = p / p.sum(axis=-1, keepdims=True)
+            o = np.einsum("hnm,mhd->nhd", p, v)
+            O[b, ys, xs, :] = o.reshape(-1, C)
+    return O
+
+
+def lepe(V, w, bias=None) -> np.ndarray:
+    """Local enhancement term (p2 §4 depthwise Conv2d on V; p1 §3 adds it to the
+    attention output; R9).
+
+    V: [B, H, W, C]; w: [C, ks, ks]; bias: [C] or None.
+    L[b, y, x, c] = bias[c] + sum_{i,j} w[c, i, j] * V[b, y+i-ks//2, x+j-ks//2, c],
+    with V taken as zero outside the image.
+    """
+    V = _f64(V)
+    w = _f64(w)
+    B, H, W, C = V.shape
+    ks = w.shape[-1]
+    if w.shape != (C, ks, ks) or ks % 2 == 0:
+        raise ValueError("w must be [C, ks, ks] with odd ks")
+    p = ks // 2
+    Vp = np.zeros((B, H + 2 * p, W + 2 * p, C), dtype=np.float64)
+    Vp[:, p:p + H, p:p + W, :] = V
+    L = np.zeros_like(V)
+    for i in range(ks):
+        for j in range(ks):
+            L += w[:, i, j] * Vp[:, i:i + H, j:j + W, :]
+    if bias is not None:
+        L += _f64(bias)
+    return L
+
+
+def bra_forward(Q, K, V, heads: int, S: int, topk: int, w=None, bias=None,
+                route_scale: float | None = None, attn_scale: float | None = None,
+                return_parts: bool = False):
+    """The whole BRA forward pass in the pages' order (p1 §3; p2 §2, §4).
+
+    partition -> region means -> scaled affinity -> top-k index ->
+    attention over the routed regions -> + LePE(V).
+    Returns (out, idx) or, with return_parts, a dict with every intermediate.
+    """
+    Q = _f64(Q)
+    K = _f64(K)
+    V = _f64(V)
+    B, H, W, C = Q.shape
+    region_shape(H, W, S)
+    if route_scale is None:
+        route_scale = C ** -0.5
+    if attn_scale is None:
+        attn_scale = (C // heads) ** -0.5
+    q_r = region_mean(Q, S)
+    k_r = region_mean(K, S)
+    A = region_affinity(q_r, k_r, route_scale)
+    idx = topk_route(A, topk)
+    O = routed_attention(Q, K, V, idx, heads, S, attn_scale)
+    L = lepe(V, w, bias) if w is not None else np.zeros_like(O)
+    out = O + L
+    if return_parts:
+        return {"out": out, "idx": idx, "q_r": q_r, "k_r": k_r, "A": A,
+                "O": O, "L": L}
+    return out, idx

@@ -1,0 +1,354 @@
+"""Pins for the fp64 oracle: checks against facts the oracle does not produce.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+a closed form, a hand-worked value, a brute-force definition written here
+independently, or a library routine (PyTorch CPU, float64).  The same
+functions run against deliberately broken copies of the oracle in
+``test_oracle_mutations.py`` to show that each plausible mistake is caught.
+
+Page keys (p1 cybasar.com BiFormer BRA explainer, p2 snabindia.com BRA
+article, p4 un.csdn.net window-attention write-up, p5 the arXiv 2303.08810
+abstract) are described in the oracle's header.
+"""
+
+from __future__ import annotations
+
+import glob
+import json
+import os
+
+import numpy as np
+
+import oracle.bra_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TIGHT = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, tol=TIGHT, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    scale = max(1.0, float(np.max(np.abs(b))) if b.size else 1.0)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol * scale, f"{what}: max abs err {err:.3e} > {tol * scale:.3e}"
+
+
+# --------------------------------------------------------------------------
+# independent brute-force definitions (written here, not taken from the oracle)
+
+def _pixel_region(H, W, S):
+    """Region id per flattened pixel, computed by scanning the grid cells."""
+    hs, ws = H // S, W // S
+    reg = np.empty(H * W, dtype=np.int64)
+    for y in range(H):
+        for x in range(W):
+            reg[y * W + x] = (y // hs) * S + (x // ws)
+    return reg
+
+
+def brute_masked_attention(Q, K, V, idx, heads, S, scale):
+    """Dense HW x HW attention with every key outside the routed regions
+    masked out (p5: attention over the union of the routed regions)."""
+    B, H, W, C = Q.shape
+    d = C // heads
+    reg = _pixel_region(H, W, S)
+    out = np.zeros((B, H * W, C))
+    for b in range(B):
+        q = Q[b].reshape(H * W, C)
+        k = K[b].reshape(H * W, C)
+        v = V[b].reshape(H * W, C)
+        allowed = np.zeros((H * W, H * W), dtype=bool)
+        for p in range(H * W):
+            allowed[p] = np.isin(reg, idx[b, reg[p]])
+        for m in range(heads):
+            sl = slice(m * d, (m + 1) * d)
+            logits = scale * (q[:, sl] @ k[:, sl].T)
+            logits = np.where(allowed, logits, -np.inf)
+            logits -= logits.max(axis=1, keepdims=True)
+            e = np.exp(logits)
+            out[b, :, sl] = (e / e.sum(axis=1, keepdims=True)) @ v[:, sl]
+    return out.reshape(B, H, W, C)
+
+
+def global_attention(Q, K, V, heads, scale):
+    """Textbook multi-head softmax(scale Q K^T) V over all H*W keys."""
+    B, H, W, C = Q.shape
+    d = C // heads
+    q = Q.reshape(B, H * W, heads, d).transpose(0, 2, 1, 3)
+    k = K.reshape(B, H * W, heads, d).transpose(0, 2, 1, 3)
+    v = V.reshape(B, H * W, heads, d).transpose(0, 2, 1, 3)
+    s = scale * q @ k.transpose(0, 1, 3, 2)
+    s -= s.max(-1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(-1, keepdims=True)
+    return (p @ v).transpose(0, 2, 1, 3).reshape(B, H, W, C)
+
+
+def window_attention(Q, K, V, heads, S, scale):
+    """p4's local window attention: split into non-overlapping windows,
+    softmax(Q K^T / sqrt(d_k)) V inside each, merge back."""
+    B, H, W, C = Q.shape
+    hs, ws = H // S, W // S
+
+    def split(X):  # [B, S, hs, S, ws, C] -> [B*S*S, hs*ws, C]
+        return X.reshape(B, S, hs, S, ws, C).transpose(0, 1, 3, 2, 4, 5).reshape(-1, hs * ws, C)
+
+    o = global_attention(split(Q)[:, :, None, :], split(K)[:, :, None, :],
+                         split(V)[:, :, None, :], heads, scale)
+    o = o.reshape(B, S, S, hs, ws, C).transpose(0, 1, 3, 2, 4, 5)
+    return o.reshape(B, H, W, C)
+
+
+def _rand(seed, B, H, W, C):
+    r = _rng(seed)
+    return r.normal(size=(B, H, W, C)), r.normal(size=(B, H, W, C)), r.normal(size=(B, H, W, C))
+
+
+# --------------------------------------------------------------------------
+# pins
+
+def pin_golden():
+    """Hand-worked fixtures under tests/golden/."""
+    files = sorted(glob.glob(os.path.join(GOLDEN, "*.json")))
+    assert files, "no golden fixtures"
+    for f in files:
+        g = json.load(open(f))
+        q, k, v = (np.array(g[n], dtype=np.float64) for n in ("q", "k", "v"))
+        C, ks = g["C"], g["lepe_ks"]
+        w = np.zeros((C, ks, ks))
+        for c, i, j, val in g["lepe_taps"]:
+            w[c, i, j] = val
+        bias = None if g["bias"] is None else np.array(g["bias"], dtype=np.float64)
+        parts = O.bra_forward(q, k, v, g["heads"], g["S"], g["topk"], w, bias,
+                              return_parts=True)
+        name = os.path.basename(f)
+        assert np.array_equal(parts["idx"], np.array(g["expect_idx"])), f"{name}: idx"
+        _close(parts["O"], g["expect_O"], 1e-14, f"{name}: O")
+        if "expect_L" in g:
+            _close(parts["L"], g["expect_L"], 1e-14, f"{name}: L")
+        _close(parts["out"], g["expect_out"], 1e-14, f"{name}: out")
+
+
+def pin_partition_layout():
+    """Region/token order equals p1 §3's reshape (S, H/S, S, W/S, C) with
+    axes 1 and 2 swapped, flattened to [S*S, n, C] (reading R2)."""
+    for (B, H, W, S) in ((1, 4, 6, 2), (2, 6, 6, 3), (1, 8, 4, 4)):
+        C = 3
+        X = _rng(1).normal(size=(B, H, W, C))
+        hs, ws = H // S, W // S
+        view = X.reshape(B, S, hs, S, ws, C).transpose(0, 1, 3, 2, 4, 5).reshape(B, S * S, hs * ws, C)
+        region, token = O.region_token_maps(H, W, S)
+        for r in range(S * S):
+            ys, xs = O.region_tokens(H, W, S, r)
+            assert np.array_equal(X[:, ys, xs, :], view[:, r]), "region_tokens order"
+            assert np.all(region[ys, xs] == r)
+            assert np.array_equal(token[ys, xs], np.arange(hs * ws))
+
+
+def pin_pool_avgpool():
+    """Region mean equals torch avg_pool2d with kernel = stride = region size."""
+    import torch
+    import torch.nn.functional as F
+    for (B, H, W, C, S) in ((2, 8, 8, 5, 2), (1, 12, 6, 4, 3), (1, 7, 7, 2, 7), (2, 4, 4, 3, 1)):
+        X = _rng(2).normal(size=(B, H, W, C))
+        ref = F.avg_pool2d(torch.from_numpy(X).permute(0, 3, 1, 2), (H // S, W // S))
+        ref = ref.permute(0, 2, 3, 1).reshape(B, S * S, C).numpy()
+        _close(O.region_mean(X, S), ref, 1e-13, "region_mean vs avg_pool2d")
+
+
+def pin_affinity_orientation():
+    """Constructed means: q_r = e0 for every region, k_r[s] = (s+1) e0, so
+    A[r, s] = scale (s+1) and every row routes to the last regions first."""
+    R, C = 9, 4
+    q = np.zeros((1, R, C))
+    q[..., 0] = 1.0
+    k = np.zeros((1, R, C))
+    k[0, :, 0] = np.arange(1, R + 1)
+    A = O.region_affinity(q, k, 0.5)
+    _close(A[0], np.tile(0.5 * np.arange(1, R + 1), (R, 1)), 1e-15, "affinity")
+    idx = O.topk_route(A, 3)
+    assert np.array_equal(idx[0], np.tile([8, 7, 6], (R, 1))), idx[0]
+    # orientation: a row-specific query picks a row-specific key region
+    q2 = np.eye(R)[None]
+    k2 = np.eye(R)[None][:, ::-1]          # key region s is e_{R-1-s}
+    idx2 = O.topk_route(O.region_affinity(q2, k2, 1.0), 1)[0, :, 0]
+    assert np.array_equal(idx2, np.arange(R)[::-1]), idx2
+
+
+def pin_topk_bruteforce():
+    """Top-k equals a plain-Python selection (largest first, ties to the lower
+    index) on small matrices with many exact ties, and torch.topk's values."""
+    import torch
+    r = _rng(3)
+    for trial in range(20):
+        R = int(r.integers(1, 12))
+        A = r.integers(-3, 4, size=(2, R, R)).astype(np.float64)   # many ties
+        for k in range(1, R + 1):
+            idx = O.topk_route(A, k)
+            for b in range(2):
+                for row in range(R):
+                    vals = list(A[b, row])
+                    chosen = []
+                    for _ in range(k):
+                        best = None
+                        for s in range(R):
+                            if s in chosen:
+                                continue
+                            if best is None or vals[s] > vals[best]:
+                                best = s
+                        chosen.append(best)
+                    assert list(idx[b, row]) == chosen, (A[b, row], idx[b, row], chosen)
+            tv = torch.topk(torch.from_numpy(A), k, dim=-1).values.numpy()
+            assert np.array_equal(np.take_along_axis(A, idx.astype(np.int64), -1), tv)
+
+
+def pin_scale_invariance():
+    """idx does not change under any positive routing scale (reading R5)."""
+    Q, K, _ = _rand(4, 2, 8, 8, 6)
+    qr, kr = O.region_mean(Q, 4), O.region_mean(K, 4)
+    base = O.topk_route(O.region_affinity(qr, kr, 1.0), 5)
+    for s in (1e-3, 0.37, 7.0):
+        assert np.array_equal(O.topk_route(O.region_affinity(qr, kr, s), 5), base)
+
+
+def pin_masked_dense():
+    """BRA attention equals dense attention masked to the routed regions, for
+    the oracle's own routes and for arbitrary routes (p5)."""
+    r = _rng(5)
+    for (B, H, W, C, heads, S) in ((2, 8, 8, 8, 2, 2), (1, 8, 8, 4, 1, 4), (1, 6, 9, 6, 3, 3)):
+        Q, K, V = _rand(int(r.integers(1 << 30)), B, H, W, C)
+        scale = (C // heads) ** -0.5
+        for topk in range(1, S * S + 1):
+            _, idx = O.bra_forward(Q, K, V, heads, S, topk)
+            got = O.routed_attention(Q, K, V, idx, heads, S, scale)
+            _close(got, brute_masked_attention(Q, K, V, idx, heads, S, scale), TIGHT,
+                   f"masked dense S={S} topk={topk}")
+            ridx = np.stack([np.stack([r.permutation(S * S)[:topk] for _ in range(S * S)])
+                             for _ in range(B)]).astype(np.int32)
+            got = O.routed_attention(Q, K, V, ridx, heads, S, scale)
+            _close(got, brute_masked_attention(Q, K, V, ridx, heads, S, scale), TIGHT,
+                   f"masked dense, random idx S={S} topk={topk}")
+
+
+def pin_global_when_all_routed():
+    """topk = S*S routes every region, so BRA is global attention + LePE."""
+    for (B, H, W, C, heads, S) in ((1, 6, 6, 4, 2, 3), (2, 8, 4, 6, 3, 2)):
+        Q, K, V = _rand(6, B, H, W, C)
+        w = _rng(7).normal(size=(C, 3, 3))
+        out, _ = O.bra_forward(Q, K, V, heads, S, S * S, w)
+        ref = global_attention(Q, K, V, heads, (C // heads) ** -0.5) + O.lepe(V, w)
+        _close(out, ref, TIGHT, "topk=S^2 vs global attention")
+
+
+def pin_plain_when_one_region():
+    """S = 1: one region holding every token, so BRA is plain attention."""
+    Q, K, V = _rand(8, 2, 5, 7, 4)
+    out, idx = O.bra_forward(Q, K, V, 2, 1, 1)
+    assert np.array_equal(idx, np.zeros((2, 1, 1), dtype=np.int32))
+    _close(out, global_attention(Q, K, V, 2, 2 ** -0.5), TIGHT, "S=1 vs plain attention")
+
+
+def pin_window_when_identity():
+    """idx[r] = [r] with topk = 1 is p4's non-overlapping window attention."""
+    for (B, H, W, C, heads, S) in ((2, 8, 8, 4, 2, 2), (1, 9, 6, 6, 1, 3)):
+        Q, K, V = _rand(9, B, H, W, C)
+        idx = np.tile(np.arange(S * S, dtype=np.int32)[None, :, None], (B, 1, 1))
+        scale = (C // heads) ** -0.5
+        _close(O.routed_attention(Q, K, V, idx, heads, S, scale),
+               window_attention(Q, K, V, heads, S, scale), TIGHT, "identity idx vs window")
+
+
+def pin_sdpa_masked():
+    """Attention equals torch scaled_dot_product_attention (fp64 CPU) with a
+    boolean mask built from the routing index."""
+    import torch
+    import torch.nn.functional as F
+    B, H, W, C, heads, S, topk = 2, 8, 8, 8, 2, 4, 3
+    Q, K, V = _rand(10, B, H, W, C)
+    _, idx = O.bra_forward(Q, K, V, heads, S, topk)
+    d = C // heads
+    reg = _pixel_region(H, W, S)
+    mask = np.stack([np.stack([np.isin(reg, idx[b, reg[p]]) for p in range(H * W)])
+                     for b in range(B)])                      # [B, HW, HW]
+    t = lambda X: torch.from_numpy(X.reshape(B, H * W, heads, d)).permute(0, 2, 1, 3)
+    ref = F.scaled_dot_product_attention(t(Q), t(K), t(V),
+                                         attn_mask=torch.from_numpy(mask)[:, None],
+                                         scale=d ** -0.5)
+    ref = ref.permute(0, 2, 1, 3).reshape(B, H, W, C).numpy()
+    _close(O.routed_attention(Q, K, V, idx, heads, S, d ** -0.5), ref, 1e-12, "sdpa")
+
+
+def pin_lepe_conv2d():
+    """LePE equals torch conv2d(groups=C, padding=ks//2) -- p2 §4's depthwise
+    Conv2d -- with an asymmetric kernel and a bias, for ks = 1, 3, 5, 7."""
+    import torch
+    import torch.nn.functional as F
+    for ks in (1, 3, 5, 7):
+        B, H, W, C = 2, 9, 6, 5
+        V = _rng(11).normal(size=(B, H, W, C))
+        w = _rng(12 + ks).normal(size=(C, ks, ks))
+        b = _rng(13).normal(size=C)
+        ref = F.conv2d(torch.from_numpy(V).permute(0, 3, 1, 2), torch.from_numpy(w)[:, None],
+                       torch.from_numpy(b), padding=ks // 2, groups=C)
+        _close(O.lepe(V, w, b), ref.permute(0, 2, 3, 1).numpy(), 1e-13, f"lepe ks={ks}")
+
+
+def pin_invariants():
+    """Closed-form special cases of the attention and LePE steps."""
+    B, H, W, C, heads, S, topk = 2, 8, 8, 6, 3, 4, 3
+    Q, K, V = _rand(14, B, H, W, C)
+    scale = (C // heads) ** -0.5
+    _, idx = O.bra_forward(Q, K, V, heads, S, topk)
+    base = O.routed_attention(Q, K, V, idx, heads, S, scale)
+    # permuting the routed regions inside a row changes nothing
+    perm = idx[..., ::-1].copy()
+    _close(O.routed_attention(Q, K, V, perm, heads, S, scale), base, TIGHT, "idx permutation")
+    # constant V: every output equals that vector
+    cv = np.broadcast_to(np.arange(1.0, C + 1), V.shape).copy()
+    _close(O.routed_attention(Q, K, cv, idx, heads, S, scale), cv, TIGHT, "constant V")
+    # Q = 0: uniform weights, output = mean of the gathered V
+    Z = np.zeros_like(Q)
+    got = O.routed_attention(Z, K, V, idx, heads, S, scale)
+    for b in range(B):
+        for r in range(S * S):
+            ys = np.concatenate([O.region_tokens(H, W, S, s)[0] for s in idx[b, r]])
+            xs = np.concatenate([O.region_tokens(H, W, S, s)[1] for s in idx[b, r]])
+            mean_v = V[b, ys, xs, :].mean(axis=0)
+            qy, qx = O.region_tokens(H, W, S, r)
+            _close(got[b, qy, qx, :], np.broadcast_to(mean_v, (len(qy), C)), TIGHT, "Q=0")
+    # zero LePE weights: out = O; centre-tap delta: L = V
+    ks = 5
+    out0, _ = O.bra_forward(Q, K, V, heads, S, topk, np.zeros((C, ks, ks)))
+    _close(out0, base, TIGHT, "w = 0")
+    delta = np.zeros((C, ks, ks))
+    delta[:, ks // 2, ks // 2] = 1.0
+    _close(O.lepe(V, delta), V, TIGHT, "delta kernel")
+    # one off-centre tap shifts V by one pixel with a zero border
+    shift = np.zeros((C, ks, ks))
+    shift[:, ks // 2, ks // 2 + 1] = 1.0
+    ref = np.zeros_like(V)
+    ref[:, :, :-1, :] = V[:, :, 1:, :]
+    _close(O.lepe(V, shift), ref, TIGHT, "shift kernel")
+
+
+def pin_route_ties():
+    """Exactly equal affinities go to the lower region index (reading R6)."""
+    R = 6
+    A = np.zeros((1, R, R))
+    A[0, 0] = [1, 3, 3, 2, 3, 0]
+    idx = O.topk_route(A, 4)
+    assert list(idx[0, 0]) == [1, 2, 4, 3]
+    assert list(idx[0, 1]) == [0, 1, 2, 3]
+
+
+ALL_PINS = [
+    pin_golden, pin_partition_layout, pin_pool_avgpool, pin_affinity_orientation,
+    pin_topk_bruteforce, pin_scale_invariance, pin_masked_dense,
+    pin_global_when_all_routed, pin_plain_when_one_region, pin_window_when_identity,
+    pin_sdpa_masked, pin_lepe_conv2d, pin_invariants, pin_route_ties,
+]

@@ -1,0 +1,135 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check that the pins
+catch every one of them.  Each mutant replaces one oracle function for the
+duration of a test; at least one pin must then fail."""
+
+import numpy as np
+import pytest
+
+import oracle.bra_oracle as O
+from oracle_pins import ALL_PINS
+
+_orig = {name: getattr(O, name) for name in
+         ("region_mean", "region_affinity", "topk_route", "routed_attention", "lepe",
+          "region_tokens")}
+
+
+def _mean_as_sum(X, S):
+    B, H, W, C = np.shape(X)
+    return _orig["region_mean"](X, S) * ((H // S) * (W // S))
+
+
+def _mean_column_major(X, S):
+    m = _orig["region_mean"](X, S)
+    B, R, C = m.shape
+    return m.reshape(B, S, S, C).transpose(0, 2, 1, 3).reshape(B, R, C)
+
+
+def _affinity_transposed(q_r, k_r, s):
+    return _orig["region_affinity"](k_r, q_r, s)
+
+
+def _topk_smallest(A, k):
+    return np.argsort(np.asarray(A), axis=-1, kind="stable")[..., :k].astype(np.int32)
+
+
+def _topk_ties_high(A, k):
+    A = np.asarray(A)
+    R = A.shape[-1]
+    order = np.argsort(-A[..., ::-1], axis=-1, kind="stable")
+    return (R - 1 - order[..., :k]).astype(np.int32)
+
+
+def _attn_unscaled(Q, K, V, idx, heads, S, scale):
+    return _orig["routed_attention"](Q, K, V, idx, heads, S, 1.0)
+
+
+def _attn_first_region_only(Q, K, V, idx, heads, S, scale):
+    idx = np.asarray(idx)
+    return _orig["routed_attention"](Q, K, V, np.repeat(idx[..., :1], idx.shape[-1], -1),
+                                     heads, S, scale)
+
+
+def _attn_heads_interleaved(Q, K, V, idx, heads, S, scale):
+    C = np.shape(Q)[-1]
+    d = C // heads
+    perm = np.arange(C).reshape(d, heads).T.reshape(-1)      # channel c*heads+m -> head m
+    inv = np.argsort(perm)
+    P = lambda X: np.asarray(X, dtype=np.float64)[..., perm]
+    return _orig["routed_attention"](P(Q), P(K), P(V), idx, heads, S, scale)[..., inv]
+
+
+def _attn_softmax_over_queries(Q, K, V, idx, heads, S, scale):
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    B, H, W, C = Q.shape
+    d = C // heads
+    out = np.zeros_like(Q)
+    for b in range(B):
+        for r in range(S * S):
+            ys, xs = O.region_tokens(H, W, S, r)
+            ky = np.concatenate([O.region_tokens(H, W, S, s)[0] for s in idx[b, r]])
+            kx = np.concatenate([O.region_tokens(H, W, S, s)[1] for s in idx[b, r]])
+            q = Q[b, ys, xs].reshape(-1, heads, d)
+            k = K[b, ky, kx].reshape(-1, heads, d)
+            v = V[b, ky, kx].reshape(-1, heads, d)
+            lg = scale * np.einsum("nhd,mhd->hnm", q, k)
+            p = np.exp(lg - lg.max(axis=1, keepdims=True))
+            p = p / p.sum(axis=1, keepdims=True)
+            out[b, ys, xs] = np.einsum("hnm,mhd->nhd", p, v).reshape(-1, C)
+    return out
+
+
+def _lepe_flipped(V, w, bias=None):
+    return _orig["lepe"](V, np.asarray(w)[:, ::-1, ::-1], bias)
+
+
+def _lepe_transposed(V, w, bias=None):
+    return _orig["lepe"](V, np.swapaxes(np.asarray(w), 1, 2), bias)
+
+
+def _lepe_no_bias(V, w, bias=None):
+    return _orig["lepe"](V, w, None)
+
+
+def _lepe_circular(V, w, bias=None):
+    V = np.asarray(V, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    ks = w.shape[-1]
+    p = ks // 2
+    L = np.zeros_like(V)
+    for i in range(ks):
+        for j in range(ks):
+            L += w[:, i, j] * np.roll(V, shift=(p - i, p - j), axis=(1, 2))
+    return L + (0 if bias is None else np.asarray(bias))
+
+
+def _tokens_column_major(H, W, S, r):
+    hs, ws = H // S, W // S
+    ry, rx = divmod(int(r), S)
+    t = np.arange(hs * ws)
+    return ry * hs + t % hs, rx * ws + t // hs
+
+
+MUTANTS = {
+    "region_mean": [_mean_as_sum, _mean_column_major],
+    "region_affinity": [_affinity_transposed],
+    "topk_route": [_topk_smallest, _topk_ties_high],
+    "routed_attention": [_attn_unscaled, _attn_first_region_only, _attn_heads_interleaved,
+                         _attn_softmax_over_queries],
+    "lepe": [_lepe_flipped, _lepe_transposed, _lepe_no_bias, _lepe_circular],
+    "region_tokens": [_tokens_column_major],
+}
+CASES = [(name, m) for name, ms in MUTANTS.items() for m in ms]
+
+
+@pytest.mark.parametrize("name,mutant", CASES, ids=[m.__name__.strip("_") for _, m in CASES])
+def test_mutant_is_caught(monkeypatch, name, mutant):
+    monkeypatch.setattr(O, name, mutant)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except Exception as e:  # AssertionError, or a shape error from the mutant
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the mutant {mutant.__name__} of {name}"

@@ -1,0 +1,10 @@
+"""The fp64 oracle against facts it does not produce itself (CPU only)."""
+
+import pytest
+
+from oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_pin(pin):
+    pin()

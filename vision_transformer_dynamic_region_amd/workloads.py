@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs for the BRA forward pass.
+
+This module only draws numbers: it holds none of the method's arithmetic.
+Both the HIP path's callers (tests, bench) and the fp64 oracle take their
+inputs from here, so that they see the same bits.
+
+Recipe (stands in for the BiFormer stage shapes of 224x224 ImageNet
+classification and the stride-4 map of 512x512 segmentation):
+
+* NumPy ``default_rng(seed)`` (PCG64), float64 draws, cast to float32.
+* seed = 1000 * config_index + {Q: 0, K: 1, V: 2, w: 3, mu_Q: 4, mu_K: 5, mu_V: 6}.
+* Q, K, V ~ N(0, 1) i.i.d.; the dense-prediction shape also adds a per-region
+  offset mu[b, region, c] ~ N(0, 0.5), drawn separately for Q, K and V and
+  broadcast over the region's pixels, so that routing is non-uniform.
+* LePE weights w ~ N(0, 0.02), shape [C, 5, 5], float32; no bias.
+* For bf16 workloads the float32 values are rounded to bfloat16 with
+  round-to-nearest-even; the rounded values (exact in float32 and float64)
+  are what both sides receive.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "bf16_round", "bf16_bits", "make_inputs",
+           "workload"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int          # seed base = 1000 * index
+    dtype: str          # "f32" or "bf16"
+    B: int
+    H: int
+    W: int
+    C: int
+    heads: int
+    S: int
+    topk: int
+    lepe_ks: int = 5
+    region_offset_std: float = 0.0   # std of the per-region mean offset (0: none)
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.H * self.W
+
+    @property
+    def n(self) -> int:
+        """Tokens per region."""
+        return (self.H // self.S) * (self.W // self.S)
+
+    @property
+    def keys(self) -> int:
+        """Keys seen by each query: topk routed regions of n tokens."""
+        return self.topk * self.n
+
+    @property
+    def d(self) -> int:
+        return self.C // self.heads
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def tensor_bytes(self) -> int:
+        return self.tokens * self.C * self.elem_bytes
+
+    @property
+    def attn_flops(self) -> int:
+        """Routed attention work: 2 GEMMs of 2*keys*C flops per token."""
+        return 4 * self.tokens * self.keys * self.C
+
+    def scaled(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 0, "f32", 1, 28, 28, 64, 2, 7, 4),
+    "st1": Workload("st1", 1, "bf16", 64, 56, 56, 64, 2, 7, 1),
+    "st2": Workload("st2", 2, "bf16", 64, 28, 28, 128, 4, 7, 4),
+    "st3": Workload("st3", 3, "bf16", 64, 14, 14, 256, 8, 7, 16),
+    "dense": Workload("dense", 4, "bf16", 8, 128, 128, 64, 2, 16, 4,
+                      region_offset_std=0.5),
+}
+
+
+def workload(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even.
+
+    Finite inputs only (the generators never produce inf or nan).
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    u = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return u.astype(np.uint16)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float32 values rounded to the nearest bfloat16 (ties to even), as float32."""
+    bits = bf16_bits(x).astype(np.uint32) << np.uint32(16)
+    return bits.view(np.float32)
+
+
+def _normal(seed: int, shape, std: float = 1.0) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    return rng.normal(0.0, std, size=shape)
+
+
+def make_inputs(wl: Workload, seed_base: int | None = None, with_weights: bool = True):
+    """Draw (Q, K, V, w) for a workload.
+
+    Returns a dict with float32 arrays ``q``, ``k``, ``v`` [B, H, W, C]
+    (already rounded to bf16 values for bf16 workloads), ``w`` [C, ks, ks]
+    float32 (or None) and ``bias`` (always None: the workloads carry none).
+    """
+    base = 1000 * wl.index if seed_base is None else seed_base
+    shape = (wl.B, wl.H, wl.W, wl.C)
+    out = {}
+    for name, off, mu_off in (("q", 0, 4), ("k", 1, 5), ("v", 2, 6)):
+        x = _normal(base + off, shape)
+        if wl.region_offset_std > 0.0:
+            hs, ws = wl.H // wl.S, wl.W // wl.S
+            mu = _normal(base + mu_off, (wl.B, wl.S, wl.S, wl.C), wl.region_offset_std)
+            # broadcast the per-region offset over the region's pixels
+            x = x + np.repeat(np.repeat(mu, hs, axis=1), ws, axis=2)
+        x = x.astype(np.float32)
+        if wl.dtype == "bf16":
+            x = bf16_round(x)
+        out[name] = x
+    if with_weights and wl.lepe_ks > 0:
+        out["w"] = _normal(base + 3, (wl.C, wl.lepe_ks, wl.lepe_ks), 0.02).astype(np.float32)
+    else:
+        out["w"] = None
+    out["bias"] = None
+    return out
