@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Throughput of the BRA forward pass on one MI355X.
+
+A step is one bra_forward call (region pooling, routing, gather-attention,
+LePE) over one batch of seeded synthetic input of the BiFormer stage-1 shape
+(B=64, 56x56, C=64, 2 heads of 32, S=7, topk=1, 5x5 LePE) unless --workload
+says otherwise.  Inputs are resident in HBM before timing starts.  Several
+copies of the batch are rotated so that a step does not find its inputs in
+the 256 MB Infinity Cache left there by the previous step.
+
+Prints one JSON line: tokens/s of the whole pass, the attention kernel's
+roofline (HIP events on the launch stream), and the fp64 CPU oracle's
+throughput on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import resource
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "BRA fwd tokens/s + attention TFLOP/s (% of MI355X bf16 MFMA peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+MALL_BYTES = 256 << 20         # Infinity Cache
+KERNEL_SOURCES = [
+    "vision_transformer_dynamic_region_amd/csrc/bra_kernels.hip",
+    "vision_transformer_dynamic_region_amd/csrc/bra_api.cpp",
+]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="st1", choices=["tiny", "st1", "st2", "st3", "dense"])
+    p.add_argument("--sets", type=int, default=0,
+                   help="input copies rotated across steps (0: enough to exceed the MALL)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--copy-probe-mb", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def copy_probe(mb: int) -> None:
+    import torch
+    n = mb << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}))
+
+
+def cpu_baseline(wl, x, target_s: float):
+    """Time the fp64 oracle on the first images of the same batch."""
+    import numpy as np
+    import oracle
+
+    def run(nb):
+        ru0 = resource.getrusage(resource.RUSAGE_SELF)
+        t0 = time.perf_counter()
+        oracle.bra_forward(x["q"][:nb], x["k"][:nb], x["v"][:nb], wl.heads, wl.S, wl.topk, x["w"])
+        dt = time.perf_counter() - t0
+        ru1 = resource.getrusage(resource.RUSAGE_SELF)
+        cpu = (ru1.ru_utime - ru0.ru_utime) + (ru1.ru_stime - ru0.ru_stime)
+        return dt, cpu
+
+    t1, _ = run(1)
+    nb = int(max(1, min(wl.B, target_s / max(t1, 1e-3))))
+    dt, cpu = run(nb)
+    tokens = nb * wl.H * wl.W
+    return {
+        "value": tokens / dt,
+        "unit": "tokens/s",
+        "cores": max(1, int(round(cpu / dt))),
+        "kind": "oracle",
+        "sample": (f"{wl.name}: first {nb} of {wl.B} images ({tokens} tokens), full fp64 "
+                   f"pass in {dt:.1f} s; host has {len(os.sched_getaffinity(0))} usable cores"),
+    }
+
+
+def main() -> int:
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the BRA forward "
+              "pass here is a single-GPU kernel path", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import vision_transformer_dynamic_region_amd as bra
+    from vision_transformer_dynamic_region_amd.workloads import WORKLOADS, bf16_bits, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if a.copy_probe_mb:
+        copy_probe(a.copy_probe_mb)
+        return 0
+
+    wl = WORKLOADS[a.workload]
+    dev = torch.device("cuda:0")
+    log(f"workload {wl}")
+    x = make_inputs(wl)
+    if wl.dtype == "bf16":
+        up = lambda arr: torch.from_numpy(bf16_bits(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        up = lambda arr: torch.from_numpy(arr).to(dev)
+    q0, k0, v0 = up(x["q"]), up(x["k"]), up(x["v"])
+    w = torch.from_numpy(x["w"]).to(dev)
+    set_bytes = 4 * wl.tensor_bytes
+    sets = a.sets or max(1, -(-3 * MALL_BYTES // set_bytes))
+    wsb = bra.workspace_bytes(wl.B, wl.S, wl.C)
+    bufs = []
+    for i in range(sets):
+        bufs.append(dict(q=q0.clone(), k=k0.clone(), v=v0.clone(), out=torch.empty_like(q0),
+                         idx=torch.empty((wl.B, wl.S * wl.S, wl.topk), dtype=torch.int32, device=dev),
+                         ws=torch.empty(wsb, dtype=torch.uint8, device=dev)))
+    torch.cuda.synchronize()
+    log(f"{sets} input sets of {set_bytes / 1e6:.1f} MB rotated per step")
+
+    def step(i):
+        b = bufs[i % sets]
+        bra.forward(b["q"], b["k"], b["v"], wl.heads, wl.S, wl.topk, w, out=b["out"],
+                    idx=b["idx"], workspace=b["ws"])
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {a.warmup} steps done")
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(a.steps):
+        step(i)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / a.steps
+    log(f"timed {a.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / a.steps:.4f} ms/step)")
+
+    # Per-kernel durations: the same kernels launched through the two
+    # single-stage entry points (bra_route: pooling + routing; bra_attend:
+    # gather-attention with the LePE term fused), with HIP events between
+    # them on the stream the kernels run on (torch's current stream, which
+    # the binding passes to the library).
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    for i in range(a.steps):
+        b = bufs[i % sets]
+        ev[i][0].record(stream)
+        bra.route(b["q"], b["k"], wl.S, wl.topk, workspace=b["ws"])
+        ev[i][1].record(stream)
+        bra.attend(b["q"], b["k"], b["v"], b["idx"], wl.heads, wl.S, lepe_w=w, out=b["out"])
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t_route = sum(e[0].elapsed_time(e[1]) for e in ev) / a.steps
+    t_attn = sum(e[1].elapsed_time(e[2]) for e in ev) / a.steps
+    log(f"per stage (ms): pool+route {t_route:.4f}  attend+lepe {t_attn:.4f}")
+
+    tokens = wl.tokens
+    attn_bytes = 4 * wl.tensor_bytes           # Q, K, V read once + out written once
+    attn_gbs = attn_bytes / (t_attn * 1e-3) / 1e9
+    attn_tflops = wl.attn_flops / (t_attn * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("kernel_sha") == kernel_sha() and rec.get("workload") == wl.name:
+            traffic = rec.get("bytes_per_launch")
+
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: B={wl.B} H=W={wl.H} C={wl.C} heads={wl.heads} "
+                               f"d={wl.d} S={wl.S} topk={wl.topk} LePE {wl.lepe_ks}x{wl.lepe_ks}",
+                   "tokens_per_step": tokens, "input_sets_rotated": sets},
+        "attention": {"tflops": attn_tflops, "frac_bf16_peak": attn_tflops / BF16_PEAK_TFLOPS,
+                      "ms": t_attn},
+        "stages_ms": {"pool_route": t_route, "attend_lepe": t_attn},
+        "roofline": {"kernel": "attend_kernel", "bound": "hbm", "achieved": attn_gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes": attn_bytes},
+        "kernel_sha": kernel_sha(),
+    }
+    if not a.no_cpu_baseline:
+        log("timing the fp64 oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

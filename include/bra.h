@@ -1,0 +1,123 @@
+/*
+ * bra.h -- C ABI of libbra: the Bi-Level Routing Attention (BRA) forward pass
+ * of BiFormer on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (page keys: p1 = cybasar.com "CVPR2023: BiFormer中的双层
+ * 路由注意力机制解析", p2 = snabindia.com "从静态到动态：BRA双层路由注意力如何
+ * 革新视觉Transformer的计算范式", p5 = hyper.ai abstract of arXiv 2303.08810):
+ *
+ *   1. partition (p1 §3): an H x W map is split into S x S regions of
+ *      hs = H/S by ws = W/S pixels; regions are numbered row-major over the
+ *      grid, pixels row-major inside a region;
+ *   2. region means (p1 §3, p2 §2): q_r, k_r = mean of Q, K over each region;
+ *   3. affinity (p1 §3, p2 §4): A[r][s] = route_scale * <q_r[r], k_r[s]>;
+ *   4. routing (p1 §3, p2 §4): idx[r] = the topk columns of row r of A,
+ *      largest first, equal values by lower region index;
+ *   5. attention (p1 §3, p5): every query pixel of region r attends, per head
+ *      (d = C / heads contiguous channels), over all tokens of the regions
+ *      idx[r][0..topk-1] with softmax(attn_scale * q.k) weights;
+ *   6. LePE (p2 §4, p1 §3): out = attention + bias + depthwise ks x ks
+ *      cross-correlation of V over the whole image, zero padded.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors Q, K, V and out are [B, H, W, C] channels-last, contiguous,
+ *     in the element type `dtype` (BRA_F32 or BRA_BF16), 16-byte aligned.
+ *   - idx is int32 [B, S*S, topk], contiguous.
+ *   - LePE weights are float32 [C, ks, ks] (PyTorch depthwise Conv2d weight
+ *     without its singleton axis); bias is float32 [C] or NULL.
+ *   - All pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises; it enqueues kernels on
+ *     `stream` (a hipStream_t; NULL means the default stream) and returns.
+ *   - Every argument is checked on the host before anything is enqueued; a
+ *     rejected call enqueues nothing.  A failed launch returns BRA_E_HIP.
+ *     bra_last_error() gives a thread-local message for the last failure.
+ *   - Supported: head width d = C / heads == 32, odd ks in 1..7, S*S <= 1024,
+ *     C <= 1024.  Other valid shapes return BRA_E_UNSUPPORTED.
+ *   - Calls on one stream are ordered; calls that share a workspace or
+ *     output on different streams race.
+ */
+#ifndef BRA_H_
+#define BRA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { BRA_F32 = 0, BRA_BF16 = 1 } bra_dtype;
+
+typedef enum {
+  BRA_OK = 0,
+  BRA_E_INVAL = 1,        /* bad shape, pointer, alignment or value     */
+  BRA_E_UNSUPPORTED = 2,  /* valid BRA problem this build does not run  */
+  BRA_E_WORKSPACE = 3,    /* workspace missing or too small             */
+  BRA_E_HIP = 4           /* a HIP launch or runtime call failed        */
+} bra_status;
+
+/* Bytes of workspace bra_route / bra_forward need: two float64 tensors
+ * [B, S*S, C] holding the region means of Q (first) and K (second).  After a
+ * successful call the workspace holds exactly those means (p1 §3 region-mean
+ * step), which callers may read.  Returns 0 for non-positive sizes. */
+size_t bra_workspace_bytes(int B, int S, int C);
+
+/* Steps 1-4: region means of Q and K, scaled region affinity and per-row
+ * top-k (p1 §3; p2 §2 and §4 TopkRouting).
+ *   q, k        [B,H,W,C] dtype, device.
+ *   route_scale positive scale of the affinity (p2 §4); any positive value
+ *               gives the same idx.  Non-positive or non-finite: BRA_E_INVAL.
+ *   idx         out: int32 [B, S*S, topk], device.
+ *   topk_logits out: float32 [B, S*S, topk] affinities of the chosen regions
+ *               (same order as idx), device; may be NULL.
+ *   ws          device workspace of at least bra_workspace_bytes(B, S, C). */
+bra_status bra_route(const void* q, const void* k, int B, int H, int W, int C,
+                     int S, int topk, bra_dtype dtype, float route_scale,
+                     int32_t* idx, float* topk_logits, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Steps 5-6 with a caller-supplied routing index: gather-attention over the
+ * routed regions (p1 §3; p5) plus, when lepe_w is not NULL, the LePE term
+ * (p2 §4).  This is also the fixed-routing use: an index held constant
+ * across calls (p2 §5).
+ *   idx         int32 [B, S*S, topk], device; entries must lie in
+ *               [0, S*S) (entries outside are clamped, not trusted).
+ *   attn_scale  finite scale of q.k inside the softmax (1/sqrt(d) usual).
+ *   lepe_w      float32 [C, ks, ks] or NULL (no LePE); lepe_b float32 [C]
+ *               or NULL; lepe_ks odd in 1..7 (ignored when lepe_w is NULL).
+ *   out         [B,H,W,C] dtype, device; must not overlap q, k or v. */
+bra_status bra_attend(const void* q, const void* k, const void* v,
+                      const int32_t* idx, int B, int H, int W, int C,
+                      int heads, int S, int topk, bra_dtype dtype,
+                      float attn_scale, const float* lepe_w,
+                      const float* lepe_b, int lepe_ks, void* out,
+                      void* stream);
+
+/* The whole forward pass, steps 1-6 (p1 §3): bra_route then bra_attend on
+ * the same stream.  Arguments as above. */
+bra_status bra_forward(const void* q, const void* k, const void* v, int B,
+                       int H, int W, int C, int heads, int S, int topk,
+                       bra_dtype dtype, float route_scale, float attn_scale,
+                       const float* lepe_w, const float* lepe_b, int lepe_ks,
+                       void* out, int32_t* idx, float* topk_logits, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Step 6 alone, in place: out += bias + depthwise ks x ks cross-correlation
+ * of v (p2 §4 depthwise Conv2d; p1 §3 adds it to the attention output).
+ *   v, out [B,H,W,C] dtype, device, not overlapping; w float32 [C,ks,ks];
+ *   b float32 [C] or NULL. */
+bra_status bra_lepe(const void* v, const float* w, const float* b, int ks,
+                    int B, int H, int W, int C, bra_dtype dtype, void* out,
+                    void* stream);
+
+/* Static text for a status code. */
+const char* bra_strerror(int status);
+
+/* Thread-local detail of the last failed call on this thread ("" if none). */
+const char* bra_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BRA_H_ */

@@ -1,0 +1,143 @@
+"""The C ABI on the host: the library loads, exports what include/bra.h
+declares, and rejects bad arguments before touching the GPU (CPU only; no
+call here gets past argument checking)."""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import vision_transformer_dynamic_region_amd as bra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bra.h")
+
+OK, INVAL, UNSUP, WSERR = 0, 1, 2, 3
+F32, BF16 = 0, 1
+P = 0x10000          # a fake, 16-byte aligned device address; never dereferenced
+P2 = 0x20000000
+P3 = 0x40000000
+P4 = 0x60000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(bra_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bra.lib_path()):
+        pytest.skip("libbra.so not built")
+    return bra.load(require_torch=False)
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("bra_route", "bra_attend", "bra_forward", "bra_lepe", "bra_workspace_bytes",
+              "bra_strerror", "bra_last_error"):
+        assert n in names
+
+
+def test_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", bra.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(bra_\w+)$", out, re.M))
+    for n in declared_functions():
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_workspace_bytes(lib):
+    assert lib.bra_workspace_bytes(64, 7, 64) == 2 * 64 * 49 * 64 * 8
+    assert lib.bra_workspace_bytes(0, 7, 64) == 0
+
+
+def test_strerror(lib):
+    assert lib.bra_strerror(0) == b"ok"
+    assert b"workspace" in lib.bra_strerror(3)
+    assert lib.bra_strerror(99) == b"unknown status"
+
+
+def route(lib, q=P, k=P2, B=2, H=8, W=8, C=64, S=2, topk=2, dt=BF16, scale=0.125, idx=P3,
+          logits=None, ws=P4, wsb=1 << 20):
+    return lib.bra_route(q, k, B, H, W, C, S, topk, dt, scale, idx, logits, ws, wsb, None)
+
+
+def attend(lib, q=P, k=P2, v=P3, idx=P4, B=2, H=8, W=8, C=64, heads=2, S=2, topk=2, dt=BF16,
+           scale=0.17, w=None, b=None, ks=5, out=0x70000000):
+    return lib.bra_attend(q, k, v, idx, B, H, W, C, heads, S, topk, dt, scale, w, b, ks, out, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(H=9), INVAL, "divide"),
+    (dict(S=3), INVAL, "divide"),
+    (dict(topk=0), INVAL, "topk"),
+    (dict(topk=5), INVAL, "topk"),
+    (dict(B=0), INVAL, "positive"),
+    (dict(q=None), INVAL, "q is NULL"),
+    (dict(q=P + 8), INVAL, "aligned"),
+    (dict(idx=None), INVAL, "idx"),
+    (dict(scale=0.0), INVAL, "route_scale"),
+    (dict(scale=-1.0), INVAL, "route_scale"),
+    (dict(scale=math.nan), INVAL, "route_scale"),
+    (dict(scale=math.inf), INVAL, "route_scale"),
+    (dict(ws=None), WSERR, "NULL"),
+    (dict(wsb=100), WSERR, "needed"),
+    (dict(ws=P4 + 8), WSERR, "aligned"),
+    (dict(dt=7), INVAL, "dtype"),
+    (dict(C=60), UNSUP, "multiple of 8"),
+    (dict(C=2048), UNSUP, "exceeds"),
+    (dict(H=66, W=66, S=33), UNSUP, "regions"),
+])
+def test_route_rejects(lib, kw, status, msg):
+    assert route(lib, **kw) == status
+    assert msg in lib.bra_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(heads=3), INVAL, "heads"),
+    (dict(heads=0), INVAL, "heads"),
+    (dict(heads=1), UNSUP, "head width"),
+    (dict(C=128, heads=2), UNSUP, "head width"),
+    (dict(v=None), INVAL, "v is NULL"),
+    (dict(out=None), INVAL, "out is NULL"),
+    (dict(out=P + 1024), INVAL, "overlaps"),
+    (dict(out=P3), INVAL, "overlaps"),
+    (dict(scale=math.inf), INVAL, "attn_scale"),
+    (dict(w=P, ks=4), UNSUP, "lepe_ks"),
+    (dict(w=P, ks=9), UNSUP, "lepe_ks"),
+    (dict(w=P, ks=5, b=P + 4), INVAL, "bias"),
+    (dict(dt=F32, C=1024, heads=32), UNSUP, "exceeds"),
+    (dict(topk=9), INVAL, "topk"),
+])
+def test_attend_rejects(lib, kw, status, msg):
+    assert attend(lib, **kw) == status
+    assert msg in lib.bra_last_error().decode()
+
+
+def test_forward_checks_both_halves(lib):
+    st = lib.bra_forward(P, P2, P3, 2, 8, 8, 64, 2, 2, 2, BF16, 0.125, 0.17, None, None, 5,
+                         0x70000000, P4, None, None, 0, None)
+    assert st == WSERR
+    st = lib.bra_forward(P, P2, P3, 2, 8, 8, 64, 3, 2, 2, BF16, 0.125, 0.17, None, None, 5,
+                         0x70000000, P4, None, 0x7A000000, 1 << 20, None)
+    assert st == INVAL
+
+
+def test_lepe_rejects(lib):
+    assert lib.bra_lepe(P, P2, None, 5, 2, 8, 8, 48, BF16, P3, None) == UNSUP
+    assert lib.bra_lepe(P, None, None, 5, 2, 8, 8, 64, BF16, P3, None) == INVAL
+    assert lib.bra_lepe(P, P2, None, 6, 2, 8, 8, 64, BF16, P3, None) == UNSUP
+    assert lib.bra_lepe(P, P2, None, 5, 2, 8, 8, 64, BF16, P + 64, None) == INVAL
+
+
+def test_error_is_thread_local_and_cleared(lib):
+    assert route(lib, topk=0) == INVAL
+    assert lib.bra_last_error() != b""
+    # a later rejected call overwrites the message
+    assert route(lib, q=None) == INVAL
+    assert b"q is NULL" in lib.bra_last_error()

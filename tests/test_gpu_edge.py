@@ -1,0 +1,127 @@
+"""Edge cases of the HIP path vs the fp64 oracle, through the C ABI:
+ragged regions and key tails, non-square regions, topk = 1 and S*S, S = 1,
+one pixel per region, many tasks per region, the largest region grid, wide
+channels, float32, LePE kernel sizes and bias, exact ties, identity routing,
+out-of-range indices, determinism and a non-default stream."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_close, check_idx, oracle_parts, to_dev, to_host
+from vision_transformer_dynamic_region_amd.workloads import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+EDGE = {
+    # name: (B, H, W, C, heads, S, topk, dtype, ks)
+    "ragged_n36": (2, 12, 12, 64, 2, 2, 3, "bf16", 5),
+    "nonsquare_3x5": (1, 12, 20, 64, 2, 4, 5, "bf16", 5),
+    "topk1": (2, 16, 16, 64, 2, 4, 1, "bf16", 5),
+    "topk_all": (2, 16, 16, 64, 2, 4, 16, "bf16", 5),
+    "S1_plain": (2, 8, 8, 64, 2, 1, 1, "bf16", 5),
+    "one_pixel_regions": (1, 4, 4, 32, 1, 4, 3, "bf16", 3),
+    "many_tasks": (1, 16, 16, 256, 8, 2, 2, "bf16", 5),
+    "S32_R1024": (1, 64, 64, 32, 1, 32, 8, "bf16", 5),
+    "wide_C1024": (1, 8, 8, 1024, 32, 2, 2, "bf16", 3),
+    "f32_ragged": (1, 12, 12, 64, 2, 2, 3, "f32", 5),
+    "f32_all": (2, 16, 16, 128, 4, 4, 16, "f32", 7),
+    "f32_wide_C512": (1, 8, 8, 512, 16, 2, 2, "f32", 1),
+    "ks7_tall": (2, 24, 8, 96, 3, 4, 6, "bf16", 7),
+}
+
+
+def run(cuda, name, B, H, W, C, heads, S, topk, dtype, ks, bias=True, seed=None):
+    import torch
+    import vision_transformer_dynamic_region_amd as bra
+    wl = Workload(name, 100 + (seed or 0), dtype, B, H, W, C, heads, S, topk, lepe_ks=ks)
+    x = make_inputs(wl)
+    b = np.random.default_rng(7).normal(0, 0.1, size=C).astype(np.float32) if bias else None
+    ref = oracle_parts(x, heads, S, topk, x["w"], b)
+    q, k, v = (to_dev(x[n], dtype) for n in ("q", "k", "v"))
+    w = torch.from_numpy(x["w"]).to(cuda)
+    bt = torch.from_numpy(b).to(cuda) if b is not None else None
+    out, idx = bra.forward(q, k, v, heads, S, topk, w, bt)
+    torch.cuda.synchronize()
+    return wl, x, ref, out, idx, (q, k, v, w, bt)
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_forward(cuda, name):
+    print(f"[edge] {name} {EDGE[name]}", flush=True)
+    wl, x, ref, out, idx, _ = run(cuda, name, *EDGE[name])
+    idx_g = idx.cpu().numpy()
+    ties = check_idx(idx_g, ref["idx"], ref["A"])
+    out_ref = ref["out"]
+    if ties:
+        O = oracle.routed_attention(x["q"], x["k"], x["v"], idx_g, wl.heads, wl.S, wl.d ** -0.5)
+        out_ref = O + ref["L"]
+    assert_close(to_host(out), out_ref, wl.dtype, name)
+
+
+def test_exact_ties_go_to_lower_index(cuda):
+    """Q = 0 makes every affinity 0: the route must be 0, 1, ..., topk-1."""
+    import torch
+    import vision_transformer_dynamic_region_amd as bra
+    B, H, W, C, heads, S, topk = 2, 16, 16, 64, 2, 4, 5
+    wl = Workload("ties", 200, "bf16", B, H, W, C, heads, S, topk)
+    x = make_inputs(wl)
+    x["q"] = np.zeros_like(x["q"])
+    ref = oracle_parts(x, heads, S, topk, x["w"])
+    assert np.array_equal(ref["idx"][0, 0], np.arange(topk))
+    q, k, v = (to_dev(x[n], "bf16") for n in ("q", "k", "v"))
+    w = torch.from_numpy(x["w"]).to(cuda)
+    out, idx = bra.forward(q, k, v, heads, S, topk, w)
+    assert np.array_equal(idx.cpu().numpy(), ref["idx"])
+    assert_close(to_host(out), ref["out"], "bf16", "ties")
+
+
+def test_identity_route_is_window_attention(cuda):
+    """bra_attend with idx[r] = [r] (topk 1) is window attention inside each
+    region; the oracle's routed attention with that index is pinned to the
+    window formula on the CPU."""
+    import torch
+    import vision_transformer_dynamic_region_amd as bra
+    B, H, W, C, heads, S = 2, 16, 16, 64, 2, 4
+    wl = Workload("window", 300, "bf16", B, H, W, C, heads, S, 1)
+    x = make_inputs(wl)
+    ident = np.tile(np.arange(S * S, dtype=np.int32)[None, :, None], (B, 1, 1))
+    ref = oracle.routed_attention(x["q"], x["k"], x["v"], ident, heads, S, wl.d ** -0.5)
+    q, k, v = (to_dev(x[n], "bf16") for n in ("q", "k", "v"))
+    out = bra.attend(q, k, v, torch.from_numpy(ident).to(cuda), heads, S)
+    assert_close(to_host(out), ref, "bf16", "window")
+
+
+def test_out_of_range_index_is_clamped(cuda):
+    import torch
+    import vision_transformer_dynamic_region_amd as bra
+    B, H, W, C, heads, S, topk = 1, 8, 8, 64, 2, 2, 2
+    wl = Workload("clamp", 400, "f32", B, H, W, C, heads, S, topk)
+    x = make_inputs(wl)
+    bad = np.array([[[9, -3], [1, 0], [2, 77], [-1, 3]]], dtype=np.int32)
+    ref = oracle.routed_attention(x["q"], x["k"], x["v"], np.clip(bad, 0, S * S - 1), heads, S,
+                                  wl.d ** -0.5)
+    q, k, v = (to_dev(x[n], "f32") for n in ("q", "k", "v"))
+    out = bra.attend(q, k, v, torch.from_numpy(bad).to(cuda), heads, S)
+    assert_close(to_host(out), ref, "f32", "clamped index")
+
+
+def test_deterministic_and_stream(cuda):
+    import torch
+    import vision_transformer_dynamic_region_amd as bra
+    name = "topk_all"
+    wl, x, ref, out, idx, (q, k, v, w, bt) = run(cuda, name, *EDGE[name])
+    B, H, W, C, heads, S, topk, dtype, ks = EDGE[name]
+    for _ in range(3):
+        out2, idx2 = bra.forward(q, k, v, heads, S, topk, w, bt)
+        torch.cuda.synchronize()
+        assert torch.equal(idx2, idx)
+        assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out3, idx3 = bra.forward(q, k, v, heads, S, topk, w, bt)
+    s.synchronize()
+    assert torch.equal(idx3, idx)
+    assert torch.equal(out3.view(torch.int16), out.view(torch.int16))

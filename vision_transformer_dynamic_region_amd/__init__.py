@@ -1,0 +1,236 @@
+"""Bi-Level Routing Attention (BiFormer) forward pass on AMD MI355X.
+
+A thin ctypes binding over ``libbra.so`` (declared in ``include/bra.h``).
+It only marshals arguments: every step of the computation runs in the HIP
+kernels of the library.  PyTorch supplies device memory and the stream.
+
+    out, idx = forward(q, k, v, heads, S, topk, lepe_w)
+
+q, k, v: CUDA tensors [B, H, W, C] (float32 or bfloat16), contiguous;
+lepe_w: float32 [C, ks, ks] (depthwise conv weight), optional.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["BraError", "lib_path", "load", "workspace_bytes", "route", "attend",
+           "forward", "lepe", "STATUS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+STATUS = {0: "BRA_OK", 1: "BRA_E_INVAL", 2: "BRA_E_UNSUPPORTED", 3: "BRA_E_WORKSPACE",
+          4: "BRA_E_HIP"}
+_F32, _BF16 = 0, 1
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+_SIGNATURES = {
+    "bra_workspace_bytes": (_sz, [_i, _i, _i]),
+    "bra_route": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz, _vp]),
+    "bra_attend": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i,
+                        _vp, _vp]),
+    "bra_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _f, _vp, _vp, _i,
+                         _vp, _vp, _vp, _vp, _sz, _vp]),
+    "bra_lepe": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp]),
+    "bra_strerror": (ctypes.c_char_p, [_i]),
+    "bra_last_error": (ctypes.c_char_p, []),
+}
+
+
+class BraError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libbra.so")
+
+
+def load(require_torch: bool = True):
+    """Load libbra.so once.  With require_torch, torch is imported first so
+    that the library binds to the HIP runtime torch already loaded."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if require_torch:
+        import torch  # noqa: F401
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m vision_transformer_dynamic_region_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise BraError(status, load().bra_last_error().decode())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return _F32
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _dev(t, name, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def workspace_bytes(B: int, S: int, C: int) -> int:
+    return int(load().bra_workspace_bytes(B, S, C))
+
+
+def _bhwc(q):
+    if q.dim() != 4:
+        raise ValueError("tensors must be [B, H, W, C]")
+    return tuple(int(x) for x in q.shape)
+
+
+def _lepe_args(lepe_w, lepe_b, C):
+    import torch
+    if lepe_w is None:
+        return None, None, 0
+    _dev(lepe_w, "lepe_w", torch.float32)
+    if lepe_w.dim() != 3 or lepe_w.shape[0] != C or lepe_w.shape[1] != lepe_w.shape[2]:
+        raise ValueError("lepe_w must be [C, ks, ks]")
+    bptr = None
+    if lepe_b is not None:
+        _dev(lepe_b, "lepe_b", torch.float32)
+        if tuple(lepe_b.shape) != (C,):
+            raise ValueError("lepe_b must be [C]")
+        bptr = lepe_b.data_ptr()
+    return lepe_w.data_ptr(), bptr, int(lepe_w.shape[-1])
+
+
+def route(q, k, S: int, topk: int, route_scale: float | None = None, workspace=None,
+          return_logits: bool = False):
+    """Region means, scaled region affinity and per-row top-k (bra_route).
+
+    Returns idx int32 [B, S*S, topk] (and float32 logits with return_logits).
+    workspace, if given, is a CUDA uint8 tensor of >= workspace_bytes(B, S, C)
+    bytes; after the call it holds the float64 region means of q then k.
+    """
+    import torch
+    B, H, W, C = _bhwc(q)
+    dt = _dtype_code(q)
+    _dev(q, "q")
+    _dev(k, "k", q.dtype)
+    if tuple(k.shape) != (B, H, W, C):
+        raise ValueError("q and k must have the same shape")
+    if route_scale is None:
+        route_scale = C ** -0.5
+    idx = torch.empty((B, S * S, topk), dtype=torch.int32, device=q.device)
+    logits = torch.empty((B, S * S, topk), dtype=torch.float32, device=q.device) if return_logits else None
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(B, S, C), 16), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    _check(load().bra_route(q.data_ptr(), k.data_ptr(), B, H, W, C, S, topk, dt, float(route_scale),
+                            idx.data_ptr(), logits.data_ptr() if logits is not None else None,
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                            _stream(q)))
+    return (idx, logits) if return_logits else idx
+
+
+def attend(q, k, v, idx, heads: int, S: int, attn_scale: float | None = None, lepe_w=None,
+           lepe_b=None, out=None):
+    """Gather-attention over the routed regions plus optional LePE (bra_attend)."""
+    import torch
+    B, H, W, C = _bhwc(q)
+    dt = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, q.dtype)
+        if tuple(t.shape) != (B, H, W, C):
+            raise ValueError("q, k, v must have the same shape")
+    _dev(idx, "idx", torch.int32)
+    if idx.dim() != 3 or idx.shape[0] != B or idx.shape[1] != S * S:
+        raise ValueError("idx must be [B, S*S, topk]")
+    topk = int(idx.shape[2])
+    if attn_scale is None:
+        attn_scale = (C // heads) ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    wp, bp, ks = _lepe_args(lepe_w, lepe_b, C)
+    _check(load().bra_attend(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), B, H, W, C,
+                             heads, S, topk, dt, float(attn_scale), wp, bp, ks, out.data_ptr(),
+                             _stream(q)))
+    return out
+
+
+def forward(q, k, v, heads: int, S: int, topk: int, lepe_w=None, lepe_b=None,
+            route_scale: float | None = None, attn_scale: float | None = None, out=None,
+            idx=None, workspace=None, return_logits: bool = False):
+    """The whole BRA forward pass (bra_forward).  Returns (out, idx) or
+    (out, idx, logits) with return_logits."""
+    import torch
+    B, H, W, C = _bhwc(q)
+    dt = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, q.dtype)
+        if tuple(t.shape) != (B, H, W, C):
+            raise ValueError("q, k, v must have the same shape")
+    if route_scale is None:
+        route_scale = C ** -0.5
+    if attn_scale is None:
+        attn_scale = (C // heads) ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    if idx is None:
+        idx = torch.empty((B, S * S, topk), dtype=torch.int32, device=q.device)
+    _dev(idx, "idx", torch.int32)
+    if idx.numel() != B * S * S * topk:
+        raise ValueError("idx must hold B*S*S*topk entries")
+    logits = torch.empty((B, S * S, topk), dtype=torch.float32, device=q.device) if return_logits else None
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(B, S, C), 16), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    wp, bp, ks = _lepe_args(lepe_w, lepe_b, C)
+    _check(load().bra_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, W, C, heads, S, topk,
+                              dt, float(route_scale), float(attn_scale), wp, bp, ks, out.data_ptr(),
+                              idx.data_ptr(), logits.data_ptr() if logits is not None else None,
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              _stream(q)))
+    return (out, idx, logits) if return_logits else (out, idx)
+
+
+def lepe(v, w, b, out):
+    """out += b + depthwise conv(v, w) in place (bra_lepe).  Returns out."""
+    B, H, W, C = _bhwc(v)
+    dt = _dtype_code(v)
+    _dev(v, "v")
+    _dev(out, "out", v.dtype)
+    if tuple(out.shape) != (B, H, W, C):
+        raise ValueError("v and out must have the same shape")
+    wp, bp, ks = _lepe_args(w, b, C)
+    if wp is None:
+        raise ValueError("w is required")
+    _check(load().bra_lepe(v.data_ptr(), wp, bp, ks, B, H, W, C, dt, out.data_ptr(), _stream(v)))
+    return out

@@ -1,0 +1,41 @@
+// Internal interface between the C-ABI front end (bra_api.cpp) and the HIP
+// kernels (bra_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bra {
+
+// Problem shape after validation.  All sizes are positive, S divides H and
+// W, heads * 32 == C.
+struct Shape {
+  int B, H, W, C, S, heads, topk;
+  int hs, ws;     // region height / width in pixels
+  int n;          // pixels per region = hs * ws
+  int R;          // regions per image = S * S
+};
+
+// Region means of q and k into qm, km (float64 [B, R, C] each).
+hipError_t launch_pool(const void* q, const void* k, double* qm, double* km,
+                       const Shape& s, bool bf16, hipStream_t st);
+
+// Scaled affinity of the region means and per-row top-k.
+hipError_t launch_route(const double* qm, const double* km, const Shape& s,
+                        double route_scale, int32_t* idx, float* logits,
+                        hipStream_t st);
+
+// Gather-attention over the routed regions, plus the LePE term when w is
+// not null (fused into the attention epilogue when the region's halo tile
+// fits in LDS, otherwise written first by the standalone kernel).
+hipError_t launch_attend(const void* q, const void* k, const void* v,
+                         const int32_t* idx, const Shape& s, bool bf16,
+                         float attn_scale, const float* w, const float* bias,
+                         int ks, void* out, hipStream_t st);
+
+// out += bias + depthwise ks x ks cross-correlation of v.
+hipError_t launch_lepe(const void* v, const float* w, const float* b, int ks,
+                       const Shape& s, bool bf16, void* out, hipStream_t st);
+
+}  // namespace bra
