@@ -32,8 +32,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20         # Infinity Cache
 KERNEL_SOURCES = [
-    "vision_transformer_dynamic_region_amd/csrc/bra_kernels.hip",
-    "vision_transformer_dynamic_region_amd/csrc/bra_api.cpp",
+    "vision_transformer_dynamic_region_amd/csrc/attend_kernels.hip",
+    "vision_transformer_dynamic_region_amd/csrc/device_common.h",
+    "vision_transformer_dynamic_region_amd/csrc/fastdiv.h",
 ]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
 

@@ -82,7 +82,8 @@ bra_status bra_route(const void* q, const void* k, int B, int H, int W, int C,
  * across calls (p2 §5).
  *   idx         int32 [B, S*S, topk], device; entries must lie in
  *               [0, S*S) (entries outside are clamped, not trusted).
- *   attn_scale  finite scale of q.k inside the softmax (1/sqrt(d) usual).
+ *   attn_scale  positive, finite scale of q.k inside the softmax
+ *               (1/sqrt(d) usual); anything else: BRA_E_INVAL.
  *   lepe_w      float32 [C, ks, ks] or NULL (no LePE); lepe_b float32 [C]
  *               or NULL; lepe_ks odd in 1..7 (ignored when lepe_w is NULL).
  *   out         [B,H,W,C] dtype, device; must not overlap q, k or v. */

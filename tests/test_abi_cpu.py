@@ -108,6 +108,8 @@ def test_route_rejects(lib, kw, status, msg):
     (dict(out=P + 1024), INVAL, "overlaps"),
     (dict(out=P3), INVAL, "overlaps"),
     (dict(scale=math.inf), INVAL, "attn_scale"),
+    (dict(scale=0.0), INVAL, "attn_scale"),
+    (dict(scale=-0.2), INVAL, "attn_scale"),
     (dict(w=P, ks=4), UNSUP, "lepe_ks"),
     (dict(w=P, ks=9), UNSUP, "lepe_ks"),
     (dict(w=P, ks=5, b=P + 4), INVAL, "bias"),

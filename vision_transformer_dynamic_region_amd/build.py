@@ -15,7 +15,13 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbra.so")
-SOURCES = ["bra_kernels.hip", "bra_api.cpp"]
+SOURCES = ["route_kernels.hip", "attend_kernels.hip", "bra_api.cpp"]
+# per-file extra flags: the attention file assumes finite, non-NaN data (NaN
+# inputs give unspecified outputs) so that max/min need no NaN quieting, and
+# keeps MFMA accumulators in ordinary VGPRs next to the softmax arithmetic
+EXTRA_FLAGS = {
+    "attend_kernels.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -41,7 +47,8 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [cc, *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src),
+               "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)

@@ -60,6 +60,8 @@ bra_status check_shape(int B, int H, int W, int C, int S, int heads, int topk, b
   const long long pixels = (long long)B * H * W;
   if (pixels > (1LL << 31) / 8 || (long long)B * S * S > (1LL << 24))
     return fail(BRA_E_UNSUPPORTED, "problem too large (B*H*W=%lld)", pixels);
+  if ((long long)H * W * C >= (1LL << 31))
+    return fail(BRA_E_UNSUPPORTED, "one image of H*W*C=%lld elements exceeds 2^31", (long long)H * W * C);
   const long long n = (long long)(H / S) * (W / S);
   if (n * topk > (1LL << 30)) return fail(BRA_E_UNSUPPORTED, "topk*n=%lld keys per query is too many", n * topk);
   bra::Shape s;
@@ -114,7 +116,8 @@ bra_status check_attend_args(const void* q, const void* k, const void* v, const 
     return st;
   if (!idx) return fail(BRA_E_INVAL, "idx is NULL");
   if ((uintptr_t)idx & 3u) return fail(BRA_E_INVAL, "idx is not 4-byte aligned");
-  if (!std::isfinite(attn_scale)) return fail(BRA_E_INVAL, "attn_scale must be finite");
+  if (!(attn_scale > 0.f) || !std::isfinite(attn_scale))
+    return fail(BRA_E_INVAL, "attn_scale=%g must be positive and finite", (double)attn_scale);
   const size_t bytes = (size_t)s.B * s.H * s.W * s.C * elem_size(dt);
   if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
     return fail(BRA_E_INVAL, "out overlaps q, k or v");

@@ -1,0 +1,352 @@
+// Region pooling and routing kernels of the BRA forward pass (gfx950).
+//
+// Page keys: p1 = cybasar.com "CVPR2023: BiFormer中的双层路由注意力机制解析",
+// p2 = snabindia.com "从静态到动态：BRA双层路由注意力如何革新视觉Transformer的
+// 计算范式".
+
+#include <climits>
+
+#include "device_common.h"
+
+namespace bra {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Pool: region means of Q and K in float64 (p1 §3 region-mean step; p2 §2
+// mean over the region-internal axes).
+//
+// 32 lanes (half a wavefront) per region, 8 regions per workgroup.  A lane
+// owns one 16-byte channel group (gl lanes per pixel, gl the largest power
+// of two <= min(groups, 32); wider pixels take several passes) and a strided
+// subset of the region's pixels, whose loads it issues in batches.  The
+// partial sums of the 32/gl pixel lanes are then added across lanes with
+// row rotations (DPP) and a row swap (v_permlane16_swap): no LDS, no
+// barrier, and a fixed order, so the result is deterministic.  Summing bf16
+// or f32 values in float64 is exact or within one rounding of the exact
+// sum, so routing sees the same means as a float64 reference.
+// ---------------------------------------------------------------------------
+constexpr int kPoolBatch = 4;
+constexpr int kRegionsPerPoolBlock = kThreads / 32;
+
+struct PoolArgs {
+  const uint4* q;
+  const uint4* k;
+  double* qm;
+  double* km;
+  Shape s;
+  int gl;          // lanes per pixel (power of two, <= 32)
+  int units;       // B * R
+  FastDiv f_ws, f_R, f_S;
+};
+
+// Row rotation by SH lanes (DPP row_ror), applied to both halves of a double.
+template <int SH>
+__device__ __forceinline__ double ror_row(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), 0x120 | SH, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), 0x120 | SH, 0xf, 0xf, false);
+  return __hiloint2double(hi, lo);
+}
+
+// The value of lane l ^ 16 (rows swapped in pairs).
+__device__ __forceinline__ double xor16d(double v) {
+  const auto a = __builtin_amdgcn_permlane16_swap((unsigned)__double2loint(v), (unsigned)__double2loint(v), false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap((unsigned)__double2hiint(v), (unsigned)__double2hiint(v), false, false);
+  const bool up = threadIdx.x & 16;
+  return __hiloint2double((int)(up ? b[0] : b[1]), (int)(up ? a[0] : a[1]));
+}
+
+// Sum over the lanes of a 32-lane half that share lane % gl.
+__device__ __forceinline__ double half_sum(double v, int gl) {
+  if (gl <= 1) v += ror_row<1>(v);
+  if (gl <= 2) v += ror_row<2>(v);
+  if (gl <= 4) v += ror_row<4>(v);
+  if (gl <= 8) v += ror_row<8>(v);
+  if (gl <= 16) v += xor16d(v);
+  return v;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs A) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  const Shape& s = A.s;
+  const int br = blockIdx.x * kRegionsPerPoolBlock + (threadIdx.x >> 5);
+  if (br >= A.units) return;                 // no barrier follows
+  const int l32 = threadIdx.x & 31;
+  const int b = fdiv(br, A.f_R), r = br - b * s.R;
+  const int ry = fdiv(r, A.f_S), rx = r - ry * s.S;
+  const int G = s.C / VEC;                   // 16-byte groups per pixel
+  const int gl = A.gl, PL = 32 / gl;
+  const int pl = l32 / gl, gi = l32 - pl * gl;
+  const double inv_n = 1.0 / (double)s.n;
+  const uint4* __restrict__ q = A.q + (size_t)b * s.H * s.W * G;
+  const uint4* __restrict__ k = A.k + (size_t)b * s.H * s.W * G;
+  const int base = (ry * s.hs * s.W + rx * s.ws) * G;
+  for (int g0 = 0; g0 < G; g0 += gl) {
+    const int g = g0 + gi;
+    const bool gok = g < G;
+    double aq[VEC], ak[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) { aq[e] = 0.0; ak[e] = 0.0; }
+    for (int t0 = pl; t0 < s.n; t0 += kPoolBatch * PL) {
+      uint4 uq[kPoolBatch], uk[kPoolBatch];
+#pragma unroll
+      for (int u = 0; u < kPoolBatch; ++u) {
+        const int t = t0 + u * PL;
+        uq[u] = make_uint4(0, 0, 0, 0);
+        uk[u] = make_uint4(0, 0, 0, 0);
+        if (gok && t < s.n) {
+          const int ty = fdiv(t, A.f_ws), tx = t - ty * s.ws;
+          const int off = base + (ty * s.W + tx) * G + g;
+          uq[u] = q[off];
+          uk[u] = k[off];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kPoolBatch; ++u) {
+        float fq[VEC], fk[VEC];
+        unpack16<BF16>(uq[u], fq);
+        unpack16<BF16>(uk[u], fk);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) { aq[e] += (double)fq[e]; ak[e] += (double)fk[e]; }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      aq[e] = half_sum(aq[e], gl);
+      ak[e] = half_sum(ak[e], gl);
+    }
+    if (pl == 0 && gok) {
+      const size_t o = (size_t)br * s.C + (size_t)g * VEC;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        A.qm[o + e] = aq[e] * inv_n;
+        A.km[o + e] = ak[e] * inv_n;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Route: A[r][s] = route_scale * <q_r[r], k_r[s]> in float64, then per row
+// the topk largest entries, largest first, equal values by lower index (p1
+// §3 affinity and top-k; p2 §4 scaled affinity and top-k).
+//
+// One workgroup per (image, block of 16 rows).  The 16 x R affinity strip is
+// a small float64 GEMM on the matrix cores (v_mfma_f64_16x16x4, one 16 x 16
+// tile per wavefront at a time); each lane feeds 4 consecutive channels as
+// the K elements of 4 successive MFMAs, so one 32-byte load serves 4 steps.
+// The strip lives in LDS only; nothing of A is written to memory.  Ranking
+// then runs per row on one wavefront, either by counting (rank(s) = number
+// of entries ranking before s, each entry broadcast through a scalar
+// register; R <= 64) or by topk rounds of a wavefront arg-max (DPP row
+// rotations and row swaps, no LDS), whichever costs fewer steps; both rank
+// through an order-preserving int64 key (after turning -0 into +0, so that
+// 0 and -0 tie, as they compare equal) and give the same answer.
+// ---------------------------------------------------------------------------
+constexpr int kRouteRows = 16;
+constexpr int kRouteMaxJ = 16;    // R <= 1024 = 16 candidates per lane
+
+__device__ __forceinline__ long long order_key(double v) {
+  v = v + 0.0;                                   // -0 -> +0
+  const long long k = __double_as_longlong(v);
+  return k ^ ((k >> 63) & 0x7fffffffffffffffLL);
+}
+
+// true if (ka, ia) ranks before (kb, ib)
+__device__ __forceinline__ bool ranks_before(long long ka, int ia, long long kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// (key, index) of another lane, moved by a DPP row rotation or a row swap.
+template <int SH>
+__device__ __forceinline__ void ror_pair(long long& k, int& i) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)k, 0x120 | SH, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(k >> 32), 0x120 | SH, 0xf, 0xf, false);
+  const int ii = __builtin_amdgcn_update_dpp(0, i, 0x120 | SH, 0xf, 0xf, false);
+  k = ((long long)hi << 32) | (unsigned)lo;
+  i = ii;
+}
+
+// All lanes end with the (key, index) ranking first over the wavefront:
+// rotations inside each 16-lane row, then swaps between rows.
+__device__ __forceinline__ void wave_best(long long& bk, int& bi) {
+#define BRA_ROW_STEP(SH)                                  \
+  {                                                       \
+    long long ok = bk;                                    \
+    int oi = bi;                                          \
+    ror_pair<SH>(ok, oi);                                 \
+    if (ranks_before(ok, oi, bk, bi)) { bk = ok; bi = oi; } \
+  }
+  BRA_ROW_STEP(8)
+  BRA_ROW_STEP(4)
+  BRA_ROW_STEP(2)
+  BRA_ROW_STEP(1)
+#undef BRA_ROW_STEP
+  {
+    const bool up16 = threadIdx.x & 16, up32 = threadIdx.x & 32;
+    auto a = __builtin_amdgcn_permlane16_swap((unsigned)bk, (unsigned)bk, false, false);
+    auto h = __builtin_amdgcn_permlane16_swap((unsigned)(bk >> 32), (unsigned)(bk >> 32), false, false);
+    auto x = __builtin_amdgcn_permlane16_swap((unsigned)bi, (unsigned)bi, false, false);
+    long long ok = ((long long)(up16 ? h[0] : h[1]) << 32) | (up16 ? a[0] : a[1]);
+    int oi = (int)(up16 ? x[0] : x[1]);
+    if (ranks_before(ok, oi, bk, bi)) { bk = ok; bi = oi; }
+    a = __builtin_amdgcn_permlane32_swap((unsigned)bk, (unsigned)bk, false, false);
+    h = __builtin_amdgcn_permlane32_swap((unsigned)(bk >> 32), (unsigned)(bk >> 32), false, false);
+    x = __builtin_amdgcn_permlane32_swap((unsigned)bi, (unsigned)bi, false, false);
+    ok = ((long long)(up32 ? h[0] : h[1]) << 32) | (up32 ? a[0] : a[1]);
+    oi = (int)(up32 ? x[0] : x[1]);
+    if (ranks_before(ok, oi, bk, bi)) { bk = ok; bi = oi; }
+  }
+}
+
+struct RouteArgs {
+  const double* qm;
+  const double* km;
+  int32_t* idx;
+  float* logits;
+  Shape s;
+  double scale;
+  int use_select;
+  int lda;          // LDS row stride of the affinity strip (doubles)
+  int nrb;          // row blocks per image
+};
+
+__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs A) {
+  extern __shared__ double strip[];                // [kRouteRows][lda]
+  const Shape& s = A.s;
+  const int R = s.R, C = s.C, topk = s.topk;
+  const int b = blockIdx.x / A.nrb, r0 = (blockIdx.x - b * A.nrb) * kRouteRows;
+  const int rows = min(kRouteRows, R - r0);
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int l16 = lane & 15, lk = lane >> 4;
+
+  // affinity strip on the matrix cores
+  const double* __restrict__ qimg = A.qm + (size_t)b * R * C;
+  const double* __restrict__ kimg = A.km + (size_t)b * R * C;
+  const int arow = r0 + l16;
+  const int ntile = (R + 15) / 16;
+  for (int ct = wave; ct < ntile; ct += kWaves) {
+    const int bcol = ct * 16 + l16;
+    const double* qp = qimg + (size_t)min(arow, R - 1) * C + 4 * lk;
+    const double* kp = kimg + (size_t)min(bcol, R - 1) * C + 4 * lk;
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+    for (int c0 = 0; c0 < C; c0 += 64) {
+      // lane group lk supplies channels c + 4*lk .. c + 4*lk + 3 (c = c0 + 16*u)
+      // over 4 steps; all 8 loads of the chunk are issued before the MFMAs
+      double4 a4[4], b4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int cc = c0 + 16 * u;
+        a4[u] = make_double4(0.0, 0.0, 0.0, 0.0);
+        b4[u] = make_double4(0.0, 0.0, 0.0, 0.0);
+        if (cc + 4 * lk < C) {
+          a4[u] = *(const double4*)(qp + cc);
+          b4[u] = *(const double4*)(kp + cc);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].x, b4[u].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].y, b4[u].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].z, b4[u].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].w, b4[u].w, acc, 0, 0, 0);
+      }
+    }
+    // D layout (f64 16x16x4): lane holds column l16 of the tile, rows lk + 4*i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = lk + 4 * i, cc = ct * 16 + l16;
+      if (rr < rows && cc < R) strip[rr * A.lda + cc] = A.scale * acc[i];
+    }
+  }
+  __syncthreads();
+
+  for (int rl = wave; rl < rows; rl += kWaves) {
+    const double* ar = strip + rl * A.lda;
+    int32_t* irow = A.idx + ((size_t)b * R + r0 + rl) * topk;
+    float* lrow = A.logits ? A.logits + ((size_t)b * R + r0 + rl) * topk : nullptr;
+    if (!A.use_select) {
+      // R <= 64: one candidate per lane; rank = number of candidates ranking
+      // before it, each broadcast from its lane through a scalar register
+      const double v = lane < R ? ar[lane] : 0.0;
+      const long long kv = order_key(v);
+      int rank = 0;
+      for (int s2 = 0; s2 < R; ++s2) {
+        const long long k2 = ((long long)__builtin_amdgcn_readlane((int)(kv >> 32), s2) << 32) |
+                             (unsigned)__builtin_amdgcn_readlane((int)kv, s2);
+        rank += ranks_before(k2, s2, kv, lane) ? 1 : 0;
+      }
+      if (lane < R && rank < topk) {
+        irow[rank] = lane;
+        if (lrow) lrow[rank] = (float)v;
+      }
+    } else {
+      // topk rounds of a wavefront arg-max over the remaining candidates
+      long long keys[kRouteMaxJ];
+      const int J = (R + 63) / 64;
+#pragma unroll
+      for (int j = 0; j < kRouteMaxJ; ++j)
+        keys[j] = (j < J && lane + 64 * j < R) ? order_key(ar[lane + 64 * j]) : LLONG_MIN;
+      unsigned taken = 0;
+      for (int kk = 0; kk < topk; ++kk) {
+        long long bk = LLONG_MIN;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int j = 0; j < kRouteMaxJ; ++j) {
+          const int sc = lane + 64 * j;
+          if (j < J && sc < R && !((taken >> j) & 1u) && ranks_before(keys[j], sc, bk, bi)) {
+            bk = keys[j];
+            bi = sc;
+          }
+        }
+        wave_best(bk, bi);
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        if (lane == 0) {
+          irow[kk] = bi;
+          if (lrow) lrow[kk] = (float)ar[bi];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pool(const void* q, const void* k, double* qm, double* km, const Shape& s,
+                       bool bf16, hipStream_t st) {
+  PoolArgs a;
+  a.q = (const uint4*)q; a.k = (const uint4*)k; a.qm = qm; a.km = km; a.s = s;
+  const int G = s.C / (bf16 ? 8 : 4);
+  a.gl = 1;
+  while (a.gl * 2 <= G && a.gl * 2 <= 32) a.gl *= 2;
+  a.units = s.B * s.R;
+  a.f_ws = make_fastdiv(s.ws);
+  a.f_R = make_fastdiv(s.R);
+  a.f_S = make_fastdiv(s.S);
+  const dim3 grid((unsigned)((a.units + kRegionsPerPoolBlock - 1) / kRegionsPerPoolBlock));
+  if (bf16)
+    hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(pool_kernel<false>, grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_route(const double* qm, const double* km, const Shape& s, double route_scale,
+                        int32_t* idx, float* logits, hipStream_t st) {
+  RouteArgs a;
+  a.qm = qm; a.km = km; a.idx = idx; a.logits = logits; a.s = s; a.scale = route_scale;
+  a.nrb = (s.R + kRouteRows - 1) / kRouteRows;
+  a.lda = (s.R + 15) / 16 * 16 + 1;
+  // rank counting (one candidate per lane, R steps) needs R <= 64; otherwise,
+  // or when few rounds suffice, topk rounds of a wavefront arg-max
+  const int J = (s.R + 63) / 64;
+  a.use_select = (s.R > 64 || (long long)s.topk * (J + 12) < (long long)s.R) ? 1 : 0;
+  const size_t lds = (size_t)kRouteRows * a.lda * sizeof(double);
+  const hipError_t e = hipFuncSetAttribute((const void*)route_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(route_kernel, dim3((unsigned)(s.B * a.nrb)), dim3(kThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace bra
