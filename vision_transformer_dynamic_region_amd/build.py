@@ -15,12 +15,13 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbra.so")
-SOURCES = ["route_kernels.hip", "attend_kernels.hip", "bra_api.cpp"]
+SOURCES = ["route_kernels.hip", "attend_kernels.hip", "region_kernels.hip", "bra_api.cpp"]
 # per-file extra flags: the attention file assumes finite, non-NaN data (NaN
 # inputs give unspecified outputs) so that max/min need no NaN quieting, and
 # keeps MFMA accumulators in ordinary VGPRs next to the softmax arithmetic
 EXTRA_FLAGS = {
     "attend_kernels.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "region_kernels.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 ARCH = "gfx950"
 
@@ -41,9 +42,10 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     cc = hipcc()
-    objs = []
     tmpdir = os.path.join(HERE, "_build")
     os.makedirs(tmpdir, exist_ok=True)
+    objs, procs = [], []
+    # one compiler process per source, all at once (a handful of files)
     for src in SOURCES:
         obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
@@ -51,8 +53,11 @@ def build(verbose: bool = False) -> str:
                "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        procs.append((src, subprocess.Popen(cmd)))
         objs.append(obj)
+    failed = [src for src, p in procs if p.wait() != 0]
+    if failed:
+        raise RuntimeError(f"hipcc failed on {', '.join(failed)}")
     tmp = LIB + ".tmp"
     cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:

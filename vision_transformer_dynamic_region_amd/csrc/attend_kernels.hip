@@ -1093,6 +1093,11 @@ hipError_t attend_launch(const AttnArgs& a, int ks, int ty, int kstep, dim3 grid
 hipError_t launch_attend(const void* q, const void* k, const void* v, const int32_t* idx,
                          const Shape& s, bool bf16, float attn_scale, const float* w,
                          const float* bias, int ks, void* out, hipStream_t st) {
+  if (bf16 && w) {
+    // a region shape with its own kernel runs there
+    const hipError_t e = launch_attend_region(q, k, v, idx, s, attn_scale, w, bias, ks, out, st);
+    if (e != hipErrorNotSupported) return e;
+  }
   AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.idx = idx; a.out = out; a.w = w; a.bias = bias; a.s = s;
   a.scale_log2 = attn_scale * 1.4426950408889634f;

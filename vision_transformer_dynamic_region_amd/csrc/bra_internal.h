@@ -34,6 +34,15 @@ hipError_t launch_attend(const void* q, const void* k, const void* v,
                          float attn_scale, const float* w, const float* bias,
                          int ks, void* out, hipStream_t st);
 
+// The same for bf16 inputs of a region shape with a dedicated kernel (LePE
+// fused); hipErrorNotSupported for any other shape, before anything is
+// enqueued.
+hipError_t launch_attend_region(const void* q, const void* k, const void* v,
+                                const int32_t* idx, const Shape& s,
+                                float attn_scale, const float* w,
+                                const float* bias, int ks, void* out,
+                                hipStream_t st);
+
 // out += bias + depthwise ks x ks cross-correlation of v.
 hipError_t launch_lepe(const void* v, const float* w, const float* b, int ks,
                        const Shape& s, bool bf16, void* out, hipStream_t st);
