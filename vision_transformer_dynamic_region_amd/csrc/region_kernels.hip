@@ -96,7 +96,7 @@ struct Rc {
 
   static_assert(C % CB == 0 && CB % kHd == 0, "channel blocking");
   static_assert(kThreads % GB == 0, "a thread stages one fixed 16-byte vector of a pixel");
-  static_assert(KC % 32 == 0 && KC <= 64, "routed keys: a multiple of 32, one softmax step");
+  static_assert(KC % 32 == 0 && KC <= 256, "routed keys: a multiple of 32, one softmax step");
   static_assert(W16 || (kThreads % CP == 0 && ITEMS <= kThreads), "one LePE item per thread");
   static_assert(!W16 || (KS == 5 && CB % 16 == 0 && (XG == 4 || XG == 2) && ITEMS_W <= kThreads &&
                          kThreads % CB == 0),
@@ -598,6 +598,8 @@ hipError_t region_launch(RegionArgs a, hipStream_t st) {
 using St1 = Rc<64, BRA_CB_ST1, 8, 8, 1, 5, BRA_OCC_ST1>;
 using St2 = Rc<128, BRA_CB_ST2, 4, 4, 4, 5, BRA_OCC_ST2>;
 using St3 = Rc<256, 128, 2, 2, 16, 5, BRA_OCC_ST3>;
+// the 512^2 segmentation shape: 128^2 map, S = 16, top-k 4 (256 keys), d = 32
+using Dense = Rc<64, 32, 8, 8, 4, 5>;
 
 }  // namespace
 
@@ -629,6 +631,10 @@ hipError_t launch_attend_region(const void* q, const void* k, const void* v, con
   if (is(St3::C, St3::HS, St3::WS, St3::TOPK, St3::KS)) {
     a.units = s.B * s.R * St3::NCB;
     return region_launch<St3>(a, st);
+  }
+  if (is(Dense::C, Dense::HS, Dense::WS, Dense::TOPK, Dense::KS)) {
+    a.units = s.B * s.R * Dense::NCB;
+    return region_launch<Dense>(a, st);
   }
   return hipErrorNotSupported;
 }

@@ -126,6 +126,91 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs A) {
   }
 }
 
+// Bandwidth-first pooling for pixels of G <= 64 16-byte groups (G a power of
+// two): one wavefront per region, lane (p, g) = (lane / G, lane % G) owns
+// channel group g of pixels p, p + 64/G, ...; every load of a batch of up to
+// kWavePass passes (two tensors) is issued before the first add.  The float64
+// partial sums of the 64/G lanes sharing g are then added with row rotations
+// and row swaps, in a fixed order.
+constexpr int kWavePass = 8;
+
+template <int SH>
+__device__ __forceinline__ double ror_rowd(double v) { return ror_row<SH>(v); }
+
+__device__ __forceinline__ double xor32d(double v) {
+  const auto a = __builtin_amdgcn_permlane32_swap((unsigned)__double2loint(v), (unsigned)__double2loint(v), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap((unsigned)__double2hiint(v), (unsigned)__double2hiint(v), false, false);
+  const bool up = threadIdx.x & 32;
+  return __hiloint2double((int)(up ? b[0] : b[1]), (int)(up ? a[0] : a[1]));
+}
+
+// Sum over the lanes of the wavefront that share lane % G.
+template <int G>
+__device__ __forceinline__ double group_sum(double v) {
+  if constexpr (G <= 1) v += ror_row<1>(v);
+  if constexpr (G <= 2) v += ror_row<2>(v);
+  if constexpr (G <= 4) v += ror_row<4>(v);
+  if constexpr (G <= 8) v += ror_row<8>(v);
+  if constexpr (G <= 16) v += xor16d(v);
+  if constexpr (G <= 32) v += xor32d(v);
+  return v;
+}
+
+template <bool BF16, int G>
+__global__ __launch_bounds__(kThreads) void pool_wave_kernel(PoolArgs A) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int PP = 64 / G;                 // pixels per pass
+  const Shape& s = A.s;
+  const int br = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (br >= A.units) return;                 // no barrier follows
+  const int lane = threadIdx.x & 63, g = lane % G, p0 = lane / G;
+  const int b = fdiv(br, A.f_R), r = br - b * s.R;
+  const int ry = fdiv(r, A.f_S), rx = r - ry * s.S;
+  const uint4* __restrict__ q = A.q + (size_t)b * s.H * s.W * G;
+  const uint4* __restrict__ k = A.k + (size_t)b * s.H * s.W * G;
+  const int base = (ry * s.hs * s.W + rx * s.ws) * G + g;
+  double aq[VEC], ak[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) { aq[e] = 0.0; ak[e] = 0.0; }
+  for (int t0 = p0; t0 < s.n; t0 += kWavePass * PP) {
+    uint4 uq[kWavePass], uk[kWavePass];
+#pragma unroll
+    for (int u = 0; u < kWavePass; ++u) {
+      const int t = t0 + u * PP;
+      uq[u] = make_uint4(0, 0, 0, 0);
+      uk[u] = make_uint4(0, 0, 0, 0);
+      if (t < s.n) {
+        const int ty = fdiv(t, A.f_ws), tx = t - ty * s.ws;
+        const int off = base + (ty * s.W + tx) * G;
+        uq[u] = q[off];
+        uk[u] = k[off];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kWavePass; ++u) {
+      float fq[VEC], fk[VEC];
+      unpack16<BF16>(uq[u], fq);
+      unpack16<BF16>(uk[u], fk);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) { aq[e] += (double)fq[e]; ak[e] += (double)fk[e]; }
+    }
+  }
+  const double inv_n = 1.0 / (double)s.n;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    aq[e] = group_sum<G>(aq[e]);
+    ak[e] = group_sum<G>(ak[e]);
+  }
+  if (p0 == 0) {
+    const size_t o = (size_t)br * s.C + (size_t)g * VEC;
+#pragma unroll
+    for (int e = 0; e < VEC; e += 2) {
+      *(double2*)(A.qm + o + e) = make_double2(aq[e] * inv_n, aq[e + 1] * inv_n);
+      *(double2*)(A.km + o + e) = make_double2(ak[e] * inv_n, ak[e + 1] * inv_n);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Route: A[r][s] = route_scale * <q_r[r], k_r[s]> in float64, then per row
 // the topk largest entries, largest first, equal values by lower index (p1
@@ -310,6 +395,95 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs A) {
   }
 }
 
+// Route for R <= 64 regions (one candidate per lane).  One 16-wavefront
+// workgroup per (image, 16-row strip).  Wavefront w computes column tile
+// w % 4 of the strip over channel quarter w / 4 (v_mfma_f64_16x16x4f64, its
+// loads all issued before the first MFMA); the four partial strips of each
+// tile are added in LDS, in a fixed order.  Then wavefront w ranks strip row
+// w: for topk <= 2 by topk rounds of a wavefront arg-max, otherwise by
+// counting (each lane counts the candidates of its row that rank before its
+// own, keys broadcast from LDS, and the lanes of rank < topk write
+// themselves).  Sixteen wavefronts per CU hide the load and MFMA latency.
+constexpr int kSmallWaves = 16;
+constexpr int kSelectMaxK = 2;    // arg-max rounds up to this topk, rank counting above
+constexpr int kSmallMaxC4 = 4;     // double4 loads per operand and lane (C <= 256 per pass)
+
+__global__ __launch_bounds__(kSmallWaves * 64) void route_small_kernel(RouteArgs A) {
+  __shared__ double part[4][kRouteRows][64];
+  __shared__ long long keys[kRouteRows][64];
+  const Shape& s = A.s;
+  const int R = s.R, C = s.C, topk = s.topk;
+  const int b = blockIdx.x / A.nrb, r0 = (blockIdx.x - b * A.nrb) * kRouteRows;
+  const int rows = min(kRouteRows, R - r0);
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int l16 = lane & 15, lk = lane >> 4;
+  const int tile = wave & 3, quarter = wave >> 2;
+  const double* __restrict__ qimg = A.qm + (size_t)b * R * C;
+  const double* __restrict__ kimg = A.km + (size_t)b * R * C;
+  const int ntile = (R + 15) / 16;
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  if (tile < ntile) {
+    const double* qp = qimg + (size_t)min(r0 + l16, R - 1) * C + 4 * lk;
+    const double* kp = kimg + (size_t)min(16 * tile + l16, R - 1) * C + 4 * lk;
+    // channel groups of 16 of this quarter: c = 16 * (quarter + 4 * u)
+    for (int c0 = 16 * quarter; c0 < C; c0 += 64 * kSmallMaxC4) {
+      double4 a4[kSmallMaxC4], b4[kSmallMaxC4];
+#pragma unroll
+      for (int u = 0; u < kSmallMaxC4; ++u) {
+        const int c = c0 + 64 * u;
+        const bool ok = c + 4 * lk < C;
+        a4[u] = ok ? *(const double4*)(qp + c) : make_double4(0.0, 0.0, 0.0, 0.0);
+        b4[u] = ok ? *(const double4*)(kp + c) : make_double4(0.0, 0.0, 0.0, 0.0);
+      }
+#pragma unroll
+      for (int u = 0; u < kSmallMaxC4; ++u) {
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].x, b4[u].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].y, b4[u].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].z, b4[u].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].w, b4[u].w, acc, 0, 0, 0);
+      }
+    }
+    // D layout (f64 16x16x4): lane holds column l16 of the tile, rows lk + 4*i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[quarter][lk + 4 * i][16 * tile + l16] = acc[i];
+  }
+  __syncthreads();
+
+  const int rl = wave;
+  if (rl >= rows) return;                          // no barrier follows
+  const double v =
+      ((part[0][rl][lane] + part[1][rl][lane]) + (part[2][rl][lane] + part[3][rl][lane])) * A.scale;
+  const long long key = lane < R ? order_key(v) : LLONG_MIN;
+  if (topk <= kSelectMaxK) {
+    // topk rounds of a wavefront arg-max over the candidates not yet taken
+    bool taken = lane >= R;
+    for (int kk = 0; kk < topk; ++kk) {
+      long long bk = taken ? LLONG_MIN : key;
+      int bi = taken ? 0x7fffffff : lane;
+      wave_best(bk, bi);
+      if (lane == bi) {
+        taken = true;
+        const size_t o = ((size_t)b * R + r0 + rl) * topk + kk;
+        A.idx[o] = lane;
+        if (A.logits) A.logits[o] = (float)v;
+      }
+    }
+    return;
+  }
+  // rank of this candidate = number of candidates ranking before it; every
+  // lane reads each key of its row (one LDS broadcast per candidate)
+  keys[rl][lane] = key;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // the row's keys are visible
+  int rank = 0;
+#pragma unroll 8
+  for (int s2 = 0; s2 < R; ++s2) rank += ranks_before(keys[rl][s2], s2, key, lane) ? 1 : 0;
+  if (lane < R && rank < topk) {
+    const size_t o = ((size_t)b * R + r0 + rl) * topk + rank;
+    A.idx[o] = lane;
+    if (A.logits) A.logits[o] = (float)v;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_pool(const void* q, const void* k, double* qm, double* km, const Shape& s,
@@ -323,6 +497,20 @@ hipError_t launch_pool(const void* q, const void* k, double* qm, double* km, con
   a.f_ws = make_fastdiv(s.ws);
   a.f_R = make_fastdiv(s.R);
   a.f_S = make_fastdiv(s.S);
+  if (G <= 64 && (G & (G - 1)) == 0) {
+    const dim3 wgrid((unsigned)((a.units + kWaves - 1) / kWaves));
+#define BRA_POOL_G(GG)                                                                     \
+    if (G == GG) {                                                                         \
+      if (bf16)                                                                            \
+        hipLaunchKernelGGL((pool_wave_kernel<true, GG>), wgrid, dim3(kThreads), 0, st, a); \
+      else                                                                                 \
+        hipLaunchKernelGGL((pool_wave_kernel<false, GG>), wgrid, dim3(kThreads), 0, st, a);\
+      return hipGetLastError();                                                            \
+    }
+    BRA_POOL_G(1) BRA_POOL_G(2) BRA_POOL_G(4) BRA_POOL_G(8) BRA_POOL_G(16) BRA_POOL_G(32)
+    BRA_POOL_G(64)
+#undef BRA_POOL_G
+  }
   const dim3 grid((unsigned)((a.units + kRegionsPerPoolBlock - 1) / kRegionsPerPoolBlock));
   if (bf16)
     hipLaunchKernelGGL(pool_kernel<true>, grid, dim3(kThreads), 0, st, a);
@@ -337,6 +525,11 @@ hipError_t launch_route(const double* qm, const double* km, const Shape& s, doub
   a.qm = qm; a.km = km; a.idx = idx; a.logits = logits; a.s = s; a.scale = route_scale;
   a.nrb = (s.R + kRouteRows - 1) / kRouteRows;
   a.lda = (s.R + 15) / 16 * 16 + 1;
+  if (s.R <= 64) {
+    hipLaunchKernelGGL(route_small_kernel, dim3((unsigned)(s.B * a.nrb)), dim3(kSmallWaves * 64), 0,
+                       st, a);
+    return hipGetLastError();
+  }
   // rank counting (one candidate per lane, R steps) needs R <= 64; otherwise,
   // or when few rounds suffice, topk rounds of a wavefront arg-max
   const int J = (s.R + 63) / 64;
