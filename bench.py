@@ -31,12 +31,15 @@ METRIC = "BRA fwd tokens/s + attention TFLOP/s (% of MI355X bf16 MFMA peak), 1 G
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20         # Infinity Cache
+# sources of the attention kernels (the traffic record is void once they change)
 KERNEL_SOURCES = [
+    "vision_transformer_dynamic_region_amd/csrc/region_kernels.hip",
     "vision_transformer_dynamic_region_amd/csrc/attend_kernels.hip",
     "vision_transformer_dynamic_region_amd/csrc/device_common.h",
     "vision_transformer_dynamic_region_amd/csrc/fastdiv.h",
 ]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
+ATTEND_KERNELS = ("attend_region_kernel", "attend_stream_kernel", "attend_kernel")
 
 
 def log(msg: str) -> None:
@@ -64,7 +67,66 @@ def parse():
                    help="target CPU time of the oracle sample")
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="only run a plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                   help="rocprofv3 --pmc output folders (FETCH_SIZE / WRITE_SIZE of this bench, "
+                        "then of --copy-probe-mb 256); writes the attention kernel's HBM traffic "
+                        "record and exits (no GPU needed)")
     return p.parse_args()
+
+
+def _pmc_rows(folder: str):
+    """(kernel name, counter, value) of every dispatch in a rocprofv3 csv folder."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    with open(files[0]) as f:
+        return [(r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]))
+                for r in csv.DictReader(f)]
+
+
+def _mean(rows, counter, match):
+    vals = [v for k, c, v in rows if c == counter and match(k)]
+    if not vals:
+        raise SystemExit(f"no {counter} dispatch matched")
+    return sum(vals) / len(vals), len(vals)
+
+
+def write_traffic(a) -> int:
+    """HBM bytes per launch of the attention kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for a plain
+    device copy of 256 MiB (bytes moved / counter bytes)."""
+    fetch_dir, write_dir, cf_dir, cw_dir = a.traffic_from
+    is_attn = lambda k: any(n in k for n in ATTEND_KERNELS)
+    is_copy = lambda k: "copyBuffer" in k or "copy" in k.lower()
+    f_kib, nf = _mean(_pmc_rows(fetch_dir), "FETCH_SIZE", is_attn)
+    w_kib, nw = _mean(_pmc_rows(write_dir), "WRITE_SIZE", is_attn)
+    cf_kib, _ = _mean(_pmc_rows(cf_dir), "FETCH_SIZE", is_copy)
+    cw_kib, _ = _mean(_pmc_rows(cw_dir), "WRITE_SIZE", is_copy)
+    moved = 256 * 1024 * 1024
+    f_scale, w_scale = moved / (cf_kib * 1024), moved / (cw_kib * 1024)
+    rec = {
+        "workload": a.workload,
+        "kernel_sha": kernel_sha(),
+        "fetch_kib_per_launch": f_kib, "write_kib_per_launch": w_kib, "dispatches": [nf, nw],
+        "copy_fetch_kib": cf_kib, "copy_write_kib": cw_kib,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "bytes_per_launch": f_kib * 1024 * f_scale + w_kib * 1024 * w_scale,
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+    return 0
+
+
+def attend_kernel_name(wl) -> str:
+    """The attention kernel the library launches for this workload (the
+    specialised kernel for the bf16 BiFormer stage and dense shapes)."""
+    special = {("bf16", 64, 8, 1), ("bf16", 128, 4, 4), ("bf16", 256, 2, 16), ("bf16", 64, 8, 4)}
+    key = (wl.dtype, wl.C, wl.H // wl.S, wl.topk)
+    return "attend_region_kernel" if key in special and wl.lepe_ks == 5 else "attend_kernel"
 
 
 def copy_probe(mb: int) -> None:
@@ -94,20 +156,26 @@ def cpu_baseline(wl, x, target_s: float):
 
     t1, _ = run(1)
     nb = int(max(1, min(wl.B, target_s / max(t1, 1e-3))))
-    dt, cpu = run(nb)
-    tokens = nb * wl.H * wl.W
+    dt, cpu, reps = 0.0, 0.0, 0
+    while reps == 0 or (nb == wl.B and dt < target_s and reps < 20):
+        d, c = run(nb)       # the whole batch is cheap: repeat it up to the target time
+        dt, cpu, reps = dt + d, cpu + c, reps + 1
+    tokens = nb * wl.H * wl.W * reps
     return {
         "value": tokens / dt,
         "unit": "tokens/s",
         "cores": max(1, int(round(cpu / dt))),
         "kind": "oracle",
-        "sample": (f"{wl.name}: first {nb} of {wl.B} images ({tokens} tokens), full fp64 "
-                   f"pass in {dt:.1f} s; host has {len(os.sched_getaffinity(0))} usable cores"),
+        "sample": (f"{wl.name}: first {nb} of {wl.B} images x {reps} passes ({tokens} tokens), "
+                   f"full fp64 oracle in {dt:.1f} s; host has {len(os.sched_getaffinity(0))} "
+                   f"usable cores"),
     }
 
 
 def main() -> int:
     a = parse()
+    if a.traffic_from:
+        return write_traffic(a)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the BRA forward "
               "pass here is a single-GPU kernel path", file=sys.stderr)
@@ -168,24 +236,27 @@ def main() -> int:
     ms = start.elapsed_time(stop) / a.steps
     log(f"timed {a.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / a.steps:.4f} ms/step)")
 
-    # Per-kernel durations: the same kernels launched through the two
-    # single-stage entry points (bra_route: pooling + routing; bra_attend:
-    # gather-attention with the LePE term fused), with HIP events between
-    # them on the stream the kernels run on (torch's current stream, which
-    # the binding passes to the library).
+    # Per-stage durations: the same kernels launched through the two
+    # single-stage entry points, each stage as its own back-to-back loop over
+    # the rotating input sets (bra_route: pooling + routing; bra_attend:
+    # gather-attention with the LePE term fused), bracketed by HIP events on
+    # the stream the kernels run on (torch's current stream, which the binding
+    # passes to the library).
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    for i in range(a.steps):
-        b = bufs[i % sets]
-        ev[i][0].record(stream)
-        bra.route(b["q"], b["k"], wl.S, wl.topk, workspace=b["ws"])
-        ev[i][1].record(stream)
-        bra.attend(b["q"], b["k"], b["v"], b["idx"], wl.heads, wl.S, lepe_w=w, out=b["out"])
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    t_route = sum(e[0].elapsed_time(e[1]) for e in ev) / a.steps
-    t_attn = sum(e[1].elapsed_time(e[2]) for e in ev) / a.steps
+
+    def stage_ms(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(a.steps):
+            fn(bufs[i % sets])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / a.steps
+
+    t_route = stage_ms(lambda b: bra.route(b["q"], b["k"], wl.S, wl.topk, workspace=b["ws"]))
+    t_attn = stage_ms(lambda b: bra.attend(b["q"], b["k"], b["v"], b["idx"], wl.heads, wl.S,
+                                           lepe_w=w, out=b["out"]))
     log(f"per stage (ms): pool+route {t_route:.4f}  attend+lepe {t_attn:.4f}")
 
     tokens = wl.tokens
@@ -218,7 +289,7 @@ def main() -> int:
         "attention": {"tflops": attn_tflops, "frac_bf16_peak": attn_tflops / BF16_PEAK_TFLOPS,
                       "ms": t_attn},
         "stages_ms": {"pool_route": t_route, "attend_lepe": t_attn},
-        "roofline": {"kernel": "attend_kernel", "bound": "hbm", "achieved": attn_gbs,
+        "roofline": {"kernel": attend_kernel_name(wl), "bound": "hbm", "achieved": attn_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": attn_bytes},
         "kernel_sha": kernel_sha(),
