@@ -1,6 +1,6 @@
 // Fused gather-attention + LePE for bf16 inputs whose region shape is known at
-// compile time (the BiFormer stage shapes): one persistent, software-pipelined
-// kernel per shape.
+// compile time (the BiFormer stage shapes and the 512^2 segmentation shape):
+// one persistent, software-pipelined kernel per shape.
 //
 // Page keys: p1 = cybasar.com "CVPR2023: BiFormer中的双层路由注意力机制解析"
 // (§3: gather of the routed regions' tokens, softmax attention, LePE added to
@@ -9,25 +9,37 @@
 // abstract of BiFormer (token-to-token attention over the union of the routed
 // regions).
 //
-// What a workgroup does.  A unit is (image, query region, block of CB
-// channels = CB/32 heads).  The units of an XCD are dealt round-robin to that
-// XCD's workgroups, so at any moment one XCD works on neighbouring regions of
-// one image and its L2 serves their shared halo rows and routed regions.  Per
+// Work split.  A unit is (image, query region, block of CB channels = CB/32
+// heads) and has exactly four tasks (16-query block x head), one per
+// wavefront.  The units of an XCD are dealt round-robin to that XCD's
+// workgroups, so at any moment one XCD works on neighbouring regions of one
+// image and its L2 serves their shared halo rows and routed regions.  Per
 // unit:
-//   1. the unit's V halo (the region plus KS/2 pixels each side, zero
-//      outside the image) goes from registers to LDS as float32, the routed
-//      regions' K rows to LDS row-major (16-byte chunks XOR-swizzled by row),
-//      their V rows to LDS transposed [channel][key]; barrier;
-//   2. the global loads of the next unit (its query operands, routed K/V
-//      vectors and halo) are issued into registers;
-//   3. attention: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (one query per
-//      lane column), softmax in float32 with the scale folded into exp2,
-//      O^T = V^T P^T with P rounded to bf16;
-//   4. LePE: each thread convolves one channel pair over one column of TY
-//      rows from the float32 halo, with its 2 x KS x KS weights held in
-//      registers for the life of the workgroup; the float32 L tile goes to
+//   1. commit: the unit's V halo (region plus 2 pixels each side, zero
+//      outside the image; bf16 as loaded), the routed regions' K and V rows
+//      (row-major, 16-byte chunks XOR-swizzled by row) go from registers to
 //      LDS; barrier;
-//   5. out = O / l + L, rounded once to bf16, stored.
+//   2. the global loads of the next unit (query operands, routed K/V vectors,
+//      halo) are issued into registers;
+//   3. each wavefront, on its own task only:
+//      attention  S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (one query per lane
+//                 column), softmax numerators in float32 with the scale
+//                 folded into exp2, rounded to bf16; O^T = V^T P^T with the
+//                 V^T operands read straight from the row-major V tile by the
+//                 transposing LDS read; the row sums by one more MFMA against
+//                 a ones operand (so O is normalised by exactly the weights
+//                 it was built from);
+//      LePE       the wavefront's own 16 pixels x 32 channels: 5x5
+//                 cross-correlation on v_dot2_f32_bf16 (tap pairs along x,
+//                 weights rounded once to bf16, products exact, float32
+//                 accumulation), four halo pixels of a channel fetched per
+//                 transposing LDS read; the two are interleaved phase by
+//                 phase so the convolution fills the MFMA/softmax latency;
+//      epilogue   L through a wavefront-private LDS tile into the MFMA
+//                 layout, out = O / l + L rounded once to bf16, 16-byte
+//                 stores;
+//   4. with one staging buffer, a barrier before the next commit; with two
+//      (DB), none: the next unit stages into the other buffer.
 // Nothing but the output is written to memory: the gathered K/V exist only
 // in LDS.
 
@@ -38,38 +50,17 @@ namespace {
 
 constexpr int kHd = 32;    // head width
 
-// Rows per LePE item: the smallest divisor TY of HS such that the items
-// (channel pairs x columns x row blocks) fit one per thread.
-constexpr int pick_ty(int cw, int hs) {
-  for (int ty = 1; ty <= hs; ++ty)
-    if (hs % ty == 0 && cw * (hs / ty) <= kThreads) return ty;
-  return hs;
-}
-
-// OCC: workgroups per CU the layout is sized for.  With OCC >= 3 the L tile
-// reuses the K/V area (one more barrier per unit) and registers are capped
-// accordingly.
-#ifndef BRA_LEPE_BF16W
-#define BRA_LEPE_BF16W 1
-#endif
-
-// W16: LePE on v_dot2_f32_bf16 (weights rounded once to bf16, products exact,
-// float32 accumulation) from a bf16 halo; otherwise float32 FMAs from a
-// float32 halo.
-template <int C_, int CB_, int HS_, int WS_, int TOPK_, int KS_, int OCC_ = 2,
-          bool W16_ = BRA_LEPE_BF16W>
+template <int C_, int CB_, int HS_, int WS_, int TOPK_, int KS_, bool DB_, int OCC_ = 2>
 struct Rc {
   static constexpr int C = C_, CB = CB_, HS = HS_, WS = WS_, TOPK = TOPK_, KS = KS_;
-  static constexpr int OCC = OCC_;
-  static constexpr bool W16 = W16_;
-  static constexpr bool L_ALIAS = OCC_ >= 3;
+  static constexpr bool DB = DB_;                  // double-buffered staging
+  static constexpr int OCC = OCC_;                 // workgroups per CU to allow for
   static constexpr int NCB = C / CB;               // channel blocks per region
   static constexpr int n = HS * WS;                // queries per region
   static constexpr int KC = TOPK * n;              // routed keys, all in LDS at once
   static constexpr int NQB = (n + 15) / 16;        // 16-query blocks
   static constexpr int HB = CB / kHd;              // heads per unit
   static constexpr int TASKS = NQB * HB;
-  static constexpr int TPW = (TASKS + kWaves - 1) / kWaves;
   static constexpr int P = KS / 2;
   static constexpr int KK = KS * KS;
   static constexpr int HH = HS + KS - 1, HW = WS + KS - 1;
@@ -77,48 +68,38 @@ struct Rc {
   static constexpr int PSTEP = kThreads / GB;      // pixels per staging pass
   static constexpr int HPT = (HH * HW + PSTEP - 1) / PSTEP;
   static constexpr int KPT = (KC + PSTEP - 1) / PSTEP;
-  static constexpr int CP = CB / 2;                // LePE channel pairs
-  static constexpr int TY = pick_ty(CP * WS, HS);
-  static constexpr int ITEMS = CP * WS * (HS / TY);
-  static constexpr int LS = CB + 4;                // L row stride (floats)
-  // dot2 LePE items: one channel, XG columns (tap pairs along x), TYW rows
+  // LePE items of a wavefront: 32 channels x the block's pixels, two items
+  // per channel lane, each XG columns (tap pairs along x) by TYW rows
+  static constexpr int QR = (n < 16 ? n : 16) / WS;      // pixel rows of a query block
   static constexpr int XG = WS % 4 == 0 ? 4 : WS;
   static constexpr int NXG = WS / XG;
-  static constexpr int TYW = pick_ty(CB * NXG, HS);
-  static constexpr int ITEMS_W = CB * NXG * (HS / TYW);
-  static constexpr int HALO_BYTES = HH * HW * CB * (W16 ? 2 : 4);
-  static constexpr int K_OFF = HALO_BYTES > KK * CB * 4 ? HALO_BYTES : KK * CB * 4;
-  static constexpr int V_OFF = K_OFF + KC * CB * 2;
-  static constexpr int KV_END = V_OFF + KC * CB * 2;
-  static constexpr int L_OFF = L_ALIAS ? K_OFF : KV_END;
-  static constexpr int IT_OFF = L_ALIAS ? (KV_END > L_OFF + n * LS * 4 ? KV_END : L_OFF + n * LS * 4)
-                                        : L_OFF + n * LS * 4;
+  static constexpr int TYW = QR * NXG / 2;
+  static constexpr int LSW = kHd + 4;               // wavefront L tile row stride (floats)
+  // LDS: [halo | K | V] x (DB ? 2 : 1), wavefront L tiles, routing table
+  static constexpr int HALO = HH * HW * CB * 2;
+  static constexpr int KVB = KC * CB * 2;
+  static constexpr int BUF = (HALO + 2 * KVB + 15) / 16 * 16;
+  static constexpr int L_OFF = BUF * (DB ? 2 : 1);
+  static constexpr int IT_OFF = L_OFF + kWaves * 16 * LSW * 4;
 
   static_assert(C % CB == 0 && CB % kHd == 0, "channel blocking");
+  static_assert(TASKS == kWaves, "one task (16 queries x 1 head) per wavefront");
+  static_assert(n >= 16 ? 16 % WS == 0 : n % WS == 0, "query blocks are whole pixel rows");
   static_assert(kThreads % GB == 0, "a thread stages one fixed 16-byte vector of a pixel");
   static_assert(KC % 32 == 0 && KC <= 256, "routed keys: a multiple of 32, one softmax step");
-  static_assert(W16 || (kThreads % CP == 0 && ITEMS <= kThreads), "one LePE item per thread");
-  static_assert(!W16 || (KS == 5 && CB % 16 == 0 && (XG == 4 || XG == 2) && ITEMS_W <= kThreads &&
-                         kThreads % CB == 0),
-                "dot2 LePE: 5x5 taps, 16-channel lane rows, one item per thread");
+  static_assert(KS == 5 && (XG == 4 || XG == 2) && TYW >= 1 && (QR * NXG) % 2 == 0,
+                "dot2 LePE: 5x5 taps, two items per channel lane");
+  static_assert(KK * CB * 4 <= BUF, "weights are staged through the first buffer");
 };
 
-// K tile swizzle: chunk g (16 bytes) of key row kk sits at chunk g ^ kswz(kk),
-// so the 16 rows one operand load reads fall into 16 distinct bank groups.
+// K/V tile swizzle: chunk g (16 bytes) of key row kk sits at chunk
+// g ^ kswz(kk), so the 16 rows one operand load reads fall into 16 distinct
+// bank groups.  kswz(kk + 16m) == kswz(kk).
 template <int GB>
 __device__ __forceinline__ int kswz(int kk) {
   if constexpr (GB >= 16) return kk & 15;
   else if constexpr (GB == 8) return (kk >> 1) & 7;
   else return (kk >> 2) & 3;
-}
-
-// Float32 halo pixel layout: the 16-byte vector g of a pixel (channels
-// 8g..8g+7) is split so that channels 8g..8g+3 sit at floats 4g..4g+3 and
-// 8g+4..8g+7 at CB/2 + 4g..: the two 16-byte LDS writes of consecutive lanes
-// are then contiguous.  hpos gives a channel's float position.
-template <int CB>
-__device__ __forceinline__ int hpos(int c) {
-  return ((c & 4) ? CB / 2 : 0) + (c >> 3) * 4 + (c & 3);
 }
 
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane
@@ -179,15 +160,11 @@ __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off,
 template <class G>
 __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionArgs A) {
   constexpr int C = G::C, CB = G::CB, HS = G::HS, WS = G::WS, TOPK = G::TOPK;
-  constexpr int n = G::n, KC = G::KC, NQB = G::NQB, TASKS = G::TASKS, TPW = G::TPW;
+  constexpr int n = G::n, KC = G::KC, NQB = G::NQB, NCB = G::NCB;
   constexpr int P = G::P, KS = G::KS, KK = G::KK, HH = G::HH, HW = G::HW, GB = G::GB;
-  constexpr int PSTEP = G::PSTEP, HPT = G::HPT, KPT = G::KPT, CP = G::CP, TY = G::TY;
-  constexpr int LS = G::LS, NCB = G::NCB;
+  constexpr int PSTEP = G::PSTEP, HPT = G::HPT, KPT = G::KPT;
+  constexpr int XG = G::XG, NXG = G::NXG, TYW = G::TYW, LSW = G::LSW;
   extern __shared__ __align__(16) unsigned char lds[];
-  float* Hs = (float*)lds;
-  uint16_t* Ks = (uint16_t*)(lds + G::K_OFF);
-  uint16_t* Vs = (uint16_t*)(lds + G::V_OFF);
-  float* Ls = (float*)(lds + G::L_OFF);
   int* itab = (int*)(lds + G::IT_OFF);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -208,34 +185,36 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
     const int sy = fdiv(reg, A.f_S), sx = reg - sy * A.S;
     itab[e] = (sy * HS * A.W + sx * WS) * C;
   }
-  // this block's LePE weights, transposed to [tap][channel] in the halo area
-  // (consecutive threads write consecutive LDS words)
-  for (int e = tid; e < KK * CB; e += kThreads) {
-    const int t = e / CB, c = e - t * CB;
-    Hs[e] = A.w[(size_t)(cb0 + c) * KK + t];
+  // this block's LePE weights, transposed to [tap][channel] in the first
+  // buffer (consecutive threads write consecutive LDS words)
+  {
+    float* wst = (float*)lds;
+    for (int e = tid; e < KK * CB; e += kThreads) {
+      const int t = e / CB, c = e - t * CB;
+      wst[e] = A.w[(size_t)(cb0 + c) * KK + t];
+    }
   }
   __syncthreads();
 
-  // LePE item of this thread.
-  //  float32 path: channel pair cp, column xc, rows y0 .. y0+TY-1;
-  //  dot2 path: channel cw, columns xw .. xw+XG-1, rows yw .. yw+TYW-1.
-  constexpr int XG = G::XG, NXG = G::NXG, TYW = G::TYW;
-  const bool conv_on = G::W16 ? (G::ITEMS_W == kThreads || tid < G::ITEMS_W)
-                              : (G::ITEMS == kThreads || tid < G::ITEMS);
-  const int cp = tid % CP, xc = (tid / CP) % WS, y0 = (tid / (CP * WS)) * TY;
-  const int cw = tid % CB, xw = ((tid / CB) % NXG) * XG, yw = (tid / (CB * NXG)) * TYW;
-  float wr[G::W16 ? 1 : KK][2];
+  // this wavefront's task: query block qb of head hb
+  const int qb = wave % NQB, hb = wave / NQB;
+  const int qrow0 = qb * 16 / WS;                  // first pixel row of the block
+  // LePE items: channel cw (of the unit's block) of head hb, columns
+  // xw .. xw+XG-1, block rows yl .. yl+TYW-1
+  const int grp = lane >> 5;
+  const int cw = hb * kHd + (lane & 31);
+  const int xw = (grp % NXG) * XG, yl = (grp / NXG) * TYW;
   // dot2 weights per kernel row i: for an even output column the tap pairs
   // (w0,w1) (w2,w3) (w4,0) over input pairs (x,x+1) (x+2,x+3) (x+4,x+5); for
   // the odd column after it (0,w0) (w1,w2) (w3,w4) over the same pairs
-  uint32_t we[G::W16 ? KS : 1][3], wo[G::W16 ? KS : 1][3];
-  float b0 = 0.f, b1 = 0.f;
-  if constexpr (G::W16) {
+  uint32_t we[KS][3], wo[KS][3];
+  {
+    const float* wst = (const float*)lds;
 #pragma unroll
     for (int i = 0; i < KS; ++i) {
       float t[5];
 #pragma unroll
-      for (int jx = 0; jx < 5; ++jx) t[jx] = Hs[(i * KS + jx) * CB + cw];
+      for (int jx = 0; jx < 5; ++jx) t[jx] = wst[(i * KS + jx) * CB + cw];
       we[i][0] = pack_bf16x2(t[0], t[1]);
       we[i][1] = pack_bf16x2(t[2], t[3]);
       we[i][2] = pack_bf16x2(t[4], 0.f);
@@ -243,19 +222,8 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
       wo[i][1] = pack_bf16x2(t[1], t[2]);
       wo[i][2] = pack_bf16x2(t[3], t[4]);
     }
-    if (A.bias) b0 = A.bias[cb0 + cw];
-  } else {
-#pragma unroll
-    for (int t = 0; t < KK; ++t) {
-      const float2 u = *(const float2*)(Hs + t * CB + 2 * cp);
-      wr[t][0] = u.x;
-      wr[t][1] = u.y;
-    }
-    if (A.bias) {
-      b0 = A.bias[cb0 + 2 * cp];
-      b1 = A.bias[cb0 + 2 * cp + 1];
-    }
   }
+  const float b0 = A.bias ? A.bias[cb0 + cw] : 0.f;
 
   const int g = tid % GB, pk = tid / GB;           // staged vector: pixel pk + PSTEP*i, chunk g
   auto decode = [&](int j, int& b, int& ry, int& rx) {
@@ -267,7 +235,8 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
   };
 
   const uint32_t img_elems = (uint32_t)A.H * A.W * C;
-  uint4 qn[TPW], kn[KPT], vn[KPT], hn[G::HPT];
+  const int q = qb * 16 + lq;                      // this lane's query (column of the MFMAs)
+  uint4 qn, kn[KPT], vn[KPT], hn[HPT];
   auto prefetch = [&](int j) {
     int b, ry, rx;
     decode(j, b, ry, rx);
@@ -275,20 +244,18 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
     const auto Q = image_rsrc(A.q + img, img_elems * 2);
     const auto K = image_rsrc(A.k + img, img_elems * 2);
     const auto V = image_rsrc(A.v + img, img_elems * 2);
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int t = wave + kWaves * i;
-      const int qb = t % NQB, hb = t / NQB, q = qb * 16 + lq;
-      const bool ok = (TASKS % kWaves == 0 || t < TASKS) && q < n;
+    {
       const uint32_t off = ((ry * HS + q / WS) * A.W + rx * WS + q % WS) * C + cb0 + hb * kHd + 8 * lg;
-      qn[i] = bload16(Q, ok ? off * 2 : kOob);
+      qn = bload16(Q, q < n ? off * 2 : kOob);
     }
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int kk = pk + PSTEP * i;
+      const int kk = pk + PSTEP * i;               // pk < PSTEP
       const int tj = kk / n, tok = kk % n;
       const uint32_t off =
-          (PSTEP * (i + 1) <= KC || kk < KC) ? (itab[j * TOPK + tj] + ((tok / WS) * A.W + tok % WS) * C + cb0 + g * 8) * 2 : kOob;
+          (PSTEP * (i + 1) <= KC || kk < KC)
+              ? (itab[j * TOPK + tj] + ((tok / WS) * A.W + tok % WS) * C + cb0 + g * 8) * 2
+              : kOob;
       kn[i] = bload16(K, off);
       vn[i] = bload16(V, off);
     }
@@ -304,21 +271,15 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
     }
   };
 
-  bf16x8 qop[TPW];
-  auto commit = [&]() {
+  bf16x8 qop;
+  auto commit = [&](unsigned char* buf) {
+    uint16_t* Hs = (uint16_t*)buf;
+    uint16_t* Ks = (uint16_t*)(buf + G::HALO);
+    uint16_t* Vs = (uint16_t*)(buf + G::HALO + G::KVB);
 #pragma unroll
     for (int i = 0; i < HPT; ++i) {
-      const int pix = pk + PSTEP * i;                 // pk < PSTEP
-      if (PSTEP * (i + 1) <= HH * HW || pix < HH * HW) {
-        const uint4 u = hn[i];
-        if constexpr (G::W16) {
-          *(uint4*)((uint16_t*)Hs + pix * CB + g * 8) = u;
-        } else {
-          float* d = Hs + pix * CB + g * 4;
-          *(float4*)d = make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
-          *(float4*)(d + CB / 2) = make_float4(bf16_lo(u.z), bf16_hi(u.z), bf16_lo(u.w), bf16_hi(u.w));
-        }
-      }
+      const int pix = pk + PSTEP * i;
+      if (PSTEP * (i + 1) <= HH * HW || pix < HH * HW) *(uint4*)(Hs + pix * CB + g * 8) = hn[i];
     }
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -329,211 +290,143 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
         *(uint4*)(Vs + o) = vn[i];
       }
     }
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) qop[i] = __builtin_bit_cast(bf16x8, qn[i]);
+    qop = __builtin_bit_cast(bf16x8, qn);
   };
 
   const float c = A.scale_log2;
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u,
+                                                            0x3f803f80u, 0x3f803f80u));
+  float* Lw = (float*)(lds + G::L_OFF) + wave * 16 * LSW;   // this wavefront's L tile
   prefetch(0);
-  __syncthreads();                                  // weights read; the halo area is free
+  __syncthreads();                                  // weights read; the first buffer is free
 
   for (int j = 0; j < nu; ++j) {
-    commit();
+    unsigned char* buf = lds + (G::DB ? (j & 1) * G::BUF : 0);
+    commit(buf);
     __syncthreads();
     if (j + 1 < nu) prefetch(j + 1);
+    const uint16_t* Hs = (const uint16_t*)buf;
+    const uint16_t* Ks = (const uint16_t*)(buf + G::HALO);
+    const uint16_t* Vs = (const uint16_t*)(buf + G::HALO + G::KVB);
 
-    // ---- attention over the KC routed keys (one softmax step) and the
-    // LePE convolution, interleaved phase by phase: the convolution's
-    // independent FMAs fill the latency of the MFMA -> softmax -> MFMA chain.
-    // sched_barrier keeps the compiler from regrouping the phases.
-    f32x4 acc0[TPW], acc1[TPW];
-    float lsum[TPW];
-    float x[TPW][KC / 4];
-    uint32_t ph[TPW][KC / 8];                         // bf16 pairs of P, slot order
-
-    float la[TY][2];
+    // ---- LePE of this lane's items, in three slices of input rows ----
     float lw[TYW][XG];
-#pragma unroll
-    for (int r = 0; r < TY; ++r) {
-      la[r][0] = b0;
-      la[r][1] = b1;
-    }
 #pragma unroll
     for (int r = 0; r < TYW; ++r)
 #pragma unroll
       for (int k = 0; k < XG; ++k) lw[r][k] = b0;
-    const float* hp = Hs + (y0 * HW + xc) * CB + hpos<CB>(2 * cp);
-    // dot2 path: transposing reads of 4 consecutive halo pixels of one
-    // channel.  Lane i of a 16-lane row addresses pixel xw + i/4 (+4 for the
-    // second read), channels (cw & ~15) + 4(i % 4) .. +3, and receives
-    // channel cw of the four pixels: two bf16 pairs along x.
-    const uint16_t* trp = (const uint16_t*)Hs + (yw * HW + xw + ((tid & 15) >> 2)) * CB +
-                          (cw & ~15) + 4 * (tid & 3);
-    // LePE input rows dy0 .. dy1-1 of this thread's item
+    // transposing reads of 4 consecutive halo pixels of one channel: lane i
+    // of a 16-lane row addresses pixel xw + i/4 (+4 for the second read),
+    // channels (cw & ~15) + 4(i % 4) .. +3, and receives channel cw of the
+    // four pixels as two bf16 pairs along x
+    const uint16_t* trp = Hs + ((qrow0 + yl) * HW + xw + (lq >> 2)) * CB + (cw & ~15) + 4 * (lane & 3);
     auto conv_rows = [&](int dy0, int dy1) {
-      if (!conv_on) return;
-      if constexpr (G::W16) {
 #pragma unroll
-        for (int dy = 0; dy < TYW + KS - 1; ++dy) {
-          if (dy < dy0 || dy >= dy1) continue;
-          const uint2 a = lds_read_tr16(trp + (dy * HW) * CB);
-          const uint2 b = lds_read_tr16(trp + (dy * HW + 4) * CB);
-          const uint32_t p0 = a.x, p1 = a.y, p2 = b.x, p3 = b.y;   // pixel pairs
-#pragma unroll
-          for (int i = 0; i < KS; ++i) {
-            const int r = dy - i;
-            if (r < 0 || r >= TYW) continue;
-            lw[r][0] = dot2(we[i][2], p2, dot2(we[i][1], p1, dot2(we[i][0], p0, lw[r][0])));
-            lw[r][1] = dot2(wo[i][2], p2, dot2(wo[i][1], p1, dot2(wo[i][0], p0, lw[r][1])));
-            if constexpr (XG == 4) {
-              lw[r][2] = dot2(we[i][2], p3, dot2(we[i][1], p2, dot2(we[i][0], p1, lw[r][2])));
-              lw[r][3] = dot2(wo[i][2], p3, dot2(wo[i][1], p2, dot2(wo[i][0], p1, lw[r][3])));
-            }
-          }
-        }
-        return;
-      }
-#pragma unroll
-      for (int dy = 0; dy < TY + KS - 1; ++dy) {
+      for (int dy = 0; dy < TYW + KS - 1; ++dy) {
         if (dy < dy0 || dy >= dy1) continue;
-        float2 vv[KS];
-#pragma unroll
-        for (int jx = 0; jx < KS; ++jx) vv[jx] = *(const float2*)(hp + (dy * HW + jx) * CB);
+        const uint2 a = lds_read_tr16(trp + (dy * HW) * CB);
+        const uint2 b = lds_read_tr16(trp + (dy * HW + 4) * CB);
+        const uint32_t p0 = a.x, p1 = a.y, p2 = b.x, p3 = b.y;   // pixel pairs
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
           const int r = dy - i;
-          if (r < 0 || r >= TY) continue;
-#pragma unroll
-          for (int jx = 0; jx < KS; ++jx) {
-            la[r][0] = fmaf(wr[i * KS + jx][0], vv[jx].x, la[r][0]);
-            la[r][1] = fmaf(wr[i * KS + jx][1], vv[jx].y, la[r][1]);
+          if (r < 0 || r >= TYW) continue;
+          lw[r][0] = dot2(we[i][2], p2, dot2(we[i][1], p1, dot2(we[i][0], p0, lw[r][0])));
+          lw[r][1] = dot2(wo[i][2], p2, dot2(wo[i][1], p1, dot2(wo[i][0], p0, lw[r][1])));
+          if constexpr (XG == 4) {
+            lw[r][2] = dot2(we[i][2], p3, dot2(we[i][1], p2, dot2(we[i][0], p1, lw[r][2])));
+            lw[r][3] = dot2(wo[i][2], p3, dot2(wo[i][1], p2, dot2(wo[i][0], p1, lw[r][3])));
           }
         }
       }
     };
-    constexpr int NR = (G::W16 ? TYW : TY) + KS - 1;   // input rows of an item
+    constexpr int NR = TYW + KS - 1;                   // input rows of an item
 
-    // phase 1: S^T = K Q^T for every task
+    // ---- attention phase 1: S^T = K Q^T ----
+    float x[KC / 4];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      acc0[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc1[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      lsum[i] = 0.f;
-      const int t = wave + kWaves * i;
-      if (TASKS % kWaves != 0 && t >= TASKS) continue;   // uniform over the wave
-      const int hb = t / NQB;
+    for (int kb = 0; kb < KC / 16; ++kb) {
+      const int key = 16 * kb + lq;
+      const bf16x8 ka = *(const bf16x8*)(Ks + key * CB + (((hb * 4 + lg) ^ kswz<GB>(key)) * 8));
+      const f32x4 sv = mfma_bf16(ka, qop, f32x4{0.f, 0.f, 0.f, 0.f});
+      // lane holds keys 16*kb + 4*lg + e of query lq
 #pragma unroll
-      for (int kb = 0; kb < KC / 16; ++kb) {
-        const int key = 16 * kb + lq;
-        const bf16x8 ka =
-            *(const bf16x8*)(Ks + key * CB + (((hb * 4 + lg) ^ kswz<GB>(key)) * 8));
-        const f32x4 sv = mfma_bf16(ka, qop[i], f32x4{0.f, 0.f, 0.f, 0.f});
-        // lane holds keys 16*kb + 4*lg + e of query lq
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[i][4 * kb + e] = sv[e];
-      }
+      for (int e = 0; e < 4; ++e) x[4 * kb + e] = sv[e];
     }
     __builtin_amdgcn_sched_barrier(0);
     conv_rows(0, NR / 3);
     __builtin_amdgcn_sched_barrier(0);
 
-    // phase 2: softmax numerators, rounded to bf16 in P^T slot order
+    // ---- phase 2: softmax numerators, rounded to bf16 in P^T slot order ----
+    uint32_t ph[KC / 8];
+    {
+      float m = x[0];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int t = wave + kWaves * i;
-      if (TASKS % kWaves != 0 && t >= TASKS) continue;
-      float m = x[i][0];
-#pragma unroll
-      for (int e = 1; e < KC / 4; ++e) m = fmaxf(m, x[i][e]);
+      for (int e = 1; e < KC / 4; ++e) m = fmaxf(m, x[e]);
       m = fmaxf(m, xor16(m));
       m = fmaxf(m, xor32(m));
       const float mc = m * c;
-      float p[KC / 4];
 #pragma unroll
-      for (int e = 0; e < KC / 4; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(x[i][e], c, -mc));
-      float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < KC / 4; ++e) ps += p[e];
-      lsum[i] = ps;
-#pragma unroll
-      for (int e = 0; e < KC / 8; ++e) ph[i][e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+      for (int e = 0; e < KC / 8; ++e)
+        ph[e] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(x[2 * e], c, -mc)),
+                            __builtin_amdgcn_exp2f(fmaf(x[2 * e + 1], c, -mc)));
     }
     __builtin_amdgcn_sched_barrier(0);
     conv_rows(NR / 3, 2 * NR / 3);
     __builtin_amdgcn_sched_barrier(0);
 
-    // phase 3: O^T += V^T P^T.  V^T operands come straight from the
-    // row-major V tile by transposing reads: lane (lq, lg) addresses key
-    // 4lg + lq/4 (+16 for slots 4-7), channels d0 + 4(lq % 4) .. +3, and
-    // receives channel d0 + lq of keys 4lg + 0..3 -- the slot order of P^T
-    // (slots e: keys 32h + 4lg + e for e < 4, 32h + 16 + 4lg + e - 4 after).
-    const int vrow = 4 * lg + (lq >> 2);                   // key within a 16-key block
-    const int vsw = kswz<GB>(vrow);                        // same for vrow + 16m
-    const uint16_t* vbase = Vs + vrow * CB + 4 * (lq & 1);
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int t = wave + kWaves * i;
-      if (TASKS % kWaves != 0 && t >= TASKS) continue;
-      const int hb = t / NQB;
+    // ---- phase 3: O^T += V^T P^T, row sums += ones P^T ----
+    // V^T operands by transposing reads of the row-major V tile: lane (lq, lg)
+    // addresses key 4lg + lq/4 (+16 for slots 4-7), channels d0 + 4(lq % 4)
+    // .. +3, and receives channel d0 + lq of keys 4lg + 0..3 -- the slot order
+    // of P^T (slots e: keys 32h + 4lg + e for e < 4, 32h + 16 + 4lg + e - 4).
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
+    {
+      const int vrow = 4 * lg + (lq >> 2);             // key within a 16-key block
+      const int vsw = kswz<GB>(vrow);                  // same for vrow + 16m
+      const uint16_t* vbase = Vs + vrow * CB + 4 * (lq & 1);
       const int ca = ((hb * 4 + ((lq >> 1) & 1)) ^ vsw) * 8;       // d0 = 32hb
-      const int cb = ((hb * 4 + 2 + ((lq >> 1) & 1)) ^ vsw) * 8;   // d0 = 32hb + 16
+      const int cbo = ((hb * 4 + 2 + ((lq >> 1) & 1)) ^ vsw) * 8;  // d0 = 32hb + 16
 #pragma unroll
       for (int h = 0; h < KC / 32; ++h) {
         const uint16_t* r0 = vbase + (32 * h) * CB;
         const uint16_t* r1 = r0 + 16 * CB;
         const uint2 a0 = lds_read_tr16(r0 + ca), a1 = lds_read_tr16(r1 + ca);
-        const uint2 c0 = lds_read_tr16(r0 + cb), c1 = lds_read_tr16(r1 + cb);
+        const uint2 c0 = lds_read_tr16(r0 + cbo), c1 = lds_read_tr16(r1 + cbo);
         const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
         const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(c0.x, c0.y, c1.x, c1.y));
-        const bf16x8 phi = __builtin_bit_cast(
-            bf16x8, make_uint4(ph[i][4 * h], ph[i][4 * h + 1], ph[i][4 * h + 2], ph[i][4 * h + 3]));
-        acc0[i] = mfma_bf16(va, phi, acc0[i]);      // O^T rows d = 4lg + e
-        acc1[i] = mfma_bf16(vb, phi, acc1[i]);      // O^T rows d = 16 + 4lg + e
+        const bf16x8 phi =
+            __builtin_bit_cast(bf16x8, make_uint4(ph[4 * h], ph[4 * h + 1], ph[4 * h + 2], ph[4 * h + 3]));
+        acc0 = mfma_bf16(va, phi, acc0);               // O^T rows d = 4lg + e
+        acc1 = mfma_bf16(vb, phi, acc1);               // O^T rows d = 16 + 4lg + e
+        accl = mfma_bf16(ones, phi, accl);             // every row: sum over keys
       }
     }
     __builtin_amdgcn_sched_barrier(0);
     conv_rows(2 * NR / 3, NR);
 
-    // The L tile has its own area unless it reuses K/V (then every wave must
-    // be done with the attention first).  Either way the epilogue of the
-    // previous unit ended before this unit's first barrier.
-    if constexpr (G::L_ALIAS) __syncthreads();
-    if (conv_on) {
-      if constexpr (G::W16) {
+    // ---- L through the wavefront's tile into the MFMA layout ----
 #pragma unroll
-        for (int r = 0; r < TYW; ++r)
+    for (int r = 0; r < TYW; ++r)
 #pragma unroll
-          for (int k = 0; k < XG; ++k) Ls[((yw + r) * WS + xw + k) * LS + cw] = lw[r][k];
-      } else {
-#pragma unroll
-        for (int r = 0; r < TY; ++r)
-          *(float2*)(Ls + ((y0 + r) * WS + xc) * LS + 2 * cp) = make_float2(la[r][0], la[r][1]);
-      }
-    }
-    __syncthreads();   // L complete; halo and K/V free for the next unit
+      for (int k = 0; k < XG; ++k) Lw[((yl + r) * WS + xw + k) * LSW + (lane & 31)] = lw[r][k];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
-    // ---- out = O / l + L, one rounding ----
-    int b, ry, rx;
-    decode(j, b, ry, rx);
-    const auto O = image_rsrc(A.out + (size_t)b * img_elems, img_elems * 2);
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int t = wave + kWaves * i;
-      if (TASKS % kWaves != 0 && t >= TASKS) continue;
-      const int qb = t % NQB, hb = t / NQB, q = qb * 16 + lq;
-      float l = lsum[i];
-      l += xor16(l);
-      l += xor32(l);
-      const float inv = __builtin_amdgcn_rcpf(l);
-      const float* lp = Ls + (q < n ? q : 0) * LS + hb * kHd;   // rows >= n: not stored
+    // ---- out = O / l + L, one rounding, 16-byte stores ----
+    {
+      int b, ry, rx;
+      decode(j, b, ry, rx);
+      const auto O = image_rsrc(A.out + (size_t)b * img_elems, img_elems * 2);
+      const float inv = __builtin_amdgcn_rcpf(accl[0]);
+      const float* lp = Lw + (q < n ? lq : 0) * LSW;     // pixels past n: not stored
       const float4 a0 = *(const float4*)(lp + 4 * lg);
       const float4 a1 = *(const float4*)(lp + 16 + 4 * lg);
-      uint32_t o0x = pack_bf16x2(fmaf(acc0[i][0], inv, a0.x), fmaf(acc0[i][1], inv, a0.y));
-      uint32_t o0y = pack_bf16x2(fmaf(acc0[i][2], inv, a0.z), fmaf(acc0[i][3], inv, a0.w));
-      uint32_t o1x = pack_bf16x2(fmaf(acc1[i][0], inv, a1.x), fmaf(acc1[i][1], inv, a1.y));
-      uint32_t o1y = pack_bf16x2(fmaf(acc1[i][2], inv, a1.z), fmaf(acc1[i][3], inv, a1.w));
-      // Lane rows lg, lg^1 trade halves: even rows end up with channels
-      // 4lg..4lg+7, odd rows with 16+4(lg-1)..16+4lg+3 -- 16 contiguous bytes.
+      const uint32_t o0x = pack_bf16x2(fmaf(acc0[0], inv, a0.x), fmaf(acc0[1], inv, a0.y));
+      const uint32_t o0y = pack_bf16x2(fmaf(acc0[2], inv, a0.z), fmaf(acc0[3], inv, a0.w));
+      const uint32_t o1x = pack_bf16x2(fmaf(acc1[0], inv, a1.x), fmaf(acc1[1], inv, a1.y));
+      const uint32_t o1y = pack_bf16x2(fmaf(acc1[2], inv, a1.z), fmaf(acc1[3], inv, a1.w));
+      // lane rows lg, lg^1 trade halves: even rows end up with channels
+      // 4lg..4lg+7, odd rows with 16+4(lg-1)..16+4lg+3 -- 16 contiguous bytes
       const auto sx = __builtin_amdgcn_permlane16_swap(o0x, o1x, false, false);
       const auto sy = __builtin_amdgcn_permlane16_swap(o0y, o1y, false, false);
       const bool odd = lg & 1;
@@ -542,7 +435,7 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
       const uint32_t op = ((ry * HS + q / WS) * A.W + rx * WS + q % WS) * C + cb0 + hb * kHd + ch;
       bstore16(O, q < n ? op * 2 : kOob, ov);
     }
-    if constexpr (G::L_ALIAS) __syncthreads();   // L read before K/V are restaged
+    if constexpr (!G::DB) __syncthreads();         // the buffer is restaged next
   }
 }
 
@@ -578,28 +471,20 @@ hipError_t region_launch(RegionArgs a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// The shapes with a dedicated kernel: the BiFormer stage shapes at 224^2
-// (56^2 / 28^2 / 14^2 maps, S = 7, top-k 1 / 4 / 16, d = 32) with 5x5 LePE.
-#ifndef BRA_OCC_ST1
-#define BRA_OCC_ST1 2
+// The shapes with a dedicated kernel (d = 32, 5x5 LePE): the BiFormer stage
+// shapes at 224^2 (56^2 / 28^2 / 14^2 maps, S = 7, top-k 1 / 4 / 16) and the
+// 512^2 segmentation shape (128^2 map, S = 16, top-k 4).  Four tasks per
+// unit: one head for the 8x8 regions, four heads for the 4x4 and 2x2 ones.
+#ifndef BRA_DB_ST1
+#define BRA_DB_ST1 true
 #endif
-#ifndef BRA_CB_ST1
-#define BRA_CB_ST1 64
+#ifndef BRA_DB_DENSE
+#define BRA_DB_DENSE false
 #endif
-#ifndef BRA_CB_ST2
-#define BRA_CB_ST2 128
-#endif
-#ifndef BRA_OCC_ST2
-#define BRA_OCC_ST2 2
-#endif
-#ifndef BRA_OCC_ST3
-#define BRA_OCC_ST3 2
-#endif
-using St1 = Rc<64, BRA_CB_ST1, 8, 8, 1, 5, BRA_OCC_ST1>;
-using St2 = Rc<128, BRA_CB_ST2, 4, 4, 4, 5, BRA_OCC_ST2>;
-using St3 = Rc<256, 128, 2, 2, 16, 5, BRA_OCC_ST3>;
-// the 512^2 segmentation shape: 128^2 map, S = 16, top-k 4 (256 keys), d = 32
-using Dense = Rc<64, 32, 8, 8, 4, 5>;
+using St1 = Rc<64, 32, 8, 8, 1, 5, BRA_DB_ST1>;
+using St2 = Rc<128, 128, 4, 4, 4, 5, false>;
+using St3 = Rc<256, 128, 2, 2, 16, 5, false>;
+using Dense = Rc<64, 32, 8, 8, 4, 5, BRA_DB_DENSE>;
 
 }  // namespace
 

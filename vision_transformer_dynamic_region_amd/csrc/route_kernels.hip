@@ -132,7 +132,14 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs A) {
 // kWavePass passes (two tensors) is issued before the first add.  The float64
 // partial sums of the 64/G lanes sharing g are then added with row rotations
 // and row swaps, in a fixed order.
-constexpr int kWavePass = 8;
+#ifndef BRA_POOL_NPMAX
+#define BRA_POOL_NPMAX 4
+#endif
+#ifndef BRA_POOL_WAVES
+#define BRA_POOL_WAVES 4
+#endif
+constexpr int kPoolWaves = BRA_POOL_WAVES;      // wavefronts (regions) per workgroup
+constexpr int kWavePass = BRA_POOL_NPMAX;
 
 template <int SH>
 __device__ __forceinline__ double ror_rowd(double v) { return ror_row<SH>(v); }
@@ -156,12 +163,12 @@ __device__ __forceinline__ double group_sum(double v) {
   return v;
 }
 
-template <bool BF16, int G>
-__global__ __launch_bounds__(kThreads) void pool_wave_kernel(PoolArgs A) {
+template <bool BF16, int G, int NP>
+__global__ __launch_bounds__(kPoolWaves * 64) void pool_wave_kernel(PoolArgs A) {
   constexpr int VEC = BF16 ? 8 : 4;
   constexpr int PP = 64 / G;                 // pixels per pass
   const Shape& s = A.s;
-  const int br = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int br = blockIdx.x * kPoolWaves + (threadIdx.x >> 6);
   if (br >= A.units) return;                 // no barrier follows
   const int lane = threadIdx.x & 63, g = lane % G, p0 = lane / G;
   const int b = fdiv(br, A.f_R), r = br - b * s.R;
@@ -172,10 +179,10 @@ __global__ __launch_bounds__(kThreads) void pool_wave_kernel(PoolArgs A) {
   double aq[VEC], ak[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) { aq[e] = 0.0; ak[e] = 0.0; }
-  for (int t0 = p0; t0 < s.n; t0 += kWavePass * PP) {
-    uint4 uq[kWavePass], uk[kWavePass];
+  for (int t0 = p0; t0 < s.n; t0 += NP * PP) {
+    uint4 uq[NP], uk[NP];
 #pragma unroll
-    for (int u = 0; u < kWavePass; ++u) {
+    for (int u = 0; u < NP; ++u) {
       const int t = t0 + u * PP;
       uq[u] = make_uint4(0, 0, 0, 0);
       uk[u] = make_uint4(0, 0, 0, 0);
@@ -187,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void pool_wave_kernel(PoolArgs A) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < kWavePass; ++u) {
+    for (int u = 0; u < NP; ++u) {
       float fq[VEC], fk[VEC];
       unpack16<BF16>(uq[u], fq);
       unpack16<BF16>(uk[u], fk);
@@ -498,18 +505,23 @@ hipError_t launch_pool(const void* q, const void* k, double* qm, double* km, con
   a.f_R = make_fastdiv(s.R);
   a.f_S = make_fastdiv(s.S);
   if (G <= 64 && (G & (G - 1)) == 0) {
-    const dim3 wgrid((unsigned)((a.units + kWaves - 1) / kWaves));
-#define BRA_POOL_G(GG)                                                                     \
-    if (G == GG) {                                                                         \
-      if (bf16)                                                                            \
-        hipLaunchKernelGGL((pool_wave_kernel<true, GG>), wgrid, dim3(kThreads), 0, st, a); \
-      else                                                                                 \
-        hipLaunchKernelGGL((pool_wave_kernel<false, GG>), wgrid, dim3(kThreads), 0, st, a);\
-      return hipGetLastError();                                                            \
+    // passes per load batch: just enough for the region (at most kWavePass)
+    const int passes = (s.n + 64 / G - 1) / (64 / G);
+    const int np = passes >= kWavePass ? kWavePass : passes > 2 ? 4 : passes > 1 ? 2 : 1;
+    const dim3 wgrid((unsigned)((a.units + kPoolWaves - 1) / kPoolWaves));
+#define BRA_POOL_NP(GG, NN)                                                                   \
+    if (G == GG && np == NN) {                                                               \
+      if (bf16)                                                                              \
+        hipLaunchKernelGGL((pool_wave_kernel<true, GG, NN>), wgrid, dim3(kPoolWaves * 64), 0, st, a); \
+      else                                                                                   \
+        hipLaunchKernelGGL((pool_wave_kernel<false, GG, NN>), wgrid, dim3(kPoolWaves * 64), 0, st, a);\
+      return hipGetLastError();                                                              \
     }
+#define BRA_POOL_G(GG) BRA_POOL_NP(GG, 1) BRA_POOL_NP(GG, 2) BRA_POOL_NP(GG, 4) BRA_POOL_NP(GG, 8)
     BRA_POOL_G(1) BRA_POOL_G(2) BRA_POOL_G(4) BRA_POOL_G(8) BRA_POOL_G(16) BRA_POOL_G(32)
     BRA_POOL_G(64)
 #undef BRA_POOL_G
+#undef BRA_POOL_NP
   }
   const dim3 grid((unsigned)((a.units + kRegionsPerPoolBlock - 1) / kRegionsPerPoolBlock));
   if (bf16)
