@@ -1,8 +1,9 @@
 """Edge cases of the HIP path vs the fp64 oracle, through the C ABI:
 ragged regions and key tails, non-square regions, topk = 1 and S*S, S = 1,
 one pixel per region, many tasks per region, the largest region grid, wide
-channels, float32, LePE kernel sizes and bias, exact ties, identity routing,
-out-of-range indices, determinism and a non-default stream."""
+channels, float32, LePE kernel sizes and bias, the shapes with a dedicated
+kernel at small batch, exact ties, identity routing, out-of-range indices,
+determinism and a non-default stream."""
 
 from __future__ import annotations
 
@@ -30,6 +31,12 @@ EDGE = {
     "f32_all": (2, 16, 16, 128, 4, 4, 16, "f32", 7),
     "f32_wide_C512": (1, 8, 8, 512, 16, 2, 2, "f32", 1),
     "ks7_tall": (2, 24, 8, 96, 3, 4, 6, "bf16", 7),
+    # the shapes with a dedicated kernel, at small batch (workgroups left
+    # without units) and with a LePE bias
+    "st1_shape_B2": (2, 56, 56, 64, 2, 7, 1, "bf16", 5),
+    "st2_shape_B1": (1, 28, 28, 128, 4, 7, 4, "bf16", 5),
+    "st3_shape_B1": (1, 14, 14, 256, 8, 7, 16, "bf16", 5),
+    "dense_shape_B1": (1, 128, 128, 64, 2, 16, 4, "bf16", 5),
 }
 
 
@@ -108,10 +115,10 @@ def test_out_of_range_index_is_clamped(cuda):
     assert_close(to_host(out), ref, "f32", "clamped index")
 
 
-def test_deterministic_and_stream(cuda):
+@pytest.mark.parametrize("name", ["topk_all", "st1_shape_B2"])
+def test_deterministic_and_stream(cuda, name):
     import torch
     import vision_transformer_dynamic_region_amd as bra
-    name = "topk_all"
     wl, x, ref, out, idx, (q, k, v, w, bt) = run(cuda, name, *EDGE[name])
     B, H, W, C, heads, S, topk, dtype, ks = EDGE[name]
     for _ in range(3):
