@@ -122,11 +122,14 @@ def write_traffic(a) -> int:
 
 
 def attend_kernel_name(wl) -> str:
-    """The attention kernel the library launches for this workload (the
-    specialised kernel for the bf16 BiFormer stage and dense shapes)."""
+    """The attention kernel the library launches for this workload: the
+    specialised kernel for the bf16 BiFormer stage and dense shapes, else the
+    pipelined general kernel or, when its routed keys or LePE halo do not fit
+    that one, the chunked general kernel."""
     special = {("bf16", 64, 8, 1), ("bf16", 128, 4, 4), ("bf16", 256, 2, 16), ("bf16", 64, 8, 4)}
     key = (wl.dtype, wl.C, wl.H // wl.S, wl.topk)
-    return "attend_region_kernel" if key in special and wl.lepe_ks == 5 else "attend_kernel"
+    return "attend_region_kernel" if key in special and wl.lepe_ks == 5 \
+        else "attend_stream_kernel|attend_kernel"
 
 
 def copy_probe(mb: int) -> None:
