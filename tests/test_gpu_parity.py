@@ -87,3 +87,25 @@ def test_route_alone(cuda, name):
     q, k = (to_dev(x[n], wl.dtype) for n in ("q", "k"))
     idx = bra.route(q, k, wl.S, wl.topk).cpu().numpy()
     check_idx(idx, ref["idx"], ref["A"])
+
+
+@pytest.mark.parametrize("name", ["st1", "st2", "st3", "dense"])
+def test_repeated_launches(cuda, name):
+    """Many launches in a row of the persistent attention kernel on the same
+    inputs: every launch writes every output element, bit for bit as the
+    first, which matches the oracle."""
+    import torch
+    import vision_transformer_dynamic_region_amd as bra
+    wl, x, ref = case(name)
+    print(f"[parity] repeated launches {name}", flush=True)
+    q, k, v = (to_dev(x[n], wl.dtype) for n in ("q", "k", "v"))
+    idx = torch.from_numpy(ref["idx"]).to(cuda)
+    w = torch.from_numpy(x["w"]).to(cuda)
+    first = bra.attend(q, k, v, idx, wl.heads, wl.S, lepe_w=w)
+    outs = [torch.full_like(first, float("nan")) for _ in range(40)]
+    for o in outs:
+        bra.attend(q, k, v, idx, wl.heads, wl.S, lepe_w=w, out=o)
+    torch.cuda.synchronize()
+    assert_close(to_host(first), ref["out"], wl.dtype, f"{name} first launch")
+    for i, o in enumerate(outs):
+        assert torch.equal(o.view(torch.int16), first.view(torch.int16)), f"launch {i + 1}"
