@@ -7,6 +7,8 @@ leg may import it.  It shares no code with the HIP library.
 from .bra_oracle import (  # noqa: F401
     bra_forward,
     lepe,
+    linear,
+    module_forward,
     region_affinity,
     region_mean,
     region_shape,

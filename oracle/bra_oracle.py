@@ -54,6 +54,19 @@ its reason in the design notes of the repository):
       routing.
   R11 Output of the method is (out, idx); no Q/K/V or output projection.
 
+Readings for the module around the method (``module_forward``):
+
+  M1  Q, K and V are per-token linear maps of the input x (p1 §3 q_proj,
+      k_proj, v_proj) in the PyTorch Linear convention y = x W^T + b.  The
+      three weights are stacked into one [3C, C] matrix (rows 0..C-1 give Q,
+      then K, then V) with an optional [3C] bias; p2 §2 slices its keys out
+      of one projected tensor, which is the same thing.  A per-token map
+      commutes with the partition, so it is applied before it.
+  M2  The pages show no output projection.  The module takes an optional
+      [C, C] output Linear (with optional bias) applied to out = O + L;
+      without it the module returns O + L.
+  M3  LePE is taken on the projected V (p1 §3 adds lce(v) to the output).
+
 Parity pins for every function live in ``tests/test_oracle_pins.py``.
 """
 
@@ -71,6 +84,8 @@ __all__ = [
     "routed_attention",
     "lepe",
     "bra_forward",
+    "linear",
+    "module_forward",
 ]
 
 
@@ -245,3 +260,48 @@ def bra_forward(Q, K, V, heads: int, S: int, topk: int, w=None, bias=None,
         return {"out": out, "idx": idx, "q_r": q_r, "k_r": k_r, "A": A,
                 "O": O, "L": L}
     return out, idx
+
+
+def linear(X, w, b=None) -> np.ndarray:
+    """Per-token linear map in the PyTorch Linear convention (p1 §3 q_proj /
+    k_proj / v_proj; readings M1, M2).
+
+    X: [..., K]; w: [N, K]; b: [N] or None.  Returns X w^T + b, [..., N].
+    """
+    X = _f64(X)
+    w = _f64(w)
+    if w.ndim != 2 or w.shape[1] != X.shape[-1]:
+        raise ValueError("w must be [N, K] with K the last axis of X")
+    Y = np.matmul(X, w.T)
+    if b is not None:
+        Y = Y + _f64(b)
+    return Y
+
+
+def module_forward(x, w_qkv, b_qkv, heads: int, S: int, topk: int, lepe_w=None,
+                   lepe_b=None, w_out=None, b_out=None, route_scale: float | None = None,
+                   attn_scale: float | None = None, return_parts: bool = False):
+    """BRA as a module (p1 §3): Q, K, V = projections of x (M1), the BRA
+    forward pass on them with LePE on the projected V (M3), then the optional
+    output projection (M2).
+
+    x: [B, H, W, C]; w_qkv: [3C, C]; b_qkv: [3C] or None; w_out: [C, C] or
+    None; b_out: [C] or None.  Returns (out, idx) or, with return_parts, a
+    dict with every intermediate (those of bra_forward under their names, plus
+    q, k, v, y = O + L and out).
+    """
+    x = _f64(x)
+    C = x.shape[-1]
+    if np.shape(w_qkv) != (3 * C, C):
+        raise ValueError("w_qkv must be [3C, C]")
+    qkv = linear(x, w_qkv, b_qkv)
+    q, k, v = qkv[..., :C], qkv[..., C:2 * C], qkv[..., 2 * C:]
+    parts = bra_forward(q, k, v, heads, S, topk, lepe_w, lepe_b, route_scale, attn_scale,
+                        return_parts=True)
+    y = parts["out"]
+    out = linear(y, w_out, b_out) if w_out is not None else y
+    if return_parts:
+        parts = dict(parts)
+        parts.update({"q": q, "k": k, "v": v, "y": y, "out": out})
+        return parts
+    return out, parts["idx"]

@@ -114,7 +114,7 @@ def _rand(seed, B, H, W, C):
 
 def pin_golden():
     """Hand-worked fixtures under tests/golden/."""
-    files = sorted(glob.glob(os.path.join(GOLDEN, "*.json")))
+    files = sorted(glob.glob(os.path.join(GOLDEN, "hand_*.json")))
     assert files, "no golden fixtures"
     for f in files:
         g = json.load(open(f))
@@ -346,9 +346,83 @@ def pin_route_ties():
     assert list(idx[0, 1]) == [0, 1, 2, 3]
 
 
+# --------------------------------------------------------------------------
+# the module around the method (readings M1-M3)
+
+def _module_golden_args(g):
+    C, ks = g["C"], g["lepe_ks"]
+    w = np.zeros((C, ks, ks))
+    for c, i, j, val in g["lepe_taps"]:
+        w[c, i, j] = val
+    a = lambda n: None if g[n] is None else np.array(g[n], dtype=np.float64)
+    return (a("x"), a("w_qkv"), a("b_qkv"), g["heads"], g["S"], g["topk"], w, a("lepe_bias"),
+            a("w_out"), a("b_out"))
+
+
+def pin_module_golden():
+    """Hand-worked module fixtures (tests/golden/module_*.json)."""
+    files = sorted(glob.glob(os.path.join(GOLDEN, "module_*.json")))
+    assert files, "no module fixtures"
+    for f in files:
+        g = json.load(open(f))
+        parts = O.module_forward(*_module_golden_args(g), return_parts=True)
+        name = os.path.basename(f)
+        assert np.array_equal(parts["idx"], np.array(g["expect_idx"])), f"{name}: idx"
+        _close(parts["y"], g["expect_y"], 1e-14, f"{name}: y")
+        _close(parts["out"], g["expect_out"], 1e-14, f"{name}: out")
+
+
+def pin_linear_torch():
+    """The projection equals torch.nn.functional.linear in float64 (the
+    PyTorch Linear of p1 §3's q_proj / k_proj / v_proj), with and without
+    bias, on non-square and square weights."""
+    import torch
+    import torch.nn.functional as F
+    X = _rng(21).normal(size=(2, 3, 5, 7))
+    for N in (7, 12):
+        w = _rng(22 + N).normal(size=(N, 7))
+        b = _rng(23).normal(size=N)
+        for bias in (None, b):
+            ref = F.linear(torch.from_numpy(X), torch.from_numpy(w),
+                           None if bias is None else torch.from_numpy(bias)).numpy()
+            _close(O.linear(X, w, bias), ref, 1e-13, f"linear N={N} bias={bias is not None}")
+
+
+def pin_module_reduces_to_bra():
+    """With w_qkv = [I; I; I], no biases and no output projection the module
+    is bra_forward(x, x, x); with w_out = I and no output bias it returns
+    y = O + L unchanged (readings M1, M2)."""
+    B, H, W, C, heads, S, topk = 1, 8, 8, 6, 2, 4, 3
+    x = _rng(24).normal(size=(B, H, W, C))
+    lw = _rng(25).normal(size=(C, 3, 3))
+    eye3 = np.concatenate([np.eye(C)] * 3)
+    out, idx = O.module_forward(x, eye3, None, heads, S, topk, lw)
+    ref, ref_idx = O.bra_forward(x, x, x, heads, S, topk, lw)
+    assert np.array_equal(idx, ref_idx)
+    _close(out, ref, TIGHT, "identity projections")
+    w = _rng(26).normal(size=(3 * C, C))
+    b = _rng(27).normal(size=3 * C)
+    p = O.module_forward(x, w, b, heads, S, topk, lw, w_out=np.eye(C), return_parts=True)
+    _close(p["out"], p["y"], TIGHT, "identity output projection")
+
+
+def pin_pool_commutes_with_projection():
+    """Region means of a projection are the projection of the region means
+    (the map is linear and the mean weights sum to one), so routing can be
+    taken from the projected means of x: the two orders agree in float64."""
+    B, H, W, C, S = 2, 12, 8, 5, 4
+    x = _rng(28).normal(size=(B, H, W, C))
+    w = _rng(29).normal(size=(3, C))
+    b = _rng(30).normal(size=3)
+    _close(O.region_mean(O.linear(x, w, b), S), O.linear(O.region_mean(x, S), w, b), 1e-13,
+           "mean/projection order")
+
+
 ALL_PINS = [
     pin_golden, pin_partition_layout, pin_pool_avgpool, pin_affinity_orientation,
     pin_topk_bruteforce, pin_scale_invariance, pin_masked_dense,
     pin_global_when_all_routed, pin_plain_when_one_region, pin_window_when_identity,
     pin_sdpa_masked, pin_lepe_conv2d, pin_invariants, pin_route_ties,
+    pin_module_golden, pin_linear_torch, pin_module_reduces_to_bra,
+    pin_pool_commutes_with_projection,
 ]

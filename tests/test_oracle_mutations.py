@@ -10,7 +10,7 @@ from oracle_pins import ALL_PINS
 
 _orig = {name: getattr(O, name) for name in
          ("region_mean", "region_affinity", "topk_route", "routed_attention", "lepe",
-          "region_tokens")}
+          "region_tokens", "linear", "module_forward")}
 
 
 def _mean_as_sum(X, S):
@@ -111,6 +111,61 @@ def _tokens_column_major(H, W, S, r):
     return ry * hs + t % hs, rx * ws + t // hs
 
 
+def _linear_transposed(X, w, b=None):
+    w = np.asarray(w)
+    return _orig["linear"](X, w.T if w.shape[0] == w.shape[1] else w, b)
+
+
+def _linear_no_bias(X, w, b=None):
+    return _orig["linear"](X, w, None)
+
+
+def _linear_bias_subtracted(X, w, b=None):
+    return _orig["linear"](X, w, None if b is None else -np.asarray(b))
+
+
+def _module_qk_swapped(x, w_qkv, b_qkv, *a, **k):
+    C = np.shape(x)[-1]
+    w = np.asarray(w_qkv)
+    w = np.concatenate([w[C:2 * C], w[:C], w[2 * C:]])
+    b = None if b_qkv is None else np.concatenate(
+        [np.asarray(b_qkv)[C:2 * C], np.asarray(b_qkv)[:C], np.asarray(b_qkv)[2 * C:]])
+    return _orig["module_forward"](x, w, b, *a, **k)
+
+
+def _module_lepe_on_x(x, w_qkv, b_qkv, heads, S, topk, lepe_w=None, lepe_b=None, w_out=None,
+                      b_out=None, route_scale=None, attn_scale=None, return_parts=False):
+    x = np.asarray(x, dtype=np.float64)
+    C = x.shape[-1]
+    qkv = O.linear(x, w_qkv, b_qkv)
+    q, k, v = qkv[..., :C], qkv[..., C:2 * C], qkv[..., 2 * C:]
+    p = O.bra_forward(q, k, v, heads, S, topk, None, None, route_scale, attn_scale,
+                      return_parts=True)
+    y = p["O"] + (O.lepe(x, lepe_w, lepe_b) if lepe_w is not None else 0.0)
+    out = O.linear(y, w_out, b_out) if w_out is not None else y
+    if return_parts:
+        return dict(p, q=q, k=k, v=v, y=y, out=out)
+    return out, p["idx"]
+
+
+def _module_out_before_lepe(x, w_qkv, b_qkv, heads, S, topk, lepe_w=None, lepe_b=None,
+                            w_out=None, b_out=None, route_scale=None, attn_scale=None,
+                            return_parts=False):
+    x = np.asarray(x, dtype=np.float64)
+    C = x.shape[-1]
+    qkv = O.linear(x, w_qkv, b_qkv)
+    q, k, v = qkv[..., :C], qkv[..., C:2 * C], qkv[..., 2 * C:]
+    p = O.bra_forward(q, k, v, heads, S, topk, None, None, route_scale, attn_scale,
+                      return_parts=True)
+    o = O.linear(p["O"], w_out, b_out) if w_out is not None else p["O"]
+    L = O.lepe(v, lepe_w, lepe_b) if lepe_w is not None else 0.0
+    y = p["O"] + L
+    out = o + L
+    if return_parts:
+        return dict(p, q=q, k=k, v=v, y=y, out=out)
+    return out, p["idx"]
+
+
 MUTANTS = {
     "region_mean": [_mean_as_sum, _mean_column_major],
     "region_affinity": [_affinity_transposed],
@@ -119,6 +174,8 @@ MUTANTS = {
                          _attn_softmax_over_queries],
     "lepe": [_lepe_flipped, _lepe_transposed, _lepe_no_bias, _lepe_circular],
     "region_tokens": [_tokens_column_major],
+    "linear": [_linear_transposed, _linear_no_bias, _linear_bias_subtracted],
+    "module_forward": [_module_qk_swapped, _module_lepe_on_x, _module_out_before_lepe],
 }
 CASES = [(name, m) for name, ms in MUTANTS.items() for m in ms]
 

@@ -4,7 +4,8 @@ import numpy as np
 import torch
 
 from vision_transformer_dynamic_region_amd.workloads import (WORKLOADS, bf16_bits,
-                                                              bf16_round, make_inputs)
+                                                              bf16_round, make_inputs,
+                                                              make_module_inputs)
 
 
 def test_bf16_rounding_matches_torch():
@@ -49,3 +50,18 @@ def test_dense_has_region_offsets():
     means = x["k"].reshape(1, wl.S, hs, wl.S, hs, wl.C).mean(axis=(2, 4))
     # region means carry the N(0, 0.5) offset on top of N(0, 1/64) noise
     assert 0.4 < float(means.std()) < 0.6
+
+
+def test_module_inputs_seeded_and_rounded():
+    wl = WORKLOADS["st2"].scaled(B=2)
+    a, b = make_module_inputs(wl), make_module_inputs(wl)
+    for n in ("x", "w_qkv", "b_qkv", "w_out", "b_out", "w"):
+        assert np.array_equal(a[n], b[n]) and a[n].dtype == np.float32
+    C = wl.C
+    assert a["x"].shape == (2, 28, 28, C)
+    assert a["w_qkv"].shape == (3 * C, C) and a["w_out"].shape == (C, C)
+    assert a["b_qkv"].shape == (3 * C,) and a["b_out"].shape == (C,)
+    for n in ("x", "w_qkv", "w_out"):
+        assert np.array_equal(a[n], bf16_round(a[n]))
+    # projections keep unit scale: w ~ N(0, C^-1/2)
+    assert abs(float(a["w_qkv"].std()) * C ** 0.5 - 1.0) < 0.05

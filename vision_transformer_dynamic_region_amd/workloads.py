@@ -16,6 +16,13 @@ classification and the stride-4 map of 512x512 segmentation):
 * For bf16 workloads the float32 values are rounded to bfloat16 with
   round-to-nearest-even; the rounded values (exact in float32 and float64)
   are what both sides receive.
+
+The module around the method (projections of an input x) draws, with the
+same seed base: x ~ N(0, 1) (seed + 7; the dense shape adds its per-region
+offset, seed + 12), w_qkv ~ N(0, C**-0.5) [3C, C] (seed + 8), b_qkv ~ N(0, 0.1)
+[3C] (seed + 9), w_out ~ N(0, C**-0.5) [C, C] (seed + 10), b_out ~ N(0, 0.1)
+[C] (seed + 11) and the LePE weights as above.  x and the two weights are
+rounded to bf16 for bf16 workloads; biases stay float32.
 """
 
 from __future__ import annotations
@@ -25,7 +32,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "bf16_round", "bf16_bits", "make_inputs",
-           "workload"]
+           "make_module_inputs", "workload"]
 
 
 @dataclass(frozen=True)
@@ -140,4 +147,32 @@ def make_inputs(wl: Workload, seed_base: int | None = None, with_weights: bool =
     else:
         out["w"] = None
     out["bias"] = None
+    return out
+
+
+def make_module_inputs(wl: Workload, seed_base: int | None = None):
+    """Draw the module's input x and its weights for a workload.
+
+    Returns a dict: ``x`` [B, H, W, C], ``w_qkv`` [3C, C], ``w_out`` [C, C]
+    (bf16-rounded for bf16 workloads), ``b_qkv`` [3C], ``b_out`` [C] float32,
+    ``w`` [C, ks, ks] float32 LePE weights and ``bias`` (None).
+    """
+    base = 1000 * wl.index if seed_base is None else seed_base
+    C = wl.C
+    x = _normal(base + 7, (wl.B, wl.H, wl.W, C))
+    if wl.region_offset_std > 0.0:
+        hs, ws = wl.H // wl.S, wl.W // wl.S
+        mu = _normal(base + 12, (wl.B, wl.S, wl.S, C), wl.region_offset_std)
+        x = x + np.repeat(np.repeat(mu, hs, axis=1), ws, axis=2)
+    rnd = (lambda a: bf16_round(a.astype(np.float32))) if wl.dtype == "bf16" else \
+        (lambda a: a.astype(np.float32))
+    out = {
+        "x": rnd(x),
+        "w_qkv": rnd(_normal(base + 8, (3 * C, C), C ** -0.5)),
+        "b_qkv": _normal(base + 9, (3 * C,), 0.1).astype(np.float32),
+        "w_out": rnd(_normal(base + 10, (C, C), C ** -0.5)),
+        "b_out": _normal(base + 11, (C,), 0.1).astype(np.float32),
+        "w": _normal(base + 3, (C, wl.lepe_ks, wl.lepe_ks), 0.02).astype(np.float32),
+        "bias": None,
+    }
     return out
