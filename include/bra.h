@@ -111,6 +111,56 @@ bra_status bra_lepe(const void* v, const float* w, const float* b, int ks,
                     int B, int H, int W, int C, bra_dtype dtype, void* out,
                     void* stream);
 
+/* ------------------------------------------------------------------------
+ * The module around the method (p1 §3: q_proj / k_proj / v_proj of x before
+ * the routing; the pages show no output projection, so it is optional).
+ * Weights follow the PyTorch Linear convention y = x W^T + b: a weight is
+ * [out_features, in_features] row-major in `dtype`, 16-byte aligned; biases
+ * are float32, 16-byte aligned, or NULL.
+ * ------------------------------------------------------------------------ */
+
+/* Per-token linear map y = x w^T + b on the matrix cores (float32
+ * accumulation, one rounding to dtype).
+ *   x   [rows, K] dtype, device;  w [N, K] dtype, device;  b float32 [N] or
+ *       NULL;  y out: [rows, N] dtype, device, not overlapping x or w.
+ *   K must be a multiple of 32 and N of 4; every operand must stay below
+ *   2 GiB (BRA_E_UNSUPPORTED otherwise). */
+bra_status bra_linear(const void* x, int rows, int K, const void* w,
+                      const float* b, int N, bra_dtype dtype, void* y,
+                      void* stream);
+
+/* Bytes of workspace bra_module_forward needs for these sizes; with_out_proj
+ * non-zero when an output projection will be passed.  Layout, each part
+ * starting on a 256-byte boundary: float64 [B, S*S, C] region means of x,
+ * float64 [B, S*S, C] region means of Q, the same of K, then Q, K, V as
+ * [B, H, W, C] dtype each, then (with_out_proj) y = attention + LePE as
+ * [B, H, W, C] dtype.  After a successful call the workspace holds exactly
+ * those values, which callers may read.  0 for invalid sizes. */
+size_t bra_module_workspace_bytes(int B, int H, int W, int C, int S,
+                                  bra_dtype dtype, int with_out_proj);
+
+/* The BRA module forward pass:
+ *   Q, K, V = x w_qkv^T + b_qkv (w_qkv [3C, C]: rows 0..C-1 give Q, then K,
+ *             then V; b_qkv float32 [3C] or NULL);
+ *   steps 1-6 above on Q, K, V (LePE on the projected V);
+ *   out = y w_out^T + b_out when w_out ([C, C]) is not NULL, else out = y.
+ * Routing uses the region means of x projected in float64 (a region mean
+ * commutes with a per-token linear map), so idx matches a float64
+ * evaluation of the definition up to exact ties.
+ *   x    [B,H,W,C] dtype, device (may be the same memory as out).
+ *   out  [B,H,W,C] dtype, device; idx out: int32 [B, S*S, topk], device.
+ *   ws   device workspace of >= bra_module_workspace_bytes(...) bytes, not
+ *        overlapping x, out or idx.
+ * Other arguments and limits as in bra_forward. */
+bra_status bra_module_forward(const void* x, int B, int H, int W, int C,
+                              int heads, int S, int topk, bra_dtype dtype,
+                              const void* w_qkv, const float* b_qkv,
+                              float route_scale, float attn_scale,
+                              const float* lepe_w, const float* lepe_b,
+                              int lepe_ks, const void* w_out,
+                              const float* b_out, void* out, int32_t* idx,
+                              void* ws, size_t ws_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* bra_strerror(int status);
 

@@ -9,6 +9,7 @@ from .bra_oracle import (  # noqa: F401
     lepe,
     linear,
     module_forward,
+    round_storage,
     region_affinity,
     region_mean,
     region_shape,

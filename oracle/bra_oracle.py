@@ -66,6 +66,14 @@ Readings for the module around the method (``module_forward``):
       [C, C] output Linear (with optional bias) applied to out = O + L;
       without it the module returns O + L.
   M3  LePE is taken on the projected V (p1 §3 adds lce(v) to the output).
+  M4  The pages fix no precision.  A model that runs in a narrower format
+      stores each layer's output in that format: Q, K and V as the
+      projection's output, y = O + L as the attention layer's output
+      (``storage``: None keeps float64, "f32" / "bf16" round to nearest
+      even).  The region means that decide the routing are those of the
+      projections as computed, before they are stored (equivalently the
+      projection of x's region means, since a region mean commutes with a
+      per-token linear map).
 
 Parity pins for every function live in ``tests/test_oracle_pins.py``.
 """
@@ -85,6 +93,7 @@ __all__ = [
     "lepe",
     "bra_forward",
     "linear",
+    "round_storage",
     "module_forward",
 ]
 
@@ -278,30 +287,59 @@ def linear(X, w, b=None) -> np.ndarray:
     return Y
 
 
+def round_storage(X, storage):
+    """Round to a layer output's storage format (reading M4): None keeps
+    float64, "f32" rounds to float32 (NumPy's cast rounds to nearest even),
+    "bf16" to bfloat16 with round-to-nearest-even on the float64 value
+    (8 significant bits; below 2**-126 a fixed spacing of 2**-133, as in
+    float32; finite values only)."""
+    X = _f64(X)
+    if storage is None:
+        return X
+    if storage == "f32":
+        return X.astype(np.float32).astype(np.float64)
+    if storage != "bf16":
+        raise ValueError(f"storage {storage!r} is not None, 'f32' or 'bf16'")
+    _, e = np.frexp(X)                    # X = m * 2**e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)               # spacing 2**(e - 8), at least 2**-133
+    return np.ldexp(np.round(np.ldexp(X, 8 - e)), e - 8)
+
+
 def module_forward(x, w_qkv, b_qkv, heads: int, S: int, topk: int, lepe_w=None,
                    lepe_b=None, w_out=None, b_out=None, route_scale: float | None = None,
-                   attn_scale: float | None = None, return_parts: bool = False):
-    """BRA as a module (p1 §3): Q, K, V = projections of x (M1), the BRA
-    forward pass on them with LePE on the projected V (M3), then the optional
-    output projection (M2).
+                   attn_scale: float | None = None, storage: str | None = None,
+                   return_parts: bool = False):
+    """BRA as a module (p1 §3): Q, K, V = projections of x (M1); routing on
+    their region means; attention over the routed regions and LePE on the
+    projected V (M3), with Q, K, V and y = O + L stored per ``storage`` (M4);
+    then the optional output projection (M2).
 
     x: [B, H, W, C]; w_qkv: [3C, C]; b_qkv: [3C] or None; w_out: [C, C] or
     None; b_out: [C] or None.  Returns (out, idx) or, with return_parts, a
-    dict with every intermediate (those of bra_forward under their names, plus
-    q, k, v, y = O + L and out).
+    dict with every intermediate: q, k, v (as stored), q_r, k_r, A, idx, O,
+    L, y (as stored) and out.
     """
     x = _f64(x)
-    C = x.shape[-1]
+    B, H, W, C = x.shape
+    region_shape(H, W, S)
     if np.shape(w_qkv) != (3 * C, C):
         raise ValueError("w_qkv must be [3C, C]")
+    if route_scale is None:
+        route_scale = C ** -0.5
+    if attn_scale is None:
+        attn_scale = (C // heads) ** -0.5
     qkv = linear(x, w_qkv, b_qkv)
     q, k, v = qkv[..., :C], qkv[..., C:2 * C], qkv[..., 2 * C:]
-    parts = bra_forward(q, k, v, heads, S, topk, lepe_w, lepe_b, route_scale, attn_scale,
-                        return_parts=True)
-    y = parts["out"]
+    q_r = region_mean(q, S)
+    k_r = region_mean(k, S)
+    A = region_affinity(q_r, k_r, route_scale)
+    idx = topk_route(A, topk)
+    q, k, v = (round_storage(t, storage) for t in (q, k, v))
+    O = routed_attention(q, k, v, idx, heads, S, attn_scale)
+    L = lepe(v, lepe_w, lepe_b) if lepe_w is not None else np.zeros_like(O)
+    y = round_storage(O + L, storage)
     out = linear(y, w_out, b_out) if w_out is not None else y
     if return_parts:
-        parts = dict(parts)
-        parts.update({"q": q, "k": k, "v": v, "y": y, "out": out})
-        return parts
-    return out, parts["idx"]
+        return {"q": q, "k": k, "v": v, "q_r": q_r, "k_r": k_r, "A": A, "idx": idx, "O": O,
+                "L": L, "y": y, "out": out}
+    return out, idx

@@ -418,11 +418,56 @@ def pin_pool_commutes_with_projection():
            "mean/projection order")
 
 
+def pin_round_storage_torch():
+    """bf16 storage rounding equals torch's float32 -> bfloat16 conversion
+    (round to nearest even), on random values over a wide range and on exact
+    halfway cases; f32 storage equals the float32 cast (reading M4)."""
+    import torch
+    r = _rng(31)
+    x = np.concatenate([r.normal(size=20000), r.normal(size=2000) * 1e-20,
+                        r.normal(size=2000) * 1e20]).astype(np.float32)
+    u = (r.integers(0, 1 << 15, size=2000, dtype=np.uint32) << 16) | 0x8000   # ties
+    u = u[(u >> 23) & 0xFF != 0xFF]
+    x = np.concatenate([x, u.view(np.float32), np.float32([0.0, -0.0, 1.0, -3.5])])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_storage(x.astype(np.float64), "bf16")
+    assert np.array_equal(got, ref), "bf16 rounding"
+    y = r.normal(size=1000)
+    assert np.array_equal(O.round_storage(y, "f32"), y.astype(np.float32).astype(np.float64))
+    assert np.array_equal(O.round_storage(y, None), y)
+
+
+def pin_module_storage():
+    """Reading M4: routing is decided on the projections as computed (the
+    region means are those of the unrounded projections, and idx does not
+    depend on the storage format); with projections that are exactly
+    representable in bf16, storage changes only y, by rounding it."""
+    B, H, W, C, heads, S, topk = 1, 8, 8, 6, 2, 4, 3
+    x = _rng(32).normal(size=(B, H, W, C))
+    w = _rng(33).normal(size=(3 * C, C))
+    b = _rng(34).normal(size=3 * C)
+    lw = _rng(35).normal(size=(C, 3, 3))
+    p64 = O.module_forward(x, w, b, heads, S, topk, lw, return_parts=True)
+    p16 = O.module_forward(x, w, b, heads, S, topk, lw, storage="bf16", return_parts=True)
+    qkv = O.linear(x, w, b)
+    _close(p16["q_r"], O.region_mean(qkv[..., :C], S), 1e-14, "means of unrounded q")
+    _close(p16["k_r"], O.region_mean(qkv[..., C:2 * C], S), 1e-14, "means of unrounded k")
+    assert np.array_equal(p16["idx"], p64["idx"])
+    assert not np.array_equal(p16["q"], p64["q"])
+    # bf16-exact projections: identity weights on bf16-representable x
+    xb = O.round_storage(x, "bf16")
+    eye3 = np.concatenate([np.eye(C)] * 3)
+    a = O.module_forward(xb, eye3, None, heads, S, topk, lw, return_parts=True)
+    c = O.module_forward(xb, eye3, None, heads, S, topk, lw, storage="bf16", return_parts=True)
+    _close(c["O"], a["O"], 0.0, "O unchanged")
+    assert np.array_equal(c["y"], O.round_storage(a["y"], "bf16"))
+
+
 ALL_PINS = [
     pin_golden, pin_partition_layout, pin_pool_avgpool, pin_affinity_orientation,
     pin_topk_bruteforce, pin_scale_invariance, pin_masked_dense,
     pin_global_when_all_routed, pin_plain_when_one_region, pin_window_when_identity,
     pin_sdpa_masked, pin_lepe_conv2d, pin_invariants, pin_route_ties,
     pin_module_golden, pin_linear_torch, pin_module_reduces_to_bra,
-    pin_pool_commutes_with_projection,
+    pin_pool_commutes_with_projection, pin_round_storage_torch, pin_module_storage,
 ]

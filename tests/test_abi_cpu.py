@@ -38,7 +38,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("bra_route", "bra_attend", "bra_forward", "bra_lepe", "bra_workspace_bytes",
-              "bra_strerror", "bra_last_error"):
+              "bra_strerror", "bra_last_error", "bra_linear", "bra_module_workspace_bytes",
+              "bra_module_forward"):
         assert n in names
 
 
@@ -143,3 +144,63 @@ def test_error_is_thread_local_and_cleared(lib):
     # a later rejected call overwrites the message
     assert route(lib, q=None) == INVAL
     assert b"q is NULL" in lib.bra_last_error()
+
+
+def test_module_workspace_layout(lib):
+    # means: 3 x B*S*S*C float64; tensors: Q, K, V (+ y) of B*H*W*C elements;
+    # each part rounded up to 256 bytes
+    B, H, W, C, S = 2, 14, 14, 64, 7
+    means = 2 * 49 * 64 * 8
+    tensor = 2 * 14 * 14 * 64 * 2
+    up = lambda x: (x + 255) // 256 * 256
+    assert lib.bra_module_workspace_bytes(B, H, W, C, S, BF16, 0) == 3 * up(means) + 3 * up(tensor)
+    assert lib.bra_module_workspace_bytes(B, H, W, C, S, BF16, 1) == 3 * up(means) + 4 * up(tensor)
+    assert lib.bra_module_workspace_bytes(B, H, W, C, S, F32, 1) == 3 * up(means) + 4 * up(2 * tensor)
+    assert lib.bra_module_workspace_bytes(0, H, W, C, S, BF16, 1) == 0
+    assert lib.bra_module_workspace_bytes(B, H, W, C, S, 5, 1) == 0
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(K=48), UNSUP, "multiple of 32"),
+    (dict(N=6), UNSUP, "multiple of 4"),
+    (dict(rows=0), INVAL, "positive"),
+    (dict(x=None), INVAL, "x is NULL"),
+    (dict(w=P2 + 8), INVAL, "aligned"),
+    (dict(b=P3 + 4), INVAL, "aligned"),
+    (dict(y=P + 64), INVAL, "overlaps"),
+    (dict(dt=3), INVAL, "dtype"),
+    (dict(rows=1 << 24, K=64), UNSUP, "2 GiB"),
+])
+def test_linear_rejects(lib, kw, status, msg):
+    a = dict(x=P, rows=100, K=64, w=P2, b=None, N=64, dt=BF16, y=P4)
+    a.update(kw)
+    assert lib.bra_linear(a["x"], a["rows"], a["K"], a["w"], a["b"], a["N"], a["dt"], a["y"],
+                          None) == status
+    assert msg in lib.bra_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(heads=3), INVAL, "heads"),
+    (dict(heads=1), UNSUP, "head width"),
+    (dict(w_qkv=None), INVAL, "w_qkv is NULL"),
+    (dict(b_qkv=P3 + 4), INVAL, "b_qkv"),
+    (dict(b_out=P3), INVAL, "without w_out"),
+    (dict(idx=None), INVAL, "idx is NULL"),
+    (dict(rs=0.0), INVAL, "route_scale"),
+    (dict(ascale=math.nan), INVAL, "attn_scale"),
+    (dict(ws=None), WSERR, "NULL"),
+    (dict(wsb=1000), WSERR, "needed"),
+    (dict(ws=P + 256), INVAL, "workspace overlaps x"),
+    (dict(lw=P2, ks=4), UNSUP, "lepe_ks"),
+])
+def test_module_rejects(lib, kw, status, msg):
+    a = dict(x=P, B=2, H=8, W=8, C=64, heads=2, S=2, topk=2, dt=BF16, w_qkv=P2, b_qkv=None,
+             rs=0.125, ascale=0.17, lw=None, lb=None, ks=5, w_out=None, b_out=None,
+             out=0x70000000, idx=P4, ws=0x7A000000, wsb=1 << 24)
+    a.update(kw)
+    st = lib.bra_module_forward(a["x"], a["B"], a["H"], a["W"], a["C"], a["heads"], a["S"],
+                                a["topk"], a["dt"], a["w_qkv"], a["b_qkv"], a["rs"], a["ascale"],
+                                a["lw"], a["lb"], a["ks"], a["w_out"], a["b_out"], a["out"],
+                                a["idx"], a["ws"], a["wsb"], None)
+    assert st == status
+    assert msg in lib.bra_last_error().decode()

@@ -1,0 +1,156 @@
+"""The BRA module on the GPU (bra_linear, bra_module_forward) against the fp64
+oracle's linear and module_forward, through the C ABI.
+
+The module's routing takes the region means of x projected in float64, so
+its means of Q and K match the oracle's (means of the float64 projections)
+to float64 rounding, and idx matches exactly up to near-ties.  Q, K, V and
+y = O + L are stored in the input dtype, as a model in that dtype stores its
+layer outputs; the oracle takes the same storage points (its reading M4,
+rounding with its own definition), computes everything else in float64, and
+the output is compared at the contract tolerance."""
+
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_close, check_idx, to_dev, to_host
+from vision_transformer_dynamic_region_amd.workloads import (WORKLOADS, Workload,
+                                                              make_module_inputs)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rows,K,N,bias", [
+    (1000, 64, 192, True),      # ragged token tile, three feature tiles
+    (129, 32, 4, False),        # one token past a tile, a partial feature tile
+    (300, 96, 100, True),       # K of three 32-steps, N not a multiple of 64
+    (257, 288, 64, True),       # K over the 256-column LDS chunk
+    (64, 1024, 36, False),      # widest K, four chunks
+])
+def test_linear(cuda, dtype, rows, K, N, bias):
+    import torch
+    import vision_transformer_dynamic_region_amd as bra
+    print(f"[module] linear {dtype} rows={rows} K={K} N={N} bias={bias}", flush=True)
+    r = np.random.default_rng(rows * 7 + K + N)
+    x = r.normal(size=(rows, K)).astype(np.float32)
+    w = (r.normal(size=(N, K)) * K ** -0.5).astype(np.float32)
+    b = r.normal(0, 0.1, size=N).astype(np.float32) if bias else None
+    if dtype == "bf16":
+        from vision_transformer_dynamic_region_amd.workloads import bf16_round
+        x, w = bf16_round(x), bf16_round(w)
+    y = bra.linear(to_dev(x, dtype), to_dev(w, dtype),
+                   torch.from_numpy(b).to(cuda) if bias else None)
+    torch.cuda.synchronize()
+    ref = oracle.linear(x, w, b)
+    assert_close(to_host(y), ref, dtype, f"linear {rows}x{K}x{N}")
+    if dtype == "f32":
+        # float32 accumulation of K exact products: far inside the contract
+        err = np.max(np.abs(to_host(y) - ref)) / np.sqrt(np.mean(ref ** 2))
+        assert err < 1e-5, err
+
+
+MODULE_CASES = {
+    # name: (workload, with output projection, with biases)
+    "tiny": ("tiny", True, True),
+    "st1": ("st1", True, True),
+    "st2": ("st2", True, True),
+    "st3": ("st3", True, True),
+    "dense": ("dense", True, True),
+    "tiny_no_out_no_bias": ("tiny", False, False),
+    "st1_B2_no_out": ("st1:B=2", False, True),
+    "ragged_bf16": ("ragged", True, True),
+}
+
+
+def _workload(spec: str) -> Workload:
+    if spec == "ragged":
+        return Workload("ragged", 50, "bf16", 2, 12, 20, 96, 3, 4, 5)
+    if ":" in spec:
+        name, kv = spec.split(":")
+        k, v = kv.split("=")
+        return WORKLOADS[name].scaled(**{k: int(v)})
+    return WORKLOADS[spec]
+
+
+@functools.lru_cache(maxsize=None)
+def module_case(name):
+    spec, with_out, with_bias = MODULE_CASES[name]
+    wl = _workload(spec)
+    m = make_module_inputs(wl)
+    if not with_bias:
+        m["b_qkv"] = None
+        m["b_out"] = None
+    if not with_out:
+        m["w_out"] = None
+        m["b_out"] = None
+    ref = oracle.module_forward(m["x"], m["w_qkv"], m["b_qkv"], wl.heads, wl.S, wl.topk, m["w"],
+                                None, m["w_out"], m["b_out"], storage=wl.dtype,
+                                return_parts=True)
+    return wl, m, ref
+
+
+@pytest.mark.parametrize("name", list(MODULE_CASES))
+def test_module_parity(cuda, name):
+    import torch
+    import vision_transformer_dynamic_region_amd as bra
+    wl, m, ref = module_case(name)
+    print(f"[module] forward {name} {wl}", flush=True)
+    dt = wl.dtype
+    dev = lambda a: None if a is None else to_dev(a, dt)
+    f32 = lambda a: None if a is None else torch.from_numpy(a).to(cuda)
+    x = dev(m["x"])
+    B, H, W, C, S = wl.B, wl.H, wl.W, wl.C, wl.S
+    code = 1 if dt == "bf16" else 0
+    ws = torch.empty(bra.module_workspace_bytes(B, H, W, C, S, code, m["w_out"] is not None),
+                     dtype=torch.uint8, device=cuda)
+    out, idx = bra.module_forward(x, dev(m["w_qkv"]), f32(m["b_qkv"]), wl.heads, S, wl.topk,
+                                  f32(m["w"]), None, dev(m["w_out"]), f32(m["b_out"]),
+                                  workspace=ws)
+    torch.cuda.synchronize()
+    # workspace: float64 means of x, Q and K, then Q, K, V
+    up = lambda n: (n + 255) // 256 * 256
+    R = S * S
+    mb = up(B * R * C * 8)
+    w8 = ws.cpu().numpy()
+    means = [w8[i * mb:i * mb + B * R * C * 8].view(np.float64).reshape(B, R, C) for i in range(3)]
+    xm_ref = oracle.region_mean(m["x"], S)
+    assert np.max(np.abs(means[0] - xm_ref)) <= 1e-12 * max(1.0, np.abs(xm_ref).max())
+    for got, want, nm in ((means[1], ref["q_r"], "q_r"), (means[2], ref["k_r"], "k_r")):
+        assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.abs(want).max()), nm
+    es = 2 if dt == "bf16" else 4
+    tb = up(B * H * W * C * es)
+    for i, nm in enumerate(("q", "k", "v")):
+        raw = ws[3 * mb + i * tb:3 * mb + i * tb + B * H * W * C * es]
+        t = raw.view(torch.bfloat16 if dt == "bf16" else torch.float32).reshape(B, H, W, C)
+        assert_close(to_host(t), ref[nm], dt, f"{name} {nm}")
+    idx_g = idx.cpu().numpy()
+    ties = check_idx(idx_g, ref["idx"], ref["A"])
+    want = ref["out"]
+    if ties:
+        print(f"[module] {name}: {len(ties)} near-tie rows; comparing with the GPU index",
+              flush=True)
+        O = oracle.routed_attention(ref["q"], ref["k"], ref["v"], idx_g, wl.heads, S, wl.d ** -0.5)
+        y = oracle.round_storage(O + ref["L"], dt)
+        want = oracle.linear(y, m["w_out"], m["b_out"]) if m["w_out"] is not None else y
+    e = assert_close(to_host(out), want, dt, f"{name} out")
+    print(f"[module] {name}: idx exact ({len(ties)} tie rows), out err/RMS {e:.2e}", flush=True)
+
+
+def test_module_in_place(cuda):
+    """out may be the same memory as x (x is last read before out is written)."""
+    import torch
+    import vision_transformer_dynamic_region_amd as bra
+    wl, m, ref = module_case("tiny")
+    x = to_dev(m["x"], wl.dtype)
+    args = (to_dev(m["w_qkv"], wl.dtype), torch.from_numpy(m["b_qkv"]).to(cuda), wl.heads, wl.S,
+            wl.topk, torch.from_numpy(m["w"]).to(cuda), None, to_dev(m["w_out"], wl.dtype),
+            torch.from_numpy(m["b_out"]).to(cuda))
+    want, _ = bra.module_forward(x, *args)
+    bra.module_forward(x, *args, out=x)
+    torch.cuda.synchronize()
+    assert torch.equal(x, want)

@@ -10,7 +10,7 @@ from oracle_pins import ALL_PINS
 
 _orig = {name: getattr(O, name) for name in
          ("region_mean", "region_affinity", "topk_route", "routed_attention", "lepe",
-          "region_tokens", "linear", "module_forward")}
+          "region_tokens", "linear", "module_forward", "round_storage")}
 
 
 def _mean_as_sum(X, S):
@@ -134,7 +134,8 @@ def _module_qk_swapped(x, w_qkv, b_qkv, *a, **k):
 
 
 def _module_lepe_on_x(x, w_qkv, b_qkv, heads, S, topk, lepe_w=None, lepe_b=None, w_out=None,
-                      b_out=None, route_scale=None, attn_scale=None, return_parts=False):
+                      b_out=None, route_scale=None, attn_scale=None, storage=None,
+                      return_parts=False):
     x = np.asarray(x, dtype=np.float64)
     C = x.shape[-1]
     qkv = O.linear(x, w_qkv, b_qkv)
@@ -150,7 +151,7 @@ def _module_lepe_on_x(x, w_qkv, b_qkv, heads, S, topk, lepe_w=None, lepe_b=None,
 
 def _module_out_before_lepe(x, w_qkv, b_qkv, heads, S, topk, lepe_w=None, lepe_b=None,
                             w_out=None, b_out=None, route_scale=None, attn_scale=None,
-                            return_parts=False):
+                            storage=None, return_parts=False):
     x = np.asarray(x, dtype=np.float64)
     C = x.shape[-1]
     qkv = O.linear(x, w_qkv, b_qkv)
@@ -166,6 +167,41 @@ def _module_out_before_lepe(x, w_qkv, b_qkv, heads, S, topk, lepe_w=None, lepe_b
     return out, p["idx"]
 
 
+def _round_truncating(X, storage):
+    X = np.asarray(X, dtype=np.float64)
+    if storage != "bf16":
+        return _orig["round_storage"](X, storage)
+    _, e = np.frexp(X)
+    e = np.maximum(e, -125)
+    return np.ldexp(np.trunc(np.ldexp(X, 8 - e)), e - 8)
+
+
+def _round_ties_away(X, storage):
+    X = np.asarray(X, dtype=np.float64)
+    if storage != "bf16":
+        return _orig["round_storage"](X, storage)
+    _, e = np.frexp(X)
+    e = np.maximum(e, -125)
+    t = np.ldexp(X, 8 - e)
+    return np.ldexp(np.sign(t) * np.floor(np.abs(t) + 0.5), e - 8)
+
+
+def _module_round_before_routing(x, w_qkv, b_qkv, heads, S, topk, lepe_w=None, lepe_b=None,
+                                 w_out=None, b_out=None, route_scale=None, attn_scale=None,
+                                 storage=None, return_parts=False):
+    x = np.asarray(x, dtype=np.float64)
+    C = x.shape[-1]
+    qkv = O.round_storage(O.linear(x, w_qkv, b_qkv), storage)
+    q, k, v = qkv[..., :C], qkv[..., C:2 * C], qkv[..., 2 * C:]
+    p = O.bra_forward(q, k, v, heads, S, topk, lepe_w, lepe_b, route_scale, attn_scale,
+                      return_parts=True)
+    y = O.round_storage(p["out"], storage)
+    out = O.linear(y, w_out, b_out) if w_out is not None else y
+    if return_parts:
+        return dict(p, q=q, k=k, v=v, y=y, out=out)
+    return out, p["idx"]
+
+
 MUTANTS = {
     "region_mean": [_mean_as_sum, _mean_column_major],
     "region_affinity": [_affinity_transposed],
@@ -175,7 +211,9 @@ MUTANTS = {
     "lepe": [_lepe_flipped, _lepe_transposed, _lepe_no_bias, _lepe_circular],
     "region_tokens": [_tokens_column_major],
     "linear": [_linear_transposed, _linear_no_bias, _linear_bias_subtracted],
-    "module_forward": [_module_qk_swapped, _module_lepe_on_x, _module_out_before_lepe],
+    "module_forward": [_module_qk_swapped, _module_lepe_on_x, _module_out_before_lepe,
+                       _module_round_before_routing],
+    "round_storage": [_round_truncating, _round_ties_away],
 }
 CASES = [(name, m) for name, ms in MUTANTS.items() for m in ms]
 

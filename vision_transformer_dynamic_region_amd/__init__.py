@@ -16,7 +16,8 @@ import ctypes
 import os
 
 __all__ = ["BraError", "lib_path", "load", "workspace_bytes", "route", "attend",
-           "forward", "lepe", "STATUS"]
+           "forward", "lepe", "linear", "module_workspace_bytes", "module_forward",
+           "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -35,6 +36,10 @@ _SIGNATURES = {
     "bra_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _f, _vp, _vp, _i,
                          _vp, _vp, _vp, _vp, _sz, _vp]),
     "bra_lepe": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp]),
+    "bra_linear": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _vp]),
+    "bra_module_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "bra_module_forward": (_i, [_vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _f, _f, _vp, _vp,
+                                _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bra_strerror": (ctypes.c_char_p, [_i]),
     "bra_last_error": (ctypes.c_char_p, []),
 }
@@ -234,3 +239,83 @@ def lepe(v, w, b, out):
         raise ValueError("w is required")
     _check(load().bra_lepe(v.data_ptr(), wp, bp, ks, B, H, W, C, dt, out.data_ptr(), _stream(v)))
     return out
+
+
+def _opt(t, name, dtype, shape):
+    """Pointer of an optional device tensor of the given dtype and shape."""
+    if t is None:
+        return None
+    _dev(t, name, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}")
+    return t.data_ptr()
+
+
+def linear(x, w, b=None, out=None):
+    """y = x w^T + b over the last axis (bra_linear): x [..., K], w [N, K] in
+    x's dtype, b float32 [N] or None.  Returns y [..., N]."""
+    import torch
+    dt = _dtype_code(x)
+    _dev(x, "x")
+    _dev(w, "w", x.dtype)
+    if w.dim() != 2 or w.shape[1] != x.shape[-1]:
+        raise ValueError("w must be [N, K] with K = x.shape[-1]")
+    N, K = int(w.shape[0]), int(w.shape[1])
+    rows = x.numel() // K
+    bp = _opt(b, "b", torch.float32, (N,))
+    if out is None:
+        out = torch.empty((*x.shape[:-1], N), dtype=x.dtype, device=x.device)
+    _dev(out, "out", x.dtype)
+    if out.numel() != rows * N:
+        raise ValueError("out must hold rows * N elements")
+    _check(load().bra_linear(x.data_ptr(), rows, K, w.data_ptr(), bp, N, dt, out.data_ptr(),
+                             _stream(x)))
+    return out
+
+
+def module_workspace_bytes(B: int, H: int, W: int, C: int, S: int, dtype_code: int,
+                           with_out_proj: bool) -> int:
+    return int(load().bra_module_workspace_bytes(B, H, W, C, S, dtype_code, int(bool(with_out_proj))))
+
+
+def module_forward(x, w_qkv, b_qkv, heads: int, S: int, topk: int, lepe_w=None, lepe_b=None,
+                   w_out=None, b_out=None, route_scale: float | None = None,
+                   attn_scale: float | None = None, out=None, idx=None, workspace=None):
+    """The BRA module (bra_module_forward): Q, K, V = x w_qkv^T + b_qkv, the
+    BRA forward pass with LePE on V, then the optional output projection.
+    Returns (out, idx).  workspace, if given, is a CUDA uint8 tensor of at
+    least module_workspace_bytes(...) bytes; afterwards it holds the region
+    means of x, Q and K and the tensors Q, K, V (and y when w_out is given)."""
+    import torch
+    B, H, W, C = _bhwc(x)
+    dt = _dtype_code(x)
+    _dev(x, "x")
+    _dev(w_qkv, "w_qkv", x.dtype)
+    if tuple(w_qkv.shape) != (3 * C, C):
+        raise ValueError("w_qkv must be [3C, C]")
+    bq = _opt(b_qkv, "b_qkv", torch.float32, (3 * C,))
+    wo = _opt(w_out, "w_out", x.dtype, (C, C))
+    bo = _opt(b_out, "b_out", torch.float32, (C,))
+    if route_scale is None:
+        route_scale = C ** -0.5
+    if attn_scale is None:
+        attn_scale = (C // heads) ** -0.5
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "out", x.dtype)
+    if idx is None:
+        idx = torch.empty((B, S * S, topk), dtype=torch.int32, device=x.device)
+    _dev(idx, "idx", torch.int32)
+    if idx.numel() != B * S * S * topk:
+        raise ValueError("idx must hold B*S*S*topk entries")
+    if workspace is None:
+        need = module_workspace_bytes(B, H, W, C, S, dt, w_out is not None)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace")
+    wp, bp, ks = _lepe_args(lepe_w, lepe_b, C)
+    _check(load().bra_module_forward(x.data_ptr(), B, H, W, C, heads, S, topk, dt,
+                                     w_qkv.data_ptr(), bq, float(route_scale), float(attn_scale),
+                                     wp, bp, ks, wo, bo, out.data_ptr(), idx.data_ptr(),
+                                     workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(), _stream(x)))
+    return out, idx

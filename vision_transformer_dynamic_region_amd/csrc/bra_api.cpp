@@ -39,6 +39,12 @@ bool overlaps(const void* a, const void* b, size_t bytes) {
   return x < y + bytes && y < x + bytes;
 }
 
+// [a, a + an) and [b, b + bn) intersect
+bool overlaps2(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + bn && y < x + an;
+}
+
 // Shape checks shared by every entry point.  heads <= 0 means "not used".
 bra_status check_shape(int B, int H, int W, int C, int S, int heads, int topk, bra_dtype dt,
                        bra::Shape* out) {
@@ -122,6 +128,35 @@ bra_status check_attend_args(const void* q, const void* k, const void* v, const 
   if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
     return fail(BRA_E_INVAL, "out overlaps q, k or v");
   if (w && (st = check_lepe_args(w, b, ks, s))) return st;
+  return BRA_OK;
+}
+
+constexpr long long kMaxOperandBytes = 1LL << 31;   // 32-bit buffer offsets
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Byte offsets of the module workspace parts (see bra_module_workspace_bytes).
+struct ModuleLayout {
+  size_t xm, qm, km, q, k, v, y, total;
+};
+
+ModuleLayout module_layout(int B, int H, int W, int C, int S, bra_dtype dt, bool with_out) {
+  ModuleLayout l;
+  const size_t means = align256((size_t)B * S * S * C * sizeof(double));
+  const size_t tensor = align256((size_t)B * H * W * C * elem_size(dt));
+  l.xm = 0;
+  l.qm = l.xm + means;
+  l.km = l.qm + means;
+  l.q = l.km + means;
+  l.k = l.q + tensor;
+  l.v = l.k + tensor;
+  l.y = l.v + tensor;
+  l.total = l.y + (with_out ? tensor : 0);
+  return l;
+}
+
+bra_status check_bias(const float* b, const char* name) {
+  if (b && !aligned16(b)) return fail(BRA_E_INVAL, "%s is not 16-byte aligned", name);
   return BRA_OK;
 }
 
@@ -212,6 +247,111 @@ bra_status bra_lepe(const void* v, const float* w, const float* b, int ks, int B
   if ((st = check_lepe_args(w, b, ks, s))) return st;
   return hip_status(bra::launch_lepe(v, w, b, ks, s, dtype == BRA_BF16, out, (hipStream_t)stream),
                     "lepe launch");
+}
+
+bra_status bra_linear(const void* x, int rows, int K, const void* w, const float* b, int N,
+                      bra_dtype dtype, void* y, void* stream) {
+  g_last_error[0] = 0;
+  bra_status st;
+  if (dtype != BRA_F32 && dtype != BRA_BF16) return fail(BRA_E_INVAL, "dtype %d is not BRA_F32 or BRA_BF16", (int)dtype);
+  if (rows < 1 || K < 1 || N < 1) return fail(BRA_E_INVAL, "rows=%d K=%d N=%d must be positive", rows, K, N);
+  if ((st = check_tensor(x, "x")) || (st = check_tensor(w, "w")) || (st = check_tensor(y, "y")) ||
+      (st = check_bias(b, "b")))
+    return st;
+  if (K % 32) return fail(BRA_E_UNSUPPORTED, "K=%d must be a multiple of 32", K);
+  if (N % 4) return fail(BRA_E_UNSUPPORTED, "N=%d must be a multiple of 4", N);
+  const size_t es = elem_size(dtype);
+  if ((long long)rows * K * (long long)es >= kMaxOperandBytes ||
+      (long long)rows * N * (long long)es >= kMaxOperandBytes)
+    return fail(BRA_E_UNSUPPORTED, "operands of %d rows exceed 2 GiB", rows);
+  if (overlaps(y, x, (size_t)rows * K * es) || overlaps(y, w, (size_t)N * K * es))
+    return fail(BRA_E_INVAL, "y overlaps x or w");
+  void* ys[1] = {y};
+  return hip_status(bra::launch_linear(x, rows, K, w, b, N, ys, 1, dtype == BRA_BF16,
+                                       (hipStream_t)stream),
+                    "linear launch");
+}
+
+size_t bra_module_workspace_bytes(int B, int H, int W, int C, int S, bra_dtype dtype,
+                                  int with_out_proj) {
+  if (B < 1 || H < 1 || W < 1 || C < 1 || S < 1) return 0;
+  if (dtype != BRA_F32 && dtype != BRA_BF16) return 0;
+  return module_layout(B, H, W, C, S, dtype, with_out_proj != 0).total;
+}
+
+bra_status bra_module_forward(const void* x, int B, int H, int W, int C, int heads, int S,
+                              int topk, bra_dtype dtype, const void* w_qkv, const float* b_qkv,
+                              float route_scale, float attn_scale, const float* lepe_w,
+                              const float* lepe_b, int lepe_ks, const void* w_out,
+                              const float* b_out, void* out, int32_t* idx, void* ws,
+                              size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  bra::Shape s;
+  bra_status st;
+  if (heads < 1) return fail(BRA_E_INVAL, "heads=%d must be positive", heads);
+  if ((st = check_shape(B, H, W, C, S, heads, topk, dtype, &s))) return st;
+  if ((st = check_tensor(x, "x")) || (st = check_tensor(w_qkv, "w_qkv")) ||
+      (st = check_tensor(out, "out")) || (st = check_bias(b_qkv, "b_qkv")) ||
+      (st = check_bias(b_out, "b_out")))
+    return st;
+  if (w_out && (st = check_tensor(w_out, "w_out"))) return st;
+  if (b_out && !w_out) return fail(BRA_E_INVAL, "b_out given without w_out");
+  if (!idx) return fail(BRA_E_INVAL, "idx is NULL");
+  if ((uintptr_t)idx & 3u) return fail(BRA_E_INVAL, "idx is not 4-byte aligned");
+  if (!(route_scale > 0.f) || !std::isfinite(route_scale))
+    return fail(BRA_E_INVAL, "route_scale=%g must be positive and finite", (double)route_scale);
+  if (!(attn_scale > 0.f) || !std::isfinite(attn_scale))
+    return fail(BRA_E_INVAL, "attn_scale=%g must be positive and finite", (double)attn_scale);
+  if (lepe_w && (st = check_lepe_args(lepe_w, lepe_b, lepe_ks, s))) return st;
+  const size_t es = elem_size(dtype);
+  const size_t tbytes = (size_t)B * H * W * C * es;
+  if ((long long)tbytes >= kMaxOperandBytes)
+    return fail(BRA_E_UNSUPPORTED, "a [B,H,W,C] tensor of %zu bytes exceeds 2 GiB", tbytes);
+  const ModuleLayout l = module_layout(B, H, W, C, S, dtype, w_out != nullptr);
+  if (!ws) return fail(BRA_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", l.total);
+  if (!aligned16(ws)) return fail(BRA_E_WORKSPACE, "workspace is not 16-byte aligned");
+  if (ws_bytes < l.total) return fail(BRA_E_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, l.total);
+  const size_t ibytes = (size_t)B * s.R * topk * sizeof(int32_t);
+  if (overlaps2(ws, l.total, x, tbytes)) return fail(BRA_E_INVAL, "workspace overlaps x");
+  if (overlaps2(ws, l.total, out, tbytes)) return fail(BRA_E_INVAL, "workspace overlaps out");
+  if (overlaps2(ws, l.total, idx, ibytes)) return fail(BRA_E_INVAL, "workspace overlaps idx");
+  if (overlaps2(out, tbytes, idx, ibytes) || overlaps2(x, tbytes, idx, ibytes))
+    return fail(BRA_E_INVAL, "idx overlaps x or out");
+  if (overlaps2(out, tbytes, w_qkv, (size_t)3 * C * C * es) ||
+      (w_out && overlaps2(out, tbytes, w_out, (size_t)C * C * es)))
+    return fail(BRA_E_INVAL, "out overlaps a weight");
+  hipStream_t hs = (hipStream_t)stream;
+  const bool bf16 = dtype == BRA_BF16;
+  unsigned char* w8 = (unsigned char*)ws;
+  double* xm = (double*)(w8 + l.xm);
+  double* qm = (double*)(w8 + l.qm);
+  double* km = (double*)(w8 + l.km);
+  void* qkv[3] = {w8 + l.q, w8 + l.k, w8 + l.v};
+  void* y = w_out ? (void*)(w8 + l.y) : out;
+  const int T = B * H * W;
+  // routing: region means of x, projected in float64 (mean commutes with
+  // the per-token map), scaled affinity and top-k
+  if ((st = hip_status(bra::launch_pool(x, nullptr, xm, nullptr, s, bf16, hs), "pool launch")))
+    return st;
+  if ((st = hip_status(bra::launch_means_proj(xm, B * s.R, C, w_qkv, b_qkv, bf16, qm, km, hs),
+                       "means projection launch")))
+    return st;
+  if ((st = hip_status(bra::launch_route(qm, km, s, (double)route_scale, idx, nullptr, hs),
+                       "route launch")))
+    return st;
+  // Q, K, V
+  if ((st = hip_status(bra::launch_linear(x, T, C, w_qkv, b_qkv, 3 * C, qkv, 3, bf16, hs),
+                       "qkv projection launch")))
+    return st;
+  // attention + LePE on the projected V
+  if ((st = hip_status(bra::launch_attend(qkv[0], qkv[1], qkv[2], idx, s, bf16, attn_scale, lepe_w,
+                                          lepe_b, lepe_ks, y, hs),
+                       "attend launch")))
+    return st;
+  if (!w_out) return BRA_OK;
+  void* outs[1] = {out};
+  return hip_status(bra::launch_linear(y, T, C, w_out, b_out, C, outs, 1, bf16, hs),
+                    "output projection launch");
 }
 
 const char* bra_strerror(int status) {

@@ -17,9 +17,21 @@ struct Shape {
   int R;          // regions per image = S * S
 };
 
-// Region means of q and k into qm, km (float64 [B, R, C] each).
+// Region means of q and k into qm, km (float64 [B, R, C] each); with k (and
+// km) null, the means of q alone.
 hipError_t launch_pool(const void* q, const void* k, double* qm, double* km,
                        const Shape& s, bool bf16, hipStream_t st);
+
+// y[g] = columns [g*N/groups, (g+1)*N/groups) of x w^T + b, for x [T, K],
+// w [N, K], b [N] or null (groups <= 3).  K % 32 == 0, N % (4 * groups) == 0.
+hipError_t launch_linear(const void* x, int T, int K, const void* w, const float* b, int N,
+                         void* const* y, int groups, bool bf16, hipStream_t st);
+
+// qm = xm Wq^T + bq, km = xm Wk^T + bk in float64, with Wq, Wk the first two
+// C-row blocks of w_qkv [3C, C] and bq, bk those of b_qkv (or null).
+hipError_t launch_means_proj(const double* xm, int rows, int C, const void* w_qkv,
+                             const float* b_qkv, bool bf16, double* qm, double* km,
+                             hipStream_t st);
 
 // Scaled affinity of the region means and per-row top-k.
 hipError_t launch_route(const double* qm, const double* km, const Shape& s,

@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs A) {
   const int pl = l32 / gl, gi = l32 - pl * gl;
   const double inv_n = 1.0 / (double)s.n;
   const uint4* __restrict__ q = A.q + (size_t)b * s.H * s.W * G;
-  const uint4* __restrict__ k = A.k + (size_t)b * s.H * s.W * G;
+  const bool two = A.k != nullptr;                // else: means of q only
+  const uint4* __restrict__ k = two ? A.k + (size_t)b * s.H * s.W * G : nullptr;
   const int base = (ry * s.hs * s.W + rx * s.ws) * G;
   for (int g0 = 0; g0 < G; g0 += gl) {
     const int g = g0 + gi;
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs A) {
           const int ty = fdiv(t, A.f_ws), tx = t - ty * s.ws;
           const int off = base + (ty * s.W + tx) * G + g;
           uq[u] = q[off];
-          uk[u] = k[off];
+          if (two) uk[u] = k[off];
         }
       }
 #pragma unroll
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs A) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         A.qm[o + e] = aq[e] * inv_n;
-        A.km[o + e] = ak[e] * inv_n;
+        if (two) A.km[o + e] = ak[e] * inv_n;
       }
     }
   }
@@ -163,7 +164,7 @@ __device__ __forceinline__ double group_sum(double v) {
   return v;
 }
 
-template <bool BF16, int G, int NP>
+template <bool BF16, int G, int NP, bool TWO>
 __global__ __launch_bounds__(kPoolWaves * 64) void pool_wave_kernel(PoolArgs A) {
   constexpr int VEC = BF16 ? 8 : 4;
   constexpr int PP = 64 / G;                 // pixels per pass
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(kPoolWaves * 64) void pool_wave_kernel(PoolArgs A) 
   const int b = fdiv(br, A.f_R), r = br - b * s.R;
   const int ry = fdiv(r, A.f_S), rx = r - ry * s.S;
   const uint4* __restrict__ q = A.q + (size_t)b * s.H * s.W * G;
-  const uint4* __restrict__ k = A.k + (size_t)b * s.H * s.W * G;
+  const uint4* __restrict__ k = TWO ? A.k + (size_t)b * s.H * s.W * G : nullptr;
   const int base = (ry * s.hs * s.W + rx * s.ws) * G + g;
   double aq[VEC], ak[VEC];
 #pragma unroll
@@ -190,30 +191,33 @@ __global__ __launch_bounds__(kPoolWaves * 64) void pool_wave_kernel(PoolArgs A) 
         const int ty = fdiv(t, A.f_ws), tx = t - ty * s.ws;
         const int off = base + (ty * s.W + tx) * G;
         uq[u] = q[off];
-        uk[u] = k[off];
+        if constexpr (TWO) uk[u] = k[off];
       }
     }
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       float fq[VEC], fk[VEC];
       unpack16<BF16>(uq[u], fq);
-      unpack16<BF16>(uk[u], fk);
+      if constexpr (TWO) unpack16<BF16>(uk[u], fk);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) { aq[e] += (double)fq[e]; ak[e] += (double)fk[e]; }
+      for (int e = 0; e < VEC; ++e) {
+        aq[e] += (double)fq[e];
+        if constexpr (TWO) ak[e] += (double)fk[e];
+      }
     }
   }
   const double inv_n = 1.0 / (double)s.n;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     aq[e] = group_sum<G>(aq[e]);
-    ak[e] = group_sum<G>(ak[e]);
+    if constexpr (TWO) ak[e] = group_sum<G>(ak[e]);
   }
   if (p0 == 0) {
     const size_t o = (size_t)br * s.C + (size_t)g * VEC;
 #pragma unroll
     for (int e = 0; e < VEC; e += 2) {
       *(double2*)(A.qm + o + e) = make_double2(aq[e] * inv_n, aq[e + 1] * inv_n);
-      *(double2*)(A.km + o + e) = make_double2(ak[e] * inv_n, ak[e + 1] * inv_n);
+      if constexpr (TWO) *(double2*)(A.km + o + e) = make_double2(ak[e] * inv_n, ak[e + 1] * inv_n);
     }
   }
 }
@@ -509,12 +513,15 @@ hipError_t launch_pool(const void* q, const void* k, double* qm, double* km, con
     const int passes = (s.n + 64 / G - 1) / (64 / G);
     const int np = passes >= kWavePass ? kWavePass : passes > 2 ? 4 : passes > 1 ? 2 : 1;
     const dim3 wgrid((unsigned)((a.units + kPoolWaves - 1) / kPoolWaves));
+#define BRA_POOL_LAUNCH(BB, GG, NN, TT) \
+    hipLaunchKernelGGL((pool_wave_kernel<BB, GG, NN, TT>), wgrid, dim3(kPoolWaves * 64), 0, st, a)
 #define BRA_POOL_NP(GG, NN)                                                                   \
     if (G == GG && np == NN) {                                                               \
-      if (bf16)                                                                              \
-        hipLaunchKernelGGL((pool_wave_kernel<true, GG, NN>), wgrid, dim3(kPoolWaves * 64), 0, st, a); \
-      else                                                                                   \
-        hipLaunchKernelGGL((pool_wave_kernel<false, GG, NN>), wgrid, dim3(kPoolWaves * 64), 0, st, a);\
+      if (bf16) {                                                                            \
+        if (k) BRA_POOL_LAUNCH(true, GG, NN, true); else BRA_POOL_LAUNCH(true, GG, NN, false);   \
+      } else {                                                                               \
+        if (k) BRA_POOL_LAUNCH(false, GG, NN, true); else BRA_POOL_LAUNCH(false, GG, NN, false); \
+      }                                                                                      \
       return hipGetLastError();                                                              \
     }
 #define BRA_POOL_G(GG) BRA_POOL_NP(GG, 1) BRA_POOL_NP(GG, 2) BRA_POOL_NP(GG, 4) BRA_POOL_NP(GG, 8)
@@ -522,6 +529,7 @@ hipError_t launch_pool(const void* q, const void* k, double* qm, double* km, con
     BRA_POOL_G(64)
 #undef BRA_POOL_G
 #undef BRA_POOL_NP
+#undef BRA_POOL_LAUNCH
   }
   const dim3 grid((unsigned)((a.units + kRegionsPerPoolBlock - 1) / kRegionsPerPoolBlock));
   if (bf16)
