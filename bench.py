@@ -60,6 +60,9 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="st1", choices=["tiny", "st1", "st2", "st3", "dense"])
+    p.add_argument("--path", default="bra", choices=["bra", "module"],
+                   help="bra: the BRA forward pass on given Q, K, V (the default line); module: "
+                        "the module around it (Q/K/V projections of x, BRA, output projection)")
     p.add_argument("--sets", type=int, default=0,
                    help="input copies rotated across steps (0: enough to exceed the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -175,6 +178,125 @@ def cpu_baseline(wl, x, target_s: float):
     }
 
 
+def module_cpu_baseline(wl, m, target_s: float) -> dict:
+    """The fp64 oracle's module_forward as it stands, on the first images of
+    the same batch, repeated to about target_s seconds."""
+    import oracle
+
+    def run(nb):
+        ru0 = resource.getrusage(resource.RUSAGE_SELF)
+        t0 = time.perf_counter()
+        oracle.module_forward(m["x"][:nb], m["w_qkv"], m["b_qkv"], wl.heads, wl.S, wl.topk,
+                              m["w"], None, m["w_out"], m["b_out"], storage=wl.dtype)
+        dt = time.perf_counter() - t0
+        ru1 = resource.getrusage(resource.RUSAGE_SELF)
+        return dt, (ru1.ru_utime - ru0.ru_utime) + (ru1.ru_stime - ru0.ru_stime)
+
+    t1, _ = run(1)
+    nb = int(max(1, min(wl.B, target_s / max(t1, 1e-3))))
+    dt, cpu, reps = 0.0, 0.0, 0
+    while reps == 0 or (nb == wl.B and dt < target_s and reps < 20):
+        d, c = run(nb)
+        dt, cpu, reps = dt + d, cpu + c, reps + 1
+    tokens = nb * wl.H * wl.W * reps
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": max(1, int(round(cpu / dt))),
+            "kind": "oracle",
+            "sample": (f"{wl.name} module: first {nb} of {wl.B} images x {reps} passes "
+                       f"({tokens} tokens), fp64 oracle module_forward in {dt:.1f} s")}
+
+
+def run_module(a, wl) -> int:
+    """One step = bra_module_forward over one batch: pooling of x, float64
+    projection of the means, routing, the Q/K/V projection, attention with
+    LePE, the output projection."""
+    import numpy as np
+    import torch
+
+    import vision_transformer_dynamic_region_amd as bra
+    from vision_transformer_dynamic_region_amd.workloads import bf16_bits, make_module_inputs
+
+    dev = torch.device("cuda:0")
+    m = make_module_inputs(wl)
+    if wl.dtype == "bf16":
+        up = lambda arr: torch.from_numpy(bf16_bits(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        up = lambda arr: torch.from_numpy(arr).to(dev)
+    f32 = lambda arr: torch.from_numpy(arr).to(dev)
+    w_qkv, w_out = up(m["w_qkv"]), up(m["w_out"])
+    b_qkv, b_out, lw = f32(m["b_qkv"]), f32(m["b_out"]), f32(m["w"])
+    x0 = up(m["x"])
+    code = 1 if wl.dtype == "bf16" else 0
+    wsb = bra.module_workspace_bytes(wl.B, wl.H, wl.W, wl.C, wl.S, code, True)
+    set_bytes = 2 * wl.tensor_bytes + wsb
+    sets = a.sets or max(1, -(-3 * MALL_BYTES // set_bytes))
+    bufs = [dict(x=x0.clone(), out=torch.empty_like(x0),
+                 idx=torch.empty((wl.B, wl.S * wl.S, wl.topk), dtype=torch.int32, device=dev),
+                 ws=torch.empty(wsb, dtype=torch.uint8, device=dev)) for _ in range(sets)]
+    torch.cuda.synchronize()
+    log(f"module: {sets} sets of {set_bytes / 1e6:.1f} MB (x, out, workspace) rotated per step")
+
+    def step(i):
+        b = bufs[i % sets]
+        bra.module_forward(b["x"], w_qkv, b_qkv, wl.heads, wl.S, wl.topk, lw, None, w_out, b_out,
+                           out=b["out"], idx=b["idx"], workspace=b["ws"])
+
+    for i in range(a.warmup):
+        step(i)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(a.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    log(f"module: {ms:.4f} ms/step")
+
+    # the Q/K/V projection alone: x read once, Q, K, V written once
+    qkv_views = []
+    for b in bufs:
+        qkv_views.append(torch.empty((wl.B, wl.H, wl.W, 3 * wl.C), dtype=x0.dtype, device=dev))
+
+    def lin_step(i):
+        b = bufs[i % sets]
+        bra.linear(b["x"], w_qkv, b_qkv, out=qkv_views[i % sets])
+
+    for i in range(a.warmup):
+        lin_step(i)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(a.steps):
+        lin_step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_lin = e0.elapsed_time(e1) / a.steps
+    lin_bytes = 4 * wl.tensor_bytes
+    lin_gbs = lin_bytes / (t_lin * 1e-3) / 1e9
+    res = {
+        "metric": "BRA module fwd tokens/s (x -> QKV projection -> BRA -> output projection), 1 GPU",
+        "value": wl.tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name} module: B={wl.B} H=W={wl.H} C={wl.C} "
+                               f"heads={wl.heads} S={wl.S} topk={wl.topk} LePE "
+                               f"{wl.lepe_ks}x{wl.lepe_ks}, w_qkv [3C,C], w_out [C,C]",
+                   "tokens_per_step": wl.tokens, "input_sets_rotated": sets},
+        "stages_ms": {"qkv_linear": t_lin},
+        "roofline": {"kernel": "linear_kernel (Q/K/V projection)", "bound": "hbm",
+                     "achieved": lin_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": lin_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": lin_bytes},
+    }
+    if not a.no_cpu_baseline:
+        log("timing the fp64 oracle module on the host")
+        res["cpu_baseline"] = module_cpu_baseline(wl, m, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     a = parse()
     if a.traffic_from:
@@ -197,6 +319,8 @@ def main() -> int:
         return 0
 
     wl = WORKLOADS[a.workload]
+    if a.path == "module":
+        return run_module(a, wl)
     dev = torch.device("cuda:0")
     log(f"workload {wl}")
     x = make_inputs(wl)

@@ -16,12 +16,13 @@
 
 #include "device_common.h"
 
+#include <type_traits>
+
 namespace bra {
 namespace {
 
 constexpr int kLinRows = 128;     // tokens per workgroup (32 per wavefront)
 constexpr int kLinCols = 64;      // output features per workgroup
-constexpr int kLinKChunk = 256;   // weight columns staged in LDS at a time
 constexpr uint32_t kLinOob = 0x80000000u;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -39,129 +40,200 @@ struct LinArgs {
   void* y[3];           // output groups: columns [g*ng, (g+1)*ng) go to y[g], [T, ng]
   int ng;               // columns per output group
   int T, K, N;
-  int col_tiles, tiles, per_xcd;
+  int col_tiles, row_tiles, per_xcd;
+  int col_groups;       // workgroups per row tile (each takes a share of the feature tiles)
 };
 
 // Y = X W^T + b on the matrix cores, computed as Y^T = W X^T so that a lane
 // ends with 4 consecutive output features of one token (one 8- or 16-byte
-// store).  A workgroup owns 128 tokens x 64 features; wavefront w its tokens
-// 32w .. 32w+31 (two 16-token blocks) against all 64 features (four 16-row
-// blocks of W).  W's 64 x 256 chunk is staged in LDS with its 16-byte chunks
-// XOR-swizzled by row; X is read straight from memory in the operand layout
-// (one 16-byte row segment per lane).  Tiles go to XCDs in contiguous
-// ranges, features fastest, so the workgroups that share X rows share an L2.
-template <bool BF16>
+// store).  A workgroup owns 128 tokens (wavefront w: tokens 32w .. 32w+31, two
+// 16-token blocks) and walks all output features in tiles of 64 (four 16-row
+// blocks of W), K in chunks of KCH columns.  Each (feature tile, chunk) step
+// stages W's 64 x KCH block in LDS (16-byte chunks XOR-swizzled by row, two
+// buffers), the next step's block being loaded into registers while the
+// current one is multiplied.  X is read straight from memory in the operand
+// layout (one 16-byte row segment per lane); when K fits one chunk it is
+// read once and reused for every feature tile.  When there are few row
+// tiles, the feature tiles of a row tile are shared among col_groups
+// workgroups.  Work items go to XCDs in contiguous ranges.  The output tile
+// of a wavefront (32 tokens x 64 features) goes through LDS so that each
+// 128-byte line of a token's features is written by 8 adjacent lanes in one
+// store.
+template <bool BF16, int KCH>
 __global__ __launch_bounds__(kThreads) void linear_kernel(LinArgs a) {
   constexpr int ES = BF16 ? 2 : 4;                 // element bytes
   constexpr int KSTEP = BF16 ? 32 : 4;             // k per MFMA
   constexpr int CE = 16 / ES;                      // elements per 16-byte chunk
+  constexpr int NKS = KCH / KSTEP;                 // k-steps of a full chunk
+  constexpr int XPL = BF16 ? 1 : 8;                // f32: 8 one-float k-steps per group
+  constexpr int CPR = KCH / CE;                    // 16-byte chunks per staged row (full chunk)
+  constexpr int WPT = kLinCols * CPR / kThreads;   // staged chunks per thread
+  constexpr int BUFB = kLinCols * KCH * ES;        // bytes of one staging buffer
+  constexpr int ORB = kLinCols * ES + 16;          // output staging row (padded)
+  using XT = typename std::conditional<BF16, bf16x8, float>::type;
   extern __shared__ __align__(16) unsigned char lds[];
   const int xcd = blockIdx.x % kXcds, loc = blockIdx.x / kXcds;
-  const int id = xcd * a.per_xcd + loc;
-  if (loc >= a.per_xcd || id >= a.tiles) return;   // uniform; no barrier passed yet
-  const int rt = id / a.col_tiles, ct = id - rt * a.col_tiles;
-  const int t0 = rt * kLinRows, n0 = ct * kLinCols;
+  const int item = xcd * a.per_xcd + loc;
+  if (loc >= a.per_xcd || item >= a.row_tiles * a.col_groups) return;   // uniform; no barrier yet
+  const int rt = item / a.col_groups, cg = item - rt * a.col_groups;
+  const int ct_per = (a.col_tiles + a.col_groups - 1) / a.col_groups;
+  const int ct0 = cg * ct_per, ct1 = min(a.col_tiles, ct0 + ct_per);
+  const int t0 = rt * kLinRows;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lq = lane & 15, lg = lane >> 4;
   const auto X = lin_rsrc(a.x, (uint32_t)a.T * a.K * ES);
   const unsigned char* W = (const unsigned char*)a.w;
+  const int nch = (a.K + KCH - 1) / KCH;
+  const int nsteps = (ct1 - ct0) * nch;
+  unsigned char* ost = lds + 2 * BUFB + wave * 32 * ORB;   // this wavefront's output tile
 
-  f32x4 acc[2][4];
+  uint4 wv[WPT];
+  auto load_w = [&](int step) {                    // W block of a step into registers
+    const int ct = ct0 + step / nch, kc = (step % nch) * KCH;
+    const int kn = min(KCH, a.K - kc), cpr = kn / CE;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int kc = 0; kc < a.K; kc += kLinKChunk) {
-    const int kn = min(kLinKChunk, a.K - kc);      // a multiple of 32
-    const int cpr = kn / CE;                        // 16-byte chunks per staged row
-    const int sw = cpr % 8 == 0 ? 7 : 3;            // cpr is a multiple of 4
-    if (kc > 0) __syncthreads();                   // previous chunk fully read
-    // stage W[n0 .. n0+63][kc .. kc+kn): row r, chunk c at chunk c ^ (r & sw)
-    for (int e = tid; e < kLinCols * cpr; e += kThreads) {
+    for (int i = 0; i < WPT; ++i) {
+      const int e = tid + i * kThreads;
       const int r = e / cpr, c = e - r * cpr;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n0 + r < a.N)
-        v = *(const uint4*)(W + ((size_t)(n0 + r) * a.K + kc + c * CE) * ES);
-      *(uint4*)(lds + (r * cpr + (c ^ (r & sw))) * 16) = v;
+      const int n = ct * kLinCols + r;
+      wv[i] = make_uint4(0, 0, 0, 0);
+      if (e < kLinCols * cpr && n < a.N)
+        wv[i] = *(const uint4*)(W + ((size_t)n * a.K + kc + c * CE) * ES);
+    }
+  };
+  XT xo[NKS / XPL][2][XPL];
+  auto load_x = [&](int kc) {                      // this wavefront's X operands of a chunk
+    const int kn = min(KCH, a.K - kc);
+#pragma unroll
+    for (int ks = 0; ks < NKS / XPL; ++ks)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int u = 0; u < XPL; ++u) {
+          const int kk = (ks * XPL + u) * KSTEP;
+          const int t = t0 + 32 * wave + 16 * tb + lq;
+          const bool ok = t < a.T && kk < kn;
+          if constexpr (BF16) {
+            const uint32_t off = ok ? ((uint32_t)t * a.K + kc + kk + 8 * lg) * 2 : kLinOob;
+            xo[ks][tb][u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(X, off, 0, 0));
+          } else {
+            const uint32_t off = ok ? ((uint32_t)t * a.K + kc + kk + lg) * 4 : kLinOob;
+            xo[ks][tb][u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(X, off, 0, 0));
+          }
+        }
+  };
+
+  load_w(0);
+  if (nch == 1) load_x(0);                         // reused by every feature tile
+  f32x4 acc[2][4];
+  for (int step = 0; step < nsteps; ++step) {
+    const int ct = ct0 + step / nch, ch = step % nch, kc = ch * KCH;
+    const int kn = min(KCH, a.K - kc), cpr = kn / CE;
+    const int sw = cpr % 8 == 0 ? 7 : 3;           // cpr is a multiple of 4
+    unsigned char* buf = lds + (step & 1) * BUFB;
+    if (nch > 1) load_x(kc);
+    // staged row r, chunk c at chunk c ^ (r & sw); the barrier of the
+    // previous step ordered every read of this buffer (two steps ago) first
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int e = tid + i * kThreads;
+      const int r = e / cpr, c = e - r * cpr;
+      if (e < kLinCols * cpr) *(uint4*)(buf + (r * cpr + (c ^ (r & sw))) * 16) = wv[i];
     }
     __syncthreads();
-    for (int kk = 0; kk < kn; kk += KSTEP) {
-      // X^T operand: token 16tb + lq of this wavefront, k = kc + kk + (8 | 1) lg
-      if constexpr (BF16) {
-        bf16x8 xb[2];
+    if (step + 1 < nsteps) load_w(step + 1);
+    if (ch == 0) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const int t = t0 + 32 * wave + 16 * tb + lq;
-          const uint32_t off = t < a.T ? ((uint32_t)t * a.K + kc + kk + 8 * lg) * 2 : kLinOob;
-          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(X, off, 0, 0);
-          xb[tb] = __builtin_bit_cast(bf16x8, v);
-        }
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int r = 16 * nb + lq;
-          const int c = (kk >> 3) + lg;            // chunk of k = kk + 8 lg
-          const bf16x8 wa = *(const bf16x8*)(lds + (r * cpr + (c ^ (r & sw))) * 16);
+        for (int nb = 0; nb < 4; ++nb) acc[tb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-            acc[tb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xb[tb], acc[tb][nb], 0, 0, 0);
-        }
-      } else {
-        float xf[2];
+    for (int ks = 0; ks < NKS / XPL; ++ks)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const int t = t0 + 32 * wave + 16 * tb + lq;
-          const uint32_t off = t < a.T ? ((uint32_t)t * a.K + kc + kk + lg) * 4 : kLinOob;
-          xf[tb] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(X, off, 0, 0));
-        }
+      for (int u = 0; u < XPL; ++u) {
+        const int kk = (ks * XPL + u) * KSTEP;
+        if (kk >= kn) continue;                    // uniform
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const int r = 16 * nb + lq;
-          const int k = kk + lg, c = k >> 2;
-          const float wa = *(const float*)(lds + (r * cpr + (c ^ (r & sw))) * 16 + (k & 3) * 4);
+          if constexpr (BF16) {
+            const int c = (kk >> 3) + lg;          // chunk of k = kk + 8 lg
+            const bf16x8 wa = *(const bf16x8*)(buf + (r * cpr + (c ^ (r & sw))) * 16);
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-            acc[tb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(wa, xf[tb], acc[tb][nb], 0, 0, 0);
+            for (int tb = 0; tb < 2; ++tb)
+              acc[tb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xo[ks][tb][u], acc[tb][nb], 0, 0, 0);
+          } else {
+            const int k = kk + lg, c = k >> 2;
+            const float wa = *(const float*)(buf + (r * cpr + (c ^ (r & sw))) * 16 + (k & 3) * 4);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+              acc[tb][nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(wa, xo[ks][tb][u], acc[tb][nb], 0, 0, 0);
+          }
+        }
+      }
+    if (ch != nch - 1) continue;
+    // bias, one rounding, then the tile through this wavefront's LDS rows:
+    // lane (lq, lg) holds Y[token 16tb + lq][features 16nb + 4lg + 0..3]
+    const int n0 = ct * kLinCols;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int n = n0 + 16 * nb + 4 * lg;
+      float bb[4] = {0.f, 0.f, 0.f, 0.f};
+      if (a.b && n < a.N) {                        // N % 4 == 0: all four or none
+        const float4 bv = *(const float4*)(a.b + n);
+        bb[0] = bv.x; bb[1] = bv.y; bb[2] = bv.z; bb[3] = bv.w;
+      }
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const f32x4 v = acc[tb][nb];
+        unsigned char* d = ost + (16 * tb + lq) * ORB + (16 * nb + 4 * lg) * ES;
+        if constexpr (BF16) {
+          *(uint2*)d = make_uint2(pack_bf16x2(v[0] + bb[0], v[1] + bb[1]),
+                                  pack_bf16x2(v[2] + bb[2], v[3] + bb[3]));
+        } else {
+          *(float4*)d = make_float4(v[0] + bb[0], v[1] + bb[1], v[2] + bb[2], v[3] + bb[3]);
         }
       }
     }
-  }
-
-  // lane (lq, lg) holds Y[token 16tb + lq][features 16nb + 4lg + 0..3]
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    // 16-byte chunks: kLinCols * ES / 16 per token row, 64 lanes per store
+    constexpr int CPRO = kLinCols * ES / 16;
+    constexpr int TPS = 64 / CPRO;                 // token rows per store
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int n = n0 + 16 * nb + 4 * lg;
-    const bool nok = n < a.N;                      // N % 4 == 0: all four or none
-    const int g = nok ? n / a.ng : 0, col = n - g * a.ng;
-    float bb[4] = {0.f, 0.f, 0.f, 0.f};
-    if (a.b && nok) {
-      const float4 bv = *(const float4*)(a.b + n);
-      bb[0] = bv.x; bb[1] = bv.y; bb[2] = bv.z; bb[3] = bv.w;
-    }
-    const auto Y = lin_rsrc(a.y[g], (uint32_t)a.T * a.ng * ES);
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int t = t0 + 32 * wave + 16 * tb + lq;
-      const uint32_t off =
-          (nok && t < a.T) ? ((uint32_t)t * a.ng + col) * ES : kLinOob;
-      const f32x4 v = acc[tb][nb];
-      if constexpr (BF16) {
-        const u32x2 p = {pack_bf16x2(v[0] + bb[0], v[1] + bb[1]),
-                         pack_bf16x2(v[2] + bb[2], v[3] + bb[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(p, Y, off, 0, 0);
-      } else {
-        const u32x4 p = {__float_as_uint(v[0] + bb[0]), __float_as_uint(v[1] + bb[1]),
-                         __float_as_uint(v[2] + bb[2]), __float_as_uint(v[3] + bb[3])};
+    for (int i = 0; i < 32 / TPS; ++i) {
+      const int tr = TPS * i + lane / CPRO, ck = lane % CPRO;
+      const uint4 v = *(const uint4*)(ost + tr * ORB + ck * 16);
+      const int t = t0 + 32 * wave + tr, n = n0 + ck * CE;
+      const bool ok = n < a.N && t < a.T;
+      // a chunk lies in one group (ng is a multiple of 8 or the chunk is the
+      // last, partial one of a single group: N % 8 == 4 in bf16)
+      const int g = ok ? n / a.ng : 0, col = n - g * a.ng;
+      const auto Y = lin_rsrc(a.y[g], (uint32_t)a.T * a.ng * ES);
+      const uint32_t off = ok ? ((uint32_t)t * a.ng + col) * ES : kLinOob;
+      if (n + CE <= a.N) {
+        const u32x4 p = {v.x, v.y, v.z, v.w};
         __builtin_amdgcn_raw_buffer_store_b128(p, Y, off, 0, 0);
+      } else {                                     // 4 features left (bf16 only)
+        const u32x2 p = {v.x, v.y};
+        __builtin_amdgcn_raw_buffer_store_b64(p, Y, off, 0, 0);
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // tile read before the next one
   }
 }
 
 // qm = xm Wq^T + bq and km = xm Wk^T + bk in float64 (Wq, Wk: rows 0..C-1
-// and C..2C-1 of w_qkv), one 16 x 16 output tile per wavefront on
-// v_mfma_f64_16x16x4f64.  Each lane feeds 4 consecutive channels as the k
-// slots of 4 successive MFMAs (the same permutation on both operands).
+// and C..2C-1 of w_qkv) on v_mfma_f64_16x16x4f64.  A workgroup owns one
+// 16-row tile of the means and 16 column tiles of 16 (of the 2C outputs);
+// wavefront w takes column tiles w, w+4, w+8, w+12, so each load of a row
+// segment of xm feeds four independent accumulators.  Each lane feeds 4
+// consecutive channels as the k slots of 4 successive MFMAs (the same
+// permutation on both operands); the next 16-channel step's operands are
+// loaded while the current one is multiplied.
+constexpr int kMeansTilesPerWave = 4;
+constexpr int kMeansTilesPerBlock = kMeansTilesPerWave * kWaves;
+
 struct MeansArgs {
   const double* xm;     // [rows, C]
   const void* w;        // w_qkv [3C, C]
@@ -169,44 +241,73 @@ struct MeansArgs {
   double* qm;           // [rows, C]
   double* km;           // [rows, C]
   int rows, C;
-  int col_tiles, tiles;
+  int col_tiles, col_blocks;
 };
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void means_proj_kernel(MeansArgs a) {
-  const int tile = blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (tile >= a.tiles) return;                    // no barrier in this kernel
-  const int lane = threadIdx.x & 63, l16 = lane & 15, lk = lane >> 4;
-  const int rt = tile / a.col_tiles, ct = tile - rt * a.col_tiles;
-  const int r0 = rt * 16, n0 = ct * 16;           // n over the 2C columns (q then k)
+  constexpr int NT = kMeansTilesPerWave;
+  const int rt = blockIdx.x / a.col_blocks, cbk = blockIdx.x - rt * a.col_blocks;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, lk = lane >> 4;
+  const int r0 = rt * 16;
   const int C = a.C;
   const double* xp = a.xm + (size_t)min(r0 + l16, a.rows - 1) * C + 4 * lk;
-  const int wn = n0 + l16;                         // weight row (< 2C: C % 16 == 0)
-  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-  for (int c = 0; c < C; c += 16) {
-    const double4 xa = *(const double4*)(xp + c);
-    double wb[4];
-    if constexpr (BF16) {
-      const uint2 u = *(const uint2*)((const uint16_t*)a.w + (size_t)wn * C + c + 4 * lk);
-      wb[0] = bf16_lo(u.x); wb[1] = bf16_hi(u.x); wb[2] = bf16_lo(u.y); wb[3] = bf16_hi(u.y);
-    } else {
-      const float4 u = *(const float4*)((const float*)a.w + (size_t)wn * C + c + 4 * lk);
-      wb[0] = u.x; wb[1] = u.y; wb[2] = u.z; wb[3] = u.w;
+  int wn[NT];                                       // weight row of each tile (clamped)
+  bool tok[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int ct = cbk * kMeansTilesPerBlock + wave + kWaves * j;
+    tok[j] = ct < a.col_tiles;
+    wn[j] = tok[j] ? ct * 16 + l16 : 0;
+  }
+  double4 xa;
+  double wb[NT][4];
+  auto load = [&](int c) {
+    xa = *(const double4*)(xp + c);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      if constexpr (BF16) {
+        const uint2 w = *(const uint2*)((const uint16_t*)a.w + (size_t)wn[j] * C + c + 4 * lk);
+        wb[j][0] = bf16_lo(w.x); wb[j][1] = bf16_hi(w.x); wb[j][2] = bf16_lo(w.y); wb[j][3] = bf16_hi(w.y);
+      } else {
+        const float4 w = *(const float4*)((const float*)a.w + (size_t)wn[j] * C + c + 4 * lk);
+        wb[j][0] = w.x; wb[j][1] = w.y; wb[j][2] = w.z; wb[j][3] = w.w;
+      }
     }
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xa.x, wb[0], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xa.y, wb[1], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xa.z, wb[2], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xa.w, wb[3], acc, 0, 0, 0);
+  };
+  f64x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  load(0);
+  for (int c = 0; c < C; c += 16) {
+    const double4 xc = xa;
+    double wc[NT][4];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wc[j][e] = wb[j][e];
+    if (c + 16 < C) load(c + 16);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(xc.x, wc[j][0], acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(xc.y, wc[j][1], acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(xc.z, wc[j][2], acc[j], 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(xc.w, wc[j][3], acc[j], 0, 0, 0);
+    }
   }
   // D layout (f64 16x16x4): lane holds column l16 of the tile, rows lk + 4i
-  const int n = n0 + l16;
-  const double bias = a.b ? (double)a.b[n] : 0.0;
-  double* dst = n < C ? a.qm : a.km;
-  const int col = n < C ? n : n - C;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r0 + lk + 4 * i;
-    if (r < a.rows) dst[(size_t)r * C + col] = acc[i] + bias;
+  for (int j = 0; j < NT; ++j) {
+    if (!tok[j]) continue;
+    const int n = wn[j];
+    const double bias = a.b ? (double)a.b[n] : 0.0;
+    double* dst = n < C ? a.qm : a.km;
+    const int col = n < C ? n : n - C;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = r0 + lk + 4 * i;
+      if (r < a.rows) dst[(size_t)r * C + col] = acc[j][i] + bias;
+    }
   }
 }
 
@@ -215,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void means_proj_kernel(MeansArgs a) {
 hipError_t launch_linear(const void* x, int T, int K, const void* w, const float* b, int N,
                          void* const* y, int groups, bool bf16, hipStream_t st) {
   if (T <= 0 || K <= 0 || N <= 0 || K % 32 || N % 4 || groups < 1 || groups > 3 ||
-      N % groups || (N / groups) % 4)
+      N % groups || (N / groups) % (groups > 1 ? 8 : 4))
     return hipErrorInvalidValue;
   const int es = bf16 ? 2 : 4;
   // buffer offsets are 32-bit: every operand below 2 GiB
@@ -227,14 +328,26 @@ hipError_t launch_linear(const void* x, int T, int K, const void* w, const float
   a.ng = N / groups;
   a.T = T; a.K = K; a.N = N;
   a.col_tiles = (N + kLinCols - 1) / kLinCols;
-  a.tiles = ((T + kLinRows - 1) / kLinRows) * a.col_tiles;
-  a.per_xcd = (a.tiles + kXcds - 1) / kXcds;
-  const size_t lds = (size_t)kLinCols * (K < kLinKChunk ? K : kLinKChunk) * es;
+  a.row_tiles = (T + kLinRows - 1) / kLinRows;
+  // few row tiles: share each row tile's feature tiles among workgroups
+  a.col_groups = (512 + a.row_tiles - 1) / a.row_tiles;
+  if (a.col_groups > a.col_tiles) a.col_groups = a.col_tiles;
+  if (a.col_groups < 1) a.col_groups = 1;
+  a.col_groups = (a.col_tiles + (a.col_tiles + a.col_groups - 1) / a.col_groups - 1) /
+                 ((a.col_tiles + a.col_groups - 1) / a.col_groups);   // no empty group
+  a.per_xcd = (a.row_tiles * a.col_groups + kXcds - 1) / kXcds;
   const dim3 grid((unsigned)(a.per_xcd * kXcds));
-  if (bf16)
-    hipLaunchKernelGGL(linear_kernel<true>, grid, dim3(kThreads), lds, st, a);
+  // K chunk: all of K up to 256 in bf16 (X read once), 64 for float32
+  const int kch = !bf16 ? 64 : K <= 64 ? 64 : K <= 128 ? 128 : 256;
+  const size_t lds = (size_t)2 * kLinCols * kch * es + (size_t)kWaves * 32 * (kLinCols * es + 16);
+  if (bf16 && kch == 64)
+    hipLaunchKernelGGL((linear_kernel<true, 64>), grid, dim3(kThreads), lds, st, a);
+  else if (bf16 && kch == 128)
+    hipLaunchKernelGGL((linear_kernel<true, 128>), grid, dim3(kThreads), lds, st, a);
+  else if (bf16)
+    hipLaunchKernelGGL((linear_kernel<true, 256>), grid, dim3(kThreads), lds, st, a);
   else
-    hipLaunchKernelGGL(linear_kernel<false>, grid, dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((linear_kernel<false, 64>), grid, dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
 
@@ -246,8 +359,8 @@ hipError_t launch_means_proj(const double* xm, int rows, int C, const void* w_qk
   a.xm = xm; a.w = w_qkv; a.b = b_qkv; a.qm = qm; a.km = km;
   a.rows = rows; a.C = C;
   a.col_tiles = 2 * C / 16;
-  a.tiles = ((rows + 15) / 16) * a.col_tiles;
-  const dim3 grid((unsigned)((a.tiles + kWaves - 1) / kWaves));
+  a.col_blocks = (a.col_tiles + kMeansTilesPerBlock - 1) / kMeansTilesPerBlock;
+  const dim3 grid((unsigned)(((rows + 15) / 16) * a.col_blocks));
   if (bf16)
     hipLaunchKernelGGL(means_proj_kernel<true>, grid, dim3(kThreads), 0, st, a);
   else
