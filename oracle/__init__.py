@@ -5,7 +5,10 @@ leg may import it.  It shares no code with the HIP library.
 """
 
 from .bra_oracle import (  # noqa: F401
+    block_forward,
     bra_forward,
+    gelu,
+    layer_norm,
     lepe,
     linear,
     module_forward,

@@ -75,10 +75,33 @@ Readings for the module around the method (``module_forward``):
       projection of x's region means, since a region mean commutes with a
       per-token linear map).
 
+Readings for the BiFormer block around the module (``block_forward``):
+
+  B1  Structure (p3 §3.1 BiFormerBlock, pre-norm residuals; p1 §4 3x3 conv
+      position encoding and a two-layer MLP of ratio 3):
+        x1 = x + dwconv3x3(x) + b_pos
+        x2 = x1 + module(LN1(x1))
+        x3 = x2 + fc2(GELU(fc1(LN2(x2))))
+      p3's ConvFFN is not used: p1 (the more detailed page on the block's
+      parts) gives a plain two-layer MLP, and the 3x3 conv is the position
+      encoding before the attention.
+  B2  The position encoding is a depthwise 3x3 cross-correlation (groups = C,
+      zero padding 1) with bias, like the LePE term.
+  B3  LayerNorm over the C channels of each token, biased variance, eps 1e-5
+      (PyTorch nn.LayerNorm, as p3's block uses), with per-channel scale and
+      shift.
+  B4  The MLP's activation is GELU in its exact (erf) form; the pages name no
+      activation, and GELU is the usual one of a transformer MLP.
+  B5  Storage (as M4): x1, LN1(x1), the module's stored values, x2,
+      LN2(x2), the hidden GELU output and x3 are layer outputs, stored per
+      ``storage``.
+
 Parity pins for every function live in ``tests/test_oracle_pins.py``.
 """
 
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -95,6 +118,9 @@ __all__ = [
     "linear",
     "round_storage",
     "module_forward",
+    "layer_norm",
+    "gelu",
+    "block_forward",
 ]
 
 
@@ -343,3 +369,48 @@ def module_forward(x, w_qkv, b_qkv, heads: int, S: int, topk: int, lepe_w=None,
         return {"q": q, "k": k, "v": v, "q_r": q_r, "k_r": k_r, "A": A, "idx": idx, "O": O,
                 "L": L, "y": y, "out": out}
     return out, idx
+
+
+def layer_norm(X, gamma, beta, eps: float = 1e-5) -> np.ndarray:
+    """LayerNorm over the last axis (reading B3): (X - mean) / sqrt(var + eps)
+    * gamma + beta, with the biased variance of the channels."""
+    X = _f64(X)
+    mu = X.mean(axis=-1, keepdims=True)
+    var = ((X - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (X - mu) / np.sqrt(var + eps) * _f64(gamma) + _f64(beta)
+
+
+def gelu(X) -> np.ndarray:
+    """GELU, exact form (reading B4): x * Phi(x) = x / 2 * (1 + erf(x / sqrt 2))."""
+    X = _f64(X)
+    erf = np.vectorize(math.erf, otypes=[np.float64])
+    return 0.5 * X * (1.0 + erf(X / math.sqrt(2.0)))
+
+
+def block_forward(x, p: dict, heads: int, S: int, topk: int, route_scale: float | None = None,
+                  attn_scale: float | None = None, storage: str | None = None,
+                  return_parts: bool = False):
+    """One BiFormer block (readings B1-B5) around the BRA module.
+
+    p holds the parameters: pos_w [C, 3, 3], pos_b [C]; ln1_g, ln1_b [C];
+    w_qkv [3C, C], b_qkv [3C]; lepe_w [C, ks, ks], lepe_b [C] or None; w_out
+    [C, C], b_out [C]; ln2_g, ln2_b [C]; w_fc1 [3C, C], b_fc1 [3C]; w_fc2
+    [C, 3C], b_fc2 [C].  Returns (out, idx) or, with return_parts, every
+    stored intermediate (x1, n1, the module's parts under "mod", x2, n2, h,
+    out).
+    """
+    st = lambda t: round_storage(t, storage)
+    x = _f64(x)
+    x1 = st(x + lepe(x, p["pos_w"], p["pos_b"]))
+    n1 = st(layer_norm(x1, p["ln1_g"], p["ln1_b"]))
+    mod = module_forward(n1, p["w_qkv"], p["b_qkv"], heads, S, topk, p["lepe_w"], p["lepe_b"],
+                         p["w_out"], p["b_out"], route_scale, attn_scale, storage,
+                         return_parts=True)
+    x2 = st(x1 + mod["out"])
+    n2 = st(layer_norm(x2, p["ln2_g"], p["ln2_b"]))
+    h = st(gelu(linear(n2, p["w_fc1"], p["b_fc1"])))
+    out = st(x2 + linear(h, p["w_fc2"], p["b_fc2"]))
+    if return_parts:
+        return {"x1": x1, "n1": n1, "mod": mod, "x2": x2, "n2": n2, "h": h, "out": out,
+                "idx": mod["idx"]}
+    return out, mod["idx"]

@@ -463,6 +463,70 @@ def pin_module_storage():
     assert np.array_equal(c["y"], O.round_storage(a["y"], "bf16"))
 
 
+# --------------------------------------------------------------------------
+# the BiFormer block (readings B1-B5)
+
+def block_params(C, ks=5, seed=40):
+    """Random block parameters (float64) for the pins."""
+    r = _rng(seed)
+    n = lambda *shape, s=1.0: r.normal(0.0, s, size=shape)
+    return {"pos_w": n(C, 3, 3, s=0.3), "pos_b": n(C, s=0.1),
+            "ln1_g": 1.0 + n(C, s=0.2), "ln1_b": n(C, s=0.2),
+            "w_qkv": n(3 * C, C, s=C ** -0.5), "b_qkv": n(3 * C, s=0.1),
+            "lepe_w": n(C, ks, ks, s=0.1), "lepe_b": n(C, s=0.1),
+            "w_out": n(C, C, s=C ** -0.5), "b_out": n(C, s=0.1),
+            "ln2_g": 1.0 + n(C, s=0.2), "ln2_b": n(C, s=0.2),
+            "w_fc1": n(3 * C, C, s=C ** -0.5), "b_fc1": n(3 * C, s=0.1),
+            "w_fc2": n(C, 3 * C, s=(3 * C) ** -0.5), "b_fc2": n(C, s=0.1)}
+
+
+def pin_layer_norm_torch():
+    """LayerNorm equals torch.nn.functional.layer_norm (eps 1e-5, affine) in
+    float64 (reading B3)."""
+    import torch
+    import torch.nn.functional as F
+    X = _rng(41).normal(size=(3, 5, 4, 12)) * 3.0 + 1.5
+    g, b = _rng(42).normal(size=12), _rng(43).normal(size=12)
+    ref = F.layer_norm(torch.from_numpy(X), (12,), torch.from_numpy(g), torch.from_numpy(b),
+                       eps=1e-5).numpy()
+    _close(O.layer_norm(X, g, b), ref, 1e-13, "layer_norm")
+
+
+def pin_gelu_torch():
+    """GELU equals torch's exact (erf) GELU in float64 (reading B4)."""
+    import torch
+    import torch.nn.functional as F
+    X = np.concatenate([_rng(44).normal(size=5000) * 3, np.array([0.0, -0.0, 8.0, -8.0, 1e-8])])
+    ref = F.gelu(torch.from_numpy(X), approximate="none").numpy()
+    _close(O.gelu(X), ref, 1e-15, "gelu")
+
+
+def pin_block_torch():
+    """The block around the module equals the composition of torch's conv2d
+    (groups = C, padding 1), layer_norm, linear and gelu with the pinned
+    module (reading B1), in float64."""
+    import torch
+    import torch.nn.functional as F
+    B, H, W, C, heads, S, topk = 1, 8, 8, 8, 2, 4, 3
+    C = 8
+    x = _rng(45).normal(size=(B, H, W, C))
+    p = block_params(C, ks=3)
+    out, idx = O.block_forward(x, p, 2, S, topk)
+    T = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    xt = T(x).permute(0, 3, 1, 2)
+    x1 = (xt + F.conv2d(xt, T(p["pos_w"])[:, None], T(p["pos_b"]), padding=1, groups=C))
+    x1 = x1.permute(0, 2, 3, 1)
+    n1 = F.layer_norm(x1, (C,), T(p["ln1_g"]), T(p["ln1_b"]), eps=1e-5)
+    mod, midx = O.module_forward(n1.numpy(), p["w_qkv"], p["b_qkv"], 2, S, topk, p["lepe_w"],
+                                 p["lepe_b"], p["w_out"], p["b_out"])
+    x2 = x1 + T(mod)
+    n2 = F.layer_norm(x2, (C,), T(p["ln2_g"]), T(p["ln2_b"]), eps=1e-5)
+    h = F.gelu(F.linear(n2, T(p["w_fc1"]), T(p["b_fc1"])), approximate="none")
+    ref = x2 + F.linear(h, T(p["w_fc2"]), T(p["b_fc2"]))
+    assert np.array_equal(idx, midx)
+    _close(out, ref.numpy(), 1e-12, "block")
+
+
 ALL_PINS = [
     pin_golden, pin_partition_layout, pin_pool_avgpool, pin_affinity_orientation,
     pin_topk_bruteforce, pin_scale_invariance, pin_masked_dense,
@@ -470,4 +534,5 @@ ALL_PINS = [
     pin_sdpa_masked, pin_lepe_conv2d, pin_invariants, pin_route_ties,
     pin_module_golden, pin_linear_torch, pin_module_reduces_to_bra,
     pin_pool_commutes_with_projection, pin_round_storage_torch, pin_module_storage,
+    pin_layer_norm_torch, pin_gelu_torch, pin_block_torch,
 ]

@@ -10,7 +10,8 @@ from oracle_pins import ALL_PINS
 
 _orig = {name: getattr(O, name) for name in
          ("region_mean", "region_affinity", "topk_route", "routed_attention", "lepe",
-          "region_tokens", "linear", "module_forward", "round_storage")}
+          "region_tokens", "linear", "module_forward", "round_storage", "layer_norm", "gelu",
+          "block_forward")}
 
 
 def _mean_as_sum(X, S):
@@ -202,6 +203,46 @@ def _module_round_before_routing(x, w_qkv, b_qkv, heads, S, topk, lepe_w=None, l
     return out, p["idx"]
 
 
+def _ln_unbiased(X, gamma, beta, eps=1e-5):
+    X = np.asarray(X, dtype=np.float64)
+    mu = X.mean(axis=-1, keepdims=True)
+    var = ((X - mu) ** 2).sum(axis=-1, keepdims=True) / (X.shape[-1] - 1)
+    return (X - mu) / np.sqrt(var + eps) * gamma + beta
+
+
+def _ln_no_shift(X, gamma, beta, eps=1e-5):
+    return _orig["layer_norm"](X, gamma, np.zeros_like(np.asarray(beta)), eps)
+
+
+def _gelu_tanh(X):
+    X = np.asarray(X, dtype=np.float64)
+    return 0.5 * X * (1 + np.tanh(np.sqrt(2 / np.pi) * (X + 0.044715 * X ** 3)))
+
+
+def _block_no_pos_residual(x, p, heads, S, topk, route_scale=None, attn_scale=None,
+                           storage=None, return_parts=False):
+    x = np.asarray(x, dtype=np.float64)
+    q = dict(p)
+    # x1 = conv(x) + b only: subtract x again through a centre tap of -1
+    w = np.array(p["pos_w"], dtype=np.float64)
+    w[:, 1, 1] -= 1.0
+    q["pos_w"] = w
+    return _orig["block_forward"](x, q, heads, S, topk, route_scale, attn_scale, storage,
+                                  return_parts)
+
+
+def _block_post_norm(x, p, heads, S, topk, route_scale=None, attn_scale=None, storage=None,
+                     return_parts=False):
+    x = np.asarray(x, dtype=np.float64)
+    x1 = x + O.lepe(x, p["pos_w"], p["pos_b"])
+    mod, idx = O.module_forward(x1, p["w_qkv"], p["b_qkv"], heads, S, topk, p["lepe_w"],
+                                p["lepe_b"], p["w_out"], p["b_out"], route_scale, attn_scale)
+    x2 = O.layer_norm(x1 + mod, p["ln1_g"], p["ln1_b"])
+    out = O.layer_norm(x2 + O.linear(O.gelu(O.linear(x2, p["w_fc1"], p["b_fc1"])), p["w_fc2"],
+                                     p["b_fc2"]), p["ln2_g"], p["ln2_b"])
+    return (dict(out=out, idx=idx) if return_parts else (out, idx))
+
+
 MUTANTS = {
     "region_mean": [_mean_as_sum, _mean_column_major],
     "region_affinity": [_affinity_transposed],
@@ -214,6 +255,9 @@ MUTANTS = {
     "module_forward": [_module_qk_swapped, _module_lepe_on_x, _module_out_before_lepe,
                        _module_round_before_routing],
     "round_storage": [_round_truncating, _round_ties_away],
+    "layer_norm": [_ln_unbiased, _ln_no_shift],
+    "gelu": [_gelu_tanh],
+    "block_forward": [_block_no_pos_residual, _block_post_norm],
 }
 CASES = [(name, m) for name, ms in MUTANTS.items() for m in ms]
 

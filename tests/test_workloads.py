@@ -5,6 +5,7 @@ import torch
 
 from vision_transformer_dynamic_region_amd.workloads import (WORKLOADS, bf16_bits,
                                                               bf16_round, make_inputs,
+                                                              make_block_inputs,
                                                               make_module_inputs)
 
 
@@ -65,3 +66,17 @@ def test_module_inputs_seeded_and_rounded():
         assert np.array_equal(a[n], bf16_round(a[n]))
     # projections keep unit scale: w ~ N(0, C^-1/2)
     assert abs(float(a["w_qkv"].std()) * C ** 0.5 - 1.0) < 0.05
+
+
+def test_block_inputs_seeded_and_shaped():
+    wl = WORKLOADS["st1"].scaled(B=1)
+    a, b = make_block_inputs(wl), make_block_inputs(wl)
+    C = wl.C
+    shapes = {"pos_w": (C, 3, 3), "pos_b": (C,), "ln1_g": (C,), "ln2_b": (C,),
+              "w_fc1": (3 * C, C), "b_fc1": (3 * C,), "w_fc2": (C, 3 * C), "b_fc2": (C,)}
+    for n, shp in shapes.items():
+        assert a[n].shape == shp and a[n].dtype == np.float32
+        assert np.array_equal(a[n], b[n])
+    for n in ("w_fc1", "w_fc2"):
+        assert np.array_equal(a[n], bf16_round(a[n]))
+    assert np.array_equal(a["x"], make_module_inputs(wl)["x"])

@@ -23,6 +23,14 @@ offset, seed + 12), w_qkv ~ N(0, C**-0.5) [3C, C] (seed + 8), b_qkv ~ N(0, 0.1)
 [3C] (seed + 9), w_out ~ N(0, C**-0.5) [C, C] (seed + 10), b_out ~ N(0, 0.1)
 [C] (seed + 11) and the LePE weights as above.  x and the two weights are
 rounded to bf16 for bf16 workloads; biases stay float32.
+
+The BiFormer block adds (same seed base): the 3x3 position-encoding conv
+pos_w ~ N(0, 0.1) [C, 3, 3] (seed + 13) and pos_b ~ N(0, 0.02) (seed + 14),
+LayerNorm scales 1 + N(0, 0.1) and shifts N(0, 0.1) (seeds + 15 .. + 18), the
+MLP's fc1 ~ N(0, C**-0.5) [3C, C] (seed + 19) with bias N(0, 0.1) (seed + 20)
+and fc2 ~ N(0, (3C)**-0.5) [C, 3C] (seed + 21) with bias N(0, 0.1) (seed + 22);
+conv and LayerNorm parameters and biases are float32, fc weights follow the
+workload dtype.
 """
 
 from __future__ import annotations
@@ -32,7 +40,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "bf16_round", "bf16_bits", "make_inputs",
-           "make_module_inputs", "workload"]
+           "make_module_inputs", "make_block_inputs", "workload"]
 
 
 @dataclass(frozen=True)
@@ -175,4 +183,29 @@ def make_module_inputs(wl: Workload, seed_base: int | None = None):
         "w": _normal(base + 3, (C, wl.lepe_ks, wl.lepe_ks), 0.02).astype(np.float32),
         "bias": None,
     }
+    return out
+
+
+def make_block_inputs(wl: Workload, seed_base: int | None = None):
+    """Draw the BiFormer block's input and parameters for a workload: the
+    module's (x, w_qkv, b_qkv, w_out, b_out, LePE w as ``lepe_w``) plus
+    pos_w, pos_b, ln1_g, ln1_b, ln2_g, ln2_b, w_fc1, b_fc1, w_fc2, b_fc2."""
+    base = 1000 * wl.index if seed_base is None else seed_base
+    C = wl.C
+    m = make_module_inputs(wl, seed_base)
+    rnd = (lambda a: bf16_round(a.astype(np.float32))) if wl.dtype == "bf16" else \
+        (lambda a: a.astype(np.float32))
+    f32 = lambda a: a.astype(np.float32)
+    out = {"x": m["x"], "w_qkv": m["w_qkv"], "b_qkv": m["b_qkv"], "w_out": m["w_out"],
+           "b_out": m["b_out"], "lepe_w": m["w"], "lepe_b": None,
+           "pos_w": f32(_normal(base + 13, (C, 3, 3), 0.1)),
+           "pos_b": f32(_normal(base + 14, (C,), 0.02)),
+           "ln1_g": f32(1.0 + _normal(base + 15, (C,), 0.1)),
+           "ln1_b": f32(_normal(base + 16, (C,), 0.1)),
+           "ln2_g": f32(1.0 + _normal(base + 17, (C,), 0.1)),
+           "ln2_b": f32(_normal(base + 18, (C,), 0.1)),
+           "w_fc1": rnd(_normal(base + 19, (3 * C, C), C ** -0.5)),
+           "b_fc1": f32(_normal(base + 20, (3 * C,), 0.1)),
+           "w_fc2": rnd(_normal(base + 21, (C, 3 * C), (3 * C) ** -0.5)),
+           "b_fc2": f32(_normal(base + 22, (C,), 0.1))}
     return out
