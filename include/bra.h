@@ -119,15 +119,18 @@ bra_status bra_lepe(const void* v, const float* w, const float* b, int ks,
  * are float32, 16-byte aligned, or NULL.
  * ------------------------------------------------------------------------ */
 
-/* Per-token linear map y = x w^T + b on the matrix cores (float32
+/* Per-token linear map y = act(x w^T + b) + r on the matrix cores (float32
  * accumulation, one rounding to dtype).
  *   x   [rows, K] dtype, device;  w [N, K] dtype, device;  b float32 [N] or
  *       NULL;  y out: [rows, N] dtype, device, not overlapping x or w.
+ *   act 0: none, 1: GELU in its exact (erf) form (the block's MLP).
+ *   r   [rows, N] dtype, device, or NULL: a residual added after act (the
+ *       block's residual connections); may be y itself; not with act 1.
  *   K must be a multiple of 32 and N of 4; every operand must stay below
  *   2 GiB (BRA_E_UNSUPPORTED otherwise). */
 bra_status bra_linear(const void* x, int rows, int K, const void* w,
-                      const float* b, int N, bra_dtype dtype, void* y,
-                      void* stream);
+                      const float* b, int N, int act, const void* r,
+                      bra_dtype dtype, void* y, void* stream);
 
 /* Bytes of workspace bra_module_forward needs for these sizes; with_out_proj
  * non-zero when an output projection will be passed.  Layout, each part
@@ -160,6 +163,72 @@ bra_status bra_module_forward(const void* x, int B, int H, int W, int C,
                               int lepe_ks, const void* w_out,
                               const float* b_out, void* out, int32_t* idx,
                               void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The BiFormer block around the module (p3 §3.1: pre-norm residual blocks,
+ * x + bra(norm1(x)), x + ffn(norm2(x)); p1 §4: a 3x3 convolution as the
+ * position encoding and a two-layer MLP of ratio 3):
+ *   x1  = x + dwconv3x3(x) + pos_b        (depthwise, zero padding 1)
+ *   x2  = x1 + module(LN1(x1))             (bra_module_forward, with w_out)
+ *   out = x2 + fc2(GELU(fc1(LN2(x2))))     (fc1 [3C, C], fc2 [C, 3C])
+ * LayerNorm: over C, biased variance, eps 1e-5, per-channel scale/shift.
+ * GELU: exact (erf) form.  Every layer output above is stored in dtype.
+ * ------------------------------------------------------------------------ */
+
+/* out = x + b + depthwise 3x3 cross-correlation of x over each image (zero
+ * padding 1): the block's position encoding (p1 §4).
+ *   x, out [B,H,W,C] dtype, device, not overlapping; w float32 [C, 3, 3];
+ *   b float32 [C] or NULL; C a multiple of 8 (bf16) or 4 (f32). */
+bra_status bra_pos_conv(const void* x, const float* w, const float* b, int B,
+                        int H, int W, int C, bra_dtype dtype, void* out,
+                        void* stream);
+
+/* LayerNorm of `rows` rows of C channels: (x - mean) / sqrt(var + eps) *
+ * gamma + beta, float32 statistics, one rounding to dtype.
+ *   x, y [rows, C] dtype, device (y may be x); gamma, beta float32 [C].
+ *   C must be a multiple of 8 (bf16) or 4 (f32) whose 16-byte groups split
+ *   into at most 4 per lane (every multiple of 32 up to 512 does). */
+bra_status bra_layer_norm(const void* x, int rows, int C, const float* gamma,
+                          const float* beta, float eps, bra_dtype dtype,
+                          void* y, void* stream);
+
+/* Parameters of one block: device pointers, float32 unless noted; weights
+ * in the PyTorch Linear / depthwise Conv2d layouts, 16-byte aligned. */
+typedef struct {
+  const float* pos_w;   /* [C, 3, 3] position conv                         */
+  const float* pos_b;   /* [C] or NULL                                      */
+  const float* ln1_g;   /* [C]                                              */
+  const float* ln1_b;   /* [C]                                              */
+  const void* w_qkv;    /* [3C, C] dtype                                    */
+  const float* b_qkv;   /* [3C] or NULL                                     */
+  const float* lepe_w;  /* [C, ks, ks] or NULL                              */
+  const float* lepe_b;  /* [C] or NULL                                      */
+  int lepe_ks;          /* odd, 1..7                                        */
+  const void* w_out;    /* [C, C] dtype (required)                          */
+  const float* b_out;   /* [C] or NULL                                      */
+  const float* ln2_g;   /* [C]                                              */
+  const float* ln2_b;   /* [C]                                              */
+  const void* w_fc1;    /* [3C, C] dtype                                    */
+  const float* b_fc1;   /* [3C] or NULL                                     */
+  const void* w_fc2;    /* [C, 3C] dtype                                    */
+  const float* b_fc2;   /* [C] or NULL                                      */
+} bra_block_params;
+
+/* Bytes of workspace bra_block_forward needs: x1, LN1(x1), x2, LN2(x2) as
+ * [B,H,W,C] dtype each (256-byte aligned), then a module workspace with
+ * output projection (bra_module_workspace_bytes(..., 1)), whose Q/K/V space
+ * later holds the MLP's [B,H,W,3C] hidden tensor.  0 for invalid sizes. */
+size_t bra_block_workspace_bytes(int B, int H, int W, int C, int S,
+                                 bra_dtype dtype);
+
+/* One BiFormer block.  x, out [B,H,W,C] dtype, device (out may be x);
+ * idx out: int32 [B, S*S, topk]; ws as above, not overlapping x, out, idx.
+ * Other arguments and limits as in bra_module_forward. */
+bra_status bra_block_forward(const void* x, int B, int H, int W, int C,
+                             int heads, int S, int topk, bra_dtype dtype,
+                             const bra_block_params* params, float route_scale,
+                             float attn_scale, void* out, int32_t* idx,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* bra_strerror(int status);

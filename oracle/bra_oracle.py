@@ -382,8 +382,8 @@ def layer_norm(X, gamma, beta, eps: float = 1e-5) -> np.ndarray:
 
 def gelu(X) -> np.ndarray:
     """GELU, exact form (reading B4): x * Phi(x) = x / 2 * (1 + erf(x / sqrt 2))."""
+    from scipy.special import erf          # the error function, as a library step
     X = _f64(X)
-    erf = np.vectorize(math.erf, otypes=[np.float64])
     return 0.5 * X * (1.0 + erf(X / math.sqrt(2.0)))
 
 

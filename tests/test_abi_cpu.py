@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("bra_route", "bra_attend", "bra_forward", "bra_lepe", "bra_workspace_bytes",
               "bra_strerror", "bra_last_error", "bra_linear", "bra_module_workspace_bytes",
-              "bra_module_forward"):
+              "bra_module_forward", "bra_layer_norm", "bra_block_workspace_bytes",
+              "bra_block_forward", "bra_pos_conv"):
         assert n in names
 
 
@@ -170,12 +171,15 @@ def test_module_workspace_layout(lib):
     (dict(y=P + 64), INVAL, "overlaps"),
     (dict(dt=3), INVAL, "dtype"),
     (dict(rows=1 << 24, K=64), UNSUP, "2 GiB"),
+    (dict(act=2), INVAL, "act"),
+    (dict(act=1, r=P3), UNSUP, "residual with an activation"),
+    (dict(r=P4 + 64), INVAL, "overlaps r"),
 ])
 def test_linear_rejects(lib, kw, status, msg):
-    a = dict(x=P, rows=100, K=64, w=P2, b=None, N=64, dt=BF16, y=P4)
+    a = dict(x=P, rows=100, K=64, w=P2, b=None, N=64, act=0, r=None, dt=BF16, y=P4)
     a.update(kw)
-    assert lib.bra_linear(a["x"], a["rows"], a["K"], a["w"], a["b"], a["N"], a["dt"], a["y"],
-                          None) == status
+    assert lib.bra_linear(a["x"], a["rows"], a["K"], a["w"], a["b"], a["N"], a["act"], a["r"],
+                          a["dt"], a["y"], None) == status
     assert msg in lib.bra_last_error().decode()
 
 
@@ -204,3 +208,54 @@ def test_module_rejects(lib, kw, status, msg):
                                 a["idx"], a["ws"], a["wsb"], None)
     assert st == status
     assert msg in lib.bra_last_error().decode()
+
+
+def test_block_workspace_layout(lib):
+    B, H, W, C, S = 2, 14, 14, 64, 7
+    up = lambda x: (x + 255) // 256 * 256
+    tensor = up(2 * 14 * 14 * 64 * 2)
+    assert lib.bra_block_workspace_bytes(B, H, W, C, S, BF16) == \
+        4 * tensor + lib.bra_module_workspace_bytes(B, H, W, C, S, BF16, 1)
+    assert lib.bra_block_workspace_bytes(B, H, W, C, 0, BF16) == 0
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(C=60), UNSUP, "multiple of 8"),
+    (dict(C=64, dt=F32, rows=0), INVAL, "positive"),
+    (dict(eps=0.0), INVAL, "eps"),
+    (dict(gamma=None), INVAL, "gamma is NULL"),
+    (dict(y=P + 64), INVAL, "overlaps"),
+])
+def test_layer_norm_rejects(lib, kw, status, msg):
+    a = dict(x=P, rows=100, C=64, gamma=P2, beta=P3, eps=1e-5, dt=BF16, y=P4)
+    a.update(kw)
+    assert lib.bra_layer_norm(a["x"], a["rows"], a["C"], a["gamma"], a["beta"], a["eps"], a["dt"],
+                              a["y"], None) == status
+    assert msg in lib.bra_last_error().decode()
+
+
+def test_block_rejects(lib):
+    import ctypes
+    P_ = bra._BlockParams()
+    for i, n in enumerate(bra.BLOCK_PARAMS):
+        if n != "lepe_ks":
+            setattr(P_, n, 0x1000000 + i * 0x100000)
+    P_.lepe_w = None
+    call = lambda p, **kw: lib.bra_block_forward(
+        P, 2, 8, 8, 64, 2, 2, 2, BF16, p, 0.125, 0.17, 0x70000000, P4, kw.get("ws", 0x7A000000),
+        kw.get("wsb", 1 << 26), None)
+    assert call(None) == INVAL and "params is NULL" in lib.bra_last_error().decode()
+    q = bra._BlockParams.from_buffer_copy(P_)
+    q.w_fc2 = None
+    assert call(ctypes.byref(q)) == INVAL and "w_fc2" in lib.bra_last_error().decode()
+    q = bra._BlockParams.from_buffer_copy(P_)
+    q.ln1_g = 0x1000004
+    assert call(ctypes.byref(q)) == INVAL and "ln1_g" in lib.bra_last_error().decode()
+    assert call(ctypes.byref(P_), wsb=100) == WSERR
+
+
+def test_pos_conv_rejects(lib):
+    assert lib.bra_pos_conv(P, None, None, 2, 8, 8, 64, BF16, P4, None) == INVAL
+    assert lib.bra_pos_conv(P, P2, None, 2, 8, 8, 60, BF16, P4, None) == UNSUP
+    assert lib.bra_pos_conv(P, P2, None, 2, 8, 8, 64, BF16, P + 64, None) == INVAL
+    assert lib.bra_pos_conv(P, P2, P3 + 4, 2, 8, 8, 64, BF16, P4, None) == INVAL

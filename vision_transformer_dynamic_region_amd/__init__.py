@@ -17,6 +17,7 @@ import os
 
 __all__ = ["BraError", "lib_path", "load", "workspace_bytes", "route", "attend",
            "forward", "lepe", "linear", "module_workspace_bytes", "module_forward",
+           "layer_norm", "pos_conv", "block_workspace_bytes", "block_forward", "BLOCK_PARAMS",
            "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,10 +37,15 @@ _SIGNATURES = {
     "bra_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _f, _vp, _vp, _i,
                          _vp, _vp, _vp, _vp, _sz, _vp]),
     "bra_lepe": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp]),
-    "bra_linear": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _vp]),
+    "bra_linear": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _i, _vp, _vp]),
+    "bra_pos_conv": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "bra_module_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "bra_module_forward": (_i, [_vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _f, _f, _vp, _vp,
                                 _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "bra_layer_norm": (_i, [_vp, _i, _i, _vp, _vp, _f, _i, _vp, _vp]),
+    "bra_block_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "bra_block_forward": (_i, [_vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _f, _f, _vp, _vp, _vp,
+                               _sz, _vp]),
     "bra_strerror": (ctypes.c_char_p, [_i]),
     "bra_last_error": (ctypes.c_char_p, []),
 }
@@ -251,9 +257,10 @@ def _opt(t, name, dtype, shape):
     return t.data_ptr()
 
 
-def linear(x, w, b=None, out=None):
-    """y = x w^T + b over the last axis (bra_linear): x [..., K], w [N, K] in
-    x's dtype, b float32 [N] or None.  Returns y [..., N]."""
+def linear(x, w, b=None, out=None, act: str | None = None, residual=None):
+    """y = act(x w^T + b) + residual over the last axis (bra_linear): x [..., K],
+    w [N, K] in x's dtype, b float32 [N] or None, act None or "gelu",
+    residual [..., N] in x's dtype or None.  Returns y [..., N]."""
     import torch
     dt = _dtype_code(x)
     _dev(x, "x")
@@ -263,13 +270,37 @@ def linear(x, w, b=None, out=None):
     N, K = int(w.shape[0]), int(w.shape[1])
     rows = x.numel() // K
     bp = _opt(b, "b", torch.float32, (N,))
+    if act not in (None, "gelu"):
+        raise ValueError("act must be None or 'gelu'")
     if out is None:
         out = torch.empty((*x.shape[:-1], N), dtype=x.dtype, device=x.device)
     _dev(out, "out", x.dtype)
     if out.numel() != rows * N:
         raise ValueError("out must hold rows * N elements")
-    _check(load().bra_linear(x.data_ptr(), rows, K, w.data_ptr(), bp, N, dt, out.data_ptr(),
-                             _stream(x)))
+    rp = None
+    if residual is not None:
+        _dev(residual, "residual", x.dtype)
+        if residual.numel() != rows * N:
+            raise ValueError("residual must hold rows * N elements")
+        rp = residual.data_ptr()
+    _check(load().bra_linear(x.data_ptr(), rows, K, w.data_ptr(), bp, N, 1 if act else 0, rp, dt,
+                             out.data_ptr(), _stream(x)))
+    return out
+
+
+def pos_conv(x, w, b=None, out=None):
+    """out = x + b + depthwise 3x3 conv of x (bra_pos_conv); w float32 [C, 3, 3]."""
+    import torch
+    B, H, W, C = _bhwc(x)
+    dt = _dtype_code(x)
+    _dev(x, "x")
+    _opt(w, "w", torch.float32, (C, 3, 3))
+    bp = _opt(b, "b", torch.float32, (C,))
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "out", x.dtype)
+    _check(load().bra_pos_conv(x.data_ptr(), w.data_ptr(), bp, B, H, W, C, dt, out.data_ptr(),
+                               _stream(x)))
     return out
 
 
@@ -318,4 +349,78 @@ def module_forward(x, w_qkv, b_qkv, heads: int, S: int, topk: int, lepe_w=None, 
                                      wp, bp, ks, wo, bo, out.data_ptr(), idx.data_ptr(),
                                      workspace.data_ptr(),
                                      workspace.numel() * workspace.element_size(), _stream(x)))
+    return out, idx
+
+
+def layer_norm(x, gamma, beta, eps: float = 1e-5, out=None):
+    """LayerNorm over the last axis (bra_layer_norm); gamma, beta float32 [C]."""
+    import torch
+    dt = _dtype_code(x)
+    _dev(x, "x")
+    C = int(x.shape[-1])
+    _opt(gamma, "gamma", torch.float32, (C,))
+    _opt(beta, "beta", torch.float32, (C,))
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "out", x.dtype)
+    _check(load().bra_layer_norm(x.data_ptr(), x.numel() // C, C, gamma.data_ptr(),
+                                 beta.data_ptr(), float(eps), dt, out.data_ptr(), _stream(x)))
+    return out
+
+
+# field order of bra_block_params (include/bra.h)
+BLOCK_PARAMS = ("pos_w", "pos_b", "ln1_g", "ln1_b", "w_qkv", "b_qkv", "lepe_w", "lepe_b",
+                "lepe_ks", "w_out", "b_out", "ln2_g", "ln2_b", "w_fc1", "b_fc1", "w_fc2",
+                "b_fc2")
+
+
+class _BlockParams(ctypes.Structure):
+    _fields_ = [(n, _i if n == "lepe_ks" else _vp) for n in BLOCK_PARAMS]
+
+
+def block_workspace_bytes(B: int, H: int, W: int, C: int, S: int, dtype_code: int) -> int:
+    return int(load().bra_block_workspace_bytes(B, H, W, C, S, dtype_code))
+
+
+def block_forward(x, params: dict, heads: int, S: int, topk: int,
+                  route_scale: float | None = None, attn_scale: float | None = None, out=None,
+                  idx=None, workspace=None):
+    """One BiFormer block (bra_block_forward).  params maps the names of
+    BLOCK_PARAMS to CUDA tensors (weights w_qkv, w_out, w_fc1, w_fc2 in x's
+    dtype, the rest float32; biases and lepe_w may be None; lepe_ks is taken
+    from lepe_w).  Returns (out, idx)."""
+    import torch
+    B, H, W, C = _bhwc(x)
+    dt = _dtype_code(x)
+    _dev(x, "x")
+    shapes = {"pos_w": (C, 3, 3), "pos_b": (C,), "ln1_g": (C,), "ln1_b": (C,),
+              "w_qkv": (3 * C, C), "b_qkv": (3 * C,), "lepe_b": (C,), "w_out": (C, C),
+              "b_out": (C,), "ln2_g": (C,), "ln2_b": (C,), "w_fc1": (3 * C, C),
+              "b_fc1": (3 * C,), "w_fc2": (C, 3 * C), "b_fc2": (C,)}
+    wdt = {"w_qkv", "w_out", "w_fc1", "w_fc2"}
+    p = _BlockParams()
+    for n, shp in shapes.items():
+        setattr(p, n, _opt(params.get(n), n, x.dtype if n in wdt else torch.float32, shp))
+    wp, _, ks = _lepe_args(params.get("lepe_w"), None, C)
+    p.lepe_w, p.lepe_ks = wp, ks
+    if route_scale is None:
+        route_scale = C ** -0.5
+    if attn_scale is None:
+        attn_scale = (C // heads) ** -0.5
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "out", x.dtype)
+    if idx is None:
+        idx = torch.empty((B, S * S, topk), dtype=torch.int32, device=x.device)
+    _dev(idx, "idx", torch.int32)
+    if idx.numel() != B * S * S * topk:
+        raise ValueError("idx must hold B*S*S*topk entries")
+    if workspace is None:
+        workspace = torch.empty(max(block_workspace_bytes(B, H, W, C, S, dt), 16),
+                                dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace")
+    _check(load().bra_block_forward(x.data_ptr(), B, H, W, C, heads, S, topk, dt, ctypes.byref(p),
+                                    float(route_scale), float(attn_scale), out.data_ptr(),
+                                    idx.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(x)))
     return out, idx

@@ -165,6 +165,72 @@ bra_status hip_status(hipError_t e, const char* what) {
   return fail(BRA_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+constexpr float kLayerNormEps = 1e-5f;
+
+// The module's launch sequence on validated arguments; ws holds the module
+// workspace laid out as l.  With w_out, y goes to the workspace and out =
+// y w_out^T + b_out (+ resid when resid is not null); without, out = y.
+bra_status module_launches(const void* x, const bra::Shape& s, bra_dtype dtype, const void* w_qkv,
+                           const float* b_qkv, float route_scale, float attn_scale,
+                           const float* lepe_w, const float* lepe_b, int lepe_ks,
+                           const void* w_out, const float* b_out, const void* resid, void* out,
+                           int32_t* idx, unsigned char* w8, const ModuleLayout& l, hipStream_t hs) {
+  bra_status st;
+  const bool bf16 = dtype == BRA_BF16;
+  const int C = s.C;
+  double* xm = (double*)(w8 + l.xm);
+  double* qm = (double*)(w8 + l.qm);
+  double* km = (double*)(w8 + l.km);
+  void* qkv[3] = {w8 + l.q, w8 + l.k, w8 + l.v};
+  void* y = w_out ? (void*)(w8 + l.y) : out;
+  const int T = s.B * s.H * s.W;
+  // routing: region means of x, projected in float64 (mean commutes with
+  // the per-token map), scaled affinity and top-k
+  if ((st = hip_status(bra::launch_pool(x, nullptr, xm, nullptr, s, bf16, hs), "pool launch")))
+    return st;
+  if ((st = hip_status(bra::launch_means_proj(xm, s.B * s.R, C, w_qkv, b_qkv, bf16, qm, km, hs),
+                       "means projection launch")))
+    return st;
+  if ((st = hip_status(bra::launch_route(qm, km, s, (double)route_scale, idx, nullptr, hs),
+                       "route launch")))
+    return st;
+  // Q, K, V
+  if ((st = hip_status(bra::launch_linear(x, T, C, w_qkv, b_qkv, 3 * C, qkv, 3, bf16, hs),
+                       "qkv projection launch")))
+    return st;
+  // attention + LePE on the projected V
+  if ((st = hip_status(bra::launch_attend(qkv[0], qkv[1], qkv[2], idx, s, bf16, attn_scale, lepe_w,
+                                          lepe_b, lepe_ks, y, hs),
+                       "attend launch")))
+    return st;
+  if (!w_out) return BRA_OK;
+  void* outs[1] = {out};
+  return hip_status(bra::launch_linear(y, T, C, w_out, b_out, C, outs, 1, bf16, hs,
+                                       resid ? 2 : 0, resid),
+                    "output projection launch");
+}
+
+// Byte offsets of the block workspace: x1, n1, x2, n2 ([B,H,W,C] each), then
+// a module workspace with its output projection (whose Q/K/V space later
+// holds the [B,H,W,3C] hidden tensor of the MLP).
+struct BlockLayout {
+  size_t x1, n1, x2, n2, mod, total;
+  ModuleLayout ml;
+};
+
+BlockLayout block_layout(int B, int H, int W, int C, int S, bra_dtype dt) {
+  BlockLayout b;
+  const size_t tensor = align256((size_t)B * H * W * C * elem_size(dt));
+  b.x1 = 0;
+  b.n1 = b.x1 + tensor;
+  b.x2 = b.n1 + tensor;
+  b.n2 = b.x2 + tensor;
+  b.mod = b.n2 + tensor;
+  b.ml = module_layout(B, H, W, C, S, dt, true);
+  b.total = b.mod + b.ml.total;
+  return b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -250,7 +316,7 @@ bra_status bra_lepe(const void* v, const float* w, const float* b, int ks, int B
 }
 
 bra_status bra_linear(const void* x, int rows, int K, const void* w, const float* b, int N,
-                      bra_dtype dtype, void* y, void* stream) {
+                      int act, const void* r, bra_dtype dtype, void* y, void* stream) {
   g_last_error[0] = 0;
   bra_status st;
   if (dtype != BRA_F32 && dtype != BRA_BF16) return fail(BRA_E_INVAL, "dtype %d is not BRA_F32 or BRA_BF16", (int)dtype);
@@ -258,18 +324,40 @@ bra_status bra_linear(const void* x, int rows, int K, const void* w, const float
   if ((st = check_tensor(x, "x")) || (st = check_tensor(w, "w")) || (st = check_tensor(y, "y")) ||
       (st = check_bias(b, "b")))
     return st;
+  if (act != 0 && act != 1) return fail(BRA_E_INVAL, "act=%d must be 0 (none) or 1 (GELU)", act);
+  if (r && act) return fail(BRA_E_UNSUPPORTED, "a residual with an activation is not supported");
+  if (r && (st = check_tensor(r, "r"))) return st;
   if (K % 32) return fail(BRA_E_UNSUPPORTED, "K=%d must be a multiple of 32", K);
   if (N % 4) return fail(BRA_E_UNSUPPORTED, "N=%d must be a multiple of 4", N);
   const size_t es = elem_size(dtype);
   if ((long long)rows * K * (long long)es >= kMaxOperandBytes ||
       (long long)rows * N * (long long)es >= kMaxOperandBytes)
     return fail(BRA_E_UNSUPPORTED, "operands of %d rows exceed 2 GiB", rows);
-  if (overlaps(y, x, (size_t)rows * K * es) || overlaps(y, w, (size_t)N * K * es))
+  const size_t ybytes = (size_t)rows * N * es;
+  if (overlaps2(y, ybytes, x, (size_t)rows * K * es) || overlaps2(y, ybytes, w, (size_t)N * K * es))
     return fail(BRA_E_INVAL, "y overlaps x or w");
+  if (r && r != y && overlaps2(y, ybytes, r, ybytes)) return fail(BRA_E_INVAL, "y overlaps r (other than in place)");
   void* ys[1] = {y};
   return hip_status(bra::launch_linear(x, rows, K, w, b, N, ys, 1, dtype == BRA_BF16,
-                                       (hipStream_t)stream),
+                                       (hipStream_t)stream, r ? 2 : act, r),
                     "linear launch");
+}
+
+bra_status bra_pos_conv(const void* x, const float* w, const float* b, int B, int H, int W, int C,
+                        bra_dtype dtype, void* out, void* stream) {
+  g_last_error[0] = 0;
+  bra::Shape s;
+  bra_status st;
+  if ((st = check_shape(B, H, W, C, 1, 0, 1, dtype, &s))) return st;
+  if ((st = check_tensor(x, "x")) || (st = check_tensor(out, "out")) || (st = check_bias(b, "b")))
+    return st;
+  if (!w) return fail(BRA_E_INVAL, "w is NULL");
+  if ((uintptr_t)w & 3u) return fail(BRA_E_INVAL, "w is not 4-byte aligned");
+  if (dtype == BRA_F32 ? C % 4 : C % 8) return fail(BRA_E_UNSUPPORTED, "C=%d must be a multiple of %d", C, dtype == BRA_F32 ? 4 : 8);
+  const size_t bytes = (size_t)B * H * W * C * elem_size(dtype);
+  if (overlaps2(x, bytes, out, bytes)) return fail(BRA_E_INVAL, "out overlaps x");
+  return hip_status(bra::launch_pos_conv(x, w, b, s, dtype == BRA_BF16, out, (hipStream_t)stream),
+                    "position conv launch");
 }
 
 size_t bra_module_workspace_bytes(int B, int H, int W, int C, int S, bra_dtype dtype,
@@ -320,38 +408,111 @@ bra_status bra_module_forward(const void* x, int B, int H, int W, int C, int hea
   if (overlaps2(out, tbytes, w_qkv, (size_t)3 * C * C * es) ||
       (w_out && overlaps2(out, tbytes, w_out, (size_t)C * C * es)))
     return fail(BRA_E_INVAL, "out overlaps a weight");
+  return module_launches(x, s, dtype, w_qkv, b_qkv, route_scale, attn_scale, lepe_w, lepe_b,
+                         lepe_ks, w_out, b_out, nullptr, out, idx, (unsigned char*)ws, l,
+                         (hipStream_t)stream);
+}
+
+bra_status bra_layer_norm(const void* x, int rows, int C, const float* gamma, const float* beta,
+                          float eps, bra_dtype dtype, void* y, void* stream) {
+  g_last_error[0] = 0;
+  bra_status st;
+  if (dtype != BRA_F32 && dtype != BRA_BF16) return fail(BRA_E_INVAL, "dtype %d is not BRA_F32 or BRA_BF16", (int)dtype);
+  if (rows < 1 || C < 1) return fail(BRA_E_INVAL, "rows=%d C=%d must be positive", rows, C);
+  if ((st = check_tensor(x, "x")) || (st = check_tensor(y, "y")) || (st = check_tensor(gamma, "gamma")) ||
+      (st = check_tensor(beta, "beta")))
+    return st;
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(BRA_E_INVAL, "eps=%g must be positive and finite", (double)eps);
+  int L, NG;
+  if (!bra::layer_norm_shape(C, dtype == BRA_BF16, &L, &NG))
+    return fail(BRA_E_UNSUPPORTED, "C=%d: LayerNorm needs C a multiple of %d with at most 4 groups per lane",
+                C, dtype == BRA_BF16 ? 8 : 4);
+  const size_t bytes = (size_t)rows * C * elem_size(dtype);
+  if (overlaps2(x, bytes, y, bytes) && x != y) return fail(BRA_E_INVAL, "y overlaps x (other than in place)");
+  return hip_status(bra::launch_layer_norm(x, rows, C, gamma, beta, eps, dtype == BRA_BF16, y,
+                                           (hipStream_t)stream),
+                    "layer norm launch");
+}
+
+size_t bra_block_workspace_bytes(int B, int H, int W, int C, int S, bra_dtype dtype) {
+  if (B < 1 || H < 1 || W < 1 || C < 1 || S < 1) return 0;
+  if (dtype != BRA_F32 && dtype != BRA_BF16) return 0;
+  return block_layout(B, H, W, C, S, dtype).total;
+}
+
+bra_status bra_block_forward(const void* x, int B, int H, int W, int C, int heads, int S, int topk,
+                             bra_dtype dtype, const bra_block_params* p, float route_scale,
+                             float attn_scale, void* out, int32_t* idx, void* ws, size_t ws_bytes,
+                             void* stream) {
+  g_last_error[0] = 0;
+  bra::Shape s;
+  bra_status st;
+  if (!p) return fail(BRA_E_INVAL, "params is NULL");
+  if (heads < 1) return fail(BRA_E_INVAL, "heads=%d must be positive", heads);
+  if ((st = check_shape(B, H, W, C, S, heads, topk, dtype, &s))) return st;
+  if ((st = check_tensor(x, "x")) || (st = check_tensor(out, "out"))) return st;
+  if ((st = check_tensor(p->pos_w, "pos_w")) || (st = check_bias(p->pos_b, "pos_b")) ||
+      (st = check_tensor(p->ln1_g, "ln1_g")) || (st = check_tensor(p->ln1_b, "ln1_b")) ||
+      (st = check_tensor(p->w_qkv, "w_qkv")) || (st = check_bias(p->b_qkv, "b_qkv")) ||
+      (st = check_tensor(p->w_out, "w_out")) || (st = check_bias(p->b_out, "b_out")) ||
+      (st = check_tensor(p->ln2_g, "ln2_g")) || (st = check_tensor(p->ln2_b, "ln2_b")) ||
+      (st = check_tensor(p->w_fc1, "w_fc1")) || (st = check_bias(p->b_fc1, "b_fc1")) ||
+      (st = check_tensor(p->w_fc2, "w_fc2")) || (st = check_bias(p->b_fc2, "b_fc2")))
+    return st;
+  if (!idx) return fail(BRA_E_INVAL, "idx is NULL");
+  if ((uintptr_t)idx & 3u) return fail(BRA_E_INVAL, "idx is not 4-byte aligned");
+  if (!(route_scale > 0.f) || !std::isfinite(route_scale))
+    return fail(BRA_E_INVAL, "route_scale=%g must be positive and finite", (double)route_scale);
+  if (!(attn_scale > 0.f) || !std::isfinite(attn_scale))
+    return fail(BRA_E_INVAL, "attn_scale=%g must be positive and finite", (double)attn_scale);
+  if (p->lepe_w && (st = check_lepe_args(p->lepe_w, p->lepe_b, p->lepe_ks, s))) return st;
+  int L, NG;
+  if (!bra::layer_norm_shape(C, dtype == BRA_BF16, &L, &NG))
+    return fail(BRA_E_UNSUPPORTED, "C=%d: LayerNorm needs at most 4 channel groups per lane", C);
+  const size_t es = elem_size(dtype);
+  const size_t tbytes = (size_t)B * H * W * C * es;
+  if ((long long)tbytes * 3 >= kMaxOperandBytes)
+    return fail(BRA_E_UNSUPPORTED, "the [B,H,W,3C] hidden tensor of %zu bytes exceeds 2 GiB", tbytes * 3);
+  const BlockLayout bl = block_layout(B, H, W, C, S, dtype);
+  if (!ws) return fail(BRA_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", bl.total);
+  if (!aligned16(ws)) return fail(BRA_E_WORKSPACE, "workspace is not 16-byte aligned");
+  if (ws_bytes < bl.total) return fail(BRA_E_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, bl.total);
+  const size_t ibytes = (size_t)B * s.R * topk * sizeof(int32_t);
+  if (overlaps2(ws, bl.total, x, tbytes)) return fail(BRA_E_INVAL, "workspace overlaps x");
+  if (overlaps2(ws, bl.total, out, tbytes)) return fail(BRA_E_INVAL, "workspace overlaps out");
+  if (overlaps2(ws, bl.total, idx, ibytes)) return fail(BRA_E_INVAL, "workspace overlaps idx");
+  if (overlaps2(out, tbytes, idx, ibytes) || overlaps2(x, tbytes, idx, ibytes))
+    return fail(BRA_E_INVAL, "idx overlaps x or out");
   hipStream_t hs = (hipStream_t)stream;
   const bool bf16 = dtype == BRA_BF16;
   unsigned char* w8 = (unsigned char*)ws;
-  double* xm = (double*)(w8 + l.xm);
-  double* qm = (double*)(w8 + l.qm);
-  double* km = (double*)(w8 + l.km);
-  void* qkv[3] = {w8 + l.q, w8 + l.k, w8 + l.v};
-  void* y = w_out ? (void*)(w8 + l.y) : out;
+  void* x1 = w8 + bl.x1;
+  void* n1 = w8 + bl.n1;
+  void* x2 = w8 + bl.x2;
+  void* n2 = w8 + bl.n2;
+  unsigned char* mws = w8 + bl.mod;
   const int T = B * H * W;
-  // routing: region means of x, projected in float64 (mean commutes with
-  // the per-token map), scaled affinity and top-k
-  if ((st = hip_status(bra::launch_pool(x, nullptr, xm, nullptr, s, bf16, hs), "pool launch")))
+  // x1 = x + pos conv;  x2 = x1 + module(LN1(x1))
+  if ((st = hip_status(bra::launch_pos_conv(x, p->pos_w, p->pos_b, s, bf16, x1, hs), "position conv launch")))
     return st;
-  if ((st = hip_status(bra::launch_means_proj(xm, B * s.R, C, w_qkv, b_qkv, bf16, qm, km, hs),
-                       "means projection launch")))
+  if ((st = hip_status(bra::launch_layer_norm(x1, T, C, p->ln1_g, p->ln1_b, kLayerNormEps, bf16, n1, hs),
+                       "layer norm launch")))
     return st;
-  if ((st = hip_status(bra::launch_route(qm, km, s, (double)route_scale, idx, nullptr, hs),
-                       "route launch")))
+  if ((st = module_launches(n1, s, dtype, p->w_qkv, p->b_qkv, route_scale, attn_scale, p->lepe_w,
+                            p->lepe_b, p->lepe_ks, p->w_out, p->b_out, x1, x2, idx, mws, bl.ml, hs)))
     return st;
-  // Q, K, V
-  if ((st = hip_status(bra::launch_linear(x, T, C, w_qkv, b_qkv, 3 * C, qkv, 3, bf16, hs),
-                       "qkv projection launch")))
+  // out = x2 + fc2(GELU(fc1(LN2(x2)))); the hidden tensor reuses the module's Q/K/V space
+  if ((st = hip_status(bra::launch_layer_norm(x2, T, C, p->ln2_g, p->ln2_b, kLayerNormEps, bf16, n2, hs),
+                       "layer norm launch")))
     return st;
-  // attention + LePE on the projected V
-  if ((st = hip_status(bra::launch_attend(qkv[0], qkv[1], qkv[2], idx, s, bf16, attn_scale, lepe_w,
-                                          lepe_b, lepe_ks, y, hs),
-                       "attend launch")))
+  void* h = mws + bl.ml.q;
+  void* hv[1] = {h};
+  if ((st = hip_status(bra::launch_linear(n2, T, C, p->w_fc1, p->b_fc1, 3 * C, hv, 1, bf16, hs, 1),
+                       "fc1 launch")))
     return st;
-  if (!w_out) return BRA_OK;
-  void* outs[1] = {out};
-  return hip_status(bra::launch_linear(y, T, C, w_out, b_out, C, outs, 1, bf16, hs),
-                    "output projection launch");
+  void* ov[1] = {out};
+  return hip_status(bra::launch_linear(h, T, 3 * C, p->w_fc2, p->b_fc2, C, ov, 1, bf16, hs, 2, x2),
+                    "fc2 launch");
 }
 
 const char* bra_strerror(int status) {

@@ -23,9 +23,23 @@ hipError_t launch_pool(const void* q, const void* k, double* qm, double* km,
                        const Shape& s, bool bf16, hipStream_t st);
 
 // y[g] = columns [g*N/groups, (g+1)*N/groups) of x w^T + b, for x [T, K],
-// w [N, K], b [N] or null (groups <= 3).  K % 32 == 0, N % (4 * groups) == 0.
+// w [N, K], b [N] or null (groups <= 3).  K % 32 == 0, N % 4 == 0 and, with
+// several groups, N / groups % 8 == 0.  epi 1 applies GELU (exact form)
+// after the bias; epi 2 adds resid [T, N] (one group) before the rounding.
 hipError_t launch_linear(const void* x, int T, int K, const void* w, const float* b, int N,
-                         void* const* y, int groups, bool bf16, hipStream_t st);
+                         void* const* y, int groups, bool bf16, hipStream_t st, int epi = 0,
+                         const void* resid = nullptr);
+
+// out = x + b + depthwise 3x3 cross-correlation of x (w [C, 3, 3], zero
+// padding 1), [B, H, W, C].
+hipError_t launch_pos_conv(const void* x, const float* w, const float* b, const Shape& s,
+                           bool bf16, void* out, hipStream_t st);
+
+// LayerNorm of each of `rows` rows of C channels (biased variance, eps).
+// layer_norm_shape says whether C is supported and how rows are split.
+bool layer_norm_shape(int C, bool bf16, int* lanes_per_row, int* groups_per_lane);
+hipError_t launch_layer_norm(const void* x, long long rows, int C, const float* g,
+                             const float* b, float eps, bool bf16, void* y, hipStream_t st);
 
 // qm = xm Wq^T + bq, km = xm Wk^T + bk in float64, with Wq, Wk the first two
 // C-row blocks of w_qkv [3C, C] and bq, bk those of b_qkv (or null).

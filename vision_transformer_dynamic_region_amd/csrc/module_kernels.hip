@@ -37,6 +37,7 @@ struct LinArgs {
   const void* x;        // [T, K]
   const void* w;        // [N, K]
   const float* b;       // [N] or null
+  const void* r;        // residual [T, N] added before the rounding (EPI 2), or null
   void* y[3];           // output groups: columns [g*ng, (g+1)*ng) go to y[g], [T, ng]
   int ng;               // columns per output group
   int T, K, N;
@@ -58,8 +59,15 @@ struct LinArgs {
 // workgroups.  Work items go to XCDs in contiguous ranges.  The output tile
 // of a wavefront (32 tokens x 64 features) goes through LDS so that each
 // 128-byte line of a token's features is written by 8 adjacent lanes in one
-// store.
-template <bool BF16, int KCH>
+// store.  Epilogue EPI: 0 bias only, 1 bias then GELU (exact erf form), 2
+// bias then a residual tensor added; each rounds once to the output type.
+template <int EPI>
+__device__ __forceinline__ float lin_act(float v) {
+  if constexpr (EPI == 1) return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+  return v;
+}
+
+template <bool BF16, int KCH, int EPI>
 __global__ __launch_bounds__(kThreads) void linear_kernel(LinArgs a) {
   constexpr int ES = BF16 ? 2 : 4;                 // element bytes
   constexpr int KSTEP = BF16 ? 32 : 4;             // k per MFMA
@@ -68,8 +76,9 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinArgs a) {
   constexpr int XPL = BF16 ? 1 : 8;                // f32: 8 one-float k-steps per group
   constexpr int CPR = KCH / CE;                    // 16-byte chunks per staged row (full chunk)
   constexpr int WPT = kLinCols * CPR / kThreads;   // staged chunks per thread
-  constexpr int BUFB = kLinCols * KCH * ES;        // bytes of one staging buffer
-  constexpr int ORB = kLinCols * ES + 16;          // output staging row (padded)
+  constexpr bool F32ST = EPI == 2 || !BF16;        // output tile staged in float32
+  constexpr int SES = F32ST ? 4 : ES;
+  constexpr int ORB = kLinCols * SES + 16;         // output staging row (padded)
   using XT = typename std::conditional<BF16, bf16x8, float>::type;
   extern __shared__ __align__(16) unsigned char lds[];
   const int xcd = blockIdx.x % kXcds, loc = blockIdx.x / kXcds;
@@ -85,7 +94,8 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinArgs a) {
   const unsigned char* W = (const unsigned char*)a.w;
   const int nch = (a.K + KCH - 1) / KCH;
   const int nsteps = (ct1 - ct0) * nch;
-  unsigned char* ost = lds + 2 * BUFB + wave * 32 * ORB;   // this wavefront's output tile
+  const int bufb = kLinCols * min(a.K, KCH) * ES;  // bytes of one W staging buffer
+  unsigned char* ost = lds + 2 * bufb + wave * 32 * ORB;   // this wavefront's output tile
 
   uint4 wv[WPT];
   auto load_w = [&](int step) {                    // W block of a step into registers
@@ -130,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinArgs a) {
     const int ct = ct0 + step / nch, ch = step % nch, kc = ch * KCH;
     const int kn = min(KCH, a.K - kc), cpr = kn / CE;
     const int sw = cpr % 8 == 0 ? 7 : 3;           // cpr is a multiple of 4
-    unsigned char* buf = lds + (step & 1) * BUFB;
+    unsigned char* buf = lds + (step & 1) * bufb;
     if (nch > 1) load_x(kc);
     // staged row r, chunk c at chunk c ^ (r & sw); the barrier of the
     // previous step ordered every read of this buffer (two steps ago) first
@@ -187,25 +197,43 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinArgs a) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
         const f32x4 v = acc[tb][nb];
-        unsigned char* d = ost + (16 * tb + lq) * ORB + (16 * nb + 4 * lg) * ES;
-        if constexpr (BF16) {
-          *(uint2*)d = make_uint2(pack_bf16x2(v[0] + bb[0], v[1] + bb[1]),
-                                  pack_bf16x2(v[2] + bb[2], v[3] + bb[3]));
-        } else {
-          *(float4*)d = make_float4(v[0] + bb[0], v[1] + bb[1], v[2] + bb[2], v[3] + bb[3]);
-        }
+        unsigned char* d = ost + (16 * tb + lq) * ORB + (16 * nb + 4 * lg) * SES;
+        const float o0 = lin_act<EPI>(v[0] + bb[0]), o1 = lin_act<EPI>(v[1] + bb[1]);
+        const float o2 = lin_act<EPI>(v[2] + bb[2]), o3 = lin_act<EPI>(v[3] + bb[3]);
+        if constexpr (F32ST) *(float4*)d = make_float4(o0, o1, o2, o3);
+        else *(uint2*)d = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    // 16-byte chunks: kLinCols * ES / 16 per token row, 64 lanes per store
+    // 16-byte chunks of output: kLinCols * ES / 16 per token row, 64 lanes per store
     constexpr int CPRO = kLinCols * ES / 16;
     constexpr int TPS = 64 / CPRO;                 // token rows per store
 #pragma unroll
     for (int i = 0; i < 32 / TPS; ++i) {
       const int tr = TPS * i + lane / CPRO, ck = lane % CPRO;
-      const uint4 v = *(const uint4*)(ost + tr * ORB + ck * 16);
+      const unsigned char* sp = ost + tr * ORB + ck * CE * SES;
+      uint4 v;
       const int t = t0 + 32 * wave + tr, n = n0 + ck * CE;
       const bool ok = n < a.N && t < a.T;
+      if constexpr (EPI == 2) {
+        // residual chunk at the same place of r ([T, N], one group)
+        const auto R = lin_rsrc(a.r, (uint32_t)a.T * a.N * ES);
+        const uint32_t roff = ok ? ((uint32_t)t * a.N + n) * ES : kLinOob;
+        const u32x4 rv = __builtin_amdgcn_raw_buffer_load_b128(R, roff, 0, 0);
+        float rf[CE];
+        unpack16<BF16>(make_uint4(rv.x, rv.y, rv.z, rv.w), rf);
+        if constexpr (BF16) {
+          const float4 a0 = *(const float4*)sp, a1 = *(const float4*)(sp + 16);
+          v = make_uint4(pack_bf16x2(a0.x + rf[0], a0.y + rf[1]), pack_bf16x2(a0.z + rf[2], a0.w + rf[3]),
+                         pack_bf16x2(a1.x + rf[4], a1.y + rf[5]), pack_bf16x2(a1.z + rf[6], a1.w + rf[7]));
+        } else {
+          const float4 a0 = *(const float4*)sp;
+          v = make_uint4(__float_as_uint(a0.x + rf[0]), __float_as_uint(a0.y + rf[1]),
+                         __float_as_uint(a0.z + rf[2]), __float_as_uint(a0.w + rf[3]));
+        }
+      } else {
+        v = *(const uint4*)sp;                     // bf16 staged, or float32 output
+      }
       // a chunk lies in one group (ng is a multiple of 8 or the chunk is the
       // last, partial one of a single group: N % 8 == 4 in bf16)
       const int g = ok ? n / a.ng : 0, col = n - g * a.ng;
@@ -314,7 +342,8 @@ __global__ __launch_bounds__(kThreads) void means_proj_kernel(MeansArgs a) {
 }  // namespace
 
 hipError_t launch_linear(const void* x, int T, int K, const void* w, const float* b, int N,
-                         void* const* y, int groups, bool bf16, hipStream_t st) {
+                         void* const* y, int groups, bool bf16, hipStream_t st, int epi,
+                         const void* resid) {
   if (T <= 0 || K <= 0 || N <= 0 || K % 32 || N % 4 || groups < 1 || groups > 3 ||
       N % groups || (N / groups) % (groups > 1 ? 8 : 4))
     return hipErrorInvalidValue;
@@ -322,8 +351,9 @@ hipError_t launch_linear(const void* x, int T, int K, const void* w, const float
   // buffer offsets are 32-bit: every operand below 2 GiB
   if ((long long)T * K * es >= (long long)kLinOob || (long long)T * (N / groups) * es >= (long long)kLinOob)
     return hipErrorNotSupported;
+  if (epi < 0 || epi > 2 || (epi == 2 && (!resid || groups != 1))) return hipErrorInvalidValue;
   LinArgs a;
-  a.x = x; a.w = w; a.b = b;
+  a.x = x; a.w = w; a.b = b; a.r = resid;
   for (int g = 0; g < 3; ++g) a.y[g] = g < groups ? y[g] : y[0];
   a.ng = N / groups;
   a.T = T; a.K = K; a.N = N;
@@ -339,15 +369,18 @@ hipError_t launch_linear(const void* x, int T, int K, const void* w, const float
   const dim3 grid((unsigned)(a.per_xcd * kXcds));
   // K chunk: all of K up to 256 in bf16 (X read once), 64 for float32
   const int kch = !bf16 ? 64 : K <= 64 ? 64 : K <= 128 ? 128 : 256;
-  const size_t lds = (size_t)2 * kLinCols * kch * es + (size_t)kWaves * 32 * (kLinCols * es + 16);
-  if (bf16 && kch == 64)
-    hipLaunchKernelGGL((linear_kernel<true, 64>), grid, dim3(kThreads), lds, st, a);
-  else if (bf16 && kch == 128)
-    hipLaunchKernelGGL((linear_kernel<true, 128>), grid, dim3(kThreads), lds, st, a);
-  else if (bf16)
-    hipLaunchKernelGGL((linear_kernel<true, 256>), grid, dim3(kThreads), lds, st, a);
-  else
-    hipLaunchKernelGGL((linear_kernel<false, 64>), grid, dim3(kThreads), lds, st, a);
+  const size_t orb = (size_t)kLinCols * ((epi == 2 || !bf16) ? 4 : es) + 16;
+  const size_t lds = (size_t)2 * kLinCols * (K < kch ? K : kch) * es + (size_t)kWaves * 32 * orb;
+#define BRA_LIN(BB, KK, EE) \
+  hipLaunchKernelGGL((linear_kernel<BB, KK, EE>), grid, dim3(kThreads), lds, st, a)
+#define BRA_LIN_E(BB, KK) \
+  if (epi == 0) BRA_LIN(BB, KK, 0); else if (epi == 1) BRA_LIN(BB, KK, 1); else BRA_LIN(BB, KK, 2)
+  if (bf16 && kch == 64) { BRA_LIN_E(true, 64); }
+  else if (bf16 && kch == 128) { BRA_LIN_E(true, 128); }
+  else if (bf16) { BRA_LIN_E(true, 256); }
+  else { BRA_LIN_E(false, 64); }
+#undef BRA_LIN_E
+#undef BRA_LIN
   return hipGetLastError();
 }
 
