@@ -60,9 +60,10 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="st1", choices=["tiny", "st1", "st2", "st3", "dense"])
-    p.add_argument("--path", default="bra", choices=["bra", "module"],
+    p.add_argument("--path", default="bra", choices=["bra", "module", "block"],
                    help="bra: the BRA forward pass on given Q, K, V (the default line); module: "
-                        "the module around it (Q/K/V projections of x, BRA, output projection)")
+                        "the module around it (Q/K/V projections of x, BRA, output projection); "
+                        "block: one BiFormer block (position conv, LN, module, LN, MLP)")
     p.add_argument("--sets", type=int, default=0,
                    help="input copies rotated across steps (0: enough to exceed the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -297,6 +298,83 @@ def run_module(a, wl) -> int:
     return 0
 
 
+def run_block(a, wl) -> int:
+    """One step = bra_block_forward over one batch."""
+    import numpy as np
+    import torch
+
+    import vision_transformer_dynamic_region_amd as bra
+    from vision_transformer_dynamic_region_amd.workloads import bf16_bits, make_block_inputs
+
+    dev = torch.device("cuda:0")
+    p = make_block_inputs(wl)
+    if wl.dtype == "bf16":
+        up = lambda arr: torch.from_numpy(bf16_bits(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        up = lambda arr: torch.from_numpy(arr).to(dev)
+    wdt = {"w_qkv", "w_out", "w_fc1", "w_fc2"}
+    params = {n: (up(p[n]) if n in wdt else torch.from_numpy(p[n]).to(dev))
+              for n in bra.BLOCK_PARAMS if n != "lepe_ks" and p.get(n) is not None}
+    x0 = up(p["x"])
+    code = 1 if wl.dtype == "bf16" else 0
+    wsb = bra.block_workspace_bytes(wl.B, wl.H, wl.W, wl.C, wl.S, code)
+    set_bytes = 2 * wl.tensor_bytes + wsb
+    sets = a.sets or max(1, -(-3 * MALL_BYTES // set_bytes))
+    bufs = [dict(x=x0.clone(), out=torch.empty_like(x0),
+                 idx=torch.empty((wl.B, wl.S * wl.S, wl.topk), dtype=torch.int32, device=dev),
+                 ws=torch.empty(wsb, dtype=torch.uint8, device=dev)) for _ in range(sets)]
+    torch.cuda.synchronize()
+    log(f"block: {sets} sets of {set_bytes / 1e6:.1f} MB (x, out, workspace) rotated per step")
+
+    def step(i):
+        b = bufs[i % sets]
+        bra.block_forward(b["x"], params, wl.heads, wl.S, wl.topk, out=b["out"], idx=b["idx"],
+                          workspace=b["ws"])
+
+    for i in range(a.warmup):
+        step(i)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(a.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    log(f"block: {ms:.4f} ms/step")
+    res = {
+        "metric": "BiFormer block fwd tokens/s (pos conv, LN, BRA module, LN, MLP ratio 3), 1 GPU",
+        "value": wl.tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name} block: B={wl.B} H=W={wl.H} C={wl.C} "
+                               f"heads={wl.heads} S={wl.S} topk={wl.topk}, MLP 3C",
+                   "tokens_per_step": wl.tokens, "input_sets_rotated": sets},
+    }
+    if not a.no_cpu_baseline:
+        import oracle as O
+        log("timing the fp64 oracle block on the host")
+        ru0 = resource.getrusage(resource.RUSAGE_SELF)
+        t0 = time.perf_counter()
+        nb, reps = 1, 0
+        while time.perf_counter() - t0 < a.cpu_seconds and reps < 50:
+            O.block_forward(p["x"][:nb], p, wl.heads, wl.S, wl.topk, storage=wl.dtype)
+            reps += 1
+        dt = time.perf_counter() - t0
+        ru1 = resource.getrusage(resource.RUSAGE_SELF)
+        cpu = (ru1.ru_utime - ru0.ru_utime) + (ru1.ru_stime - ru0.ru_stime)
+        tokens = nb * wl.H * wl.W * reps
+        res["cpu_baseline"] = {"value": tokens / dt, "unit": "tokens/s",
+                               "cores": max(1, int(round(cpu / dt))), "kind": "oracle",
+                               "sample": (f"{wl.name} block: 1 image x {reps} passes ({tokens} "
+                                          f"tokens), fp64 oracle block_forward in {dt:.1f} s")}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     a = parse()
     if a.traffic_from:
@@ -321,6 +399,8 @@ def main() -> int:
     wl = WORKLOADS[a.workload]
     if a.path == "module":
         return run_module(a, wl)
+    if a.path == "block":
+        return run_block(a, wl)
     dev = torch.device("cuda:0")
     log(f"workload {wl}")
     x = make_inputs(wl)
