@@ -178,7 +178,8 @@ bra_status bra_module_forward(const void* x, int B, int H, int W, int C,
 /* out = x + b + depthwise 3x3 cross-correlation of x over each image (zero
  * padding 1): the block's position encoding (p1 §4).
  *   x, out [B,H,W,C] dtype, device, not overlapping; w float32 [C, 3, 3];
- *   b float32 [C] or NULL; C a multiple of 8 (bf16) or 4 (f32). */
+ *   b float32 [C] or NULL (all 16-byte aligned); C a multiple of 8 (bf16)
+ *   or 4 (f32). */
 bra_status bra_pos_conv(const void* x, const float* w, const float* b, int B,
                         int H, int W, int C, bra_dtype dtype, void* out,
                         void* stream);

@@ -12,56 +12,87 @@ namespace bra {
 namespace {
 
 // out = x + b + depthwise 3x3 cross-correlation of x (zero padding 1), one
-// rounding.  A thread owns one 16-byte channel group of one pixel and reads
-// the 9 neighbouring vectors (the tile's pixels are shared through L1/L2);
-// consecutive threads take consecutive groups of a pixel, then pixels along
-// a row, so every load and the store are coalesced.
+// rounding.  Thread (x, g) owns 16-byte channel group g of pixel column x
+// over a strip of kPosRows rows: its 9 x VEC weights are loaded once, and a
+// 3 x 3 window of vectors slides down the strip, three new loads per output
+// row.  Consecutive threads take consecutive groups of a pixel, then pixels
+// along the row, so every load and the store are coalesced.  32-bit indices
+// within an image.
+constexpr int kPosRows = 8;
+
 struct PosArgs {
   const void* x;
   const float* w;       // [C, 3, 3]
   const float* b;       // [C] or null
   void* out;
   int H, W, C, G;       // G = 16-byte groups per pixel
-  long long total;      // B * H * W * G
+  int row_items;        // W * G
+  FastDiv f_G;
 };
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void pos_conv_kernel(PosArgs a) {
   constexpr int VEC = BF16 ? 8 : 4;
-  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= a.total) return;
-  const int g = (int)(i % a.G);
-  const long long p = i / a.G;                      // pixel index b*H*W + y*W + x
-  const int xq = (int)(p % a.W);
-  const long long by = p / a.W;
-  const int yq = (int)(by % a.H);
-  const uint4* X = (const uint4*)a.x;
-  float acc[VEC], ctr[VEC];
-  unpack16<BF16>(X[i], ctr);
+  const int t = blockIdx.x * kThreads + threadIdx.x;
+  if (t >= a.row_items) return;
+  const int y0 = blockIdx.y * kPosRows, b = blockIdx.z;
+  const int xq = fdiv(t, a.f_G), g = t - xq * a.G;
+  const size_t img = (size_t)b * a.H * a.row_items;
+  const uint4* X = (const uint4*)a.x + img;
+  uint4* O = (uint4*)a.out + img;
+  float wt[VEC][9], bias[VEC];
+  {
+    const float4* wp = (const float4*)(a.w + g * VEC * 9);   // VEC * 9 contiguous floats
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) acc[e] = ctr[e] + (a.b ? a.b[g * VEC + e] : 0.f);
+    for (int k = 0; k < VEC * 9 / 4; ++k) {
+      const float4 f = wp[k];
+      const float fv[4] = {f.x, f.y, f.z, f.w};
 #pragma unroll
-  for (int dy = -1; dy <= 1; ++dy) {
-    if ((unsigned)(yq + dy) >= (unsigned)a.H) continue;
-#pragma unroll
-    for (int dx = -1; dx <= 1; ++dx) {
-      if ((unsigned)(xq + dx) >= (unsigned)a.W) continue;
-      float v[VEC];
-      unpack16<BF16>(X[i + ((long long)dy * a.W + dx) * a.G], v);
-      const int tap = (dy + 1) * 3 + (dx + 1);
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] = fmaf(a.w[(g * VEC + e) * 9 + tap], v[e], acc[e]);
+      for (int u = 0; u < 4; ++u) wt[(4 * k + u) / 9][(4 * k + u) % 9] = fv[u];
     }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) bias[e] = a.b ? a.b[g * VEC + e] : 0.f;
   }
-  uint4 o;
-  if constexpr (BF16) {
-    o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                   pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
-  } else {
-    o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                   __float_as_uint(acc[3]));
+  const bool lft = xq > 0, rgt = xq + 1 < a.W;
+  auto ld = [&](int y, int dx) {                   // vector at (y, x + dx), zero outside
+    const bool ok = (unsigned)y < (unsigned)a.H && (dx < 0 ? lft : dx > 0 ? rgt : true);
+    return ok ? X[y * a.row_items + t + dx * a.G] : make_uint4(0, 0, 0, 0);
+  };
+  uint4 win[3][3];                                  // rows y-1, y, y+1; columns x-1, x, x+1
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) win[r + 1][c] = ld(y0 - 1 + r, c - 1);
+  const int y1 = min(y0 + kPosRows, a.H);
+  for (int y = y0; y < y1; ++y) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      win[0][c] = win[1][c];
+      win[1][c] = win[2][c];
+      win[2][c] = ld(y + 1, c - 1);
+    }
+    float acc[VEC], v[VEC];
+    unpack16<BF16>(win[1][1], v);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = v[e] + bias[e];
+#pragma unroll
+    for (int r = 0; r < 3; ++r)
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        unpack16<BF16>(win[r][c], v);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = fmaf(wt[e][r * 3 + c], v[e], acc[e]);
+      }
+    uint4 o;
+    if constexpr (BF16) {
+      o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    } else {
+      o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                     __float_as_uint(acc[3]));
+    }
+    O[y * a.row_items + t] = o;
   }
-  ((uint4*)a.out)[i] = o;
 }
 
 // LayerNorm over the C channels of each row (p3 §3.1 nn.LayerNorm): float32
@@ -134,8 +165,11 @@ hipError_t launch_pos_conv(const void* x, const float* w, const float* b, const 
   a.x = x; a.w = w; a.b = b; a.out = out;
   a.H = s.H; a.W = s.W; a.C = s.C;
   a.G = s.C / (bf16 ? 8 : 4);
-  a.total = (long long)s.B * s.H * s.W * a.G;
-  const dim3 grid((unsigned)((a.total + kThreads - 1) / kThreads));
+  a.row_items = s.W * a.G;
+  a.f_G = make_fastdiv(a.G);
+  if (s.H > 65535 || s.B > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.row_items + kThreads - 1) / kThreads),
+                  (unsigned)((s.H + kPosRows - 1) / kPosRows), (unsigned)s.B);
   if (bf16)
     hipLaunchKernelGGL(pos_conv_kernel<true>, grid, dim3(kThreads), 0, st, a);
   else

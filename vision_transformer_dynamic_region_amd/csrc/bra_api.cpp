@@ -351,8 +351,7 @@ bra_status bra_pos_conv(const void* x, const float* w, const float* b, int B, in
   if ((st = check_shape(B, H, W, C, 1, 0, 1, dtype, &s))) return st;
   if ((st = check_tensor(x, "x")) || (st = check_tensor(out, "out")) || (st = check_bias(b, "b")))
     return st;
-  if (!w) return fail(BRA_E_INVAL, "w is NULL");
-  if ((uintptr_t)w & 3u) return fail(BRA_E_INVAL, "w is not 4-byte aligned");
+  if ((st = check_tensor(w, "w"))) return st;
   if (dtype == BRA_F32 ? C % 4 : C % 8) return fail(BRA_E_UNSUPPORTED, "C=%d must be a multiple of %d", C, dtype == BRA_F32 ? 4 : 8);
   const size_t bytes = (size_t)B * H * W * C * elem_size(dtype);
   if (overlaps2(x, bytes, out, bytes)) return fail(BRA_E_INVAL, "out overlaps x");

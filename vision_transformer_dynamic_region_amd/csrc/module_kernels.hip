@@ -43,6 +43,7 @@ struct LinArgs {
   int T, K, N;
   int col_tiles, row_tiles, per_xcd;
   int col_groups;       // workgroups per row tile (each takes a share of the feature tiles)
+  int nbuf;             // W staging buffers (1 when a workgroup has one step)
 };
 
 // Y = X W^T + b on the matrix cores, computed as Y^T = W X^T so that a lane
@@ -61,9 +62,24 @@ struct LinArgs {
 // 128-byte line of a token's features is written by 8 adjacent lanes in one
 // store.  Epilogue EPI: 0 bias only, 1 bias then GELU (exact erf form), 2
 // bias then a residual tensor added; each rounds once to the output type.
+// GELU in its exact form, x Phi(x) = x/2 (1 + erf(x / sqrt 2)), with erf by
+// Abramowitz & Stegun 7.1.26 (absolute error below 1.5e-7): for z >= 0,
+// erfc(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 +
+// p z); 1 + erf(z) is 2 - erfc(z) for z >= 0 and erfc(-z) below.
+__device__ __forceinline__ float gelu_as(float v) {
+  const float z = v * 0.70710678118654752f, az = fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, az, 1.0f));
+  float pz = fmaf(t, 1.061405429f, -1.453152027f);
+  pz = fmaf(t, pz, 1.421413741f);
+  pz = fmaf(t, pz, -0.284496736f);
+  pz = fmaf(t, pz, 0.254829592f);
+  const float ec = t * pz * __builtin_amdgcn_exp2f(-az * az * 1.4426950408889634f);
+  return 0.5f * v * (z >= 0.f ? 2.0f - ec : ec);
+}
+
 template <int EPI>
 __device__ __forceinline__ float lin_act(float v) {
-  if constexpr (EPI == 1) return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+  if constexpr (EPI == 1) return gelu_as(v);
   return v;
 }
 
@@ -95,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinArgs a) {
   const int nch = (a.K + KCH - 1) / KCH;
   const int nsteps = (ct1 - ct0) * nch;
   const int bufb = kLinCols * min(a.K, KCH) * ES;  // bytes of one W staging buffer
-  unsigned char* ost = lds + 2 * bufb + wave * 32 * ORB;   // this wavefront's output tile
+  unsigned char* ost = lds + a.nbuf * bufb + wave * 32 * ORB;   // this wavefront's output tile
 
   uint4 wv[WPT];
   auto load_w = [&](int step) {                    // W block of a step into registers
@@ -370,7 +386,10 @@ hipError_t launch_linear(const void* x, int T, int K, const void* w, const float
   // K chunk: all of K up to 256 in bf16 (X read once), 64 for float32
   const int kch = !bf16 ? 64 : K <= 64 ? 64 : K <= 128 ? 128 : 256;
   const size_t orb = (size_t)kLinCols * ((epi == 2 || !bf16) ? 4 : es) + 16;
-  const size_t lds = (size_t)2 * kLinCols * (K < kch ? K : kch) * es + (size_t)kWaves * 32 * orb;
+  const int ct_per = (a.col_tiles + a.col_groups - 1) / a.col_groups;
+  a.nbuf = ct_per * ((K + kch - 1) / kch) > 1 ? 2 : 1;   // steps of a workgroup
+  const size_t lds = (size_t)a.nbuf * kLinCols * (K < kch ? K : kch) * es +
+                     (size_t)kWaves * 32 * orb;
 #define BRA_LIN(BB, KK, EE) \
   hipLaunchKernelGGL((linear_kernel<BB, KK, EE>), grid, dim3(kThreads), lds, st, a)
 #define BRA_LIN_E(BB, KK) \
