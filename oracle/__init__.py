@@ -6,6 +6,7 @@ leg may import it.  It shares no code with the HIP library.
 
 from .bra_oracle import (  # noqa: F401
     block_forward,
+    bra_backward,
     bra_forward,
     gelu,
     layer_norm,

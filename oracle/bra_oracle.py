@@ -96,6 +96,22 @@ Readings for the BiFormer block around the module (``block_forward``):
       LN2(x2), the hidden GELU output and x3 are layer outputs, stored per
       ``storage``.
 
+The backward pass with a fixed routing index (``bra_backward``): the pages
+train with the routing held fixed for a while (p2 §5 and p1 §5 keep the
+index constant; p2 §4 detaches the routing inputs unless diff_routing is
+set), so the index receives no gradient and the gradients of
+out = O(Q, K, V; idx) + LePE(V) are those of the attention and of the
+depthwise conv:
+
+  G1  Per query region and head, with p = softmax(s), s = scale q k^T over
+      the routed keys: dv = p^T do, dp = do v^T, ds = p * (dp - rowsum(p *
+      dp)), dq = scale ds k, dk = scale ds^T q; dk and dv are added into the
+      key tokens' rows (a key region routed from several query regions
+      collects all their terms).
+  G2  LePE: db = the sum of dout over the pixels, dw[c, i, j] = the sum of
+      dout * V shifted by (i - P, j - P) (zero outside), and dV gains the
+      transposed conv of dout with w.
+
 Parity pins for every function live in ``tests/test_oracle_pins.py``.
 """
 
@@ -121,6 +137,7 @@ __all__ = [
     "layer_norm",
     "gelu",
     "block_forward",
+    "bra_backward",
 ]
 
 
@@ -414,3 +431,69 @@ def block_forward(x, p: dict, heads: int, S: int, topk: int, route_scale: float 
         return {"x1": x1, "n1": n1, "mod": mod, "x2": x2, "n2": n2, "h": h, "out": out,
                 "idx": mod["idx"]}
     return out, mod["idx"]
+
+
+def bra_backward(Q, K, V, idx, heads: int, S: int, dout, w=None, bias=None,
+                 attn_scale: float | None = None) -> dict:
+    """Gradients of out = routed attention(Q, K, V; idx) + LePE(V) with the
+    routing index held fixed (readings G1, G2).
+
+    dout: [B, H, W, C], the gradient of the output.  Returns a dict with dQ,
+    dK, dV ([B, H, W, C]) and, when w is given, dw [C, ks, ks] and db [C]
+    (db is returned whether or not the forward pass had a bias).
+    """
+    Q = _f64(Q)
+    K = _f64(K)
+    V = _f64(V)
+    G = _f64(dout)
+    idx = np.asarray(idx)
+    B, H, W, C = Q.shape
+    if C % heads:
+        raise ValueError("heads must divide C")
+    d = C // heads
+    if attn_scale is None:
+        attn_scale = d ** -0.5
+    coords = [region_tokens(H, W, S, r) for r in range(S * S)]
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for b in range(B):
+        for r in range(S * S):
+            ys, xs = coords[r]
+            ky = np.concatenate([coords[s][0] for s in idx[b, r]])
+            kx = np.concatenate([coords[s][1] for s in idx[b, r]])
+            q = Q[b, ys, xs].reshape(-1, heads, d)
+            k = K[b, ky, kx].reshape(-1, heads, d)
+            v = V[b, ky, kx].reshape(-1, heads, d)
+            do = G[b, ys, xs].reshape(-1, heads, d)
+            s_ = attn_scale * np.einsum("nhd,mhd->hnm", q, k)
+            p = np.exp(s_ - s_.max(axis=-1, keepdims=True))
+            p = p / p.sum(axis=-1, keepdims=True)                   # [h, n, m]
+            dv = np.einsum("hnm,nhd->mhd", p, do)
+            dp = np.einsum("nhd,mhd->hnm", do, v)
+            ds = p * (dp - (p * dp).sum(axis=-1, keepdims=True))
+            dq = attn_scale * np.einsum("hnm,mhd->nhd", ds, k)
+            dk = attn_scale * np.einsum("hnm,nhd->mhd", ds, q)
+            dQ[b, ys, xs] += dq.reshape(-1, C)
+            # keys may repeat across (and, for a caller's index, within) rows
+            np.add.at(dK[b], (ky, kx), dk.reshape(-1, C))
+            np.add.at(dV[b], (ky, kx), dv.reshape(-1, C))
+    out = {"dQ": dQ, "dK": dK, "dV": dV}
+    if w is not None:
+        w = _f64(w)
+        ks = w.shape[-1]
+        P = ks // 2
+        Vp = np.zeros((B, H + 2 * P, W + 2 * P, C))
+        Vp[:, P:P + H, P:P + W] = V
+        Gp = np.zeros((B, H + 2 * P, W + 2 * P, C))
+        Gp[:, P:P + H, P:P + W] = G
+        dw = np.zeros((C, ks, ks))
+        for i in range(ks):
+            for j in range(ks):
+                dw[:, i, j] = np.sum(G * Vp[:, i:i + H, j:j + W], axis=(0, 1, 2))
+                # L[y, x] += w[i, j] V[y + i - P, x + j - P], so V[y', x'] feeds
+                # L[y' - i + P, x' - j + P]
+                dV += w[:, i, j] * Gp[:, 2 * P - i:2 * P - i + H, 2 * P - j:2 * P - j + W]
+        out["dw"] = dw
+        out["db"] = G.sum(axis=(0, 1, 2))
+    return out

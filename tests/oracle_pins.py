@@ -527,6 +527,91 @@ def pin_block_torch():
     _close(out, ref.numpy(), 1e-12, "block")
 
 
+# --------------------------------------------------------------------------
+# the backward pass with a fixed index (readings G1, G2)
+
+def _torch_bra_loss(Qt, Kt, Vt, wt, bt, idx, heads, S, scale, Gt):
+    """sum(out * dout) of the BRA forward written with torch ops: masked
+    dense attention over the routed regions (the mask of pin P1) plus
+    conv2d(groups = C) for LePE."""
+    import torch
+    import torch.nn.functional as F
+    B, H, W, C = Qt.shape
+    d = C // heads
+    reg = torch.from_numpy(_pixel_region(H, W, S))
+    out = torch.zeros_like(Qt)
+    for b in range(B):
+        allowed = torch.zeros(S * S, S * S, dtype=torch.bool)
+        for r in range(S * S):
+            allowed[r, torch.from_numpy(np.asarray(idx[b, r], dtype=np.int64))] = True
+        mask = allowed[reg][:, reg]                                  # [HW, HW]
+        q = Qt[b].reshape(H * W, heads, d).transpose(0, 1)
+        k = Kt[b].reshape(H * W, heads, d).transpose(0, 1)
+        v = Vt[b].reshape(H * W, heads, d).transpose(0, 1)
+        logits = scale * q @ k.transpose(1, 2)
+        logits = logits.masked_fill(~mask, float("-inf"))
+        o = torch.softmax(logits, dim=-1) @ v
+        out[b] = o.transpose(0, 1).reshape(H, W, C)
+    if wt is not None:
+        ks = wt.shape[-1]
+        lep = F.conv2d(Vt.permute(0, 3, 1, 2), wt[:, None], bt, padding=ks // 2, groups=C)
+        out = out + lep.permute(0, 2, 3, 1)
+    return (out * Gt).sum()
+
+
+def pin_backward_autograd():
+    """The fixed-index gradients equal torch autograd of the same forward
+    (masked dense attention + conv2d) in float64, with distinct routes per
+    row and a key region that no row routes to."""
+    import torch
+    B, H, W, C, heads, S, topk, ks = 2, 8, 8, 8, 2, 4, 3, 5
+    r = _rng(50)
+    Q, K, V, G = (r.normal(size=(B, H, W, C)) for _ in range(4))
+    w, b = r.normal(size=(C, ks, ks)) * 0.3, r.normal(size=C)
+    others = np.array([s for s in range(S * S) if s != 5])   # region 5: routed from nowhere
+    idx = np.stack([np.stack([r.permutation(others)[:topk] for _ in range(S * S)])
+                    for _ in range(B)]).astype(np.int32)
+    scale = (C // heads) ** -0.5
+    got = O.bra_backward(Q, K, V, idx, heads, S, G, w, b)
+    T = lambda a: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+    Qt, Kt, Vt, wt, bt = T(Q), T(K), T(V), T(w), T(b)
+    _torch_bra_loss(Qt, Kt, Vt, wt, bt, idx, heads, S, scale, torch.from_numpy(G)).backward()
+    for name, t in (("dQ", Qt), ("dK", Kt), ("dV", Vt), ("dw", wt), ("db", bt)):
+        _close(got[name], t.grad.numpy(), 1e-11, f"backward {name}")
+    ys, xs = O.region_tokens(H, W, S, 5)
+    assert np.all(got["dK"][:, ys, xs] == 0.0), "a key region routed from nowhere gets no dK"
+
+
+def pin_backward_finite_differences():
+    """Central differences of sum(out * dout) in float64 match the analytic
+    gradients at sampled coordinates of Q, K, V, w and b."""
+    B, H, W, C, heads, S, topk, ks = 1, 4, 4, 4, 2, 2, 2, 3
+    r = _rng(51)
+    Q, K, V, G = (r.normal(size=(B, H, W, C)) for _ in range(4))
+    w, b = r.normal(size=(C, ks, ks)) * 0.5, r.normal(size=C)
+    idx = np.array([[[0, 2], [1, 3], [3, 0], [2, 1]]], dtype=np.int32)
+    got = O.bra_backward(Q, K, V, idx, heads, S, G, w, b)
+
+    def loss(Q_, K_, V_, w_, b_):
+        out = O.routed_attention(Q_, K_, V_, idx, heads, S, (C // heads) ** -0.5) + O.lepe(V_, w_, b_)
+        return float(np.sum(out * G))
+
+    h = 1e-6
+    args = {"dQ": Q, "dK": K, "dV": V, "dw": w, "db": b}
+    order = ["dQ", "dK", "dV", "dw", "db"]
+    for name in order:
+        arr = args[name]
+        for flat in r.choice(arr.size, size=min(6, arr.size), replace=False):
+            pos = np.unravel_index(flat, arr.shape)
+            plus = [a.copy() for a in (Q, K, V, w, b)]
+            minus = [a.copy() for a in (Q, K, V, w, b)]
+            plus[order.index(name)][pos] += h
+            minus[order.index(name)][pos] -= h
+            fd = (loss(*plus) - loss(*minus)) / (2 * h)
+            assert abs(fd - got[name][pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd,
+                                                                         got[name][pos])
+
+
 ALL_PINS = [
     pin_golden, pin_partition_layout, pin_pool_avgpool, pin_affinity_orientation,
     pin_topk_bruteforce, pin_scale_invariance, pin_masked_dense,
@@ -535,4 +620,5 @@ ALL_PINS = [
     pin_module_golden, pin_linear_torch, pin_module_reduces_to_bra,
     pin_pool_commutes_with_projection, pin_round_storage_torch, pin_module_storage,
     pin_layer_norm_torch, pin_gelu_torch, pin_block_torch,
+    pin_backward_autograd, pin_backward_finite_differences,
 ]

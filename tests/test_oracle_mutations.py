@@ -11,7 +11,7 @@ from oracle_pins import ALL_PINS
 _orig = {name: getattr(O, name) for name in
          ("region_mean", "region_affinity", "topk_route", "routed_attention", "lepe",
           "region_tokens", "linear", "module_forward", "round_storage", "layer_norm", "gelu",
-          "block_forward")}
+          "block_forward", "bra_backward")}
 
 
 def _mean_as_sum(X, S):
@@ -243,6 +243,54 @@ def _block_post_norm(x, p, heads, S, topk, route_scale=None, attn_scale=None, st
     return (dict(out=out, idx=idx) if return_parts else (out, idx))
 
 
+def _bw_scale_dk_twice(Q, K, V, idx, heads, S, dout, w=None, bias=None, attn_scale=None):
+    g = _orig["bra_backward"](Q, K, V, idx, heads, S, dout, w, bias, attn_scale)
+    g["dK"] = g["dK"] * 2.0
+    return g
+
+
+def _bw_no_softmax_term(Q, K, V, idx, heads, S, dout, w=None, bias=None, attn_scale=None):
+    """ds = p * dp (the rowsum term dropped): recompute dQ/dK that way."""
+    g = _orig["bra_backward"](Q, K, V, idx, heads, S, dout, w, bias, attn_scale)
+    Q_, K_, V_, G = (np.asarray(a, dtype=np.float64) for a in (Q, K, V, dout))
+    B, H, W, C = Q_.shape
+    d = C // heads
+    sc = d ** -0.5 if attn_scale is None else attn_scale
+    dQ = np.zeros_like(Q_)
+    for b in range(B):
+        for r in range(S * S):
+            ys, xs = O.region_tokens(H, W, S, r)
+            ky = np.concatenate([O.region_tokens(H, W, S, s)[0] for s in idx[b, r]])
+            kx = np.concatenate([O.region_tokens(H, W, S, s)[1] for s in idx[b, r]])
+            q = Q_[b, ys, xs].reshape(-1, heads, d)
+            k = K_[b, ky, kx].reshape(-1, heads, d)
+            v = V_[b, ky, kx].reshape(-1, heads, d)
+            do = G[b, ys, xs].reshape(-1, heads, d)
+            lg = sc * np.einsum("nhd,mhd->hnm", q, k)
+            p = np.exp(lg - lg.max(-1, keepdims=True))
+            p /= p.sum(-1, keepdims=True)
+            ds = p * np.einsum("nhd,mhd->hnm", do, v)
+            dQ[b, ys, xs] = (sc * np.einsum("hnm,mhd->nhd", ds, k)).reshape(-1, C)
+    g["dQ"] = dQ
+    return g
+
+
+def _bw_lepe_not_transposed(Q, K, V, idx, heads, S, dout, w=None, bias=None, attn_scale=None):
+    g = _orig["bra_backward"](Q, K, V, idx, heads, S, dout, None, None, attn_scale)
+    if w is not None:
+        g["dV"] = g["dV"] + O.lepe(dout, w)              # correlation instead of its transpose
+        full = _orig["bra_backward"](Q, K, V, idx, heads, S, dout, w, bias, attn_scale)
+        g["dw"], g["db"] = full["dw"], full["db"]
+    return g
+
+
+def _bw_dw_unshifted(Q, K, V, idx, heads, S, dout, w=None, bias=None, attn_scale=None):
+    g = _orig["bra_backward"](Q, K, V, idx, heads, S, dout, w, bias, attn_scale)
+    if w is not None:
+        g["dw"] = g["dw"][:, ::-1, ::-1].copy()
+    return g
+
+
 MUTANTS = {
     "region_mean": [_mean_as_sum, _mean_column_major],
     "region_affinity": [_affinity_transposed],
@@ -258,6 +306,8 @@ MUTANTS = {
     "layer_norm": [_ln_unbiased, _ln_no_shift],
     "gelu": [_gelu_tanh],
     "block_forward": [_block_no_pos_residual, _block_post_norm],
+    "bra_backward": [_bw_scale_dk_twice, _bw_no_softmax_term, _bw_lepe_not_transposed,
+                     _bw_dw_unshifted],
 }
 CASES = [(name, m) for name, ms in MUTANTS.items() for m in ms]
 
