@@ -231,6 +231,40 @@ bra_status bra_block_forward(const void* x, int B, int H, int W, int C,
                              float attn_scale, void* out, int32_t* idx,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Backward pass with the routing index held fixed (training with frozen
+ * routing: p2 §4 detaches the routing inputs unless diff_routing is set;
+ * p1 §5 and p2 §5 keep the index constant).  The index gets no gradient.
+ * For out = attention(Q, K, V; idx) + LePE(V):
+ *   dV includes the LePE term (the transposed depthwise conv of dout);
+ *   dK, dV collect the terms of every query region that routes to a key;
+ *   dw = sum over pixels of dout * shifted V, db = sum of dout.
+ * bf16 only (BRA_E_UNSUPPORTED for f32), topk * n <= 256 keys per query.
+ * Deterministic: every sum has a fixed order, no atomics.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of workspace bra_attend_backward needs (lepe_ks 0 without LePE):
+ * per-pixel softmax statistics, the inverse routing lists, and with LePE the
+ * float32 LePE part of dV and per-row partial sums of dw and db. */
+size_t bra_backward_workspace_bytes(int B, int H, int W, int C, int heads,
+                                    int S, int topk, int lepe_ks);
+
+/* Gradients of bra_attend's output (with LePE when lepe_w is not NULL).
+ *   q, k, v, dout [B,H,W,C] bf16, device; idx int32 [B, S*S, topk] (entries
+ *   clamped into [0, S*S) as in bra_attend); attn_scale as in bra_attend.
+ *   dq, dk, dv out: [B,H,W,C] bf16, device, overlapping no input or each
+ *   other.  dlepe_w out: float32 [C, ks, ks] (required with lepe_w);
+ *   dlepe_b out: float32 [C] or NULL.  ws: device workspace of at least
+ *   bra_backward_workspace_bytes(...) bytes. */
+bra_status bra_attend_backward(const void* q, const void* k, const void* v,
+                               const int32_t* idx, const void* dout, int B,
+                               int H, int W, int C, int heads, int S, int topk,
+                               bra_dtype dtype, float attn_scale,
+                               const float* lepe_w, int lepe_ks, void* dq,
+                               void* dk, void* dv, float* dlepe_w,
+                               float* dlepe_b, void* ws, size_t ws_bytes,
+                               void* stream);
+
 /* Static text for a status code. */
 const char* bra_strerror(int status);
 

@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
     for n in ("bra_route", "bra_attend", "bra_forward", "bra_lepe", "bra_workspace_bytes",
               "bra_strerror", "bra_last_error", "bra_linear", "bra_module_workspace_bytes",
               "bra_module_forward", "bra_layer_norm", "bra_block_workspace_bytes",
-              "bra_block_forward", "bra_pos_conv"):
+              "bra_block_forward", "bra_pos_conv", "bra_backward_workspace_bytes",
+              "bra_attend_backward"):
         assert n in names
 
 
@@ -259,3 +260,23 @@ def test_pos_conv_rejects(lib):
     assert lib.bra_pos_conv(P, P2, None, 2, 8, 8, 60, BF16, P4, None) == UNSUP
     assert lib.bra_pos_conv(P, P2, None, 2, 8, 8, 64, BF16, P + 64, None) == INVAL
     assert lib.bra_pos_conv(P, P2, P3 + 4, 2, 8, 8, 64, BF16, P4, None) == INVAL
+
+
+def test_backward_rejects(lib):
+    def call(**kw):
+        a = dict(q=P, k=P2, v=P3, idx=P4, dout=0x50000000, dt=BF16, scale=0.17, w=None, ks=5,
+                 dq=0x70000000, dk=0x74000000, dv=0x78000000, dw=None, db=None, ws=0x7C000000,
+                 wsb=1 << 26, C=64, heads=2, topk=2)
+        a.update(kw)
+        return lib.bra_attend_backward(a["q"], a["k"], a["v"], a["idx"], a["dout"], 2, 8, 8, a["C"],
+                                       a["heads"], 2, a["topk"], a["dt"], a["scale"], a["w"], a["ks"],
+                                       a["dq"], a["dk"], a["dv"], a["dw"], a["db"], a["ws"],
+                                       a["wsb"], None)
+    assert call(dt=F32) == UNSUP and "bf16" in lib.bra_last_error().decode()
+    assert call(dq=P2) == INVAL and "overlaps" in lib.bra_last_error().decode()
+    assert call(dk=0x70000000) == INVAL
+    assert call(w=P, dw=None) == INVAL and "dlepe_w" in lib.bra_last_error().decode()
+    assert call(wsb=16) == WSERR
+    assert call(scale=0.0) == INVAL
+    assert lib.bra_backward_workspace_bytes(2, 8, 8, 64, 2, 2, 2, 5) > \
+        lib.bra_backward_workspace_bytes(2, 8, 8, 64, 2, 2, 2, 0) > 0

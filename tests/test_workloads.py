@@ -5,6 +5,7 @@ import torch
 
 from vision_transformer_dynamic_region_amd.workloads import (WORKLOADS, bf16_bits,
                                                               bf16_round, make_inputs,
+                                                              make_backward_inputs,
                                                               make_block_inputs,
                                                               make_module_inputs)
 
@@ -80,3 +81,16 @@ def test_block_inputs_seeded_and_shaped():
     for n in ("w_fc1", "w_fc2"):
         assert np.array_equal(a[n], bf16_round(a[n]))
     assert np.array_equal(a["x"], make_module_inputs(wl)["x"])
+
+
+def test_backward_inputs_seeded_and_valid():
+    wl = WORKLOADS["tiny"]
+    a, b = make_backward_inputs(wl), make_backward_inputs(wl)
+    for n in ("q", "k", "v", "dout"):
+        assert a[n].shape == (1, 28, 28, 64) and a[n].dtype == np.float32
+        assert np.array_equal(a[n], b[n]) and np.array_equal(a[n], bf16_round(a[n]))
+    assert np.array_equal(a["q"], bf16_round(make_inputs(wl)["q"]))
+    idx = a["idx"]
+    assert idx.shape == (1, 49, 4) and idx.dtype == np.int32 and np.array_equal(idx, b["idx"])
+    assert idx.min() >= 0 and idx.max() < 49
+    assert all(len(set(row)) == 4 for row in idx[0])

@@ -18,7 +18,7 @@ import os
 __all__ = ["BraError", "lib_path", "load", "workspace_bytes", "route", "attend",
            "forward", "lepe", "linear", "module_workspace_bytes", "module_forward",
            "layer_norm", "pos_conv", "block_workspace_bytes", "block_forward", "BLOCK_PARAMS",
-           "STATUS"]
+           "attend_backward", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -46,6 +46,9 @@ _SIGNATURES = {
     "bra_block_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "bra_block_forward": (_i, [_vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _f, _f, _vp, _vp, _vp,
                                _sz, _vp]),
+    "bra_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "bra_attend_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f,
+                                 _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bra_strerror": (ctypes.c_char_p, [_i]),
     "bra_last_error": (ctypes.c_char_p, []),
 }
@@ -424,3 +427,39 @@ def block_forward(x, params: dict, heads: int, S: int, topk: int,
                                     idx.data_ptr(), workspace.data_ptr(),
                                     workspace.numel() * workspace.element_size(), _stream(x)))
     return out, idx
+
+
+def attend_backward(q, k, v, idx, dout, heads: int, S: int, attn_scale: float | None = None,
+                    lepe_w=None, workspace=None):
+    """Gradients of attend(q, k, v, idx, heads, S, lepe_w=lepe_w) with the
+    routing index held fixed (bra_attend_backward, bf16).  Returns (dq, dk,
+    dv) or, with lepe_w, (dq, dk, dv, dw, db)."""
+    import torch
+    B, H, W, C = _bhwc(q)
+    dt = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _dev(t, n, q.dtype)
+        if tuple(t.shape) != (B, H, W, C):
+            raise ValueError("q, k, v, dout must have the same shape")
+    _dev(idx, "idx", torch.int32)
+    if idx.dim() != 3 or idx.shape[0] != B or idx.shape[1] != S * S:
+        raise ValueError("idx must be [B, S*S, topk]")
+    topk = int(idx.shape[2])
+    if attn_scale is None:
+        attn_scale = (C // heads) ** -0.5
+    wp, _, ks = _lepe_args(lepe_w, None, C)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dw = torch.empty_like(lepe_w) if lepe_w is not None else None
+    db = torch.empty(C, dtype=torch.float32, device=q.device) if lepe_w is not None else None
+    if workspace is None:
+        need = int(load().bra_backward_workspace_bytes(B, H, W, C, heads, S, topk, ks))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace")
+    _check(load().bra_attend_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
+                                      dout.data_ptr(), B, H, W, C, heads, S, topk, dt,
+                                      float(attn_scale), wp, ks, dq.data_ptr(), dk.data_ptr(),
+                                      dv.data_ptr(), dw.data_ptr() if dw is not None else None,
+                                      db.data_ptr() if db is not None else None,
+                                      workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size(), _stream(q)))
+    return (dq, dk, dv, dw, db) if lepe_w is not None else (dq, dk, dv)

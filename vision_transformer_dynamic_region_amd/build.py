@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbra.so")
 SOURCES = ["route_kernels.hip", "attend_kernels.hip", "region_kernels.hip", "module_kernels.hip",
-           "block_kernels.hip",
+           "block_kernels.hip", "backward_kernels.hip",
            "bra_api.cpp"]
 # per-file extra flags: the attention file assumes finite, non-NaN data (NaN
 # inputs give unspecified outputs) so that max/min need no NaN quieting, and

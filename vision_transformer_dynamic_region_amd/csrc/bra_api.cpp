@@ -514,6 +514,60 @@ bra_status bra_block_forward(const void* x, int B, int H, int W, int C, int head
                     "fc2 launch");
 }
 
+size_t bra_backward_workspace_bytes(int B, int H, int W, int C, int heads, int S, int topk,
+                                    int lepe_ks) {
+  if (B < 1 || H < 1 || W < 1 || C < 1 || heads < 1 || S < 1 || topk < 1 || lepe_ks < 0) return 0;
+  return bra::bwd_workspace_bytes(B, H, W, C, heads, S, topk, lepe_ks, lepe_ks > 0);
+}
+
+bra_status bra_attend_backward(const void* q, const void* k, const void* v, const int32_t* idx,
+                               const void* dout, int B, int H, int W, int C, int heads, int S,
+                               int topk, bra_dtype dtype, float attn_scale, const float* lepe_w,
+                               int lepe_ks, void* dq, void* dk, void* dv, float* dlepe_w,
+                               float* dlepe_b, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  bra::Shape s;
+  bra_status st;
+  if (heads < 1) return fail(BRA_E_INVAL, "heads=%d must be positive", heads);
+  if ((st = check_shape(B, H, W, C, S, heads, topk, dtype, &s))) return st;
+  if (dtype != BRA_BF16) return fail(BRA_E_UNSUPPORTED, "the backward pass runs in bf16 only");
+  if ((st = check_tensor(q, "q")) || (st = check_tensor(k, "k")) || (st = check_tensor(v, "v")) ||
+      (st = check_tensor(dout, "dout")) || (st = check_tensor(dq, "dq")) ||
+      (st = check_tensor(dk, "dk")) || (st = check_tensor(dv, "dv")))
+    return st;
+  if (!idx) return fail(BRA_E_INVAL, "idx is NULL");
+  if ((uintptr_t)idx & 3u) return fail(BRA_E_INVAL, "idx is not 4-byte aligned");
+  if (!(attn_scale > 0.f) || !std::isfinite(attn_scale))
+    return fail(BRA_E_INVAL, "attn_scale=%g must be positive and finite", (double)attn_scale);
+  if (s.topk * s.n > 256)
+    return fail(BRA_E_UNSUPPORTED, "topk*n=%d routed keys per query; the backward pass takes up to 256",
+                s.topk * s.n);
+  if (lepe_w) {
+    if ((st = check_lepe_args(lepe_w, nullptr, lepe_ks, s))) return st;
+    if (!dlepe_w) return fail(BRA_E_INVAL, "dlepe_w is NULL while lepe_w is given");
+    if ((uintptr_t)dlepe_w & 3u) return fail(BRA_E_INVAL, "dlepe_w is not 4-byte aligned");
+    if (C > 512) return fail(BRA_E_UNSUPPORTED, "the LePE gradient takes C <= 512");
+  }
+  if (dlepe_b && ((uintptr_t)dlepe_b & 3u)) return fail(BRA_E_INVAL, "dlepe_b is not 4-byte aligned");
+  const size_t tb = (size_t)B * H * W * C * 2;
+  const void* ins[4] = {q, k, v, dout};
+  void* outs[3] = {dq, dk, dv};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 4; ++j)
+      if (overlaps2(outs[i], tb, ins[j], tb)) return fail(BRA_E_INVAL, "a gradient overlaps an input");
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps2(outs[i], tb, outs[j], tb)) return fail(BRA_E_INVAL, "two gradients overlap");
+  }
+  const size_t need = bra::bwd_workspace_bytes(B, H, W, C, heads, S, topk, lepe_ks, lepe_w != nullptr);
+  if (!ws) return fail(BRA_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned16(ws)) return fail(BRA_E_WORKSPACE, "workspace is not 16-byte aligned");
+  if (ws_bytes < need) return fail(BRA_E_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+  return hip_status(bra::launch_backward(q, k, v, idx, dout, s, attn_scale, lepe_w, lepe_ks, dq, dk,
+                                         dv, lepe_w ? dlepe_w : nullptr, lepe_w ? dlepe_b : nullptr,
+                                         ws, (hipStream_t)stream),
+                    "backward launch");
+}
+
 const char* bra_strerror(int status) {
   switch (status) {
     case BRA_OK: return "ok";

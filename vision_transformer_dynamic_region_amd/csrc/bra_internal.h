@@ -35,6 +35,16 @@ hipError_t launch_linear(const void* x, int T, int K, const void* w, const float
 hipError_t launch_pos_conv(const void* x, const float* w, const float* b, const Shape& s,
                            bool bf16, void* out, hipStream_t st);
 
+// Backward pass with a fixed routing index (bf16, head width 32, topk * n
+// <= 256): dq, dk, dv (bf16, dV with the LePE term when w is not null) and
+// dw, db (float32; db may be null).  ws holds bwd_workspace_bytes.
+size_t bwd_workspace_bytes(int B, int H, int W, int C, int heads, int S, int topk, int ks,
+                           bool lepe);
+hipError_t launch_backward(const void* q, const void* k, const void* v, const int32_t* idx,
+                           const void* dout, const Shape& s, float attn_scale, const float* w,
+                           int ks, void* dq, void* dk, void* dv, float* dw, float* db, void* ws,
+                           hipStream_t st);
+
 // LayerNorm of each of `rows` rows of C channels (biased variance, eps).
 // layer_norm_shape says whether C is supported and how rows are split.
 bool layer_norm_shape(int C, bool bf16, int* lanes_per_row, int* groups_per_lane);

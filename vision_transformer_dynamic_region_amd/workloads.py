@@ -31,6 +31,14 @@ MLP's fc1 ~ N(0, C**-0.5) [3C, C] (seed + 19) with bias N(0, 0.1) (seed + 20)
 and fc2 ~ N(0, (3C)**-0.5) [C, 3C] (seed + 21) with bias N(0, 0.1) (seed + 22);
 conv and LayerNorm parameters and biases are float32, fc weights follow the
 workload dtype.
+
+The backward pass (bf16 only) takes Q, K, V and w as above, all rounded to
+bf16 whatever the workload's dtype, an output gradient dout ~ N(0, 1)
+rounded to bf16 (seed + 23), and a routing index drawn uniformly: for each
+image and query region, topk distinct regions in random order (one
+permutation per row, generator seed + 24).  The index is an input of the
+backward pass, so any valid index tests it; a routing computed by the
+forward pass is used where the timing should see its skew.
 """
 
 from __future__ import annotations
@@ -40,7 +48,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "bf16_round", "bf16_bits", "make_inputs",
-           "make_module_inputs", "make_block_inputs", "workload"]
+           "make_module_inputs", "make_block_inputs", "make_backward_inputs", "workload"]
 
 
 @dataclass(frozen=True)
@@ -208,4 +216,24 @@ def make_block_inputs(wl: Workload, seed_base: int | None = None):
            "b_fc1": f32(_normal(base + 20, (3 * C,), 0.1)),
            "w_fc2": rnd(_normal(base + 21, (C, 3 * C), (3 * C) ** -0.5)),
            "b_fc2": f32(_normal(base + 22, (C,), 0.1))}
+    return out
+
+
+def make_backward_inputs(wl: Workload, seed_base: int | None = None):
+    """Draw the backward pass's inputs for a workload: ``q``, ``k``, ``v``
+    [B, H, W, C] and ``dout`` (bf16-rounded float32), ``w`` [C, ks, ks]
+    float32 (None when the workload has no LePE) and ``idx`` int32
+    [B, S*S, topk] with distinct regions in each row."""
+    base = 1000 * wl.index if seed_base is None else seed_base
+    x = make_inputs(wl, seed_base)
+    out = {n: bf16_round(x[n]) for n in ("q", "k", "v")}
+    out["w"] = x["w"]
+    out["dout"] = bf16_round(_normal(base + 23, (wl.B, wl.H, wl.W, wl.C)).astype(np.float32))
+    rng = np.random.default_rng(base + 24)
+    R = wl.S * wl.S
+    idx = np.empty((wl.B, R, wl.topk), dtype=np.int32)
+    for b in range(wl.B):
+        for r in range(R):
+            idx[b, r] = rng.permutation(R)[:wl.topk]
+    out["idx"] = idx
     return out
