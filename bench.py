@@ -60,10 +60,11 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="st1", choices=["tiny", "st1", "st2", "st3", "dense"])
-    p.add_argument("--path", default="bra", choices=["bra", "module", "block"],
+    p.add_argument("--path", default="bra", choices=["bra", "module", "block", "backward"],
                    help="bra: the BRA forward pass on given Q, K, V (the default line); module: "
                         "the module around it (Q/K/V projections of x, BRA, output projection); "
-                        "block: one BiFormer block (position conv, LN, module, LN, MLP)")
+                        "block: one BiFormer block (position conv, LN, module, LN, MLP); "
+                        "backward: gradients of the BRA forward (with LePE) for a fixed index")
     p.add_argument("--sets", type=int, default=0,
                    help="input copies rotated across steps (0: enough to exceed the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -375,6 +376,102 @@ def run_block(a, wl) -> int:
     return 0
 
 
+def run_backward(a, wl) -> int:
+    """One step = bra_attend_backward over one batch (bf16): dQ, dK, dV with
+    the LePE term, dw and db, for the routing index that bra_route computes
+    from the same Q and K (so the inverse lists see the forward's skew)."""
+    import numpy as np
+    import torch
+
+    import vision_transformer_dynamic_region_amd as bra
+    from vision_transformer_dynamic_region_amd.workloads import bf16_bits, make_backward_inputs
+
+    dev = torch.device("cuda:0")
+    x = make_backward_inputs(wl)
+    up = lambda arr: torch.from_numpy(bf16_bits(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+    q0, k0, v0, g0 = (up(x[n]) for n in ("q", "k", "v", "dout"))
+    w = torch.from_numpy(x["w"]).to(dev)
+    idx = bra.route(q0, k0, wl.S, wl.topk)
+    B, H, W, C = wl.B, wl.H, wl.W, wl.C
+    wsb = int(bra.load().bra_backward_workspace_bytes(B, H, W, C, wl.heads, wl.S, wl.topk,
+                                                      wl.lepe_ks))
+    tb = B * H * W * C * 2
+    set_bytes = 7 * tb + wsb
+    sets = a.sets or max(1, -(-3 * MALL_BYTES // set_bytes))
+    bufs = [dict(q=q0.clone(), k=k0.clone(), v=v0.clone(), g=g0.clone(),
+                 ws=torch.empty(wsb, dtype=torch.uint8, device=dev)) for _ in range(sets)]
+    outs = [(torch.empty_like(q0), torch.empty_like(q0), torch.empty_like(q0),
+             torch.empty_like(w), torch.empty(C, dtype=torch.float32, device=dev))
+            for _ in range(sets)]
+    torch.cuda.synchronize()
+    log(f"backward: {sets} sets of {set_bytes / 1e6:.1f} MB (q, k, v, dout, dq, dk, dv, "
+        f"workspace) rotated per step")
+    L = bra.load()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step(i):
+        b, o = bufs[i % sets], outs[i % sets]
+        st = L.bra_attend_backward(b["q"].data_ptr(), b["k"].data_ptr(), b["v"].data_ptr(),
+                                   idx.data_ptr(), b["g"].data_ptr(), B, H, W, C, wl.heads, wl.S,
+                                   wl.topk, 1, wl.d ** -0.5, w.data_ptr(), wl.lepe_ks,
+                                   o[0].data_ptr(), o[1].data_ptr(), o[2].data_ptr(),
+                                   o[3].data_ptr(), o[4].data_ptr(), b["ws"].data_ptr(), wsb, sp)
+        if st != 0:
+            raise RuntimeError(L.bra_last_error().decode())
+
+    for i in range(a.warmup):
+        step(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(a.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    log(f"backward: {ms:.4f} ms/step")
+    # minimum traffic of the whole pass: q, k, v, dout read once, dq, dk, dv
+    # written once (dw, db and the saved statistics are small)
+    alg = 7 * tb
+    gbs = alg / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "BRA backward tokens/s (dQ, dK, dV, LePE dw/db; fixed routing), 1 GPU",
+        "value": wl.tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name} backward: B={B} H=W={H} C={C} heads={wl.heads} "
+                               f"S={wl.S} topk={wl.topk} LePE {wl.lepe_ks}x{wl.lepe_ks}",
+                   "tokens_per_step": wl.tokens, "input_sets_rotated": sets},
+        "roofline": {"kernel": "bra_attend_backward (all launches)", "bound": "hbm",
+                     "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": alg},
+    }
+    if not a.no_cpu_baseline:
+        import oracle as O
+        log("timing the fp64 oracle backward on the host")
+        idx_h = idx.cpu().numpy()
+        ru0 = resource.getrusage(resource.RUSAGE_SELF)
+        t0 = time.perf_counter()
+        nb, reps = 1, 0
+        while time.perf_counter() - t0 < a.cpu_seconds and reps < 50:
+            O.bra_backward(x["q"][:nb], x["k"][:nb], x["v"][:nb], idx_h[:nb], wl.heads, wl.S,
+                           x["dout"][:nb], x["w"])
+            reps += 1
+        dt = time.perf_counter() - t0
+        ru1 = resource.getrusage(resource.RUSAGE_SELF)
+        cpu = (ru1.ru_utime - ru0.ru_utime) + (ru1.ru_stime - ru0.ru_stime)
+        tokens = nb * H * W * reps
+        res["cpu_baseline"] = {"value": tokens / dt, "unit": "tokens/s",
+                               "cores": max(1, int(round(cpu / dt))), "kind": "oracle",
+                               "sample": (f"{wl.name} backward: 1 image x {reps} passes ({tokens} "
+                                          f"tokens), fp64 oracle bra_backward in {dt:.1f} s")}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     a = parse()
     if a.traffic_from:
@@ -401,6 +498,8 @@ def main() -> int:
         return run_module(a, wl)
     if a.path == "block":
         return run_block(a, wl)
+    if a.path == "backward":
+        return run_backward(a, wl)
     dev = torch.device("cuda:0")
     log(f"workload {wl}")
     x = make_inputs(wl)

@@ -244,8 +244,8 @@ bra_status bra_block_forward(const void* x, int B, int H, int W, int C,
  * ------------------------------------------------------------------------ */
 
 /* Bytes of workspace bra_attend_backward needs (lepe_ks 0 without LePE):
- * per-pixel softmax statistics, the inverse routing lists, and with LePE the
- * float32 LePE part of dV and per-row partial sums of dw and db. */
+ * per-pixel softmax statistics and, with LePE, the float32 LePE term of dV
+ * and float32 partial sums of dw and db. */
 size_t bra_backward_workspace_bytes(int B, int H, int W, int C, int heads,
                                     int S, int topk, int lepe_ks);
 

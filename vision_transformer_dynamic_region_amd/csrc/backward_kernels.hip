@@ -13,8 +13,8 @@
 // dk = scale ds^T q.  Two kernels, no atomics, a fixed order of every sum:
 //   bwd_dq_kernel   per (image, query region, head): all routed keys in
 //                   LDS, 16 queries per wavefront; s and dp on the matrix
-//                   cores, the softmax in float32, dq = scale K^T ds^T with
-//                   ds split into hi + lo bf16 operands;
+//                   cores, the softmax in float32 (two sweeps), dq = scale
+//                   K^T ds^T with ds split into hi + lo bf16 operands;
 //                   writes dq and each query's log2-sum-exp and D;
 //   bwd_dkv_kernel  per (image, key region, head): 16 keys per wavefront
 //                   held as operands; walks the query regions that route to
@@ -22,10 +22,10 @@
 //                   order), recomputes p from the saved log-sum-exp and
 //                   accumulates dv^T = do^T p and dk^T = q^T ds in
 //                   registers (p and ds as hi + lo bf16 operands); adds the
-//                   LePE term of dV before its single rounding.
-// The LePE gradient: dV_L is the transposed depthwise conv of dout (float32,
-// consumed by bwd_dkv_kernel); dw and db are sums over the pixels, per image
-// row first, then over the rows.
+//                   LePE term of dV (the transposed depthwise conv of dout)
+//                   before its single rounding.
+// dw and db are sums over the pixels: float32 partial sums per workgroup
+// (a strip of rows of a few columns), then float64 sums of the partials.
 
 #include "device_common.h"
 
@@ -59,6 +59,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 __device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v.x, v.y);
 }
 
 // A [row][32 channel] bf16 tile, 64 bytes a row, 16-byte chunk c of row r
@@ -112,9 +116,7 @@ struct BwArgs {
   uint16_t* dv;
   float* lse;             // [B, H, W, heads]: log2-sum-exp of the scaled logits
   float* dd;              // [B, H, W, heads]: D = rowsum(p dp)
-  const float* dv_lepe;   // [B, H, W, C] float32 or null
-  const int32_t* inv_off; // [B, R + 1] offsets into inv_rows
-  const int32_t* inv_rows;// [B, R * topk] query regions routing to each key region
+  const float* dv_lepe;   // [B, H, W, C] float32: the LePE term of dV, or null
   int B, H, W, C, S, R, hs, ws, n, heads, topk;
   float scale, scale_log2;
 };
@@ -126,11 +128,16 @@ __device__ __forceinline__ int tok_off(const BwArgs& a, int r, int t) {
   return ((ry * a.hs + ty) * a.W + rx * a.ws + tx) * a.C;
 }
 
-template <int NH>                        // 32-key steps: KC rounded up to 32 * NH
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a) {
+// Query-centric pass, two sweeps over the routed keys held in LDS: the
+// first keeps a running maximum, sum of exponentials and sum of p * dp per
+// lane (each lane sees a quarter of a query's keys) and combines the four
+// lanes of a query at the end, giving its log-sum-exp and D; the second
+// recomputes s and dp, forms ds = p (dp - D) and accumulates dq^T = K^T ds^T.
+// Nothing is held per key, so the register count does not grow with topk * n.
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH) {
   extern __shared__ __align__(16) unsigned char lds[];
   uint16_t* Ks = (uint16_t*)lds;
-  constexpr int KCP = 32 * NH;
+  const int KCP = 32 * NH;
   const int KC = a.topk * a.n;
   uint16_t* Vs = Ks + KCP * kHd;
   const int u = blockIdx.x;
@@ -141,6 +148,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a) {
   const auto Kr = rsrc(a.k + (size_t)b * img, img * 2), Vr = rsrc(a.v + (size_t)b * img, img * 2);
   const auto Qr = rsrc(a.q + (size_t)b * img, img * 2), Gr = rsrc(a.dout + (size_t)b * img, img * 2);
   const int32_t* route = a.idx + (size_t)br * a.topk;
+  const int nqb = (a.n + 15) / 16;
+  auto qoff_of = [&](int qb) -> uint32_t {
+    const int q = 16 * qb + lq;
+    return (qb < nqb && q < a.n) ? (tok_off(a, r, q) + h * kHd + 8 * lg) * 2 : kBwOob;
+  };
+  // the first query block's operands are in flight during the staging
+  uint32_t qoff = qoff_of(wave);
+  uint4 qn = ld16(Qr, qoff), gn = ld16(Gr, qoff);
   // routed keys (regions in route order, tokens row-major), zero past KC
   for (int e = tid; e < KCP * 4; e += kThreads) {
     const int kk = e >> 2, c = e & 3;
@@ -154,56 +169,77 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a) {
   }
   __syncthreads();
   const float c2 = a.scale_log2;
-  const int nqb = (a.n + 15) / 16;
   for (int qb = wave; qb < nqb; qb += kWaves) {
     const int q = 16 * qb + lq;
     const bool qok = q < a.n;
-    const uint32_t qoff = qok ? (tok_off(a, r, q) + h * kHd + 8 * lg) * 2 : kBwOob;
-    const bf16x8 qop = __builtin_bit_cast(bf16x8, ld16(Qr, qoff));
-    const bf16x8 gop = __builtin_bit_cast(bf16x8, ld16(Gr, qoff));
-    // s^T and dp^T: lane holds keys 16 kb + 4 lg + e of query lq
-    float s[KCP / 4], dp[KCP / 4];
-    float m = -3.0e38f;
+    const bf16x8 qop = __builtin_bit_cast(bf16x8, qn);
+    const bf16x8 gop = __builtin_bit_cast(bf16x8, gn);
+    qoff = qoff_of(qb + kWaves);
+    qn = ld16(Qr, qoff);
+    gn = ld16(Gr, qoff);
+    // sweep 1: lane-local running max m, sum l of 2^((s - m) c2), sum D of
+    // those weights times dp (keys 32 hh + 16 half + 4 lg + e of query lq)
+    float m = -3.0e38f, l = 0.f, D = 0.f;
+    for (int hh = 0; hh < NH; ++hh) {
+      float sv[8], pv[8];
 #pragma unroll
-    for (int kb = 0; kb < KCP / 16; ++kb) {
-      const int key = 16 * kb + lq;
-      const f32x4 sv = mfma16(row_op(Ks, key, lg), qop, f32x4{0.f, 0.f, 0.f, 0.f});
-      const f32x4 pv = mfma16(row_op(Vs, key, lg), gop, f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int half = 0; half < 2; ++half) {
+        const int key = 32 * hh + 16 * half + lq;
+        const f32x4 s4 = mfma16(row_op(Ks, key, lg), qop, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 p4 = mfma16(row_op(Vs, key, lg), gop, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool kok = 16 * kb + 4 * lg + e < KC;
-        s[4 * kb + e] = kok ? sv[e] : -3.0e38f;
-        dp[4 * kb + e] = pv[e];
-        m = fmaxf(m, s[4 * kb + e]);
+        for (int e = 0; e < 4; ++e) {
+          const bool kok = 32 * hh + 16 * half + 4 * lg + e < KC;
+          sv[4 * half + e] = kok ? s4[e] : -3.0e38f;
+          pv[4 * half + e] = p4[e];
+        }
       }
-    }
-    m = fmaxf(m, xor16(m));
-    m = fmaxf(m, xor32(m));
-    float l = 0.f;
+      float mc = sv[0];
 #pragma unroll
-    for (int e = 0; e < KCP / 4; ++e) {
-      s[e] = __builtin_amdgcn_exp2f((s[e] - m) * c2);   // p, unnormalised (0 past KC)
-      l += s[e];
+      for (int e = 1; e < 8; ++e) mc = fmaxf(mc, sv[e]);
+      const float mn = fmaxf(m, mc);
+      const float sc = __builtin_amdgcn_exp2f((m - mn) * c2);
+      l *= sc;
+      D *= sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = sv[e] > -1.0e38f ? __builtin_amdgcn_exp2f((sv[e] - mn) * c2) : 0.f;
+        l += pe;
+        D = fmaf(pe, pv[e], D);
+      }
+      m = mn;
     }
+    // combine the four lanes of query lq
+    float mt = fmaxf(m, xor16(m));
+    mt = fmaxf(mt, xor32(mt));
+    const float f = __builtin_amdgcn_exp2f((m - mt) * c2);
+    l *= f;
+    D *= f;
     l += xor16(l);
     l += xor32(l);
-    const float inv = 1.0f / l;
-    float D = 0.f;
-#pragma unroll
-    for (int e = 0; e < KCP / 4; ++e) D = fmaf(s[e] * inv, dp[e], D);
     D += xor16(D);
     D += xor32(D);
-    // ds^T packed in the slot order of 32-key steps, then dq^T = K^T ds^T
+    D /= l;
+    const float lse = mt * c2 + __log2f(l);
+    // sweep 2: ds = p (dp - D) in the slot order of each 32-key step, then
+    // dq^T = K^T ds^T with ds as hi + lo bf16 operands
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
       uint32_t pk[4], pl[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // s[4 kb + e] holds key 16 kb + 4 lg + e: slots of step hh are
-        // s[8 hh .. 8 hh + 7] (kb = 2 hh, then 2 hh + 1)
-        const int e0 = 8 * hh + 2 * j;
-        split_bf16x2(s[e0] * inv * (dp[e0] - D), s[e0 + 1] * inv * (dp[e0 + 1] - D), pk[j], pl[j]);
+      for (int half = 0; half < 2; ++half) {
+        const int key = 32 * hh + 16 * half + lq;
+        const f32x4 s4 = mfma16(row_op(Ks, key, lg), qop, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 p4 = mfma16(row_op(Vs, key, lg), gop, f32x4{0.f, 0.f, 0.f, 0.f});
+        float ds[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool kok = 32 * hh + 16 * half + 4 * lg + e < KC;
+          const float p = kok ? __builtin_amdgcn_exp2f(s4[e] * c2 - lse) : 0.f;
+          ds[e] = p * (p4[e] - D);
+        }
+        split_bf16x2(ds[0], ds[1], pk[2 * half], pl[2 * half]);
+        split_bf16x2(ds[2], ds[3], pk[2 * half + 1], pl[2 * half + 1]);
       }
       const bf16x8 dsb = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
       const bf16x8 dsl = __builtin_bit_cast(bf16x8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
@@ -223,20 +259,33 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a) {
                                                 pack_bf16x2(acc1[2] * a.scale, acc1[3] * a.scale));
       if (lg == 0) {
         const size_t pix = (size_t)b * a.H * a.W + tok_off(a, r, q) / a.C;
-        a.lse[pix * a.heads + h] = m * c2 + __log2f(l);
+        a.lse[pix * a.heads + h] = lse;
         a.dd[pix * a.heads + h] = D;
       }
     }
   }
 }
 
+// Key-centric pass.  The query regions that route to key region s are found
+// by a stable compaction of the image's routing index (a ballot and a prefix
+// count per wavefront, chunk after chunk, so the list is in ascending order
+// of query region and slot, with repeats kept) and their query tokens are
+// staged as one flat list, kDkvTile rows a tile, whatever the region size.
+// Wavefronts take 16-key blocks; when a region has fewer than four blocks,
+// the spare wavefronts take every QS-th 32-query sub-tile of the same key
+// block (query splits), and the splits' sums are added in a fixed order at
+// the end.  The LePE term of dV comes in as float32 (lepe_bwd_kernel) and is
+// added before the single rounding.
+constexpr int kDkvTile = 128;            // query rows staged per tile
+constexpr int kDkvList = 1024;           // query regions held at once
+
 __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a) {
-  extern __shared__ __align__(16) unsigned char lds[];
-  const int NQP = (a.n + 31) / 32 * 32;
-  uint16_t* Qs = (uint16_t*)lds;
-  uint16_t* Gs = Qs + NQP * kHd;
-  float* Ls = (float*)(Gs + NQP * kHd);            // log2-sum-exp of the staged queries
-  float* Ds = Ls + NQP;
+  __shared__ __align__(16) uint16_t tiles[2 * kDkvTile * kHd];   // Q tile, then dO tile
+  uint16_t* Qs = tiles;
+  uint16_t* Gs = tiles + kDkvTile * kHd;
+  __shared__ float Ls[kDkvTile], Ds[kDkvTile];
+  __shared__ int mlist[kDkvList];
+  __shared__ int wcnt[kWaves];
   const int u = blockIdx.x;
   const int h = u % a.heads, bs = u / a.heads;
   const int b = bs / a.R, s = bs - b * a.R;
@@ -245,83 +294,148 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a) {
   const auto Kr = rsrc(a.k + (size_t)b * img, img * 2), Vr = rsrc(a.v + (size_t)b * img, img * 2);
   const auto Qr = rsrc(a.q + (size_t)b * img, img * 2), Gr = rsrc(a.dout + (size_t)b * img, img * 2);
   const float c2 = a.scale_log2;
-  const int nkb = (a.n + 15) / 16;
-  const int beg = a.inv_off[b * (a.R + 1) + s], end = a.inv_off[b * (a.R + 1) + s + 1];
-  const int32_t* rows = a.inv_rows + (size_t)b * a.R * a.topk;
-  for (int kb = wave; kb < nkb + ((nkb + kWaves - 1) / kWaves * kWaves - nkb); kb += kWaves) {
-    // every wavefront runs the same number of passes (the barriers below)
-    const bool kact = kb < nkb;
+  const int RT = a.R * a.topk;
+  const int32_t* ib = a.idx + (size_t)b * RT;
+  const int KB = (a.n + 15) / 16;
+  const int QS = KB >= kWaves ? 1 : kWaves / KB;
+  const int groups = KB >= kWaves ? (KB + kWaves - 1) / kWaves : 1;
+  for (int grp = 0; grp < groups; ++grp) {
+    const int kb = QS == 1 ? grp * kWaves + wave : wave % KB;
+    const int split = QS == 1 ? 0 : wave / KB;
+    const bool act = kb < KB && split < QS;
     const int key = 16 * kb + lq;
-    const bool kok = kact && key < a.n;
+    const bool kok = act && key < a.n;
     const uint32_t koff = kok ? (tok_off(a, s, key) + h * kHd + 8 * lg) * 2 : kBwOob;
     const bf16x8 kop = __builtin_bit_cast(bf16x8, ld16(Kr, koff));
     const bf16x8 vop = __builtin_bit_cast(bf16x8, ld16(Vr, koff));
     f32x4 ak0 = {0.f, 0.f, 0.f, 0.f}, ak1 = ak0, av0 = ak0, av1 = ak0;
-    for (int it = beg; it < end; ++it) {
-      const int r = rows[it];
-      __syncthreads();                              // the previous tiles are consumed
-      for (int e = tid; e < NQP * 4; e += kThreads) {
-        const int qq = e >> 2, c = e & 3;
-        const uint32_t off = qq < a.n ? (tok_off(a, r, qq) + h * kHd + 8 * c) * 2 : kBwOob;
-        *(uint4*)trow(Qs, qq, c) = ld16(Qr, off);
-        *(uint4*)trow(Gs, qq, c) = ld16(Gr, off);
-      }
-      for (int qq = tid; qq < NQP; qq += kThreads) {
-        float lv = 3.0e38f, dv = 0.f;               // padding queries: p = 0
-        if (qq < a.n) {
-          const size_t pix = (size_t)b * a.H * a.W + tok_off(a, r, qq) / a.C;
-          lv = a.lse[pix * a.heads + h];
-          dv = a.dd[pix * a.heads + h];
+    int e0 = 0;
+    do {
+      // compact the query regions routing to s, up to kDkvList of them
+      int cnt = 0;
+      while (e0 < RT && cnt <= kDkvList - kThreads) {
+        const int e = e0 + tid;
+        const bool pred = e < RT && min(max(ib[e], 0), a.R - 1) == s;
+        const uint64_t bal = __ballot(pred);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        if (lane == 0) wcnt[wave] = __popcll(bal);
+        __syncthreads();
+        int base = cnt, tot = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const int c = wcnt[w];
+          base += w < wave ? c : 0;
+          tot += c;
         }
-        Ls[qq] = lv;
-        Ds[qq] = dv;
+        if (pred) mlist[base + below] = e / a.topk;
+        cnt += tot;
+        e0 += kThreads;
+        __syncthreads();
+      }
+      const int nrows = cnt * a.n;
+      for (int t0 = 0; t0 < nrows; t0 += kDkvTile) {
+        for (int e = tid; e < kDkvTile * 4; e += kThreads) {
+          const int row = e >> 2, c = e & 3, fi = t0 + row;
+          uint32_t off = kBwOob;
+          if (fi < nrows) {
+            const int m = fi / a.n;
+            off = (tok_off(a, mlist[m], fi - m * a.n) + h * kHd + 8 * c) * 2;
+          }
+          *(uint4*)trow(Qs, row, c) = ld16(Qr, off);
+          *(uint4*)trow(Gs, row, c) = ld16(Gr, off);
+        }
+        for (int row = tid; row < kDkvTile; row += kThreads) {
+          const int fi = t0 + row;
+          float lv = 3.0e38f, dv = 0.f;               // padding queries: p = 0
+          if (fi < nrows) {
+            const int m = fi / a.n;
+            const size_t pix = (size_t)b * a.H * a.W + tok_off(a, mlist[m], fi - m * a.n) / a.C;
+            lv = a.lse[pix * a.heads + h];
+            dv = a.dd[pix * a.heads + h];
+          }
+          Ls[row] = lv;
+          Ds[row] = dv;
+        }
+        __syncthreads();
+        const int nsub = (min(kDkvTile, nrows - t0) + 31) / 32;
+        if (act) {
+          for (int hh = split; hh < nsub; hh += QS) {
+            uint32_t pp[4], pd[4], ppl[4], pdl[4];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const int qrow = 32 * hh + 16 * half + lq;  // A rows: queries
+              const f32x4 sv = mfma16(row_op(Qs, qrow, lg), kop, f32x4{0.f, 0.f, 0.f, 0.f});
+              const f32x4 gv = mfma16(row_op(Gs, qrow, lg), vop, f32x4{0.f, 0.f, 0.f, 0.f});
+              // lane holds key lq, queries 32hh + 16half + 4lg + e
+              float p[4], ds[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int qe = 32 * hh + 16 * half + 4 * lg + e;
+                p[e] = __builtin_amdgcn_exp2f(sv[e] * c2 - Ls[qe]);
+                ds[e] = p[e] * (gv[e] - Ds[qe]);
+              }
+              split_bf16x2(p[0], p[1], pp[2 * half], ppl[2 * half]);
+              split_bf16x2(p[2], p[3], pp[2 * half + 1], ppl[2 * half + 1]);
+              split_bf16x2(ds[0], ds[1], pd[2 * half], pdl[2 * half]);
+              split_bf16x2(ds[2], ds[3], pd[2 * half + 1], pdl[2 * half + 1]);
+            }
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pp[0], pp[1], pp[2], pp[3]));
+            const bf16x8 pbl = __builtin_bit_cast(bf16x8, make_uint4(ppl[0], ppl[1], ppl[2], ppl[3]));
+            const bf16x8 db = __builtin_bit_cast(bf16x8, make_uint4(pd[0], pd[1], pd[2], pd[3]));
+            const bf16x8 dbl = __builtin_bit_cast(bf16x8, make_uint4(pdl[0], pdl[1], pdl[2], pdl[3]));
+            bf16x8 lo, hi;
+            trans_ops(Gs, hh, lq, lg, lo, hi);          // dO^T
+            av0 = mfma16(lo, pb, av0);
+            av1 = mfma16(hi, pb, av1);
+            av0 = mfma16(lo, pbl, av0);
+            av1 = mfma16(hi, pbl, av1);
+            trans_ops(Qs, hh, lq, lg, lo, hi);          // Q^T
+            ak0 = mfma16(lo, db, ak0);
+            ak1 = mfma16(hi, db, ak1);
+            ak0 = mfma16(lo, dbl, ak0);
+            ak1 = mfma16(hi, dbl, ak1);
+          }
+        }
+        __syncthreads();                              // the tile is consumed
+      }
+    } while (e0 < RT);
+    if (QS > 1) {
+      // splits 1 .. QS-1 hand their sums to split 0 through the tile buffer
+      // (free now): [QS - 1][KB][16][64] floats, at most 12 KB of its 16
+      float* red = (float*)tiles;
+      if (act && split > 0) {
+        float* rw = red + ((split - 1) * KB + kb) * 16 * 64 + lane;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          rw[(e + 0) * 64] = ak0[e];
+          rw[(e + 4) * 64] = ak1[e];
+          rw[(e + 8) * 64] = av0[e];
+          rw[(e + 12) * 64] = av1[e];
+        }
       }
       __syncthreads();
-      if (!kact) continue;
-      for (int hh = 0; hh < NQP / 32; ++hh) {
-        uint32_t pp[4], pd[4], ppl[4], pdl[4];
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int qrow = 32 * hh + 16 * half + lq;  // A rows: queries
-          const f32x4 sv = mfma16(row_op(Qs, qrow, lg), kop, f32x4{0.f, 0.f, 0.f, 0.f});
-          const f32x4 gv = mfma16(row_op(Gs, qrow, lg), vop, f32x4{0.f, 0.f, 0.f, 0.f});
-          // lane holds key lq, queries 32hh + 16half + 4lg + e
-          float p[4], ds[4];
+      if (act && split == 0) {
+        for (int sp = 1; sp < QS; ++sp) {
+          const float* rr = red + ((sp - 1) * KB + kb) * 16 * 64 + lane;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int qe = 32 * hh + 16 * half + 4 * lg + e;
-            p[e] = __builtin_amdgcn_exp2f(sv[e] * c2 - Ls[qe]);
-            ds[e] = p[e] * (gv[e] - Ds[qe]);
+            ak0[e] += rr[(e + 0) * 64];
+            ak1[e] += rr[(e + 4) * 64];
+            av0[e] += rr[(e + 8) * 64];
+            av1[e] += rr[(e + 12) * 64];
           }
-          split_bf16x2(p[0], p[1], pp[2 * half], ppl[2 * half]);
-          split_bf16x2(p[2], p[3], pp[2 * half + 1], ppl[2 * half + 1]);
-          split_bf16x2(ds[0], ds[1], pd[2 * half], pdl[2 * half]);
-          split_bf16x2(ds[2], ds[3], pd[2 * half + 1], pdl[2 * half + 1]);
         }
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pp[0], pp[1], pp[2], pp[3]));
-        const bf16x8 pbl = __builtin_bit_cast(bf16x8, make_uint4(ppl[0], ppl[1], ppl[2], ppl[3]));
-        const bf16x8 db = __builtin_bit_cast(bf16x8, make_uint4(pd[0], pd[1], pd[2], pd[3]));
-        const bf16x8 dbl = __builtin_bit_cast(bf16x8, make_uint4(pdl[0], pdl[1], pdl[2], pdl[3]));
-        bf16x8 lo, hi;
-        trans_ops(Gs, hh, lq, lg, lo, hi);          // dO^T
-        av0 = mfma16(lo, pb, av0);
-        av1 = mfma16(hi, pb, av1);
-        av0 = mfma16(lo, pbl, av0);
-        av1 = mfma16(hi, pbl, av1);
-        trans_ops(Qs, hh, lq, lg, lo, hi);          // Q^T
-        ak0 = mfma16(lo, db, ak0);
-        ak1 = mfma16(hi, db, ak1);
-        ak0 = mfma16(lo, dbl, ak0);
-        ak1 = mfma16(hi, dbl, ak1);
       }
+      __syncthreads();
     }
-    if (kok) {
+    if (kok && split == 0) {
       // lane holds channels 4 lg + e (acc 0) and 16 + 4 lg + e (acc 1) of key `key`
       const int to = tok_off(a, s, key) + h * kHd;
       float l0[4] = {0.f, 0.f, 0.f, 0.f}, l1[4] = {0.f, 0.f, 0.f, 0.f};
       if (a.dv_lepe) {
-        const float4 x0 = *(const float4*)(a.dv_lepe + (size_t)b * img + to + 4 * lg);
-        const float4 x1 = *(const float4*)(a.dv_lepe + (size_t)b * img + to + 16 + 4 * lg);
+        const float* lp = a.dv_lepe + (size_t)b * img + to + 4 * lg;
+        const float4 x0 = *(const float4*)lp, x1 = *(const float4*)(lp + 16);
         l0[0] = x0.x; l0[1] = x0.y; l0[2] = x0.z; l0[3] = x0.w;
         l1[0] = x1.x; l1[1] = x1.y; l1[2] = x1.z; l1[3] = x1.w;
       }
@@ -340,135 +454,187 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a) {
   }
 }
 
-// Inverse routing: for image b and key region s, the query regions r with
-// s in idx[b][r] (with multiplicity), ascending in r then slot.  One thread
-// per (b, s) scans the image's index: deterministic, no atomics.
-__global__ __launch_bounds__(kThreads) void inv_route_kernel(const int32_t* idx, int B, int R,
-                                                              int topk, int32_t* off,
-                                                              int32_t* rows) {
-  const int t = blockIdx.x * kThreads + threadIdx.x;
-  if (t >= B * R) return;
-  const int b = t / R, s = t - b * R;
-  const int32_t* ib = idx + (size_t)b * R * topk;
-  int before = 0, cnt = 0;
-  for (int e = 0; e < R * topk; ++e) {
-    const int reg = min(max(ib[e], 0), R - 1);
-    before += reg < s;
-    cnt += reg == s;
-  }
-  int32_t* rb = rows + (size_t)b * R * topk + before;
-  int k = 0;
-  for (int e = 0; e < R * topk && k < cnt; ++e) {
-    const int reg = min(max(ib[e], 0), R - 1);
-    if (reg == s) rb[k++] = e / topk;
-  }
-  off[b * (R + 1) + s] = before;
-  if (s == R - 1) off[b * (R + 1) + R] = before + cnt;
-}
+// The LePE gradients from one sliding window of dout.  Thread (channel pair
+// cp, column x) of image b walks a strip of rows, holding the KS x KS window
+// G(i, j) = dout(y - i + P, x - j + P) (two bf16 channels a word); then
+//   dV_L(y, x) = sum_{i,j} w(i, j) G(i, j)          (written as float32),
+//   dw(i, j)  += V(y, x) G(i, j),   db += dout(y, x)
+// (the second is the correlation sum over pixels with the centre moved to
+// the V side).  Rows are fetched kLepeRows at a time, so that many loads are
+// in flight per thread.  The workgroup's columns are added in LDS in column
+// order and written as one row of part: [(b * nstrips + strip) * nxb + xb]
+// [C][KK + 1] (the KK taps, then db).  Consecutive threads take consecutive
+// channel pairs of one pixel, so every load is coalesced.
+struct DwPlan {
+  int cpb, xc, nxb, ncb, sr, nstrips;   // pairs/workgroup, columns/workgroup, blocks, strip rows
+  long long rows;                       // partial rows
+};
+constexpr int kLepeRows = 4;
+constexpr int kMaxCols = 16;            // columns a workgroup holds: 256 / (C / 2), C >= 32
 
-// dV_L[y, x, c] = sum_{i,j} w[c, i, j] dout[y - i + P, x - j + P, c] (zero
-// outside), float32.  Thread (x, g) of one image row: 16-byte channel group
-// g of pixel x; the block's weights are staged in LDS as [tap][channel].
 template <int KS>
-__global__ __launch_bounds__(kThreads) void lepe_dv_kernel(const uint16_t* g, const float* w,
-                                                           int H, int W, int C, float* dvl) {
-  extern __shared__ float wt[];                     // [KS * KS][C]
-  constexpr int P = KS / 2, KK = KS * KS;
-  for (int e = threadIdx.x; e < KK * C; e += kThreads) {
-    const int c = e / KK, t = e - c * KK;
-    wt[t * C + c] = w[e];
-  }
-  __syncthreads();
-  const int G = C / 8;
-  const int t = blockIdx.x * kThreads + threadIdx.x;
-  if (t >= W * G) return;
-  const int y = blockIdx.y, b = blockIdx.z;
-  const int x = t / G, gi = t - x * G;
-  const uint16_t* gb = g + (size_t)b * H * W * C;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < KS; ++i) {
-    const int yy = y - i + P;
-    if ((unsigned)yy >= (unsigned)H) continue;
-    for (int j = 0; j < KS; ++j) {
-      const int xx = x - j + P;
-      if ((unsigned)xx >= (unsigned)W) continue;
-      float v[8];
-      unpack16<true>(*(const uint4*)(gb + ((size_t)yy * W + xx) * C + gi * 8), v);
-      const float4 w0 = *(const float4*)(wt + (i * KS + j) * C + gi * 8);
-      const float4 w1 = *(const float4*)(wt + (i * KS + j) * C + gi * 8 + 4);
-      acc[0] = fmaf(w0.x, v[0], acc[0]); acc[1] = fmaf(w0.y, v[1], acc[1]);
-      acc[2] = fmaf(w0.z, v[2], acc[2]); acc[3] = fmaf(w0.w, v[3], acc[3]);
-      acc[4] = fmaf(w1.x, v[4], acc[4]); acc[5] = fmaf(w1.y, v[5], acc[5]);
-      acc[6] = fmaf(w1.z, v[6], acc[6]); acc[7] = fmaf(w1.w, v[7], acc[7]);
+__global__ __launch_bounds__(kThreads) void lepe_bwd_kernel(const uint32_t* g, const uint32_t* v,
+                                                            const float* w, int H, int W, int CP,
+                                                            DwPlan pl, float* part, float* dvl) {
+  constexpr int P = KS / 2, KK = KS * KS, NV = 2 * (KK + 1);
+  __shared__ float red[32][kThreads];
+  const int tid = threadIdx.x;
+  const int cpl = tid % pl.cpb, xl = tid / pl.cpb;
+  const int cp = blockIdx.y * pl.cpb + cpl;
+  const int x = blockIdx.x * pl.xc + xl;
+  const int strip = blockIdx.z % pl.nstrips, b = blockIdx.z / pl.nstrips;
+  const bool ok = xl < pl.xc && cp < CP && x < W;
+  float acc[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) acc[e] = 0.f;
+  if (ok) {
+    const size_t ioff = (size_t)b * H * W * CP + cp;
+    const uint32_t* gb = g + ioff;
+    const uint32_t* vb = v + ioff;
+    float2* db2 = (float2*)dvl + ioff;
+    float w0[KK], w1[KK];                 // taps of channels 2 cp and 2 cp + 1
+#pragma unroll
+    for (int t = 0; t < KK; ++t) {
+      w0[t] = w[(2 * cp) * KK + t];
+      w1[t] = w[(2 * cp + 1) * KK + t];
     }
-  }
-  float* o = dvl + (((size_t)b * H + y) * W + x) * C + gi * 8;
-  *(float4*)o = make_float4(acc[0], acc[1], acc[2], acc[3]);
-  *(float4*)(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-}
-
-// Per-row partial sums of dw and db: one workgroup per (image, row), a
-// thread per channel (consecutive threads read consecutive channels of a
-// pixel, so the loads coalesce); each thread walks the row's pixels and the
-// taps in order.  part[(b * H + y) * C + c][KK + 1]: the KK taps, then db.
-template <int KS>
-__global__ __launch_bounds__(kThreads) void lepe_dw_rows_kernel(const uint16_t* g,
-                                                                const uint16_t* v, int H, int W,
-                                                                int C, float* part) {
-  constexpr int P = KS / 2, KK = KS * KS;
-  const int y = blockIdx.y, b = blockIdx.z;
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= C) return;
-  const uint16_t* gb = g + (size_t)b * H * W * C + c;
-  const uint16_t* vb = v + (size_t)b * H * W * C + c;
-  float acc[KK + 1];
+    auto ldg = [&](int y, int xx) -> uint32_t {
+      return ((unsigned)y < (unsigned)H && (unsigned)xx < (unsigned)W) ? gb[(y * W + xx) * CP] : 0u;
+    };
+    const int y0 = strip * pl.sr, y1 = min(H, y0 + pl.sr);
+    // win[r][c] = dout(y - P + r, x - P + c), so G(i, j) = win[KS-1-i][KS-1-j]
+    uint32_t win[KS][KS];
 #pragma unroll
-  for (int t = 0; t <= KK; ++t) acc[t] = 0.f;
-  for (int x = 0; x < W; ++x) {
-    const float gv = __uint_as_float((uint32_t)gb[((size_t)y * W + x) * C] << 16);
-    acc[KK] += gv;
+    for (int r = 0; r + 1 < KS; ++r)
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      const int yy = y + i - P;
-      if ((unsigned)yy >= (unsigned)H) continue;
+      for (int c = 0; c < KS; ++c) win[r + 1][c] = ldg(y0 - P + r, x - P + c);
+    for (int yb = y0; yb < y1; yb += kLepeRows) {
+      uint32_t nxt[kLepeRows][KS], vc[kLepeRows];
 #pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        const int xx = x + j - P;
-        if ((unsigned)xx >= (unsigned)W) continue;
-        const float vv = __uint_as_float((uint32_t)vb[((size_t)yy * W + xx) * C] << 16);
-        acc[i * KS + j] = fmaf(gv, vv, acc[i * KS + j]);
+      for (int u = 0; u < kLepeRows; ++u) {
+        const int y = yb + u;
+#pragma unroll
+        for (int c = 0; c < KS; ++c) nxt[u][c] = ldg(y + P, x - P + c);
+        vc[u] = y < y1 ? vb[(y * W + x) * CP] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kLepeRows; ++u) {
+        const int y = yb + u;
+#pragma unroll
+        for (int r = 0; r + 1 < KS; ++r)
+#pragma unroll
+          for (int c = 0; c < KS; ++c) win[r][c] = win[r + 1][c];
+#pragma unroll
+        for (int c = 0; c < KS; ++c) win[KS - 1][c] = nxt[u][c];
+        if (y >= y1) break;
+        const float v0 = bf16_lo(vc[u]), v1 = bf16_hi(vc[u]);
+        float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < KS; ++i)
+#pragma unroll
+          for (int j = 0; j < KS; ++j) {
+            const uint32_t gw = win[KS - 1 - i][KS - 1 - j];
+            const float g0 = bf16_lo(gw), g1 = bf16_hi(gw);
+            const int t = i * KS + j;
+            l0 = fmaf(w0[t], g0, l0);
+            l1 = fmaf(w1[t], g1, l1);
+            acc[2 * t] = fmaf(v0, g0, acc[2 * t]);
+            acc[2 * t + 1] = fmaf(v1, g1, acc[2 * t + 1]);
+          }
+        const uint32_t gc = win[P][P];                // dout(y, x)
+        acc[2 * KK] += bf16_lo(gc);
+        acc[2 * KK + 1] += bf16_hi(gc);
+        db2[(y * W + x) * CP] = make_float2(l0, l1);
       }
     }
   }
-  float* pp = part + (((size_t)b * H + y) * C + c) * (KK + 1);
+  // column sums: item (j, pair) of a 32-value slice, one per thread at a
+  // time, the xc columns (at most kMaxCols) added in column order
+  float* pr = part + ((size_t)blockIdx.z * gridDim.x + blockIdx.x) * (size_t)(2 * CP) * (KK + 1);
 #pragma unroll
-  for (int t = 0; t <= KK; ++t) pp[t] = acc[t];
+  for (int c0 = 0; c0 < NV; c0 += 32) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if (c0 + j < NV) red[j][tid] = acc[c0 + j];
+    __syncthreads();
+    for (int it = tid; it < 32 * pl.cpb; it += kThreads) {
+      const int j = it / pl.cpb, pc = it - j * pl.cpb, cpp = blockIdx.y * pl.cpb + pc;
+      if (c0 + j < NV && cpp < CP) {
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < kMaxCols; ++q)
+          if (q < pl.xc) sum += red[j][q * pl.cpb + pc];
+        const int vi = c0 + j, t = vi >> 1, half = vi & 1;
+        pr[(2 * cpp + half) * (KK + 1) + t] = sum;
+      }
+    }
+    __syncthreads();
+  }
 }
 
-// dw[c][t] and db[c]: the sums of the per-row partials over all rows, one
-// thread per (c, t), rows in order.
-__global__ __launch_bounds__(kThreads) void lepe_dw_sum_kernel(const float* part, int rows, int C,
-                                                               int KK, float* dw, float* db) {
-  const int e = blockIdx.x * kThreads + threadIdx.x;
-  if (e >= C * (KK + 1)) return;
-  const int c = e / (KK + 1), t = e - c * (KK + 1);
-  double s = 0.0;                                   // many rows: keep the sum exact enough
-  for (int r = 0; r < rows; ++r) s += part[((size_t)r * C + c) * (KK + 1) + t];
-  if (t < KK) dw[c * KK + t] = (float)s;
-  else if (db) db[c] = (float)s;
+// dw[c][t] and db[c]: float64 sums of the partial rows.  A workgroup takes 8
+// columns of part with 32 row phases each; the phases are added in order.
+__global__ __launch_bounds__(kThreads) void lepe_dw_sum_kernel(const float* part, long long rows,
+                                                               int CT, int KK, float* dw,
+                                                               float* db) {
+  __shared__ double red[32][8];
+  const int cl = threadIdx.x & 7, ph = threadIdx.x >> 3;
+  const int col = blockIdx.x * 8 + cl;
+  double s = 0.0;
+  if (col < CT) {
+    long long r = ph;
+    for (; r + 7 * 32 < rows; r += 8 * 32) {       // eight loads in flight, added in order
+      float t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = part[(size_t)(r + 32 * u) * CT + col];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += t[u];
+    }
+    for (; r < rows; r += 32) s += part[(size_t)r * CT + col];
+  }
+  red[ph][cl] = s;
+  __syncthreads();
+  if (ph == 0 && col < CT) {
+    double t = 0.0;
+    for (int p = 0; p < 32; ++p) t += red[p][cl];
+    const int c = col / (KK + 1), tt = col - c * (KK + 1);
+    if (tt < KK) dw[c * KK + tt] = (float)t;
+    else if (db) db[c] = (float)t;
+  }
+}
+
+DwPlan dw_plan(int B, int H, int W, int C) {
+  DwPlan p;
+  const int CP = C / 2;
+  p.cpb = CP < kThreads ? CP : kThreads;
+  p.xc = kThreads / p.cpb;
+  if (p.xc > kMaxCols) p.xc = kMaxCols;
+  p.nxb = (W + p.xc - 1) / p.xc;
+  p.ncb = (CP + p.cpb - 1) / p.cpb;
+  // enough row strips for about 4096 wavefronts, strips of at least 4 rows
+  const long long waves = (long long)B * p.nxb * p.ncb * kWaves;
+  long long ns = (4096 + waves - 1) / waves;
+  const long long nmax = (H + 3) / 4;
+  if (ns > nmax) ns = nmax;
+  if (ns < 1) ns = 1;
+  p.sr = (int)((H + ns - 1) / ns);
+  p.nstrips = (H + p.sr - 1) / p.sr;
+  p.rows = (long long)B * p.nstrips * p.nxb;
+  return p;
 }
 
 }  // namespace
 
 size_t bwd_workspace_bytes(int B, int H, int W, int C, int heads, int S, int topk, int ks,
                            bool lepe) {
+  (void)S; (void)topk;
   const size_t px = (size_t)B * H * W;
   size_t bytes = 2 * px * heads * sizeof(float);                   // lse, D
-  bytes += ((size_t)B * (S * S + 1) + (size_t)B * S * S * topk) * sizeof(int32_t);
   bytes = (bytes + 255) / 256 * 256;
   if (lepe) {
+    const DwPlan p = dw_plan(B, H, W, C);
     bytes += px * C * sizeof(float);                               // dV_L
-    bytes += (size_t)B * H * C * (ks * ks + 1) * sizeof(float);    // per-row partials
+    bytes += (size_t)p.rows * C * (ks * ks + 1) * sizeof(float);   // dw / db partial rows
   }
   return (bytes + 255) / 256 * 256;
 }
@@ -478,6 +644,7 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const in
                            int ks, void* dq, void* dk, void* dvv, float* dw, float* db, void* ws,
                            hipStream_t st) {
   if (s.C != s.heads * kHd || s.topk * s.n > kBwMaxKeys) return hipErrorNotSupported;
+  if (w && (ks < 1 || ks > 7 || ks % 2 == 0)) return hipErrorInvalidValue;
   // buffer offsets of one image (bytes) stay below 2^31
   if ((long long)s.H * s.W * s.C * 2 >= (long long)kBwOob) return hipErrorNotSupported;
   BwArgs a;
@@ -492,72 +659,46 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const in
   unsigned char* w8 = (unsigned char*)ws;
   a.lse = (float*)w8;
   a.dd = a.lse + px * s.heads;
-  a.inv_off = (const int32_t*)(a.dd + px * s.heads);
-  int32_t* inv_off = (int32_t*)a.inv_off;
-  int32_t* inv_rows = inv_off + (size_t)s.B * (s.R + 1);
-  a.inv_rows = inv_rows;
-  size_t used = 2 * px * s.heads * sizeof(float) +
-                ((size_t)s.B * (s.R + 1) + (size_t)s.B * s.R * s.topk) * sizeof(int32_t);
+  size_t used = 2 * px * s.heads * sizeof(float);
   used = (used + 255) / 256 * 256;
-  float* dvl = w ? (float*)(w8 + used) : nullptr;
-  float* part = w ? dvl + px * s.C : nullptr;
-  a.dv_lepe = dvl;
   hipError_t e;
-  // inverse routing lists
-  hipLaunchKernelGGL(inv_route_kernel, dim3((unsigned)((s.B * s.R + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, st, idx, s.B, s.R, s.topk, inv_off, inv_rows);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // LePE: dV_L, dw, db
+  const unsigned units = (unsigned)(s.B * s.R * s.heads);
+  a.dv_lepe = nullptr;
+  // LePE: dV's LePE term (float32, added by bwd_dkv_kernel), dw, db
   if (w) {
-    if (s.H > 65535 || s.B > 65535 || s.C > 65535) return hipErrorNotSupported;
-    const dim3 g1((unsigned)((s.W * (s.C / 8) + kThreads - 1) / kThreads), (unsigned)s.H, (unsigned)s.B);
-    const size_t wl = (size_t)ks * ks * s.C * sizeof(float);
-    const int tpb = s.C < kThreads ? s.C : kThreads;
-    const dim3 g2((unsigned)((s.C + tpb - 1) / tpb), (unsigned)s.H, (unsigned)s.B);
-    const int rows = s.B * s.H, KK = ks * ks;
-    const dim3 g3((unsigned)((s.C * (KK + 1) + kThreads - 1) / kThreads));
-#define BRA_LEPE_BW(KSV)                                                                       \
-    case KSV: {                                                                                \
-      e = hipFuncSetAttribute((const void*)lepe_dv_kernel<KSV>,                                \
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)wl);            \
-      if (e != hipSuccess) return e;                                                           \
-      hipLaunchKernelGGL(lepe_dv_kernel<KSV>, g1, dim3(kThreads), wl, st, (const uint16_t*)dout, \
-                         w, s.H, s.W, s.C, dvl);                                               \
-      hipLaunchKernelGGL(lepe_dw_rows_kernel<KSV>, g2, dim3(tpb), 0, st,                       \
-                         (const uint16_t*)dout, (const uint16_t*)v, s.H, s.W, s.C, part);      \
-      break;                                                                                   \
-    }
+    const DwPlan pl = dw_plan(s.B, s.H, s.W, s.C);
+    if ((long long)s.B * pl.nstrips > 65535 || pl.ncb > 65535) return hipErrorNotSupported;
+    float* dvl = (float*)(w8 + used);
+    float* part = dvl + px * s.C;
+    a.dv_lepe = dvl;
+    const dim3 g1((unsigned)pl.nxb, (unsigned)pl.ncb, (unsigned)(s.B * pl.nstrips));
+    const uint32_t* g32 = (const uint32_t*)dout;
+    const uint32_t* v32 = (const uint32_t*)v;
+#define BRA_LEPE_BW(KSV) \
+    hipLaunchKernelGGL(lepe_bwd_kernel<KSV>, g1, dim3(kThreads), 0, st, g32, v32, w, s.H, s.W, \
+                       s.C / 2, pl, part, dvl)
     switch (ks) {
-      BRA_LEPE_BW(1) BRA_LEPE_BW(3) BRA_LEPE_BW(5) BRA_LEPE_BW(7)
-      default: return hipErrorInvalidValue;
+      case 1: BRA_LEPE_BW(1); break;
+      case 3: BRA_LEPE_BW(3); break;
+      case 5: BRA_LEPE_BW(5); break;
+      default: BRA_LEPE_BW(7); break;
     }
 #undef BRA_LEPE_BW
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(lepe_dw_sum_kernel, g3, dim3(kThreads), 0, st, part, rows, s.C, KK, dw, db);
+    const int KK = ks * ks, CT = s.C * (KK + 1);
+    hipLaunchKernelGGL(lepe_dw_sum_kernel, dim3((unsigned)((CT + 7) / 8)), dim3(kThreads), 0, st,
+                       part, pl.rows, CT, KK, dw, db);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // dq (and the saved statistics), then dk / dv
   const int NH = (s.topk * s.n + 31) / 32;
   const size_t lq = (size_t)2 * 32 * NH * kHd * 2;
-  const unsigned units = (unsigned)(s.B * s.R * s.heads);
-#define BRA_DQ(NN)                                                                             \
-    case NN:                                                                                   \
-      e = hipFuncSetAttribute((const void*)bwd_dq_kernel<NN>,                                  \
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lq);            \
-      if (e != hipSuccess) return e;                                                           \
-      hipLaunchKernelGGL(bwd_dq_kernel<NN>, dim3(units), dim3(kThreads), lq, st, a);           \
-      break;
-  switch (NH) {
-    BRA_DQ(1) BRA_DQ(2) BRA_DQ(3) BRA_DQ(4) BRA_DQ(5) BRA_DQ(6) BRA_DQ(7) BRA_DQ(8)
-    default: return hipErrorNotSupported;
-  }
-#undef BRA_DQ
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int NQP = (s.n + 31) / 32 * 32;
-  const size_t lk = (size_t)2 * NQP * kHd * 2 + (size_t)2 * NQP * sizeof(float);
-  e = hipFuncSetAttribute((const void*)bwd_dkv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lk);
+  e = hipFuncSetAttribute((const void*)bwd_dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lq);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkv_kernel, dim3(units), dim3(kThreads), lk, st, a);
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(units), dim3(kThreads), lq, st, a, NH);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dkv_kernel, dim3(units), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

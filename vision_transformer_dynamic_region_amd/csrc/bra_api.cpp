@@ -546,7 +546,6 @@ bra_status bra_attend_backward(const void* q, const void* k, const void* v, cons
     if ((st = check_lepe_args(lepe_w, nullptr, lepe_ks, s))) return st;
     if (!dlepe_w) return fail(BRA_E_INVAL, "dlepe_w is NULL while lepe_w is given");
     if ((uintptr_t)dlepe_w & 3u) return fail(BRA_E_INVAL, "dlepe_w is not 4-byte aligned");
-    if (C > 512) return fail(BRA_E_UNSUPPORTED, "the LePE gradient takes C <= 512");
   }
   if (dlepe_b && ((uintptr_t)dlepe_b & 3u)) return fail(BRA_E_INVAL, "dlepe_b is not 4-byte aligned");
   const size_t tb = (size_t)B * H * W * C * 2;
