@@ -455,24 +455,26 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a) {
 }
 
 // The LePE gradients from one sliding window of dout.  Thread (channel pair
-// cp, column x) of image b walks a strip of rows, holding the KS x KS window
-// G(i, j) = dout(y - i + P, x - j + P) (two bf16 channels a word); then
+// cp, NCOL adjacent columns from x) of image b walks a strip of rows, holding
+// the window G(i, j) = dout(y - i + P, x - j + P) (two bf16 channels a word;
+// one such window per column); then
 //   dV_L(y, x) = sum_{i,j} w(i, j) G(i, j)          (written as float32),
 //   dw(i, j)  += V(y, x) G(i, j),   db += dout(y, x)
 // (the second is the correlation sum over pixels with the centre moved to
-// the V side).  Rows are fetched kLepeRows at a time, so that many loads are
-// in flight per thread.  The workgroup's columns are added in LDS in column
-// order and written as one row of part: [(b * nstrips + strip) * nxb + xb]
-// [C][KK + 1] (the KK taps, then db).  Consecutive threads take consecutive
-// channel pairs of one pixel, so every load is coalesced.
+// the V side).  Rows are fetched KS at a time, so that many loads are in
+// flight per thread, and the window is a circular buffer of KS rows whose
+// slot indices are compile-time in a KS-row batch: no data moves.  The
+// workgroup's thread columns are added in LDS in column order and written as
+// one row of part: [(b * nstrips + strip) * nxb + xb][C][KK + 1] (the KK
+// taps, then db).  Consecutive threads take consecutive channel pairs of one
+// pixel, so every load is coalesced.
 struct DwPlan {
   int cpb, xc, nxb, ncb, sr, nstrips;   // pairs/workgroup, columns/workgroup, blocks, strip rows
   long long rows;                       // partial rows
 };
-constexpr int kLepeRows = 4;
-constexpr int kMaxCols = 16;            // columns a workgroup holds: 256 / (C / 2), C >= 32
+constexpr int kMaxCols = 16;            // thread columns of a workgroup: 256 / (C / 2), C >= 32
 
-template <int KS>
+template <int KS, int NCOL>              // NCOL: adjacent pixel columns per thread
 __global__ __launch_bounds__(kThreads) void lepe_bwd_kernel(const uint32_t* g, const uint32_t* v,
                                                             const float* w, int H, int W, int CP,
                                                             DwPlan pl, float* part, float* dvl) {
@@ -481,70 +483,110 @@ __global__ __launch_bounds__(kThreads) void lepe_bwd_kernel(const uint32_t* g, c
   const int tid = threadIdx.x;
   const int cpl = tid % pl.cpb, xl = tid / pl.cpb;
   const int cp = blockIdx.y * pl.cpb + cpl;
-  const int x = blockIdx.x * pl.xc + xl;
+  const int x = (blockIdx.x * pl.xc + xl) * NCOL;
   const int strip = blockIdx.z % pl.nstrips, b = blockIdx.z / pl.nstrips;
   const bool ok = xl < pl.xc && cp < CP && x < W;
   float acc[NV];
 #pragma unroll
   for (int e = 0; e < NV; ++e) acc[e] = 0.f;
   if (ok) {
-    const size_t ioff = (size_t)b * H * W * CP + cp;
-    const uint32_t* gb = g + ioff;
-    const uint32_t* vb = v + ioff;
-    float2* db2 = (float2*)dvl + ioff;
+    const uint32_t iw = (uint32_t)H * W * CP;        // words of one image
+    const auto Gr = rsrc(g + (size_t)b * iw, iw * 4), Vr = rsrc(v + (size_t)b * iw, iw * 4);
+    float2* dl = (float2*)dvl + (size_t)b * iw + cp;
+    // byte offset of word (y, x - P + c) of this channel pair, past the
+    // record (reads zero) outside the image; unsigned arithmetic wraps back
+    // to the right value for the columns that are inside
+    constexpr int WC = KS + NCOL - 1;            // window columns
+    const uint32_t rowb = (uint32_t)W * CP * 4, colb = (uint32_t)CP * 4;
+    const uint32_t cb0 = ((uint32_t)(x - P) * CP + cp) * 4;
+    bool colok[WC];
+#pragma unroll
+    for (int c = 0; c < WC; ++c) colok[c] = (unsigned)(x - P + c) < (unsigned)W;
+    auto goff = [&](int y, int c) -> uint32_t {
+      return ((unsigned)y < (unsigned)H && colok[c]) ? (uint32_t)y * rowb + cb0 + c * colb : kBwOob;
+    };
+    auto ldw = [&](__amdgpu_buffer_rsrc_t r, uint32_t o) -> uint32_t {
+      return __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0);
+    };
     float w0[KK], w1[KK];                 // taps of channels 2 cp and 2 cp + 1
 #pragma unroll
     for (int t = 0; t < KK; ++t) {
       w0[t] = w[(2 * cp) * KK + t];
       w1[t] = w[(2 * cp + 1) * KK + t];
     }
-    auto ldg = [&](int y, int xx) -> uint32_t {
-      return ((unsigned)y < (unsigned)H && (unsigned)xx < (unsigned)W) ? gb[(y * W + xx) * CP] : 0u;
-    };
     const int y0 = strip * pl.sr, y1 = min(H, y0 + pl.sr);
-    // win[r][c] = dout(y - P + r, x - P + c), so G(i, j) = win[KS-1-i][KS-1-j]
-    uint32_t win[KS][KS];
+    // circular window of dout rows: while row y = yb + u of a batch is
+    // processed, row y - P + r sits in slot (u + r) % KS (r < KS), columns
+    // x - P .. x + NCOL - 1 + P; a batch of KS rows returns the slots to
+    // phase 0.  Up to 5 x 5 the window is held as floats (converted once per
+    // load).
+    constexpr bool FW = KS <= 5;
+    float wf[FW ? KS : 1][FW ? WC : 1][2];
+    uint32_t wu[FW ? 1 : KS][FW ? 1 : WC];
+    auto put = [&](int r, int c, uint32_t u32) {
+      if constexpr (FW) {
+        wf[r][c][0] = bf16_lo(u32);
+        wf[r][c][1] = bf16_hi(u32);
+      } else {
+        wu[r][c] = u32;
+      }
+    };
+    auto get = [&](int r, int c, float& a0, float& a1) {
+      if constexpr (FW) {
+        a0 = wf[r][c][0];
+        a1 = wf[r][c][1];
+      } else {
+        a0 = bf16_lo(wu[r][c]);
+        a1 = bf16_hi(wu[r][c]);
+      }
+    };
 #pragma unroll
     for (int r = 0; r + 1 < KS; ++r)
 #pragma unroll
-      for (int c = 0; c < KS; ++c) win[r + 1][c] = ldg(y0 - P + r, x - P + c);
-    for (int yb = y0; yb < y1; yb += kLepeRows) {
-      uint32_t nxt[kLepeRows][KS], vc[kLepeRows];
+      for (int c = 0; c < WC; ++c) put(r, c, ldw(Gr, goff(y0 - P + r, c)));
+    for (int yb = y0; yb < y1; yb += KS) {
+      uint32_t nx[KS][WC], vc[KS][NCOL];         // the batch's new rows, in flight together
 #pragma unroll
-      for (int u = 0; u < kLepeRows; ++u) {
-        const int y = yb + u;
+      for (int u = 0; u < KS; ++u) {
 #pragma unroll
-        for (int c = 0; c < KS; ++c) nxt[u][c] = ldg(y + P, x - P + c);
-        vc[u] = y < y1 ? vb[(y * W + x) * CP] : 0u;
+        for (int c = 0; c < WC; ++c) nx[u][c] = ldw(Gr, goff(yb + u + P, c));
+#pragma unroll
+        for (int o = 0; o < NCOL; ++o) vc[u][o] = ldw(Vr, goff(yb + u, P + o));
       }
 #pragma unroll
-      for (int u = 0; u < kLepeRows; ++u) {
+      for (int u = 0; u < KS; ++u) {
         const int y = yb + u;
+        const int sn = (KS - 1 + u) % KS;             // slot of the new row y + P
 #pragma unroll
-        for (int r = 0; r + 1 < KS; ++r)
+        for (int c = 0; c < WC; ++c) put(sn, c, nx[u][c]);
+        // rows past the strip (and columns past the image) are computed with
+        // zero weight and not stored
+        const float fv = y < y1 ? 1.f : 0.f;
 #pragma unroll
-          for (int c = 0; c < KS; ++c) win[r][c] = win[r + 1][c];
+        for (int o = 0; o < NCOL; ++o) {
+          const float v0 = bf16_lo(vc[u][o]) * fv, v1 = bf16_hi(vc[u][o]) * fv;
+          float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-        for (int c = 0; c < KS; ++c) win[KS - 1][c] = nxt[u][c];
-        if (y >= y1) break;
-        const float v0 = bf16_lo(vc[u]), v1 = bf16_hi(vc[u]);
-        float l0 = 0.f, l1 = 0.f;
+          for (int i = 0; i < KS; ++i) {
+            const int sl = (u + KS - 1 - i) % KS;     // dout row y - i + P
 #pragma unroll
-        for (int i = 0; i < KS; ++i)
-#pragma unroll
-          for (int j = 0; j < KS; ++j) {
-            const uint32_t gw = win[KS - 1 - i][KS - 1 - j];
-            const float g0 = bf16_lo(gw), g1 = bf16_hi(gw);
-            const int t = i * KS + j;
-            l0 = fmaf(w0[t], g0, l0);
-            l1 = fmaf(w1[t], g1, l1);
-            acc[2 * t] = fmaf(v0, g0, acc[2 * t]);
-            acc[2 * t + 1] = fmaf(v1, g1, acc[2 * t + 1]);
+            for (int j = 0; j < KS; ++j) {
+              float g0, g1;
+              get(sl, KS - 1 - j + o, g0, g1);        // dout(y - i + P, x + o - j + P)
+              const int t = i * KS + j;
+              l0 = fmaf(w0[t], g0, l0);
+              l1 = fmaf(w1[t], g1, l1);
+              acc[2 * t] = fmaf(v0, g0, acc[2 * t]);
+              acc[2 * t + 1] = fmaf(v1, g1, acc[2 * t + 1]);
+            }
           }
-        const uint32_t gc = win[P][P];                // dout(y, x)
-        acc[2 * KK] += bf16_lo(gc);
-        acc[2 * KK + 1] += bf16_hi(gc);
-        db2[(y * W + x) * CP] = make_float2(l0, l1);
+          const float fo = colok[P + o] ? fv : 0.f;
+          float gc0, gc1;
+          get((u + P) % KS, P + o, gc0, gc1);         // dout(y, x + o)
+          acc[2 * KK] = fmaf(fo, gc0, acc[2 * KK]);
+          acc[2 * KK + 1] = fmaf(fo, gc1, acc[2 * KK + 1]);
+          if (y < y1 && colok[P + o]) dl[(size_t)(y * W + x + o) * CP] = make_float2(l0, l1);
+        }
       }
     }
   }
@@ -603,13 +645,18 @@ __global__ __launch_bounds__(kThreads) void lepe_dw_sum_kernel(const float* part
   }
 }
 
-DwPlan dw_plan(int B, int H, int W, int C) {
+// columns per thread of lepe_bwd_kernel: two up to 5 x 5 (the weights and
+// dw sums of a channel pair are then shared by twice the pixels), else one
+int lepe_cols(int ks) { return ks <= 5 ? 2 : 1; }
+
+DwPlan dw_plan(int B, int H, int W, int C, int ks) {
+  const int ncol = lepe_cols(ks);
   DwPlan p;
   const int CP = C / 2;
   p.cpb = CP < kThreads ? CP : kThreads;
   p.xc = kThreads / p.cpb;
   if (p.xc > kMaxCols) p.xc = kMaxCols;
-  p.nxb = (W + p.xc - 1) / p.xc;
+  p.nxb = (W + p.xc * ncol - 1) / (p.xc * ncol);
   p.ncb = (CP + p.cpb - 1) / p.cpb;
   // enough row strips for about 4096 wavefronts, strips of at least 4 rows
   const long long waves = (long long)B * p.nxb * p.ncb * kWaves;
@@ -632,7 +679,7 @@ size_t bwd_workspace_bytes(int B, int H, int W, int C, int heads, int S, int top
   size_t bytes = 2 * px * heads * sizeof(float);                   // lse, D
   bytes = (bytes + 255) / 256 * 256;
   if (lepe) {
-    const DwPlan p = dw_plan(B, H, W, C);
+    const DwPlan p = dw_plan(B, H, W, C, ks);
     bytes += px * C * sizeof(float);                               // dV_L
     bytes += (size_t)p.rows * C * (ks * ks + 1) * sizeof(float);   // dw / db partial rows
   }
@@ -666,7 +713,7 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const in
   a.dv_lepe = nullptr;
   // LePE: dV's LePE term (float32, added by bwd_dkv_kernel), dw, db
   if (w) {
-    const DwPlan pl = dw_plan(s.B, s.H, s.W, s.C);
+    const DwPlan pl = dw_plan(s.B, s.H, s.W, s.C, ks);
     if ((long long)s.B * pl.nstrips > 65535 || pl.ncb > 65535) return hipErrorNotSupported;
     float* dvl = (float*)(w8 + used);
     float* part = dvl + px * s.C;
@@ -675,8 +722,8 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const in
     const uint32_t* g32 = (const uint32_t*)dout;
     const uint32_t* v32 = (const uint32_t*)v;
 #define BRA_LEPE_BW(KSV) \
-    hipLaunchKernelGGL(lepe_bwd_kernel<KSV>, g1, dim3(kThreads), 0, st, g32, v32, w, s.H, s.W, \
-                       s.C / 2, pl, part, dvl)
+    hipLaunchKernelGGL((lepe_bwd_kernel<KSV, KSV <= 5 ? 2 : 1>), g1, dim3(kThreads), 0, st, g32, \
+                       v32, w, s.H, s.W, s.C / 2, pl, part, dvl)
     switch (ks) {
       case 1: BRA_LEPE_BW(1); break;
       case 3: BRA_LEPE_BW(3); break;
