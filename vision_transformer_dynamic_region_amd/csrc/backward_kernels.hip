@@ -134,14 +134,15 @@ __device__ __forceinline__ int tok_off(const BwArgs& a, int r, int t) {
 // lanes of a query at the end, giving its log-sum-exp and D; the second
 // recomputes s and dp, forms ds = p (dp - D) and accumulates dq^T = K^T ds^T.
 // Nothing is held per key, so the register count does not grow with topk * n.
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH) {
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH, int hpw) {
   extern __shared__ __align__(16) unsigned char lds[];
-  uint16_t* Ks = (uint16_t*)lds;
   const int KCP = 32 * NH;
   const int KC = a.topk * a.n;
-  uint16_t* Vs = Ks + KCP * kHd;
+  uint16_t* Ks0 = (uint16_t*)lds;                  // [hpw][KCP][32]
+  uint16_t* Vs0 = Ks0 + hpw * KCP * kHd;           // [hpw][KCP][32]
+  const int ng = a.heads / hpw;
   const int u = blockIdx.x;
-  const int h = u % a.heads, br = u / a.heads;
+  const int hg = u % ng, br = u / ng;
   const int b = br / a.R, r = br - b * a.R;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 15, lg = lane >> 4;
   const uint32_t img = (uint32_t)a.H * a.W * a.C;
@@ -149,32 +150,39 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH) {
   const auto Qr = rsrc(a.q + (size_t)b * img, img * 2), Gr = rsrc(a.dout + (size_t)b * img, img * 2);
   const int32_t* route = a.idx + (size_t)br * a.topk;
   const int nqb = (a.n + 15) / 16;
-  auto qoff_of = [&](int qb) -> uint32_t {
+  const int ntask = nqb * hpw;                     // (query block, head) pairs
+  auto qoff_of = [&](int t) -> uint32_t {
+    const int qb = t / hpw, hh = hg * hpw + (t - (t / hpw) * hpw);
     const int q = 16 * qb + lq;
-    return (qb < nqb && q < a.n) ? (tok_off(a, r, q) + h * kHd + 8 * lg) * 2 : kBwOob;
+    return (t < ntask && q < a.n) ? (tok_off(a, r, q) + hh * kHd + 8 * lg) * 2 : kBwOob;
   };
-  // the first query block's operands are in flight during the staging
+  // the first task's query operands are in flight during the staging
   uint32_t qoff = qoff_of(wave);
   uint4 qn = ld16(Qr, qoff), gn = ld16(Gr, qoff);
-  // routed keys (regions in route order, tokens row-major), zero past KC
-  for (int e = tid; e < KCP * 4; e += kThreads) {
-    const int kk = e >> 2, c = e & 3;
+  // routed keys of the group's heads (regions in route order, tokens
+  // row-major), zero past KC; consecutive threads take consecutive 16-byte
+  // chunks of a key row across the heads
+  for (int e = tid; e < KCP * 4 * hpw; e += kThreads) {
+    const int c = e & 3, rest = e >> 2, kk = rest / hpw, hl = rest - kk * hpw;
     uint32_t off = kBwOob;
     if (kk < KC) {
       const int reg = min(max(route[kk / a.n], 0), a.R - 1);
-      off = (tok_off(a, reg, kk % a.n) + h * kHd + 8 * c) * 2;
+      off = (tok_off(a, reg, kk % a.n) + (hg * hpw + hl) * kHd + 8 * c) * 2;
     }
-    *(uint4*)trow(Ks, kk, c) = ld16(Kr, off);
-    *(uint4*)trow(Vs, kk, c) = ld16(Vr, off);
+    *(uint4*)trow(Ks0 + hl * KCP * kHd, kk, c) = ld16(Kr, off);
+    *(uint4*)trow(Vs0 + hl * KCP * kHd, kk, c) = ld16(Vr, off);
   }
   __syncthreads();
   const float c2 = a.scale_log2;
-  for (int qb = wave; qb < nqb; qb += kWaves) {
+  for (int t = wave; t < ntask; t += kWaves) {
+    const int qb = t / hpw, hl = t - qb * hpw, h = hg * hpw + hl;
+    const uint16_t* Ks = Ks0 + hl * KCP * kHd;
+    const uint16_t* Vs = Vs0 + hl * KCP * kHd;
     const int q = 16 * qb + lq;
     const bool qok = q < a.n;
     const bf16x8 qop = __builtin_bit_cast(bf16x8, qn);
     const bf16x8 gop = __builtin_bit_cast(bf16x8, gn);
-    qoff = qoff_of(qb + kWaves);
+    qoff = qoff_of(t + kWaves);
     qn = ld16(Qr, qoff);
     gn = ld16(Gr, qoff);
     // sweep 1: lane-local running max m, sum l of 2^((s - m) c2), sum D of
@@ -279,15 +287,15 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH) {
 constexpr int kDkvTile = 128;            // query rows staged per tile
 constexpr int kDkvList = 1024;           // query regions held at once
 
-__global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a) {
-  __shared__ __align__(16) uint16_t tiles[2 * kDkvTile * kHd];   // Q tile, then dO tile
-  uint16_t* Qs = tiles;
-  uint16_t* Gs = tiles + kDkvTile * kHd;
-  __shared__ float Ls[kDkvTile], Ds[kDkvTile];
+__global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a, int hpw) {
+  __shared__ __align__(16) uint16_t tiles[2 * kDkvTile * kHd];   // Q, dO tiles: [hpw][TR][32] each
+  __shared__ float Ls0[kDkvTile], Ds0[kDkvTile];                  // [hpw][TR]
   __shared__ int mlist[kDkvList];
   __shared__ int wcnt[kWaves];
+  const int TR = kDkvTile / hpw;                  // query rows a tile
+  const int ng = a.heads / hpw;
   const int u = blockIdx.x;
-  const int h = u % a.heads, bs = u / a.heads;
+  const int hg = u % ng, bs = u / ng;
   const int b = bs / a.R, s = bs - b * a.R;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 15, lg = lane >> 4;
   const uint32_t img = (uint32_t)a.H * a.W * a.C;
@@ -297,12 +305,23 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a) {
   const int RT = a.R * a.topk;
   const int32_t* ib = a.idx + (size_t)b * RT;
   const int KB = (a.n + 15) / 16;
-  const int QS = KB >= kWaves ? 1 : kWaves / KB;
+  // roles: (head, key block) pairs, hpw * KB <= kWaves when hpw > 1; spare
+  // wavefronts split the query sub-tiles (QS); with KB >= kWaves, groups of
+  // kWaves key blocks one after another
+  const int roles = KB >= kWaves ? kWaves : KB * hpw;
+  const int QS = KB >= kWaves ? 1 : kWaves / roles;
   const int groups = KB >= kWaves ? (KB + kWaves - 1) / kWaves : 1;
   for (int grp = 0; grp < groups; ++grp) {
-    const int kb = QS == 1 ? grp * kWaves + wave : wave % KB;
-    const int split = QS == 1 ? 0 : wave / KB;
+    const int role = wave % roles;
+    const int hl = KB >= kWaves ? 0 : role / KB;
+    const int kb = KB >= kWaves ? grp * kWaves + wave : role - hl * KB;
+    const int split = wave / roles;
     const bool act = kb < KB && split < QS;
+    const int h = hg * hpw + hl;
+    uint16_t* Qs = tiles + hl * TR * kHd;
+    uint16_t* Gs = tiles + kDkvTile * kHd + hl * TR * kHd;
+    const float* Ls = Ls0 + hl * TR;
+    const float* Ds = Ds0 + hl * TR;
     const int key = 16 * kb + lq;
     const bool kok = act && key < a.n;
     const uint32_t koff = kok ? (tok_off(a, s, key) + h * kHd + 8 * lg) * 2 : kBwOob;
@@ -334,31 +353,34 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a) {
         __syncthreads();
       }
       const int nrows = cnt * a.n;
-      for (int t0 = 0; t0 < nrows; t0 += kDkvTile) {
+      for (int t0 = 0; t0 < nrows; t0 += TR) {
+        // consecutive threads take consecutive 16-byte chunks of a query row
+        // across the group's heads
         for (int e = tid; e < kDkvTile * 4; e += kThreads) {
-          const int row = e >> 2, c = e & 3, fi = t0 + row;
+          const int c = e & 3, rest = e >> 2, row = rest / hpw, h2 = rest - row * hpw;
+          const int fi = t0 + row;
           uint32_t off = kBwOob;
           if (fi < nrows) {
             const int m = fi / a.n;
-            off = (tok_off(a, mlist[m], fi - m * a.n) + h * kHd + 8 * c) * 2;
+            off = (tok_off(a, mlist[m], fi - m * a.n) + (hg * hpw + h2) * kHd + 8 * c) * 2;
           }
-          *(uint4*)trow(Qs, row, c) = ld16(Qr, off);
-          *(uint4*)trow(Gs, row, c) = ld16(Gr, off);
+          *(uint4*)trow(tiles + h2 * TR * kHd, row, c) = ld16(Qr, off);
+          *(uint4*)trow(tiles + kDkvTile * kHd + h2 * TR * kHd, row, c) = ld16(Gr, off);
         }
-        for (int row = tid; row < kDkvTile; row += kThreads) {
-          const int fi = t0 + row;
+        for (int e = tid; e < kDkvTile; e += kThreads) {
+          const int row = e / hpw, h2 = e - row * hpw, fi = t0 + row;
           float lv = 3.0e38f, dv = 0.f;               // padding queries: p = 0
           if (fi < nrows) {
             const int m = fi / a.n;
             const size_t pix = (size_t)b * a.H * a.W + tok_off(a, mlist[m], fi - m * a.n) / a.C;
-            lv = a.lse[pix * a.heads + h];
-            dv = a.dd[pix * a.heads + h];
+            lv = a.lse[pix * a.heads + hg * hpw + h2];
+            dv = a.dd[pix * a.heads + hg * hpw + h2];
           }
-          Ls[row] = lv;
-          Ds[row] = dv;
+          Ls0[h2 * TR + row] = lv;
+          Ds0[h2 * TR + row] = dv;
         }
         __syncthreads();
-        const int nsub = (min(kDkvTile, nrows - t0) + 31) / 32;
+        const int nsub = (min(TR, nrows - t0) + 31) / 32;
         if (act) {
           for (int hh = split; hh < nsub; hh += QS) {
             uint32_t pp[4], pd[4], ppl[4], pdl[4];
@@ -402,10 +424,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a) {
     } while (e0 < RT);
     if (QS > 1) {
       // splits 1 .. QS-1 hand their sums to split 0 through the tile buffer
-      // (free now): [QS - 1][KB][16][64] floats, at most 12 KB of its 16
+      // (free now): [QS - 1][roles][16][64] floats, at most 12 KB of its 16
       float* red = (float*)tiles;
       if (act && split > 0) {
-        float* rw = red + ((split - 1) * KB + kb) * 16 * 64 + lane;
+        float* rw = red + ((split - 1) * roles + role) * 16 * 64 + lane;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           rw[(e + 0) * 64] = ak0[e];
@@ -417,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a) {
       __syncthreads();
       if (act && split == 0) {
         for (int sp = 1; sp < QS; ++sp) {
-          const float* rr = red + ((sp - 1) * KB + kb) * 16 * 64 + lane;
+          const float* rr = red + ((sp - 1) * roles + role) * 16 * 64 + lane;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             ak0[e] += rr[(e + 0) * 64];
@@ -738,14 +760,22 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const in
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // dq (and the saved statistics), then dk / dv
+  // heads per workgroup: small regions leave wavefronts without a query
+  // block (dq) or key block (dk, dv) of their own; they take more heads
   const int NH = (s.topk * s.n + 31) / 32;
-  const size_t lq = (size_t)2 * 32 * NH * kHd * 2;
+  const int nqb = (s.n + 15) / 16, KB = nqb;
+  int hq = 1, hk = 1;
+  for (int c = kWaves; c > 1; c /= 2) {
+    if (hq == 1 && nqb * c <= kWaves && s.heads % c == 0 && 32 * NH * c <= 512) hq = c;
+    if (hk == 1 && KB * c <= kWaves && s.heads % c == 0) hk = c;
+  }
+  const size_t lq = (size_t)2 * hq * 32 * NH * kHd * 2;
   e = hipFuncSetAttribute((const void*)bwd_dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)lq);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3(units), dim3(kThreads), lq, st, a, NH);
+  hipLaunchKernelGGL(bwd_dq_kernel, dim3(units / hq), dim3(kThreads), lq, st, a, NH, hq);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkv_kernel, dim3(units), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL(bwd_dkv_kernel, dim3(units / hk), dim3(kThreads), 0, st, a, hk);
   return hipGetLastError();
 }
 
