@@ -21,4 +21,6 @@ from .bra_oracle import (  # noqa: F401
     region_tokens,
     routed_attention,
     topk_route,
+    video_forward,
+    video_regions,
 )

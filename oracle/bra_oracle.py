@@ -112,6 +112,24 @@ depthwise conv:
       dout * V shifted by (i - P, j - P) (zero outside), and dV gains the
       transposed conv of dout with w.
 
+Readings for video (``video_forward``), from the one line p3 gives under
+§6.1 (video adaptation: the spatio-temporal cube is cut into T x K x K
+regions):
+
+  V1  T is the clip's frame count, so a region is one frame's K x K block
+      (K = S, the image model's grid); regions are numbered frame-major, then
+      row-major over the frame's grid: r = t * S*S + ry * S + rx, tokens
+      row-major inside the region (as R2).
+  V2  Routing runs over all T*S*S regions of a clip: one affinity matrix per
+      clip and a top-k per row, as in the image case (R4-R6), so a region
+      may route to regions of other frames.
+  V3  LePE is the image model's 2-D depthwise conv applied to each frame
+      (zero padding at the frame's borders); the pages give no temporal
+      kernel.
+  V4  p3 §6.1's optical-flow modulation of the temporal routing weights and
+      its cross-frame token sharing are not modelled: no flow input is given
+      and the sharing is not specified.
+
 Parity pins for every function live in ``tests/test_oracle_pins.py``.
 """
 
@@ -138,6 +156,8 @@ __all__ = [
     "gelu",
     "block_forward",
     "bra_backward",
+    "video_regions",
+    "video_forward",
 ]
 
 
@@ -311,6 +331,78 @@ def bra_forward(Q, K, V, heads: int, S: int, topk: int, w=None, bias=None,
     if return_parts:
         return {"out": out, "idx": idx, "q_r": q_r, "k_r": k_r, "A": A,
                 "O": O, "L": L}
+    return out, idx
+
+
+def video_regions(T: int, H: int, W: int, S: int) -> list:
+    """3-D partition of a clip (p3 §6.1; readings V1, V2).
+
+    Returns, for r = t * S*S + ry * S + rx, the (ts, ys, xs) coordinates of
+    region r's tokens in token order: frame t, rows ry*hs .. ry*hs+hs-1,
+    columns rx*ws .. rx*ws+ws-1, row-major.
+    """
+    hs, ws = region_shape(H, W, S)
+    regs = []
+    for t in range(T):
+        for ry in range(S):
+            for rx in range(S):
+                tok = np.arange(hs * ws)
+                regs.append((np.full(hs * ws, t), ry * hs + tok // ws, rx * ws + tok % ws))
+    return regs
+
+
+def video_forward(Q, K, V, heads: int, S: int, topk: int, w=None, bias=None,
+                  route_scale: float | None = None, attn_scale: float | None = None,
+                  return_parts: bool = False):
+    """BRA on a clip (p3 §6.1 T x K x K regions; readings V1-V4).
+
+    Q, K, V: [B, T, H, W, C].  Per clip: the means of the T*S*S regions, the
+    scaled affinity between them, the top-k index per region (over the whole
+    clip), attention of each query token over the tokens of its routed
+    regions, plus the per-frame LePE of V.  Returns (out [B, T, H, W, C],
+    idx [B, T*S*S, topk]) or, with return_parts, a dict of intermediates.
+    """
+    Q = _f64(Q)
+    K = _f64(K)
+    V = _f64(V)
+    B, T, H, W, C = Q.shape
+    if C % heads:
+        raise ValueError("heads must divide C")
+    d = C // heads
+    if route_scale is None:
+        route_scale = C ** -0.5
+    if attn_scale is None:
+        attn_scale = d ** -0.5
+    regs = video_regions(T, H, W, S)
+    R = len(regs)
+    q_r = np.empty((B, R, C))
+    k_r = np.empty((B, R, C))
+    for r, (ts, ys, xs) in enumerate(regs):
+        q_r[:, r] = Q[:, ts, ys, xs].mean(axis=1)
+        k_r[:, r] = K[:, ts, ys, xs].mean(axis=1)
+    A = region_affinity(q_r, k_r, route_scale)
+    idx = topk_route(A, topk)
+    O = np.zeros_like(Q)
+    for b in range(B):
+        for r, (ts, ys, xs) in enumerate(regs):
+            q = Q[b, ts, ys, xs].reshape(-1, heads, d)
+            kt = np.concatenate([regs[s][0] for s in idx[b, r]])
+            ky = np.concatenate([regs[s][1] for s in idx[b, r]])
+            kx = np.concatenate([regs[s][2] for s in idx[b, r]])
+            k = K[b, kt, ky, kx].reshape(-1, heads, d)
+            v = V[b, kt, ky, kx].reshape(-1, heads, d)
+            logits = attn_scale * np.einsum("nhd,mhd->hnm", q, k)
+            logits = logits - logits.max(axis=-1, keepdims=True)
+            p = np.exp(logits)
+            p = p / p.sum(axis=-1, keepdims=True)
+            O[b, ts, ys, xs] = np.einsum("hnm,mhd->nhd", p, v).reshape(-1, C)
+    if w is not None:
+        L = lepe(V.reshape(B * T, H, W, C), w, bias).reshape(B, T, H, W, C)
+    else:
+        L = np.zeros_like(O)
+    out = O + L
+    if return_parts:
+        return {"out": out, "idx": idx, "q_r": q_r, "k_r": k_r, "A": A, "O": O, "L": L}
     return out, idx
 
 

@@ -612,6 +612,90 @@ def pin_backward_finite_differences():
                                                                          got[name][pos])
 
 
+# --------------------------------------------------------------------------
+# video: T x S x S regions, one frame each (readings V1-V4)
+
+def pin_video_single_frame():
+    """A one-frame clip is an image: video_forward equals bra_forward."""
+    r = _rng(60)
+    B, H, W, C, heads, S, topk, ks = 2, 8, 8, 8, 2, 2, 3, 3
+    Q, K, V = (r.normal(size=(B, 1, H, W, C)) for _ in range(3))
+    w, b = r.normal(size=(C, ks, ks)) * 0.3, r.normal(size=C)
+    got, gi = O.video_forward(Q, K, V, heads, S, topk, w, b)
+    want, wi = O.bra_forward(Q[:, 0], K[:, 0], V[:, 0], heads, S, topk, w, b)
+    assert np.array_equal(gi, wi)
+    _close(got[:, 0], want, 1e-12, "video T=1 vs image")
+
+
+def _torch_video(Q, K, V, w, b, heads, S, topk):
+    """BRA on a clip written with torch ops: region means by a reshape, the
+    affinity by a matmul, torch.topk, masked dense attention over all the
+    clip's tokens, and conv2d(groups = C) on the frames."""
+    import torch
+    import torch.nn.functional as F
+    Qt, Kt, Vt = (torch.from_numpy(x) for x in (Q, K, V))
+    B, T, H, W, C = Qt.shape
+    hs, ws, d = H // S, W // S, C // heads
+    mean = lambda X: X.reshape(B, T, S, hs, S, ws, C).mean(dim=(3, 5)).reshape(B, T * S * S, C)
+    A = C ** -0.5 * mean(Qt) @ mean(Kt).transpose(1, 2)
+    idx = torch.topk(A, topk, dim=-1).indices
+    t = torch.arange(T)[:, None, None]
+    y = torch.arange(H)[None, :, None]
+    x = torch.arange(W)[None, None, :]
+    reg = (t * S * S + (y // hs) * S + x // ws).reshape(-1)            # [T*H*W]
+    out = torch.empty_like(Qt)
+    for bb in range(B):
+        allowed = torch.zeros(T * S * S, T * S * S, dtype=torch.bool)
+        allowed.scatter_(1, idx[bb], True)
+        mask = allowed[reg][:, reg]
+        q = Qt[bb].reshape(-1, heads, d).transpose(0, 1)
+        k = Kt[bb].reshape(-1, heads, d).transpose(0, 1)
+        v = Vt[bb].reshape(-1, heads, d).transpose(0, 1)
+        lg = (d ** -0.5) * q @ k.transpose(1, 2)
+        o = torch.softmax(lg.masked_fill(~mask, float("-inf")), dim=-1) @ v
+        out[bb] = o.transpose(0, 1).reshape(T, H, W, C)
+    ksz = w.shape[-1]
+    lep = F.conv2d(Vt.reshape(B * T, H, W, C).permute(0, 3, 1, 2), torch.from_numpy(w)[:, None],
+                   torch.from_numpy(b), padding=ksz // 2, groups=C)
+    out = out + lep.permute(0, 2, 3, 1).reshape(B, T, H, W, C)
+    return out.numpy(), idx.numpy()
+
+
+def pin_video_masked_dense_torch():
+    """video_forward equals a torch formulation of the same definition
+    (region means by reshape, topk, masked dense attention over the whole
+    clip, per-frame conv2d), index included; V gets a value only in the
+    first frame's last row so that LePE leaking across frames would show."""
+    r = _rng(61)
+    B, T, H, W, C, heads, S, topk, ks = 2, 3, 4, 4, 8, 2, 2, 3, 3
+    Q, K, V = (r.normal(size=(B, T, H, W, C)) for _ in range(3))
+    V[:, 1, 0] += 5.0                                   # next to frame 0's last row
+    w, b = r.normal(size=(C, ks, ks)), r.normal(size=C)
+    got, gi = O.video_forward(Q, K, V, heads, S, topk, w, b)
+    want, wi = _torch_video(Q, K, V, w, b, heads, S, topk)
+    assert np.array_equal(gi, wi), "video routing index"
+    _close(got, want, 1e-12, "video vs torch")
+
+
+def pin_video_frame_permutation():
+    """Reordering the frames reorders the output and relabels the routing
+    (region (t, j) of the new clip is region (perm[t], j) of the old)."""
+    r = _rng(62)
+    B, T, H, W, C, heads, S, topk, ks = 1, 4, 4, 4, 8, 2, 2, 5, 3
+    Q, K, V = (r.normal(size=(B, T, H, W, C)) for _ in range(3))
+    w = r.normal(size=(C, ks, ks)) * 0.3
+    perm = np.array([2, 0, 3, 1])
+    inv = np.argsort(perm)
+    out, idx = O.video_forward(Q, K, V, heads, S, topk, w)
+    out2, idx2 = O.video_forward(Q[:, perm], K[:, perm], V[:, perm], heads, S, topk, w)
+    _close(out2, out[:, perm], 1e-12, "video frame permutation")
+    SS = S * S
+    rows = (perm[:, None] * SS + np.arange(SS)[None, :]).reshape(-1)   # new row -> old row
+    mapped = idx[:, rows]                                              # old labels
+    relabel = inv[mapped // SS] * SS + mapped % SS
+    assert np.array_equal(idx2, relabel), "video routing relabelled"
+
+
 ALL_PINS = [
     pin_golden, pin_partition_layout, pin_pool_avgpool, pin_affinity_orientation,
     pin_topk_bruteforce, pin_scale_invariance, pin_masked_dense,
@@ -621,4 +705,5 @@ ALL_PINS = [
     pin_pool_commutes_with_projection, pin_round_storage_torch, pin_module_storage,
     pin_layer_norm_torch, pin_gelu_torch, pin_block_torch,
     pin_backward_autograd, pin_backward_finite_differences,
+    pin_video_single_frame, pin_video_masked_dense_torch, pin_video_frame_permutation,
 ]

@@ -11,7 +11,7 @@ from oracle_pins import ALL_PINS
 _orig = {name: getattr(O, name) for name in
          ("region_mean", "region_affinity", "topk_route", "routed_attention", "lepe",
           "region_tokens", "linear", "module_forward", "round_storage", "layer_norm", "gelu",
-          "block_forward", "bra_backward")}
+          "block_forward", "bra_backward", "video_forward")}
 
 
 def _mean_as_sum(X, S):
@@ -291,6 +291,55 @@ def _bw_dw_unshifted(Q, K, V, idx, heads, S, dout, w=None, bias=None, attn_scale
     return g
 
 
+def _video_lepe_stacked(Q, K, V, heads, S, topk, w=None, bias=None, route_scale=None,
+                        attn_scale=None, return_parts=False):
+    """LePE over the frame-stacked image: it leaks across frame borders."""
+    out, idx = _orig["video_forward"](Q, K, V, heads, S, topk, None, None, route_scale, attn_scale)
+    if w is not None:
+        B, T, H, W, C = np.shape(V)
+        out = out + O.lepe(np.reshape(V, (B, T * H, W, C)), w, bias).reshape(B, T, H, W, C)
+    return out, idx
+
+
+def _video_route_within_frame(Q, K, V, heads, S, topk, w=None, bias=None, route_scale=None,
+                              attn_scale=None, return_parts=False):
+    """Each frame routed on its own (no cross-frame routing)."""
+    T = np.shape(Q)[1]
+    C = np.shape(Q)[-1]
+    rs = C ** -0.5 if route_scale is None else route_scale
+    outs, idxs = [], []
+    for t in range(T):
+        o, i = _orig["video_forward"](Q[:, t:t + 1], K[:, t:t + 1], V[:, t:t + 1], heads, S,
+                                      min(topk, S * S), w, bias, rs, attn_scale)
+        outs.append(o)
+        idxs.append(i + t * S * S)
+    out = np.concatenate(outs, axis=1)
+    idx = np.concatenate(idxs, axis=1)
+    if idx.shape[-1] < topk:
+        idx = np.concatenate([idx, np.repeat(idx[..., -1:], topk - idx.shape[-1], -1)], -1)
+    return out, idx
+
+
+def _video_time_minor_labels(Q, K, V, heads, S, topk, w=None, bias=None, route_scale=None,
+                             attn_scale=None, return_parts=False):
+    """Regions numbered with time as the fastest axis."""
+    out, idx = _orig["video_forward"](Q, K, V, heads, S, topk, w, bias, route_scale, attn_scale)
+    T, SS = np.shape(Q)[1], S * S
+    lab = lambda r: (r % SS) * T + r // SS
+    rows = np.argsort(lab(np.arange(T * SS)))
+    return out, lab(idx)[:, rows]
+
+
+def _video_rows_cols_swapped(Q, K, V, heads, S, topk, w=None, bias=None, route_scale=None,
+                             attn_scale=None, return_parts=False):
+    """Regions column-major inside a frame (rows and columns swapped)."""
+    tr = lambda X: None if X is None else np.swapaxes(np.asarray(X, dtype=np.float64), 2, 3)
+    out, idx = _orig["video_forward"](tr(Q), tr(K), tr(V), heads, S, topk,
+                                      None if w is None else np.swapaxes(w, 1, 2), bias,
+                                      route_scale, attn_scale)
+    return tr(out), idx
+
+
 MUTANTS = {
     "region_mean": [_mean_as_sum, _mean_column_major],
     "region_affinity": [_affinity_transposed],
@@ -308,6 +357,8 @@ MUTANTS = {
     "block_forward": [_block_no_pos_residual, _block_post_norm],
     "bra_backward": [_bw_scale_dk_twice, _bw_no_softmax_term, _bw_lepe_not_transposed,
                      _bw_dw_unshifted],
+    "video_forward": [_video_lepe_stacked, _video_route_within_frame, _video_time_minor_labels,
+                      _video_rows_cols_swapped],
 }
 CASES = [(name, m) for name, ms in MUTANTS.items() for m in ms]
 
