@@ -265,6 +265,35 @@ bra_status bra_attend_backward(const void* q, const void* k, const void* v,
                                float* dlepe_b, void* ws, size_t ws_bytes,
                                void* stream);
 
+/* ------------------------------------------------------------------------
+ * Video clips (p3 §6.1: the spatio-temporal cube cut into T x K x K
+ * regions).  A region is one frame's S x S block (K = S), numbered
+ * r = t*S*S + ry*S + rx; routing runs over all T*S*S regions of a clip, so
+ * a region may attend to regions of other frames; LePE is the 2-D
+ * depthwise conv of each frame, zero padded at the frame's borders.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes of bra_video_forward: 2*B*T*S*S*C*8 (float64 region means
+ * of q, then of k). */
+size_t bra_video_workspace_bytes(int B, int T, int S, int C);
+
+/* The forward pass on clips.
+ *   q, k, v, out  [B, T, H, W, C] dtype, device (frames contiguous; as for
+ *                 bra_forward, out must not overlap q, k or v).
+ *   idx           out: int32 [B, T*S*S, topk], device; topk_logits
+ *                 float32 of the same shape or NULL.
+ *   T*S*S <= 1024 regions per clip and T*H*W*C < 2^31 (BRA_E_UNSUPPORTED
+ *   otherwise); the remaining arguments and errors as bra_forward, with
+ *   topk in [1, T*S*S]. */
+bra_status bra_video_forward(const void* q, const void* k, const void* v,
+                             int B, int T, int H, int W, int C, int heads,
+                             int S, int topk, bra_dtype dtype,
+                             float route_scale, float attn_scale,
+                             const float* lepe_w, const float* lepe_b,
+                             int lepe_ks, void* out, int32_t* idx,
+                             float* topk_logits, void* ws, size_t ws_bytes,
+                             void* stream);
+
 /* Static text for a status code. */
 const char* bra_strerror(int status);
 

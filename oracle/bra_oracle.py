@@ -353,7 +353,7 @@ def video_regions(T: int, H: int, W: int, S: int) -> list:
 
 def video_forward(Q, K, V, heads: int, S: int, topk: int, w=None, bias=None,
                   route_scale: float | None = None, attn_scale: float | None = None,
-                  return_parts: bool = False):
+                  return_parts: bool = False, idx=None):
     """BRA on a clip (p3 §6.1 T x K x K regions; readings V1-V4).
 
     Q, K, V: [B, T, H, W, C].  Per clip: the means of the T*S*S regions, the
@@ -361,6 +361,8 @@ def video_forward(Q, K, V, heads: int, S: int, topk: int, w=None, bias=None,
     clip), attention of each query token over the tokens of its routed
     regions, plus the per-frame LePE of V.  Returns (out [B, T, H, W, C],
     idx [B, T*S*S, topk]) or, with return_parts, a dict of intermediates.
+    With idx given, that index is used for the attention (the fixed-routing
+    use) and the routing only fills the returned parts.
     """
     Q = _f64(Q)
     K = _f64(K)
@@ -381,7 +383,7 @@ def video_forward(Q, K, V, heads: int, S: int, topk: int, w=None, bias=None,
         q_r[:, r] = Q[:, ts, ys, xs].mean(axis=1)
         k_r[:, r] = K[:, ts, ys, xs].mean(axis=1)
     A = region_affinity(q_r, k_r, route_scale)
-    idx = topk_route(A, topk)
+    idx = topk_route(A, topk) if idx is None else np.asarray(idx)
     O = np.zeros_like(Q)
     for b in range(B):
         for r, (ts, ys, xs) in enumerate(regs):

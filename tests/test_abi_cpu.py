@@ -41,7 +41,7 @@ def test_header_declares_the_boundary():
               "bra_strerror", "bra_last_error", "bra_linear", "bra_module_workspace_bytes",
               "bra_module_forward", "bra_layer_norm", "bra_block_workspace_bytes",
               "bra_block_forward", "bra_pos_conv", "bra_backward_workspace_bytes",
-              "bra_attend_backward"):
+              "bra_attend_backward", "bra_video_workspace_bytes", "bra_video_forward"):
         assert n in names
 
 
@@ -280,3 +280,20 @@ def test_backward_rejects(lib):
     assert call(scale=0.0) == INVAL
     assert lib.bra_backward_workspace_bytes(2, 8, 8, 64, 2, 2, 2, 5) > \
         lib.bra_backward_workspace_bytes(2, 8, 8, 64, 2, 2, 2, 0) > 0
+
+
+def test_video_rejects(lib):
+    def call(**kw):
+        a = dict(B=2, T=4, H=16, W=16, C=64, heads=2, S=2, topk=3, dt=BF16, ws=0x7C000000,
+                 wsb=1 << 26, w=None, out=0x70000000, idx=0x74000000)
+        a.update(kw)
+        return lib.bra_video_forward(P, P2, P3, a["B"], a["T"], a["H"], a["W"], a["C"], a["heads"],
+                                     a["S"], a["topk"], a["dt"], 0.125, 0.17, a["w"], None, 5,
+                                     a["out"], a["idx"], None, a["ws"], a["wsb"], None)
+    assert call(T=0) == INVAL and "T=0" in lib.bra_last_error().decode()
+    assert call(S=3) == INVAL                                   # S must divide H, W
+    assert call(topk=17) == INVAL and "T*S*S=16" in lib.bra_last_error().decode()
+    assert call(T=65, S=4, H=16) == UNSUP                       # 1040 regions a clip
+    assert call(wsb=16) == WSERR
+    assert lib.bra_video_workspace_bytes(2, 4, 2, 64) == 2 * 2 * 4 * 4 * 64 * 8
+    assert lib.bra_video_workspace_bytes(0, 4, 2, 64) == 0

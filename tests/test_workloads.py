@@ -6,6 +6,7 @@ import torch
 from vision_transformer_dynamic_region_amd.workloads import (WORKLOADS, bf16_bits,
                                                               bf16_round, make_inputs,
                                                               make_backward_inputs,
+                                                              make_video_inputs, VIDEO_WORKLOADS,
                                                               make_block_inputs,
                                                               make_module_inputs)
 
@@ -94,3 +95,15 @@ def test_backward_inputs_seeded_and_valid():
     assert idx.shape == (1, 49, 4) and idx.dtype == np.int32 and np.array_equal(idx, b["idx"])
     assert idx.min() >= 0 and idx.max() < 49
     assert all(len(set(row)) == 4 for row in idx[0])
+
+
+def test_video_inputs_seeded_and_shaped():
+    wl = VIDEO_WORKLOADS["video"].scaled(B=1, T=2)
+    a, b = make_video_inputs(wl), make_video_inputs(wl)
+    for n in ("q", "k", "v"):
+        assert a[n].shape == (1, 2, 56, 56, 64) and a[n].dtype == np.float32
+        assert np.array_equal(a[n], b[n]) and np.array_equal(a[n], bf16_round(a[n]))
+    # the per-position offset is shared by the frames: frame means of a region agree closely
+    m = a["q"].reshape(1, 2, 7, 8, 7, 8, 64).mean(axis=(3, 5))
+    assert np.corrcoef(m[0, 0].ravel(), m[0, 1].ravel())[0, 1] > 0.8
+    assert VIDEO_WORKLOADS["video"].tokens == 8 * 8 * 56 * 56

@@ -18,7 +18,7 @@ import os
 __all__ = ["BraError", "lib_path", "load", "workspace_bytes", "route", "attend",
            "forward", "lepe", "linear", "module_workspace_bytes", "module_forward",
            "layer_norm", "pos_conv", "block_workspace_bytes", "block_forward", "BLOCK_PARAMS",
-           "attend_backward", "STATUS"]
+           "attend_backward", "video_workspace_bytes", "video_forward", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -49,6 +49,9 @@ _SIGNATURES = {
     "bra_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "bra_attend_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f,
                                  _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "bra_video_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "bra_video_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _f, _vp,
+                               _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bra_strerror": (ctypes.c_char_p, [_i]),
     "bra_last_error": (ctypes.c_char_p, []),
 }
@@ -463,3 +466,46 @@ def attend_backward(q, k, v, idx, dout, heads: int, S: int, attn_scale: float | 
                                       workspace.data_ptr(),
                                       workspace.numel() * workspace.element_size(), _stream(q)))
     return (dq, dk, dv, dw, db) if lepe_w is not None else (dq, dk, dv)
+
+
+def video_workspace_bytes(B: int, T: int, S: int, C: int) -> int:
+    return int(load().bra_video_workspace_bytes(B, T, S, C))
+
+
+def video_forward(q, k, v, heads: int, S: int, topk: int, lepe_w=None, lepe_b=None,
+                  route_scale: float | None = None, attn_scale: float | None = None, out=None,
+                  idx=None, workspace=None, return_logits: bool = False):
+    """BRA on clips [B, T, H, W, C] (bra_video_forward): T*S*S regions of one
+    frame each, routing over the whole clip, per-frame LePE.  Returns
+    (out, idx) or (out, idx, logits)."""
+    import torch
+    if q.dim() != 5:
+        raise ValueError("clips must be [B, T, H, W, C]")
+    B, T, H, W, C = (int(x) for x in q.shape)
+    dt = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, q.dtype)
+        if tuple(t.shape) != (B, T, H, W, C):
+            raise ValueError("q, k, v must have the same shape")
+    if route_scale is None:
+        route_scale = C ** -0.5
+    if attn_scale is None:
+        attn_scale = (C // heads) ** -0.5
+    R = T * S * S
+    out = torch.empty_like(q) if out is None else out
+    _dev(out, "out", q.dtype)
+    idx = torch.empty((B, R, topk), dtype=torch.int32, device=q.device) if idx is None else idx
+    _dev(idx, "idx", torch.int32)
+    logits = torch.empty((B, R, topk), dtype=torch.float32, device=q.device) if return_logits else None
+    if workspace is None:
+        workspace = torch.empty(max(video_workspace_bytes(B, T, S, C), 16), dtype=torch.uint8,
+                                device=q.device)
+    _dev(workspace, "workspace")
+    wp, bp, ks = _lepe_args(lepe_w, lepe_b, C)
+    _check(load().bra_video_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, W, C, heads,
+                                    S, topk, dt, float(route_scale), float(attn_scale), wp, bp, ks,
+                                    out.data_ptr(), idx.data_ptr(),
+                                    logits.data_ptr() if logits is not None else None,
+                                    workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(q)))
+    return (out, idx, logits) if return_logits else (out, idx)

@@ -115,12 +115,13 @@ __device__ __forceinline__ void stage_halo(const void* __restrict__ Vimg,
   constexpr int P = KS / 2;
   const T* V = (const T*)Vimg;
   const int G = nslices * GS;                    // 16-byte groups per pixel
+  const int ftop = y0 / s.Hf * s.Hf;             // first row of the region's frame
   for (int e = threadIdx.x; e < hh * hw * G; e += kThreads) {
     const int pix = fdiv(e, f_gs), g = e - pix * G;
     const int hy = fdiv(pix, f_hw), hx = pix - hy * hw;
     const int y = y0 + hy - P, x = x0 + hx - P;
     uint4 val = make_uint4(0, 0, 0, 0);
-    if (y >= 0 && y < s.H && x >= 0 && x < s.W)
+    if (y >= ftop && y < ftop + s.Hf && x >= 0 && x < s.W)
       val = *(const uint4*)(V + (y * s.W + x) * s.C + c0 + g * VEC);
     const int slice = g / GS, gi = g - slice * GS;
     *(uint4*)((T*)Hs + ((slice * hh + hy) * hw + hx) * kSlice + gi * VEC) = val;
@@ -350,6 +351,7 @@ __global__ __launch_bounds__(kThreads, BRA_ATTN_WAVES_PER_SIMD) void attend_kern
       constexpr int GS = kSlice / VEC;
       const int slice = g_t / GS, gi = g_t - slice * GS;
       const int hy0 = ry * s.hs - P, hx0 = rx * s.ws - P;
+      const int ftop = ry * s.hs / s.Hf * s.Hf;   // first row of the region's frame
 #pragma unroll
       for (int i = 0; i < kHaloRegs; ++i) {
         const int pix = p_t + i * p_stride;
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(kThreads, BRA_ATTN_WAVES_PER_SIMD) void attend_kern
         const int y = hy0 + hy, x = hx0 + hx;
         hreg[i] = make_uint4(0, 0, 0, 0);
         hoffs[i] = pix < hh * hw ? ((slice * hh + hy) * hw + hx) * kSlice + gi * VEC : -1;
-        if (pix < hh * hw && y >= 0 && y < s.H && x >= 0 && x < s.W)
+        if (pix < hh * hw && y >= ftop && y < ftop + s.Hf && x >= 0 && x < s.W)
           hreg[i] = *(const uint4*)(V + (y * s.W + x) * s.C + g_t * VEC);
       }
     }
@@ -737,11 +739,13 @@ __global__ __launch_bounds__(kThreads) void attend_stream_kernel(StreamArgs SA) 
     int b, y0, x0;
     region_of(ubase + k * ustride, b, y0, x0);
     const T* V = (const T*)A.v + (size_t)b * s.H * s.W * s.C;
+    const int ftop = y0 / s.Hf * s.Hf;           // first row of the region's frame
 #pragma unroll
     for (int i = 0; i < kStreamHalo; ++i) {
       hreg[i] = make_uint4(0, 0, 0, 0);
       const int y = y0 + h_dy[i], x = x0 + h_dx[i];
-      if (i < SA.nhalo && p_t + i * p_stride < hh * hw && y >= 0 && y < s.H && x >= 0 && x < s.W)
+      if (i < SA.nhalo && p_t + i * p_stride < hh * hw && y >= ftop && y < ftop + s.Hf &&
+          x >= 0 && x < s.W)
         hreg[i] = *(const uint4*)(V + (y * s.W + x) * s.C + g_t * VEC);
     }
   };
@@ -990,8 +994,13 @@ hipError_t lepe_launch_ks(const void* v, const float* w, const float* b, const S
 }
 
 template <bool BF16, bool ACCUM>
-hipError_t lepe_launch(const void* v, const float* w, const float* b, int ks, const Shape& s,
+hipError_t lepe_launch(const void* v, const float* w, const float* b, int ks, const Shape& s0,
                        void* out, hipStream_t st) {
+  // LePE is per frame: a clip of H / Hf stacked frames is a batch of frames
+  Shape s = s0;
+  if (s0.Hf < 1 || s0.H % s0.Hf) return hipErrorInvalidValue;
+  s.B = s0.B * (s0.H / s0.Hf);
+  s.H = s0.Hf;
   switch (ks) {
     case 1: return lepe_launch_ks<BF16, 1, ACCUM>(v, w, b, s, out, st);
     case 3: return lepe_launch_ks<BF16, 3, ACCUM>(v, w, b, s, out, st);

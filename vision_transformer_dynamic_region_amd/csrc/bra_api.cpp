@@ -72,7 +72,7 @@ bra_status check_shape(int B, int H, int W, int C, int S, int heads, int topk, b
   if (n * topk > (1LL << 30)) return fail(BRA_E_UNSUPPORTED, "topk*n=%lld keys per query is too many", n * topk);
   bra::Shape s;
   s.B = B; s.H = H; s.W = W; s.C = C; s.S = S; s.heads = heads; s.topk = topk;
-  s.hs = H / S; s.ws = W / S; s.n = (int)n; s.R = S * S;
+  s.hs = H / S; s.ws = W / S; s.n = (int)n; s.R = S * S; s.Hf = H;
   *out = s;
   return BRA_OK;
 }
@@ -93,7 +93,7 @@ bra_status check_route_args(const void* q, const void* k, const bra::Shape& s, b
   if (logits && ((uintptr_t)logits & 3u)) return fail(BRA_E_INVAL, "topk_logits is not 4-byte aligned");
   if (!(route_scale > 0.f) || !std::isfinite(route_scale))
     return fail(BRA_E_INVAL, "route_scale=%g must be positive and finite", (double)route_scale);
-  const size_t need = bra_workspace_bytes(s.B, s.S, s.C);
+  const size_t need = (size_t)2 * s.B * s.R * s.C * sizeof(double);   // means of q, then k
   if (!ws) return fail(BRA_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (!aligned16(ws)) return fail(BRA_E_WORKSPACE, "workspace is not 16-byte aligned");
   if (ws_bytes < need) return fail(BRA_E_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
@@ -231,6 +231,51 @@ BlockLayout block_layout(int B, int H, int W, int C, int S, bra_dtype dt) {
   return b;
 }
 
+// pool, route, attend on validated arguments (an image batch or a clip batch)
+bra_status forward_launches(const void* q, const void* k, const void* v, const bra::Shape& s,
+                            bra_dtype dtype, float route_scale, float attn_scale,
+                            const float* lepe_w, const float* lepe_b, int lepe_ks, void* out,
+                            int32_t* idx, float* topk_logits, void* ws, void* stream) {
+  bra_status st;
+  hipStream_t hs = (hipStream_t)stream;
+  const bool bf16 = dtype == BRA_BF16;
+  double* qm = (double*)ws;
+  double* km = qm + (size_t)s.B * s.R * s.C;
+  if ((st = hip_status(bra::launch_pool(q, k, qm, km, s, bf16, hs), "pool launch"))) return st;
+  if ((st = hip_status(bra::launch_route(qm, km, s, (double)route_scale, idx, topk_logits, hs),
+                       "route launch")))
+    return st;
+  return hip_status(bra::launch_attend(q, k, v, idx, s, bf16, attn_scale, lepe_w, lepe_b, lepe_ks,
+                                       out, hs),
+                    "attend launch");
+}
+
+// A clip batch [B, T, H, W, C] as the frame-stacked image batch [B, T*H, W, C]
+// with a (T*S) x S region grid: region r = t*S*S + ry*S + rx, one frame each.
+bra_status check_video_shape(int B, int T, int H, int W, int C, int S, int heads, int topk,
+                             bra_dtype dt, bra::Shape* out) {
+  bra_status st;
+  if (T < 1) return fail(BRA_E_INVAL, "T=%d frames must be positive", T);
+  if (heads < 1) return fail(BRA_E_INVAL, "heads=%d must be positive", heads);
+  if ((long long)B * T > (1 << 30)) return fail(BRA_E_UNSUPPORTED, "B*T=%lld clips x frames", (long long)B * T);
+  // one frame as an image of the batch of B*T frames
+  if ((st = check_shape(B * T, H, W, C, S, heads, 1, dt, out))) return st;
+  const long long R = (long long)T * S * S;
+  if (R > kMaxRegions)
+    return fail(BRA_E_UNSUPPORTED, "T*S*S=%lld regions per clip exceed the supported %d", R, kMaxRegions);
+  if (topk < 1 || topk > R) return fail(BRA_E_INVAL, "topk=%d must be in [1, T*S*S=%lld]", topk, R);
+  if ((long long)T * H * W * C >= (1LL << 31))
+    return fail(BRA_E_UNSUPPORTED, "one clip of T*H*W*C=%lld elements exceeds 2^31", (long long)T * H * W * C);
+  if ((long long)B * R > (1LL << 24)) return fail(BRA_E_UNSUPPORTED, "B*T*S*S=%lld regions", (long long)B * R);
+  if ((long long)out->n * topk > (1LL << 30)) return fail(BRA_E_UNSUPPORTED, "topk*n too large");
+  out->B = B;
+  out->H = T * H;
+  out->Hf = H;
+  out->R = (int)R;
+  out->topk = topk;
+  return BRA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -288,18 +333,38 @@ bra_status bra_forward(const void* q, const void* k, const void* v, int B, int H
   if ((st = check_route_args(q, k, s, dtype, route_scale, idx, topk_logits, ws, ws_bytes))) return st;
   if ((st = check_attend_args(q, k, v, idx, s, dtype, attn_scale, lepe_w, lepe_b, lepe_ks, out)))
     return st;
-  hipStream_t hs = (hipStream_t)stream;
-  const bool bf16 = dtype == BRA_BF16;
-  double* qm = (double*)ws;
-  double* km = qm + (size_t)B * s.R * C;
-  if ((st = hip_status(bra::launch_pool(q, k, qm, km, s, bf16, hs), "pool launch"))) return st;
-  if ((st = hip_status(bra::launch_route(qm, km, s, (double)route_scale, idx, topk_logits, hs),
-                       "route launch")))
-    return st;
-  return hip_status(bra::launch_attend(q, k, v, idx, s, bf16, attn_scale, lepe_w, lepe_b, lepe_ks,
-                                       out, hs),
-                    "attend launch");
+  return forward_launches(q, k, v, s, dtype, route_scale, attn_scale, lepe_w, lepe_b, lepe_ks, out,
+                          idx, topk_logits, ws, stream);
 }
+
+size_t bra_video_workspace_bytes(int B, int T, int S, int C) {
+  if (B < 1 || T < 1 || S < 1 || C < 1) return 0;
+  return (size_t)2 * B * T * S * S * C * sizeof(double);
+}
+
+bra_status bra_video_forward(const void* q, const void* k, const void* v, int B, int T, int H,
+                             int W, int C, int heads, int S, int topk, bra_dtype dtype,
+                             float route_scale, float attn_scale, const float* lepe_w,
+                             const float* lepe_b, int lepe_ks, void* out, int32_t* idx,
+                             float* topk_logits, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  bra::Shape s;
+  bra_status st;
+  if ((st = check_video_shape(B, T, H, W, C, S, heads, topk, dtype, &s))) return st;
+  if ((st = check_route_args(q, k, s, dtype, route_scale, idx, topk_logits, ws, ws_bytes))) return st;
+  if ((st = check_attend_args(q, k, v, idx, s, dtype, attn_scale, lepe_w, lepe_b, lepe_ks, out)))
+    return st;
+  if (lepe_w) {
+    // the LePE grid runs over the batch of B*T frames
+    bra::Shape f = s;
+    f.B = B * T;
+    f.H = H;
+    if ((st = check_lepe_args(lepe_w, lepe_b, lepe_ks, f))) return st;
+  }
+  return forward_launches(q, k, v, s, dtype, route_scale, attn_scale, lepe_w, lepe_b, lepe_ks, out,
+                          idx, topk_logits, ws, stream);
+}
+
 
 bra_status bra_lepe(const void* v, const float* w, const float* b, int ks, int B, int H, int W,
                     int C, bra_dtype dtype, void* out, void* stream) {

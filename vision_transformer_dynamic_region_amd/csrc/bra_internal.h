@@ -14,7 +14,9 @@ struct Shape {
   int B, H, W, C, S, heads, topk;
   int hs, ws;     // region height / width in pixels
   int n;          // pixels per region = hs * ws
-  int R;          // regions per image = S * S
+  int R;          // regions per image: S * S, or T * S * S for a clip of T frames
+  int Hf;         // rows of one frame (H for an image); a clip of T frames is
+                  // stacked as H = T * Hf rows, and LePE stays inside a frame
 };
 
 // Region means of q and k into qm, km (float64 [B, R, C] each); with k (and

@@ -127,11 +127,12 @@ struct RegionArgs {
   const float* w;       // [C, KS, KS]
   const float* bias;    // [C] or null
   int H, W, S, R;
+  int Hf;               // rows of one frame; the LePE halo stays inside it
   float scale_log2;     // attn_scale * log2(e)
   int units;            // B * R * NCB
   int per_xcd;          // units per XCD (a multiple of NCB)
   int bpx;              // workgroups per XCD (a multiple of NCB)
-  FastDiv f_R, f_S;
+  FastDiv f_R, f_S, f_syf;   // f_syf: region rows per frame
 };
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -259,14 +260,15 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
       kn[i] = bload16(K, off);
       vn[i] = bload16(V, off);
     }
+    const int ftop = (int)fdiv(ry, A.f_syf) * A.Hf;  // first row of the region's frame
 #pragma unroll
     for (int i = 0; i < HPT; ++i) {
       const int pix = pk + PSTEP * i;
       const int hy = pix / HW, hx = pix % HW;
       const int y = ry * HS - P + hy, x = rx * WS - P + hx;
       // one unsigned compare per bound; & rather than && keeps this branch-free
-      const bool ok = (PSTEP * (i + 1) <= HH * HW || pix < HH * HW) & ((unsigned)y < (unsigned)A.H) &
-                      ((unsigned)x < (unsigned)A.W);
+      const bool ok = (PSTEP * (i + 1) <= HH * HW || pix < HH * HW) &
+                      ((unsigned)(y - ftop) < (unsigned)A.Hf) & ((unsigned)x < (unsigned)A.W);
       hn[i] = bload16(V, ok ? (uint32_t)((__umul24(y, A.W) + x) * C + cb0 + g * 8) * 2 : kOob);
     }
   };
@@ -497,10 +499,12 @@ hipError_t launch_attend_region(const void* q, const void* k, const void* v, con
   RegionArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.idx = idx; a.out = (uint16_t*)out; a.w = w; a.bias = bias;
-  a.H = s.H; a.W = s.W; a.S = s.S; a.R = s.R;
+  a.H = s.H; a.W = s.W; a.S = s.S; a.R = s.R; a.Hf = s.Hf;
   a.scale_log2 = attn_scale * 1.4426950408889634f;
   a.f_R = make_fastdiv(s.R);
   a.f_S = make_fastdiv(s.S);
+  if (s.Hf < 1 || s.Hf % s.hs || s.H % s.Hf) return hipErrorInvalidValue;
+  a.f_syf = make_fastdiv(s.Hf / s.hs);
   a.per_xcd = a.bpx = 0;
   auto is = [&](int C, int hs, int ws, int topk, int kks) {
     return s.C == C && s.hs == hs && s.ws == ws && s.topk == topk && ks == kks;

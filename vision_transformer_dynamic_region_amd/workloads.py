@@ -32,6 +32,14 @@ and fc2 ~ N(0, (3C)**-0.5) [C, 3C] (seed + 21) with bias N(0, 0.1) (seed + 22);
 conv and LayerNorm parameters and biases are float32, fc weights follow the
 workload dtype.
 
+Video clips (``VIDEO_WORKLOADS``, ``make_video_inputs``) draw Q, K, V ~ N(0, 1)
+as [B, T, H, W, C] (seeds + 0, 1, 2) plus, when region_offset_std > 0, one
+offset per clip, region position and channel ~ N(0, region_offset_std)
+(seeds + 4, 5, 6), the same in every frame, so that a region position looks
+alike across frames and routing across frames is not uniform; the LePE
+weights as above.  The stage-1 clip: 8 clips of 8 frames of 56x56, C = 64,
+S = 7 (392 regions a clip), top-4.
+
 The backward pass (bf16 only) takes Q, K, V and w as above, all rounded to
 bf16 whatever the workload's dtype, an output gradient dout ~ N(0, 1)
 rounded to bf16 (seed + 23), and a routing index drawn uniformly: for each
@@ -48,7 +56,8 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "bf16_round", "bf16_bits", "make_inputs",
-           "make_module_inputs", "make_block_inputs", "make_backward_inputs", "workload"]
+           "make_module_inputs", "make_block_inputs", "make_backward_inputs", "workload",
+           "VIDEO_WORKLOADS", "make_video_inputs"]
 
 
 @dataclass(frozen=True)
@@ -65,10 +74,11 @@ class Workload:
     topk: int
     lepe_ks: int = 5
     region_offset_std: float = 0.0   # std of the per-region mean offset (0: none)
+    T: int = 1                       # frames of a clip (video workloads)
 
     @property
     def tokens(self) -> int:
-        return self.B * self.H * self.W
+        return self.B * self.T * self.H * self.W
 
     @property
     def n(self) -> int:
@@ -108,6 +118,14 @@ WORKLOADS = {
     "st3": Workload("st3", 3, "bf16", 64, 14, 14, 256, 8, 7, 16),
     "dense": Workload("dense", 4, "bf16", 8, 128, 128, 64, 2, 16, 4,
                       region_offset_std=0.5),
+}
+
+
+VIDEO_WORKLOADS = {
+    # 8 clips of 8 frames at the stage-1 map (56x56, C = 64), 7x7 regions of
+    # 8x8 pixels per frame (392 regions a clip), top-4 routed regions
+    "video": Workload("video", 5, "bf16", 8, 56, 56, 64, 2, 7, 4, region_offset_std=0.5, T=8),
+    "video_tiny": Workload("video_tiny", 6, "f32", 1, 16, 16, 64, 2, 2, 3, T=4),
 }
 
 
@@ -236,4 +254,29 @@ def make_backward_inputs(wl: Workload, seed_base: int | None = None):
         for r in range(R):
             idx[b, r] = rng.permutation(R)[:wl.topk]
     out["idx"] = idx
+    return out
+
+
+def make_video_inputs(wl: Workload, seed_base: int | None = None, with_weights: bool = True):
+    """Draw (Q, K, V, w) for a clip workload: ``q``, ``k``, ``v`` [B, T, H, W,
+    C] float32 (bf16-rounded for bf16 workloads), ``w`` [C, ks, ks] float32
+    (or None) and ``bias`` (None)."""
+    base = 1000 * wl.index if seed_base is None else seed_base
+    shape = (wl.B, wl.T, wl.H, wl.W, wl.C)
+    out = {}
+    for name, off, mu_off in (("q", 0, 4), ("k", 1, 5), ("v", 2, 6)):
+        x = _normal(base + off, shape)
+        if wl.region_offset_std > 0.0:
+            hs, ws = wl.H // wl.S, wl.W // wl.S
+            mu = _normal(base + mu_off, (wl.B, 1, wl.S, wl.S, wl.C), wl.region_offset_std)
+            x = x + np.repeat(np.repeat(mu, hs, axis=2), ws, axis=3)
+        x = x.astype(np.float32)
+        if wl.dtype == "bf16":
+            x = bf16_round(x)
+        out[name] = x
+    if with_weights and wl.lepe_ks > 0:
+        out["w"] = _normal(base + 3, (wl.C, wl.lepe_ks, wl.lepe_ks), 0.02).astype(np.float32)
+    else:
+        out["w"] = None
+    out["bias"] = None
     return out
