@@ -59,12 +59,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="st1", choices=["tiny", "st1", "st2", "st3", "dense"])
-    p.add_argument("--path", default="bra", choices=["bra", "module", "block", "backward"],
+    p.add_argument("--workload", default="st1",
+                   choices=["tiny", "st1", "st2", "st3", "dense", "video", "video_tiny"])
+    p.add_argument("--path", default="bra", choices=["bra", "module", "block", "backward", "video"],
                    help="bra: the BRA forward pass on given Q, K, V (the default line); module: "
                         "the module around it (Q/K/V projections of x, BRA, output projection); "
                         "block: one BiFormer block (position conv, LN, module, LN, MLP); "
-                        "backward: gradients of the BRA forward (with LePE) for a fixed index")
+                        "backward: gradients of the BRA forward (with LePE) for a fixed index; "
+                        "video: BRA on clips of T frames (--workload video)")
     p.add_argument("--sets", type=int, default=0,
                    help="input copies rotated across steps (0: enough to exceed the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -472,6 +474,93 @@ def run_backward(a, wl) -> int:
     return 0
 
 
+def run_video(a, wl) -> int:
+    """One step = bra_video_forward over one batch of clips (routing over
+    each clip's T*S*S regions, attention, per-frame LePE)."""
+    import numpy as np
+    import torch
+
+    import vision_transformer_dynamic_region_amd as bra
+    from vision_transformer_dynamic_region_amd.workloads import bf16_bits, make_video_inputs
+
+    dev = torch.device("cuda:0")
+    log(f"workload {wl}")
+    x = make_video_inputs(wl)
+    if wl.dtype == "bf16":
+        up = lambda arr: torch.from_numpy(bf16_bits(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        up = lambda arr: torch.from_numpy(arr).to(dev)
+    q0, k0, v0 = up(x["q"]), up(x["k"]), up(x["v"])
+    w = torch.from_numpy(x["w"]).to(dev)
+    R = wl.T * wl.S * wl.S
+    wsb = bra.video_workspace_bytes(wl.B, wl.T, wl.S, wl.C)
+    set_bytes = 4 * wl.tensor_bytes
+    sets = a.sets or max(1, -(-3 * MALL_BYTES // set_bytes))
+    bufs = [dict(q=q0.clone(), k=k0.clone(), v=v0.clone(), out=torch.empty_like(q0),
+                 idx=torch.empty((wl.B, R, wl.topk), dtype=torch.int32, device=dev),
+                 ws=torch.empty(wsb, dtype=torch.uint8, device=dev)) for _ in range(sets)]
+    torch.cuda.synchronize()
+    log(f"video: {sets} input sets of {set_bytes / 1e6:.1f} MB rotated per step")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for i in range(a.warmup):
+            fn(bufs[i % sets])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(a.steps):
+            fn(bufs[i % sets])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / a.steps
+
+    ms = timed(lambda b: bra.video_forward(b["q"], b["k"], b["v"], wl.heads, wl.S, wl.topk, w,
+                                           out=b["out"], idx=b["idx"], workspace=b["ws"]))
+    t_route = timed(lambda b: bra.video_route(b["q"], b["k"], wl.S, wl.topk, workspace=b["ws"]))
+    t_attn = timed(lambda b: bra.video_attend(b["q"], b["k"], b["v"], b["idx"], wl.heads, wl.S,
+                                              lepe_w=w, out=b["out"]))
+    log(f"video: {ms:.4f} ms/step; pool+route {t_route:.4f}, attend+lepe {t_attn:.4f}")
+    attn_bytes = 4 * wl.tensor_bytes
+    gbs = attn_bytes / (t_attn * 1e-3) / 1e9
+    res = {
+        "metric": "BRA video fwd tokens/s (T x S x S regions, clip-wide routing, per-frame "
+                  "LePE), 1 GPU",
+        "value": wl.tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name}: B={wl.B} clips x T={wl.T} frames of {wl.H}x{wl.W}, "
+                               f"C={wl.C} heads={wl.heads} S={wl.S} ({R} regions a clip) "
+                               f"topk={wl.topk} LePE {wl.lepe_ks}x{wl.lepe_ks}",
+                   "tokens_per_step": wl.tokens, "input_sets_rotated": sets},
+        "stages_ms": {"pool_route": t_route, "attend_lepe": t_attn},
+        "roofline": {"kernel": attend_kernel_name(wl), "bound": "hbm", "achieved": gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes": attn_bytes},
+    }
+    if not a.no_cpu_baseline:
+        import oracle as O
+        log("timing the fp64 oracle video_forward on the host")
+        ru0 = resource.getrusage(resource.RUSAGE_SELF)
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < a.cpu_seconds and reps < 50:
+            O.video_forward(x["q"][:1], x["k"][:1], x["v"][:1], wl.heads, wl.S, wl.topk, x["w"])
+            reps += 1
+        dt = time.perf_counter() - t0
+        ru1 = resource.getrusage(resource.RUSAGE_SELF)
+        cpu = (ru1.ru_utime - ru0.ru_utime) + (ru1.ru_stime - ru0.ru_stime)
+        tokens = wl.T * wl.H * wl.W * reps
+        res["cpu_baseline"] = {"value": tokens / dt, "unit": "tokens/s",
+                               "cores": max(1, int(round(cpu / dt))), "kind": "oracle",
+                               "sample": (f"{wl.name}: 1 clip x {reps} passes ({tokens} tokens), "
+                                          f"fp64 oracle video_forward in {dt:.1f} s")}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     a = parse()
     if a.traffic_from:
@@ -493,6 +582,12 @@ def main() -> int:
         copy_probe(a.copy_probe_mb)
         return 0
 
+    if a.path == "video" or a.workload.startswith("video"):
+        from vision_transformer_dynamic_region_amd.workloads import VIDEO_WORKLOADS
+        if a.path not in ("bra", "video") or not a.workload.startswith("video"):
+            print("--path video takes --workload video or video_tiny", file=sys.stderr)
+            return 2
+        return run_video(a, VIDEO_WORKLOADS[a.workload])
     wl = WORKLOADS[a.workload]
     if a.path == "module":
         return run_module(a, wl)

@@ -277,7 +277,26 @@ bra_status bra_attend_backward(const void* q, const void* k, const void* v,
  * of q, then of k). */
 size_t bra_video_workspace_bytes(int B, int T, int S, int C);
 
-/* The forward pass on clips.
+/* Region means, affinity and top-k over each clip's T*S*S regions
+ * (bra_route for clips): q, k [B, T, H, W, C]; idx [B, T*S*S, topk];
+ * ws of bra_video_workspace_bytes(B, T, S, C). */
+bra_status bra_video_route(const void* q, const void* k, int B, int T, int H,
+                           int W, int C, int S, int topk, bra_dtype dtype,
+                           float route_scale, int32_t* idx,
+                           float* topk_logits, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Gather-attention over the routed regions of a clip plus per-frame LePE,
+ * with a caller-supplied index (bra_attend for clips; the fixed-routing use
+ * of p2 §5): idx [B, T*S*S, topk], entries clamped into [0, T*S*S). */
+bra_status bra_video_attend(const void* q, const void* k, const void* v,
+                            const int32_t* idx, int B, int T, int H, int W,
+                            int C, int heads, int S, int topk,
+                            bra_dtype dtype, float attn_scale,
+                            const float* lepe_w, const float* lepe_b,
+                            int lepe_ks, void* out, void* stream);
+
+/* The forward pass on clips: bra_video_route then bra_video_attend.
  *   q, k, v, out  [B, T, H, W, C] dtype, device (frames contiguous; as for
  *                 bra_forward, out must not overlap q, k or v).
  *   idx           out: int32 [B, T*S*S, topk], device; topk_logits

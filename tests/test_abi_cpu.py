@@ -41,7 +41,8 @@ def test_header_declares_the_boundary():
               "bra_strerror", "bra_last_error", "bra_linear", "bra_module_workspace_bytes",
               "bra_module_forward", "bra_layer_norm", "bra_block_workspace_bytes",
               "bra_block_forward", "bra_pos_conv", "bra_backward_workspace_bytes",
-              "bra_attend_backward", "bra_video_workspace_bytes", "bra_video_forward"):
+              "bra_attend_backward", "bra_video_workspace_bytes", "bra_video_forward",
+              "bra_video_route", "bra_video_attend"):
         assert n in names
 
 

@@ -18,7 +18,8 @@ import os
 __all__ = ["BraError", "lib_path", "load", "workspace_bytes", "route", "attend",
            "forward", "lepe", "linear", "module_workspace_bytes", "module_forward",
            "layer_norm", "pos_conv", "block_workspace_bytes", "block_forward", "BLOCK_PARAMS",
-           "attend_backward", "video_workspace_bytes", "video_forward", "STATUS"]
+           "attend_backward", "video_workspace_bytes", "video_forward", "video_route",
+           "video_attend", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -50,6 +51,10 @@ _SIGNATURES = {
     "bra_attend_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f,
                                  _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bra_video_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "bra_video_route": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _vp, _sz,
+                             _vp]),
+    "bra_video_attend": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp,
+                              _vp, _i, _vp, _vp]),
     "bra_video_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f, _f, _vp,
                                _vp, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bra_strerror": (ctypes.c_char_p, [_i]),
@@ -509,3 +514,42 @@ def video_forward(q, k, v, heads: int, S: int, topk: int, lepe_w=None, lepe_b=No
                                     workspace.data_ptr(),
                                     workspace.numel() * workspace.element_size(), _stream(q)))
     return (out, idx, logits) if return_logits else (out, idx)
+
+
+def video_route(q, k, S: int, topk: int, route_scale: float | None = None, workspace=None):
+    """Routing of clips (bra_video_route): idx int32 [B, T*S*S, topk]."""
+    import torch
+    B, T, H, W, C = (int(x) for x in q.shape)
+    dt = _dtype_code(q)
+    _dev(q, "q")
+    _dev(k, "k", q.dtype)
+    if route_scale is None:
+        route_scale = C ** -0.5
+    idx = torch.empty((B, T * S * S, topk), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(video_workspace_bytes(B, T, S, C), 16), dtype=torch.uint8,
+                                device=q.device)
+    _check(load().bra_video_route(q.data_ptr(), k.data_ptr(), B, T, H, W, C, S, topk, dt,
+                                  float(route_scale), idx.data_ptr(), None, workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), _stream(q)))
+    return idx
+
+
+def video_attend(q, k, v, idx, heads: int, S: int, attn_scale: float | None = None, lepe_w=None,
+                 lepe_b=None, out=None):
+    """Attention of clips over a given index plus per-frame LePE (bra_video_attend)."""
+    import torch
+    B, T, H, W, C = (int(x) for x in q.shape)
+    dt = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, q.dtype)
+    _dev(idx, "idx", torch.int32)
+    topk = int(idx.shape[-1])
+    if attn_scale is None:
+        attn_scale = (C // heads) ** -0.5
+    out = torch.empty_like(q) if out is None else out
+    wp, bp, ks = _lepe_args(lepe_w, lepe_b, C)
+    _check(load().bra_video_attend(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), B, T,
+                                   H, W, C, heads, S, topk, dt, float(attn_scale), wp, bp, ks,
+                                   out.data_ptr(), _stream(q)))
+    return out

@@ -256,7 +256,7 @@ bra_status check_video_shape(int B, int T, int H, int W, int C, int S, int heads
                              bra_dtype dt, bra::Shape* out) {
   bra_status st;
   if (T < 1) return fail(BRA_E_INVAL, "T=%d frames must be positive", T);
-  if (heads < 1) return fail(BRA_E_INVAL, "heads=%d must be positive", heads);
+  if (heads < 0) return fail(BRA_E_INVAL, "heads=%d must be positive", heads);   // 0: unused
   if ((long long)B * T > (1 << 30)) return fail(BRA_E_UNSUPPORTED, "B*T=%lld clips x frames", (long long)B * T);
   // one frame as an image of the batch of B*T frames
   if ((st = check_shape(B * T, H, W, C, S, heads, 1, dt, out))) return st;
@@ -337,6 +337,45 @@ bra_status bra_forward(const void* q, const void* k, const void* v, int B, int H
                           idx, topk_logits, ws, stream);
 }
 
+bra_status bra_video_route(const void* q, const void* k, int B, int T, int H, int W, int C, int S,
+                           int topk, bra_dtype dtype, float route_scale, int32_t* idx,
+                           float* topk_logits, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  bra::Shape s;
+  bra_status st;
+  if ((st = check_video_shape(B, T, H, W, C, S, 0, topk, dtype, &s))) return st;
+  if ((st = check_route_args(q, k, s, dtype, route_scale, idx, topk_logits, ws, ws_bytes))) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  double* qm = (double*)ws;
+  double* km = qm + (size_t)B * s.R * C;
+  if ((st = hip_status(bra::launch_pool(q, k, qm, km, s, dtype == BRA_BF16, hs), "pool launch")))
+    return st;
+  return hip_status(bra::launch_route(qm, km, s, (double)route_scale, idx, topk_logits, hs),
+                    "route launch");
+}
+
+bra_status bra_video_attend(const void* q, const void* k, const void* v, const int32_t* idx, int B,
+                            int T, int H, int W, int C, int heads, int S, int topk,
+                            bra_dtype dtype, float attn_scale, const float* lepe_w,
+                            const float* lepe_b, int lepe_ks, void* out, void* stream) {
+  g_last_error[0] = 0;
+  bra::Shape s;
+  bra_status st;
+  if (heads < 1) return fail(BRA_E_INVAL, "heads=%d must be positive", heads);
+  if ((st = check_video_shape(B, T, H, W, C, S, heads, topk, dtype, &s))) return st;
+  if ((st = check_attend_args(q, k, v, idx, s, dtype, attn_scale, lepe_w, lepe_b, lepe_ks, out)))
+    return st;
+  if (lepe_w) {
+    bra::Shape f = s;
+    f.B = B * T;
+    f.H = H;
+    if ((st = check_lepe_args(lepe_w, lepe_b, lepe_ks, f))) return st;
+  }
+  return hip_status(bra::launch_attend(q, k, v, idx, s, dtype == BRA_BF16, attn_scale, lepe_w,
+                                       lepe_b, lepe_ks, out, (hipStream_t)stream),
+                    "attend launch");
+}
+
 size_t bra_video_workspace_bytes(int B, int T, int S, int C) {
   if (B < 1 || T < 1 || S < 1 || C < 1) return 0;
   return (size_t)2 * B * T * S * S * C * sizeof(double);
@@ -350,6 +389,7 @@ bra_status bra_video_forward(const void* q, const void* k, const void* v, int B,
   g_last_error[0] = 0;
   bra::Shape s;
   bra_status st;
+  if (heads < 1) return fail(BRA_E_INVAL, "heads=%d must be positive", heads);
   if ((st = check_video_shape(B, T, H, W, C, S, heads, topk, dtype, &s))) return st;
   if ((st = check_route_args(q, k, s, dtype, route_scale, idx, topk_logits, ws, ws_bytes))) return st;
   if ((st = check_attend_args(q, k, v, idx, s, dtype, attn_scale, lepe_w, lepe_b, lepe_ks, out)))
