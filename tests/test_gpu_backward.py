@@ -41,6 +41,10 @@ CASES = {
                        "skewed", True),
     "no_lepe": (Workload("nolepe", 53, "bf16", 2, 16, 24, 128, 4, 4, 2, lepe_ks=0), "uniform",
                 False),
+    # a 4 x 64 region with 7x7 LePE: its dout halo does not fit the dK/dV
+    # kernel's LDS, so the LePE term of dV takes the float32 path
+    "wide_ks7_float32_term": (Workload("wide", 55, "bf16", 1, 4, 64, 64, 2, 1, 1, lepe_ks=7),
+                              "uniform", True),
     # 1x1 LePE, a single region (global attention)
     "global_ks1": (Workload("glob", 54, "bf16", 1, 8, 16, 64, 2, 1, 1, lepe_ks=1), "uniform",
                    True),

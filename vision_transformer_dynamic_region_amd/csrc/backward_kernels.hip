@@ -119,13 +119,17 @@ struct BwArgs {
   const float* dv_lepe;   // [B, H, W, C] float32: the LePE term of dV, or null
   int B, H, W, C, S, R, hs, ws, n, heads, topk;
   float scale, scale_log2;
+  FastDiv f_S, f_ws, f_n, f_topk, f_R;   // divisions by launch constants (no integer divide)
 };
 
-// element offset of token t of region r (image-relative)
+// pixel index and element offset of token t of region r (image-relative)
+__device__ __forceinline__ int tok_pix(const BwArgs& a, int r, int t) {
+  const int ry = fdiv(r, a.f_S), rx = r - ry * a.S;
+  const int ty = fdiv(t, a.f_ws), tx = t - ty * a.ws;
+  return (ry * a.hs + ty) * a.W + rx * a.ws + tx;
+}
 __device__ __forceinline__ int tok_off(const BwArgs& a, int r, int t) {
-  const int ry = r / a.S, rx = r - ry * a.S;
-  const int ty = t / a.ws, tx = t - ty * a.ws;
-  return ((ry * a.hs + ty) * a.W + rx * a.ws + tx) * a.C;
+  return tok_pix(a, r, t) * a.C;
 }
 
 // Query-centric pass, two sweeps over the routed keys held in LDS: the
@@ -143,8 +147,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH, int 
   const int ng = a.heads / hpw;
   const int u = blockIdx.x;
   const int hg = u % ng, br = u / ng;
-  const int b = br / a.R, r = br - b * a.R;
+  const int b = fdiv(br, a.f_R), r = br - b * a.R;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 15, lg = lane >> 4;
+  const int lh = hpw == 4 ? 2 : hpw == 2 ? 1 : 0;   // log2(hpw)
   const uint32_t img = (uint32_t)a.H * a.W * a.C;
   const auto Kr = rsrc(a.k + (size_t)b * img, img * 2), Vr = rsrc(a.v + (size_t)b * img, img * 2);
   const auto Qr = rsrc(a.q + (size_t)b * img, img * 2), Gr = rsrc(a.dout + (size_t)b * img, img * 2);
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH, int 
   const int nqb = (a.n + 15) / 16;
   const int ntask = nqb * hpw;                     // (query block, head) pairs
   auto qoff_of = [&](int t) -> uint32_t {
-    const int qb = t / hpw, hh = hg * hpw + (t - (t / hpw) * hpw);
+    const int qb = t >> lh, hh = hg * hpw + (t & (hpw - 1));
     const int q = 16 * qb + lq;
     return (t < ntask && q < a.n) ? (tok_off(a, r, q) + hh * kHd + 8 * lg) * 2 : kBwOob;
   };
@@ -163,11 +168,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH, int 
   // row-major), zero past KC; consecutive threads take consecutive 16-byte
   // chunks of a key row across the heads
   for (int e = tid; e < KCP * 4 * hpw; e += kThreads) {
-    const int c = e & 3, rest = e >> 2, kk = rest / hpw, hl = rest - kk * hpw;
+    const int c = e & 3, rest = e >> 2, kk = rest >> lh, hl = rest & (hpw - 1);
     uint32_t off = kBwOob;
     if (kk < KC) {
-      const int reg = min(max(route[kk / a.n], 0), a.R - 1);
-      off = (tok_off(a, reg, kk % a.n) + (hg * hpw + hl) * kHd + 8 * c) * 2;
+      const int j = fdiv(kk, a.f_n);
+      const int reg = min(max(route[j], 0), a.R - 1);
+      off = (tok_off(a, reg, kk - j * a.n) + (hg * hpw + hl) * kHd + 8 * c) * 2;
     }
     *(uint4*)trow(Ks0 + hl * KCP * kHd, kk, c) = ld16(Kr, off);
     *(uint4*)trow(Vs0 + hl * KCP * kHd, kk, c) = ld16(Vr, off);
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH, int 
   __syncthreads();
   const float c2 = a.scale_log2;
   for (int t = wave; t < ntask; t += kWaves) {
-    const int qb = t / hpw, hl = t - qb * hpw, h = hg * hpw + hl;
+    const int qb = t >> lh, hl = t & (hpw - 1), h = hg * hpw + hl;
     const uint16_t* Ks = Ks0 + hl * KCP * kHd;
     const uint16_t* Vs = Vs0 + hl * KCP * kHd;
     const int q = 16 * qb + lq;
@@ -260,13 +266,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH, int 
     }
     if (qok) {
       // lane holds channels 4 lg + e (acc0) and 16 + 4 lg + e (acc1) of query q
-      uint16_t* dqp = a.dq + (size_t)b * img + tok_off(a, r, q) + h * kHd;
+      const int qpix = tok_pix(a, r, q);
+      uint16_t* dqp = a.dq + (size_t)b * img + qpix * a.C + h * kHd;
       *(uint2*)(dqp + 4 * lg) = make_uint2(pack_bf16x2(acc0[0] * a.scale, acc0[1] * a.scale),
                                            pack_bf16x2(acc0[2] * a.scale, acc0[3] * a.scale));
       *(uint2*)(dqp + 16 + 4 * lg) = make_uint2(pack_bf16x2(acc1[0] * a.scale, acc1[1] * a.scale),
                                                 pack_bf16x2(acc1[2] * a.scale, acc1[3] * a.scale));
       if (lg == 0) {
-        const size_t pix = (size_t)b * a.H * a.W + tok_off(a, r, q) / a.C;
+        const size_t pix = (size_t)b * a.H * a.W + qpix;
         a.lse[pix * a.heads + h] = lse;
         a.dd[pix * a.heads + h] = D;
       }
@@ -296,8 +303,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a, int hpw) {
   const int ng = a.heads / hpw;
   const int u = blockIdx.x;
   const int hg = u % ng, bs = u / ng;
-  const int b = bs / a.R, s = bs - b * a.R;
+  const int b = fdiv(bs, a.f_R), s = bs - b * a.R;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lq = lane & 15, lg = lane >> 4;
+  const int lh = hpw == 4 ? 2 : hpw == 2 ? 1 : 0;   // log2(hpw)
   const uint32_t img = (uint32_t)a.H * a.W * a.C;
   const auto Kr = rsrc(a.k + (size_t)b * img, img * 2), Vr = rsrc(a.v + (size_t)b * img, img * 2);
   const auto Qr = rsrc(a.q + (size_t)b * img, img * 2), Gr = rsrc(a.dout + (size_t)b * img, img * 2);
@@ -347,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a, int hpw) {
           base += w < wave ? c : 0;
           tot += c;
         }
-        if (pred) mlist[base + below] = e / a.topk;
+        if (pred) mlist[base + below] = fdiv(e, a.f_topk);
         cnt += tot;
         e0 += kThreads;
         __syncthreads();
@@ -357,22 +365,22 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a, int hpw) {
         // consecutive threads take consecutive 16-byte chunks of a query row
         // across the group's heads
         for (int e = tid; e < kDkvTile * 4; e += kThreads) {
-          const int c = e & 3, rest = e >> 2, row = rest / hpw, h2 = rest - row * hpw;
+          const int c = e & 3, rest = e >> 2, row = rest >> lh, h2 = rest & (hpw - 1);
           const int fi = t0 + row;
           uint32_t off = kBwOob;
           if (fi < nrows) {
-            const int m = fi / a.n;
+            const int m = fdiv(fi, a.f_n);
             off = (tok_off(a, mlist[m], fi - m * a.n) + (hg * hpw + h2) * kHd + 8 * c) * 2;
           }
           *(uint4*)trow(tiles + h2 * TR * kHd, row, c) = ld16(Qr, off);
           *(uint4*)trow(tiles + kDkvTile * kHd + h2 * TR * kHd, row, c) = ld16(Gr, off);
         }
         for (int e = tid; e < kDkvTile; e += kThreads) {
-          const int row = e / hpw, h2 = e - row * hpw, fi = t0 + row;
+          const int row = e >> lh, h2 = e & (hpw - 1), fi = t0 + row;
           float lv = 3.0e38f, dv = 0.f;               // padding queries: p = 0
           if (fi < nrows) {
-            const int m = fi / a.n;
-            const size_t pix = (size_t)b * a.H * a.W + tok_off(a, mlist[m], fi - m * a.n) / a.C;
+            const int m = fdiv(fi, a.f_n);
+            const size_t pix = (size_t)b * a.H * a.W + tok_pix(a, mlist[m], fi - m * a.n);
             lv = a.lse[pix * a.heads + hg * hpw + h2];
             dv = a.dd[pix * a.heads + hg * hpw + h2];
           }
@@ -724,6 +732,11 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const in
   a.n = s.n; a.heads = s.heads; a.topk = s.topk;
   a.scale = attn_scale;
   a.scale_log2 = attn_scale * 1.4426950408889634f;
+  a.f_S = make_fastdiv(s.S);
+  a.f_ws = make_fastdiv(s.ws);
+  a.f_n = make_fastdiv(s.n);
+  a.f_topk = make_fastdiv(s.topk);
+  a.f_R = make_fastdiv(s.R);
   const size_t px = (size_t)s.B * s.H * s.W;
   unsigned char* w8 = (unsigned char*)ws;
   a.lse = (float*)w8;
