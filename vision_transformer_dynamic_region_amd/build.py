@@ -24,6 +24,7 @@ SOURCES = ["route_kernels.hip", "attend_kernels.hip", "region_kernels.hip", "mod
 EXTRA_FLAGS = {
     "attend_kernels.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "region_kernels.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "backward_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 ARCH = "gfx950"
 

@@ -138,6 +138,7 @@ __device__ __forceinline__ int tok_off(const BwArgs& a, int r, int t) {
 // lanes of a query at the end, giving its log-sum-exp and D; the second
 // recomputes s and dp, forms ds = p (dp - D) and accumulates dq^T = K^T ds^T.
 // Nothing is held per key, so the register count does not grow with topk * n.
+template <bool FULL>                     // FULL: topk * n is a multiple of 32, no key is masked
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH, int hpw) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int KCP = 32 * NH;
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH, int 
         const f32x4 p4 = mfma16(row_op(Vs, key, lg), gop, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool kok = 32 * hh + 16 * half + 4 * lg + e < KC;
+          const bool kok = FULL || 32 * hh + 16 * half + 4 * lg + e < KC;
           sv[4 * half + e] = kok ? s4[e] : -3.0e38f;
           pv[4 * half + e] = p4[e];
         }
@@ -217,7 +218,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH, int 
       D *= sc;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float pe = sv[e] > -1.0e38f ? __builtin_amdgcn_exp2f((sv[e] - mn) * c2) : 0.f;
+        const float ex = __builtin_amdgcn_exp2f((sv[e] - mn) * c2);
+        const float pe = FULL || sv[e] > -1.0e38f ? ex : 0.f;
         l += pe;
         D = fmaf(pe, pv[e], D);
       }
@@ -248,8 +250,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH, int 
         float ds[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool kok = 32 * hh + 16 * half + 4 * lg + e < KC;
-          const float p = kok ? __builtin_amdgcn_exp2f(s4[e] * c2 - lse) : 0.f;
+          const bool kok = FULL || 32 * hh + 16 * half + 4 * lg + e < KC;
+          const float ex = __builtin_amdgcn_exp2f(s4[e] * c2 - lse);
+          const float p = kok ? ex : 0.f;
           ds[e] = p * (p4[e] - D);
         }
         split_bf16x2(ds[0], ds[1], pk[2 * half], pl[2 * half]);
@@ -783,10 +786,14 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const in
     if (hk == 1 && KB * c <= kWaves && s.heads % c == 0) hk = c;
   }
   const size_t lq = (size_t)2 * hq * 32 * NH * kHd * 2;
-  e = hipFuncSetAttribute((const void*)bwd_dq_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lq);
+  const bool full = (s.topk * s.n) % 32 == 0;
+  const void* dqf = full ? (const void*)bwd_dq_kernel<true> : (const void*)bwd_dq_kernel<false>;
+  e = hipFuncSetAttribute(dqf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lq);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3(units / hq), dim3(kThreads), lq, st, a, NH, hq);
+  if (full)
+    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(units / hq), dim3(kThreads), lq, st, a, NH, hq);
+  else
+    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(units / hq), dim3(kThreads), lq, st, a, NH, hq);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_dkv_kernel, dim3(units / hk), dim3(kThreads), 0, st, a, hk);
   return hipGetLastError();
