@@ -14,11 +14,14 @@ namespace {
 // out = x + b + depthwise 3x3 cross-correlation of x (zero padding 1), one
 // rounding.  Thread (x, g) owns 16-byte channel group g of pixel column x
 // over a strip of kPosRows rows: its 9 x VEC weights are loaded once, and a
-// 3 x 3 window of vectors slides down the strip, three new loads per output
-// row.  Consecutive threads take consecutive groups of a pixel, then pixels
-// along the row, so every load and the store are coalesced.  32-bit indices
-// within an image.
-constexpr int kPosRows = 8;
+// circular window of three rows of three vectors walks down the strip.  The
+// rows come in batches of three, loaded together by buffer loads that read
+// zero outside the image (no branches); within a batch the window's slots are
+// compile-time, so no data moves.  Consecutive threads take consecutive
+// groups of a pixel, then pixels along the row, so every load and the store
+// are coalesced.  32-bit offsets within an image.
+constexpr int kPosRows = 9;
+static_assert(kPosRows % 3 == 0, "strips are whole batches of three rows");
 
 struct PosArgs {
   const void* x;
@@ -30,6 +33,8 @@ struct PosArgs {
   FastDiv f_G;
 };
 
+typedef uint32_t pos_u32x4 __attribute__((ext_vector_type(4)));
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void pos_conv_kernel(PosArgs a) {
   constexpr int VEC = BF16 ? 8 : 4;
@@ -37,9 +42,11 @@ __global__ __launch_bounds__(kThreads) void pos_conv_kernel(PosArgs a) {
   if (t >= a.row_items) return;
   const int y0 = blockIdx.y * kPosRows, b = blockIdx.z;
   const int xq = fdiv(t, a.f_G), g = t - xq * a.G;
-  const size_t img = (size_t)b * a.H * a.row_items;
-  const uint4* X = (const uint4*)a.x + img;
-  uint4* O = (uint4*)a.out + img;
+  const uint32_t img_bytes = (uint32_t)a.H * a.row_items * 16;
+  const auto X = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>((const void*)((const uint4*)a.x + (size_t)b * a.H * a.row_items)), (short)0,
+      (int)img_bytes, 0x00020000);
+  uint4* O = (uint4*)a.out + (size_t)b * a.H * a.row_items;
   float wt[VEC][9], bias[VEC];
   {
     const float4* wp = (const float4*)(a.w + g * VEC * 9);   // VEC * 9 contiguous floats
@@ -53,45 +60,55 @@ __global__ __launch_bounds__(kThreads) void pos_conv_kernel(PosArgs a) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) bias[e] = a.b ? a.b[g * VEC + e] : 0.f;
   }
-  const bool lft = xq > 0, rgt = xq + 1 < a.W;
-  auto ld = [&](int y, int dx) {                   // vector at (y, x + dx), zero outside
-    const bool ok = (unsigned)y < (unsigned)a.H && (dx < 0 ? lft : dx > 0 ? rgt : true);
-    return ok ? X[y * a.row_items + t + dx * a.G] : make_uint4(0, 0, 0, 0);
+  const bool colok[3] = {xq > 0, true, xq + 1 < a.W};
+  // vector at (y, x + c - 1), zero outside the image
+  auto ld = [&](int y, int c) -> uint4 {
+    const uint32_t off = ((unsigned)y < (unsigned)a.H && colok[c])
+                             ? (uint32_t)(y * a.row_items + t + (c - 1) * a.G) * 16 : 0x80000000u;
+    const pos_u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(X, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
   };
-  uint4 win[3][3];                                  // rows y-1, y, y+1; columns x-1, x, x+1
+  // while row y = yb + u of a batch is computed, row y - 1 + r sits in slot
+  // (u + r) % 3
+  uint4 win[3][3];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int c = 0; c < 3; ++c) win[r + 1][c] = ld(y0 - 1 + r, c - 1);
+    for (int c = 0; c < 3; ++c) win[r][c] = ld(y0 - 1 + r, c);
   const int y1 = min(y0 + kPosRows, a.H);
-  for (int y = y0; y < y1; ++y) {
+  for (int yb = y0; yb < y1; yb += 3) {
+    uint4 nx[3][3];
 #pragma unroll
-    for (int c = 0; c < 3; ++c) {
-      win[0][c] = win[1][c];
-      win[1][c] = win[2][c];
-      win[2][c] = ld(y + 1, c - 1);
-    }
-    float acc[VEC], v[VEC];
-    unpack16<BF16>(win[1][1], v);
+    for (int u = 0; u < 3; ++u)
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = v[e] + bias[e];
+      for (int c = 0; c < 3; ++c) nx[u][c] = ld(yb + u + 1, c);
 #pragma unroll
-    for (int r = 0; r < 3; ++r)
+    for (int u = 0; u < 3; ++u) {
+      const int y = yb + u;
 #pragma unroll
-      for (int c = 0; c < 3; ++c) {
-        unpack16<BF16>(win[r][c], v);
+      for (int c = 0; c < 3; ++c) win[(u + 2) % 3][c] = nx[u][c];
+      float acc[VEC], v[VEC];
+      unpack16<BF16>(win[(u + 1) % 3][1], v);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = fmaf(wt[e][r * 3 + c], v[e], acc[e]);
+      for (int e = 0; e < VEC; ++e) acc[e] = v[e] + bias[e];
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+          unpack16<BF16>(win[(u + r) % 3][c], v);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[e] = fmaf(wt[e][r * 3 + c], v[e], acc[e]);
+        }
+      uint4 o;
+      if constexpr (BF16) {
+        o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                       pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+      } else {
+        o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                       __float_as_uint(acc[3]));
       }
-    uint4 o;
-    if constexpr (BF16) {
-      o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
-    } else {
-      o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
-                     __float_as_uint(acc[3]));
+      if (y < y1) O[y * a.row_items + t] = o;
     }
-    O[y * a.row_items + t] = o;
   }
 }
 
@@ -168,6 +185,8 @@ hipError_t launch_pos_conv(const void* x, const float* w, const float* b, const 
   a.row_items = s.W * a.G;
   a.f_G = make_fastdiv(a.G);
   if (s.H > 65535 || s.B > 65535) return hipErrorInvalidValue;
+  // byte offsets within an image stay below the out-of-range marker
+  if ((long long)s.H * a.row_items * 16 >= 0x80000000LL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((a.row_items + kThreads - 1) / kThreads),
                   (unsigned)((s.H + kPosRows - 1) / kPosRows), (unsigned)s.B);
   if (bf16)
