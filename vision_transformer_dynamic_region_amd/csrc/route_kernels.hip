@@ -130,11 +130,13 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs A) {
 // Bandwidth-first pooling for pixels of G <= 64 16-byte groups (G a power of
 // two): one wavefront per region, lane (p, g) = (lane / G, lane % G) owns
 // channel group g of pixels p, p + 64/G, ...; every load of a batch of up to
-// kWavePass passes (two tensors) is issued before the first add.  The float64
+// kWavePass passes (two tensors; eight passes cover an 8x8 region of
+// 128-byte pixels in one batch) is issued before the first add, as buffer
+// loads with no branch (tokens past the region read zero).  The float64
 // partial sums of the 64/G lanes sharing g are then added with row rotations
 // and row swaps, in a fixed order.
 #ifndef BRA_POOL_NPMAX
-#define BRA_POOL_NPMAX 4
+#define BRA_POOL_NPMAX 8
 #endif
 #ifndef BRA_POOL_WAVES
 #define BRA_POOL_WAVES 4
@@ -174,8 +176,14 @@ __global__ __launch_bounds__(kPoolWaves * 64) void pool_wave_kernel(PoolArgs A) 
   const int lane = threadIdx.x & 63, g = lane % G, p0 = lane / G;
   const int b = fdiv(br, A.f_R), r = br - b * s.R;
   const int ry = fdiv(r, A.f_S), rx = r - ry * s.S;
-  const uint4* __restrict__ q = A.q + (size_t)b * s.H * s.W * G;
-  const uint4* __restrict__ k = TWO ? A.k + (size_t)b * s.H * s.W * G : nullptr;
+  // buffer loads: a token past the region reads zero at an offset past the
+  // record, so every load of a batch is issued unconditionally
+  const uint32_t img_bytes = (uint32_t)s.H * s.W * G * 16;
+  const auto qr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4*>(A.q + (size_t)b * s.H * s.W * G), (short)0, (int)img_bytes, 0x00020000);
+  const auto kr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4*>(TWO ? A.k + (size_t)b * s.H * s.W * G : A.q), (short)0, (int)img_bytes,
+      0x00020000);
   const int base = (ry * s.hs * s.W + rx * s.ws) * G + g;
   double aq[VEC], ak[VEC];
 #pragma unroll
@@ -185,13 +193,16 @@ __global__ __launch_bounds__(kPoolWaves * 64) void pool_wave_kernel(PoolArgs A) 
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       const int t = t0 + u * PP;
-      uq[u] = make_uint4(0, 0, 0, 0);
-      uk[u] = make_uint4(0, 0, 0, 0);
-      if (t < s.n) {
-        const int ty = fdiv(t, A.f_ws), tx = t - ty * s.ws;
-        const int off = base + (ty * s.W + tx) * G;
-        uq[u] = q[off];
-        if constexpr (TWO) uk[u] = k[off];
+      const int ty = fdiv(t, A.f_ws), tx = t - ty * s.ws;
+      const uint32_t off = t < s.n ? (uint32_t)(base + (ty * s.W + tx) * G) * 16 : 0x80000000u;
+      typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+      const u32x4_t vq = __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0);
+      uq[u] = make_uint4(vq.x, vq.y, vq.z, vq.w);
+      if constexpr (TWO) {
+        const u32x4_t vk = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
+        uk[u] = make_uint4(vk.x, vk.y, vk.z, vk.w);
+      } else {
+        uk[u] = make_uint4(0, 0, 0, 0);
       }
     }
 #pragma unroll
@@ -508,7 +519,8 @@ hipError_t launch_pool(const void* q, const void* k, double* qm, double* km, con
   a.f_ws = make_fastdiv(s.ws);
   a.f_R = make_fastdiv(s.R);
   a.f_S = make_fastdiv(s.S);
-  if (G <= 64 && (G & (G - 1)) == 0) {
+  // the wavefront kernel's buffer offsets within an image stay below 2^31
+  if (G <= 64 && (G & (G - 1)) == 0 && (long long)s.H * s.W * G * 16 < 0x80000000LL) {
     // passes per load batch: just enough for the region (at most kWavePass)
     const int passes = (s.n + 64 / G - 1) / (64 / G);
     const int np = passes >= kWavePass ? kWavePass : passes > 2 ? 4 : passes > 1 ? 2 : 1;
