@@ -252,6 +252,10 @@ __global__ __launch_bounds__(kPoolWaves * 64) void pool_wave_kernel(PoolArgs A) 
 // ---------------------------------------------------------------------------
 constexpr int kRouteRows = 16;
 constexpr int kRouteMaxJ = 16;    // R <= 1024 = 16 candidates per lane
+#ifndef BRA_ROUTE_WAVES
+#define BRA_ROUTE_WAVES 16
+#endif
+constexpr int kRouteWaves = BRA_ROUTE_WAVES;   // wavefronts of a route_kernel workgroup
 
 __device__ __forceinline__ long long order_key(double v) {
   v = v + 0.0;                                   // -0 -> +0
@@ -318,7 +322,7 @@ struct RouteArgs {
   int nrb;          // row blocks per image
 };
 
-__global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs A) {
+__global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(RouteArgs A) {
   extern __shared__ double strip[];                // [kRouteRows][lda]
   const Shape& s = A.s;
   const int R = s.R, C = s.C, topk = s.topk;
@@ -332,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs A) {
   const double* __restrict__ kimg = A.km + (size_t)b * R * C;
   const int arow = r0 + l16;
   const int ntile = (R + 15) / 16;
-  for (int ct = wave; ct < ntile; ct += kWaves) {
+  for (int ct = wave; ct < ntile; ct += kRouteWaves) {
     const int bcol = ct * 16 + l16;
     const double* qp = qimg + (size_t)min(arow, R - 1) * C + 4 * lk;
     const double* kp = kimg + (size_t)min(bcol, R - 1) * C + 4 * lk;
@@ -368,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs A) {
   }
   __syncthreads();
 
-  for (int rl = wave; rl < rows; rl += kWaves) {
+  for (int rl = wave; rl < rows; rl += kRouteWaves) {
     const double* ar = strip + rl * A.lda;
     int32_t* irow = A.idx + ((size_t)b * R + r0 + rl) * topk;
     float* lrow = A.logits ? A.logits + ((size_t)b * R + r0 + rl) * topk : nullptr;
@@ -570,7 +574,8 @@ hipError_t launch_route(const double* qm, const double* km, const Shape& s, doub
   const hipError_t e = hipFuncSetAttribute((const void*)route_kernel,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_kernel, dim3((unsigned)(s.B * a.nrb)), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL(route_kernel, dim3((unsigned)(s.B * a.nrb)), dim3(kRouteWaves * 64), lds, st,
+                     a);
   return hipGetLastError();
 }
 
