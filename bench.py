@@ -346,6 +346,27 @@ def run_block(a, wl) -> int:
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / a.steps
     log(f"block: {ms:.4f} ms/step")
+
+    # the largest launch alone: fc1 with the GELU epilogue, [tokens, C] ->
+    # [tokens, 3C] (x read once, the hidden layer written once)
+    hid = [torch.empty((wl.B, wl.H, wl.W, 3 * wl.C), dtype=x0.dtype, device=dev)
+           for _ in range(sets)]
+
+    def fc1_step(i):
+        bra.linear(bufs[i % sets]["x"], params["w_fc1"], params["b_fc1"], out=hid[i % sets],
+                   act="gelu")
+
+    for i in range(a.warmup):
+        fc1_step(i)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(a.steps):
+        fc1_step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_fc1 = e0.elapsed_time(e1) / a.steps
+    fc1_bytes = 4 * wl.tensor_bytes          # x (C) read, hidden (3C) written
+    fc1_gbs = fc1_bytes / (t_fc1 * 1e-3) / 1e9
     res = {
         "metric": "BiFormer block fwd tokens/s (pos conv, LN, BRA module, LN, MLP ratio 3), 1 GPU",
         "value": wl.tokens / (ms * 1e-3),
@@ -356,6 +377,11 @@ def run_block(a, wl) -> int:
         "config": {"workload": f"{wl.name} block: B={wl.B} H=W={wl.H} C={wl.C} "
                                f"heads={wl.heads} S={wl.S} topk={wl.topk}, MLP 3C",
                    "tokens_per_step": wl.tokens, "input_sets_rotated": sets},
+        "stages_ms": {"fc1_gelu": t_fc1},
+        "roofline": {"kernel": "linear_kernel (fc1 with GELU)", "bound": "hbm",
+                     "achieved": fc1_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": fc1_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": fc1_bytes},
     }
     if not a.no_cpu_baseline:
         import oracle as O
