@@ -296,6 +296,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwArgs a, int NH, int 
 // added before the single rounding.
 constexpr int kDkvTile = 128;            // query rows staged per tile
 constexpr int kDkvList = 1024;           // query regions held at once
+static_assert(kDkvTile * 4 == 2 * kThreads && kDkvTile <= kThreads,
+              "tile staging: two 16-byte chunks and at most one statistic a thread");
 
 __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a, int hpw) {
   __shared__ __align__(16) uint16_t tiles[2 * kDkvTile * kHd];   // Q, dO tiles: [hpw][TR][32] each
@@ -366,8 +368,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a, int hpw) {
       const int nrows = cnt * a.n;
       for (int t0 = 0; t0 < nrows; t0 += TR) {
         // consecutive threads take consecutive 16-byte chunks of a query row
-        // across the group's heads
-        for (int e = tid; e < kDkvTile * 4; e += kThreads) {
+        // across the group's heads (two chunks a thread); every load of the
+        // tile, the statistics included, is issued before the first LDS store
+        uint4 fq[2], fg[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int e = tid + kThreads * u;
           const int c = e & 3, rest = e >> 2, row = rest >> lh, h2 = rest & (hpw - 1);
           const int fi = t0 + row;
           uint32_t off = kBwOob;
@@ -375,18 +381,28 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a, int hpw) {
             const int m = fdiv(fi, a.f_n);
             off = (tok_off(a, mlist[m], fi - m * a.n) + (hg * hpw + h2) * kHd + 8 * c) * 2;
           }
-          *(uint4*)trow(tiles + h2 * TR * kHd, row, c) = ld16(Qr, off);
-          *(uint4*)trow(tiles + kDkvTile * kHd + h2 * TR * kHd, row, c) = ld16(Gr, off);
+          fq[u] = ld16(Qr, off);
+          fg[u] = ld16(Gr, off);
         }
-        for (int e = tid; e < kDkvTile; e += kThreads) {
-          const int row = e >> lh, h2 = e & (hpw - 1), fi = t0 + row;
-          float lv = 3.0e38f, dv = 0.f;               // padding queries: p = 0
+        float lv = 3.0e38f, dv = 0.f;                 // padding queries: p = 0
+        if (tid < kDkvTile) {
+          const int row = tid >> lh, h2 = tid & (hpw - 1), fi = t0 + row;
           if (fi < nrows) {
             const int m = fdiv(fi, a.f_n);
             const size_t pix = (size_t)b * a.H * a.W + tok_pix(a, mlist[m], fi - m * a.n);
             lv = a.lse[pix * a.heads + hg * hpw + h2];
             dv = a.dd[pix * a.heads + hg * hpw + h2];
           }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int e = tid + kThreads * u;
+          const int c = e & 3, rest = e >> 2, row = rest >> lh, h2 = rest & (hpw - 1);
+          *(uint4*)trow(tiles + h2 * TR * kHd, row, c) = fq[u];
+          *(uint4*)trow(tiles + kDkvTile * kHd + h2 * TR * kHd, row, c) = fg[u];
+        }
+        if (tid < kDkvTile) {
+          const int row = tid >> lh, h2 = tid & (hpw - 1);
           Ls0[h2 * TR + row] = lv;
           Ds0[h2 * TR + row] = dv;
         }
