@@ -222,6 +222,9 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinArgs a) {
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     // 16-byte chunks of output: kLinCols * ES / 16 per token row, 64 lanes per store
+    const int n_last = min(n0 + kLinCols, a.N) - 1;
+    const int g_tile = __builtin_amdgcn_readfirstlane(n0 / a.ng);
+    const bool one_group = g_tile == __builtin_amdgcn_readfirstlane(n_last / a.ng);
     constexpr int CPRO = kLinCols * ES / 16;
     constexpr int TPS = 64 / CPRO;                 // token rows per store
 #pragma unroll
@@ -251,8 +254,14 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinArgs a) {
         v = *(const uint4*)sp;                     // bf16 staged, or float32 output
       }
       // a chunk lies in one group (ng is a multiple of 8 or the chunk is the
-      // last, partial one of a single group: N % 8 == 4 in bf16)
-      const int g = ok ? n / a.ng : 0, col = n - g * a.ng;
+      // last, partial one of a single group: N % 8 == 4 in bf16).  When the
+      // whole tile lies in one group (the usual case) the group is uniform
+      // and its descriptor is built once in scalar registers; otherwise each
+      // lane's group is used (the compiler then loops over the distinct ones)
+      int g;
+      if (one_group) g = g_tile;
+      else g = ok ? n / a.ng : 0;
+      const int col = n - g * a.ng;
       const auto Y = lin_rsrc(a.y[g], (uint32_t)a.T * a.ng * ES);
       const uint32_t off = ok ? ((uint32_t)t * a.ng + col) * ES : kLinOob;
       if (n + CE <= a.N) {

@@ -171,7 +171,9 @@ __global__ __launch_bounds__(kPoolWaves * 64) void pool_wave_kernel(PoolArgs A) 
   constexpr int VEC = BF16 ? 8 : 4;
   constexpr int PP = 64 / G;                 // pixels per pass
   const Shape& s = A.s;
-  const int br = blockIdx.x * kPoolWaves + (threadIdx.x >> 6);
+  // the wavefront's region, uniform by construction (readfirstlane tells the
+  // compiler so: the buffer descriptors below then live in scalar registers)
+  const int br = __builtin_amdgcn_readfirstlane(blockIdx.x * kPoolWaves + (threadIdx.x >> 6));
   if (br >= A.units) return;                 // no barrier follows
   const int lane = threadIdx.x & 63, g = lane % G, p0 = lane / G;
   const int b = fdiv(br, A.f_R), r = br - b * s.R;
