@@ -132,3 +132,38 @@ def test_deterministic_and_stream(cuda, name):
     s.synchronize()
     assert torch.equal(idx3, idx)
     assert torch.equal(out3.view(torch.int16), out.view(torch.int16))
+
+
+POOL = {
+    # name: (B, H, W, C, S, dtype): the float64 region means of every pooling
+    # kernel and lane layout
+    "two_regions_per_wave_odd_count": (43, 28, 28, 64, 7, "bf16"),     # 2107 regions
+    "two_regions_per_wave_full_batch": (43, 56, 56, 64, 7, "bf16"),    # 8 passes a region
+    "ragged_passes": (2, 12, 12, 64, 2, "bf16"),        # 36 pixels: 5 of 8 passes hold tokens
+    "f32_G16": (3, 16, 16, 64, 4, "f32"),
+    "f32_G32": (2, 8, 8, 128, 2, "f32"),
+    "G64_no_scatter": (3, 4, 4, 512, 2, "bf16"),        # a lane's values span q and k
+    "G4_wave_kernel": (2, 16, 16, 32, 4, "bf16"),
+    "G12_lane_kernel": (2, 24, 8, 96, 4, "bf16"),
+    "G64_many_passes": (1, 8, 8, 512, 2, "bf16"),       # 16 pixels: more than one batch
+}
+
+
+@pytest.mark.parametrize("name", list(POOL))
+def test_region_means(cuda, name):
+    """bra_route's workspace holds the float64 means of Q then K; summing bf16
+    or f32 values in float64 is exact or within a rounding of the oracle's."""
+    import torch
+    import vision_transformer_dynamic_region_amd as bra
+    B, H, W, C, S, dtype = POOL[name]
+    print(f"[edge] pool {name} {POOL[name]}", flush=True)
+    wl = Workload(name, 500, dtype, B, H, W, C, max(1, C // 32), S, 1)
+    x = make_inputs(wl)
+    q, k = to_dev(x["q"], dtype), to_dev(x["k"], dtype)
+    ws = torch.full((bra.workspace_bytes(B, S, C),), 0xFF, dtype=torch.uint8, device=cuda)
+    bra.route(q, k, S, 1, workspace=ws)
+    torch.cuda.synchronize()
+    means = ws.view(torch.float64).cpu().numpy().reshape(2, B, S * S, C)
+    for got, t in ((means[0], x["q"]), (means[1], x["k"])):
+        want = oracle.region_mean(t, S)
+        assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, float(np.abs(want).max())), name

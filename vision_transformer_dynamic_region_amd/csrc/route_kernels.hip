@@ -5,6 +5,7 @@
 // 计算范式".
 
 #include <climits>
+#include <type_traits>
 
 #include "device_common.h"
 
@@ -36,6 +37,7 @@ struct PoolArgs {
   Shape s;
   int gl;          // lanes per pixel (power of two, <= 32)
   int units;       // B * R
+  int rpw;         // regions per wavefront (pool_pipe_kernel)
   FastDiv f_ws, f_R, f_S;
 };
 
@@ -144,6 +146,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(PoolArgs A) {
 constexpr int kPoolWaves = BRA_POOL_WAVES;      // wavefronts (regions) per workgroup
 constexpr int kWavePass = BRA_POOL_NPMAX;
 
+
 template <int SH>
 __device__ __forceinline__ double ror_rowd(double v) { return ror_row<SH>(v); }
 
@@ -233,6 +236,145 @@ __global__ __launch_bounds__(kPoolWaves * 64) void pool_wave_kernel(PoolArgs A) 
       if constexpr (TWO) *(double2*)(A.km + o + e) = make_double2(ak[e] * inv_n, ak[e + 1] * inv_n);
     }
   }
+}
+
+// Pipelined pooling for pixels of G in {8, 16, 32, 64} 16-byte groups whose
+// region fits one batch of passes: each wavefront takes rpw consecutive
+// regions.  Lane (p, g) = (lane / G, lane % G) owns group g of pixels p,
+// p + 64/G, ...  As soon as pass u of region r has been added, the load of
+// pass u of region r + 1 goes out into the same registers, so the float64
+// adds of one region overlap the loads of the next.  The last region issues
+// no loads, so none is in flight when the wavefront ends.
+//
+// The float64 partial sums of the 64/G lanes that share g are combined by a
+// reduce-scatter over lane bits 5, 4, 3 (as far as they index pixels): at
+// each step a lane pair exchanges half of its values, so the lane with the
+// bit clear ends with the pair's sums of the lower half and its partner with
+// those of the upper half.  Bits 5 and 4 use the row-swap permutes, which move
+// both halves in one instruction; bit 3 a DPP row rotation.  Afterwards lane
+// (p, g) holds values p*KEEP .. p*KEEP + KEEP - 1 of its group (value index
+// = tensor * VEC + channel), fully summed in a fixed order, and stores them.
+// Offsets are 32-bit over the whole tensor (the launcher checks its size).
+// ---------------------------------------------------------------------------
+
+// Exchange within lane pairs differing in bit BIT: the lane with the bit
+// clear returns x + x', the lane with it set y + y' (primes: the partner's).
+template <int BIT>
+__device__ __forceinline__ double pair_keep(double x, double y) {
+  if constexpr (BIT == 5 || BIT == 4) {
+    const unsigned xl = (unsigned)__double2loint(x), xh = (unsigned)__double2hiint(x);
+    const unsigned yl = (unsigned)__double2loint(y), yh = (unsigned)__double2hiint(y);
+    // vdst's upper half (rows 1, 3) trades places with src0's lower half
+    // (rows 0, 2): a clear lane ends with (own x, partner's x), a set lane
+    // with (partner's y, own y)
+    const auto l = BIT == 5 ? __builtin_amdgcn_permlane32_swap(xl, yl, false, false)
+                            : __builtin_amdgcn_permlane16_swap(xl, yl, false, false);
+    const auto h = BIT == 5 ? __builtin_amdgcn_permlane32_swap(xh, yh, false, false)
+                            : __builtin_amdgcn_permlane16_swap(xh, yh, false, false);
+    return __hiloint2double((int)h[0], (int)l[0]) + __hiloint2double((int)h[1], (int)l[1]);
+  } else {
+    static_assert(BIT == 3, "pixel lanes start at bit 3 or above");
+    const bool up = threadIdx.x & 8;
+    const double send = up ? x : y, keep = up ? y : x;
+    return keep + ror_row<8>(send);       // row rotation by 8 = lane ^ 8
+  }
+}
+
+template <int BIT, int M>
+__device__ __forceinline__ void scatter_step(double* v) {
+#pragma unroll
+  for (int i = 0; i < M / 2; ++i) v[i] = pair_keep<BIT>(v[i], v[i + M / 2]);
+}
+
+template <bool BF16, int G, int NP, bool TWO>
+__global__ __launch_bounds__(kPoolWaves * 64) void pool_pipe_kernel(PoolArgs A) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int PP = 64 / G;                 // pixels per pass = lanes sharing g
+  constexpr int NT = TWO ? 2 : 1;
+  constexpr int NV = NT * VEC;               // values per lane
+  constexpr int KEEP = NV / PP;              // values per lane after the scatter
+  static_assert(G >= 8 && G <= 64 && KEEP >= 1, "shape handled by pool_wave_kernel");
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const Shape& s = A.s;
+  const int wv = __builtin_amdgcn_readfirstlane(blockIdx.x * kPoolWaves + (threadIdx.x >> 6));
+  const int r0 = wv * A.rpw;
+  if (r0 >= A.units) return;                 // no barrier follows
+  const int r1 = min(r0 + A.rpw, A.units);
+  const int lane = threadIdx.x & 63, g = lane % G, p = lane / G;
+  const uint32_t bytes = (uint32_t)s.B * s.H * s.W * G * 16;
+  const auto qr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(A.q), (short)0, (int)bytes,
+                                                    0x00020000);
+  const auto kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(TWO ? A.k : A.q), (short)0,
+                                                    (int)bytes, 0x00020000);
+  // this lane's token offsets within a region (bytes); tokens past the
+  // region get an offset past any record
+  uint32_t toff[NP];
+#pragma unroll
+  for (int u = 0; u < NP; ++u) {
+    const int t = p + u * PP;
+    const int ty = fdiv(t, A.f_ws), tx = t - ty * s.ws;
+    toff[u] = t < s.n ? (uint32_t)(((ty * s.W + tx) * G + g) * 16) : 0x80000000u;
+  }
+  // byte offset of region br's first pixel
+  auto region_base = [&](int br) -> uint32_t {
+    const int b = fdiv(br, A.f_R), r = br - b * s.R;
+    const int ry = fdiv(r, A.f_S), rx = r - ry * s.S;
+    return (uint32_t)(((b * s.H + ry * s.hs) * s.W + rx * s.ws) * G * 16);
+  };
+  uint4 bq[NP], bk[NP];
+  auto issue = [&](int u, uint32_t base) {
+    const uint32_t off = base + toff[u];
+    const u32x4_t vq = __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0);
+    bq[u] = make_uint4(vq.x, vq.y, vq.z, vq.w);
+    if constexpr (TWO) {
+      const u32x4_t vk = __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0);
+      bk[u] = make_uint4(vk.x, vk.y, vk.z, vk.w);
+    }
+  };
+  {
+    const uint32_t base = region_base(r0);
+#pragma unroll
+    for (int u = 0; u < NP; ++u) issue(u, base);
+  }
+  const double inv_n = 1.0 / (double)s.n;
+  // one region: add its passes (handing each pass's registers to the next
+  // region's load when NEXT), then reduce and store
+  auto region = [&](int br, auto next) {
+    constexpr bool NEXT = decltype(next)::value;
+    const uint32_t nbase = NEXT ? region_base(br + 1) : 0u;
+    double v[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) v[e] = 0.0;
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      float f[VEC];
+      unpack16<BF16>(bq[u], f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v[e] += (double)f[e];
+      if constexpr (TWO) {
+        unpack16<BF16>(bk[u], f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[VEC + e] += (double)f[e];
+      }
+      if constexpr (NEXT) issue(u, nbase);
+    }
+    if constexpr (PP >= 2) scatter_step<5, NV>(v);
+    if constexpr (PP >= 4) scatter_step<4, NV / 2>(v);
+    if constexpr (PP >= 8) scatter_step<3, NV / 4>(v);
+    // lane p holds values p*KEEP .. p*KEEP + KEEP - 1
+#pragma unroll
+    for (int j = 0; j < KEEP; j += (KEEP >= 2 ? 2 : 1)) {
+      const int o = p * KEEP + j;
+      const int tsr = o / VEC, e = o - tsr * VEC;
+      double* dst = (tsr ? A.km : A.qm) + (size_t)br * s.C + g * VEC + e;
+      if constexpr (KEEP >= 2)
+        *(double2*)dst = make_double2(v[j] * inv_n, v[j + 1] * inv_n);
+      else
+        *dst = v[j] * inv_n;
+    }
+  };
+  for (int br = r0; br + 1 < r1; ++br) region(br, std::true_type());
+  region(r1 - 1, std::false_type());
 }
 
 // ---------------------------------------------------------------------------
@@ -512,6 +654,14 @@ __global__ __launch_bounds__(kSmallWaves * 64) void route_small_kernel(RouteArgs
   }
 }
 
+// Launches pool_pipe_kernel for shapes it covers (one value or more per lane
+// after the scatter); the launcher never selects the others.
+template <bool BF16, int G, int NP, bool TWO>
+void launch_pool_pipe(dim3 grid, const PoolArgs& a, hipStream_t st) {
+  if constexpr ((BF16 ? 8 : 4) * (TWO ? 2 : 1) >= 64 / G)
+    hipLaunchKernelGGL((pool_pipe_kernel<BF16, G, NP, TWO>), grid, dim3(kPoolWaves * 64), 0, st, a);
+}
+
 }  // namespace
 
 hipError_t launch_pool(const void* q, const void* k, double* qm, double* km, const Shape& s,
@@ -525,6 +675,38 @@ hipError_t launch_pool(const void* q, const void* k, double* qm, double* km, con
   a.f_ws = make_fastdiv(s.ws);
   a.f_R = make_fastdiv(s.R);
   a.f_S = make_fastdiv(s.S);
+  const int nv = (bf16 ? 8 : 4) * (k ? 2 : 1);
+  const bool pipe_g = G == 8 || G == 16 || G == 32 || G == 64;
+  const int passes_pipe = pipe_g ? (s.n + 64 / G - 1) / (64 / G) : 0;
+  // the pipelined kernel: offsets over the whole tensor below 2^31, pixel
+  // lanes in bits 3..5, at least one value per lane after the scatter, and a
+  // region read in one batch
+  if (pipe_g && nv >= 64 / G && passes_pipe <= kWavePass &&
+      (long long)s.B * s.H * s.W * G * 16 < 0x80000000LL) {
+    // two regions per wavefront once there are enough regions to fill the
+    // chip twice over (on MI355X the 64-image 56x56 stage-1 shape then pools
+    // and routes in 16.9 us against 17.1 with one); with few regions, one
+    // each keeps more wavefronts busy
+    a.rpw = a.units >= 2048 ? 2 : 1;
+    const int np = passes_pipe > 4 ? 8 : passes_pipe > 2 ? 4 : passes_pipe > 1 ? 2 : 1;
+    const long long waves = (a.units + a.rpw - 1) / a.rpw;
+    const dim3 pgrid((unsigned)((waves + kPoolWaves - 1) / kPoolWaves));
+#define BRA_PIPE_LAUNCH(BB, GG, NN, TT) launch_pool_pipe<BB, GG, NN, TT>(pgrid, a, st)
+#define BRA_PIPE_NP(GG, NN)                                                                   \
+    if (G == GG && np == NN) {                                                               \
+      if (bf16) {                                                                            \
+        if (k) BRA_PIPE_LAUNCH(true, GG, NN, true); else BRA_PIPE_LAUNCH(true, GG, NN, false);   \
+      } else {                                                                               \
+        if (k) BRA_PIPE_LAUNCH(false, GG, NN, true); else BRA_PIPE_LAUNCH(false, GG, NN, false); \
+      }                                                                                      \
+      return hipGetLastError();                                                              \
+    }
+#define BRA_PIPE_G(GG) BRA_PIPE_NP(GG, 1) BRA_PIPE_NP(GG, 2) BRA_PIPE_NP(GG, 4) BRA_PIPE_NP(GG, 8)
+    BRA_PIPE_G(8) BRA_PIPE_G(16) BRA_PIPE_G(32) BRA_PIPE_G(64)
+#undef BRA_PIPE_G
+#undef BRA_PIPE_NP
+#undef BRA_PIPE_LAUNCH
+  }
   // the wavefront kernel's buffer offsets within an image stay below 2^31
   if (G <= 64 && (G & (G - 1)) == 0 && (long long)s.H * s.W * G * 16 < 0x80000000LL) {
     // passes per load batch: just enough for the region (at most kWavePass)
