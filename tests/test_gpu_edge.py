@@ -26,6 +26,9 @@ EDGE = {
     "one_pixel_regions": (1, 4, 4, 32, 1, 4, 3, "bf16", 3),
     "many_tasks": (1, 16, 16, 256, 8, 2, 2, "bf16", 5),
     "S32_R1024": (1, 64, 64, 32, 1, 32, 8, "bf16", 5),
+    "S10_R100": (2, 40, 40, 64, 2, 10, 7, "bf16", 5),      # 16 lanes x 8 slots a row
+    "S12_R144_ragged_slots": (1, 48, 36, 64, 2, 12, 9, "bf16", 3),   # 16 x 9 candidates
+    "S20_R400": (1, 40, 40, 32, 1, 20, 5, "f32", 3),        # 32 lanes a row
     "wide_C1024": (1, 8, 8, 1024, 32, 2, 2, "bf16", 3),
     "f32_ragged": (1, 12, 12, 64, 2, 2, 3, "f32", 5),
     "f32_all": (2, 16, 16, 128, 4, 4, 16, "f32", 7),

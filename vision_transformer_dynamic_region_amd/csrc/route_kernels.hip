@@ -387,15 +387,16 @@ __global__ __launch_bounds__(kPoolWaves * 64) void pool_pipe_kernel(PoolArgs A) 
 // tile per wavefront at a time); each lane feeds 4 consecutive channels as
 // the K elements of 4 successive MFMAs, so one 32-byte load serves 4 steps.
 // The strip lives in LDS only; nothing of A is written to memory.  Ranking
-// then runs per row on one wavefront, either by counting (rank(s) = number
-// of entries ranking before s, each entry broadcast through a scalar
-// register; R <= 64) or by topk rounds of a wavefront arg-max (DPP row
-// rotations and row swaps, no LDS), whichever costs fewer steps; both rank
-// through an order-preserving int64 key (after turning -0 into +0, so that
-// 0 and -0 tie, as they compare equal) and give the same answer.
+// runs topk rounds of an arg-max per row over a group of L = 16, 32 or 64
+// lanes (the narrowest that holds R in 16 candidates a lane: 4, 2 or 1 rows
+// per wavefront), each lane first picking its best untaken candidate, then
+// DPP row rotations and row swaps across the group, no LDS.  For R <= 64,
+// route_small_kernel ranks either that way or by counting (rank(s) = number
+// of entries ranking before s).  Both rank through an order-preserving int64
+// key (after turning -0 into +0, so that 0 and -0 tie, as they compare
+// equal), equal keys by lower index, and give the same answer.
 // ---------------------------------------------------------------------------
 constexpr int kRouteRows = 16;
-constexpr int kRouteMaxJ = 16;    // R <= 1024 = 16 candidates per lane
 #ifndef BRA_ROUTE_WAVES
 #define BRA_ROUTE_WAVES 16
 #endif
@@ -422,9 +423,11 @@ __device__ __forceinline__ void ror_pair(long long& k, int& i) {
   i = ii;
 }
 
-// All lanes end with the (key, index) ranking first over the wavefront:
-// rotations inside each 16-lane row, then swaps between rows.
-__device__ __forceinline__ void wave_best(long long& bk, int& bi) {
+// All lanes of each group of L lanes (L = 16, 32 or 64, groups aligned) end
+// with the (key, index) ranking first over the group: rotations inside each
+// 16-lane row, then, for wider groups, swaps between rows.
+template <int L>
+__device__ __forceinline__ void group_best(long long& bk, int& bi) {
 #define BRA_ROW_STEP(SH)                                  \
   {                                                       \
     long long ok = bk;                                    \
@@ -437,22 +440,27 @@ __device__ __forceinline__ void wave_best(long long& bk, int& bi) {
   BRA_ROW_STEP(2)
   BRA_ROW_STEP(1)
 #undef BRA_ROW_STEP
-  {
-    const bool up16 = threadIdx.x & 16, up32 = threadIdx.x & 32;
-    auto a = __builtin_amdgcn_permlane16_swap((unsigned)bk, (unsigned)bk, false, false);
-    auto h = __builtin_amdgcn_permlane16_swap((unsigned)(bk >> 32), (unsigned)(bk >> 32), false, false);
-    auto x = __builtin_amdgcn_permlane16_swap((unsigned)bi, (unsigned)bi, false, false);
-    long long ok = ((long long)(up16 ? h[0] : h[1]) << 32) | (up16 ? a[0] : a[1]);
-    int oi = (int)(up16 ? x[0] : x[1]);
+  if constexpr (L >= 32) {
+    const bool up16 = threadIdx.x & 16;
+    const auto a = __builtin_amdgcn_permlane16_swap((unsigned)bk, (unsigned)bk, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap((unsigned)(bk >> 32), (unsigned)(bk >> 32), false, false);
+    const auto x = __builtin_amdgcn_permlane16_swap((unsigned)bi, (unsigned)bi, false, false);
+    const long long ok = ((long long)(up16 ? h[0] : h[1]) << 32) | (up16 ? a[0] : a[1]);
+    const int oi = (int)(up16 ? x[0] : x[1]);
     if (ranks_before(ok, oi, bk, bi)) { bk = ok; bi = oi; }
-    a = __builtin_amdgcn_permlane32_swap((unsigned)bk, (unsigned)bk, false, false);
-    h = __builtin_amdgcn_permlane32_swap((unsigned)(bk >> 32), (unsigned)(bk >> 32), false, false);
-    x = __builtin_amdgcn_permlane32_swap((unsigned)bi, (unsigned)bi, false, false);
-    ok = ((long long)(up32 ? h[0] : h[1]) << 32) | (up32 ? a[0] : a[1]);
-    oi = (int)(up32 ? x[0] : x[1]);
+  }
+  if constexpr (L == 64) {
+    const bool up32 = threadIdx.x & 32;
+    const auto a = __builtin_amdgcn_permlane32_swap((unsigned)bk, (unsigned)bk, false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap((unsigned)(bk >> 32), (unsigned)(bk >> 32), false, false);
+    const auto x = __builtin_amdgcn_permlane32_swap((unsigned)bi, (unsigned)bi, false, false);
+    const long long ok = ((long long)(up32 ? h[0] : h[1]) << 32) | (up32 ? a[0] : a[1]);
+    const int oi = (int)(up32 ? x[0] : x[1]);
     if (ranks_before(ok, oi, bk, bi)) { bk = ok; bi = oi; }
   }
 }
+
+__device__ __forceinline__ void wave_best(long long& bk, int& bi) { group_best<64>(bk, bi); }
 
 struct RouteArgs {
   const double* qm;
@@ -461,11 +469,11 @@ struct RouteArgs {
   float* logits;
   Shape s;
   double scale;
-  int use_select;
   int lda;          // LDS row stride of the affinity strip (doubles)
   int nrb;          // row blocks per image
 };
 
+template <int L, int JT>
 __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(RouteArgs A) {
   extern __shared__ double strip[];                // [kRouteRows][lda]
   const Shape& s = A.s;
@@ -516,51 +524,41 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(RouteArgs A) {
   }
   __syncthreads();
 
-  for (int rl = wave; rl < rows; rl += kRouteWaves) {
-    const double* ar = strip + rl * A.lda;
-    int32_t* irow = A.idx + ((size_t)b * R + r0 + rl) * topk;
-    float* lrow = A.logits ? A.logits + ((size_t)b * R + r0 + rl) * topk : nullptr;
-    if (!A.use_select) {
-      // R <= 64: one candidate per lane; rank = number of candidates ranking
-      // before it, each broadcast from its lane through a scalar register
-      const double v = lane < R ? ar[lane] : 0.0;
-      const long long kv = order_key(v);
-      int rank = 0;
-      for (int s2 = 0; s2 < R; ++s2) {
-        const long long k2 = ((long long)__builtin_amdgcn_readlane((int)(kv >> 32), s2) << 32) |
-                             (unsigned)__builtin_amdgcn_readlane((int)kv, s2);
-        rank += ranks_before(k2, s2, kv, lane) ? 1 : 0;
-      }
-      if (lane < R && rank < topk) {
-        irow[rank] = lane;
-        if (lrow) lrow[rank] = (float)v;
-      }
-    } else {
-      // topk rounds of a wavefront arg-max over the remaining candidates
-      long long keys[kRouteMaxJ];
-      const int J = (R + 63) / 64;
+  // ranking: a group of L lanes per strip row, 64 / L rows per wavefront;
+  // lane li of a group holds candidates li, li + L, ... (JT slots), in
+  // increasing index order, so within a lane a strictly larger key is the
+  // only way to rank before the current best
+  constexpr int RPW = 64 / L;
+  if (wave * RPW >= rows) return;                  // wave-uniform; no barrier follows
+  const int rl = wave * RPW + lane / L, li = lane % L;
+  const bool live = rl < rows;
+  const double* ar = strip + min(rl, rows - 1) * A.lda;
+  long long keys[JT];
+  unsigned taken = 0;                              // bit j: slot j taken or empty
 #pragma unroll
-      for (int j = 0; j < kRouteMaxJ; ++j)
-        keys[j] = (j < J && lane + 64 * j < R) ? order_key(ar[lane + 64 * j]) : LLONG_MIN;
-      unsigned taken = 0;
-      for (int kk = 0; kk < topk; ++kk) {
-        long long bk = LLONG_MIN;
-        int bi = 0x7fffffff;
+  for (int j = 0; j < JT; ++j) {
+    const int sc = li + L * j;
+    keys[j] = sc < R ? order_key(ar[sc]) : LLONG_MIN;
+    if (sc >= R) taken |= 1u << j;
+  }
+  int32_t* irow = A.idx + ((size_t)b * R + r0 + rl) * topk;
+  float* lrow = A.logits ? A.logits + ((size_t)b * R + r0 + rl) * topk : nullptr;
+  for (int kk = 0; kk < topk; ++kk) {
+    long long bk = LLONG_MIN;
+    int bi = 0x7fffffff;
 #pragma unroll
-        for (int j = 0; j < kRouteMaxJ; ++j) {
-          const int sc = lane + 64 * j;
-          if (j < J && sc < R && !((taken >> j) & 1u) && ranks_before(keys[j], sc, bk, bi)) {
-            bk = keys[j];
-            bi = sc;
-          }
-        }
-        wave_best(bk, bi);
-        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-        if (lane == 0) {
-          irow[kk] = bi;
-          if (lrow) lrow[kk] = (float)ar[bi];
-        }
+    for (int j = 0; j < JT; ++j) {
+      const int sc = li + L * j;
+      if (!((taken >> j) & 1u) && ranks_before(keys[j], sc, bk, bi)) {
+        bk = keys[j];
+        bi = sc;
       }
+    }
+    group_best<L>(bk, bi);
+    if ((bi & (L - 1)) == li) taken |= 1u << (bi / L);
+    if (li == 0 && live) {
+      irow[kk] = bi;
+      if (lrow) lrow[kk] = (float)ar[bi];
     }
   }
 }
@@ -750,16 +748,24 @@ hipError_t launch_route(const double* qm, const double* km, const Shape& s, doub
                        st, a);
     return hipGetLastError();
   }
-  // rank counting (one candidate per lane, R steps) needs R <= 64; otherwise,
-  // or when few rounds suffice, topk rounds of a wavefront arg-max
-  const int J = (s.R + 63) / 64;
-  a.use_select = (s.R > 64 || (long long)s.topk * (J + 12) < (long long)s.R) ? 1 : 0;
+  // lanes per ranking row: the narrowest group holding R in 16 candidates
+  // a lane (R <= 1024 is checked by the callers)
+  const int L = s.R <= 256 ? 16 : s.R <= 512 ? 32 : 64;
+  const int J = (s.R + L - 1) / L;
+  const void* fn = L == 16 ? (J <= 8 ? (const void*)route_kernel<16, 8> : (const void*)route_kernel<16, 16>)
+                 : L == 32 ? (const void*)route_kernel<32, 16> : (const void*)route_kernel<64, 16>;
   const size_t lds = (size_t)kRouteRows * a.lda * sizeof(double);
-  const hipError_t e = hipFuncSetAttribute((const void*)route_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_kernel, dim3((unsigned)(s.B * a.nrb)), dim3(kRouteWaves * 64), lds, st,
-                     a);
+  const dim3 grid((unsigned)(s.B * a.nrb)), block(kRouteWaves * 64);
+  if (L == 16 && J <= 8)
+    hipLaunchKernelGGL((route_kernel<16, 8>), grid, block, lds, st, a);
+  else if (L == 16)
+    hipLaunchKernelGGL((route_kernel<16, 16>), grid, block, lds, st, a);
+  else if (L == 32)
+    hipLaunchKernelGGL((route_kernel<32, 16>), grid, block, lds, st, a);
+  else
+    hipLaunchKernelGGL((route_kernel<64, 16>), grid, block, lds, st, a);
   return hipGetLastError();
 }
 
