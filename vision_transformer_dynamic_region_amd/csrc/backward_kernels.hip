@@ -707,10 +707,16 @@ DwPlan dw_plan(int B, int H, int W, int C, int ks) {
   if (p.xc > kMaxCols) p.xc = kMaxCols;
   p.nxb = (W + p.xc * ncol - 1) / (p.xc * ncol);
   p.ncb = (CP + p.cpb - 1) / p.cpb;
-  // enough row strips for about 4096 wavefronts, strips of at least 4 rows
+  // row strips for one generation of resident wavefronts: 1024 SIMDs (256
+  // CUs x 4) times the wavefronts a SIMD holds at the kernel's register use
+  // (4 up to 3 x 3, 2 at 5 x 5, 1 at 7 x 7).  A second generation would pay
+  // the strip prologue and the batch waits again, and on MI355X ran 25-40%
+  // slower; strips stay at least two batches long, so the KS - 1 halo rows
+  // each strip reads stay a small share
   const long long waves = (long long)B * p.nxb * p.ncb * kWaves;
-  long long ns = (4096 + waves - 1) / waves;
-  const long long nmax = (H + 3) / 4;
+  const long long target = 1024LL * (ks <= 3 ? 4 : ks == 5 ? 2 : 1);
+  long long ns = (target + waves - 1) / waves;
+  const long long nmax = H / (2 * ks) > 1 ? H / (2 * ks) : 1;
   if (ns > nmax) ns = nmax;
   if (ns < 1) ns = 1;
   p.sr = (int)((H + ns - 1) / ns);
