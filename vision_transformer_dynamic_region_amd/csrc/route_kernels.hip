@@ -383,9 +383,11 @@ __global__ __launch_bounds__(kPoolWaves * 64) void pool_pipe_kernel(PoolArgs A) 
 // §3 affinity and top-k; p2 §4 scaled affinity and top-k).
 //
 // One workgroup per (image, block of 16 rows).  The 16 x R affinity strip is
-// a small float64 GEMM on the matrix cores (v_mfma_f64_16x16x4, one 16 x 16
-// tile per wavefront at a time); each lane feeds 4 consecutive channels as
-// the K elements of 4 successive MFMAs, so one 32-byte load serves 4 steps.
+// a small float64 GEMM on the matrix cores (v_mfma_f64_16x16x4, 16 x 16
+// column tiles dealt to the wavefronts); each lane feeds 4 consecutive
+// channels as the K elements of 4 successive MFMAs, so one 32-byte read
+// serves 4 steps.  The block's query-region rows come from LDS, staged once
+// for all wavefronts; each wavefront loads only its own tiles' key rows.
 // The strip lives in LDS only; nothing of A is written to memory.  Ranking
 // runs topk rounds of an arg-max per row over a group of L = 16, 32 or 64
 // lanes (the narrowest that holds R in 16 candidates a lane: 4, 2 or 1 rows
@@ -401,6 +403,9 @@ constexpr int kRouteRows = 16;
 #define BRA_ROUTE_WAVES 16
 #endif
 constexpr int kRouteWaves = BRA_ROUTE_WAVES;   // wavefronts of a route_kernel workgroup
+constexpr int kRouteTiles = 1024 / 16 / kRouteWaves;   // column tiles a wavefront, R <= 1024
+constexpr int kRouteQs = 66;      // LDS row stride of the staged query rows (doubles): the 16
+                                  // rows' 32-byte reads fall in distinct banks
 
 __device__ __forceinline__ long long order_key(double v) {
   v = v + 0.0;                                   // -0 -> +0
@@ -475,7 +480,7 @@ struct RouteArgs {
 
 template <int L, int JT>
 __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(RouteArgs A) {
-  extern __shared__ double strip[];                // [kRouteRows][lda]
+  extern __shared__ double strip[];                // [kRouteRows][lda], staged rows
   const Shape& s = A.s;
   const int R = s.R, C = s.C, topk = s.topk;
   const int b = blockIdx.x / A.nrb, r0 = (blockIdx.x - b * A.nrb) * kRouteRows;
@@ -483,43 +488,57 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(RouteArgs A) {
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int l16 = lane & 15, lk = lane >> 4;
 
-  // affinity strip on the matrix cores
+  // affinity strip on the matrix cores.  The strip's 16 query-region rows
+  // are staged once per 64-channel chunk into LDS (every wavefront reads
+  // them); each wavefront keeps the accumulators of its column tiles (at
+  // most kRouteTiles) across the chunks and loads its tiles' key rows itself
+  double* qs = strip + kRouteRows * A.lda;          // [16][kRouteQs]
   const double* __restrict__ qimg = A.qm + (size_t)b * R * C;
   const double* __restrict__ kimg = A.km + (size_t)b * R * C;
-  const int arow = r0 + l16;
   const int ntile = (R + 15) / 16;
-  for (int ct = wave; ct < ntile; ct += kRouteWaves) {
-    const int bcol = ct * 16 + l16;
-    const double* qp = qimg + (size_t)min(arow, R - 1) * C + 4 * lk;
-    const double* kp = kimg + (size_t)min(bcol, R - 1) * C + 4 * lk;
-    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-    for (int c0 = 0; c0 < C; c0 += 64) {
-      // lane group lk supplies channels c + 4*lk .. c + 4*lk + 3 (c = c0 + 16*u)
-      // over 4 steps; all 8 loads of the chunk are issued before the MFMAs
+  f64x4 acc[kRouteTiles];
+#pragma unroll
+  for (int t = 0; t < kRouteTiles; ++t) acc[t] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int c0 = 0; c0 < C; c0 += 64) {
+    {
+      const int row = threadIdx.x >> 6, ch = threadIdx.x & 63;   // 16 x 64, one a thread
+      const int rr = min(r0 + row, R - 1);
+      qs[row * kRouteQs + ch] = c0 + ch < C ? qimg[(size_t)rr * C + c0 + ch] : 0.0;
+    }
+    __syncthreads();
+    // lane group lk supplies channels c + 4*lk .. c + 4*lk + 3 (c = c0 + 16*u)
+    // over 4 steps; a tile's 8 loads are issued before its MFMAs
+#pragma unroll
+    for (int t = 0; t < kRouteTiles; ++t) {
+      const int ct = wave + t * kRouteWaves;
+      if (ct >= ntile) break;                                     // wave-uniform
+      const double* kp = kimg + (size_t)min(ct * 16 + l16, R - 1) * C + 4 * lk;
       double4 a4[4], b4[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int cc = c0 + 16 * u;
-        a4[u] = make_double4(0.0, 0.0, 0.0, 0.0);
-        b4[u] = make_double4(0.0, 0.0, 0.0, 0.0);
-        if (cc + 4 * lk < C) {
-          a4[u] = *(const double4*)(qp + cc);
-          b4[u] = *(const double4*)(kp + cc);
-        }
+        b4[u] = cc + 4 * lk < C ? *(const double4*)(kp + cc) : make_double4(0.0, 0.0, 0.0, 0.0);
+        a4[u] = *(const double4*)(qs + l16 * kRouteQs + 16 * u + 4 * lk);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].x, b4[u].x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].y, b4[u].y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].z, b4[u].z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].w, b4[u].w, acc, 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].x, b4[u].x, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].y, b4[u].y, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].z, b4[u].z, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a4[u].w, b4[u].w, acc[t], 0, 0, 0);
       }
     }
-    // D layout (f64 16x16x4): lane holds column l16 of the tile, rows lk + 4*i
+    __syncthreads();                                              // qs is restaged next
+  }
+  // D layout (f64 16x16x4): lane holds column l16 of the tile, rows lk + 4*i
+#pragma unroll
+  for (int t = 0; t < kRouteTiles; ++t) {
+    const int ct = wave + t * kRouteWaves;
+    if (ct >= ntile) break;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = lk + 4 * i, cc = ct * 16 + l16;
-      if (rr < rows && cc < R) strip[rr * A.lda + cc] = A.scale * acc[i];
+      if (rr < rows && cc < R) strip[rr * A.lda + cc] = A.scale * acc[t][i];
     }
   }
   __syncthreads();
@@ -754,7 +773,7 @@ hipError_t launch_route(const double* qm, const double* km, const Shape& s, doub
   const int J = (s.R + L - 1) / L;
   const void* fn = L == 16 ? (J <= 8 ? (const void*)route_kernel<16, 8> : (const void*)route_kernel<16, 16>)
                  : L == 32 ? (const void*)route_kernel<32, 16> : (const void*)route_kernel<64, 16>;
-  const size_t lds = (size_t)kRouteRows * a.lda * sizeof(double);
+  const size_t lds = ((size_t)kRouteRows * a.lda + (size_t)kRouteRows * kRouteQs) * sizeof(double);
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(s.B * a.nrb)), block(kRouteWaves * 64);
