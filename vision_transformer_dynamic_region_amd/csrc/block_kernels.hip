@@ -13,15 +13,21 @@ namespace {
 
 // out = x + b + depthwise 3x3 cross-correlation of x (zero padding 1), one
 // rounding.  Thread (x, g) owns 16-byte channel group g of pixel column x
-// over a strip of kPosRows rows: its 9 x VEC weights are loaded once, and a
+// over a strip of sr rows: its 9 x VEC weights are loaded once, and a
 // circular window of three rows of three vectors walks down the strip.  The
 // rows come in batches of three, loaded together by buffer loads that read
 // zero outside the image (no branches); within a batch the window's slots are
 // compile-time, so no data moves.  Consecutive threads take consecutive
 // groups of a pixel, then pixels along the row, so every load and the store
 // are coalesced.  32-bit offsets within an image.
-constexpr int kPosRows = 9;
-static_assert(kPosRows % 3 == 0, "strips are whole batches of three rows");
+// Strips are whole batches of three rows, at least kPosMinRows long, and
+// the shortest such that the launch is at most one generation of resident
+// wavefronts: kPosWaves = 1024 SIMDs x the 2 a SIMD holds at this kernel's
+// register use (190 VGPRs).  A second generation pays the window prologue
+// and the first batch's wait again (on MI355X the 64-image 56 x 56 x 64 shape
+// took 23.0 us with 9-row strips, 19.5 with 15).
+constexpr int kPosMinRows = 9;
+constexpr long long kPosWaves = 2048;
 
 struct PosArgs {
   const void* x;
@@ -30,6 +36,7 @@ struct PosArgs {
   void* out;
   int H, W, C, G;       // G = 16-byte groups per pixel
   int row_items;        // W * G
+  int sr;               // rows a strip (a multiple of 3)
   FastDiv f_G;
 };
 
@@ -40,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void pos_conv_kernel(PosArgs a) {
   constexpr int VEC = BF16 ? 8 : 4;
   const int t = blockIdx.x * kThreads + threadIdx.x;
   if (t >= a.row_items) return;
-  const int y0 = blockIdx.y * kPosRows, b = blockIdx.z;
+  const int y0 = blockIdx.y * a.sr, b = blockIdx.z;
   const int xq = fdiv(t, a.f_G), g = t - xq * a.G;
   const uint32_t img_bytes = (uint32_t)a.H * a.row_items * 16;
   const auto X = __builtin_amdgcn_make_buffer_rsrc(
@@ -75,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void pos_conv_kernel(PosArgs a) {
   for (int r = 0; r < 2; ++r)
 #pragma unroll
     for (int c = 0; c < 3; ++c) win[r][c] = ld(y0 - 1 + r, c);
-  const int y1 = min(y0 + kPosRows, a.H);
+  const int y1 = min(y0 + a.sr, a.H);
   for (int yb = y0; yb < y1; yb += 3) {
     uint4 nx[3][3];
 #pragma unroll
@@ -187,8 +194,11 @@ hipError_t launch_pos_conv(const void* x, const float* w, const float* b, const 
   if (s.H > 65535 || s.B > 65535) return hipErrorInvalidValue;
   // byte offsets within an image stay below the out-of-range marker
   if ((long long)s.H * a.row_items * 16 >= 0x80000000LL) return hipErrorInvalidValue;
+  const long long per_strip = (long long)((a.row_items + kThreads - 1) / kThreads) * s.B * kWaves;
+  a.sr = kPosMinRows;
+  while (a.sr < s.H && per_strip * ((s.H + a.sr - 1) / a.sr) > kPosWaves) a.sr += 3;
   const dim3 grid((unsigned)((a.row_items + kThreads - 1) / kThreads),
-                  (unsigned)((s.H + kPosRows - 1) / kPosRows), (unsigned)s.B);
+                  (unsigned)((s.H + a.sr - 1) / a.sr), (unsigned)s.B);
   if (bf16)
     hipLaunchKernelGGL(pos_conv_kernel<true>, grid, dim3(kThreads), 0, st, a);
   else
