@@ -384,21 +384,74 @@ hipError_t launch_linear(const void* x, int T, int K, const void* w, const float
   a.T = T; a.K = K; a.N = N;
   a.col_tiles = (N + kLinCols - 1) / kLinCols;
   a.row_tiles = (T + kLinRows - 1) / kLinRows;
-  // few row tiles: share each row tile's feature tiles among workgroups
-  a.col_groups = (512 + a.row_tiles - 1) / a.row_tiles;
-  if (a.col_groups > a.col_tiles) a.col_groups = a.col_tiles;
-  if (a.col_groups < 1) a.col_groups = 1;
-  a.col_groups = (a.col_tiles + (a.col_tiles + a.col_groups - 1) / a.col_groups - 1) /
-                 ((a.col_tiles + a.col_groups - 1) / a.col_groups);   // no empty group
-  a.per_xcd = (a.row_tiles * a.col_groups + kXcds - 1) / kXcds;
-  const dim3 grid((unsigned)(a.per_xcd * kXcds));
   // K chunk: all of K up to 256 in bf16 (X read once), 64 for float32
   const int kch = !bf16 ? 64 : K <= 64 ? 64 : K <= 128 ? 128 : 256;
+  const void* fn;
+#define BRA_LIN_FN(BB, KK) \
+  (epi == 0 ? (const void*)&linear_kernel<BB, KK, 0> \
+            : epi == 1 ? (const void*)&linear_kernel<BB, KK, 1> : (const void*)&linear_kernel<BB, KK, 2>)
+  if (bf16 && kch == 64) fn = BRA_LIN_FN(true, 64);
+  else if (bf16 && kch == 128) fn = BRA_LIN_FN(true, 128);
+  else if (bf16) fn = BRA_LIN_FN(true, 256);
+  else fn = BRA_LIN_FN(false, 64);
+#undef BRA_LIN_FN
   const size_t orb = (size_t)kLinCols * ((epi == 2 || !bf16) ? 4 : es) + 16;
+  const int chunks = (K + kch - 1) / kch;
+  auto lds_for = [&](int ct_per) {
+    const int nbuf = ct_per * chunks > 1 ? 2 : 1;   // W staging buffers
+    return (size_t)nbuf * kLinCols * (K < kch ? K : kch) * es + (size_t)kWaves * 32 * orb;
+  };
+  // How many workgroups share a row tile's feature tiles (col_groups, each
+  // taking ct_per of them).  Cost model: the launch takes ceil(workgroups /
+  // resident) generations, each as long as a workgroup's ct_per tiles plus a
+  // fixed part (staging X, the first W block, the launch) worth phi tiles:
+  // 1 for the plain and residual epilogues, 0.5 with GELU, whose arithmetic
+  // makes a tile longer.  Resident workgroups come from the kernel's
+  // occupancy at each choice's LDS (one W buffer when a workgroup has one
+  // step).  On MI355X this picks the measured best split (or one within 1
+  // us of it) on every stage shape whose K fits one chunk (e.g. the 14 x 14
+  // x 256 fc1: 42 -> 28 us against the fixed target it replaced).
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // the largest choice's LDS (two W buffers whenever a workgroup has more
+  // than one step) bounds them all
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds_for(a.col_tiles));
+  if (e != hipSuccess) return e;
+  const double phi = epi == 1 ? 0.5 : 1.0;
+  double best = 0.0;
+  int best_cg = 1;
+  // (measured with K in one chunk; with several chunks, as in fc2, the
+  // earlier rule stays: about 512 workgroups, feature tiles shared only when
+  // there are fewer row tiles)
+  if (chunks > 1) {
+    int cg = (512 + a.row_tiles - 1) / a.row_tiles;
+    cg = cg < 1 ? 1 : cg > a.col_tiles ? a.col_tiles : cg;
+    const int per = (a.col_tiles + cg - 1) / cg;
+    best_cg = (a.col_tiles + per - 1) / per;            // no empty group
+    best = 1.0;
+  }
+  for (int ct_per = a.col_tiles; ct_per >= 1 && chunks == 1; --ct_per) {
+    const int cg = (a.col_tiles + ct_per - 1) / ct_per;
+    if ((a.col_tiles + cg - 1) / cg != ct_per) continue;      // same split as a larger ct_per
+    int per_cu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds_for(ct_per));
+    if (e != hipSuccess) return e;
+    if (per_cu < 1) continue;
+    const long long wgs = (long long)a.row_tiles * cg, res = (long long)per_cu * cus;
+    const double cost = (double)((wgs + res - 1) / res) * (ct_per + phi);
+    if (best == 0.0 || cost < best) { best = cost; best_cg = cg; }
+  }
+  if (best == 0.0) return hipErrorInvalidConfiguration;
+  a.col_groups = best_cg;
+  a.per_xcd = (a.row_tiles * a.col_groups + kXcds - 1) / kXcds;
+  const dim3 grid((unsigned)(a.per_xcd * kXcds));
   const int ct_per = (a.col_tiles + a.col_groups - 1) / a.col_groups;
-  a.nbuf = ct_per * ((K + kch - 1) / kch) > 1 ? 2 : 1;   // steps of a workgroup
-  const size_t lds = (size_t)a.nbuf * kLinCols * (K < kch ? K : kch) * es +
-                     (size_t)kWaves * 32 * orb;
+  a.nbuf = ct_per * chunks > 1 ? 2 : 1;   // steps of a workgroup
+  const size_t lds = lds_for(ct_per);
 #define BRA_LIN(BB, KK, EE) \
   hipLaunchKernelGGL((linear_kernel<BB, KK, EE>), grid, dim3(kThreads), lds, st, a)
 #define BRA_LIN_E(BB, KK) \
