@@ -278,14 +278,17 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinArgs a) {
 
 // qm = xm Wq^T + bq and km = xm Wk^T + bk in float64 (Wq, Wk: rows 0..C-1
 // and C..2C-1 of w_qkv) on v_mfma_f64_16x16x4f64.  A workgroup owns one
-// 16-row tile of the means and 16 column tiles of 16 (of the 2C outputs);
-// wavefront w takes column tiles w, w+4, w+8, w+12, so each load of a row
-// segment of xm feeds four independent accumulators.  Each lane feeds 4
-// consecutive channels as the k slots of 4 successive MFMAs (the same
-// permutation on both operands); the next 16-channel step's operands are
-// loaded while the current one is multiplied.
-constexpr int kMeansTilesPerWave = 4;
-constexpr int kMeansTilesPerBlock = kMeansTilesPerWave * kWaves;
+// 16-row tile of the means and 4 NT column tiles of 16 (of the 2C outputs);
+// wavefront w takes column tiles w, w+4, ..., so each load of a row segment
+// of xm feeds NT independent accumulators.  Each lane feeds 4 consecutive
+// channels as the k slots of 4 successive MFMAs (the same permutation on both
+// operands); the next 16-channel step's operands are loaded while the
+// current one is multiplied.  NT is 1 for C <= 64 and 2 above: the launch is
+// small (one workgroup per 16 regions and 4 NT tiles), so spreading the
+// C / 4 dependent MFMAs of a tile over more wavefronts wins until the chains
+// are long enough that sharing each xm load pays (on MI355X the module step
+// on the 56 x 56 x 64 stage shape: 87.7 us with 4 tiles a wavefront, 83.7
+// with 1; on the 14 x 14 x 256 one: 111.2 with 4, 109.6 with 2, 117.3 with 1).
 
 struct MeansArgs {
   const double* xm;     // [rows, C]
@@ -297,9 +300,8 @@ struct MeansArgs {
   int col_tiles, col_blocks;
 };
 
-template <bool BF16>
+template <bool BF16, int NT>
 __global__ __launch_bounds__(kThreads) void means_proj_kernel(MeansArgs a) {
-  constexpr int NT = kMeansTilesPerWave;
   const int rt = blockIdx.x / a.col_blocks, cbk = blockIdx.x - rt * a.col_blocks;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, lk = lane >> 4;
   const int r0 = rt * 16;
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void means_proj_kernel(MeansArgs a) {
   bool tok[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    const int ct = cbk * kMeansTilesPerBlock + wave + kWaves * j;
+    const int ct = cbk * NT * kWaves + wave + kWaves * j;
     tok[j] = ct < a.col_tiles;
     wn[j] = tok[j] ? ct * 16 + l16 : 0;
   }
@@ -473,12 +475,17 @@ hipError_t launch_means_proj(const double* xm, int rows, int C, const void* w_qk
   a.xm = xm; a.w = w_qkv; a.b = b_qkv; a.qm = qm; a.km = km;
   a.rows = rows; a.C = C;
   a.col_tiles = 2 * C / 16;
-  a.col_blocks = (a.col_tiles + kMeansTilesPerBlock - 1) / kMeansTilesPerBlock;
+  const int nt = C <= 64 ? 1 : 2;                  // column tiles a wavefront
+  a.col_blocks = (a.col_tiles + nt * kWaves - 1) / (nt * kWaves);
   const dim3 grid((unsigned)(((rows + 15) / 16) * a.col_blocks));
-  if (bf16)
-    hipLaunchKernelGGL(means_proj_kernel<true>, grid, dim3(kThreads), 0, st, a);
+  if (bf16 && nt == 1)
+    hipLaunchKernelGGL((means_proj_kernel<true, 1>), grid, dim3(kThreads), 0, st, a);
+  else if (bf16)
+    hipLaunchKernelGGL((means_proj_kernel<true, 2>), grid, dim3(kThreads), 0, st, a);
+  else if (nt == 1)
+    hipLaunchKernelGGL((means_proj_kernel<false, 1>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(means_proj_kernel<false>, grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((means_proj_kernel<false, 2>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
