@@ -407,8 +407,9 @@ hipError_t launch_linear(const void* x, int T, int K, const void* w, const float
   // taking ct_per of them).  Cost model: the launch takes ceil(workgroups /
   // resident) generations, each as long as a workgroup's ct_per tiles plus a
   // fixed part (staging X, the first W block, the launch) worth phi tiles:
-  // 1 for the plain and residual epilogues, 0.5 with GELU, whose arithmetic
-  // makes a tile longer.  Resident workgroups come from the kernel's
+  // 1 for the plain and residual epilogues, 0.25 with GELU, whose arithmetic
+  // makes a tile longer (0.5 kept the 56 x 56 x 64 fc1 at one workgroup a
+  // row tile: 50.7 us against 47.8 with three).  Resident workgroups come from the kernel's
   // occupancy at each choice's LDS (one W buffer when a workgroup has one
   // step).  On MI355X this picks the measured best split (or one within 1
   // us of it) on every stage shape whose K fits one chunk (e.g. the 14 x 14
@@ -423,7 +424,7 @@ hipError_t launch_linear(const void* x, int T, int K, const void* w, const float
   e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)lds_for(a.col_tiles));
   if (e != hipSuccess) return e;
-  const double phi = epi == 1 ? 0.5 : 1.0;
+  const double phi = epi == 1 ? 0.25 : 1.0;
   double best = 0.0;
   int best_cg = 1;
   // (measured with K in one chunk; with several chunks, as in fc2, the
