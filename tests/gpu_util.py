@@ -1,5 +1,5 @@
 """Helpers for the GPU parity tests: upload seeded inputs, run the oracle,
-compare to the tolerances of the spec contract.
+compare at the accuracy contract of the path.
 
 Tolerances (floating point): max |gpu - ref| <= tol * RMS(ref) over the whole
 tensor, tol = 1e-4 for float32 and 2e-2 for bfloat16; a bfloat16 output is
