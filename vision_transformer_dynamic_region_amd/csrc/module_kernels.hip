@@ -280,10 +280,12 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinArgs a) {
 // and C..2C-1 of w_qkv) on v_mfma_f64_16x16x4f64.  A workgroup owns one
 // 16-row tile of the means and 4 NT column tiles of 16 (of the 2C outputs);
 // wavefront w takes column tiles w, w+4, ..., so each load of a row segment
-// of xm feeds NT independent accumulators.  Each lane feeds 4 consecutive
-// channels as the k slots of 4 successive MFMAs (the same permutation on both
-// operands); the next 16-channel step's operands are loaded while the
-// current one is multiplied.  NT is 1 for C <= 64 and 2 above: the launch is
+// of xm feeds NT independent accumulators.  Each lane feeds CPL consecutive
+// channels as the k slots of CPL successive MFMAs (the same permutation on
+// both operands); the next step's operands are loaded while the current one
+// is multiplied.  CPL is 8 when C is a multiple of 32, else 4: a weight row
+// then arrives as 64-byte segments instead of 32, half the requests (on
+// MI355X the 14 x 14 x 256 module step went 111.3 -> 106.0 us).  NT is 1 for C <= 64 and 2 above: the launch is
 // small (one workgroup per 16 regions and 4 NT tiles), so spreading the
 // C / 4 dependent MFMAs of a tile over more wavefronts wins until the chains
 // are long enough that sharing each xm load pays (on MI355X the module step
@@ -300,14 +302,15 @@ struct MeansArgs {
   int col_tiles, col_blocks;
 };
 
-template <bool BF16, int NT>
+template <bool BF16, int NT, int CPL>
 __global__ __launch_bounds__(kThreads) void means_proj_kernel(MeansArgs a) {
+  constexpr int STEP = 4 * CPL;                     // channels a step
   const int rt = blockIdx.x / a.col_blocks, cbk = blockIdx.x - rt * a.col_blocks;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, lk = lane >> 4;
   const int r0 = rt * 16;
   const int C = a.C;
-  const double* xp = a.xm + (size_t)min(r0 + l16, a.rows - 1) * C + 4 * lk;
-  int wn[NT];                                       // weight row of each tile (clamped)
+  const double* xp = a.xm + (size_t)min(r0 + l16, a.rows - 1) * C + CPL * lk;
+  int wn[NT];
   bool tok[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
@@ -315,18 +318,34 @@ __global__ __launch_bounds__(kThreads) void means_proj_kernel(MeansArgs a) {
     tok[j] = ct < a.col_tiles;
     wn[j] = tok[j] ? ct * 16 + l16 : 0;
   }
-  double4 xa;
-  double wb[NT][4];
+  double xa[CPL];
+  double wb[NT][CPL];
   auto load = [&](int c) {
-    xa = *(const double4*)(xp + c);
+#pragma unroll
+    for (int q = 0; q < CPL / 4; ++q) {
+      const double4 x4 = *(const double4*)(xp + c + 4 * q);
+      xa[4 * q] = x4.x; xa[4 * q + 1] = x4.y; xa[4 * q + 2] = x4.z; xa[4 * q + 3] = x4.w;
+    }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       if constexpr (BF16) {
-        const uint2 w = *(const uint2*)((const uint16_t*)a.w + (size_t)wn[j] * C + c + 4 * lk);
-        wb[j][0] = bf16_lo(w.x); wb[j][1] = bf16_hi(w.x); wb[j][2] = bf16_lo(w.y); wb[j][3] = bf16_hi(w.y);
+        const uint16_t* wp = (const uint16_t*)a.w + (size_t)wn[j] * C + c + CPL * lk;
+        if constexpr (CPL == 8) {
+          const uint4 w = *(const uint4*)wp;
+          const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { wb[j][2 * e] = bf16_lo(u[e]); wb[j][2 * e + 1] = bf16_hi(u[e]); }
+        } else {
+          const uint2 w = *(const uint2*)wp;
+          wb[j][0] = bf16_lo(w.x); wb[j][1] = bf16_hi(w.x); wb[j][2] = bf16_lo(w.y); wb[j][3] = bf16_hi(w.y);
+        }
       } else {
-        const float4 w = *(const float4*)((const float*)a.w + (size_t)wn[j] * C + c + 4 * lk);
-        wb[j][0] = w.x; wb[j][1] = w.y; wb[j][2] = w.z; wb[j][3] = w.w;
+        const float* wp = (const float*)a.w + (size_t)wn[j] * C + c + CPL * lk;
+#pragma unroll
+        for (int q = 0; q < CPL / 4; ++q) {
+          const float4 w = *(const float4*)(wp + 4 * q);
+          wb[j][4 * q] = w.x; wb[j][4 * q + 1] = w.y; wb[j][4 * q + 2] = w.z; wb[j][4 * q + 3] = w.w;
+        }
       }
     }
   };
@@ -334,21 +353,20 @@ __global__ __launch_bounds__(kThreads) void means_proj_kernel(MeansArgs a) {
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f64x4{0.0, 0.0, 0.0, 0.0};
   load(0);
-  for (int c = 0; c < C; c += 16) {
-    const double4 xc = xa;
-    double wc[NT][4];
+  for (int c = 0; c < C; c += STEP) {
+    double xc[CPL], wc[NT][CPL];
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) xc[e] = xa[e];
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) wc[j][e] = wb[j][e];
-    if (c + 16 < C) load(c + 16);
+      for (int e = 0; e < CPL; ++e) wc[j][e] = wb[j][e];
+    if (c + STEP < C) load(c + STEP);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(xc.x, wc[j][0], acc[j], 0, 0, 0);
-      acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(xc.y, wc[j][1], acc[j], 0, 0, 0);
-      acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(xc.z, wc[j][2], acc[j], 0, 0, 0);
-      acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(xc.w, wc[j][3], acc[j], 0, 0, 0);
-    }
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int e = 0; e < CPL; ++e)
+        acc[j] = __builtin_amdgcn_mfma_f64_16x16x4f64(xc[e], wc[j][e], acc[j], 0, 0, 0);
   }
   // D layout (f64 16x16x4): lane holds column l16 of the tile, rows lk + 4i
 #pragma unroll
@@ -479,14 +497,16 @@ hipError_t launch_means_proj(const double* xm, int rows, int C, const void* w_qk
   const int nt = C <= 64 ? 1 : 2;                  // column tiles a wavefront
   a.col_blocks = (a.col_tiles + nt * kWaves - 1) / (nt * kWaves);
   const dim3 grid((unsigned)(((rows + 15) / 16) * a.col_blocks));
-  if (bf16 && nt == 1)
-    hipLaunchKernelGGL((means_proj_kernel<true, 1>), grid, dim3(kThreads), 0, st, a);
-  else if (bf16)
-    hipLaunchKernelGGL((means_proj_kernel<true, 2>), grid, dim3(kThreads), 0, st, a);
-  else if (nt == 1)
-    hipLaunchKernelGGL((means_proj_kernel<false, 1>), grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((means_proj_kernel<false, 2>), grid, dim3(kThreads), 0, st, a);
+  const bool wide = C % 32 == 0;                  // 8 channels a lane
+#define BRA_MP(BB, NN, CC) hipLaunchKernelGGL((means_proj_kernel<BB, NN, CC>), grid, dim3(kThreads), 0, st, a)
+  if (bf16) {
+    if (nt == 1) { if (wide) BRA_MP(true, 1, 8); else BRA_MP(true, 1, 4); }
+    else { if (wide) BRA_MP(true, 2, 8); else BRA_MP(true, 2, 4); }
+  } else {
+    if (nt == 1) { if (wide) BRA_MP(false, 1, 8); else BRA_MP(false, 1, 4); }
+    else { if (wide) BRA_MP(false, 2, 8); else BRA_MP(false, 2, 4); }
+  }
+#undef BRA_MP
   return hipGetLastError();
 }
 
