@@ -29,6 +29,10 @@ EDGE = {
     "S10_R100": (2, 40, 40, 64, 2, 10, 7, "bf16", 5),      # 16 lanes x 8 slots a row
     "S12_R144_ragged_slots": (1, 48, 36, 64, 2, 12, 9, "bf16", 3),   # 16 x 9 candidates
     "S20_R400": (1, 40, 40, 32, 1, 20, 5, "f32", 3),        # 32 lanes a row
+    # more than 64 regions with the query rows staged in several 64-channel
+    # chunks (and a half-filled last chunk)
+    "S9_R81_C256": (1, 18, 18, 256, 8, 9, 4, "bf16", 3),
+    "S9_R81_f32_C96": (2, 18, 18, 96, 3, 9, 5, "f32", 3),
     "wide_C1024": (1, 8, 8, 1024, 32, 2, 2, "bf16", 3),
     "f32_ragged": (1, 12, 12, 64, 2, 2, 3, "f32", 5),
     "f32_all": (2, 16, 16, 128, 4, 4, 16, "f32", 7),
