@@ -283,9 +283,9 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(LinArgs a) {
 // of xm feeds NT independent accumulators.  Each lane feeds CPL consecutive
 // channels as the k slots of CPL successive MFMAs (the same permutation on
 // both operands); the next step's operands are loaded while the current one
-// is multiplied.  CPL is 8 when C is a multiple of 32, else 4: a weight row
-// then arrives as 64-byte segments instead of 32, half the requests (on
-// MI355X the 14 x 14 x 256 module step went 111.3 -> 106.0 us).  NT is 1 for C <= 64 and 2 above: the launch is
+// is multiplied.  The launcher uses CPL = 8 (the module's C is heads of 32
+// channels): a weight row arrives as 64-byte segments, half the requests of
+// CPL = 4 (on MI355X the 14 x 14 x 256 module step went 111.3 -> 106.0 us).  NT is 1 for C <= 64 and 2 above: the launch is
 // small (one workgroup per 16 regions and 4 NT tiles), so spreading the
 // C / 4 dependent MFMAs of a tile over more wavefronts wins until the chains
 // are long enough that sharing each xm load pays (on MI355X the module step
@@ -489,7 +489,7 @@ hipError_t launch_linear(const void* x, int T, int K, const void* w, const float
 hipError_t launch_means_proj(const double* xm, int rows, int C, const void* w_qkv,
                              const float* b_qkv, bool bf16, double* qm, double* km,
                              hipStream_t st) {
-  if (rows <= 0 || C <= 0 || C % 16) return hipErrorInvalidValue;
+  if (rows <= 0 || C <= 0 || C % 32) return hipErrorInvalidValue;
   MeansArgs a;
   a.xm = xm; a.w = w_qkv; a.b = b_qkv; a.qm = qm; a.km = km;
   a.rows = rows; a.C = C;
@@ -497,14 +497,11 @@ hipError_t launch_means_proj(const double* xm, int rows, int C, const void* w_qk
   const int nt = C <= 64 ? 1 : 2;                  // column tiles a wavefront
   a.col_blocks = (a.col_tiles + nt * kWaves - 1) / (nt * kWaves);
   const dim3 grid((unsigned)(((rows + 15) / 16) * a.col_blocks));
-  const bool wide = C % 32 == 0;                  // 8 channels a lane
-#define BRA_MP(BB, NN, CC) hipLaunchKernelGGL((means_proj_kernel<BB, NN, CC>), grid, dim3(kThreads), 0, st, a)
+#define BRA_MP(BB, NN) hipLaunchKernelGGL((means_proj_kernel<BB, NN, 8>), grid, dim3(kThreads), 0, st, a)
   if (bf16) {
-    if (nt == 1) { if (wide) BRA_MP(true, 1, 8); else BRA_MP(true, 1, 4); }
-    else { if (wide) BRA_MP(true, 2, 8); else BRA_MP(true, 2, 4); }
+    if (nt == 1) BRA_MP(true, 1); else BRA_MP(true, 2);
   } else {
-    if (nt == 1) { if (wide) BRA_MP(false, 1, 8); else BRA_MP(false, 1, 4); }
-    else { if (wide) BRA_MP(false, 2, 8); else BRA_MP(false, 2, 4); }
+    if (nt == 1) BRA_MP(false, 1); else BRA_MP(false, 2);
   }
 #undef BRA_MP
   return hipGetLastError();
