@@ -107,16 +107,26 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
 
 
-def _dev(t, name, dtype=None):
+def _on_device(t) -> bool:
+    return t.device.type == "cuda"
+
+
+def _dev(t, name, dtype=None, shape=None):
+    """data_ptr() of a contiguous CUDA tensor, after checking its dtype and
+    (when given) its exact shape.  Every pointer the binding hands to the
+    library passes through here, so a host tensor or a short buffer is
+    rejected before anything is launched."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not _on_device(t):
         raise ValueError(f"{name} must be a CUDA (HIP) tensor, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
     return t.data_ptr()
 
 
@@ -133,6 +143,19 @@ def _bhwc(q):
     if q.dim() != 4:
         raise ValueError("tensors must be [B, H, W, C]")
     return tuple(int(x) for x in q.shape)
+
+
+def _workspace(ws, need: int, device):
+    """(pointer, bytes) of the caller's workspace, or of a new one of
+    max(need, 16) bytes; a given workspace must hold at least need bytes."""
+    import torch
+    if ws is None:
+        ws = torch.empty(max(int(need), 16), dtype=torch.uint8, device=device)
+    ptr = _dev(ws, "workspace")
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace has {nbytes} bytes, {need} needed")
+    return ptr, nbytes
 
 
 def _lepe_args(lepe_w, lepe_b, C):
@@ -170,13 +193,10 @@ def route(q, k, S: int, topk: int, route_scale: float | None = None, workspace=N
         route_scale = C ** -0.5
     idx = torch.empty((B, S * S, topk), dtype=torch.int32, device=q.device)
     logits = torch.empty((B, S * S, topk), dtype=torch.float32, device=q.device) if return_logits else None
-    if workspace is None:
-        workspace = torch.empty(max(workspace_bytes(B, S, C), 16), dtype=torch.uint8, device=q.device)
-    _dev(workspace, "workspace")
+    wsp, wsb = _workspace(workspace, workspace_bytes(B, S, C), q.device)
     _check(load().bra_route(q.data_ptr(), k.data_ptr(), B, H, W, C, S, topk, dt, float(route_scale),
                             idx.data_ptr(), logits.data_ptr() if logits is not None else None,
-                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                            _stream(q)))
+                            wsp, wsb, _stream(q)))
     return (idx, logits) if return_logits else idx
 
 
@@ -198,7 +218,7 @@ def attend(q, k, v, idx, heads: int, S: int, attn_scale: float | None = None, le
         attn_scale = (C // heads) ** -0.5
     if out is None:
         out = torch.empty_like(q)
-    _dev(out, "out", q.dtype)
+    _dev(out, "out", q.dtype, (B, H, W, C))
     wp, bp, ks = _lepe_args(lepe_w, lepe_b, C)
     _check(load().bra_attend(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), B, H, W, C,
                              heads, S, topk, dt, float(attn_scale), wp, bp, ks, out.data_ptr(),
@@ -224,22 +244,17 @@ def forward(q, k, v, heads: int, S: int, topk: int, lepe_w=None, lepe_b=None,
         attn_scale = (C // heads) ** -0.5
     if out is None:
         out = torch.empty_like(q)
-    _dev(out, "out", q.dtype)
+    _dev(out, "out", q.dtype, (B, H, W, C))
     if idx is None:
         idx = torch.empty((B, S * S, topk), dtype=torch.int32, device=q.device)
-    _dev(idx, "idx", torch.int32)
-    if idx.numel() != B * S * S * topk:
-        raise ValueError("idx must hold B*S*S*topk entries")
+    _dev(idx, "idx", torch.int32, (B, S * S, topk))
     logits = torch.empty((B, S * S, topk), dtype=torch.float32, device=q.device) if return_logits else None
-    if workspace is None:
-        workspace = torch.empty(max(workspace_bytes(B, S, C), 16), dtype=torch.uint8, device=q.device)
-    _dev(workspace, "workspace")
+    wsp, wsb = _workspace(workspace, workspace_bytes(B, S, C), q.device)
     wp, bp, ks = _lepe_args(lepe_w, lepe_b, C)
     _check(load().bra_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, W, C, heads, S, topk,
                               dt, float(route_scale), float(attn_scale), wp, bp, ks, out.data_ptr(),
                               idx.data_ptr(), logits.data_ptr() if logits is not None else None,
-                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                              _stream(q)))
+                              wsp, wsb, _stream(q)))
     return (out, idx, logits) if return_logits else (out, idx)
 
 
@@ -309,7 +324,7 @@ def pos_conv(x, w, b=None, out=None):
     bp = _opt(b, "b", torch.float32, (C,))
     if out is None:
         out = torch.empty_like(x)
-    _dev(out, "out", x.dtype)
+    _dev(out, "out", x.dtype, (B, H, W, C))
     _check(load().bra_pos_conv(x.data_ptr(), w.data_ptr(), bp, B, H, W, C, dt, out.data_ptr(),
                                _stream(x)))
     return out
@@ -344,22 +359,17 @@ def module_forward(x, w_qkv, b_qkv, heads: int, S: int, topk: int, lepe_w=None, 
         attn_scale = (C // heads) ** -0.5
     if out is None:
         out = torch.empty_like(x)
-    _dev(out, "out", x.dtype)
+    _dev(out, "out", x.dtype, (B, H, W, C))
     if idx is None:
         idx = torch.empty((B, S * S, topk), dtype=torch.int32, device=x.device)
-    _dev(idx, "idx", torch.int32)
-    if idx.numel() != B * S * S * topk:
-        raise ValueError("idx must hold B*S*S*topk entries")
-    if workspace is None:
-        need = module_workspace_bytes(B, H, W, C, S, dt, w_out is not None)
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
-    _dev(workspace, "workspace")
+    _dev(idx, "idx", torch.int32, (B, S * S, topk))
+    wsp, wsb = _workspace(workspace, module_workspace_bytes(B, H, W, C, S, dt, w_out is not None),
+                          x.device)
     wp, bp, ks = _lepe_args(lepe_w, lepe_b, C)
     _check(load().bra_module_forward(x.data_ptr(), B, H, W, C, heads, S, topk, dt,
                                      w_qkv.data_ptr(), bq, float(route_scale), float(attn_scale),
                                      wp, bp, ks, wo, bo, out.data_ptr(), idx.data_ptr(),
-                                     workspace.data_ptr(),
-                                     workspace.numel() * workspace.element_size(), _stream(x)))
+                                     wsp, wsb, _stream(x)))
     return out, idx
 
 
@@ -373,7 +383,7 @@ def layer_norm(x, gamma, beta, eps: float = 1e-5, out=None):
     _opt(beta, "beta", torch.float32, (C,))
     if out is None:
         out = torch.empty_like(x)
-    _dev(out, "out", x.dtype)
+    _dev(out, "out", x.dtype, tuple(x.shape))
     _check(load().bra_layer_norm(x.data_ptr(), x.numel() // C, C, gamma.data_ptr(),
                                  beta.data_ptr(), float(eps), dt, out.data_ptr(), _stream(x)))
     return out
@@ -420,20 +430,14 @@ def block_forward(x, params: dict, heads: int, S: int, topk: int,
         attn_scale = (C // heads) ** -0.5
     if out is None:
         out = torch.empty_like(x)
-    _dev(out, "out", x.dtype)
+    _dev(out, "out", x.dtype, (B, H, W, C))
     if idx is None:
         idx = torch.empty((B, S * S, topk), dtype=torch.int32, device=x.device)
-    _dev(idx, "idx", torch.int32)
-    if idx.numel() != B * S * S * topk:
-        raise ValueError("idx must hold B*S*S*topk entries")
-    if workspace is None:
-        workspace = torch.empty(max(block_workspace_bytes(B, H, W, C, S, dt), 16),
-                                dtype=torch.uint8, device=x.device)
-    _dev(workspace, "workspace")
+    _dev(idx, "idx", torch.int32, (B, S * S, topk))
+    wsp, wsb = _workspace(workspace, block_workspace_bytes(B, H, W, C, S, dt), x.device)
     _check(load().bra_block_forward(x.data_ptr(), B, H, W, C, heads, S, topk, dt, ctypes.byref(p),
                                     float(route_scale), float(attn_scale), out.data_ptr(),
-                                    idx.data_ptr(), workspace.data_ptr(),
-                                    workspace.numel() * workspace.element_size(), _stream(x)))
+                                    idx.data_ptr(), wsp, wsb, _stream(x)))
     return out, idx
 
 
@@ -459,22 +463,25 @@ def attend_backward(q, k, v, idx, dout, heads: int, S: int, attn_scale: float | 
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dw = torch.empty_like(lepe_w) if lepe_w is not None else None
     db = torch.empty(C, dtype=torch.float32, device=q.device) if lepe_w is not None else None
-    if workspace is None:
-        need = int(load().bra_backward_workspace_bytes(B, H, W, C, heads, S, topk, ks))
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    _dev(workspace, "workspace")
+    need = int(load().bra_backward_workspace_bytes(B, H, W, C, heads, S, topk, ks))
+    wsp, wsb = _workspace(workspace, need, q.device)
     _check(load().bra_attend_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(),
                                       dout.data_ptr(), B, H, W, C, heads, S, topk, dt,
                                       float(attn_scale), wp, ks, dq.data_ptr(), dk.data_ptr(),
                                       dv.data_ptr(), dw.data_ptr() if dw is not None else None,
                                       db.data_ptr() if db is not None else None,
-                                      workspace.data_ptr(),
-                                      workspace.numel() * workspace.element_size(), _stream(q)))
+                                      wsp, wsb, _stream(q)))
     return (dq, dk, dv, dw, db) if lepe_w is not None else (dq, dk, dv)
 
 
 def video_workspace_bytes(B: int, T: int, S: int, C: int) -> int:
     return int(load().bra_video_workspace_bytes(B, T, S, C))
+
+
+def _clip_shape(q):
+    if q.dim() != 5:
+        raise ValueError("clips must be [B, T, H, W, C]")
+    return tuple(int(x) for x in q.shape)
 
 
 def video_forward(q, k, v, heads: int, S: int, topk: int, lepe_w=None, lepe_b=None,
@@ -484,54 +491,43 @@ def video_forward(q, k, v, heads: int, S: int, topk: int, lepe_w=None, lepe_b=No
     frame each, routing over the whole clip, per-frame LePE.  Returns
     (out, idx) or (out, idx, logits)."""
     import torch
-    if q.dim() != 5:
-        raise ValueError("clips must be [B, T, H, W, C]")
-    B, T, H, W, C = (int(x) for x in q.shape)
+    B, T, H, W, C = _clip_shape(q)
     dt = _dtype_code(q)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, n, q.dtype)
-        if tuple(t.shape) != (B, T, H, W, C):
-            raise ValueError("q, k, v must have the same shape")
+        _dev(t, n, q.dtype, (B, T, H, W, C))
     if route_scale is None:
         route_scale = C ** -0.5
     if attn_scale is None:
         attn_scale = (C // heads) ** -0.5
     R = T * S * S
     out = torch.empty_like(q) if out is None else out
-    _dev(out, "out", q.dtype)
+    _dev(out, "out", q.dtype, (B, T, H, W, C))
     idx = torch.empty((B, R, topk), dtype=torch.int32, device=q.device) if idx is None else idx
-    _dev(idx, "idx", torch.int32)
+    _dev(idx, "idx", torch.int32, (B, R, topk))
     logits = torch.empty((B, R, topk), dtype=torch.float32, device=q.device) if return_logits else None
-    if workspace is None:
-        workspace = torch.empty(max(video_workspace_bytes(B, T, S, C), 16), dtype=torch.uint8,
-                                device=q.device)
-    _dev(workspace, "workspace")
+    wsp, wsb = _workspace(workspace, video_workspace_bytes(B, T, S, C), q.device)
     wp, bp, ks = _lepe_args(lepe_w, lepe_b, C)
     _check(load().bra_video_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, T, H, W, C, heads,
                                     S, topk, dt, float(route_scale), float(attn_scale), wp, bp, ks,
                                     out.data_ptr(), idx.data_ptr(),
                                     logits.data_ptr() if logits is not None else None,
-                                    workspace.data_ptr(),
-                                    workspace.numel() * workspace.element_size(), _stream(q)))
+                                    wsp, wsb, _stream(q)))
     return (out, idx, logits) if return_logits else (out, idx)
 
 
 def video_route(q, k, S: int, topk: int, route_scale: float | None = None, workspace=None):
     """Routing of clips (bra_video_route): idx int32 [B, T*S*S, topk]."""
     import torch
-    B, T, H, W, C = (int(x) for x in q.shape)
+    B, T, H, W, C = _clip_shape(q)
     dt = _dtype_code(q)
     _dev(q, "q")
-    _dev(k, "k", q.dtype)
+    _dev(k, "k", q.dtype, (B, T, H, W, C))
     if route_scale is None:
         route_scale = C ** -0.5
     idx = torch.empty((B, T * S * S, topk), dtype=torch.int32, device=q.device)
-    if workspace is None:
-        workspace = torch.empty(max(video_workspace_bytes(B, T, S, C), 16), dtype=torch.uint8,
-                                device=q.device)
+    wsp, wsb = _workspace(workspace, video_workspace_bytes(B, T, S, C), q.device)
     _check(load().bra_video_route(q.data_ptr(), k.data_ptr(), B, T, H, W, C, S, topk, dt,
-                                  float(route_scale), idx.data_ptr(), None, workspace.data_ptr(),
-                                  workspace.numel() * workspace.element_size(), _stream(q)))
+                                  float(route_scale), idx.data_ptr(), None, wsp, wsb, _stream(q)))
     return idx
 
 
@@ -539,15 +535,18 @@ def video_attend(q, k, v, idx, heads: int, S: int, attn_scale: float | None = No
                  lepe_b=None, out=None):
     """Attention of clips over a given index plus per-frame LePE (bra_video_attend)."""
     import torch
-    B, T, H, W, C = (int(x) for x in q.shape)
+    B, T, H, W, C = _clip_shape(q)
     dt = _dtype_code(q)
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, n, q.dtype)
-    _dev(idx, "idx", torch.int32)
+        _dev(t, n, q.dtype, (B, T, H, W, C))
+    if not (isinstance(idx, torch.Tensor) and idx.dim() == 3):
+        raise ValueError("idx must be [B, T*S*S, topk]")
     topk = int(idx.shape[-1])
+    _dev(idx, "idx", torch.int32, (B, T * S * S, topk))
     if attn_scale is None:
         attn_scale = (C // heads) ** -0.5
     out = torch.empty_like(q) if out is None else out
+    _dev(out, "out", q.dtype, (B, T, H, W, C))
     wp, bp, ks = _lepe_args(lepe_w, lepe_b, C)
     _check(load().bra_video_attend(q.data_ptr(), k.data_ptr(), v.data_ptr(), idx.data_ptr(), B, T,
                                    H, W, C, heads, S, topk, dt, float(attn_scale), wp, bp, ks,
