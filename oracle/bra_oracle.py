@@ -445,16 +445,18 @@ def round_storage(X, storage):
 def module_forward(x, w_qkv, b_qkv, heads: int, S: int, topk: int, lepe_w=None,
                    lepe_b=None, w_out=None, b_out=None, route_scale: float | None = None,
                    attn_scale: float | None = None, storage: str | None = None,
-                   return_parts: bool = False):
+                   return_parts: bool = False, idx=None):
     """BRA as a module (p1 §3): Q, K, V = projections of x (M1); routing on
     their region means; attention over the routed regions and LePE on the
     projected V (M3), with Q, K, V and y = O + L stored per ``storage`` (M4);
     then the optional output projection (M2).
 
     x: [B, H, W, C]; w_qkv: [3C, C]; b_qkv: [3C] or None; w_out: [C, C] or
-    None; b_out: [C] or None.  Returns (out, idx) or, with return_parts, a
-    dict with every intermediate: q, k, v (as stored), q_r, k_r, A, idx, O,
-    L, y (as stored) and out.
+    None; b_out: [C] or None.  idx: [B, S*S, topk] to attend over a given
+    route instead of the top-k of the affinities (the fixed-index use of
+    p2 §5; the affinities are still returned).  Returns (out, idx) or, with
+    return_parts, a dict with every intermediate: q, k, v (as stored), q_r,
+    k_r, A, idx, O, L, y (as stored) and out.
     """
     x = _f64(x)
     B, H, W, C = x.shape
@@ -470,7 +472,12 @@ def module_forward(x, w_qkv, b_qkv, heads: int, S: int, topk: int, lepe_w=None,
     q_r = region_mean(q, S)
     k_r = region_mean(k, S)
     A = region_affinity(q_r, k_r, route_scale)
-    idx = topk_route(A, topk)
+    if idx is None:
+        idx = topk_route(A, topk)
+    else:
+        idx = np.asarray(idx, dtype=np.int64)
+        if idx.shape != (B, S * S, topk) or idx.min() < 0 or idx.max() >= S * S:
+            raise ValueError("idx must be [B, S*S, topk] with entries in [0, S*S)")
     q, k, v = (round_storage(t, storage) for t in (q, k, v))
     O = routed_attention(q, k, v, idx, heads, S, attn_scale)
     L = lepe(v, lepe_w, lepe_b) if lepe_w is not None else np.zeros_like(O)
@@ -500,15 +507,15 @@ def gelu(X) -> np.ndarray:
 
 def block_forward(x, p: dict, heads: int, S: int, topk: int, route_scale: float | None = None,
                   attn_scale: float | None = None, storage: str | None = None,
-                  return_parts: bool = False):
+                  return_parts: bool = False, idx=None):
     """One BiFormer block (readings B1-B5) around the BRA module.
 
     p holds the parameters: pos_w [C, 3, 3], pos_b [C]; ln1_g, ln1_b [C];
     w_qkv [3C, C], b_qkv [3C]; lepe_w [C, ks, ks], lepe_b [C] or None; w_out
     [C, C], b_out [C]; ln2_g, ln2_b [C]; w_fc1 [3C, C], b_fc1 [3C]; w_fc2
-    [C, 3C], b_fc2 [C].  Returns (out, idx) or, with return_parts, every
-    stored intermediate (x1, n1, the module's parts under "mod", x2, n2, h,
-    out).
+    [C, 3C], b_fc2 [C].  idx, if given, is the module's route (see
+    module_forward).  Returns (out, idx) or, with return_parts, every stored
+    intermediate (x1, n1, the module's parts under "mod", x2, n2, h, out).
     """
     st = lambda t: round_storage(t, storage)
     x = _f64(x)
@@ -516,7 +523,7 @@ def block_forward(x, p: dict, heads: int, S: int, topk: int, route_scale: float 
     n1 = st(layer_norm(x1, p["ln1_g"], p["ln1_b"]))
     mod = module_forward(n1, p["w_qkv"], p["b_qkv"], heads, S, topk, p["lepe_w"], p["lepe_b"],
                          p["w_out"], p["b_out"], route_scale, attn_scale, storage,
-                         return_parts=True)
+                         return_parts=True, idx=idx)
     x2 = st(x1 + mod["out"])
     n2 = st(layer_norm(x2, p["ln2_g"], p["ln2_b"]))
     h = st(gelu(linear(n2, p["w_fc1"], p["b_fc1"])))

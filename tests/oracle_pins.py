@@ -527,6 +527,69 @@ def pin_block_torch():
     _close(out, ref.numpy(), 1e-12, "block")
 
 
+def pin_block_storage():
+    """Reading B5: with bf16 storage every layer output the block keeps (x1,
+    LN1(x1), x2, LN2(x2), the hidden tensor h and out) is a bf16 number, and
+    each equals torch's float64 layer (conv2d with groups = C, layer_norm,
+    linear, gelu) applied to the previous stored value and rounded to bf16,
+    to within one bf16 ulp (two float64 evaluations may straddle a rounding
+    boundary).  A storage point left out leaves a value that is not a bf16
+    number; one moved to another place changes a value by up to an ulp."""
+    import torch
+    import torch.nn.functional as F
+    B, H, W, C, heads, S, topk = 1, 8, 8, 16, 2, 4, 3
+    x = O.round_storage(_rng(46).normal(size=(B, H, W, C)), "bf16")
+    p = block_params(C, ks=3, seed=47)
+    r = O.block_forward(x, p, heads, S, topk, storage="bf16", return_parts=True)
+    for name in ("x1", "n1", "x2", "n2", "h", "out"):
+        v = np.asarray(r[name])
+        assert np.array_equal(O.round_storage(v, "bf16"), v), f"{name} is not stored in bf16"
+    assert np.array_equal(O.round_storage(r["mod"]["y"], "bf16"), r["mod"]["y"])
+    T = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    rs = lambda t: O.round_storage(t.numpy(), "bf16")
+
+    def ulp_close(got, want, what):
+        a = np.maximum(np.abs(want), 2.0 ** -126)
+        ulp = np.exp2(np.floor(np.log2(a)) - 7)
+        assert np.all(np.abs(np.asarray(got) - want) <= ulp * (1 + 1e-12)), what
+
+    xt = T(x).permute(0, 3, 1, 2)
+    x1 = (xt + F.conv2d(xt, T(p["pos_w"])[:, None], T(p["pos_b"]), padding=1, groups=C))
+    ulp_close(r["x1"], rs(x1.permute(0, 2, 3, 1)), "x1")
+    ulp_close(r["n1"], rs(F.layer_norm(T(r["x1"]), (C,), T(p["ln1_g"]), T(p["ln1_b"]), eps=1e-5)),
+              "n1")
+    ulp_close(r["x2"], rs(T(r["x1"]) + T(r["mod"]["out"])), "x2")
+    ulp_close(r["n2"], rs(F.layer_norm(T(r["x2"]), (C,), T(p["ln2_g"]), T(p["ln2_b"]), eps=1e-5)),
+              "n2")
+    ulp_close(r["h"], rs(F.gelu(F.linear(T(r["n2"]), T(p["w_fc1"]), T(p["b_fc1"])),
+                                approximate="none")), "h")
+    ulp_close(r["out"], rs(T(r["x2"]) + F.linear(T(r["h"]), T(p["w_fc2"]), T(p["b_fc2"]))), "out")
+    # the module inside the block is the module of the stored LN1(x1)
+    m = O.module_forward(r["n1"], p["w_qkv"], p["b_qkv"], heads, S, topk, p["lepe_w"],
+                         p["lepe_b"], p["w_out"], p["b_out"], storage="bf16", return_parts=True)
+    assert np.array_equal(m["out"], r["mod"]["out"])
+
+
+def pin_block_given_route():
+    """With idx given, the block attends over that route: the route the
+    block computes itself gives back the same block, and any other route
+    gives the module's output on that route (the fixed-index use)."""
+    B, H, W, C, heads, S, topk = 1, 8, 8, 8, 2, 4, 2
+    x = _rng(48).normal(size=(B, H, W, C))
+    p = block_params(C, ks=3, seed=49)
+    r = O.block_forward(x, p, heads, S, topk, return_parts=True)
+    r2 = O.block_forward(x, p, heads, S, topk, return_parts=True, idx=r["idx"])
+    assert np.array_equal(r2["out"], r["out"])
+    other = (np.asarray(r["idx"]) + 1) % (S * S)
+    r3 = O.block_forward(x, p, heads, S, topk, return_parts=True, idx=other)
+    m = O.module_forward(r3["n1"], p["w_qkv"], p["b_qkv"], heads, S, topk, p["lepe_w"],
+                         p["lepe_b"], p["w_out"], p["b_out"], return_parts=True, idx=other)
+    assert np.array_equal(r3["idx"], other)
+    _close(r3["out"], r3["x2"] + O.linear(r3["h"], p["w_fc2"], p["b_fc2"]), 1e-13, "block out")
+    _close(r3["mod"]["out"], m["out"], 0.0, "module on the given route")
+    assert not np.allclose(r3["out"], r["out"])
+
+
 # --------------------------------------------------------------------------
 # the backward pass with a fixed index (readings G1, G2)
 
@@ -703,7 +766,8 @@ ALL_PINS = [
     pin_sdpa_masked, pin_lepe_conv2d, pin_invariants, pin_route_ties,
     pin_module_golden, pin_linear_torch, pin_module_reduces_to_bra,
     pin_pool_commutes_with_projection, pin_round_storage_torch, pin_module_storage,
-    pin_layer_norm_torch, pin_gelu_torch, pin_block_torch,
+    pin_layer_norm_torch, pin_gelu_torch, pin_block_torch, pin_block_storage,
+    pin_block_given_route,
     pin_backward_autograd, pin_backward_finite_differences,
     pin_video_single_frame, pin_video_masked_dense_torch, pin_video_frame_permutation,
 ]

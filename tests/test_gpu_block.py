@@ -5,12 +5,24 @@ oracle's block, through the C ABI.
 Each layer is first tested alone, fed the oracle's own stored input (the
 GPU may take any input; the oracle takes none from the GPU), at the contract
 tolerance; the stored references are rounded values, so a full bf16 ulp is
-granted where both sides round.  The whole block is then compared end to end
-at a tolerance derived from its structure: one BRA layer at the contract
-(2e-2) plus, for each of the four stored layer outputs after it (x2, LN2,
-the hidden tensor, the output), one bf16 ulp of disagreement at a rounding
-boundary -- at most 2^-8 of a value, 7.8e-3 of RMS for values up to two
-RMS: 2e-2 + 4 x 7.8e-3 = 5.1e-2 (float32: 5x the contract's 1e-4)."""
+granted where both sides round.
+
+The whole block is then compared end to end on every token.  The block
+routes on LN1(x1), a stored tensor the layer tests pin to one ulp, not
+exactly, so a region row may route differently where its affinities are
+within what those ulps can move them (checked against a bound computed from
+the oracle's values); the oracle is then run on the GPU's route, which is
+the one input it takes from the GPU (as for routing ties of the forward
+pass).  The end-to-end tolerance comes from the block's structure: the BRA
+layer at the contract (2e-2), plus, for each of the four stored layer
+outputs after it (x2, LN2(x2), the hidden tensor, the output), one bf16 ulp
+of disagreement at a rounding boundary -- 2^-8 of a value, 7.8e-3 of RMS
+for values up to two RMS: 2e-2 + 4 x 7.8e-3 = 5.1e-2 (float32: 5x the
+contract's 1e-4).  Rounding flips alone, between the oracle and the same
+block with float32-sized errors before each rounding (both valid
+evaluations of the stored-layer reading), already reach about 1.5e-2 of RMS
+past one ulp on the stage workloads (test_block_tolerance.py measures it on
+the CPU): half of the 3.1e-2 granted to the stored layers."""
 
 from __future__ import annotations
 
@@ -54,6 +66,7 @@ BLOCK_CASES = {
     "st3": "st3",
     "st1_B2": "st1:B=2",
     "ragged_bf16": "ragged",
+    "dense": "dense",
 }
 
 
@@ -114,13 +127,6 @@ def route_rows_match(idx_g, ref, p, wl):
     return same
 
 
-def token_mask(same, wl):
-    """[B, H, W] mask of the tokens whose region row matches."""
-    reg, _ = oracle.region_token_maps(wl.H, wl.W, wl.S)
-    m = same[:, reg]                                                   # [B, H, W]
-    return np.broadcast_to(m[..., None], (*m.shape, wl.C))
-
-
 def _params(bra, p, dt, cuda):
     import torch
     wdt = {"w_qkv", "w_out", "w_fc1", "w_fc2"}
@@ -170,7 +176,10 @@ def test_block_parity(cuda, name):
     torch.cuda.synchronize()
     idx_g = idx.cpu().numpy()
     same = route_rows_match(idx_g, ref, p, wl)
-    mask = token_mask(same, wl)                     # tokens whose region routes as the oracle's
+    if not same.all():
+        # rows routed differently within the bound: the oracle on the GPU's route
+        ref = oracle.block_forward(p["x"], p, wl.heads, wl.S, wl.topk, storage=wl.dtype,
+                                   return_parts=True, idx=idx_g)
     # the stored intermediates the workspace holds, then the output
     es = 2 if dt == "bf16" else 4
     up = lambda n: (n + 255) // 256 * 256
@@ -184,10 +193,9 @@ def test_block_parity(cuda, name):
         print(f"[block] {name} {nm}: err/RMS over one ulp "
               f"{excess_err(got[nm], ref[nm].reshape(-1), dt, stored=True):.2e}", flush=True)
     assert_close(got["x1"], ref["x1"].reshape(-1), dt, f"{name} x1", stored=True)
-    e = assert_close(to_host(out)[mask], ref["out"][mask], dt, f"{name} out", stored=True,
-                     tol=BLOCK_TOL[dt])
+    e = assert_close(to_host(out), ref["out"], dt, f"{name} out", stored=True, tol=BLOCK_TOL[dt])
     print(f"[block] {name}: {int((~same).sum())} region rows routed differently within the "
-          f"bound; out err/RMS over one ulp {e:.2e} on {mask.mean():.4f} of the tokens", flush=True)
+          f"bound; out err/RMS over one ulp {e:.2e} on every token", flush=True)
 
 
 def test_block_in_place(cuda):

@@ -220,7 +220,7 @@ def _gelu_tanh(X):
 
 
 def _block_no_pos_residual(x, p, heads, S, topk, route_scale=None, attn_scale=None,
-                           storage=None, return_parts=False):
+                           storage=None, return_parts=False, idx=None):
     x = np.asarray(x, dtype=np.float64)
     q = dict(p)
     # x1 = conv(x) + b only: subtract x again through a centre tap of -1
@@ -228,11 +228,40 @@ def _block_no_pos_residual(x, p, heads, S, topk, route_scale=None, attn_scale=No
     w[:, 1, 1] -= 1.0
     q["pos_w"] = w
     return _orig["block_forward"](x, q, heads, S, topk, route_scale, attn_scale, storage,
+                                  return_parts, idx=idx)
+
+
+def _block_storage_skipping(skip):
+    """The block with the storage rounding of one layer output left out."""
+    def block(x, p, heads, S, topk, route_scale=None, attn_scale=None, storage=None,
+              return_parts=False, idx=None):
+        st = lambda name, t: t if name == skip else O.round_storage(t, storage)
+        x = np.asarray(x, dtype=np.float64)
+        x1 = st("x1", x + O.lepe(x, p["pos_w"], p["pos_b"]))
+        n1 = st("n1", O.layer_norm(x1, p["ln1_g"], p["ln1_b"]))
+        mod = O.module_forward(n1, p["w_qkv"], p["b_qkv"], heads, S, topk, p["lepe_w"],
+                               p["lepe_b"], p["w_out"], p["b_out"], route_scale, attn_scale,
+                               storage, return_parts=True, idx=idx)
+        x2 = st("x2", x1 + mod["out"])
+        n2 = st("n2", O.layer_norm(x2, p["ln2_g"], p["ln2_b"]))
+        h = st("h", O.gelu(O.linear(n2, p["w_fc1"], p["b_fc1"])))
+        out = st("out", x2 + O.linear(h, p["w_fc2"], p["b_fc2"]))
+        if return_parts:
+            return {"x1": x1, "n1": n1, "mod": mod, "x2": x2, "n2": n2, "h": h, "out": out,
+                    "idx": mod["idx"]}
+        return out, mod["idx"]
+    block.__name__ = f"_block_{skip}_unrounded"
+    return block
+
+
+def _block_ignores_given_route(x, p, heads, S, topk, route_scale=None, attn_scale=None,
+                               storage=None, return_parts=False, idx=None):
+    return _orig["block_forward"](x, p, heads, S, topk, route_scale, attn_scale, storage,
                                   return_parts)
 
 
 def _block_post_norm(x, p, heads, S, topk, route_scale=None, attn_scale=None, storage=None,
-                     return_parts=False):
+                     return_parts=False, idx=None):
     x = np.asarray(x, dtype=np.float64)
     x1 = x + O.lepe(x, p["pos_w"], p["pos_b"])
     mod, idx = O.module_forward(x1, p["w_qkv"], p["b_qkv"], heads, S, topk, p["lepe_w"],
@@ -354,7 +383,9 @@ MUTANTS = {
     "round_storage": [_round_truncating, _round_ties_away],
     "layer_norm": [_ln_unbiased, _ln_no_shift],
     "gelu": [_gelu_tanh],
-    "block_forward": [_block_no_pos_residual, _block_post_norm],
+    "block_forward": [_block_no_pos_residual, _block_post_norm, _block_storage_skipping("h"),
+                      _block_storage_skipping("n2"), _block_storage_skipping("x1"),
+                      _block_ignores_given_route],
     "bra_backward": [_bw_scale_dk_twice, _bw_no_softmax_term, _bw_lepe_not_transposed,
                      _bw_dw_unshifted],
     "video_forward": [_video_lepe_stacked, _video_route_within_frame, _video_time_minor_labels,
