@@ -5,6 +5,7 @@
 // 计算范式", p5 = hyper.ai abstract of arXiv 2303.08810.
 
 #include "device_common.h"
+#include "launch_plan.h"
 
 namespace bra {
 namespace {
@@ -1103,8 +1104,11 @@ hipError_t launch_attend(const void* q, const void* k, const void* v, const int3
                          const Shape& s, bool bf16, float attn_scale, const float* w,
                          const float* bias, int ks, void* out, hipStream_t st) {
   if (bf16 && w) {
-    // a region shape with its own kernel runs there
-    const hipError_t e = launch_attend_region(q, k, v, idx, s, attn_scale, w, bias, ks, out, st);
+    // a shape with its own kernel runs there: whole image in LDS first, then
+    // the per-region gather
+    hipError_t e = launch_attend_image(q, k, v, idx, s, attn_scale, w, bias, ks, out, st);
+    if (e != hipErrorNotSupported) return e;
+    e = launch_attend_region(q, k, v, idx, s, attn_scale, w, bias, ks, out, st);
     if (e != hipErrorNotSupported) return e;
   }
   AttnArgs a;
@@ -1198,14 +1202,35 @@ hipError_t launch_attend(const void* q, const void* k, const void* v, const int3
       int bpc = (int)((160 * 1024) / base_lds);
       if (bpc > 4) bpc = 4;
       if (bpc < 1) bpc = 1;
-      int bpx = 32 * bpc;                           // 32 CUs per XCD
-      if (bpx > a.per_xcd) bpx = a.per_xcd;
-      sa.blocks_per_xcd = bpx;
-      sa.max_units = (a.per_xcd + bpx - 1) / bpx;
-      const size_t lds = off + (size_t)sa.max_units * s.topk * sizeof(int);
-      const dim3 sgrid((unsigned)(bpx * kXcds));
-      return bf16 ? stream_launch<true>(sa, fused_ks, ty, kstep, nkv, sgrid, lds, st)
-                  : stream_launch<false>(sa, fused_ks, ty, kstep, nkv, sgrid, lds, st);
+      // launches over image ranges that keep the routing table within
+      // kTableBytes (at least 32 workgroups per XCD)
+      const long long upi = (long long)s.R * a.groups;
+      const int per = images_per_launch(s.B, upi, kXcds, 1, 32, s.topk, kTableBytes);
+      if (per >= 1) {
+        const size_t img_bytes = (size_t)s.H * s.W * s.C * esz;
+        for (int b0 = 0; b0 < s.B; b0 += per) {
+          const int nb = s.B - b0 < per ? s.B - b0 : per;
+          StreamArgs c = sa;
+          c.a.q = (const char*)q + b0 * img_bytes;
+          c.a.k = (const char*)k + b0 * img_bytes;
+          c.a.v = (const char*)v + b0 * img_bytes;
+          c.a.out = (char*)out + b0 * img_bytes;
+          c.a.idx = idx + (size_t)b0 * s.R * s.topk;
+          c.a.s.B = nb;
+          c.a.units = (int)(nb * upi);
+          c.a.per_xcd = (int)units_per_xcd(c.a.units, kXcds, 1);
+          int bpx = 32 * bpc;                       // 32 CUs per XCD
+          if (bpx > c.a.per_xcd) bpx = c.a.per_xcd;
+          c.blocks_per_xcd = bpx;
+          c.max_units = (int)units_per_workgroup(c.a.per_xcd, bpx);
+          const size_t lds = off + (size_t)c.max_units * s.topk * sizeof(int);
+          const dim3 sgrid((unsigned)(bpx * kXcds));
+          const hipError_t e = bf16 ? stream_launch<true>(c, fused_ks, ty, kstep, nkv, sgrid, lds, st)
+                                    : stream_launch<false>(c, fused_ks, ty, kstep, nkv, sgrid, lds, st);
+          if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+      }
     }
   }
   main_lds = (main_lds + 15) / 16 * 16;

@@ -28,6 +28,7 @@
 // (a strip of rows of a few columns), then float64 sums of the partials.
 
 #include "device_common.h"
+#include "launch_plan.h"
 
 namespace bra {
 namespace {
@@ -517,11 +518,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwArgs a, int hpw) {
 // one row of part: [(b * nstrips + strip) * nxb + xb][C][KK + 1] (the KK
 // taps, then db).  Consecutive threads take consecutive channel pairs of one
 // pixel, so every load is coalesced.
-struct DwPlan {
-  int cpb, xc, nxb, ncb, sr, nstrips;   // pairs/workgroup, columns/workgroup, blocks, strip rows
-  long long rows;                       // partial rows
-};
-constexpr int kMaxCols = 16;            // thread columns of a workgroup: 256 / (C / 2), C >= 32
+// DwPlan, kMaxCols and dw_plan (the strip and column split) are host
+// arithmetic in launch_plan.h.
+static_assert(kThreads == kPlanThreads && kWaves == kPlanWaves, "launch_plan.h thread counts");
 
 template <int KS, int NCOL>              // NCOL: adjacent pixel columns per thread
 __global__ __launch_bounds__(kThreads) void lepe_bwd_kernel(const uint32_t* g, const uint32_t* v,
@@ -694,52 +693,7 @@ __global__ __launch_bounds__(kThreads) void lepe_dw_sum_kernel(const float* part
   }
 }
 
-// columns per thread of lepe_bwd_kernel: two up to 5 x 5 (the weights and
-// dw sums of a channel pair are then shared by twice the pixels), else one
-int lepe_cols(int ks) { return ks <= 5 ? 2 : 1; }
-
-DwPlan dw_plan(int B, int H, int W, int C, int ks) {
-  const int ncol = lepe_cols(ks);
-  DwPlan p;
-  const int CP = C / 2;
-  p.cpb = CP < kThreads ? CP : kThreads;
-  p.xc = kThreads / p.cpb;
-  if (p.xc > kMaxCols) p.xc = kMaxCols;
-  p.nxb = (W + p.xc * ncol - 1) / (p.xc * ncol);
-  p.ncb = (CP + p.cpb - 1) / p.cpb;
-  // row strips for one generation of resident wavefronts: 1024 SIMDs (256
-  // CUs x 4) times the wavefronts a SIMD holds at the kernel's register use
-  // (4 up to 3 x 3, 2 at 5 x 5, 1 at 7 x 7).  A second generation would pay
-  // the strip prologue and the batch waits again, and on MI355X ran 25-40%
-  // slower; strips stay at least two batches long, so the KS - 1 halo rows
-  // each strip reads stay a small share
-  const long long waves = (long long)B * p.nxb * p.ncb * kWaves;
-  const long long target = 1024LL * (ks <= 3 ? 4 : ks == 5 ? 2 : 1);
-  long long ns = (target + waves - 1) / waves;
-  const long long nmax = H / (2 * ks) > 1 ? H / (2 * ks) : 1;
-  if (ns > nmax) ns = nmax;
-  if (ns < 1) ns = 1;
-  p.sr = (int)((H + ns - 1) / ns);
-  p.nstrips = (H + p.sr - 1) / p.sr;
-  p.rows = (long long)B * p.nstrips * p.nxb;
-  return p;
-}
-
 }  // namespace
-
-size_t bwd_workspace_bytes(int B, int H, int W, int C, int heads, int S, int topk, int ks,
-                           bool lepe) {
-  (void)S; (void)topk;
-  const size_t px = (size_t)B * H * W;
-  size_t bytes = 2 * px * heads * sizeof(float);                   // lse, D
-  bytes = (bytes + 255) / 256 * 256;
-  if (lepe) {
-    const DwPlan p = dw_plan(B, H, W, C, ks);
-    bytes += px * C * sizeof(float);                               // dV_L
-    bytes += (size_t)p.rows * C * (ks * ks + 1) * sizeof(float);   // dw / db partial rows
-  }
-  return (bytes + 255) / 256 * 256;
-}
 
 hipError_t launch_backward(const void* q, const void* k, const void* v, const int32_t* idx,
                            const void* dout, const Shape& s, float attn_scale, const float* w,

@@ -206,20 +206,6 @@ hipError_t launch_pos_conv(const void* x, const float* w, const float* b, const 
   return hipGetLastError();
 }
 
-// Lanes per row and groups per lane for a LayerNorm over C channels, or
-// false when a lane would need more than 4 groups.
-bool layer_norm_shape(int C, bool bf16, int* L, int* NG) {
-  const int vec = bf16 ? 8 : 4;
-  if (C % vec) return false;
-  const int G = C / vec;
-  int l = 1;
-  while (l * 2 <= 64 && G % (l * 2) == 0) l *= 2;
-  if (G / l > 4) return false;
-  *L = l;
-  *NG = G / l;
-  return true;
-}
-
 hipError_t launch_layer_norm(const void* x, long long rows, int C, const float* g,
                              const float* b, float eps, bool bf16, void* y, hipStream_t st) {
   NormArgs a;

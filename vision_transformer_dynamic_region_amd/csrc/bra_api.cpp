@@ -231,6 +231,20 @@ BlockLayout block_layout(int B, int H, int W, int C, int S, bra_dtype dt) {
   return b;
 }
 
+// region means and routing: one fused launch where it applies (up to 64
+// regions), else pooling then routing
+bra_status route_launches(const void* q, const void* k, const bra::Shape& s, bool bf16,
+                          float route_scale, int32_t* idx, float* topk_logits, double* qm,
+                          double* km, hipStream_t hs) {
+  bra_status st;
+  const hipError_t e = bra::launch_pool_route(q, k, qm, km, s, bf16, (double)route_scale, idx,
+                                              topk_logits, hs);
+  if (e != hipErrorNotSupported) return hip_status(e, "pool-route launch");
+  if ((st = hip_status(bra::launch_pool(q, k, qm, km, s, bf16, hs), "pool launch"))) return st;
+  return hip_status(bra::launch_route(qm, km, s, (double)route_scale, idx, topk_logits, hs),
+                    "route launch");
+}
+
 // pool, route, attend on validated arguments (an image batch or a clip batch)
 bra_status forward_launches(const void* q, const void* k, const void* v, const bra::Shape& s,
                             bra_dtype dtype, float route_scale, float attn_scale,
@@ -241,10 +255,7 @@ bra_status forward_launches(const void* q, const void* k, const void* v, const b
   const bool bf16 = dtype == BRA_BF16;
   double* qm = (double*)ws;
   double* km = qm + (size_t)s.B * s.R * s.C;
-  if ((st = hip_status(bra::launch_pool(q, k, qm, km, s, bf16, hs), "pool launch"))) return st;
-  if ((st = hip_status(bra::launch_route(qm, km, s, (double)route_scale, idx, topk_logits, hs),
-                       "route launch")))
-    return st;
+  if ((st = route_launches(q, k, s, bf16, route_scale, idx, topk_logits, qm, km, hs))) return st;
   return hip_status(bra::launch_attend(q, k, v, idx, s, bf16, attn_scale, lepe_w, lepe_b, lepe_ks,
                                        out, hs),
                     "attend launch");
@@ -296,10 +307,7 @@ bra_status bra_route(const void* q, const void* k, int B, int H, int W, int C, i
   hipStream_t hs = (hipStream_t)stream;
   double* qm = (double*)ws;
   double* km = qm + (size_t)B * s.R * C;
-  if ((st = hip_status(bra::launch_pool(q, k, qm, km, s, dtype == BRA_BF16, hs), "pool launch")))
-    return st;
-  return hip_status(bra::launch_route(qm, km, s, (double)route_scale, idx, topk_logits, hs),
-                    "route launch");
+  return route_launches(q, k, s, dtype == BRA_BF16, route_scale, idx, topk_logits, qm, km, hs);
 }
 
 bra_status bra_attend(const void* q, const void* k, const void* v, const int32_t* idx, int B,
@@ -348,10 +356,7 @@ bra_status bra_video_route(const void* q, const void* k, int B, int T, int H, in
   hipStream_t hs = (hipStream_t)stream;
   double* qm = (double*)ws;
   double* km = qm + (size_t)B * s.R * C;
-  if ((st = hip_status(bra::launch_pool(q, k, qm, km, s, dtype == BRA_BF16, hs), "pool launch")))
-    return st;
-  return hip_status(bra::launch_route(qm, km, s, (double)route_scale, idx, topk_logits, hs),
-                    "route launch");
+  return route_launches(q, k, s, dtype == BRA_BF16, route_scale, idx, topk_logits, qm, km, hs);
 }
 
 bra_status bra_video_attend(const void* q, const void* k, const void* v, const int32_t* idx, int B,

@@ -59,6 +59,14 @@ hipError_t launch_means_proj(const double* xm, int rows, int C, const void* w_qk
                              const float* b_qkv, bool bf16, double* qm, double* km,
                              hipStream_t st);
 
+// Region means of q and k (float64, written to qm and km as launch_pool
+// does) and the scaled affinity's per-row top-k in one launch, for up to 64
+// regions per image; hipErrorNotSupported for other shapes, before anything
+// is enqueued.
+hipError_t launch_pool_route(const void* q, const void* k, double* qm, double* km,
+                             const Shape& s, bool bf16, double route_scale, int32_t* idx,
+                             float* logits, hipStream_t st);
+
 // Scaled affinity of the region means and per-row top-k.
 hipError_t launch_route(const double* qm, const double* km, const Shape& s,
                         double route_scale, int32_t* idx, float* logits,
@@ -80,6 +88,16 @@ hipError_t launch_attend_region(const void* q, const void* k, const void* v,
                                 float attn_scale, const float* w,
                                 const float* bias, int ks, void* out,
                                 hipStream_t st);
+
+// The same with the whole image's K and V for one head resident in LDS
+// (bf16, 5x5 LePE fused, the 4x4 / top-4 and 2x2 / top-16 region shapes on
+// maps whose padded image fits LDS); hipErrorNotSupported for any other
+// shape, before anything is enqueued.
+hipError_t launch_attend_image(const void* q, const void* k, const void* v,
+                               const int32_t* idx, const Shape& s,
+                               float attn_scale, const float* w,
+                               const float* bias, int ks, void* out,
+                               hipStream_t st);
 
 // out += bias + depthwise ks x ks cross-correlation of v.
 hipError_t launch_lepe(const void* v, const float* w, const float* b, int ks,

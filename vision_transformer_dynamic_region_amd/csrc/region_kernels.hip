@@ -44,6 +44,7 @@
 // in LDS.
 
 #include "device_common.h"
+#include "launch_plan.h"
 
 namespace bra {
 namespace {
@@ -442,20 +443,14 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
 }
 
 template <class G>
-hipError_t region_launch(RegionArgs a, hipStream_t st) {
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  const int cus_per_xcd = cus / kXcds > 0 ? cus / kXcds : 1;
-  a.per_xcd = (a.units + kXcds - 1) / kXcds;
-  a.per_xcd = (a.per_xcd + G::NCB - 1) / G::NCB * G::NCB;
-  // LDS with the routing table sized for one workgroup per CU (an upper bound)
-  const int maxu_bound = (a.per_xcd + cus_per_xcd - 1) / cus_per_xcd;
+hipError_t region_launch_images(RegionArgs a, int cus_per_xcd, int min_bpx, hipStream_t st) {
+  a.per_xcd = (int)units_per_xcd(a.units, kXcds, G::NCB);
+  // LDS with the routing table sized for the fewest workgroups an XCD gets
+  // (one per CU, rounded to whole channel blocks): an upper bound
+  const int maxu_bound = (int)units_per_workgroup(a.per_xcd, min_bpx);
   size_t lds = G::IT_OFF + (size_t)maxu_bound * G::TOPK * sizeof(int);
   const void* fn = reinterpret_cast<const void*>(&attend_region_kernel<G>);
-  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   int per_cu = 0;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_region_kernel<G>, kThreads, lds);
@@ -466,11 +461,41 @@ hipError_t region_launch(RegionArgs a, hipStream_t st) {
   if (bpx < G::NCB) bpx = G::NCB;
   if (bpx > a.per_xcd) bpx = a.per_xcd;
   a.bpx = bpx;
-  const int maxu = (a.per_xcd + bpx - 1) / bpx;
+  const int maxu = (int)units_per_workgroup(a.per_xcd, bpx);
   lds = G::IT_OFF + (size_t)maxu * G::TOPK * sizeof(int);
   hipLaunchKernelGGL(attend_region_kernel<G>, dim3((unsigned)(bpx * kXcds)), dim3(kThreads), lds,
                      st, a);
   return hipGetLastError();
+}
+
+// A batch runs as launches over image ranges small enough that a
+// workgroup's routing table stays within kTableBytes (one launch for every
+// batch of the workload shapes).
+template <class G>
+hipError_t region_launch(RegionArgs a, int B, hipStream_t st) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int cus_per_xcd = cus / kXcds > 0 ? cus / kXcds : 1;
+  const int min_bpx = cus_per_xcd / G::NCB * G::NCB > G::NCB ? cus_per_xcd / G::NCB * G::NCB
+                                                              : G::NCB;
+  const long long upi = (long long)a.R * G::NCB;
+  const int per = images_per_launch(B, upi, kXcds, G::NCB, min_bpx, G::TOPK, kTableBytes);
+  if (per < 1) return hipErrorNotSupported;
+  const size_t img_elems = (size_t)a.H * a.W * G::C;
+  for (int b0 = 0; b0 < B; b0 += per) {
+    const int nb = B - b0 < per ? B - b0 : per;
+    RegionArgs c = a;
+    c.q += b0 * img_elems; c.k += b0 * img_elems; c.v += b0 * img_elems;
+    c.out += b0 * img_elems;
+    c.idx += (size_t)b0 * a.R * G::TOPK;
+    c.units = (int)(nb * upi);
+    e = region_launch_images<G>(c, cus_per_xcd, min_bpx, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // The shapes with a dedicated kernel (d = 32, 5x5 LePE): the BiFormer stage
@@ -510,20 +535,16 @@ hipError_t launch_attend_region(const void* q, const void* k, const void* v, con
     return s.C == C && s.hs == hs && s.ws == ws && s.topk == topk && ks == kks;
   };
   if (is(St1::C, St1::HS, St1::WS, St1::TOPK, St1::KS)) {
-    a.units = s.B * s.R * St1::NCB;
-    return region_launch<St1>(a, st);
+    return region_launch<St1>(a, s.B, st);
   }
   if (is(St2::C, St2::HS, St2::WS, St2::TOPK, St2::KS)) {
-    a.units = s.B * s.R * St2::NCB;
-    return region_launch<St2>(a, st);
+    return region_launch<St2>(a, s.B, st);
   }
   if (is(St3::C, St3::HS, St3::WS, St3::TOPK, St3::KS)) {
-    a.units = s.B * s.R * St3::NCB;
-    return region_launch<St3>(a, st);
+    return region_launch<St3>(a, s.B, st);
   }
   if (is(Dense::C, Dense::HS, Dense::WS, Dense::TOPK, Dense::KS)) {
-    a.units = s.B * s.R * Dense::NCB;
-    return region_launch<Dense>(a, st);
+    return region_launch<Dense>(a, s.B, st);
   }
   return hipErrorNotSupported;
 }

@@ -671,6 +671,203 @@ __global__ __launch_bounds__(kSmallWaves * 64) void route_small_kernel(RouteArgs
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pool and route in one launch, for R <= 64 regions: one 16-wavefront
+// workgroup per (image, 16-row strip) pools the float64 means of all the
+// image's K regions and of its strip's Q regions into LDS, then forms the
+// strip's affinities and ranks them as route_small_kernel does.  Each strip
+// pools the image's K itself (the image's strips share one XCD, so the
+// repeated reads come from its L2): no second launch, no wait between
+// workgroups, and the means reach the affinity without a round trip through
+// memory.  They are still written to the workspace (K by the first strip,
+// Q by every strip for its rows), which callers may read.
+//
+// Pooling: wavefront w takes items w, w + 16, ... (K regions 0..R-1, then
+// the strip's Q regions); lane (p, g) = (lane / G, lane % G) owns 16-byte
+// channel group g of pixels p, p + 64/G, ...; IB items' loads are in flight
+// at once in a ring of registers, refilled as each item is added; the
+// float64 partial sums of the 64/G lanes sharing g are combined by the
+// reduce-scatter of pool_pipe_kernel, in a fixed order.
+// ---------------------------------------------------------------------------
+struct PoolRouteArgs {
+  const uint4* q;
+  const uint4* k;
+  double* qm;
+  double* km;
+  int32_t* idx;
+  float* logits;
+  Shape s;
+  double scale;
+  int nrb;          // 16-row strips per image
+  int ldm;          // LDS row stride of the means (doubles)
+  FastDiv f_ws, f_S;
+};
+
+template <bool BF16, int G, int NP, int IB>
+__global__ __launch_bounds__(kSmallWaves * 64) void pool_route_kernel(PoolRouteArgs A) {
+  constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int PP = 64 / G;                 // pixels per pass = lanes sharing g
+  constexpr int KEEP = VEC / PP;             // values per lane after the scatter
+  static_assert(G >= 1 && G <= 64 && KEEP >= 1, "pixel lanes in bits log2(G)..5");
+  extern __shared__ double pr_lds[];
+  const Shape& s = A.s;
+  const int R = s.R, C = s.C, topk = s.topk;
+  // workgroup -> (image, strip): the strips of an image sit on its XCD
+  const int xcd = blockIdx.x % kXcds, rest = blockIdx.x / kXcds;
+  const int t1 = rest / A.nrb, strip = rest - t1 * A.nrb;
+  const int b = t1 * kXcds + xcd;
+  if (b >= s.B) return;                      // uniform; before any barrier
+  const int r0 = strip * kRouteRows;
+  const int rows = min(kRouteRows, R - r0);
+  // the wavefront index as a scalar: items, and so the buffer descriptor
+  // each load takes, are uniform over the wavefront
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, lk = lane >> 4;
+  double* means = pr_lds;                    // [R + 16][ldm]: K regions, then the strip's Q
+
+  // ---- pool ----
+  {
+    const int g = lane % G, p = lane / G;
+    const uint32_t img_bytes = (uint32_t)s.H * s.W * G * 16;
+    const size_t img = (size_t)b * s.H * s.W * G;
+    const auto Qr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(A.q + img), (short)0,
+                                                      (int)img_bytes, 0x00020000);
+    const auto Kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(A.k + img), (short)0,
+                                                      (int)img_bytes, 0x00020000);
+    uint32_t toff[NP];
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int t = p + u * PP;
+      const int ty = fdiv(t, A.f_ws), tx = t - ty * s.ws;
+      toff[u] = t < s.n ? (uint32_t)(((ty * s.W + tx) * G + g) * 16) : 0x80000000u;
+    }
+    const int U = R + rows;
+    const int nj = wave < U ? (U - wave + kSmallWaves - 1) / kSmallWaves : 0;
+    uint4 buf[IB][NP];
+    auto issue = [&](int slot, int item) {
+      const int reg = item < R ? item : r0 + item - R;
+      const int ry = fdiv(reg, A.f_S), rx = reg - ry * s.S;
+      const uint32_t base = (uint32_t)(((ry * s.hs) * s.W + rx * s.ws) * G * 16);
+      const auto rs = item < R ? Kr : Qr;       // uniform over the wavefront
+#pragma unroll
+      for (int u = 0; u < NP; ++u) {
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, base + toff[u], 0, 0);
+        buf[slot][u] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+    };
+#pragma unroll
+    for (int sl = 0; sl < IB; ++sl)
+      if (sl < nj) issue(sl, wave + kSmallWaves * sl);
+    const double inv_n = 1.0 / (double)s.n;
+    for (int j0 = 0; j0 < nj; j0 += IB) {
+#pragma unroll
+      for (int sl = 0; sl < IB; ++sl) {
+        const int j = j0 + sl;
+        if (j >= nj) break;                      // uniform
+        const int item = wave + kSmallWaves * j;
+        double v[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[e] = 0.0;
+#pragma unroll
+        for (int u = 0; u < NP; ++u) {
+          float f[VEC];
+          unpack16<BF16>(buf[sl][u], f);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) v[e] += (double)f[e];
+        }
+        if (j + IB < nj) issue(sl, item + kSmallWaves * IB);
+        if constexpr (PP >= 2) scatter_step<5, VEC>(v);
+        if constexpr (PP >= 4) scatter_step<4, VEC / 2>(v);
+        if constexpr (PP >= 8) scatter_step<3, VEC / 4>(v);
+        // lane p holds values p*KEEP .. p*KEEP + KEEP - 1 of group g
+        const int row = item;                    // K regions first, then the strip's Q rows
+        double* gdst = item < R ? (strip == 0 ? A.km + ((size_t)b * R + item) * C : nullptr)
+                                : A.qm + ((size_t)b * R + r0 + item - R) * C;
+#pragma unroll
+        for (int jj = 0; jj < KEEP; ++jj) {
+          const int c = g * VEC + p * KEEP + jj;
+          const double m = v[jj] * inv_n;
+          means[row * A.ldm + c] = m;
+          if (gdst) gdst[c] = m;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- affinity strip: wavefront w, column tile w % 4 over channel quarter w / 4 ----
+  const int tile = wave & 3, quarter = wave >> 2;
+  const int ntile = (R + 15) / 16;
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  if (tile < ntile) {
+    const double* qp = means + (R + min(l16, rows - 1)) * A.ldm + 4 * lk;
+    const double* kp = means + min(16 * tile + l16, R - 1) * A.ldm + 4 * lk;
+    for (int c0 = 16 * quarter; c0 < C; c0 += 64) {
+      const bool ok = c0 + 4 * lk < C;
+      const double4 a4 = ok ? *(const double4*)(qp + c0) : make_double4(0.0, 0.0, 0.0, 0.0);
+      const double4 b4 = ok ? *(const double4*)(kp + c0) : make_double4(0.0, 0.0, 0.0, 0.0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4.x, b4.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4.y, b4.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4.z, b4.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a4.w, b4.w, acc, 0, 0, 0);
+    }
+  }
+  __syncthreads();                           // the means are read; their space is reused
+  double (*part)[kRouteRows][64] = (double (*)[kRouteRows][64])pr_lds;
+  long long (*keys)[64] = (long long (*)[64])(pr_lds + 4 * kRouteRows * 64);
+  if (tile < ntile) {
+    // D layout (f64 16x16x4): lane holds column l16 of the tile, rows lk + 4*i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[quarter][lk + 4 * i][16 * tile + l16] = acc[i];
+  }
+  __syncthreads();
+
+  // ---- ranking of strip row w (as route_small_kernel) ----
+  const int rl = wave;
+  if (rl >= rows) return;                    // no barrier follows
+  const double v =
+      ((part[0][rl][lane] + part[1][rl][lane]) + (part[2][rl][lane] + part[3][rl][lane])) * A.scale;
+  const long long key = lane < R ? order_key(v) : LLONG_MIN;
+  const size_t orow = ((size_t)b * R + r0 + rl) * topk;
+  if (topk <= kSelectMaxK) {
+    bool taken = lane >= R;
+    for (int kk = 0; kk < topk; ++kk) {
+      long long bk = taken ? LLONG_MIN : key;
+      int bi = taken ? 0x7fffffff : lane;
+      wave_best(bk, bi);
+      if (lane == bi) {
+        taken = true;
+        A.idx[orow + kk] = lane;
+        if (A.logits) A.logits[orow + kk] = (float)v;
+      }
+    }
+    return;
+  }
+  keys[rl][lane] = key;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // the row's keys are visible
+  int rank = 0;
+#pragma unroll 8
+  for (int s2 = 0; s2 < R; ++s2) rank += ranks_before(keys[rl][s2], s2, key, lane) ? 1 : 0;
+  if (lane < R && rank < topk) {
+    A.idx[orow + rank] = lane;
+    if (A.logits) A.logits[orow + rank] = (float)v;
+  }
+}
+
+template <bool BF16, int G, int NP>
+hipError_t pool_route_launch(const PoolRouteArgs& a, size_t lds, hipStream_t st) {
+  constexpr int IB = NP >= 8 ? 1 : 8 / NP;   // ring of IB items: 32 VGPRs of loads
+  const void* fn = reinterpret_cast<const void*>(&pool_route_kernel<BF16, G, NP, IB>);
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((a.s.B + kXcds - 1) / kXcds * kXcds * a.nrb));
+  hipLaunchKernelGGL((pool_route_kernel<BF16, G, NP, IB>), grid, dim3(kSmallWaves * 64), lds, st,
+                     a);
+  return hipGetLastError();
+}
+
 // Launches pool_pipe_kernel for shapes it covers (one value or more per lane
 // after the scatter); the launcher never selects the others.
 template <bool BF16, int G, int NP, bool TWO>
@@ -786,6 +983,53 @@ hipError_t launch_route(const double* qm, const double* km, const Shape& s, doub
   else
     hipLaunchKernelGGL((route_kernel<64, 16>), grid, block, lds, st, a);
   return hipGetLastError();
+}
+
+hipError_t launch_pool_route(const void* q, const void* k, double* qm, double* km, const Shape& s,
+                             bool bf16, double route_scale, int32_t* idx, float* logits,
+                             hipStream_t st) {
+  const int vec = bf16 ? 8 : 4;
+  if (s.R > 64 || s.C % vec) return hipErrorNotSupported;
+  const int G = s.C / vec;
+  if (G != 8 && G != 16 && G != 32 && G != 64) return hipErrorNotSupported;
+  const int PP = 64 / G;
+  if (vec < PP) return hipErrorNotSupported;                 // a value a lane after the scatter
+  const int passes = (s.n + PP - 1) / PP;
+  if (passes > 8) return hipErrorNotSupported;
+  if ((long long)s.H * s.W * G * 16 >= 0x80000000LL) return hipErrorNotSupported;
+  int dev = 0, lds_max = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return e;
+  PoolRouteArgs a;
+  a.q = (const uint4*)q; a.k = (const uint4*)k; a.qm = qm; a.km = km;
+  a.idx = idx; a.logits = logits; a.s = s; a.scale = route_scale;
+  a.nrb = (s.R + kRouteRows - 1) / kRouteRows;
+  a.ldm = s.C + 2;              // 16 bytes of padding: the 16 rows' reads spread over the banks
+  a.f_ws = make_fastdiv(s.ws);
+  a.f_S = make_fastdiv(s.S);
+  size_t lds = (size_t)(s.R + kRouteRows) * a.ldm * sizeof(double);
+  const size_t rank_lds = (size_t)(4 * kRouteRows * 64 + kRouteRows * 64) * sizeof(double);
+  if (lds < rank_lds) lds = rank_lds;
+  if (lds > (size_t)lds_max) return hipErrorNotSupported;
+  const int np = passes > 4 ? 8 : passes > 2 ? 4 : passes > 1 ? 2 : 1;
+#define BRA_PR(BB, GG)                                                   \
+  if (G == GG) {                                                         \
+    switch (np) {                                                        \
+      case 1: return pool_route_launch<BB, GG, 1>(a, lds, st);           \
+      case 2: return pool_route_launch<BB, GG, 2>(a, lds, st);           \
+      case 4: return pool_route_launch<BB, GG, 4>(a, lds, st);           \
+      default: return pool_route_launch<BB, GG, 8>(a, lds, st);          \
+    }                                                                    \
+  }
+  if (bf16) {
+    BRA_PR(true, 8) BRA_PR(true, 16) BRA_PR(true, 32) BRA_PR(true, 64)
+  } else {
+    BRA_PR(false, 16) BRA_PR(false, 32) BRA_PR(false, 64)
+  }
+#undef BRA_PR
+  return hipErrorNotSupported;
 }
 
 }  // namespace bra
