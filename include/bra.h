@@ -103,6 +103,27 @@ bra_status bra_forward(const void* q, const void* k, const void* v, int B,
                        void* out, int32_t* idx, float* topk_logits, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): bra_forward without a
+ * workspace argument.  The float64 region means go to a device array inside
+ * the library (BRA_NOALLOC_SCRATCH_BYTES on each GPU it runs on, held until
+ * the process ends); the call allocates nothing.  Sizes whose means exceed
+ * that array, 2*B*S*S*C*8 bytes > BRA_NOALLOC_SCRATCH_BYTES, return
+ * BRA_E_UNSUPPORTED before anything is enqueued.  Every call on a GPU
+ * shares its array: calls that overlap on one GPU (different streams,
+ * different threads) race; calls on one stream are ordered.  Arguments,
+ * results and the other errors as bra_forward.
+ * ------------------------------------------------------------------------ */
+#define BRA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+bra_status bra_forward_noalloc(const void* q, const void* k, const void* v,
+                               int B, int H, int W, int C, int heads, int S,
+                               int topk, bra_dtype dtype, float route_scale,
+                               float attn_scale, const float* lepe_w,
+                               const float* lepe_b, int lepe_ks, void* out,
+                               int32_t* idx, float* topk_logits, void* stream);
+
 /* Step 6 alone, in place: out += bias + depthwise ks x ks cross-correlation
  * of v (p2 §4 depthwise Conv2d; p1 §3 adds it to the attention output).
  *   v, out [B,H,W,C] dtype, device, not overlapping; w float32 [C,ks,ks];

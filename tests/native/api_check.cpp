@@ -103,6 +103,20 @@ int main() {
                                       nullptr, ptr(PW), 1 << 20, nullptr),
          BRA_E_INVAL, "heads");
 
+  // bra_forward_noalloc: the means must fit the static scratch
+  expect("noalloc too big", bra_forward_noalloc(ptr(P), ptr(P2), ptr(P3), 1024, 64, 64, 256, 8, 8, 4,
+                                                BRA_BF16, 0.125f, 0.17f, nullptr, nullptr, 5,
+                                                ptr(PO), ip(P4), nullptr, nullptr),
+         BRA_E_UNSUPPORTED, "scratch");
+  expect("noalloc heads", bra_forward_noalloc(ptr(P), ptr(P2), ptr(P3), 2, 8, 8, 64, 3, 2, 2,
+                                              BRA_BF16, 0.125f, 0.17f, nullptr, nullptr, 5,
+                                              ptr(PO), ip(P4), nullptr, nullptr),
+         BRA_E_INVAL, "heads");
+  expect("noalloc out overlaps", bra_forward_noalloc(ptr(P), ptr(P2), ptr(P3), 2, 8, 8, 64, 2, 2,
+                                                     2, BRA_BF16, 0.125f, 0.17f, nullptr, nullptr,
+                                                     5, ptr(P + 1024), ip(P4), nullptr, nullptr),
+         BRA_E_INVAL, "overlaps");
+
   // bra_lepe
   expect("lepe C", bra_lepe(ptr(P), fp(P2), nullptr, 5, 2, 8, 8, 48, BRA_BF16, ptr(P3), nullptr),
          BRA_E_UNSUPPORTED, nullptr);

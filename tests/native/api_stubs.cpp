@@ -55,6 +55,7 @@ hipError_t launch_attend_region(const void*, const void*, const void*, const int
                                 hipStream_t) {
   reached("launch_attend_region");
 }
+hipError_t scratch_buffer(void**) { reached("scratch_buffer"); }
 hipError_t launch_lepe(const void*, const float*, const float*, int, const Shape&, bool, void*,
                        hipStream_t) {
   reached("launch_lepe");

@@ -16,7 +16,7 @@ import ctypes
 import os
 
 __all__ = ["BraError", "lib_path", "load", "workspace_bytes", "route", "attend",
-           "forward", "lepe", "linear", "module_workspace_bytes", "module_forward",
+           "forward", "forward_noalloc", "lepe", "linear", "module_workspace_bytes", "module_forward",
            "layer_norm", "pos_conv", "block_workspace_bytes", "block_forward", "BLOCK_PARAMS",
            "attend_backward", "video_workspace_bytes", "video_forward", "video_route",
            "video_attend", "STATUS"]
@@ -37,6 +37,8 @@ _SIGNATURES = {
                         _vp, _vp]),
     "bra_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _f, _vp, _vp, _i,
                          _vp, _vp, _vp, _vp, _sz, _vp]),
+    "bra_forward_noalloc": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _f, _vp, _vp,
+                                 _i, _vp, _vp, _vp, _vp]),
     "bra_lepe": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp]),
     "bra_linear": (_i, [_vp, _i, _i, _vp, _vp, _i, _i, _vp, _i, _vp, _vp]),
     "bra_pos_conv": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
@@ -256,6 +258,33 @@ def forward(q, k, v, heads: int, S: int, topk: int, lepe_w=None, lepe_b=None,
                               idx.data_ptr(), logits.data_ptr() if logits is not None else None,
                               wsp, wsb, _stream(q)))
     return (out, idx, logits) if return_logits else (out, idx)
+
+
+def forward_noalloc(q, k, v, heads: int, S: int, topk: int, out, idx, lepe_w=None, lepe_b=None,
+                    route_scale: float | None = None, attn_scale: float | None = None,
+                    logits=None):
+    """bra_forward_noalloc: the forward pass for callers that cannot allocate.
+    Nothing is allocated here or in the library: out ([B, H, W, C], q's
+    dtype) and idx (int32 [B, S*S, topk]) are the caller's, as is logits
+    (float32 [B, S*S, topk]) if given; the region means go to the library's
+    static device scratch.  Returns (out, idx)."""
+    import torch
+    B, H, W, C = _bhwc(q)
+    dt = _dtype_code(q)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, q.dtype, (B, H, W, C))
+    _dev(out, "out", q.dtype, (B, H, W, C))
+    _dev(idx, "idx", torch.int32, (B, S * S, topk))
+    lp = _dev(logits, "logits", torch.float32, (B, S * S, topk)) if logits is not None else None
+    if route_scale is None:
+        route_scale = C ** -0.5
+    if attn_scale is None:
+        attn_scale = (C // heads) ** -0.5
+    wp, bp, ks = _lepe_args(lepe_w, lepe_b, C)
+    _check(load().bra_forward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, W, C, heads,
+                                      S, topk, dt, float(route_scale), float(attn_scale), wp, bp,
+                                      ks, out.data_ptr(), idx.data_ptr(), lp, _stream(q)))
+    return out, idx
 
 
 def lepe(v, w, b, out):

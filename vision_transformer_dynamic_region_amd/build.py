@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libbra.so")
 SOURCES = ["route_kernels.hip", "attend_kernels.hip", "region_kernels.hip", "image_kernels.hip",
            "module_kernels.hip",
            "block_kernels.hip", "backward_kernels.hip",
-           "host_plan.cpp", "bra_api.cpp"]
+           "scratch.hip", "host_plan.cpp", "bra_api.cpp"]
 # per-file extra flags: the attention file assumes finite, non-NaN data (NaN
 # inputs give unspecified outputs) so that max/min need no NaN quieting, and
 # keeps MFMA accumulators in ordinary VGPRs next to the softmax arithmetic

@@ -345,6 +345,35 @@ bra_status bra_forward(const void* q, const void* k, const void* v, int B, int H
                           idx, topk_logits, ws, stream);
 }
 
+bra_status bra_forward_noalloc(const void* q, const void* k, const void* v, int B, int H, int W,
+                               int C, int heads, int S, int topk, bra_dtype dtype,
+                               float route_scale, float attn_scale, const float* lepe_w,
+                               const float* lepe_b, int lepe_ks, void* out, int32_t* idx,
+                               float* topk_logits, void* stream) {
+  g_last_error[0] = 0;
+  bra::Shape s;
+  bra_status st;
+  if (heads < 1) return fail(BRA_E_INVAL, "heads=%d must be positive", heads);
+  if ((st = check_shape(B, H, W, C, S, heads, topk, dtype, &s))) return st;
+  const size_t need = bra_workspace_bytes(B, S, C);
+  if (need > bra::kScratchBytes)
+    return fail(BRA_E_UNSUPPORTED,
+                "needs %zu bytes of scratch (2*B*S*S*C*8); the static scratch holds %zu", need,
+                bra::kScratchBytes);
+  // the workspace checks below see the static scratch's size; its address
+  // is looked up only once the arguments are valid
+  const void* probe = reinterpret_cast<const void*>((uintptr_t)256);
+  if ((st = check_route_args(q, k, s, dtype, route_scale, idx, topk_logits, probe,
+                             bra::kScratchBytes)))
+    return st;
+  if ((st = check_attend_args(q, k, v, idx, s, dtype, attn_scale, lepe_w, lepe_b, lepe_ks, out)))
+    return st;
+  void* ws = nullptr;
+  if ((st = hip_status(bra::scratch_buffer(&ws), "scratch lookup"))) return st;
+  return forward_launches(q, k, v, s, dtype, route_scale, attn_scale, lepe_w, lepe_b, lepe_ks, out,
+                          idx, topk_logits, ws, stream);
+}
+
 bra_status bra_video_route(const void* q, const void* k, int B, int T, int H, int W, int C, int S,
                            int topk, bra_dtype dtype, float route_scale, int32_t* idx,
                            float* topk_logits, void* ws, size_t ws_bytes, void* stream) {

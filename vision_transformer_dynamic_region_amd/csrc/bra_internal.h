@@ -8,6 +8,13 @@
 
 namespace bra {
 
+// Bytes of the device scratch array of the allocation-free entry points.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+
+// Device address of this device's scratch array (kScratchBytes, 256-byte
+// aligned), looked up once per device.
+hipError_t scratch_buffer(void** out);
+
 // Problem shape after validation.  All sizes are positive, S divides H and
 // W, heads * 32 == C.
 struct Shape {
