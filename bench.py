@@ -34,12 +34,16 @@ MALL_BYTES = 256 << 20         # Infinity Cache
 # sources of the attention kernels (the traffic record is void once they change)
 KERNEL_SOURCES = [
     "vision_transformer_dynamic_region_amd/csrc/region_kernels.hip",
+    "vision_transformer_dynamic_region_amd/csrc/image_kernels.hip",
     "vision_transformer_dynamic_region_amd/csrc/attend_kernels.hip",
     "vision_transformer_dynamic_region_amd/csrc/device_common.h",
     "vision_transformer_dynamic_region_amd/csrc/fastdiv.h",
 ]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
-ATTEND_KERNELS = ("attend_region_kernel", "attend_stream_kernel", "attend_kernel")
+ATTEND_KERNELS = ("attend_region_kernel", "attend_image_kernel", "attend_stream_kernel",
+                  "attend_kernel")
+# measured beside the headline workload on the default line
+OTHER_WORKLOADS = ("dense", "st2", "st3")
 
 
 def log(msg: str) -> None:
@@ -70,6 +74,8 @@ def parse():
     p.add_argument("--sets", type=int, default=0,
                    help="input copies rotated across steps (0: enough to exceed the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="with the default workload, skip the other shapes measured beside it")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--copy-probe-mb", type=int, default=0,
@@ -130,12 +136,16 @@ def write_traffic(a) -> int:
 
 def attend_kernel_name(wl) -> str:
     """The attention kernel the library launches for this workload: the
-    specialised kernel for the bf16 BiFormer stage and dense shapes, else the
+    whole-image kernel for bf16 4x4 / top-4 and 2x2 / top-16 regions, the
+    per-region kernel for the bf16 stage-1 and dense shapes, else the
     pipelined general kernel or, when its routed keys or LePE halo do not fit
     that one, the chunked general kernel."""
-    special = {("bf16", 64, 8, 1), ("bf16", 128, 4, 4), ("bf16", 256, 2, 16), ("bf16", 64, 8, 4)}
+    image = {("bf16", 4, 4), ("bf16", 2, 16)}
+    region = {("bf16", 64, 8, 1), ("bf16", 64, 8, 4)}
+    if wl.lepe_ks == 5 and (wl.dtype, wl.H // wl.S, wl.topk) in image and wl.C % 32 == 0:
+        return "attend_image_kernel"
     key = (wl.dtype, wl.C, wl.H // wl.S, wl.topk)
-    return "attend_region_kernel" if key in special and wl.lepe_ks == 5 \
+    return "attend_region_kernel" if key in region and wl.lepe_ks == 5 \
         else "attend_stream_kernel|attend_kernel"
 
 
@@ -150,35 +160,58 @@ def copy_probe(mb: int) -> None:
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}))
 
 
-def cpu_baseline(wl, x, target_s: float):
-    """Time the fp64 oracle on the first images of the same batch."""
-    import numpy as np
+_ORACLE_X = {}
+
+
+def _oracle_init(name: str) -> None:
+    """Oracle baseline process start-up: the same seeded inputs the GPU got
+    (the generator is deterministic), BLAS limited to one thread."""
+    from threadpoolctl import threadpool_limits
+
+    from vision_transformer_dynamic_region_amd.workloads import WORKLOADS, make_inputs
+    threadpool_limits(1)
+    wl = WORKLOADS[name]
+    _ORACLE_X["wl"], _ORACLE_X["x"] = wl, make_inputs(wl)
+
+
+def _oracle_images(b: int) -> float:
+    """The fp64 oracle on image b of the batch; returns its seconds."""
     import oracle
+    wl, x = _ORACLE_X["wl"], _ORACLE_X["x"]
+    t0 = time.perf_counter()
+    oracle.bra_forward(x["q"][b:b + 1], x["k"][b:b + 1], x["v"][b:b + 1], wl.heads, wl.S, wl.topk,
+                       x["w"])
+    return time.perf_counter() - t0
 
-    def run(nb):
-        ru0 = resource.getrusage(resource.RUSAGE_SELF)
+
+def cpu_baseline(wl, target_s: float):
+    """Time the fp64 oracle as it stands on the host's cores: one process per
+    usable core (spawned, each single-threaded, each with its own copy of the
+    seeded batch), taking whole images, to about target_s seconds of wall
+    time."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    cores = max(1, len(os.sched_getaffinity(0)))
+    ctx = mp.get_context("spawn")
+    with cf.ProcessPoolExecutor(max_workers=cores, mp_context=ctx, initializer=_oracle_init,
+                                initargs=(wl.name,)) as pool:
+        # start-up (interpreter, imports, inputs) outside the timed part
+        t_one = max(pool.map(_oracle_images, [b % wl.B for b in range(cores)]))
+        n = max(cores, int(target_s * cores / max(t_one, 1e-3)))
+        images = [b % wl.B for b in range(n)]
         t0 = time.perf_counter()
-        oracle.bra_forward(x["q"][:nb], x["k"][:nb], x["v"][:nb], wl.heads, wl.S, wl.topk, x["w"])
+        busy = sum(pool.map(_oracle_images, images, chunksize=max(1, n // (4 * cores))))
         dt = time.perf_counter() - t0
-        ru1 = resource.getrusage(resource.RUSAGE_SELF)
-        cpu = (ru1.ru_utime - ru0.ru_utime) + (ru1.ru_stime - ru0.ru_stime)
-        return dt, cpu
-
-    t1, _ = run(1)
-    nb = int(max(1, min(wl.B, target_s / max(t1, 1e-3))))
-    dt, cpu, reps = 0.0, 0.0, 0
-    while reps == 0 or (nb == wl.B and dt < target_s and reps < 20):
-        d, c = run(nb)       # the whole batch is cheap: repeat it up to the target time
-        dt, cpu, reps = dt + d, cpu + c, reps + 1
-    tokens = nb * wl.H * wl.W * reps
+    tokens = len(images) * wl.H * wl.W
     return {
         "value": tokens / dt,
         "unit": "tokens/s",
-        "cores": max(1, int(round(cpu / dt))),
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"{wl.name}: first {nb} of {wl.B} images x {reps} passes ({tokens} tokens), "
-                   f"full fp64 oracle in {dt:.1f} s; host has {len(os.sched_getaffinity(0))} "
-                   f"usable cores"),
+        "sample": (f"{wl.name}: {len(images)} images of the batch (cycling through its {wl.B}), "
+                   f"{tokens} tokens, full fp64 oracle in {dt:.1f} s wall on {cores} "
+                   f"single-threaded processes ({busy / max(dt * cores, 1e-9):.0%} busy)"),
     }
 
 
@@ -595,11 +628,10 @@ def main() -> int:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the BRA forward "
               "pass here is a single-GPU kernel path", file=sys.stderr)
         return 2
-    import numpy as np
     import torch
 
     import vision_transformer_dynamic_region_amd as bra
-    from vision_transformer_dynamic_region_amd.workloads import WORKLOADS, bf16_bits, make_inputs
+    from vision_transformer_dynamic_region_amd.workloads import WORKLOADS
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -621,6 +653,28 @@ def main() -> int:
         return run_block(a, wl)
     if a.path == "backward":
         return run_backward(a, wl)
+    res = measure_bra(a, wl, bra, headline=True)
+    if a.workload == "st1" and not a.no_extra:
+        # the other bf16 shapes on the same line (the headline stays st1)
+        res["other_workloads"] = {n: measure_bra(a, WORKLOADS[n], bra, headline=False)
+                                  for n in OTHER_WORKLOADS}
+    if not a.no_cpu_baseline:
+        log("timing the fp64 oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def measure_bra(a, wl, bra, headline: bool) -> dict:
+    """The BRA forward pass of one workload: the whole pass over rotating
+    input sets (mean over exactly a.steps steps, and the median of per-step
+    times), the same steps on one input set left in the MALL (warm), and the
+    two stages alone (bra_route: pooling and routing; bra_attend: attention
+    with LePE), each between HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    from vision_transformer_dynamic_region_amd.workloads import bf16_bits, make_inputs
     dev = torch.device("cuda:0")
     log(f"workload {wl}")
     x = make_inputs(wl)
@@ -630,6 +684,7 @@ def main() -> int:
         up = lambda arr: torch.from_numpy(arr).to(dev)
     q0, k0, v0 = up(x["q"]), up(x["k"]), up(x["v"])
     w = torch.from_numpy(x["w"]).to(dev)
+    del x
     set_bytes = 4 * wl.tensor_bytes
     sets = a.sets or max(1, -(-3 * MALL_BYTES // set_bytes))
     wsb = bra.workspace_bytes(wl.B, wl.S, wl.C)
@@ -641,8 +696,8 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"{sets} input sets of {set_bytes / 1e6:.1f} MB rotated per step")
 
-    def step(i):
-        b = bufs[i % sets]
+    def step(i, rotate=True):
+        b = bufs[i % sets] if rotate else bufs[0]
         bra.forward(b["q"], b["k"], b["v"], wl.heads, wl.S, wl.topk, w, out=b["out"],
                     idx=b["idx"], workspace=b["ws"])
 
@@ -651,53 +706,80 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"warmup {a.warmup} steps done")
 
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    start, stop = ev(), ev()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
+    start.record(stream)
     for i in range(a.steps):
         step(i)
-    stop.record()
+    stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(stop) / a.steps
     log(f"timed {a.steps} steps: {ms:.4f} ms/step (wall {wall * 1e3 / a.steps:.4f} ms/step)")
 
-    # Per-stage durations: the same kernels launched through the two
-    # single-stage entry points, each stage as its own back-to-back loop over
-    # the rotating input sets (bra_route: pooling + routing; bra_attend:
-    # gather-attention with the LePE term fused), bracketed by HIP events on
-    # the stream the kernels run on (torch's current stream, which the binding
-    # passes to the library).
-    stream = torch.cuda.current_stream()
+    # per-step times (an event pair around each step) for the median
+    pairs = [(ev(), ev()) for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(pairs):
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms_median = float(np.median([e0.elapsed_time(e1) for e0, e1 in pairs]))
 
-    def stage_ms(fn):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def loop_ms(fn):
+        e0, e1 = ev(), ev()
         torch.cuda.synchronize()
         e0.record(stream)
         for i in range(a.steps):
-            fn(bufs[i % sets])
+            fn(i)
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / a.steps
 
-    t_route = stage_ms(lambda b: bra.route(b["q"], b["k"], wl.S, wl.topk, workspace=b["ws"]))
-    t_attn = stage_ms(lambda b: bra.attend(b["q"], b["k"], b["v"], b["idx"], wl.heads, wl.S,
-                                           lepe_w=w, out=b["out"]))
-    log(f"per stage (ms): pool+route {t_route:.4f}  attend+lepe {t_attn:.4f}")
+    # warm: every step on the same input set, which then stays in the MALL
+    ms_warm = loop_ms(lambda i: step(i, rotate=False))
+    # per stage, each as its own back-to-back loop over the rotating sets
+    t_route = loop_ms(lambda i: bra.route(bufs[i % sets]["q"], bufs[i % sets]["k"], wl.S, wl.topk,
+                                          workspace=bufs[i % sets]["ws"]))
+    t_attn = loop_ms(lambda i: bra.attend(bufs[i % sets]["q"], bufs[i % sets]["k"],
+                                          bufs[i % sets]["v"], bufs[i % sets]["idx"], wl.heads,
+                                          wl.S, lepe_w=w, out=bufs[i % sets]["out"]))
+    t_attn_warm = loop_ms(lambda i: bra.attend(bufs[0]["q"], bufs[0]["k"], bufs[0]["v"],
+                                               bufs[0]["idx"], wl.heads, wl.S, lepe_w=w,
+                                               out=bufs[0]["out"]))
+    log(f"per stage (ms): pool+route {t_route:.4f}  attend+lepe {t_attn:.4f} "
+        f"(warm {t_attn_warm:.4f}); step median {ms_median:.4f}, warm {ms_warm:.4f}")
+    del bufs
+    torch.cuda.empty_cache()
 
     tokens = wl.tokens
     attn_bytes = 4 * wl.tensor_bytes           # Q, K, V read once + out written once
     attn_gbs = attn_bytes / (t_attn * 1e-3) / 1e9
     attn_tflops = wl.attn_flops / (t_attn * 1e-3) / 1e12
+    route_bytes = 2 * wl.tensor_bytes          # Q and K read once
+    config = {"workload": f"{wl.name}: B={wl.B} H=W={wl.H} C={wl.C} heads={wl.heads} "
+                          f"d={wl.d} S={wl.S} topk={wl.topk} LePE {wl.lepe_ks}x{wl.lepe_ks}",
+              "tokens_per_step": tokens, "input_sets_rotated": sets}
+    attention = {"kernel": attend_kernel_name(wl), "ms": t_attn, "ms_warm": t_attn_warm,
+                 "tflops": attn_tflops, "frac_bf16_peak": attn_tflops / BF16_PEAK_TFLOPS,
+                 "gbs": attn_gbs, "frac_hbm": attn_gbs / HBM_PEAK_GBS}
+    stages = {"pool_route": t_route, "attend_lepe": t_attn,
+              "pool_route_frac_hbm": route_bytes / (t_route * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if not headline:
+        return {"config": config, "ms_per_step": ms, "ms_per_step_median": ms_median,
+                "ms_per_step_warm": ms_warm, "tokens_per_s": tokens / (ms * 1e-3),
+                "attention": attention, "stages_ms": stages}
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE))
         if rec.get("kernel_sha") == kernel_sha() and rec.get("workload") == wl.name:
             traffic = rec.get("bytes_per_launch")
-
-    res = {
+    return {
         "metric": METRIC,
         "value": tokens / (ms * 1e-3),
         "unit": "tokens/s",
@@ -705,27 +787,21 @@ def main() -> int:
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": ms_median,
+        "ms_per_step_warm": ms_warm,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: B={wl.B} H=W={wl.H} C={wl.C} heads={wl.heads} "
-                               f"d={wl.d} S={wl.S} topk={wl.topk} LePE {wl.lepe_ks}x{wl.lepe_ks}",
-                   "tokens_per_step": tokens, "input_sets_rotated": sets},
-        "attention": {"tflops": attn_tflops, "frac_bf16_peak": attn_tflops / BF16_PEAK_TFLOPS,
-                      "ms": t_attn},
-        "stages_ms": {"pool_route": t_route, "attend_lepe": t_attn},
+        "config": config,
+        "attention": attention,
+        "stages_ms": stages,
         "roofline": {"kernel": attend_kernel_name(wl), "bound": "hbm", "achieved": attn_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": attn_gbs / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes": attn_bytes},
         "kernel_sha": kernel_sha(),
     }
-    if not a.no_cpu_baseline:
-        log("timing the fp64 oracle on the host")
-        res["cpu_baseline"] = cpu_baseline(wl, x, a.cpu_seconds)
-    print(json.dumps(res), flush=True)
-    return 0
 
 
 if __name__ == "__main__":
