@@ -95,7 +95,9 @@ bra_status bra_attend(const void* q, const void* k, const void* v,
                       void* stream);
 
 /* The whole forward pass, steps 1-6 (p1 §3): bra_route then bra_attend on
- * the same stream.  Arguments as above. */
+ * the same stream.  Arguments as above, except that ws is scratch: its
+ * contents afterwards are unspecified (where routing runs as one launch the
+ * region means never leave the chip). */
 bra_status bra_forward(const void* q, const void* k, const void* v, int B,
                        int H, int W, int C, int heads, int S, int topk,
                        bra_dtype dtype, float route_scale, float attn_scale,
@@ -106,7 +108,8 @@ bra_status bra_forward(const void* q, const void* k, const void* v, int B,
 /* ------------------------------------------------------------------------
  * For callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): bra_forward without a
- * workspace argument.  The float64 region means go to a device array inside
+ * workspace argument.  The workspace bra_forward would take (the float64
+ * region means, where they pass through memory) is a device array inside
  * the library (BRA_NOALLOC_SCRATCH_BYTES on each GPU it runs on, held until
  * the process ends); the call allocates nothing.  Sizes whose means exceed
  * that array, 2*B*S*S*C*8 bytes > BRA_NOALLOC_SCRATCH_BYTES, return

@@ -37,12 +37,16 @@ def test_forward_parity(cuda, name):
     ws = torch.empty(bra.workspace_bytes(wl.B, wl.S, wl.C), dtype=torch.uint8, device=cuda)
     out, idx, logits = bra.forward(q, k, v, wl.heads, wl.S, wl.topk, w, workspace=ws,
                                    return_logits=True)
+    # the forward pass's workspace is scratch; bra_route's holds the float64
+    # means of Q then K, and its index is the forward pass's
+    ws2 = torch.empty_like(ws)
+    idx_r = bra.route(q, k, wl.S, wl.topk, workspace=ws2)
     torch.cuda.synchronize()
-    # region means (workspace holds float64 q means then k means)
-    means = ws.view(torch.float64).cpu().numpy().reshape(2, wl.B, wl.S * wl.S, wl.C)
+    means = ws2.view(torch.float64).cpu().numpy().reshape(2, wl.B, wl.S * wl.S, wl.C)
     scale = max(1.0, float(np.abs(ref["q_r"]).max()))
     assert np.max(np.abs(means[0] - ref["q_r"])) <= 1e-12 * scale
     assert np.max(np.abs(means[1] - ref["k_r"])) <= 1e-12 * scale
+    assert torch.equal(idx_r, idx)
     # routing index: exact modulo near-ties
     idx_g = idx.cpu().numpy()
     ties = check_idx(idx_g, ref["idx"], ref["A"])

@@ -232,7 +232,8 @@ def forward(q, k, v, heads: int, S: int, topk: int, lepe_w=None, lepe_b=None,
             route_scale: float | None = None, attn_scale: float | None = None, out=None,
             idx=None, workspace=None, return_logits: bool = False):
     """The whole BRA forward pass (bra_forward).  Returns (out, idx) or
-    (out, idx, logits) with return_logits."""
+    (out, idx, logits) with return_logits.  workspace, if given, is scratch
+    (its contents afterwards are unspecified)."""
     import torch
     B, H, W, C = _bhwc(q)
     dt = _dtype_code(q)

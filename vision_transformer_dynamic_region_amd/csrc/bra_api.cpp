@@ -232,13 +232,15 @@ BlockLayout block_layout(int B, int H, int W, int C, int S, bra_dtype dt) {
 }
 
 // region means and routing: one fused launch where it applies (up to 64
-// regions), else pooling then routing
+// regions), else pooling then routing.  keep_means: the means must be in
+// qm, km afterwards (the fused launch otherwise keeps them on chip)
 bra_status route_launches(const void* q, const void* k, const bra::Shape& s, bool bf16,
                           float route_scale, int32_t* idx, float* topk_logits, double* qm,
-                          double* km, hipStream_t hs) {
+                          double* km, bool keep_means, hipStream_t hs) {
   bra_status st;
-  const hipError_t e = bra::launch_pool_route(q, k, qm, km, s, bf16, (double)route_scale, idx,
-                                              topk_logits, hs);
+  const hipError_t e = bra::launch_pool_route(q, k, keep_means ? qm : nullptr,
+                                              keep_means ? km : nullptr, s, bf16,
+                                              (double)route_scale, idx, topk_logits, hs);
   if (e != hipErrorNotSupported) return hip_status(e, "pool-route launch");
   if ((st = hip_status(bra::launch_pool(q, k, qm, km, s, bf16, hs), "pool launch"))) return st;
   return hip_status(bra::launch_route(qm, km, s, (double)route_scale, idx, topk_logits, hs),
@@ -255,7 +257,8 @@ bra_status forward_launches(const void* q, const void* k, const void* v, const b
   const bool bf16 = dtype == BRA_BF16;
   double* qm = (double*)ws;
   double* km = qm + (size_t)s.B * s.R * s.C;
-  if ((st = route_launches(q, k, s, bf16, route_scale, idx, topk_logits, qm, km, hs))) return st;
+  if ((st = route_launches(q, k, s, bf16, route_scale, idx, topk_logits, qm, km, false, hs)))
+    return st;
   return hip_status(bra::launch_attend(q, k, v, idx, s, bf16, attn_scale, lepe_w, lepe_b, lepe_ks,
                                        out, hs),
                     "attend launch");
@@ -307,7 +310,8 @@ bra_status bra_route(const void* q, const void* k, int B, int H, int W, int C, i
   hipStream_t hs = (hipStream_t)stream;
   double* qm = (double*)ws;
   double* km = qm + (size_t)B * s.R * C;
-  return route_launches(q, k, s, dtype == BRA_BF16, route_scale, idx, topk_logits, qm, km, hs);
+  return route_launches(q, k, s, dtype == BRA_BF16, route_scale, idx, topk_logits, qm, km, true,
+                        hs);
 }
 
 bra_status bra_attend(const void* q, const void* k, const void* v, const int32_t* idx, int B,
@@ -385,7 +389,8 @@ bra_status bra_video_route(const void* q, const void* k, int B, int T, int H, in
   hipStream_t hs = (hipStream_t)stream;
   double* qm = (double*)ws;
   double* km = qm + (size_t)B * s.R * C;
-  return route_launches(q, k, s, dtype == BRA_BF16, route_scale, idx, topk_logits, qm, km, hs);
+  return route_launches(q, k, s, dtype == BRA_BF16, route_scale, idx, topk_logits, qm, km, true,
+                        hs);
 }
 
 bra_status bra_video_attend(const void* q, const void* k, const void* v, const int32_t* idx, int B,

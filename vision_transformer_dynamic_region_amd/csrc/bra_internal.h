@@ -66,10 +66,10 @@ hipError_t launch_means_proj(const double* xm, int rows, int C, const void* w_qk
                              const float* b_qkv, bool bf16, double* qm, double* km,
                              hipStream_t st);
 
-// Region means of q and k (float64, written to qm and km as launch_pool
-// does) and the scaled affinity's per-row top-k in one launch, for up to 64
-// regions per image; hipErrorNotSupported for other shapes, before anything
-// is enqueued.
+// Region means of q and k (float64; written to qm and km as launch_pool
+// does unless qm is null) and the scaled affinity's per-row top-k in one
+// launch, for up to 64 regions per image; hipErrorNotSupported for other
+// shapes, before anything is enqueued.
 hipError_t launch_pool_route(const void* q, const void* k, double* qm, double* km,
                              const Shape& s, bool bf16, double route_scale, int32_t* idx,
                              float* logits, hipStream_t st);

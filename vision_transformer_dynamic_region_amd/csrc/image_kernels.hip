@@ -227,7 +227,8 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
   uint4 qn = bload16(Qr, task < ntask ? q_off(task) : kOob);
   for (; task < ntask; task += NW) {
     const bf16x8 qop = __builtin_bit_cast(bf16x8, qn);
-    if (task + NW < ntask) qn = bload16(Qr, q_off(task + NW));
+    // the next task's Q, always issued (past the range it reads zeros)
+    qn = bload16(Qr, task + NW < ntask ? q_off(task + NW) : kOob);
     const int rl = task / NQB, qb = task - rl * NQB;
     const int r = r0 + rl;
     const int ry = fdiv(r, A.f_S), rx = r - ry * S;
@@ -378,6 +379,433 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 2x2-pixel regions.  A 16-query MFMA column block holds four whole query
+// regions, and the block is evaluated against every key of the image with
+// the routing applied as a per-(query region, key region) multiplicity
+// (0 for regions not routed to; a region listed twice counts twice, as its
+// keys would in a gather).  With four queries a region the per-region form
+// pads each 16-column block to four times its queries, so for 49 regions
+// routed to 16 this costs fewer matrix operations and softmax values than
+// the gather (208 x 224 logits an image and head against 49 x 16 x 64) and
+// reads K and V rows in order.  Per block, on one wavefront:
+//   pass 1     S^T = K Q^T over the key blocks, the maximum of the routed
+//              logits;
+//   pass 2     S^T again, p = count * 2^(s c - m c) rounded to bf16, and per
+//              32 keys O^T += V^T P^T and the row sums += ones P^T;
+//   LePE       the block's 16 pixels from the padded V image: tap pairs along
+//              x on v_dot2_f32_bf16 (weights rounded to bf16, products exact,
+//              float32 sums);
+//   epilogue   out = O / l + L, one rounding, 16-byte stores.
+// ---------------------------------------------------------------------------
+template <int TOPK_, int NW_, int NKB2_>
+struct Im {
+  // TOPK routed regions, NW wavefronts a workgroup, NKB2 steps of 32 keys
+  // (the image's keys padded to a multiple of 32)
+  static constexpr int HS = 2, WS = 2, n = 4, TOPK = TOPK_, KS = 5, NW = NW_, NKB2 = NKB2_;
+  static constexpr int NKB = 2 * NKB2;                // 16-key blocks
+  static constexpr int NT = NW * 64, P = KS / 2, KK = KS * KS, LSW = kHd + 4;
+  static constexpr int NBS = (128 * NKB2 + NT - 1) / NT;   // K (and V) chunks a thread stages
+  static constexpr int NES = (64 * TOPK + NT - 1) / NT;    // routing entries a thread (R <= 64)
+  static_assert(KS == 5 && NT >= KS * 3 * kHd, "LePE weights: one tap-pair entry a thread");
+};
+
+struct MaskArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* idx;
+  uint16_t* out;
+  const float* w;       // [C, KS, KS]
+  const float* bias;    // [C] or null
+  int B, H, W, C, S, R, heads;
+  int nqb;              // 16-query blocks per image (4 regions each)
+  int nkb;              // 16-key blocks per image (keys padded to 32 in LDS; unused)
+  int qsplit;           // workgroups per (image, head), each a range of query blocks
+  int qper;             // query blocks per workgroup
+  float scale_log2;     // attn_scale * log2(e)
+  int ks_off, vs_off, vi_off, ct_off, rt_off, ws_off, lw_off;   // LDS byte offsets
+  FastDiv f_S, f_W, f_qsplit, f_heads, f_wp4;
+};
+
+// V rows in region-major order: the two 32-byte halves of a row swap when
+// bit 1 of its position is set, so the four rows one transposing read
+// addresses (two consecutive pairs) hit four distinct 32-byte bank groups.
+__device__ __forceinline__ int vrswz(int pos) { return ((pos >> 1) & 1) << 1; }
+// Padded V image of the masked form: the halves of a pixel swap when bit 1
+// of its column is set, so the four consecutive pixels of one row that 16
+// lanes read for a LePE tap row hit four distinct 32-byte bank groups (rows
+// do not share a read, so the row takes no part).
+__device__ __forceinline__ int vmswz(int px) { return ((px >> 1) & 1) << 1; }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+template <class G>
+__global__ __launch_bounds__(G::NT) void attend_image_mask_kernel(MaskArgs A) {
+  constexpr int TOPK = G::TOPK, KS = G::KS, NW = G::NW, NT = G::NT, n = G::n;
+  constexpr int P = G::P, KK = G::KK, LSW = G::LSW, NKB = G::NKB, NKB2 = G::NKB2;
+  constexpr int NBS = G::NBS, NES = G::NES;
+  extern __shared__ __align__(16) unsigned char lds[];
+  uint16_t* Ks = (uint16_t*)(lds + A.ks_off);       // [32 NKB2][32] region-major
+  uint16_t* Vs = (uint16_t*)(lds + A.vs_off);       // the same rows of V
+  uint16_t* Vi = (uint16_t*)(lds + A.vi_off);       // the padded V image
+  unsigned char* ct = lds + A.ct_off;               // [query region][4][16] multiplicities
+  int* rtab = (int*)(lds + A.rt_off);               // per region: LePE base address
+  uint2* wpr = (uint2*)(lds + A.ws_off);            // LePE dot2 weights [KS][3][32]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lq = lane & 15, lg = lane >> 4;
+  const int xcd = blockIdx.x % kXcds, rest = blockIdx.x / kXcds;
+  const int t1 = fdiv(rest, A.f_qsplit), qs = rest - t1 * A.qsplit;
+  const int t2 = fdiv(t1, A.f_heads), h = t1 - t2 * A.heads;
+  const int b = t2 * kXcds + xcd;
+  if (b >= A.B) return;                              // uniform over the workgroup
+  const int qb0 = qs * A.qper;
+  const int qb1 = min(A.nqb, qb0 + A.qper);
+  if (qb0 >= qb1) return;
+  const int qr0 = 4 * qb0;                           // first query region of the range
+  const int nqr = min(A.R, 4 * qb1) - qr0;           // query regions of the range
+
+  const int H = A.H, W = A.W, C = A.C, S = A.S, R = A.R;
+  const int WP = W + 2 * P, HP = H + 2 * P;
+  const int nkeys = R * n;
+  const uint32_t img_elems = (uint32_t)H * W * C;
+  const size_t img = (size_t)b * img_elems;
+  const auto Qr = image_rsrc(A.q + img, img_elems * 2);
+  const auto Kr = image_rsrc(A.k + img, img_elems * 2);
+  const auto Vr = image_rsrc(A.v + img, img_elems * 2);
+  const auto Or = image_rsrc(A.out + img, img_elems * 2);
+  const int c0 = h * kHd;
+
+  // this lane's query: region 4 qb + lq / 4, token lq % 4
+  auto q_off = [&](int qb) -> uint32_t {
+    const int qr = 4 * qb + (lq >> 2), t = lq & 3;
+    const int ry = fdiv(min(qr, R - 1), A.f_S), rx = min(qr, R - 1) - ry * S;
+    const uint32_t off = ((ry * 2 + (t >> 1)) * W + rx * 2 + (t & 1)) * C + c0 + 8 * lg;
+    return qr < R ? off * 2 : kOob;
+  };
+  int qb = qb0 + wave;
+  uint4 qn = bload16(Qr, qb < qb1 ? q_off(qb) : kOob);
+
+  // ---- stage.  Every global read is issued first (K and V rows, the LePE
+  // weights, the routing entries), the LDS areas that are only cleared are
+  // cleared while they are in flight, then the loaded values are written ----
+  const int cw = lane & 31;
+  {
+    const int total = H * W * 4;                     // 16-byte chunks of this head (<= 128 NKB2)
+    uint4 kr[NBS], vr[NBS];
+#pragma unroll
+    for (int i = 0; i < NBS; ++i) {
+      const int e = i * NT + tid;
+      const uint32_t off = e < total ? (uint32_t)((e >> 2) * C + c0 + (e & 3) * 8) * 2 : kOob;
+      kr[i] = bload16(Kr, off);
+      vr[i] = bload16(Vr, off);
+    }
+    // one (kernel row, tap pair) entry of this head's LePE weights a thread
+    const int we = tid;
+    float wt[KS] = {};
+    if (we < KS * 3 * kHd) {
+      const float* wr = A.w + (size_t)(c0 + (we & 31)) * KK + ((we >> 5) / 3) * KS;
+#pragma unroll
+      for (int jx = 0; jx < KS; ++jx) wt[jx] = wr[jx];
+    }
+    // routing entries of the range's query regions, one a thread and step
+    const int nent = nqr * TOPK;
+    const auto Ir = image_rsrc(A.idx + ((size_t)b * R + qr0) * TOPK, (uint32_t)nent * 4);
+    int ent[NES];
+#pragma unroll
+    for (int i = 0; i < NES; ++i) {
+      const int e = i * NT + tid;
+      ent[i] = __builtin_amdgcn_raw_buffer_load_b32(Ir, e < nent ? (uint32_t)e * 4 : kOob, 0, 0);
+    }
+    // cleared areas: key rows past the last key (their multiplicity is zero
+    // too), the zero border of the V image, the multiplicity table
+    for (int e = nkeys * 4 + tid; e < 32 * NKB2 * 4; e += NT) {
+      *(uint4*)(Ks + e * 8) = make_uint4(0, 0, 0, 0);
+      *(uint4*)(Vs + e * 8) = make_uint4(0, 0, 0, 0);
+    }
+    for (int e = tid; e < HP * WP * 4; e += NT) {
+      const int pc = fdiv(e, A.f_wp4);
+      const int px = (e - pc * WP * 4) >> 2;
+      if ((unsigned)(pc - P) >= (unsigned)H || (unsigned)(px - P) >= (unsigned)W)
+        *(uint4*)(Vi + e * 8) = make_uint4(0, 0, 0, 0);
+    }
+    for (int e = tid; e < nqr * 4; e += NT) *(uint4*)(ct + e * 16) = make_uint4(0, 0, 0, 0);
+    // per region (padded to whole query blocks, clamped into [0, R)): the
+    // byte offset in the V image of its top-left pixel, with bit 5 carrying
+    // the parity of its region column (the swizzle of its pixel pairs)
+    for (int r = tid; r < 4 * A.nqb; r += NT) {
+      const int rr = min(r, R - 1);
+      const int ry = fdiv(rr, A.f_S), rx = rr - ry * S;
+      rtab[r] = (2 * ry * WP + 2 * rx) * kHd * 2 + ((rx & 1) << 5);
+    }
+    __syncthreads();                                 // the table is clear before the counts
+#pragma unroll
+    for (int i = 0; i < NBS; ++i) {
+      const int e = i * NT + tid;
+      if (e < total) {
+        const int p = e >> 2, g = e & 3;
+        const int y = fdiv(p, A.f_W), x = p - y * W;
+        const int ry = y >> 1, rx = x >> 1;
+        const int pos = (ry * S + rx) * n + (y & 1) * 2 + (x & 1);
+        *(uint4*)(Ks + pos * kHd + ((g ^ kswz(pos)) << 3)) = kr[i];
+        *(uint4*)(Vs + pos * kHd + ((g ^ vrswz(pos)) << 3)) = vr[i];
+        const int py = y + P, px = x + P;
+        *(uint4*)(Vi + (py * WP + px) * kHd + ((g ^ vmswz(px)) << 3)) = vr[i];
+      }
+    }
+    // LePE weights as bf16 pairs, per kernel row dy and pair kk: for the
+    // even output column of a pair of columns the taps (w0,w1) (w2,w3)
+    // (w4,0) over pixel pairs (x,x+1) (x+2,x+3) (x+4,x+5), for the odd
+    // column (0,w0) (w1,w2) (w3,w4) over the same pairs
+    if (we < KS * 3 * kHd) {
+      const int kk = (we >> 5) % 3;
+      wpr[we] = kk == 0 ? make_uint2(pack_bf16x2(wt[0], wt[1]), pack_bf16x2(0.f, wt[0]))
+              : kk == 1 ? make_uint2(pack_bf16x2(wt[2], wt[3]), pack_bf16x2(wt[1], wt[2]))
+                        : make_uint2(pack_bf16x2(wt[4], 0.f), pack_bf16x2(wt[3], wt[4]));
+    }
+    // multiplicities: routed key region kr of query region rl counts at
+    // byte (kr % 4) * 16 + kr / 4 of row rl (indices clamped into [0, R));
+    // byte counts stay below 256 (at most TOPK entries a row)
+#pragma unroll
+    for (int i = 0; i < NES; ++i) {
+      const int e = i * NT + tid;
+      if (e < nent) {
+        const int kr = min(max(ent[i], 0), R - 1);
+        const int slot = (kr & 3) * 16 + (kr >> 2);
+        __atomic_fetch_add((uint32_t*)(ct + (e / TOPK) * 64 + (slot & ~3)),
+                           1u << (8 * (slot & 3)), __ATOMIC_RELAXED);
+      }
+    }
+  }
+  const float b0 = A.bias ? A.bias[c0 + cw] : 0.f;
+  __syncthreads();
+
+  const float c = A.scale_log2;
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u,
+                                                            0x3f803f80u, 0x3f803f80u));
+  float* Lw = (float*)(lds + A.lw_off) + wave * 16 * LSW;
+  const int grp = lane >> 5;                         // LePE: region row grp of each region
+  // LePE transposing reads: lane i of a 16-lane row addresses padded pixel
+  // x + i/4 (+4 for the second read) of row 2ry + grp + dy, channels
+  // cq .. cq+3 with cq = (cw & ~15) + 4(i % 4), and receives channel cw of
+  // the four pixels as two bf16 pairs along x.  The swizzle of pixel x + i/4
+  // is bit 1 of it: the region column's parity (from the table) xor bit 3
+  // of the lane.
+  const int cq = (cw & ~15) + 4 * (lane & 3);
+  const uint32_t lx = ((uint32_t)((lq >> 3) & 1) << 5) ^ ((uint32_t)(cq >> 3) << 4);
+  const uint32_t lbase = (uint32_t)A.vi_off + (uint32_t)(grp * WP + (lq >> 2)) * kHd * 2 +
+                         (uint32_t)(cq & 7) * 2;
+  const uint32_t rs = (uint32_t)WP * kHd * 2;         // bytes per padded row
+  // the previous block's output is stored once this block's logits are
+  // under way, so the store's registers are not needed again at once
+  uint4 pend_v = make_uint4(0, 0, 0, 0);
+  uint32_t pend_off = kOob;
+  for (; qb < qb1; qb += NW) {
+    const bf16x8 qop = __builtin_bit_cast(bf16x8, qn);
+    // the next block's Q, always issued (past the range it reads zeros) and
+    // kept at the top of the block, so its latency hides behind the block
+    qn = bload16(Qr, qb + NW < qb1 ? q_off(qb + NW) : kOob);
+    __builtin_amdgcn_sched_barrier(0);
+    const int qr = 4 * qb + (lq >> 2);
+    const int qrl = min(qr, R - 1) - qr0;             // row of the multiplicity table
+    // multiplicities of key regions 4 kb + lg, kb = 0..15, for this column
+    const uint4 cnt = *(const uint4*)(ct + qrl * 64 + lg * 16);
+    const uint32_t cw4[4] = {cnt.x, cnt.y, cnt.z, cnt.w};
+
+    // ---- S^T = K Q^T over every key block; the largest routed logit ----
+    float x[NKB][4];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int pos = 16 * kb + lq;
+      const bf16x8 ka = *(const bf16x8*)(Ks + pos * kHd + ((lg ^ kswz(pos)) << 3));
+      const f32x4 sv = mfma_bf16(ka, qop, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[kb][e] = sv[e];
+    }
+    bstore16(Or, pend_off, pend_v);
+    float m = -3.0e38f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const bool routed = (cw4[kb >> 2] >> (8 * (kb & 3))) & 0xff;
+      const float mk = fmaxf(fmaxf(x[kb][0], x[kb][1]), fmaxf(x[kb][2], x[kb][3]));
+      m = routed ? fmaxf(m, mk) : m;
+    }
+    m = fmaxf(m, xor16(m));
+    m = fmaxf(m, xor32(m));
+    const float mc = m * c;
+
+    // ---- numerators in P^T slot order; O^T += V^T P^T, 32 keys a step ----
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
+    const int cc = 4 * (lq & 3);
+    const int ga = cc >> 3, gb = (16 + cc) >> 3, wi = cc & 7;
+#pragma unroll
+    for (int hh = 0; hh < NKB2; ++hh) {
+      uint32_t ph[4];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int kb = 2 * hh + half;
+        const float cm = (float)((cw4[kb >> 2] >> (8 * (kb & 3))) & 0xff);
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = cm * __builtin_amdgcn_exp2f(fmaf(x[kb][e], c, -mc));
+        ph[2 * half] = pack_bf16x2(pv[0], pv[1]);
+        ph[2 * half + 1] = pack_bf16x2(pv[2], pv[3]);
+      }
+      // V^T operands: lane (lq, lg) addresses key row 32hh + 4lg + lq/4 (+16),
+      // channels 4(lq % 4) .. +3 of each 16-channel half, and receives
+      // channel d0 + lq of rows 4lg + 0..3
+      const int vrow = 32 * hh + 4 * lg + (lq >> 2);
+      const uint16_t* r0p = Vs + vrow * kHd;
+      const uint16_t* r1p = r0p + 16 * kHd;
+      const int s0 = vrswz(vrow), s1 = vrswz(vrow + 16);
+      const uint2 a0 = lds_read_tr16(r0p + ((ga ^ s0) << 3) + wi);
+      const uint2 a1 = lds_read_tr16(r1p + ((ga ^ s1) << 3) + wi);
+      const uint2 d0 = lds_read_tr16(r0p + ((gb ^ s0) << 3) + wi);
+      const uint2 d1 = lds_read_tr16(r1p + ((gb ^ s1) << 3) + wi);
+      const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(d0.x, d0.y, d1.x, d1.y));
+      const bf16x8 phi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+      acc0 = mfma_bf16(va, phi, acc0);
+      acc1 = mfma_bf16(vb, phi, acc1);
+      accl = mfma_bf16(ones, phi, accl);
+    }
+
+    // ---- LePE of the block's 16 pixels: region j's pixel row grp, two columns ----
+    float lw[4][2];
+    {
+      const int4 tb = *(const int4*)(rtab + 4 * qb);
+      const int tj[4] = {tb.x, tb.y, tb.z, tb.w};
+      uint32_t va[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lw[j][0] = lw[j][1] = b0;
+        va[j] = ((uint32_t)tj[j] ^ lx) + lbase;
+      }
+#pragma unroll
+      for (int dy = 0; dy < KS; ++dy) {
+        const uint2 w0 = wpr[(dy * 3 + 0) * kHd + cw];
+        const uint2 w1 = wpr[(dy * 3 + 1) * kHd + cw];
+        const uint2 w2 = wpr[(dy * 3 + 2) * kHd + cw];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint16_t* pa = (const uint16_t*)(lds + va[j] + dy * rs);
+          const uint2 a = lds_read_tr16(pa);
+          const uint2 bb = lds_read_tr16(pa + 4 * kHd);
+          lw[j][0] = dot2(w2.x, bb.x, dot2(w1.x, a.y, dot2(w0.x, a.x, lw[j][0])));
+          lw[j][1] = dot2(w2.y, bb.x, dot2(w1.y, a.y, dot2(w0.y, a.x, lw[j][1])));
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int kx = 0; kx < 2; ++kx) Lw[(j * 4 + grp * 2 + kx) * LSW + cw] = lw[j][kx];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+    // ---- out = O / l + L, one rounding, 16-byte stores ----
+    {
+      const int t = lq & 3;
+      const float inv = __builtin_amdgcn_rcpf(accl[0]);
+      const float* lp = Lw + lq * LSW;
+      const float4 a0 = *(const float4*)(lp + 4 * lg);
+      const float4 a1 = *(const float4*)(lp + 16 + 4 * lg);
+      const uint32_t o0x = pack_bf16x2(fmaf(acc0[0], inv, a0.x), fmaf(acc0[1], inv, a0.y));
+      const uint32_t o0y = pack_bf16x2(fmaf(acc0[2], inv, a0.z), fmaf(acc0[3], inv, a0.w));
+      const uint32_t o1x = pack_bf16x2(fmaf(acc1[0], inv, a1.x), fmaf(acc1[1], inv, a1.y));
+      const uint32_t o1y = pack_bf16x2(fmaf(acc1[2], inv, a1.z), fmaf(acc1[3], inv, a1.w));
+      const auto sx = __builtin_amdgcn_permlane16_swap(o0x, o1x, false, false);
+      const auto sy = __builtin_amdgcn_permlane16_swap(o0y, o1y, false, false);
+      const bool odd = lg & 1;
+      const uint4 ov = odd ? make_uint4(sx[0], sy[0], o1x, o1y) : make_uint4(o0x, o0y, sx[1], sy[1]);
+      const int ch = odd ? 16 + 4 * (lg - 1) : 4 * lg;
+      const int qrc = min(qr, R - 1);
+      const int ry = fdiv(qrc, A.f_S), rx = qrc - ry * S;
+      const uint32_t op = ((ry * 2 + (t >> 1)) * W + rx * 2 + (t & 1)) * C + c0 + ch;
+      pend_off = qr < R ? op * 2 : kOob;
+      pend_v = ov;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  }
+  bstore16(Or, pend_off, pend_v);
+}
+
+template <class G>
+struct MaskLds {
+  int ks_off, vs_off, vi_off, ct_off, rt_off, ws_off, lw_off;
+  size_t bytes;
+};
+
+template <class G>
+MaskLds<G> mask_lds(int H, int W, int nqr, int nqb) {
+  MaskLds<G> l;
+  const int WP = W + 2 * G::P, HP = H + 2 * G::P;
+  const size_t rows = (size_t)G::NKB2 * 32;
+  size_t off = 0;
+  l.ks_off = (int)off;
+  off += rows * kHd * 2;
+  l.vs_off = (int)off;
+  off += rows * kHd * 2;
+  l.vi_off = (int)off;
+  off += ((size_t)HP * WP + WP) * kHd * 2;
+  l.ct_off = (int)off;
+  off += (size_t)nqr * 64;
+  off = (off + 15) / 16 * 16;
+  l.rt_off = (int)off;
+  off += (size_t)nqb * 4 * 4;
+  l.ws_off = (int)off;
+  off += (size_t)G::KS * 3 * kHd * 8;
+  l.lw_off = (int)off;
+  off += (size_t)G::NW * 16 * G::LSW * 4;
+  l.bytes = off;
+  return l;
+}
+
+template <class G>
+hipError_t mask_launch(MaskArgs a, hipStream_t st) {
+  int dev = 0, lds_max = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (lds_max < 64 * 1024) lds_max = 64 * 1024;
+  const void* fn = reinterpret_cast<const void*>(&attend_image_mask_kernel<G>);
+  const MaskLds<G> l1 = mask_lds<G>(a.H, a.W, a.R, a.nqb);
+  if (l1.bytes > (size_t)lds_max) return hipErrorNotSupported;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)l1.bytes);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_image_mask_kernel<G>, G::NT,
+                                                   l1.bytes);
+  if (e != hipSuccess) return e;
+  // workgroups per (image, head): as many query-block ranges (1, 2 or 4) as
+  // the resident workgroup slots take
+  const long long slots = (long long)cus * (per_cu > 0 ? per_cu : 1);
+  const long long base = (long long)a.B * a.heads;
+  int qsplit = 1;
+  while (qsplit < 4 && qsplit * 2 <= a.nqb && base * qsplit * 2 <= slots) qsplit *= 2;
+  a.qsplit = qsplit;
+  a.qper = (a.nqb + qsplit - 1) / qsplit;
+  a.f_qsplit = make_fastdiv(qsplit);
+  const MaskLds<G> l = mask_lds<G>(a.H, a.W, 4 * a.qper, a.nqb);
+  a.ks_off = l.ks_off; a.vs_off = l.vs_off; a.vi_off = l.vi_off; a.ct_off = l.ct_off;
+  a.rt_off = l.rt_off; a.ws_off = l.ws_off; a.lw_off = l.lw_off;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)l.bytes);
+  if (e != hipSuccess) return e;
+  const long long groups = (long long)(a.B + kXcds - 1) / kXcds * a.heads * qsplit * kXcds;
+  if (groups >= (1LL << 31)) return hipErrorNotSupported;
+  hipLaunchKernelGGL(attend_image_mask_kernel<G>, dim3((unsigned)groups), dim3(G::NT), l.bytes,
+                     st, a);
+  return hipGetLastError();
+}
+
 // LDS layout of one workgroup (bytes): K region-major [H*W][32] bf16, the
 // padded V image [(H+2P)*(W+2P)][32] bf16 (plus one row of slack for the
 // LePE reads past the last tap), the routing table [rper][topk] int2 and
@@ -459,6 +887,11 @@ hipError_t image_launch(ImageArgs a, int rsplit, hipStream_t st) {
 #endif
 using ImgSt2 = Ic<4, 4, 4, 5, BRA_IMAGE_NW2>;
 using ImgSt3 = Ic<2, 2, 16, 5, BRA_IMAGE_NW3>;
+#ifndef BRA_MASK_NW
+#define BRA_MASK_NW 8
+#endif
+template <int NKB2>
+using MaskSt3 = Im<16, BRA_MASK_NW, NKB2>;
 
 }  // namespace
 
@@ -483,6 +916,30 @@ hipError_t launch_attend_image(const void* q, const void* k, const void* v, cons
   a.f_wp4 = make_fastdiv((s.W + 4) * 4);
   const int rsplit = BRA_IMAGE_RSPLIT;                // 0: chosen from the batch
   auto is = [&](int hs, int ws, int topk) { return s.hs == hs && s.ws == ws && s.topk == topk; };
+  // 2x2 regions whose routed keys are at least a quarter of the image: the
+  // masked whole-image form (fewer MFMA and softmax operations than 16-column
+  // blocks padded from four queries)
+  if (s.hs == 2 && s.ws == 2 && s.topk == MaskSt3<1>::TOPK && 4 * s.topk >= s.R && s.R <= 64) {
+    MaskArgs m;
+    m.q = a.q; m.k = a.k; m.v = a.v; m.idx = a.idx; m.out = a.out; m.w = a.w; m.bias = a.bias;
+    m.B = s.B; m.H = s.H; m.W = s.W; m.C = s.C; m.S = s.S; m.R = s.R; m.heads = s.heads;
+    m.nqb = (s.R + 3) / 4;
+    m.nkb = (s.R * 4 + 15) / 16;
+    m.scale_log2 = a.scale_log2;
+    m.f_S = a.f_S; m.f_W = a.f_W; m.f_heads = a.f_heads; m.f_wp4 = a.f_wp4;
+    hipError_t e = hipErrorNotSupported;
+    switch ((s.R * 4 + 31) / 32) {          // 32-key steps
+      case 2: e = mask_launch<MaskSt3<2>>(m, st); break;
+      case 3: e = mask_launch<MaskSt3<3>>(m, st); break;
+      case 4: e = mask_launch<MaskSt3<4>>(m, st); break;
+      case 5: e = mask_launch<MaskSt3<5>>(m, st); break;
+      case 6: e = mask_launch<MaskSt3<6>>(m, st); break;
+      case 7: e = mask_launch<MaskSt3<7>>(m, st); break;
+      case 8: e = mask_launch<MaskSt3<8>>(m, st); break;
+      default: break;
+    }
+    if (e != hipErrorNotSupported) return e;
+  }
   if (is(ImgSt2::HS, ImgSt2::WS, ImgSt2::TOPK)) return image_launch<ImgSt2>(a, rsplit, st);
   if (is(ImgSt3::HS, ImgSt3::WS, ImgSt3::TOPK)) return image_launch<ImgSt3>(a, rsplit, st);
   return hipErrorNotSupported;

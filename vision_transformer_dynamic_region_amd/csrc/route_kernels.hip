@@ -679,8 +679,10 @@ __global__ __launch_bounds__(kSmallWaves * 64) void route_small_kernel(RouteArgs
 // pools the image's K itself (the image's strips share one XCD, so the
 // repeated reads come from its L2): no second launch, no wait between
 // workgroups, and the means reach the affinity without a round trip through
-// memory.  They are still written to the workspace (K by the first strip,
-// Q by every strip for its rows), which callers may read.
+// memory.  When asked for (qm, km not null) they are also written out (K by
+// the first strip, Q by every strip for its rows) for callers that read
+// them; the forward pass does not ask, which saves writing float64 means as
+// large as the bf16 inputs at 2x2-pixel regions.
 //
 // Pooling: wavefront w takes items w, w + 16, ... (K regions 0..R-1, then
 // the strip's Q regions); lane (p, g) = (lane / G, lane % G) owns 16-byte
@@ -783,7 +785,8 @@ __global__ __launch_bounds__(kSmallWaves * 64) void pool_route_kernel(PoolRouteA
         if constexpr (PP >= 8) scatter_step<3, VEC / 4>(v);
         // lane p holds values p*KEEP .. p*KEEP + KEEP - 1 of group g
         const int row = item;                    // K regions first, then the strip's Q rows
-        double* gdst = item < R ? (strip == 0 ? A.km + ((size_t)b * R + item) * C : nullptr)
+        double* gdst = !A.qm ? nullptr
+                     : item < R ? (strip == 0 ? A.km + ((size_t)b * R + item) * C : nullptr)
                                 : A.qm + ((size_t)b * R + r0 + item - R) * C;
 #pragma unroll
         for (int jj = 0; jj < KEEP; ++jj) {
