@@ -40,8 +40,8 @@ KERNEL_SOURCES = [
     "vision_transformer_dynamic_region_amd/csrc/fastdiv.h",
 ]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_traffic.json")
-ATTEND_KERNELS = ("attend_region_kernel", "attend_image_kernel", "attend_stream_kernel",
-                  "attend_kernel")
+ATTEND_KERNELS = ("attend_region_kernel", "attend_image_kernel", "attend_image_mask_kernel",
+                  "attend_stream_kernel", "attend_kernel")
 # measured beside the headline workload on the default line
 OTHER_WORKLOADS = ("dense", "st2", "st3")
 
@@ -136,14 +136,19 @@ def write_traffic(a) -> int:
 
 def attend_kernel_name(wl) -> str:
     """The attention kernel the library launches for this workload: the
-    whole-image kernel for bf16 4x4 / top-4 and 2x2 / top-16 regions, the
-    per-region kernel for the bf16 stage-1 and dense shapes, else the
-    pipelined general kernel or, when its routed keys or LePE halo do not fit
-    that one, the chunked general kernel."""
-    image = {("bf16", 4, 4), ("bf16", 2, 16)}
-    region = {("bf16", 64, 8, 1), ("bf16", 64, 8, 4)}
-    if wl.lepe_ks == 5 and (wl.dtype, wl.H // wl.S, wl.topk) in image and wl.C % 32 == 0:
+    masked whole-image kernel for bf16 2x2 / top-16 regions (up to 64 of
+    them, routed keys at least a quarter of the image), the whole-image
+    gather kernel for bf16 4x4 / top-4 regions, the per-region kernel for the
+    bf16 stage-1 and dense shapes, else the pipelined general kernel or, when
+    its routed keys or LePE halo do not fit that one, the chunked general
+    kernel."""
+    R = wl.S * wl.S
+    if (wl.lepe_ks == 5 and wl.dtype == "bf16" and wl.C % 32 == 0 and wl.H // wl.S == 2
+            and wl.topk == 16 and 4 * wl.topk >= R and R <= 64):
+        return "attend_image_mask_kernel"
+    if wl.lepe_ks == 5 and (wl.dtype, wl.H // wl.S, wl.topk) == ("bf16", 4, 4) and wl.C % 32 == 0:
         return "attend_image_kernel"
+    region = {("bf16", 64, 8, 1), ("bf16", 64, 8, 4)}
     key = (wl.dtype, wl.C, wl.H // wl.S, wl.topk)
     return "attend_region_kernel" if key in region and wl.lepe_ks == 5 \
         else "attend_stream_kernel|attend_kernel"

@@ -20,6 +20,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
+// Cache policy bits of the attention kernels' output stores (gfx950 buffer
+// stores: 1 = sc0, 2 = nt, 16 = sc1).
+#ifndef BRA_OUT_CPOL
+#define BRA_OUT_CPOL 2
+#endif
+
 constexpr int kThreads = 256;   // 4 wavefronts of 64
 constexpr int kWaves = 4;
 constexpr int kXcds = 8;        // MI355X: workgroups go round-robin to 8 XCDs

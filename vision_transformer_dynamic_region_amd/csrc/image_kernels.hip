@@ -96,7 +96,7 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
   const u32x4 x = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, BRA_OUT_CPOL);
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));

@@ -55,6 +55,9 @@ template <int C_, int CB_, int HS_, int WS_, int TOPK_, int KS_, bool DB_, int O
 struct Rc {
   static constexpr int C = C_, CB = CB_, HS = HS_, WS = WS_, TOPK = TOPK_, KS = KS_;
   static constexpr bool DB = DB_;                  // double-buffered staging
+  // more than 128 routed keys: S^T is computed twice (the maximum, then the
+  // numerators 32 keys a step) rather than held in 4 KC / 64 registers
+  static constexpr bool TWO_PASS = TOPK_ * HS_ * WS_ > 128;
   static constexpr int OCC = OCC_;                 // workgroups per CU to allow for
   static constexpr int NCB = C / CB;               // channel blocks per region
   static constexpr int n = HS * WS;                // queries per region
@@ -156,8 +159,12 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
   const u32x4 x = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, BRA_OUT_CPOL);
 }
+
+#ifndef BRA_PRIO_RAMP
+#define BRA_PRIO_RAMP 1
+#endif
 
 template <class G>
 __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionArgs A) {
@@ -305,6 +312,18 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
 
   for (int j = 0; j < nu; ++j) {
     unsigned char* buf = lds + (G::DB ? (j & 1) * G::BUF : 0);
+#if BRA_PRIO_RAMP
+    {
+      // waves further through their units issue at a lower priority, so the
+      // workgroups sharing a CU (older ones are otherwise issued first) keep
+      // pace and finish together
+      const int lvl = __builtin_amdgcn_readfirstlane(4 * j / nu);
+      if (lvl == 0) __builtin_amdgcn_s_setprio(3);
+      else if (lvl == 1) __builtin_amdgcn_s_setprio(2);
+      else if (lvl == 2) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
+#endif
     commit(buf);
     __syncthreads();
     if (j + 1 < nu) prefetch(j + 1);
@@ -345,65 +364,106 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
     };
     constexpr int NR = TYW + KS - 1;                   // input rows of an item
 
-    // ---- attention phase 1: S^T = K Q^T ----
-    float x[KC / 4];
-#pragma unroll
-    for (int kb = 0; kb < KC / 16; ++kb) {
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
+    // K operand of 16-key block kb: lane (lq, lg) holds channels
+    // 32hb + 8lg .. +7 of key 16kb + lq
+    auto kop = [&](int kb) -> bf16x8 {
       const int key = 16 * kb + lq;
-      const bf16x8 ka = *(const bf16x8*)(Ks + key * CB + (((hb * 4 + lg) ^ kswz<GB>(key)) * 8));
-      const f32x4 sv = mfma_bf16(ka, qop, f32x4{0.f, 0.f, 0.f, 0.f});
-      // lane holds keys 16*kb + 4*lg + e of query lq
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * kb + e] = sv[e];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    conv_rows(0, NR / 3);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- phase 2: softmax numerators, rounded to bf16 in P^T slot order ----
-    uint32_t ph[KC / 8];
-    {
-      float m = x[0];
-#pragma unroll
-      for (int e = 1; e < KC / 4; ++e) m = fmaxf(m, x[e]);
-      m = fmaxf(m, xor16(m));
-      m = fmaxf(m, xor32(m));
-      const float mc = m * c;
-#pragma unroll
-      for (int e = 0; e < KC / 8; ++e)
-        ph[e] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(x[2 * e], c, -mc)),
-                            __builtin_amdgcn_exp2f(fmaf(x[2 * e + 1], c, -mc)));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    conv_rows(NR / 3, 2 * NR / 3);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- phase 3: O^T += V^T P^T, row sums += ones P^T ----
+      return *(const bf16x8*)(Ks + key * CB + (((hb * 4 + lg) ^ kswz<GB>(key)) * 8));
+    };
     // V^T operands by transposing reads of the row-major V tile: lane (lq, lg)
     // addresses key 4lg + lq/4 (+16 for slots 4-7), channels d0 + 4(lq % 4)
     // .. +3, and receives channel d0 + lq of keys 4lg + 0..3 -- the slot order
     // of P^T (slots e: keys 32h + 4lg + e for e < 4, 32h + 16 + 4lg + e - 4).
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
-    {
-      const int vrow = 4 * lg + (lq >> 2);             // key within a 16-key block
-      const int vsw = kswz<GB>(vrow);                  // same for vrow + 16m
-      const uint16_t* vbase = Vs + vrow * CB + 4 * (lq & 1);
-      const int ca = ((hb * 4 + ((lq >> 1) & 1)) ^ vsw) * 8;       // d0 = 32hb
-      const int cbo = ((hb * 4 + 2 + ((lq >> 1) & 1)) ^ vsw) * 8;  // d0 = 32hb + 16
+    const int vrow = 4 * lg + (lq >> 2);               // key within a 16-key block
+    const int vsw = kswz<GB>(vrow);                    // same for vrow + 16m
+    const uint16_t* vbase = Vs + vrow * CB + 4 * (lq & 1);
+    const int ca = ((hb * 4 + ((lq >> 1) & 1)) ^ vsw) * 8;       // d0 = 32hb
+    const int cbo = ((hb * 4 + 2 + ((lq >> 1) & 1)) ^ vsw) * 8;  // d0 = 32hb + 16
+    // O^T += V^T P^T and the row sums += ones P^T for keys 32h .. 32h+31
+    auto pv_step = [&](int h, const uint32_t* p4) {
+      const uint16_t* r0 = vbase + (32 * h) * CB;
+      const uint16_t* r1 = r0 + 16 * CB;
+      const uint2 a0 = lds_read_tr16(r0 + ca), a1 = lds_read_tr16(r1 + ca);
+      const uint2 c0 = lds_read_tr16(r0 + cbo), c1 = lds_read_tr16(r1 + cbo);
+      const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(c0.x, c0.y, c1.x, c1.y));
+      const bf16x8 phi = __builtin_bit_cast(bf16x8, make_uint4(p4[0], p4[1], p4[2], p4[3]));
+      acc0 = mfma_bf16(va, phi, acc0);                 // O^T rows d = 4lg + e
+      acc1 = mfma_bf16(vb, phi, acc1);                 // O^T rows d = 16 + 4lg + e
+      accl = mfma_bf16(ones, phi, accl);               // every row: sum over keys
+    };
+    if constexpr (!G::TWO_PASS) {
+      // ---- attention phase 1: S^T = K Q^T, kept in registers ----
+      float x[KC / 4];
 #pragma unroll
-      for (int h = 0; h < KC / 32; ++h) {
-        const uint16_t* r0 = vbase + (32 * h) * CB;
-        const uint16_t* r1 = r0 + 16 * CB;
-        const uint2 a0 = lds_read_tr16(r0 + ca), a1 = lds_read_tr16(r1 + ca);
-        const uint2 c0 = lds_read_tr16(r0 + cbo), c1 = lds_read_tr16(r1 + cbo);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
-        const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(c0.x, c0.y, c1.x, c1.y));
-        const bf16x8 phi =
-            __builtin_bit_cast(bf16x8, make_uint4(ph[4 * h], ph[4 * h + 1], ph[4 * h + 2], ph[4 * h + 3]));
-        acc0 = mfma_bf16(va, phi, acc0);               // O^T rows d = 4lg + e
-        acc1 = mfma_bf16(vb, phi, acc1);               // O^T rows d = 16 + 4lg + e
-        accl = mfma_bf16(ones, phi, accl);             // every row: sum over keys
+      for (int kb = 0; kb < KC / 16; ++kb) {
+        const f32x4 sv = mfma_bf16(kop(kb), qop, f32x4{0.f, 0.f, 0.f, 0.f});
+        // lane holds keys 16*kb + 4*lg + e of query lq
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * kb + e] = sv[e];
       }
+      __builtin_amdgcn_sched_barrier(0);
+      conv_rows(0, NR / 3);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- phase 2: softmax numerators, rounded to bf16 in P^T slot order ----
+      uint32_t ph[KC / 8];
+      {
+        float m = x[0];
+#pragma unroll
+        for (int e = 1; e < KC / 4; ++e) m = fmaxf(m, x[e]);
+        m = fmaxf(m, xor16(m));
+        m = fmaxf(m, xor32(m));
+        const float mc = m * c;
+#pragma unroll
+        for (int e = 0; e < KC / 8; ++e)
+          ph[e] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(x[2 * e], c, -mc)),
+                              __builtin_amdgcn_exp2f(fmaf(x[2 * e + 1], c, -mc)));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      conv_rows(NR / 3, 2 * NR / 3);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- phase 3: O^T += V^T P^T, row sums += ones P^T ----
+#pragma unroll
+      for (int h = 0; h < KC / 32; ++h) pv_step(h, ph + 4 * h);
+    } else {
+      // ---- many routed keys: phase 1 keeps only the row maximum; phase 2
+      // computes S^T again, 32 keys a step, into numerators and O ----
+      float m = -3.0e38f;
+#pragma unroll
+      for (int kb = 0; kb < KC / 16; ++kb) {
+        const f32x4 sv = mfma_bf16(kop(kb), qop, f32x4{0.f, 0.f, 0.f, 0.f});
+        m = fmaxf(m, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+      }
+      m = fmaxf(m, xor16(m));
+      m = fmaxf(m, xor32(m));
+      const float mc = m * c;
+      __builtin_amdgcn_sched_barrier(0);
+      conv_rows(0, NR / 3);
+      __builtin_amdgcn_sched_barrier(0);
+      auto step = [&](int h) {
+        const f32x4 s0 = mfma_bf16(kop(2 * h), qop, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 s1 = mfma_bf16(kop(2 * h + 1), qop, f32x4{0.f, 0.f, 0.f, 0.f});
+        uint32_t p4[4];
+        p4[0] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s0[0], c, -mc)),
+                            __builtin_amdgcn_exp2f(fmaf(s0[1], c, -mc)));
+        p4[1] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s0[2], c, -mc)),
+                            __builtin_amdgcn_exp2f(fmaf(s0[3], c, -mc)));
+        p4[2] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s1[0], c, -mc)),
+                            __builtin_amdgcn_exp2f(fmaf(s1[1], c, -mc)));
+        p4[3] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s1[2], c, -mc)),
+                            __builtin_amdgcn_exp2f(fmaf(s1[3], c, -mc)));
+        pv_step(h, p4);
+      };
+#pragma unroll
+      for (int h = 0; h < KC / 64; ++h) step(h);
+      __builtin_amdgcn_sched_barrier(0);
+      conv_rows(NR / 3, 2 * NR / 3);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = KC / 64; h < KC / 32; ++h) step(h);
     }
     __builtin_amdgcn_sched_barrier(0);
     conv_rows(2 * NR / 3, NR);
@@ -511,7 +571,7 @@ hipError_t region_launch(RegionArgs a, int B, hipStream_t st) {
 using St1 = Rc<64, 32, 8, 8, 1, 5, BRA_DB_ST1>;
 using St2 = Rc<128, 128, 4, 4, 4, 5, false>;
 using St3 = Rc<256, 128, 2, 2, 16, 5, false>;
-using Dense = Rc<64, 32, 8, 8, 4, 5, BRA_DB_DENSE>;
+using Dense = Rc<64, 32, 8, 8, 4, 5, BRA_DB_DENSE, 3>;
 
 }  // namespace
 
