@@ -1,5 +1,6 @@
-"""The whole-image attention kernel (one head of one image's K and V resident
-in LDS; the 4x4-pixel / top-4 and 2x2-pixel / top-16 region shapes) against
+"""The whole-image attention kernels (one head of one image's K and V resident
+in LDS; the 4x4-pixel / top-4 and 2x2-pixel / top-16 region shapes, the
+latter in its masked form up to 64 regions and its gather form above) against
 the fp64 oracle, through the C ABI: batches that leave XCD slots empty,
 region grids other than 7x7, other head counts, a LePE bias, caller indices
 with repeated and out-of-range entries (a repeated region counts twice, as
@@ -26,6 +27,8 @@ CASES = {
     "st2_region_S8_C32": (2, 32, 32, 32, 1, 8, 4),
     "st2_region_S3_C192": (2, 12, 12, 192, 6, 3, 4),
     "st2_region_too_big_for_lds": (1, 48, 48, 128, 4, 12, 4),
+    # 81 regions of 2x2: past the masked form's 64, so the gather form runs
+    "st3_gather_S9_C64": (3, 18, 18, 64, 2, 9, 16),
 }
 
 

@@ -25,9 +25,10 @@
 //              scale folded into exp2, rounded to bf16; O^T = V^T P^T with the
 //              V^T operands read by transposing LDS reads at the routed
 //              pixels; row sums by an MFMA against a ones operand;
-//   LePE       5x5 cross-correlation of the padded V image in float32 FMAs
-//              (the float32 weights as given, the bf16 pixels widened
-//              exactly), interleaved with the attention phases;
+//   LePE       5x5 cross-correlation of the padded V image on
+//              v_dot2_f32_bf16 (tap pairs along x, weights rounded once to
+//              bf16, products exact, float32 sums), interleaved with the
+//              attention phases;
 //   epilogue   L through a wavefront-private LDS tile into the MFMA layout,
 //              out = O / l + L rounded once to bf16, 16-byte stores.
 // Q is read straight into registers, one task ahead.
@@ -116,6 +117,12 @@ __device__ __forceinline__ int kswz(int pos) { return (pos >> 1) & 3; }
 // 32-byte bank groups.
 __device__ __forceinline__ int vswz(int py, int px) { return ((py ^ (px >> 1)) & 1) << 1; }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                         __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 template <class G>
 __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
   constexpr int HS = G::HS, WS = G::WS, TOPK = G::TOPK, KS = G::KS, NW = G::NW, NT = G::NT;
@@ -194,15 +201,25 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
     }
   }
 
-  // this channel lane's LePE weights, float32 as given
+  // this channel lane's LePE weights as bf16 pairs per kernel row i: for an
+  // even output column the tap pairs (w0,w1) (w2,w3) (w4,0) over pixel pairs
+  // (x,x+1) (x+2,x+3) (x+4,x+5); for the odd column after it (0,w0) (w1,w2)
+  // (w3,w4) over the same pairs
   const int cw = lane & 31;
-  float wf[KS][KS];
+  uint32_t we[KS][3], wo[KS][3];
   {
     const float* wp = A.w + (size_t)(c0 + cw) * KK;
 #pragma unroll
-    for (int i = 0; i < KS; ++i)
-#pragma unroll
-      for (int jx = 0; jx < KS; ++jx) wf[i][jx] = wp[i * KS + jx];
+    for (int i = 0; i < KS; ++i) {
+      const float t0 = wp[i * KS], t1 = wp[i * KS + 1], t2 = wp[i * KS + 2];
+      const float t3 = wp[i * KS + 3], t4 = wp[i * KS + 4];
+      we[i][0] = pack_bf16x2(t0, t1);
+      we[i][1] = pack_bf16x2(t2, t3);
+      we[i][2] = pack_bf16x2(t4, 0.f);
+      wo[i][0] = pack_bf16x2(0.f, t0);
+      wo[i][1] = pack_bf16x2(t1, t2);
+      wo[i][2] = pack_bf16x2(t3, t4);
+    }
   }
   const float b0 = A.bias ? A.bias[c0 + cw] : 0.f;
   __syncthreads();
@@ -244,8 +261,8 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
     // transposing reads of 4 consecutive padded pixels of one channel: lane
     // i of a 16-lane row addresses pixel x + i/4 (+4 for the second read),
     // channels (cw & ~15) + 4(i % 4) .. +3, and receives channel cw of the
-    // four pixels as two bf16 pairs along x; the taps are float32 FMAs on
-    // the widened pixels
+    // four pixels as two bf16 pairs along x; the taps are dot2 products of
+    // those pairs with the weight pairs
     const int cq = (cw & ~15) + 4 * (lane & 3);       // first channel addressed
     const int py0 = ry * HS + qrow0 + yl;             // padded row of tap row 0
     const int pxa = rx * WS + xw + (lq >> 2), pxb = pxa + 4;
@@ -258,17 +275,19 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
                                       (((cq >> 3) ^ vswz(py, pxa)) << 3) + (cq & 7));
         const uint2 bb = lds_read_tr16(Vs + (py * WP + pxb) * kHd +
                                        (((cq >> 3) ^ vswz(py, pxb)) << 3) + (cq & 7));
-        // pixels x .. x+7 of this tap row (x+6, x+7 unused when XG == 2)
-        const float f[8] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
-                            bf16_lo(bb.x), bf16_hi(bb.x), bf16_lo(bb.y), bf16_hi(bb.y)};
+        // pixel pairs (x,x+1) .. (x+6,x+7) of this tap row (the last unused
+        // when XG == 2)
+        const uint32_t p0 = a.x, p1 = a.y, p2 = bb.x, p3 = bb.y;
 #pragma unroll
         for (int i = 0; i < KS; ++i) {
           const int rr = dy - i;
           if (rr < 0 || rr >= TYW) continue;
-#pragma unroll
-          for (int kx = 0; kx < XG; ++kx)
-#pragma unroll
-            for (int jx = 0; jx < KS; ++jx) lw[rr][kx] = fmaf(wf[i][jx], f[kx + jx], lw[rr][kx]);
+          lw[rr][0] = dot2(we[i][2], p2, dot2(we[i][1], p1, dot2(we[i][0], p0, lw[rr][0])));
+          lw[rr][1] = dot2(wo[i][2], p2, dot2(wo[i][1], p1, dot2(wo[i][0], p0, lw[rr][1])));
+          if constexpr (XG == 4) {
+            lw[rr][2] = dot2(we[i][2], p3, dot2(we[i][1], p2, dot2(we[i][0], p1, lw[rr][2])));
+            lw[rr][3] = dot2(wo[i][2], p3, dot2(wo[i][1], p2, dot2(wo[i][0], p1, lw[rr][3])));
+          }
         }
       }
     };
@@ -438,11 +457,6 @@ __device__ __forceinline__ int vrswz(int pos) { return ((pos >> 1) & 1) << 1; }
 // do not share a read, so the row takes no part).
 __device__ __forceinline__ int vmswz(int px) { return ((px >> 1) & 1) << 1; }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                         __builtin_bit_cast(bf16x2, b), c, false);
-}
 
 template <class G>
 __global__ __launch_bounds__(G::NT) void attend_image_mask_kernel(MaskArgs A) {

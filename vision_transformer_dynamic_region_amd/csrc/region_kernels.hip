@@ -51,7 +51,8 @@ namespace {
 
 constexpr int kHd = 32;    // head width
 
-template <int C_, int CB_, int HS_, int WS_, int TOPK_, int KS_, bool DB_, int OCC_ = 2>
+template <int C_, int CB_, int HS_, int WS_, int TOPK_, int KS_, bool DB_, int OCC_ = 2,
+          bool NT_ = false>
 struct Rc {
   static constexpr int C = C_, CB = CB_, HS = HS_, WS = WS_, TOPK = TOPK_, KS = KS_;
   static constexpr bool DB = DB_;                  // double-buffered staging
@@ -59,6 +60,9 @@ struct Rc {
   // numerators 32 keys a step) rather than held in 4 KC / 64 registers
   static constexpr bool TWO_PASS = TOPK_ * HS_ * WS_ > 128;
   static constexpr int OCC = OCC_;                 // workgroups per CU to allow for
+  // output stores non-temporal (written through, so the end-of-kernel
+  // write-back is short; each 16-byte store then costs more HBM writes)
+  static constexpr int OUT_CPOL = NT_ ? BRA_OUT_CPOL : 0;
   static constexpr int NCB = C / CB;               // channel blocks per region
   static constexpr int n = HS * WS;                // queries per region
   static constexpr int KC = TOPK * n;              // routed keys, all in LDS at once
@@ -157,9 +161,10 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+template <int CPOL>
 __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
   const u32x4 x = {v.x, v.y, v.z, v.w};
-  __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, BRA_OUT_CPOL);
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, CPOL);
 }
 
 #ifndef BRA_PRIO_RAMP
@@ -496,7 +501,7 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
       const uint4 ov = odd ? make_uint4(sx[0], sy[0], o1x, o1y) : make_uint4(o0x, o0y, sx[1], sy[1]);
       const int ch = odd ? 16 + 4 * (lg - 1) : 4 * lg;
       const uint32_t op = ((ry * HS + q / WS) * A.W + rx * WS + q % WS) * C + cb0 + hb * kHd + ch;
-      bstore16(O, q < n ? op * 2 : kOob, ov);
+      bstore16<G::OUT_CPOL>(O, q < n ? op * 2 : kOob, ov);
     }
     if constexpr (!G::DB) __syncthreads();         // the buffer is restaged next
   }
@@ -571,7 +576,7 @@ hipError_t region_launch(RegionArgs a, int B, hipStream_t st) {
 using St1 = Rc<64, 32, 8, 8, 1, 5, BRA_DB_ST1>;
 using St2 = Rc<128, 128, 4, 4, 4, 5, false>;
 using St3 = Rc<256, 128, 2, 2, 16, 5, false>;
-using Dense = Rc<64, 32, 8, 8, 4, 5, BRA_DB_DENSE, 3>;
+using Dense = Rc<64, 32, 8, 8, 4, 5, BRA_DB_DENSE, 3, true>;
 
 }  // namespace
 
