@@ -568,12 +568,12 @@ hipError_t region_launch(RegionArgs a, int B, hipStream_t st) {
 // 512^2 segmentation shape (128^2 map, S = 16, top-k 4).  Four tasks per
 // unit: one head for the 8x8 regions, four heads for the 4x4 and 2x2 ones.
 #ifndef BRA_DB_ST1
-#define BRA_DB_ST1 true
+#define BRA_DB_ST1 false
 #endif
 #ifndef BRA_DB_DENSE
 #define BRA_DB_DENSE false
 #endif
-using St1 = Rc<64, 32, 8, 8, 1, 5, BRA_DB_ST1>;
+using St1 = Rc<64, 32, 8, 8, 1, 5, BRA_DB_ST1, 4>;
 using St2 = Rc<128, 128, 4, 4, 4, 5, false>;
 using St3 = Rc<256, 128, 2, 2, 16, 5, false>;
 using Dense = Rc<64, 32, 8, 8, 4, 5, BRA_DB_DENSE, 3, true>;
