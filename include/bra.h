@@ -223,6 +223,21 @@ bra_status bra_layer_norm(const void* x, int rows, int C, const float* gamma,
                           const float* beta, float eps, bra_dtype dtype,
                           void* y, void* stream);
 
+/* The block's MLP with its residual, one launch (p1 §2: a block is the BRA
+ * attention then a 2-layer MLP, each with a residual connection):
+ *   out = r + fc2(GELU(fc1(x))),  fc1 = x w1^T + b1,  fc2 = h w2^T + b2,
+ * with the hidden layer h = GELU(fc1(x)) rounded once to bf16, as the
+ * block stores it, but kept on chip; fc2, b2 and r are summed in float32
+ * and rounded once.
+ *   x, r, out [rows, C] bf16, device (out may be r, not x); w1 [Hd, C],
+ *   w2 [C, Hd] bf16; b1 [Hd], b2 [C] float32 or NULL; all 16-byte aligned.
+ *   Supported: dtype BRA_BF16, C in {64, 128, 256}, Hd a multiple of 32;
+ *   other valid sizes return BRA_E_UNSUPPORTED (bra_linear covers them in
+ *   two calls). */
+bra_status bra_mlp(const void* x, int rows, int C, int Hd, const void* w1,
+                   const float* b1, const void* w2, const float* b2,
+                   const void* r, bra_dtype dtype, void* out, void* stream);
+
 /* Parameters of one block: device pointers, float32 unless noted; weights
  * in the PyTorch Linear / depthwise Conv2d layouts, 16-byte aligned. */
 typedef struct {
@@ -248,7 +263,9 @@ typedef struct {
 /* Bytes of workspace bra_block_forward needs: x1, LN1(x1), x2, LN2(x2) as
  * [B,H,W,C] dtype each (256-byte aligned), then a module workspace with
  * output projection (bra_module_workspace_bytes(..., 1)), whose Q/K/V space
- * later holds the MLP's [B,H,W,3C] hidden tensor.  0 for invalid sizes. */
+ * later holds the MLP's [B,H,W,3C] hidden tensor where the MLP runs as two
+ * linear calls (where bra_mlp's one launch covers the shape, the hidden
+ * tensor is not written).  0 for invalid sizes. */
 size_t bra_block_workspace_bytes(int B, int H, int W, int C, int S,
                                  bra_dtype dtype);
 

@@ -21,7 +21,7 @@ const float* fp(uintptr_t a) { return reinterpret_cast<const float*>(a); }
 int32_t* ip(uintptr_t a) { return reinterpret_cast<int32_t*>(a); }
 
 const uintptr_t P = 0x10000, P2 = 0x20000000, P3 = 0x40000000, P4 = 0x60000000,
-                PO = 0x70000000, PW = 0x7A000000;
+                PO = 0x70000000, PW = 0x7A000000, P5 = 0x50000000;
 
 void expect(const char* what, bra_status got, bra_status want, const char* msg) {
   ++checked;
@@ -134,6 +134,22 @@ int main() {
                                   ptr(P4), nullptr), BRA_E_INVAL, "act");
   expect("linear big", bra_linear(ptr(P), 1 << 24, 64, ptr(P2), nullptr, 64, 0, nullptr,
                                   BRA_BF16, ptr(P4), nullptr), BRA_E_UNSUPPORTED, "2 GiB");
+
+  // bra_mlp
+  expect("mlp f32", bra_mlp(ptr(P), 100, 64, 192, ptr(P2), nullptr, ptr(P3), nullptr, ptr(P5),
+                            BRA_F32, ptr(P4), nullptr), BRA_E_UNSUPPORTED, "bf16 only");
+  expect("mlp C", bra_mlp(ptr(P), 100, 96, 288, ptr(P2), nullptr, ptr(P3), nullptr, ptr(P5),
+                          BRA_BF16, ptr(P4), nullptr), BRA_E_UNSUPPORTED, "C in");
+  expect("mlp Hd", bra_mlp(ptr(P), 100, 64, 100, ptr(P2), nullptr, ptr(P3), nullptr, ptr(P5),
+                           BRA_BF16, ptr(P4), nullptr), BRA_E_UNSUPPORTED, "Hd");
+  expect("mlp x null", bra_mlp(nullptr, 100, 64, 192, ptr(P2), nullptr, ptr(P3), nullptr, ptr(P5),
+                               BRA_BF16, ptr(P4), nullptr), BRA_E_INVAL, "x is NULL");
+  expect("mlp b1 align", bra_mlp(ptr(P), 100, 64, 192, ptr(P2), fp(P3 + 4), ptr(P3), nullptr,
+                                 ptr(P5), BRA_BF16, ptr(P4), nullptr), BRA_E_INVAL, "aligned");
+  expect("mlp overlap", bra_mlp(ptr(P), 100, 64, 192, ptr(P2), nullptr, ptr(P3), nullptr,
+                                ptr(P5), BRA_BF16, ptr(P + 64), nullptr), BRA_E_INVAL, "overlaps x");
+  expect("mlp big", bra_mlp(ptr(P), 1 << 24, 64, 192, ptr(P2), nullptr, ptr(P3), nullptr,
+                            ptr(P5), BRA_BF16, ptr(P4), nullptr), BRA_E_UNSUPPORTED, "2 GiB");
 
   // bra_module_forward
   expect("module w_qkv", bra_module_forward(ptr(P), 2, 8, 8, 64, 2, 2, 2, BRA_BF16, nullptr,

@@ -21,6 +21,10 @@ hipError_t launch_linear(const void*, int, int, const void*, const float*, int, 
                          bool, hipStream_t, int, const void*) {
   reached("launch_linear");
 }
+hipError_t launch_mlp(const void*, long long, int, int, const void*, const float*, const void*,
+                      const float*, const void*, void*, hipStream_t) {
+  reached("launch_mlp");
+}
 hipError_t launch_pos_conv(const void*, const float*, const float*, const Shape&, bool, void*,
                            hipStream_t) {
   reached("launch_pos_conv");

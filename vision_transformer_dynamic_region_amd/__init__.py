@@ -46,6 +46,7 @@ _SIGNATURES = {
     "bra_module_forward": (_i, [_vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _f, _f, _vp, _vp,
                                 _i, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "bra_layer_norm": (_i, [_vp, _i, _i, _vp, _vp, _f, _i, _vp, _vp]),
+    "bra_mlp": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp]),
     "bra_block_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "bra_block_forward": (_i, [_vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _f, _f, _vp, _vp, _vp,
                                _sz, _vp]),
@@ -401,6 +402,32 @@ def module_forward(x, w_qkv, b_qkv, heads: int, S: int, topk: int, lepe_w=None, 
                                      wp, bp, ks, wo, bo, out.data_ptr(), idx.data_ptr(),
                                      wsp, wsb, _stream(x)))
     return out, idx
+
+
+def mlp(x, w1, b1, w2, b2, residual, out=None):
+    """out = residual + fc2(GELU(fc1(x))) over the last axis in one launch
+    (bra_mlp, bf16): x, residual [..., C]; w1 [Hd, C] and w2 [C, Hd] in x's
+    dtype; b1 float32 [Hd] or None, b2 float32 [C] or None.  The hidden layer
+    is rounded to bf16 and never written.  Returns out [..., C]."""
+    import torch
+    dt = _dtype_code(x)
+    _dev(x, "x")
+    C = int(x.shape[-1])
+    _dev(w1, "w1", x.dtype)
+    if w1.dim() != 2 or w1.shape[1] != C:
+        raise ValueError("w1 must be [Hd, C] with C = x.shape[-1]")
+    Hd = int(w1.shape[0])
+    _dev(w2, "w2", x.dtype, (C, Hd))
+    _dev(residual, "residual", x.dtype, tuple(x.shape))
+    b1p = _opt(b1, "b1", torch.float32, (Hd,))
+    b2p = _opt(b2, "b2", torch.float32, (C,))
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, "out", x.dtype, tuple(x.shape))
+    _check(load().bra_mlp(x.data_ptr(), x.numel() // C, C, Hd, w1.data_ptr(), b1p,
+                          w2.data_ptr(), b2p, residual.data_ptr(), dt, out.data_ptr(),
+                          _stream(x)))
+    return out
 
 
 def layer_norm(x, gamma, beta, eps: float = 1e-5, out=None):

@@ -17,16 +17,18 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbra.so")
 SOURCES = ["route_kernels.hip", "attend_kernels.hip", "region_kernels.hip", "image_kernels.hip",
            "module_kernels.hip",
-           "block_kernels.hip", "backward_kernels.hip",
+           "block_kernels.hip", "mlp_kernels.hip", "backward_kernels.hip",
            "scratch.hip", "host_plan.cpp", "bra_api.cpp"]
-# per-file extra flags: the attention file assumes finite, non-NaN data (NaN
-# inputs give unspecified outputs) so that max/min need no NaN quieting, and
-# keeps MFMA accumulators in ordinary VGPRs next to the softmax arithmetic
+# per-file extra flags: the attention and MLP files assume finite, non-NaN
+# data (NaN inputs give unspecified outputs) so that max/min need no NaN
+# quieting, and keep MFMA accumulators in ordinary VGPRs next to the
+# softmax / GELU arithmetic
 EXTRA_FLAGS = {
     "attend_kernels.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "region_kernels.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "image_kernels.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
     "backward_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "mlp_kernels.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 ARCH = "gfx950"
 

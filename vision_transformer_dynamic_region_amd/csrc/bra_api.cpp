@@ -577,6 +577,29 @@ bra_status bra_layer_norm(const void* x, int rows, int C, const float* gamma, co
                     "layer norm launch");
 }
 
+bra_status bra_mlp(const void* x, int rows, int C, int Hd, const void* w1, const float* b1,
+                   const void* w2, const float* b2, const void* r, bra_dtype dtype, void* out,
+                   void* stream) {
+  g_last_error[0] = 0;
+  bra_status st;
+  if (dtype != BRA_F32 && dtype != BRA_BF16) return fail(BRA_E_INVAL, "dtype %d is not BRA_F32 or BRA_BF16", (int)dtype);
+  if (rows < 1 || C < 1 || Hd < 1) return fail(BRA_E_INVAL, "rows=%d C=%d Hd=%d must be positive", rows, C, Hd);
+  if ((st = check_tensor(x, "x")) || (st = check_tensor(w1, "w1")) || (st = check_tensor(w2, "w2")) ||
+      (st = check_tensor(r, "r")) || (st = check_tensor(out, "out")))
+    return st;
+  if ((b1 && !aligned16(b1)) || (b2 && !aligned16(b2))) return fail(BRA_E_INVAL, "b1 / b2 must be 16-byte aligned");
+  if (dtype != BRA_BF16) return fail(BRA_E_UNSUPPORTED, "the fused MLP is bf16 only (bra_linear covers float32)");
+  if ((C != 64 && C != 128 && C != 256) || Hd % 32)
+    return fail(BRA_E_UNSUPPORTED, "C=%d Hd=%d: the fused MLP needs C in {64, 128, 256} and Hd %% 32 == 0", C, Hd);
+  const size_t bytes = (size_t)rows * C * 2;
+  if (bytes >= ((size_t)1 << 31) || (size_t)Hd * C * 2 >= ((size_t)1 << 31))
+    return fail(BRA_E_UNSUPPORTED, "rows=%d C=%d Hd=%d: a tensor of 2 GiB or more", rows, C, Hd);
+  if (overlaps2(out, bytes, x, bytes)) return fail(BRA_E_INVAL, "out overlaps x");
+  if (overlaps2(out, bytes, r, bytes) && out != r) return fail(BRA_E_INVAL, "out overlaps r (other than in place)");
+  return hip_status(bra::launch_mlp(x, rows, C, Hd, w1, b1, w2, b2, r, out, (hipStream_t)stream),
+                    "mlp launch");
+}
+
 size_t bra_block_workspace_bytes(int B, int H, int W, int C, int S, bra_dtype dtype) {
   if (B < 1 || H < 1 || W < 1 || C < 1 || S < 1) return 0;
   if (dtype != BRA_F32 && dtype != BRA_BF16) return 0;
@@ -648,6 +671,12 @@ bra_status bra_block_forward(const void* x, int B, int H, int W, int C, int head
   if ((st = hip_status(bra::launch_layer_norm(x2, T, C, p->ln2_g, p->ln2_b, kLayerNormEps, bf16, n2, hs),
                        "layer norm launch")))
     return st;
+  // the MLP in one launch where the fused kernel covers the shape (bf16)
+  if (bf16) {
+    const hipError_t e = bra::launch_mlp(n2, T, C, 3 * C, p->w_fc1, p->b_fc1, p->w_fc2, p->b_fc2,
+                                         x2, out, hs);
+    if (e != hipErrorNotSupported) return hip_status(e, "mlp launch");
+  }
   void* h = mws + bl.ml.q;
   void* hv[1] = {h};
   if ((st = hip_status(bra::launch_linear(n2, T, C, p->w_fc1, p->b_fc1, 3 * C, hv, 1, bf16, hs, 1),

@@ -39,6 +39,15 @@ hipError_t launch_linear(const void* x, int T, int K, const void* w, const float
                          void* const* y, int groups, bool bf16, hipStream_t st, int epi = 0,
                          const void* resid = nullptr);
 
+// out = resid + fc2(GELU(fc1(x))) in bf16 in one launch (the hidden layer
+// [T, Hd] rounded once to bf16, never written): x, resid, out [T, C], w1
+// [Hd, C], w2 [C, Hd], b1 [Hd] / b2 [C] float32 or null.  C in {64, 128,
+// 256}, Hd % 32 == 0; hipErrorNotSupported otherwise, before anything is
+// enqueued.
+hipError_t launch_mlp(const void* x, long long T, int C, int Hd, const void* w1, const float* b1,
+                      const void* w2, const float* b2, const void* resid, void* out,
+                      hipStream_t st);
+
 // out = x + b + depthwise 3x3 cross-correlation of x (w [C, 3, 3], zero
 // padding 1), [B, H, W, C].
 hipError_t launch_pos_conv(const void* x, const float* w, const float* b, const Shape& s,

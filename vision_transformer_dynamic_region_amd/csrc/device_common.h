@@ -48,6 +48,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // Butterfly partners across lane rows without LDS traffic (gfx950
 // v_permlane16_swap / v_permlane32_swap): the value of lane l ^ 16 and of
 // lane l ^ 32.
+// GELU in its exact form, x Phi(x) = x/2 (1 + erf(x / sqrt 2)), with erf by
+// Abramowitz & Stegun 7.1.26 (absolute error below 1.5e-7): for z >= 0,
+// erfc(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 +
+// p z).  Since 1 + erf(z) is 2 - erfc(z) for z >= 0 and erfc(-z) below,
+// x Phi(x) = max(x, 0) - |x|/2 erfc(|x| / sqrt 2) for either sign; the 1/2
+// is folded into the a_i and 1/sqrt 2 into p and the exponent.
+__device__ __forceinline__ float gelu_as(float v) {
+  const float av = fabsf(v);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, av, 1.0f));
+  float pz = fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f);
+  pz = fmaf(t, pz, 0.5f * 1.421413741f);
+  pz = fmaf(t, pz, 0.5f * -0.284496736f);
+  pz = fmaf(t, pz, 0.5f * 0.254829592f);
+  // exp(-v^2 / 2) = 2^(v^2 * -log2(e) / 2)
+  const float e = __builtin_amdgcn_exp2f(v * v * -0.72134752044448170f);
+  return fmaf(-av, (t * pz) * e, fmaxf(v, 0.f));
+}
+
 __device__ __forceinline__ float xor16(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return (threadIdx.x & 16) ? __uint_as_float(r[0]) : __uint_as_float(r[1]);

@@ -62,20 +62,7 @@ struct LinArgs {
 // 128-byte line of a token's features is written by 8 adjacent lanes in one
 // store.  Epilogue EPI: 0 bias only, 1 bias then GELU (exact erf form), 2
 // bias then a residual tensor added; each rounds once to the output type.
-// GELU in its exact form, x Phi(x) = x/2 (1 + erf(x / sqrt 2)), with erf by
-// Abramowitz & Stegun 7.1.26 (absolute error below 1.5e-7): for z >= 0,
-// erfc(z) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-z^2), t = 1 / (1 +
-// p z); 1 + erf(z) is 2 - erfc(z) for z >= 0 and erfc(-z) below.
-__device__ __forceinline__ float gelu_as(float v) {
-  const float z = v * 0.70710678118654752f, az = fabsf(z);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, az, 1.0f));
-  float pz = fmaf(t, 1.061405429f, -1.453152027f);
-  pz = fmaf(t, pz, 1.421413741f);
-  pz = fmaf(t, pz, -0.284496736f);
-  pz = fmaf(t, pz, 0.254829592f);
-  const float ec = t * pz * __builtin_amdgcn_exp2f(-az * az * 1.4426950408889634f);
-  return 0.5f * v * (z >= 0.f ? 2.0f - ec : ec);
-}
+// GELU: gelu_as in device_common.h.
 
 template <int EPI>
 __device__ __forceinline__ float lin_act(float v) {
