@@ -25,8 +25,14 @@ hipError_t launch_mlp(const void*, long long, int, int, const void*, const float
                       const float*, const void*, void*, hipStream_t) {
   reached("launch_mlp");
 }
+hipError_t launch_block_tail(const void*, const void*, long long, int, int, const void*,
+                             const float*, const float*, const float*, float, const void*,
+                             const float*, const void*, const float*, void*, void*, void*,
+                             hipStream_t) {
+  reached("launch_block_tail");
+}
 hipError_t launch_pos_conv(const void*, const float*, const float*, const Shape&, bool, void*,
-                           hipStream_t) {
+                           hipStream_t, const float*, const float*, float, void*) {
   reached("launch_pos_conv");
 }
 hipError_t launch_backward(const void*, const void*, const void*, const int32_t*, const void*,

@@ -196,6 +196,8 @@ def test_block_parity(cuda, name):
         print(f"[block] {name} {nm}: err/RMS over one ulp "
               f"{excess_err(got[nm], ref[nm].reshape(-1), dt, stored=True):.2e}", flush=True)
     assert_close(got["x1"], ref["x1"].reshape(-1), dt, f"{name} x1", stored=True)
+    # LN1(x1), in the position conv's launch where the block fuses them
+    assert_close(got["n1"], ref["n1"].reshape(-1), dt, f"{name} n1", stored=True)
     e = assert_close(to_host(out), ref["out"], dt, f"{name} out", stored=True, tol=BLOCK_TOL[dt])
     print(f"[block] {name}: {int((~same).sum())} region rows routed differently within the "
           f"bound; out err/RMS over one ulp {e:.2e} on every token", flush=True)

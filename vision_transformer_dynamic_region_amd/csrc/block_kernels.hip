@@ -8,6 +8,8 @@
 
 #include "device_common.h"
 
+#include <type_traits>
+
 namespace bra {
 namespace {
 
@@ -34,6 +36,11 @@ struct PosArgs {
   const float* w;       // [C, 3, 3]
   const float* b;       // [C] or null
   void* out;
+  // LN: out's LayerNorm as well (gamma lng, beta lnb, eps) into nout
+  const float* lng;
+  const float* lnb;
+  float eps;
+  void* nout;
   int H, W, C, G;       // G = 16-byte groups per pixel
   int row_items;        // W * G
   int sr;               // rows a strip (a multiple of 3)
@@ -42,8 +49,31 @@ struct PosArgs {
 
 typedef uint32_t pos_u32x4 __attribute__((ext_vector_type(4)));
 
-template <bool BF16>
+// Sum over aligned groups of GL consecutive lanes: DPP lane moves within
+// rows of 16 (xor 1, xor 2, then the mirrored half of 8 and of 16, each
+// pairing every lane with one of the other half), lane swaps across rows.
+template <int GL>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  auto dpp = [](float x, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  if constexpr (GL > 1) v += dpp(v, std::integral_constant<int, 0xB1>());   // quad_perm 1,0,3,2
+  if constexpr (GL > 2) v += dpp(v, std::integral_constant<int, 0x4E>());   // quad_perm 2,3,0,1
+  if constexpr (GL > 4) v += dpp(v, std::integral_constant<int, 0x141>());  // row_half_mirror
+  if constexpr (GL > 8) v += dpp(v, std::integral_constant<int, 0x140>());  // row_mirror
+  if constexpr (GL > 16) v += xor16(v);
+  if constexpr (GL > 32) v += xor32(v);
+  return v;
+}
+
+// With GL > 0 (LN), the LayerNorm of each output pixel too (the block's LN1
+// of x1): a pixel's G = GL groups are GL consecutive lanes, so its float32
+// statistics of the rounded x1 (mean, then the biased variance around it,
+// as layer_norm_kernel) are lane sums; one rounding.
+template <bool BF16, int GL>
 __global__ __launch_bounds__(kThreads) void pos_conv_kernel(PosArgs a) {
+  constexpr bool LN = GL > 0;
   constexpr int VEC = BF16 ? 8 : 4;
   const int t = blockIdx.x * kThreads + threadIdx.x;
   if (t >= a.row_items) return;
@@ -54,7 +84,8 @@ __global__ __launch_bounds__(kThreads) void pos_conv_kernel(PosArgs a) {
       const_cast<void*>((const void*)((const uint4*)a.x + (size_t)b * a.H * a.row_items)), (short)0,
       (int)img_bytes, 0x00020000);
   uint4* O = (uint4*)a.out + (size_t)b * a.H * a.row_items;
-  float wt[VEC][9], bias[VEC];
+  uint4* NO = LN ? (uint4*)a.nout + (size_t)b * a.H * a.row_items : nullptr;
+  float wt[VEC][9], bias[VEC], lg_[VEC], lb_[VEC];
   {
     const float4* wp = (const float4*)(a.w + g * VEC * 9);   // VEC * 9 contiguous floats
 #pragma unroll
@@ -66,6 +97,13 @@ __global__ __launch_bounds__(kThreads) void pos_conv_kernel(PosArgs a) {
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) bias[e] = a.b ? a.b[g * VEC + e] : 0.f;
+    if constexpr (LN) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        lg_[e] = a.lng[g * VEC + e];
+        lb_[e] = a.lnb[g * VEC + e];
+      }
+    }
   }
   const bool colok[3] = {xq > 0, true, xq + 1 < a.W};
   // vector at (y, x + c - 1), zero outside the image
@@ -115,6 +153,40 @@ __global__ __launch_bounds__(kThreads) void pos_conv_kernel(PosArgs a) {
                        __float_as_uint(acc[3]));
       }
       if (y < y1) O[y * a.row_items + t] = o;
+      if constexpr (LN) {
+        float xr[VEC];
+        if constexpr (BF16) {
+          unpack16<true>(o, xr);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) xr[e] = acc[e];
+        }
+        float sm = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) sm += xr[e];
+        sm = lane_group_sum<GL>(sm);
+        const float mean = sm / (float)a.C;
+        float q = 0.f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float d = xr[e] - mean;
+          q = fmaf(d, d, q);
+        }
+        q = lane_group_sum<GL>(q);
+        const float rstd = 1.0f / sqrtf(q / (float)a.C + a.eps);
+        float nv[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) nv[e] = (xr[e] - mean) * rstd * lg_[e] + lb_[e];
+        uint4 n;
+        if constexpr (BF16) {
+          n = make_uint4(pack_bf16x2(nv[0], nv[1]), pack_bf16x2(nv[2], nv[3]),
+                         pack_bf16x2(nv[4], nv[5]), pack_bf16x2(nv[6], nv[7]));
+        } else {
+          n = make_uint4(__float_as_uint(nv[0]), __float_as_uint(nv[1]), __float_as_uint(nv[2]),
+                         __float_as_uint(nv[3]));
+        }
+        if (y < y1) NO[y * a.row_items + t] = n;
+      }
     }
   }
 }
@@ -184,9 +256,11 @@ __global__ __launch_bounds__(kThreads) void layer_norm_kernel(NormArgs a) {
 }  // namespace
 
 hipError_t launch_pos_conv(const void* x, const float* w, const float* b, const Shape& s,
-                           bool bf16, void* out, hipStream_t st) {
+                           bool bf16, void* out, hipStream_t st, const float* ln_g,
+                           const float* ln_b, float eps, void* nout) {
   PosArgs a;
   a.x = x; a.w = w; a.b = b; a.out = out;
+  a.lng = ln_g; a.lnb = ln_b; a.eps = eps; a.nout = nout;
   a.H = s.H; a.W = s.W; a.C = s.C;
   a.G = s.C / (bf16 ? 8 : 4);
   a.row_items = s.W * a.G;
@@ -199,10 +273,25 @@ hipError_t launch_pos_conv(const void* x, const float* w, const float* b, const 
   while (a.sr < s.H && per_strip * ((s.H + a.sr - 1) / a.sr) > kPosWaves) a.sr += 3;
   const dim3 grid((unsigned)((a.row_items + kThreads - 1) / kThreads),
                   (unsigned)((s.H + a.sr - 1) / a.sr), (unsigned)s.B);
+  if (nout) {
+    // a pixel's groups share one 64-lane wavefront: G a power of two, 4..64
+    if (!ln_g || !ln_b) return hipErrorNotSupported;
+#define BRA_POS_LN(GG)                                                              \
+    if (a.G == GG) {                                                                \
+      if (bf16)                                                                     \
+        hipLaunchKernelGGL((pos_conv_kernel<true, GG>), grid, dim3(kThreads), 0, st, a);  \
+      else                                                                          \
+        hipLaunchKernelGGL((pos_conv_kernel<false, GG>), grid, dim3(kThreads), 0, st, a); \
+      return hipGetLastError();                                                     \
+    }
+    BRA_POS_LN(4) BRA_POS_LN(8) BRA_POS_LN(16) BRA_POS_LN(32) BRA_POS_LN(64)
+#undef BRA_POS_LN
+    return hipErrorNotSupported;
+  }
   if (bf16)
-    hipLaunchKernelGGL(pos_conv_kernel<true>, grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((pos_conv_kernel<true, 0>), grid, dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(pos_conv_kernel<false>, grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((pos_conv_kernel<false, 0>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

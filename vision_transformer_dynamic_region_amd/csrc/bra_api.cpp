@@ -659,11 +659,35 @@ bra_status bra_block_forward(const void* x, int B, int H, int W, int C, int head
   unsigned char* mws = w8 + bl.mod;
   const int T = B * H * W;
   // x1 = x + pos conv;  x2 = x1 + module(LN1(x1))
-  if ((st = hip_status(bra::launch_pos_conv(x, p->pos_w, p->pos_b, s, bf16, x1, hs), "position conv launch")))
-    return st;
-  if ((st = hip_status(bra::launch_layer_norm(x1, T, C, p->ln1_g, p->ln1_b, kLayerNormEps, bf16, n1, hs),
-                       "layer norm launch")))
-    return st;
+  // x1 and LN1(x1) in one launch where the pixel's channel groups fit a
+  // wavefront, else two
+  const hipError_t pe = bra::launch_pos_conv(x, p->pos_w, p->pos_b, s, bf16, x1, hs, p->ln1_g,
+                                             p->ln1_b, kLayerNormEps, n1);
+  if (pe != hipErrorNotSupported) {
+    if ((st = hip_status(pe, "position conv launch"))) return st;
+  } else {
+    if ((st = hip_status(bra::launch_pos_conv(x, p->pos_w, p->pos_b, s, bf16, x1, hs),
+                         "position conv launch")))
+      return st;
+    if ((st = hip_status(bra::launch_layer_norm(x1, T, C, p->ln1_g, p->ln1_b, kLayerNormEps, bf16,
+                                                n1, hs),
+                         "layer norm launch")))
+      return st;
+  }
+  // bf16 at C <= 128: the module without its output projection (y, the
+  // attention output, into the module workspace), then the output
+  // projection, LN2 and the MLP in one launch (x2 and n2 still stored)
+  if (bf16 && (C == 64 || C == 128)) {
+    void* y = mws + bl.ml.y;
+    if ((st = module_launches(n1, s, dtype, p->w_qkv, p->b_qkv, route_scale, attn_scale,
+                              p->lepe_w, p->lepe_b, p->lepe_ks, nullptr, nullptr, nullptr, y, idx,
+                              mws, bl.ml, hs)))
+      return st;
+    const hipError_t e = bra::launch_block_tail(y, x1, T, C, 3 * C, p->w_out, p->b_out, p->ln2_g,
+                                                p->ln2_b, kLayerNormEps, p->w_fc1, p->b_fc1,
+                                                p->w_fc2, p->b_fc2, x2, n2, out, hs);
+    return hip_status(e, "block tail launch");
+  }
   if ((st = module_launches(n1, s, dtype, p->w_qkv, p->b_qkv, route_scale, attn_scale, p->lepe_w,
                             p->lepe_b, p->lepe_ks, p->w_out, p->b_out, x1, x2, idx, mws, bl.ml, hs)))
     return st;

@@ -48,10 +48,25 @@ hipError_t launch_mlp(const void* x, long long T, int C, int Hd, const void* w1,
                       const void* w2, const float* b2, const void* resid, void* out,
                       hipStream_t st);
 
+// The block's last three layers in one launch (bf16): x2 = x1 + y w_out^T
+// + b_out and n2 = LN2(x2) (eps; gamma ln_g, beta ln_b), each rounded once
+// to bf16 and written to x2 / n2 when those are not null, then out = x2 +
+// fc2(GELU(fc1(n2))) as launch_mlp.  C in {64, 128}, Hd % 32 == 0;
+// hipErrorNotSupported otherwise, before anything is enqueued.
+hipError_t launch_block_tail(const void* y, const void* x1, long long T, int C, int Hd,
+                             const void* w_out, const float* b_out, const float* ln_g,
+                             const float* ln_b, float eps, const void* w1, const float* b1,
+                             const void* w2, const float* b2, void* x2, void* n2, void* out,
+                             hipStream_t st);
+
 // out = x + b + depthwise 3x3 cross-correlation of x (w [C, 3, 3], zero
 // padding 1), [B, H, W, C].
+// With nout, also nout = LayerNorm(out) (gamma ln_g, beta ln_b, eps; out
+// rounded first, one rounding) where a pixel's 16-byte groups are a power
+// of two up to 64; hipErrorNotSupported (nothing enqueued) otherwise.
 hipError_t launch_pos_conv(const void* x, const float* w, const float* b, const Shape& s,
-                           bool bf16, void* out, hipStream_t st);
+                           bool bf16, void* out, hipStream_t st, const float* ln_g = nullptr,
+                           const float* ln_b = nullptr, float eps = 0.f, void* nout = nullptr);
 
 // Backward pass with a fixed routing index (bf16, head width 32, topk * n
 // <= 256): dq, dk, dv (bf16, dV with the LePE term when w is not null) and

@@ -24,9 +24,22 @@
 //        is permuted to match (slot 8lg + e holds hidden 4lg + e for e < 4,
 //        16 + 4lg + e - 4 above) and W2's columns are staged in that order,
 //        so H^T becomes fc2's B operand without moving.
-// Epilogue: lanes lg, lg^1 trade fp32 halves of two output tiles
-// (v_permlane16_swap), so each holds 8 consecutive channels of one token;
-// + b2 + r in fp32, one rounding, 16-byte stores.
+// Epilogue: + b2 + r in fp32 in the MFMA layout (a lane holds channels
+// 16o + 4lg .. +3 of one token for each 16-channel tile o); lanes lg, lg^1
+// then trade halves of two tiles (v_permlane16_swap), so each holds 8
+// consecutive channels; one rounding, 16-byte stores.
+//
+// Block-tail form (TAIL): the block's last three layers in the same launch,
+//   x2 = x1 + y W_out^T + b_out,  n2 = LN2(x2),  out = x2 + MLP(n2),
+// x2 and n2 rounded to bf16 as the block stores them (and written to the
+// block's workspace), with y the BRA module's attention output.  W_out is
+// staged in LDS; the output projection on the MFMAs leaves a lane with 4C/16
+// channels of one token (tiles o, rows 4lg..4lg+3), so LN2's statistics are
+// a lane sum and two lane swaps, and n2 becomes fc1's B operand directly:
+// fc1's k order is permuted as fc2's is (slot 8lg + e of k step s holds
+// channel 32s + 4lg + e for e < 4, 32s + 16 + 4lg + e - 4 above) and W1's
+// columns are staged in that order.  x2 stays in registers as the MLP's
+// residual.
 
 #include "device_common.h"
 
@@ -34,6 +47,9 @@ namespace bra {
 namespace {
 
 constexpr uint32_t kMlpOob = 0x80000000u;
+#ifndef BRA_TAIL_TW64
+#define BRA_TAIL_TW64 16
+#endif
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -57,13 +73,21 @@ struct Mg {
 };
 
 struct MlpArgs {
-  const uint16_t* x;     // [T, C]
+  const uint16_t* x;     // [T, C]: the MLP's input (TAIL: y, the attention output)
   const uint16_t* w1;    // [Hd, C]
   const float* b1;       // [Hd] or null
   const uint16_t* w2;    // [C, Hd]
   const float* b2;       // [C] or null
-  const uint16_t* r;     // residual [T, C]
+  const uint16_t* r;     // residual [T, C] (TAIL: x1, the output projection's)
   uint16_t* out;         // [T, C]
+  // TAIL only
+  const uint16_t* wo;    // [C, C] output projection
+  const float* bo;       // [C] or null
+  const float* lng;      // [C] LN2 gamma
+  const float* lnb;      // [C] LN2 beta
+  float eps;
+  uint16_t* x2;          // [T, C] or null: x2 stored
+  uint16_t* n2;          // [T, C] or null: LN2(x2) stored
   int T, Hd;
 };
 
@@ -83,12 +107,26 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <class G>
+// LDS layout: two chunk buffers [W1 32 x C | W2 C x 32 | b1 32], then b2
+// [C]; TAIL adds b_out, gamma, beta [C] each and W_out [C x C].
+template <class G, bool TAIL>
+struct MlpLds {
+  static constexpr int C = G::C;
+  static constexpr int B2 = 2 * G::BUF;
+  static constexpr int BO = B2 + C * 4;
+  static constexpr int LG = BO + C * 4;
+  static constexpr int LB = LG + C * 4;
+  static constexpr int WO = LB + C * 4;
+  static constexpr int BYTES = TAIL ? WO + C * C * 2 : BO;
+};
+
+template <class G, bool TAIL>
 __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs A) {
   constexpr int C = G::C, NB = G::NB, KS = G::KS, OT = G::OT, N1 = G::N1, N2 = G::N2;
   constexpr int SH = G::SH, MSK = G::MSK;
+  using L = MlpLds<G, TAIL>;
   extern __shared__ __align__(16) unsigned char lds[];
-  float* b2s = (float*)(lds + 2 * G::BUF);        // [C]
+  float* b2s = (float*)(lds + L::B2);              // [C]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lq = lane & 15, lg = lane >> 4;
@@ -100,25 +138,123 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs A) {
   const auto Or = mlp_rsrc(A.out, tbytes);
   const auto W1r = mlp_rsrc(A.w1, (uint32_t)Hd * C * 2);
   const auto W2r = mlp_rsrc(A.w2, (uint32_t)C * Hd * 2);
+  // this lane's token of column block nb, and the byte offset of its
+  // channels 16o + 4lg .. +3 (the MFMA output layout)
+  auto tok = [&](int nb) { return tok0 + 16 * nb + lq; };
+  auto moff = [&](int nb, int o) -> uint32_t {
+    return tok(nb) < T ? (uint32_t)(tok(nb) * C + 16 * o + 4 * lg) * 2 : kMlpOob;
+  };
 
-  // X^T operands: token tok0 + 16 nb + lq, channels 32 s + 8 lg .. +7
+  // the input's operands in natural channel order: lane (lq, lg) holds
+  // channels 32 s + 8 lg .. +7 of token tok(nb)
   bf16x8 xo[NB][KS];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int t = tok0 + 16 * nb + lq;
+  for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const uint32_t off = t < T ? (uint32_t)(t * C + 32 * s + 8 * lg) * 2 : kMlpOob;
+      const uint32_t off = tok(nb) < T ? (uint32_t)(tok(nb) * C + 32 * s + 8 * lg) * 2 : kMlpOob;
       xo[nb][s] = __builtin_bit_cast(bf16x8, mload16(Xr, off));
     }
-  }
+  // the residual of the MLP in the MFMA output layout, as bf16 pairs (TAIL:
+  // x2, computed below; else loaded for the epilogue)
+  uint2 res[NB][OT];
   for (int c = tid; c < C; c += kThreads) b2s[c] = A.b2 ? A.b2[c] : 0.f;
 
-  // staging of hidden chunk j: W1 rows j*32 .. j*32+31 (chunk c of row r at
-  // c ^ ((r >> SH) & MSK)); W2 columns j*32 .. +31 of every row o, 16-byte
-  // chunk g holding hidden 4g..4g+3 and 16+4g..16+4g+3 of the chunk (the
-  // permuted k order of fc2), at g ^ ((o >> 2) & 3); b1 of the chunk
-  uint4 p1[N1];
+  if constexpr (TAIL) {
+    // ---- x2 = x1 + y W_out^T + b_out, rounded; n2 = LN2(x2), rounded ----
+    float* bos = (float*)(lds + L::BO);
+    float* lgs = (float*)(lds + L::LG);
+    float* lbs = (float*)(lds + L::LB);
+    uint16_t* Wos = (uint16_t*)(lds + L::WO);
+    const auto Wor = mlp_rsrc(A.wo, (uint32_t)C * C * 2);
+    for (int e = tid; e < C * C / 8; e += kThreads) {
+      const int r = e / (C / 8), c = e % (C / 8);
+      *(uint4*)(Wos + r * C + ((c ^ ((r >> SH) & MSK)) << 3)) = mload16(Wor, (uint32_t)e * 16);
+    }
+    for (int c = tid; c < C; c += kThreads) {
+      bos[c] = A.bo ? A.bo[c] : 0.f;
+      lgs[c] = A.lng[c];
+      lbs[c] = A.lnb[c];
+    }
+    uint2 x1v[NB][OT];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int o = 0; o < OT; ++o) x1v[nb][o] = mload8(Rr, moff(nb, o));
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float v[OT][4];
+#pragma unroll
+      for (int o = 0; o < OT; ++o) {
+        const float4 bo4 = *(const float4*)(bos + 16 * o + 4 * lg);
+        f32x4 a = {bo4.x, bo4.y, bo4.z, bo4.w};
+        const int row = 16 * o + lq;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const int c = 4 * s + lg;
+          const bf16x8 w = *(const bf16x8*)(Wos + row * C + ((c ^ ((row >> SH) & MSK)) << 3));
+          a = mfma16(w, xo[nb][s], a);
+        }
+        // + x1, one rounding: the stored x2
+        const uint32_t p0 = pack_bf16x2(a[0] + bf16_lo(x1v[nb][o].x), a[1] + bf16_hi(x1v[nb][o].x));
+        const uint32_t p1 = pack_bf16x2(a[2] + bf16_lo(x1v[nb][o].y), a[3] + bf16_hi(x1v[nb][o].y));
+        res[nb][o] = make_uint2(p0, p1);
+        v[o][0] = bf16_lo(p0); v[o][1] = bf16_hi(p0);
+        v[o][2] = bf16_lo(p1); v[o][3] = bf16_hi(p1);
+        if (A.x2) {
+          const u32x2 st = {p0, p1};
+          __builtin_amdgcn_raw_buffer_store_b64(st, mlp_rsrc(A.x2, tbytes), moff(nb, o), 0, 0);
+        }
+      }
+      // LN2 over the token's C channels: 4C/16 a lane, the 4 lanes of one
+      // token (lg) combined by two lane swaps; float32, two passes
+      float sm = 0.f;
+#pragma unroll
+      for (int o = 0; o < OT; ++o) sm += (v[o][0] + v[o][1]) + (v[o][2] + v[o][3]);
+      sm += xor16(sm);
+      sm += xor32(sm);
+      const float mean = sm / (float)C;
+      float sq = 0.f;
+#pragma unroll
+      for (int o = 0; o < OT; ++o)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float d = v[o][e] - mean;
+          sq = fmaf(d, d, sq);
+        }
+      sq += xor16(sq);
+      sq += xor32(sq);
+      const float rstd = 1.0f / sqrtf(sq / (float)C + A.eps);
+      uint32_t np[OT][2];
+#pragma unroll
+      for (int o = 0; o < OT; ++o) {
+        const float4 g4 = *(const float4*)(lgs + 16 * o + 4 * lg);
+        const float4 b4 = *(const float4*)(lbs + 16 * o + 4 * lg);
+        np[o][0] = pack_bf16x2((v[o][0] - mean) * rstd * g4.x + b4.x,
+                               (v[o][1] - mean) * rstd * g4.y + b4.y);
+        np[o][1] = pack_bf16x2((v[o][2] - mean) * rstd * g4.z + b4.z,
+                               (v[o][3] - mean) * rstd * g4.w + b4.w);
+        if (A.n2) {
+          const u32x2 st = {np[o][0], np[o][1]};
+          __builtin_amdgcn_raw_buffer_store_b64(st, mlp_rsrc(A.n2, tbytes), moff(nb, o), 0, 0);
+        }
+      }
+      // fc1's B operands in the permuted k order: step s takes tiles 2s, 2s+1
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        xo[nb][s] = __builtin_bit_cast(
+            bf16x8, make_uint4(np[2 * s][0], np[2 * s][1], np[2 * s + 1][0], np[2 * s + 1][1]));
+    }
+  }
+
+  // staging of hidden chunk j: W1 rows j*32 .. j*32+31, 16-byte chunk c of
+  // row r at c ^ ((r >> SH) & MSK), holding columns 8c .. 8c+7 (TAIL: columns
+  // 32s + 4g .. +3 and 32s + 16 + 4g .. +3 for c = 4s + g, fc1's permuted k
+  // order); W2 columns j*32 .. +31 of every row o, 16-byte chunk g holding
+  // hidden 4g..4g+3 and 16+4g..16+4g+3 of the chunk (fc2's permuted k
+  // order), at g ^ ((o >> 2) & 3); b1 of the chunk
+  uint2 p1a[N1], p1b[N1];
   uint2 p2a[N2], p2b[N2];
   float pb1 = 0.f;
   auto prefetch = [&](int j) {
@@ -126,7 +262,11 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs A) {
     for (int i = 0; i < N1; ++i) {
       const int e = i * kThreads + tid;
       const int r = e / (C / 8), c = e % (C / 8);
-      p1[i] = mload16(W1r, e < G::W1E ? (uint32_t)((j * 32 + r) * C + 8 * c) * 2 : kMlpOob);
+      const int ca = TAIL ? 32 * (c >> 2) + 4 * (c & 3) : 8 * c;
+      const int cb = TAIL ? ca + 16 : ca + 4;
+      const uint32_t row = (uint32_t)(j * 32 + r) * C;
+      p1a[i] = mload8(W1r, e < G::W1E ? (row + ca) * 2 : kMlpOob);
+      p1b[i] = mload8(W1r, e < G::W1E ? (row + cb) * 2 : kMlpOob);
     }
 #pragma unroll
     for (int i = 0; i < N2; ++i) {
@@ -148,7 +288,8 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs A) {
       const int e = i * kThreads + tid;
       if (e < G::W1E) {
         const int r = e / (C / 8), c = e % (C / 8);
-        *(uint4*)(W1s + r * C + ((c ^ ((r >> SH) & MSK)) << 3)) = p1[i];
+        *(uint4*)(W1s + r * C + ((c ^ ((r >> SH) & MSK)) << 3)) =
+            make_uint4(p1a[i].x, p1a[i].y, p1b[i].x, p1b[i].y);
       }
     }
 #pragma unroll
@@ -223,54 +364,68 @@ __global__ __launch_bounds__(kThreads) void mlp_kernel(MlpArgs A) {
     __syncthreads();
   }
 
-  // ---- epilogue: lanes lg, lg^1 trade halves of output tiles 2m, 2m+1 ----
+  // ---- epilogue: + b2 + residual in the MFMA layout, then lanes lg, lg^1
+  // trade halves of output tiles 2m, 2m+1 ----
+  if constexpr (!TAIL) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int o = 0; o < OT; ++o) res[nb][o] = mload8(Rr, moff(nb, o));
+  }
   const bool odd = lg & 1;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int t = tok0 + 16 * nb + lq;
 #pragma unroll
     for (int m = 0; m < OT / 2; ++m) {
-      const f32x4 f0 = acc[nb][2 * m], f1 = acc[nb][2 * m + 1];
+      float f[2][4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int o = 2 * m + q;
+        const float4 b4 = *(const float4*)(b2s + 16 * o + 4 * lg);
+        f[q][0] = acc[nb][o][0] + b4.x + bf16_lo(res[nb][o].x);
+        f[q][1] = acc[nb][o][1] + b4.y + bf16_hi(res[nb][o].x);
+        f[q][2] = acc[nb][o][2] + b4.z + bf16_lo(res[nb][o].y);
+        f[q][3] = acc[nb][o][3] + b4.w + bf16_hi(res[nb][o].y);
+      }
       float v[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(f0[e]),
-                                                         __float_as_uint(f1[e]), false, false);
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(f[0][e]),
+                                                         __float_as_uint(f[1][e]), false, false);
         // even rows: channels 4lg .. 4lg+7 of the pair; odd rows: 16 + 4(lg-1) .. +7
         if (odd) {
           v[e] = __uint_as_float(sw[0]);
-          v[4 + e] = f1[e];
+          v[4 + e] = f[1][e];
         } else {
-          v[e] = f0[e];
+          v[e] = f[0][e];
           v[4 + e] = __uint_as_float(sw[1]);
         }
       }
       const int ch = 32 * m + (odd ? 16 + 4 * (lg - 1) : 4 * lg);
-      const uint32_t off = t < T ? (uint32_t)(t * C + ch) * 2 : kMlpOob;
-      const uint4 rv = mload16(Rr, off);
-      const uint32_t ru[4] = {rv.x, rv.y, rv.z, rv.w};
-      uint32_t ov[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a0 = v[2 * q] + b2s[ch + 2 * q] + bf16_lo(ru[q]);
-        const float a1 = v[2 * q + 1] + b2s[ch + 2 * q + 1] + bf16_hi(ru[q]);
-        ov[q] = pack_bf16x2(a0, a1);
-      }
-      const u32x4 x = {ov[0], ov[1], ov[2], ov[3]};
+      const uint32_t off = tok(nb) < T ? (uint32_t)(tok(nb) * C + ch) * 2 : kMlpOob;
+      const u32x4 x = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                       pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
       __builtin_amdgcn_raw_buffer_store_b128(x, Or, off, 0, 0);
     }
   }
 }
 
-template <class G>
+template <class G, bool TAIL>
 hipError_t mlp_launch(const MlpArgs& a, hipStream_t st) {
-  const size_t lds = 2 * (size_t)G::BUF + (size_t)G::C * 4;
-  const void* fn = reinterpret_cast<const void*>(&mlp_kernel<G>);
+  const size_t lds = MlpLds<G, TAIL>::BYTES;
+  const void* fn = reinterpret_cast<const void*>(&mlp_kernel<G, TAIL>);
   const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const long long groups = ((long long)a.T + G::TOK - 1) / G::TOK;
-  hipLaunchKernelGGL(mlp_kernel<G>, dim3((unsigned)groups), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((mlp_kernel<G, TAIL>), dim3((unsigned)groups), dim3(kThreads), lds, st, a);
   return hipGetLastError();
+}
+
+bool mlp_shape_ok(long long T, int C, int Hd) {
+  if (T <= 0 || Hd <= 0 || Hd % 32) return false;
+  if (C != 64 && C != 128 && C != 256) return false;
+  // buffer offsets are 32-bit
+  return T * C * 2 < (long long)kMlpOob && (long long)Hd * C * 2 < (long long)kMlpOob;
 }
 
 }  // namespace
@@ -278,18 +433,31 @@ hipError_t mlp_launch(const MlpArgs& a, hipStream_t st) {
 hipError_t launch_mlp(const void* x, long long T, int C, int Hd, const void* w1, const float* b1,
                       const void* w2, const float* b2, const void* resid, void* out,
                       hipStream_t st) {
-  if (T <= 0 || Hd <= 0 || Hd % 32) return hipErrorNotSupported;
-  if (C != 64 && C != 128 && C != 256) return hipErrorNotSupported;
-  // buffer offsets are 32-bit
-  if (T * C * 2 >= (long long)kMlpOob || (long long)Hd * C * 2 >= (long long)kMlpOob)
-    return hipErrorNotSupported;
-  MlpArgs a;
+  if (!mlp_shape_ok(T, C, Hd)) return hipErrorNotSupported;
+  MlpArgs a = {};
   a.x = (const uint16_t*)x; a.w1 = (const uint16_t*)w1; a.b1 = b1;
   a.w2 = (const uint16_t*)w2; a.b2 = b2; a.r = (const uint16_t*)resid; a.out = (uint16_t*)out;
   a.T = (int)T; a.Hd = Hd;
-  if (C == 64) return mlp_launch<Mg<64, 32>>(a, st);
-  if (C == 128) return mlp_launch<Mg<128, 16>>(a, st);
-  return mlp_launch<Mg<256, 16>>(a, st);
+  if (C == 64) return mlp_launch<Mg<64, 32>, false>(a, st);
+  if (C == 128) return mlp_launch<Mg<128, 16>, false>(a, st);
+  return mlp_launch<Mg<256, 16>, false>(a, st);
+}
+
+hipError_t launch_block_tail(const void* y, const void* x1, long long T, int C, int Hd,
+                             const void* w_out, const float* b_out, const float* ln_g,
+                             const float* ln_b, float eps, const void* w1, const float* b1,
+                             const void* w2, const float* b2, void* x2, void* n2, void* out,
+                             hipStream_t st) {
+  // W_out stays in LDS beside the chunk buffers: C up to 128
+  if (!mlp_shape_ok(T, C, Hd) || C > 128) return hipErrorNotSupported;
+  MlpArgs a = {};
+  a.x = (const uint16_t*)y; a.w1 = (const uint16_t*)w1; a.b1 = b1;
+  a.w2 = (const uint16_t*)w2; a.b2 = b2; a.r = (const uint16_t*)x1; a.out = (uint16_t*)out;
+  a.wo = (const uint16_t*)w_out; a.bo = b_out; a.lng = ln_g; a.lnb = ln_b; a.eps = eps;
+  a.x2 = (uint16_t*)x2; a.n2 = (uint16_t*)n2;
+  a.T = (int)T; a.Hd = Hd;
+  if (C == 64) return mlp_launch<Mg<64, BRA_TAIL_TW64>, true>(a, st);
+  return mlp_launch<Mg<128, 16>, true>(a, st);
 }
 
 }  // namespace bra
