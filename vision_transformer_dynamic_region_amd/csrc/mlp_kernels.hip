@@ -421,6 +421,300 @@ hipError_t mlp_launch(const MlpArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Weights-stationary form for C = 64 (Hd <= 256): every chunk of W1, W2 and
+// b1 (and in TAIL form W_out) stays in LDS for the whole launch, laid out as
+// the chunk buffers above.  Two workgroups of 8 wavefronts a CU; each
+// workgroup owns a contiguous range of 16-token blocks and its wavefronts
+// claim blocks from an LDS counter, so no barrier follows the staging and
+// the blocks of a workgroup are shared out as its wavefronts finish.  A
+// wavefront loads the inputs of its next block while it computes the
+// current one.
+// ---------------------------------------------------------------------------
+constexpr int kWsWaves = 8;
+constexpr int kWsThreads = kWsWaves * 64;
+constexpr int kWsC = 64;
+constexpr int kWsChunk = (32 * kWsC + kWsC * 32) * 2 + 32 * 4;   // W1, W2, b1 of a chunk
+
+struct WsLayout {
+  int b2, bo, lg, lb, wo, ctr, bytes;
+};
+__host__ __device__ inline WsLayout ws_layout(int nch, bool tail) {
+  WsLayout l;
+  int off = nch * kWsChunk;
+  l.b2 = off; off += kWsC * 4;
+  l.bo = off; l.lg = off + kWsC * 4; l.lb = off + 2 * kWsC * 4;
+  if (tail) off += 3 * kWsC * 4;
+  l.wo = off;
+  if (tail) off += kWsC * kWsC * 2;
+  l.ctr = off; off += 16;
+  l.bytes = off;
+  return l;
+}
+
+template <bool TAIL>
+__global__ __launch_bounds__(kWsThreads) void mlp_ws_kernel(MlpArgs A, int blk_per_wg) {
+  constexpr int C = kWsC, KS = 2, OT = 4, SH = 1, MSK = 7;
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int lq = lane & 15, lg = lane >> 4;
+  const int T = A.T, Hd = A.Hd, nch = Hd / 32;
+  const WsLayout L = ws_layout(nch, TAIL);
+  float* b2s = (float*)(lds + L.b2);
+  int* ctr = (int*)(lds + L.ctr);
+  const uint32_t tbytes = (uint32_t)T * C * 2;
+  const auto Xr = mlp_rsrc(A.x, tbytes);
+  const auto Rr = mlp_rsrc(A.r, tbytes);
+  const auto Or = mlp_rsrc(A.out, tbytes);
+  const auto W1r = mlp_rsrc(A.w1, (uint32_t)Hd * C * 2);
+  const auto W2r = mlp_rsrc(A.w2, (uint32_t)C * Hd * 2);
+
+  // ---- stage every chunk (layouts as mlp_kernel's buffers) ----
+  for (int e = tid; e < nch * 4 * C; e += kWsThreads) {
+    const int j = e / (4 * C), k = e - j * 4 * C;
+    uint16_t* W1s = (uint16_t*)(lds + j * kWsChunk);
+    const int r = k / (C / 8), c = k % (C / 8);
+    const int ca = TAIL ? 32 * (c >> 2) + 4 * (c & 3) : 8 * c;
+    const int cb = TAIL ? ca + 16 : ca + 4;
+    const uint32_t row = (uint32_t)(j * 32 + r) * C;
+    const uint2 a = mload8(W1r, (row + ca) * 2), b = mload8(W1r, (row + cb) * 2);
+    *(uint4*)(W1s + r * C + ((c ^ ((r >> SH) & MSK)) << 3)) = make_uint4(a.x, a.y, b.x, b.y);
+  }
+  for (int e = tid; e < nch * 4 * C; e += kWsThreads) {
+    const int j = e / (4 * C), k = e - j * 4 * C;
+    uint16_t* W2s = (uint16_t*)(lds + j * kWsChunk) + 32 * C;
+    const int o = k >> 2, g = k & 3;
+    const uint32_t base = (uint32_t)(o * Hd + j * 32 + 4 * g) * 2;
+    const uint2 a = mload8(W2r, base), b = mload8(W2r, base + 32);
+    *(uint4*)(W2s + o * 32 + ((g ^ ((o >> 2) & 3)) << 3)) = make_uint4(a.x, a.y, b.x, b.y);
+  }
+  for (int e = tid; e < nch * 32; e += kWsThreads) {
+    float* b1s = (float*)(lds + (e >> 5) * kWsChunk + (32 * C + C * 32) * 2);
+    b1s[e & 31] = A.b1 ? A.b1[e] : 0.f;
+  }
+  for (int c = tid; c < C; c += kWsThreads) b2s[c] = A.b2 ? A.b2[c] : 0.f;
+  if constexpr (TAIL) {
+    float* bos = (float*)(lds + L.bo);
+    float* lgs = (float*)(lds + L.lg);
+    float* lbs = (float*)(lds + L.lb);
+    uint16_t* Wos = (uint16_t*)(lds + L.wo);
+    const auto Wor = mlp_rsrc(A.wo, (uint32_t)C * C * 2);
+    for (int e = tid; e < C * C / 8; e += kWsThreads) {
+      const int r = e / (C / 8), c = e % (C / 8);
+      *(uint4*)(Wos + r * C + ((c ^ ((r >> SH) & MSK)) << 3)) = mload16(Wor, (uint32_t)e * 16);
+    }
+    for (int c = tid; c < C; c += kWsThreads) {
+      bos[c] = A.bo ? A.bo[c] : 0.f;
+      lgs[c] = A.lng[c];
+      lbs[c] = A.lnb[c];
+    }
+  }
+  if (tid == 0) *ctr = 0;
+  __syncthreads();
+
+  // ---- the workgroup's blocks, claimed one at a time by its wavefronts ----
+  const int nblk = (T + 15) >> 4;
+  const int b0 = blockIdx.x * blk_per_wg;
+  const int b1 = min(nblk, b0 + blk_per_wg);
+  auto claim = [&]() -> int {
+    int v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return b0 + __builtin_amdgcn_readfirstlane(v);
+  };
+  // inputs of block bk: the operands of x (TAIL: y) in natural channel
+  // order, and the residual (TAIL: x1) in the MFMA layout
+  auto xoff = [&](int bk, int s) -> uint32_t {
+    const int t = bk * 16 + lq;
+    return (bk < b1 && t < T) ? (uint32_t)(t * C + 32 * s + 8 * lg) * 2 : kMlpOob;
+  };
+  auto moff = [&](int bk, int o) -> uint32_t {
+    const int t = bk * 16 + lq;
+    return (bk < b1 && t < T) ? (uint32_t)(t * C + 16 * o + 4 * lg) * 2 : kMlpOob;
+  };
+  int bk = claim();
+  uint4 xin[KS];
+  uint2 rin[OT];
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2) xin[s2] = mload16(Xr, xoff(bk, s2));
+#pragma unroll
+  for (int o = 0; o < OT; ++o) rin[o] = mload8(Rr, moff(bk, o));
+  while (bk < b1) {
+    bf16x8 xo[KS];
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) xo[s2] = __builtin_bit_cast(bf16x8, xin[s2]);
+    uint2 res[OT];
+#pragma unroll
+    for (int o = 0; o < OT; ++o) res[o] = rin[o];
+    const int cur = bk;
+    // the next block's inputs, in flight while this one is computed
+    bk = claim();
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) xin[s2] = mload16(Xr, xoff(bk, s2));
+#pragma unroll
+    for (int o = 0; o < OT; ++o) rin[o] = mload8(Rr, moff(bk, o));
+
+    if constexpr (TAIL) {
+      // ---- x2 = x1 + y W_out^T + b_out, rounded; n2 = LN2(x2), rounded ----
+      const float* bos = (const float*)(lds + L.bo);
+      const float* lgs = (const float*)(lds + L.lg);
+      const float* lbs = (const float*)(lds + L.lb);
+      const uint16_t* Wos = (const uint16_t*)(lds + L.wo);
+      float v[OT][4];
+#pragma unroll
+      for (int o = 0; o < OT; ++o) {
+        const float4 bo4 = *(const float4*)(bos + 16 * o + 4 * lg);
+        f32x4 a = {bo4.x, bo4.y, bo4.z, bo4.w};
+        const int row = 16 * o + lq;
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+          const int c = 4 * s2 + lg;
+          const bf16x8 w = *(const bf16x8*)(Wos + row * C + ((c ^ ((row >> SH) & MSK)) << 3));
+          a = mfma16(w, xo[s2], a);
+        }
+        const uint32_t p0 = pack_bf16x2(a[0] + bf16_lo(res[o].x), a[1] + bf16_hi(res[o].x));
+        const uint32_t p1 = pack_bf16x2(a[2] + bf16_lo(res[o].y), a[3] + bf16_hi(res[o].y));
+        res[o] = make_uint2(p0, p1);
+        v[o][0] = bf16_lo(p0); v[o][1] = bf16_hi(p0);
+        v[o][2] = bf16_lo(p1); v[o][3] = bf16_hi(p1);
+        if (A.x2) {
+          const u32x2 st = {p0, p1};
+          __builtin_amdgcn_raw_buffer_store_b64(st, mlp_rsrc(A.x2, tbytes), moff(cur, o), 0, 0);
+        }
+      }
+      float sm = 0.f;
+#pragma unroll
+      for (int o = 0; o < OT; ++o) sm += (v[o][0] + v[o][1]) + (v[o][2] + v[o][3]);
+      sm += xor16(sm);
+      sm += xor32(sm);
+      const float mean = sm / (float)C;
+      float sq = 0.f;
+#pragma unroll
+      for (int o = 0; o < OT; ++o)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float d = v[o][e] - mean;
+          sq = fmaf(d, d, sq);
+        }
+      sq += xor16(sq);
+      sq += xor32(sq);
+      const float rstd = 1.0f / sqrtf(sq / (float)C + A.eps);
+      uint32_t np[OT][2];
+#pragma unroll
+      for (int o = 0; o < OT; ++o) {
+        const float4 g4 = *(const float4*)(lgs + 16 * o + 4 * lg);
+        const float4 b4 = *(const float4*)(lbs + 16 * o + 4 * lg);
+        np[o][0] = pack_bf16x2((v[o][0] - mean) * rstd * g4.x + b4.x,
+                               (v[o][1] - mean) * rstd * g4.y + b4.y);
+        np[o][1] = pack_bf16x2((v[o][2] - mean) * rstd * g4.z + b4.z,
+                               (v[o][3] - mean) * rstd * g4.w + b4.w);
+        if (A.n2) {
+          const u32x2 st = {np[o][0], np[o][1]};
+          __builtin_amdgcn_raw_buffer_store_b64(st, mlp_rsrc(A.n2, tbytes), moff(cur, o), 0, 0);
+        }
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        xo[s2] = __builtin_bit_cast(
+            bf16x8, make_uint4(np[2 * s2][0], np[2 * s2][1], np[2 * s2 + 1][0], np[2 * s2 + 1][1]));
+    }
+
+    // ---- the MLP over every chunk of the hidden layer ----
+    f32x4 acc[OT];
+#pragma unroll
+    for (int o = 0; o < OT; ++o) acc[o] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < nch; ++j) {
+      const unsigned char* bp = lds + j * kWsChunk;
+      const uint16_t* W1s = (const uint16_t*)bp;
+      const uint16_t* W2s = W1s + 32 * C;
+      const float* b1s = (const float*)(bp + (32 * C + C * 32) * 2);
+      f32x4 h[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float4 bt = *(const float4*)(b1s + 16 * t + 4 * lg);
+        h[t] = f32x4{bt.x, bt.y, bt.z, bt.w};
+        const int row = 16 * t + lq;
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+          const int c = 4 * s2 + lg;
+          const bf16x8 a = *(const bf16x8*)(W1s + row * C + ((c ^ ((row >> SH) & MSK)) << 3));
+          h[t] = mfma16(a, xo[s2], h[t]);
+        }
+      }
+      const uint32_t u0 = pack_bf16x2(gelu_as(h[0][0]), gelu_as(h[0][1]));
+      const uint32_t u1 = pack_bf16x2(gelu_as(h[0][2]), gelu_as(h[0][3]));
+      const uint32_t u2 = pack_bf16x2(gelu_as(h[1][0]), gelu_as(h[1][1]));
+      const uint32_t u3 = pack_bf16x2(gelu_as(h[1][2]), gelu_as(h[1][3]));
+      const bf16x8 hop = __builtin_bit_cast(bf16x8, make_uint4(u0, u1, u2, u3));
+#pragma unroll
+      for (int o = 0; o < OT; ++o) {
+        const int row = 16 * o + lq;
+        const bf16x8 a = *(const bf16x8*)(W2s + row * 32 + ((lg ^ ((row >> 2) & 3)) << 3));
+        acc[o] = mfma16(a, hop, acc[o]);
+      }
+    }
+
+    // ---- epilogue (as mlp_kernel's) ----
+    const bool odd = lg & 1;
+    const int t = cur * 16 + lq;
+#pragma unroll
+    for (int m = 0; m < OT / 2; ++m) {
+      float f[2][4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int o = 2 * m + q;
+        const float4 b4 = *(const float4*)(b2s + 16 * o + 4 * lg);
+        f[q][0] = acc[o][0] + b4.x + bf16_lo(res[o].x);
+        f[q][1] = acc[o][1] + b4.y + bf16_hi(res[o].x);
+        f[q][2] = acc[o][2] + b4.z + bf16_lo(res[o].y);
+        f[q][3] = acc[o][3] + b4.w + bf16_hi(res[o].y);
+      }
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(f[0][e]),
+                                                         __float_as_uint(f[1][e]), false, false);
+        if (odd) {
+          v[e] = __uint_as_float(sw[0]);
+          v[4 + e] = f[1][e];
+        } else {
+          v[e] = f[0][e];
+          v[4 + e] = __uint_as_float(sw[1]);
+        }
+      }
+      const int ch = 32 * m + (odd ? 16 + 4 * (lg - 1) : 4 * lg);
+      const uint32_t off = t < T ? (uint32_t)(t * C + ch) * 2 : kMlpOob;
+      const u32x4 x = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                       pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+      __builtin_amdgcn_raw_buffer_store_b128(x, Or, off, 0, 0);
+    }
+  }
+}
+
+template <bool TAIL>
+hipError_t mlp_ws_launch(const MlpArgs& a, hipStream_t st) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const WsLayout l = ws_layout(a.Hd / 32, TAIL);
+  const void* fn = reinterpret_cast<const void*>(&mlp_ws_kernel<TAIL>);
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, l.bytes);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mlp_ws_kernel<TAIL>, kWsThreads, l.bytes);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorNotSupported;
+  const long long nblk = ((long long)a.T + 15) / 16;
+  long long groups = (long long)cus * per_cu;
+  if (groups > nblk) groups = nblk;
+  const int per = (int)((nblk + groups - 1) / groups);
+  groups = (nblk + per - 1) / per;
+  hipLaunchKernelGGL((mlp_ws_kernel<TAIL>), dim3((unsigned)groups), dim3(kWsThreads), l.bytes, st,
+                     a, per);
+  return hipGetLastError();
+}
+
 bool mlp_shape_ok(long long T, int C, int Hd) {
   if (T <= 0 || Hd <= 0 || Hd % 32) return false;
   if (C != 64 && C != 128 && C != 256) return false;
@@ -438,6 +732,7 @@ hipError_t launch_mlp(const void* x, long long T, int C, int Hd, const void* w1,
   a.x = (const uint16_t*)x; a.w1 = (const uint16_t*)w1; a.b1 = b1;
   a.w2 = (const uint16_t*)w2; a.b2 = b2; a.r = (const uint16_t*)resid; a.out = (uint16_t*)out;
   a.T = (int)T; a.Hd = Hd;
+  if (C == 64 && Hd <= 256) return mlp_ws_launch<false>(a, st);
   if (C == 64) return mlp_launch<Mg<64, 32>, false>(a, st);
   if (C == 128) return mlp_launch<Mg<128, 16>, false>(a, st);
   return mlp_launch<Mg<256, 16>, false>(a, st);
@@ -456,6 +751,7 @@ hipError_t launch_block_tail(const void* y, const void* x1, long long T, int C, 
   a.wo = (const uint16_t*)w_out; a.bo = b_out; a.lng = ln_g; a.lnb = ln_b; a.eps = eps;
   a.x2 = (uint16_t*)x2; a.n2 = (uint16_t*)n2;
   a.T = (int)T; a.Hd = Hd;
+  if (C == 64 && Hd <= 256) return mlp_ws_launch<true>(a, st);
   if (C == 64) return mlp_launch<Mg<64, BRA_TAIL_TW64>, true>(a, st);
   return mlp_launch<Mg<128, 16>, true>(a, st);
 }
