@@ -673,7 +673,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void route_small_kernel(RouteArgs
 
 // ---------------------------------------------------------------------------
 // Pool and route in one launch, for R <= 64 regions: one 16-wavefront
-// workgroup per (image, 16-row strip) pools the float64 means of all the
+// workgroup per (image, strip of at most 16 rows) pools the float64 means of all the
 // image's K regions and of its strip's Q regions into LDS, then forms the
 // strip's affinities and ranks them as route_small_kernel does.  Each strip
 // pools the image's K itself (the image's strips share one XCD, so the
@@ -719,8 +719,11 @@ __global__ __launch_bounds__(kSmallWaves * 64) void pool_route_kernel(PoolRouteA
   const int t1 = rest / A.nrb, strip = rest - t1 * A.nrb;
   const int b = t1 * kXcds + xcd;
   if (b >= s.B) return;                      // uniform; before any barrier
-  const int r0 = strip * kRouteRows;
-  const int rows = min(kRouteRows, R - r0);
+  // the image's rows split evenly over its nrb strips (at most 16 each), so
+  // that no workgroup pools more than R + ceil(R / nrb) regions: at R = 49,
+  // 62 items (at most four a wavefront) rather than 16 + 49 = 65
+  const int r0 = strip * R / A.nrb;
+  const int rows = (strip + 1) * R / A.nrb - r0;
   // the wavefront index as a scalar: items, and so the buffer descriptor
   // each load takes, are uniform over the wavefront
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
