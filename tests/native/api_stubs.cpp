@@ -60,6 +60,12 @@ hipError_t launch_attend(const void*, const void*, const void*, const int32_t*, 
                          float, const float*, const float*, int, void*, hipStream_t) {
   reached("launch_attend");
 }
+bool attend_xproj_ok(const Shape&, const float*, int) { return false; }
+hipError_t launch_attend_xproj(const void*, const void*, const float*, const void*, const int32_t*,
+                               const Shape&, float, const float*, const float*, int, void*,
+                               hipStream_t) {
+  reached("launch_attend_xproj");
+}
 hipError_t launch_attend_region(const void*, const void*, const void*, const int32_t*,
                                 const Shape&, float, const float*, const float*, int, void*,
                                 hipStream_t) {

@@ -124,7 +124,12 @@ def test_module_parity(cuda, name):
         assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.abs(want).max()), nm
     es = 2 if dt == "bf16" else 4
     tb = up(B * H * W * C * es)
+    # where Q and K are projected inside the attention kernel only V is stored
+    fused = (dt == "bf16" and C == 64 and wl.heads == 2 and H // S == 8 and W // S == 8
+             and wl.topk == 1 and m["w"] is not None and m["w"].shape[-1] == 5)
     for i, nm in enumerate(("q", "k", "v")):
+        if fused and nm != "v":
+            continue
         raw = ws[3 * mb + i * tb:3 * mb + i * tb + B * H * W * C * es]
         t = raw.view(torch.bfloat16 if dt == "bf16" else torch.float32).reshape(B, H, W, C)
         assert_close(to_host(t), ref[nm], dt, f"{name} {nm}")
@@ -154,3 +159,36 @@ def test_module_in_place(cuda):
     bra.module_forward(x, *args, out=x)
     torch.cuda.synchronize()
     assert torch.equal(x, want)
+
+
+@pytest.mark.parametrize("bias,with_out", [(True, False), (False, False), (True, True)])
+def test_module_fused_projection_is_the_composition(cuda, bias, with_out):
+    """Where Q and K are projected inside the attention kernel (bf16, C = 64,
+    8x8-pixel regions, top-1, 5x5 LePE), the module's y is bit for bit the
+    unfused composition: bra.linear of x into Q, K, V, then bra.attend with
+    the module's idx.  With y in x's memory the module takes the unfused
+    path, and gives the same bits."""
+    import torch
+    import vision_transformer_dynamic_region_amd as bra
+    wl = WORKLOADS["st1"].scaled(B=5)
+    print(f"[module] fused projection, bias={bias} with_out={with_out}", flush=True)
+    m = make_module_inputs(wl)
+    x = to_dev(m["x"], wl.dtype)
+    w_qkv = to_dev(m["w_qkv"], wl.dtype)
+    b_qkv = torch.from_numpy(m["b_qkv"]).to(cuda) if bias else None
+    lw = torch.from_numpy(m["w"]).to(cuda)
+    w_out = to_dev(m["w_out"], wl.dtype) if with_out else None
+    b_out = torch.from_numpy(m["b_out"]).to(cuda) if with_out else None
+    out, idx = bra.module_forward(x, w_qkv, b_qkv, wl.heads, wl.S, wl.topk, lw, None, w_out, b_out)
+    C = wl.C
+    qkv = bra.linear(x, w_qkv, b_qkv)
+    q, k, v = (qkv[..., i * C:(i + 1) * C].contiguous() for i in range(3))
+    y = bra.attend(q, k, v, idx, wl.heads, wl.S, lepe_w=lw)
+    want = bra.linear(y, w_out, b_out) if with_out else y
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+    if not with_out:
+        x2 = x.clone()
+        bra.module_forward(x2, w_qkv, b_qkv, wl.heads, wl.S, wl.topk, lw, None, out=x2)
+        torch.cuda.synchronize()
+        assert torch.equal(x2.view(torch.int16), out.view(torch.int16))

@@ -373,7 +373,9 @@ def module_forward(x, w_qkv, b_qkv, heads: int, S: int, topk: int, lepe_w=None, 
     BRA forward pass with LePE on V, then the optional output projection.
     Returns (out, idx).  workspace, if given, is a CUDA uint8 tensor of at
     least module_workspace_bytes(...) bytes; afterwards it holds the region
-    means of x, Q and K and the tensors Q, K, V (and y when w_out is given)."""
+    means of x, Q and K and the tensors Q, K, V (and y when w_out is given),
+    except Q and K where they are projected inside the attention kernel
+    (bf16, C = 64, 8x8-pixel regions, top-1, 5x5 LePE, y not in x's memory)."""
     import torch
     B, H, W, C = _bhwc(x)
     dt = _dtype_code(x)

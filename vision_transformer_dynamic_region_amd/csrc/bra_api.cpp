@@ -194,15 +194,32 @@ bra_status module_launches(const void* x, const bra::Shape& s, bra_dtype dtype, 
   if ((st = hip_status(bra::launch_route(qm, km, s, (double)route_scale, idx, nullptr, hs),
                        "route launch")))
     return st;
-  // Q, K, V
-  if ((st = hip_status(bra::launch_linear(x, T, C, w_qkv, b_qkv, 3 * C, qkv, 3, bf16, hs),
-                       "qkv projection launch")))
-    return st;
-  // attention + LePE on the projected V
-  if ((st = hip_status(bra::launch_attend(qkv[0], qkv[1], qkv[2], idx, s, bf16, attn_scale, lepe_w,
-                                          lepe_b, lepe_ks, y, hs),
-                       "attend launch")))
-    return st;
+  const size_t xbytes = (size_t)T * C * elem_size(dtype);
+  if (bf16 && bra::attend_xproj_ok(s, lepe_w, lepe_ks) && !overlaps(y, x, xbytes)) {
+    // fused form: V alone through the projection, Q and K projected inside
+    // the attention kernel (the workspace's Q and K parts stay unwritten);
+    // not when y is x's memory, which that kernel still reads while it writes
+    const void* w_v = (const uint16_t*)w_qkv + (size_t)2 * C * C;
+    const float* b_v = b_qkv ? b_qkv + 2 * C : nullptr;
+    void* vout[1] = {qkv[2]};
+    if ((st = hip_status(bra::launch_linear(x, T, C, w_v, b_v, C, vout, 1, bf16, hs),
+                         "v projection launch")))
+      return st;
+    if ((st = hip_status(bra::launch_attend_xproj(x, w_qkv, b_qkv, qkv[2], idx, s, attn_scale,
+                                                  lepe_w, lepe_b, lepe_ks, y, hs),
+                         "fused attend launch")))
+      return st;
+  } else {
+    // Q, K, V
+    if ((st = hip_status(bra::launch_linear(x, T, C, w_qkv, b_qkv, 3 * C, qkv, 3, bf16, hs),
+                         "qkv projection launch")))
+      return st;
+    // attention + LePE on the projected V
+    if ((st = hip_status(bra::launch_attend(qkv[0], qkv[1], qkv[2], idx, s, bf16, attn_scale,
+                                            lepe_w, lepe_b, lepe_ks, y, hs),
+                         "attend launch")))
+      return st;
+  }
   if (!w_out) return BRA_OK;
   void* outs[1] = {out};
   return hip_status(bra::launch_linear(y, T, C, w_out, b_out, C, outs, 1, bf16, hs,

@@ -52,10 +52,14 @@ namespace {
 constexpr int kHd = 32;    // head width
 
 template <int C_, int CB_, int HS_, int WS_, int TOPK_, int KS_, bool DB_, int OCC_ = 2,
-          bool NT_ = false>
+          bool NT_ = false, bool XP_ = false>
 struct Rc {
   static constexpr int C = C_, CB = CB_, HS = HS_, WS = WS_, TOPK = TOPK_, KS = KS_;
   static constexpr bool DB = DB_;                  // double-buffered staging
+  // Q and K projected from x in the kernel (the module's fused form): the
+  // query region's and the routed regions' x rows are staged and multiplied
+  // by the unit's rows of Wq and Wk; V comes projected, as in the plain form
+  static constexpr bool XP = XP_;
   // more than 128 routed keys: S^T is computed twice (the maximum, then the
   // numerators 32 keys a step) rather than held in 4 KC / 64 registers
   static constexpr bool TWO_PASS = TOPK_ * HS_ * WS_ > 128;
@@ -83,12 +87,15 @@ struct Rc {
   static constexpr int NXG = WS / XG;
   static constexpr int TYW = QR * NXG / 2;
   static constexpr int LSW = kHd + 4;               // wavefront L tile row stride (floats)
-  // LDS: [halo | K | V] x (DB ? 2 : 1), wavefront L tiles, routing table
+  // LDS: [halo | K | V] x (DB ? 2 : 1), wavefront L tiles, (XP) the unit
+  // block's Wq and Wk rows and biases, routing table
   static constexpr int HALO = HH * HW * CB * 2;
   static constexpr int KVB = KC * CB * 2;
   static constexpr int BUF = (HALO + 2 * KVB + 15) / 16 * 16;
   static constexpr int L_OFF = BUF * (DB ? 2 : 1);
-  static constexpr int IT_OFF = L_OFF + kWaves * 16 * LSW * 4;
+  static constexpr int WX_OFF = L_OFF + kWaves * 16 * LSW * 4;
+  static constexpr int WX_BYTES = XP ? 2 * CB * C * 2 + 2 * CB * 4 : 0;
+  static constexpr int IT_OFF = WX_OFF + WX_BYTES;
 
   static_assert(C % CB == 0 && CB % kHd == 0, "channel blocking");
   static_assert(TASKS == kWaves, "one task (16 queries x 1 head) per wavefront");
@@ -98,7 +105,15 @@ struct Rc {
   static_assert(KS == 5 && (XG == 4 || XG == 2) && TYW >= 1 && (QR * NXG) % 2 == 0,
                 "dot2 LePE: 5x5 taps, two items per channel lane");
   static_assert(KK * CB * 4 <= BUF, "weights are staged through the first buffer");
+  static_assert(!XP || (C == 64 && n == 64 && KC == 16 * kWaves && !DB),
+                "fused projection: 64 channels of x, 8x8 regions, top-1, one buffer");
+  static_assert(!XP || 16 * CB * 2 <= 16 * LSW * 4, "a wavefront's Q tile fits its L tile");
 };
+
+// Weight-row swizzle (XP): 16-byte chunk c (of eight) of row r sits at
+// chunk c ^ ((r >> 1) & 7), so the 16 rows one operand load reads (8 even,
+// 8 odd, 128 bytes apart) fall into 16 distinct bank groups.
+__device__ __forceinline__ int xswz(int p) { return (p >> 1) & 7; }
 
 // K/V tile swizzle: chunk g (16 bytes) of key row kk sits at chunk
 // g ^ kswz(kk), so the 16 rows one operand load reads fall into 16 distinct
@@ -134,6 +149,12 @@ struct RegionArgs {
   uint16_t* out;
   const float* w;       // [C, KS, KS]
   const float* bias;    // [C] or null
+  // XP: q and k both point to x; wq, wk to the C rows of Wq and Wk ([C, C]
+  // bf16 each, rows = output channels) and bq, bk to their biases (or null)
+  const uint16_t* wq;
+  const uint16_t* wk;
+  const float* bq;
+  const float* bk;
   int H, W, S, R;
   int Hf;               // rows of one frame; the LePE halo stays inside it
   float scale_log2;     // attn_scale * log2(e)
@@ -208,6 +229,23 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
       wst[e] = A.w[(size_t)(cb0 + c) * KK + t];
     }
   }
+  if constexpr (G::XP) {
+    // the unit block's rows of Wq and Wk (x-tile swizzle) and their biases
+    uint16_t* wqs = (uint16_t*)(lds + G::WX_OFF);
+    uint16_t* wks = wqs + CB * C;
+    float* bqs = (float*)(wks + CB * C);
+    float* bks = bqs + CB;
+    for (int e = tid; e < CB * (C / 8); e += kThreads) {
+      const int r = e / (C / 8), c = e - r * (C / 8);
+      const int o = r * C + ((c ^ xswz(r)) * 8);
+      *(uint4*)(wqs + o) = *(const uint4*)(A.wq + (size_t)(cb0 + r) * C + c * 8);
+      *(uint4*)(wks + o) = *(const uint4*)(A.wk + (size_t)(cb0 + r) * C + c * 8);
+    }
+    for (int c = tid; c < CB; c += kThreads) {
+      bqs[c] = A.bq ? A.bq[cb0 + c] : 0.f;
+      bks[c] = A.bk ? A.bk[cb0 + c] : 0.f;
+    }
+  }
   __syncthreads();
 
   // this wavefront's task: query block qb of head hb
@@ -250,7 +288,9 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
 
   const uint32_t img_elems = (uint32_t)A.H * A.W * C;
   const int q = qb * 16 + lq;                      // this lane's query (column of the MFMAs)
-  uint4 qn, kn[KPT], vn[KPT], hn[HPT];
+  constexpr int KPA = G::XP ? 1 : KPT;            // (array size of the unused form: 1)
+  uint4 qn, kn[KPA], vn[KPT], hn[HPT];
+  uint4 xqn[2], xkn[2];                            // XP: x operands, k-steps 0 and 1
   auto prefetch = [&](int j) {
     int b, ry, rx;
     decode(j, b, ry, rx);
@@ -258,7 +298,19 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
     const auto Q = image_rsrc(A.q + img, img_elems * 2);
     const auto K = image_rsrc(A.k + img, img_elems * 2);
     const auto V = image_rsrc(A.v + img, img_elems * 2);
-    {
+    if constexpr (G::XP) {
+      // x in the projections' operand layout: lane (lq, lg) takes channels
+      // 32s + 8lg .. +7 of this wavefront's query lq and of routed key
+      // 16 wave + lq
+      const int key = 16 * wave + lq;
+      const uint32_t oq = ((ry * HS + q / WS) * A.W + rx * WS + q % WS) * C + 8 * lg;
+      const uint32_t ok = itab[j * TOPK] + ((key / WS) * A.W + key % WS) * C + 8 * lg;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        xqn[s2] = bload16(Q, (oq + 32 * s2) * 2);
+        xkn[s2] = bload16(K, (ok + 32 * s2) * 2);
+      }
+    } else {
       const uint32_t off = ((ry * HS + q / WS) * A.W + rx * WS + q % WS) * C + cb0 + hb * kHd + 8 * lg;
       qn = bload16(Q, q < n ? off * 2 : kOob);
     }
@@ -270,7 +322,7 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
           (PSTEP * (i + 1) <= KC || kk < KC)
               ? (itab[j * TOPK + tj] + ((tok / WS) * A.W + tok % WS) * C + cb0 + g * 8) * 2
               : kOob;
-      kn[i] = bload16(K, off);
+      if constexpr (!G::XP) kn[i] = bload16(K, off);
       vn[i] = bload16(V, off);
     }
     const int ftop = (int)fdiv(ry, A.f_syf) * A.Hf;  // first row of the region's frame
@@ -301,11 +353,11 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
       const int kk = pk + PSTEP * i;
       if (PSTEP * (i + 1) <= KC || kk < KC) {
         const int o = kk * CB + ((g ^ kswz<GB>(kk)) * 8);
-        *(uint4*)(Ks + o) = kn[i];
+        if constexpr (!G::XP) *(uint4*)(Ks + o) = kn[i];
         *(uint4*)(Vs + o) = vn[i];
       }
     }
-    qop = __builtin_bit_cast(bf16x8, qn);
+    if constexpr (!G::XP) qop = __builtin_bit_cast(bf16x8, qn);
   };
 
   const float c = A.scale_log2;
@@ -330,7 +382,50 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
     }
 #endif
     commit(buf);
-    __syncthreads();
+    if constexpr (G::XP) {
+      // ---- before the barrier that publishes the staged tiles, and before
+      // the next unit's loads reuse the x registers: K of the routed keys
+      // (key block = wavefront) and this wavefront's Q: (Wq|Wk)[rows] x^T on v_mfma_f32_16x16x32_bf16 with the
+      // bias added and one rounding to bf16, as the plain projection ----
+      const uint16_t* wqs = (const uint16_t*)(lds + G::WX_OFF);
+      const uint16_t* wks = wqs + CB * C;
+      const float* bqs = (const float*)(wks + CB * C);
+      const float* bks = bqs + CB;
+      uint16_t* Kw = (uint16_t*)(buf + G::HALO);
+      // D lane (lq, lg): channels 16cb + 4lg .. +3 of the operand's pixel lq
+      auto project = [&](const uint4* xo, const uint16_t* ws, const float* bs, int cb) -> uint2 {
+        const int r = 16 * cb + lq;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < C / 32; ++s2) {
+          const int c = 4 * s2 + lg;
+          const bf16x8 wa = *(const bf16x8*)(ws + r * C + ((c ^ xswz(r)) * 8));
+          acc = mfma_bf16(wa, __builtin_bit_cast(bf16x8, xo[s2]), acc);
+        }
+        const float4 bb = *(const float4*)(bs + 16 * cb + 4 * lg);
+        return make_uint2(pack_bf16x2(acc[0] + bb.x, acc[1] + bb.y),
+                          pack_bf16x2(acc[2] + bb.z, acc[3] + bb.w));
+      };
+      {
+        const int key = 16 * wave + lq;              // key block = wavefront
+#pragma unroll
+        for (int cb = 0; cb < CB / 16; ++cb) {
+          const uint2 kv = project(xkn, wks, bks, cb);
+          const int ch = 2 * cb + (lg >> 1);         // 16-byte chunk of channels 16cb + 4lg
+          *(uint2*)(Kw + key * CB + ((ch ^ kswz<GB>(key)) * 8) + 4 * (lg & 1)) = kv;
+        }
+      }
+      // Q through the wavefront's L tile: [query][CB] bf16, read back as the
+      // operand (channels 32hb + 8lg .. +7 of query lq)
+      uint16_t* Qw = (uint16_t*)Lw;
+#pragma unroll
+      for (int cb = 0; cb < CB / 16; ++cb)
+        *(uint2*)(Qw + lq * CB + 16 * cb + 4 * lg) = project(xqn, wqs, bqs, cb);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      qop = *(const bf16x8*)(Qw + lq * CB + hb * kHd + 8 * lg);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // read before L reuses the tile
+    }
+    __syncthreads();                                 // (XP: every key block is in place)
     if (j + 1 < nu) prefetch(j + 1);
     const uint16_t* Hs = (const uint16_t*)buf;
     const uint16_t* Ks = (const uint16_t*)(buf + G::HALO);
@@ -577,6 +672,8 @@ using St1 = Rc<64, 32, 8, 8, 1, 5, BRA_DB_ST1, 4>;
 using St2 = Rc<128, 128, 4, 4, 4, 5, false>;
 using St3 = Rc<256, 128, 2, 2, 16, 5, false>;
 using Dense = Rc<64, 32, 8, 8, 4, 5, BRA_DB_DENSE, 3, true>;
+// the module's fused form of St1: Q and K projected from x in the kernel
+using StX1 = Rc<64, 32, 8, 8, 1, 5, false, 4, false, true>;
 
 }  // namespace
 
@@ -589,6 +686,8 @@ hipError_t launch_attend_region(const void* q, const void* k, const void* v, con
   RegionArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.idx = idx; a.out = (uint16_t*)out; a.w = w; a.bias = bias;
+  a.wq = a.wk = nullptr;
+  a.bq = a.bk = nullptr;
   a.H = s.H; a.W = s.W; a.S = s.S; a.R = s.R; a.Hf = s.Hf;
   a.scale_log2 = attn_scale * 1.4426950408889634f;
   a.f_R = make_fastdiv(s.R);
@@ -612,6 +711,34 @@ hipError_t launch_attend_region(const void* q, const void* k, const void* v, con
     return region_launch<Dense>(a, s.B, st);
   }
   return hipErrorNotSupported;
+}
+
+bool attend_xproj_ok(const Shape& s, const float* w, int ks) {
+  return w && s.C == StX1::C && s.C == s.heads * kHd && s.hs == StX1::HS && s.ws == StX1::WS &&
+         s.topk == StX1::TOPK && ks == StX1::KS && s.Hf == s.H &&
+         (long long)s.H * s.W * s.C * 2 < (long long)kOob;
+}
+
+hipError_t launch_attend_xproj(const void* x, const void* w_qkv, const float* b_qkv,
+                               const void* v, const int32_t* idx, const Shape& s,
+                               float attn_scale, const float* w, const float* bias, int ks,
+                               void* out, hipStream_t st) {
+  if (!attend_xproj_ok(s, w, ks)) return hipErrorNotSupported;
+  RegionArgs a;
+  a.q = a.k = (const uint16_t*)x;
+  a.v = (const uint16_t*)v;
+  a.idx = idx; a.out = (uint16_t*)out; a.w = w; a.bias = bias;
+  a.wq = (const uint16_t*)w_qkv;
+  a.wk = (const uint16_t*)w_qkv + (size_t)s.C * s.C;
+  a.bq = b_qkv;
+  a.bk = b_qkv ? b_qkv + s.C : nullptr;
+  a.H = s.H; a.W = s.W; a.S = s.S; a.R = s.R; a.Hf = s.Hf;
+  a.scale_log2 = attn_scale * 1.4426950408889634f;
+  a.f_R = make_fastdiv(s.R);
+  a.f_S = make_fastdiv(s.S);
+  a.f_syf = make_fastdiv(s.Hf / s.hs);
+  a.per_xcd = a.bpx = 0;
+  return region_launch<StX1>(a, s.B, st);
 }
 
 }  // namespace bra
