@@ -392,9 +392,11 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
       const float* bqs = (const float*)(wks + CB * C);
       const float* bks = bqs + CB;
       uint16_t* Kw = (uint16_t*)(buf + G::HALO);
-      // D lane (lq, lg): channels 16cb + 4lg .. +3 of the operand's pixel lq
-      auto project = [&](const uint4* xo, const uint16_t* ws, const float* bs, int cb) -> uint2 {
-        const int r = 16 * cb + lq;
+      // weight row r(i) feeds D row i; D lane (lq, lg) holds the channels
+      // r(4lg .. 4lg+3) of the operand's pixel lq, biased and rounded
+      auto project = [&](const uint4* xo, const uint16_t* ws, const float* bs,
+                         auto row) -> uint2 {
+        const int r = row(lq);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s2 = 0; s2 < C / 32; ++s2) {
@@ -402,7 +404,7 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
           const bf16x8 wa = *(const bf16x8*)(ws + r * C + ((c ^ xswz(r)) * 8));
           acc = mfma_bf16(wa, __builtin_bit_cast(bf16x8, xo[s2]), acc);
         }
-        const float4 bb = *(const float4*)(bs + 16 * cb + 4 * lg);
+        const float4 bb = *(const float4*)(bs + row(4 * lg));   // r(4lg + e) = r(4lg) + e
         return make_uint2(pack_bf16x2(acc[0] + bb.x, acc[1] + bb.y),
                           pack_bf16x2(acc[2] + bb.z, acc[3] + bb.w));
       };
@@ -410,20 +412,19 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
         const int key = 16 * wave + lq;              // key block = wavefront
 #pragma unroll
         for (int cb = 0; cb < CB / 16; ++cb) {
-          const uint2 kv = project(xkn, wks, bks, cb);
+          const uint2 kv = project(xkn, wks, bks, [&](int i) { return 16 * cb + i; });
           const int ch = 2 * cb + (lg >> 1);         // 16-byte chunk of channels 16cb + 4lg
           *(uint2*)(Kw + key * CB + ((ch ^ kswz<GB>(key)) * 8) + 4 * (lg & 1)) = kv;
         }
       }
-      // Q through the wavefront's L tile: [query][CB] bf16, read back as the
-      // operand (channels 32hb + 8lg .. +7 of query lq)
-      uint16_t* Qw = (uint16_t*)Lw;
-#pragma unroll
-      for (int cb = 0; cb < CB / 16; ++cb)
-        *(uint2*)(Qw + lq * CB + 16 * cb + 4 * lg) = project(xqn, wqs, bqs, cb);
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      qop = *(const bf16x8*)(Qw + lq * CB + hb * kHd + 8 * lg);
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");   // read before L reuses the tile
+      // Q straight into the operand layout (channels 32hb + 8lg .. +7 of
+      // query lq): two products whose D rows are the weight rows 8(i/4) +
+      // i%4 and that + 4, so lane lg ends with channels 8lg .. 8lg+3 and
+      // 8lg+4 .. 8lg+7 (each element's sum is the same as unpermuted)
+      const uint2 q0 = project(xqn, wqs, bqs, [&](int i) { return hb * kHd + 8 * (i >> 2) + (i & 3); });
+      const uint2 q1 = project(xqn, wqs, bqs,
+                               [&](int i) { return hb * kHd + 8 * (i >> 2) + 4 + (i & 3); });
+      qop = __builtin_bit_cast(bf16x8, make_uint4(q0.x, q0.y, q1.x, q1.y));
     }
     __syncthreads();                                 // (XP: every key block is in place)
     if (j + 1 < nu) prefetch(j + 1);
