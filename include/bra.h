@@ -168,9 +168,10 @@ bra_status bra_linear(const void* x, int rows, int K, const void* w,
  * float64 [B, S*S, C] region means of Q, the same of K, then Q, K, V as
  * [B, H, W, C] dtype each, then (with_out_proj) y = attention + LePE as
  * [B, H, W, C] dtype.  After a successful call the workspace holds exactly
- * those values, which callers may read, except that the Q and K parts are
- * left unwritten where Q and K are projected inside the attention kernel
- * (bf16, C = 64, 8x8-pixel regions, top-1, 5x5 LePE, and y not x's memory).
+ * those values, which callers may read, except that the Q, K and V parts
+ * are left unwritten where Q, K and V are projected inside the attention
+ * kernel (bf16, C = 64, 8x8-pixel regions, top-1, 5x5 LePE, and y not x's
+ * memory).
  * 0 for invalid sizes. */
 size_t bra_module_workspace_bytes(int B, int H, int W, int C, int S,
                                   bra_dtype dtype, int with_out_proj);

@@ -61,7 +61,7 @@ hipError_t launch_attend(const void*, const void*, const void*, const int32_t*, 
   reached("launch_attend");
 }
 bool attend_xproj_ok(const Shape&, const float*, int) { return false; }
-hipError_t launch_attend_xproj(const void*, const void*, const float*, const void*, const int32_t*,
+hipError_t launch_attend_xproj(const void*, const void*, const float*, const int32_t*,
                                const Shape&, float, const float*, const float*, int, void*,
                                hipStream_t) {
   reached("launch_attend_xproj");

@@ -124,11 +124,11 @@ def test_module_parity(cuda, name):
         assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.abs(want).max()), nm
     es = 2 if dt == "bf16" else 4
     tb = up(B * H * W * C * es)
-    # where Q and K are projected inside the attention kernel only V is stored
+    # where Q, K and V are projected inside the attention kernel none is stored
     fused = (dt == "bf16" and C == 64 and wl.heads == 2 and H // S == 8 and W // S == 8
              and wl.topk == 1 and m["w"] is not None and m["w"].shape[-1] == 5)
     for i, nm in enumerate(("q", "k", "v")):
-        if fused and nm != "v":
+        if fused:
             continue
         raw = ws[3 * mb + i * tb:3 * mb + i * tb + B * H * W * C * es]
         t = raw.view(torch.bfloat16 if dt == "bf16" else torch.float32).reshape(B, H, W, C)
@@ -163,7 +163,7 @@ def test_module_in_place(cuda):
 
 @pytest.mark.parametrize("bias,with_out", [(True, False), (False, False), (True, True)])
 def test_module_fused_projection_is_the_composition(cuda, bias, with_out):
-    """Where Q and K are projected inside the attention kernel (bf16, C = 64,
+    """Where Q, K and V are projected inside the attention kernel (bf16, C = 64,
     8x8-pixel regions, top-1, 5x5 LePE), the module's y is bit for bit the
     unfused composition: bra.linear of x into Q, K, V, then bra.attend with
     the module's idx.  With y in x's memory the module takes the unfused

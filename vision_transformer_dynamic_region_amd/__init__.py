@@ -374,7 +374,7 @@ def module_forward(x, w_qkv, b_qkv, heads: int, S: int, topk: int, lepe_w=None, 
     Returns (out, idx).  workspace, if given, is a CUDA uint8 tensor of at
     least module_workspace_bytes(...) bytes; afterwards it holds the region
     means of x, Q and K and the tensors Q, K, V (and y when w_out is given),
-    except Q and K where they are projected inside the attention kernel
+    except Q, K and V where they are projected inside the attention kernel
     (bf16, C = 64, 8x8-pixel regions, top-1, 5x5 LePE, y not in x's memory)."""
     import torch
     B, H, W, C = _bhwc(x)

@@ -196,17 +196,11 @@ bra_status module_launches(const void* x, const bra::Shape& s, bra_dtype dtype, 
     return st;
   const size_t xbytes = (size_t)T * C * elem_size(dtype);
   if (bf16 && bra::attend_xproj_ok(s, lepe_w, lepe_ks) && !overlaps(y, x, xbytes)) {
-    // fused form: V alone through the projection, Q and K projected inside
-    // the attention kernel (the workspace's Q and K parts stay unwritten);
-    // not when y is x's memory, which that kernel still reads while it writes
-    const void* w_v = (const uint16_t*)w_qkv + (size_t)2 * C * C;
-    const float* b_v = b_qkv ? b_qkv + 2 * C : nullptr;
-    void* vout[1] = {qkv[2]};
-    if ((st = hip_status(bra::launch_linear(x, T, C, w_v, b_v, C, vout, 1, bf16, hs),
-                         "v projection launch")))
-      return st;
-    if ((st = hip_status(bra::launch_attend_xproj(x, w_qkv, b_qkv, qkv[2], idx, s, attn_scale,
-                                                  lepe_w, lepe_b, lepe_ks, y, hs),
+    // fused form: Q, K and V projected inside the attention kernel (the
+    // workspace's Q, K and V parts stay unwritten); not when y is x's
+    // memory, which that kernel still reads while it writes
+    if ((st = hip_status(bra::launch_attend_xproj(x, w_qkv, b_qkv, idx, s, attn_scale, lepe_w,
+                                                  lepe_b, lepe_ks, y, hs),
                          "fused attend launch")))
       return st;
   } else {

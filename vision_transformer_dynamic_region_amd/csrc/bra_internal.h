@@ -121,17 +121,16 @@ hipError_t launch_attend_region(const void* q, const void* k, const void* v,
                                 hipStream_t st);
 
 // The module's fused form of launch_attend_region for bf16 x with C = 64,
-// 8x8-pixel regions, top-1 and a 5x5 LePE (attend_xproj_ok): Q and K are
-// projected from x inside the attention kernel with the first 2C rows of
-// w_qkv ([3C, C] bf16) and b_qkv (float32 [3C] or null), bias added and
-// rounded to bf16 as launch_linear does, so they are never written; v is
-// the projected V.  hipErrorNotSupported for other shapes, before anything
-// is enqueued.
+// 8x8-pixel regions, top-1 and a 5x5 LePE (attend_xproj_ok): Q, K and V are
+// projected from x inside the attention kernel with w_qkv ([3C, C] bf16)
+// and b_qkv (float32 [3C] or null), bias added and rounded to bf16 as
+// launch_linear does, so they are never written.  hipErrorNotSupported for
+// other shapes, before anything is enqueued.
 bool attend_xproj_ok(const Shape& s, const float* w, int ks);
 hipError_t launch_attend_xproj(const void* x, const void* w_qkv, const float* b_qkv,
-                               const void* v, const int32_t* idx, const Shape& s,
-                               float attn_scale, const float* w, const float* bias, int ks,
-                               void* out, hipStream_t st);
+                               const int32_t* idx, const Shape& s, float attn_scale,
+                               const float* w, const float* bias, int ks, void* out,
+                               hipStream_t st);
 
 // The same with the whole image's K and V for one head resident in LDS
 // (bf16, 5x5 LePE fused, the 4x4 / top-4 and 2x2 / top-16 region shapes on

@@ -56,9 +56,9 @@ template <int C_, int CB_, int HS_, int WS_, int TOPK_, int KS_, bool DB_, int O
 struct Rc {
   static constexpr int C = C_, CB = CB_, HS = HS_, WS = WS_, TOPK = TOPK_, KS = KS_;
   static constexpr bool DB = DB_;                  // double-buffered staging
-  // Q and K projected from x in the kernel (the module's fused form): the
-  // query region's and the routed regions' x rows are staged and multiplied
-  // by the unit's rows of Wq and Wk; V comes projected, as in the plain form
+  // Q, K and V projected from x in the kernel (the module's fused form): x
+  // of the unit's queries, routed keys and halo pixels is loaded in the MFMA
+  // operand layout and multiplied by the unit block's rows of Wq, Wk, Wv
   static constexpr bool XP = XP_;
   // more than 128 routed keys: S^T is computed twice (the maximum, then the
   // numerators 32 keys a step) rather than held in 4 KC / 64 registers
@@ -88,13 +88,15 @@ struct Rc {
   static constexpr int TYW = QR * NXG / 2;
   static constexpr int LSW = kHd + 4;               // wavefront L tile row stride (floats)
   // LDS: [halo | K | V] x (DB ? 2 : 1), wavefront L tiles, (XP) the unit
-  // block's Wq and Wk rows and biases, routing table
+  // block's Wq, Wk and Wv rows and biases, routing table
   static constexpr int HALO = HH * HW * CB * 2;
   static constexpr int KVB = KC * CB * 2;
   static constexpr int BUF = (HALO + 2 * KVB + 15) / 16 * 16;
   static constexpr int L_OFF = BUF * (DB ? 2 : 1);
   static constexpr int WX_OFF = L_OFF + kWaves * 16 * LSW * 4;
-  static constexpr int WX_BYTES = XP ? 2 * CB * C * 2 + 2 * CB * 4 : 0;
+  static constexpr int WX_BYTES = XP ? 3 * CB * C * 2 + 3 * CB * 4 : 0;
+  static constexpr int NHB = (HH * HW + 15) / 16;  // (XP) 16-pixel blocks of the halo
+  static constexpr int HBW = (NHB + kWaves - 1) / kWaves;   // halo blocks a wavefront
   static constexpr int IT_OFF = WX_OFF + WX_BYTES;
 
   static_assert(C % CB == 0 && CB % kHd == 0, "channel blocking");
@@ -105,7 +107,7 @@ struct Rc {
   static_assert(KS == 5 && (XG == 4 || XG == 2) && TYW >= 1 && (QR * NXG) % 2 == 0,
                 "dot2 LePE: 5x5 taps, two items per channel lane");
   static_assert(KK * CB * 4 <= BUF, "weights are staged through the first buffer");
-  static_assert(!XP || (C == 64 && n == 64 && KC == 16 * kWaves && !DB),
+  static_assert(!XP || (C == 64 && n == 64 && KC == 16 * kWaves && !DB && HH * HW % 16 == 0),
                 "fused projection: 64 channels of x, 8x8 regions, top-1, one buffer");
   static_assert(!XP || 16 * CB * 2 <= 16 * LSW * 4, "a wavefront's Q tile fits its L tile");
 };
@@ -149,12 +151,15 @@ struct RegionArgs {
   uint16_t* out;
   const float* w;       // [C, KS, KS]
   const float* bias;    // [C] or null
-  // XP: q and k both point to x; wq, wk to the C rows of Wq and Wk ([C, C]
-  // bf16 each, rows = output channels) and bq, bk to their biases (or null)
+  // XP: q, k and v point to x; wq, wk, wv to the C rows of Wq, Wk and Wv
+  // ([C, C] bf16 each, rows = output channels) and bq, bk, bv to their
+  // biases (or null)
   const uint16_t* wq;
   const uint16_t* wk;
+  const uint16_t* wv;
   const float* bq;
   const float* bk;
+  const float* bv;
   int H, W, S, R;
   int Hf;               // rows of one frame; the LePE halo stays inside it
   float scale_log2;     // attn_scale * log2(e)
@@ -230,20 +235,24 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
     }
   }
   if constexpr (G::XP) {
-    // the unit block's rows of Wq and Wk (x-tile swizzle) and their biases
+    // the unit block's rows of Wq, Wk and Wv (swizzled) and their biases
     uint16_t* wqs = (uint16_t*)(lds + G::WX_OFF);
     uint16_t* wks = wqs + CB * C;
-    float* bqs = (float*)(wks + CB * C);
+    uint16_t* wvs = wks + CB * C;
+    float* bqs = (float*)(wvs + CB * C);
     float* bks = bqs + CB;
+    float* bvs = bks + CB;
     for (int e = tid; e < CB * (C / 8); e += kThreads) {
       const int r = e / (C / 8), c = e - r * (C / 8);
       const int o = r * C + ((c ^ xswz(r)) * 8);
       *(uint4*)(wqs + o) = *(const uint4*)(A.wq + (size_t)(cb0 + r) * C + c * 8);
       *(uint4*)(wks + o) = *(const uint4*)(A.wk + (size_t)(cb0 + r) * C + c * 8);
+      *(uint4*)(wvs + o) = *(const uint4*)(A.wv + (size_t)(cb0 + r) * C + c * 8);
     }
     for (int c = tid; c < CB; c += kThreads) {
       bqs[c] = A.bq ? A.bq[cb0 + c] : 0.f;
       bks[c] = A.bk ? A.bk[cb0 + c] : 0.f;
+      bvs[c] = A.bv ? A.bv[cb0 + c] : 0.f;
     }
   }
   __syncthreads();
@@ -288,9 +297,11 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
 
   const uint32_t img_elems = (uint32_t)A.H * A.W * C;
   const int q = qb * 16 + lq;                      // this lane's query (column of the MFMAs)
-  constexpr int KPA = G::XP ? 1 : KPT;            // (array size of the unused form: 1)
-  uint4 qn, kn[KPA], vn[KPT], hn[HPT];
-  uint4 xqn[2], xkn[2];                            // XP: x operands, k-steps 0 and 1
+  // (array sizes of the unused form: 1)
+  constexpr int KPA = G::XP ? 1 : KPT, HPA = G::XP ? 1 : HPT, HBA = G::XP ? G::HBW : 1;
+  uint4 qn, kn[KPA], vn[KPA], hn[HPA];
+  uint4 xqn[2], xkn[2], xhn[HBA][2];               // XP: x operands, k-steps 0 and 1
+  uint32_t hok = 0;                                // XP: bit i: halo block i's pixel is in the image
   auto prefetch = [&](int j) {
     int b, ry, rx;
     decode(j, b, ry, rx);
@@ -310,6 +321,23 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
         xqn[s2] = bload16(Q, (oq + 32 * s2) * 2);
         xkn[s2] = bload16(K, (ok + 32 * s2) * 2);
       }
+      // halo blocks wave, wave + 4, ...: pixel 16 blk + lq of the 12 x 12
+      // halo (zero outside the image, as the V halo of the plain form)
+      const int ftop = (int)fdiv(ry, A.f_syf) * A.Hf;
+      hok = 0;
+#pragma unroll
+      for (int i = 0; i < G::HBW; ++i) {
+        const int blk = wave + kWaves * i;
+        const int pix = 16 * blk + lq;
+        const int hy = pix / HW, hx = pix % HW;
+        const int y = ry * HS - P + hy, x = rx * WS - P + hx;
+        const bool in = (blk < G::NHB) & ((unsigned)(y - ftop) < (unsigned)A.Hf) &
+                        ((unsigned)x < (unsigned)A.W);
+        hok |= (in ? 1u : 0u) << i;
+        const uint32_t oh = (uint32_t)((__umul24(y, A.W) + x) * C + 8 * lg);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) xhn[i][s2] = bload16(V, in ? (oh + 32 * s2) * 2 : kOob);
+      }
     } else {
       const uint32_t off = ((ry * HS + q / WS) * A.W + rx * WS + q % WS) * C + cb0 + hb * kHd + 8 * lg;
       qn = bload16(Q, q < n ? off * 2 : kOob);
@@ -322,9 +350,12 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
           (PSTEP * (i + 1) <= KC || kk < KC)
               ? (itab[j * TOPK + tj] + ((tok / WS) * A.W + tok % WS) * C + cb0 + g * 8) * 2
               : kOob;
-      if constexpr (!G::XP) kn[i] = bload16(K, off);
-      vn[i] = bload16(V, off);
+      if constexpr (!G::XP) {
+        kn[i] = bload16(K, off);
+        vn[i] = bload16(V, off);
+      }
     }
+    if constexpr (G::XP) return;
     const int ftop = (int)fdiv(ry, A.f_syf) * A.Hf;  // first row of the region's frame
 #pragma unroll
     for (int i = 0; i < HPT; ++i) {
@@ -343,21 +374,23 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
     uint16_t* Hs = (uint16_t*)buf;
     uint16_t* Ks = (uint16_t*)(buf + G::HALO);
     uint16_t* Vs = (uint16_t*)(buf + G::HALO + G::KVB);
+    if constexpr (!G::XP) {
 #pragma unroll
-    for (int i = 0; i < HPT; ++i) {
-      const int pix = pk + PSTEP * i;
-      if (PSTEP * (i + 1) <= HH * HW || pix < HH * HW) *(uint4*)(Hs + pix * CB + g * 8) = hn[i];
-    }
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int kk = pk + PSTEP * i;
-      if (PSTEP * (i + 1) <= KC || kk < KC) {
-        const int o = kk * CB + ((g ^ kswz<GB>(kk)) * 8);
-        if constexpr (!G::XP) *(uint4*)(Ks + o) = kn[i];
-        *(uint4*)(Vs + o) = vn[i];
+      for (int i = 0; i < HPT; ++i) {
+        const int pix = pk + PSTEP * i;
+        if (PSTEP * (i + 1) <= HH * HW || pix < HH * HW) *(uint4*)(Hs + pix * CB + g * 8) = hn[i];
       }
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int kk = pk + PSTEP * i;
+        if (PSTEP * (i + 1) <= KC || kk < KC) {
+          const int o = kk * CB + ((g ^ kswz<GB>(kk)) * 8);
+          *(uint4*)(Ks + o) = kn[i];
+          *(uint4*)(Vs + o) = vn[i];
+        }
+      }
+      qop = __builtin_bit_cast(bf16x8, qn);
     }
-    if constexpr (!G::XP) qop = __builtin_bit_cast(bf16x8, qn);
   };
 
   const float c = A.scale_log2;
@@ -389,9 +422,13 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
       // bias added and one rounding to bf16, as the plain projection ----
       const uint16_t* wqs = (const uint16_t*)(lds + G::WX_OFF);
       const uint16_t* wks = wqs + CB * C;
-      const float* bqs = (const float*)(wks + CB * C);
+      const uint16_t* wvs = wks + CB * C;
+      const float* bqs = (const float*)(wvs + CB * C);
       const float* bks = bqs + CB;
+      const float* bvs = bks + CB;
+      uint16_t* Hw = (uint16_t*)buf;
       uint16_t* Kw = (uint16_t*)(buf + G::HALO);
+      uint16_t* Vw = (uint16_t*)(buf + G::HALO + G::KVB);
       // weight row r(i) feeds D row i; D lane (lq, lg) holds the channels
       // r(4lg .. 4lg+3) of the operand's pixel lq, biased and rounded
       auto project = [&](const uint4* xo, const uint16_t* ws, const float* bs,
@@ -412,9 +449,24 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
         const int key = 16 * wave + lq;              // key block = wavefront
 #pragma unroll
         for (int cb = 0; cb < CB / 16; ++cb) {
-          const uint2 kv = project(xkn, wks, bks, [&](int i) { return 16 * cb + i; });
+          const auto rows = [&](int i) { return 16 * cb + i; };
           const int ch = 2 * cb + (lg >> 1);         // 16-byte chunk of channels 16cb + 4lg
-          *(uint2*)(Kw + key * CB + ((ch ^ kswz<GB>(key)) * 8) + 4 * (lg & 1)) = kv;
+          const int o = key * CB + ((ch ^ kswz<GB>(key)) * 8) + 4 * (lg & 1);
+          *(uint2*)(Kw + o) = project(xkn, wks, bks, rows);
+          *(uint2*)(Vw + o) = project(xkn, wvs, bvs, rows);
+        }
+      }
+      // V of the halo blocks (row-major [pixel][CB], zero outside the image)
+#pragma unroll
+      for (int i = 0; i < G::HBW; ++i) {
+        const int blk = wave + kWaves * i;
+        if (blk < G::NHB) {                          // uniform
+#pragma unroll
+          for (int cb = 0; cb < CB / 16; ++cb) {
+            uint2 hv = project(xhn[i], wvs, bvs, [&](int r) { return 16 * cb + r; });
+            if (!((hok >> i) & 1u)) hv = make_uint2(0u, 0u);
+            *(uint2*)(Hw + (16 * blk + lq) * CB + 16 * cb + 4 * lg) = hv;
+          }
         }
       }
       // Q straight into the operand layout (channels 32hb + 8lg .. +7 of
@@ -674,7 +726,7 @@ using St2 = Rc<128, 128, 4, 4, 4, 5, false>;
 using St3 = Rc<256, 128, 2, 2, 16, 5, false>;
 using Dense = Rc<64, 32, 8, 8, 4, 5, BRA_DB_DENSE, 3, true>;
 // the module's fused form of St1: Q and K projected from x in the kernel
-using StX1 = Rc<64, 32, 8, 8, 1, 5, false, 4, false, true>;
+using StX1 = Rc<64, 32, 8, 8, 1, 5, false, 3, false, true>;
 
 }  // namespace
 
@@ -687,8 +739,8 @@ hipError_t launch_attend_region(const void* q, const void* k, const void* v, con
   RegionArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.idx = idx; a.out = (uint16_t*)out; a.w = w; a.bias = bias;
-  a.wq = a.wk = nullptr;
-  a.bq = a.bk = nullptr;
+  a.wq = a.wk = a.wv = nullptr;
+  a.bq = a.bk = a.bv = nullptr;
   a.H = s.H; a.W = s.W; a.S = s.S; a.R = s.R; a.Hf = s.Hf;
   a.scale_log2 = attn_scale * 1.4426950408889634f;
   a.f_R = make_fastdiv(s.R);
@@ -721,18 +773,19 @@ bool attend_xproj_ok(const Shape& s, const float* w, int ks) {
 }
 
 hipError_t launch_attend_xproj(const void* x, const void* w_qkv, const float* b_qkv,
-                               const void* v, const int32_t* idx, const Shape& s,
-                               float attn_scale, const float* w, const float* bias, int ks,
-                               void* out, hipStream_t st) {
+                               const int32_t* idx, const Shape& s, float attn_scale,
+                               const float* w, const float* bias, int ks, void* out,
+                               hipStream_t st) {
   if (!attend_xproj_ok(s, w, ks)) return hipErrorNotSupported;
   RegionArgs a;
-  a.q = a.k = (const uint16_t*)x;
-  a.v = (const uint16_t*)v;
+  a.q = a.k = a.v = (const uint16_t*)x;
   a.idx = idx; a.out = (uint16_t*)out; a.w = w; a.bias = bias;
   a.wq = (const uint16_t*)w_qkv;
   a.wk = (const uint16_t*)w_qkv + (size_t)s.C * s.C;
+  a.wv = (const uint16_t*)w_qkv + (size_t)2 * s.C * s.C;
   a.bq = b_qkv;
   a.bk = b_qkv ? b_qkv + s.C : nullptr;
+  a.bv = b_qkv ? b_qkv + 2 * s.C : nullptr;
   a.H = s.H; a.W = s.W; a.S = s.S; a.R = s.R; a.Hf = s.Hf;
   a.scale_log2 = attn_scale * 1.4426950408889634f;
   a.f_R = make_fastdiv(s.R);
