@@ -75,7 +75,8 @@ def parse():
                    help="input copies rotated across steps (0: enough to exceed the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true",
-                   help="with the default workload, skip the other shapes measured beside it")
+                   help="with the default workload, skip the other shapes and the module and block "
+                        "timings measured beside it")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--copy-probe-mb", type=int, default=0,
@@ -248,6 +249,11 @@ def module_cpu_baseline(wl, m, target_s: float) -> dict:
 
 
 def run_module(a, wl) -> int:
+    print(json.dumps(module_result(a, wl, cpu=not a.no_cpu_baseline)), flush=True)
+    return 0
+
+
+def module_result(a, wl, cpu: bool) -> dict:
     """One step = bra_module_forward over one batch: pooling of x, float64
     projection of the means, routing, the Q/K/V projection, attention with
     LePE, the output projection."""
@@ -332,14 +338,18 @@ def run_module(a, wl) -> int:
                      "frac": lin_gbs / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes": lin_bytes},
     }
-    if not a.no_cpu_baseline:
+    if cpu:
         log("timing the fp64 oracle module on the host")
         res["cpu_baseline"] = module_cpu_baseline(wl, m, a.cpu_seconds)
-    print(json.dumps(res), flush=True)
-    return 0
+    return res
 
 
 def run_block(a, wl) -> int:
+    print(json.dumps(block_result(a, wl, cpu=not a.no_cpu_baseline)), flush=True)
+    return 0
+
+
+def block_result(a, wl, cpu: bool) -> dict:
     """One step = bra_block_forward over one batch."""
     import numpy as np
     import torch
@@ -434,7 +444,7 @@ def run_block(a, wl) -> int:
                      "frac": big_gbs / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes": big_bytes},
     }
-    if not a.no_cpu_baseline:
+    if cpu:
         import oracle as O
         log("timing the fp64 oracle block on the host")
         ru0 = resource.getrusage(resource.RUSAGE_SELF)
@@ -451,8 +461,7 @@ def run_block(a, wl) -> int:
                                "cores": max(1, int(round(cpu / dt))), "kind": "oracle",
                                "sample": (f"{wl.name} block: 1 image x {reps} passes ({tokens} "
                                           f"tokens), fp64 oracle block_forward in {dt:.1f} s")}
-    print(json.dumps(res), flush=True)
-    return 0
+    return res
 
 
 def run_backward(a, wl) -> int:
@@ -676,6 +685,14 @@ def main() -> int:
         # the other bf16 shapes on the same line (the headline stays st1)
         res["other_workloads"] = {n: measure_bra(a, WORKLOADS[n], bra, headline=False)
                                   for n in OTHER_WORKLOADS}
+        # the BRA module and the whole BiFormer block on the same shape, each
+        # timed the way --path module / --path block time it (no host baseline)
+        res["other_paths"] = {}
+        for name, fn in (("module", module_result), ("block", block_result)):
+            r = fn(a, wl, cpu=False)
+            res["other_paths"][name] = {k: r[k] for k in ("metric", "value", "unit",
+                                                           "ms_per_step", "config", "stages_ms")}
+            torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
         log("timing the fp64 oracle on the host")
         res["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
