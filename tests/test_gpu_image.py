@@ -1,6 +1,7 @@
 """The whole-image attention kernels (one head of one image's K and V resident
 in LDS; the 4x4-pixel / top-4 and 2x2-pixel / top-16 region shapes, the
-latter in its masked form up to 64 regions and its gather form above) against
+latter in its grouped form up to 64 regions, its masked form where the image
+has no more keys than the routed ones, and its gather form above) against
 the fp64 oracle, through the C ABI: batches that leave XCD slots empty,
 region grids other than 7x7, other head counts, a LePE bias, caller indices
 with repeated and out-of-range entries (a repeated region counts twice, as
@@ -22,6 +23,9 @@ CASES = {
     # name: (B, H, W, C, heads, S, topk)
     "st2_B3": (3, 28, 28, 128, 4, 7, 4),
     "st3_B9": (9, 14, 14, 256, 8, 7, 16),
+    # 16 regions of 2x2 routed to all 16: no more keys than the routed ones,
+    # so the masked form runs (the grouped form takes the larger grids)
+    "st3_masked_S4_C64": (2, 8, 8, 64, 2, 4, 16),
     "st3_region_S8_C64": (2, 16, 16, 64, 2, 8, 16),
     "st3_region_S5_C32": (3, 10, 10, 32, 1, 5, 16),
     "st2_region_S8_C32": (2, 32, 32, 32, 1, 8, 4),

@@ -416,17 +416,38 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
 //              x on v_dot2_f32_bf16 (weights rounded to bf16, products exact,
 //              float32 sums);
 //   epilogue   out = O / l + L, one rounding, 16-byte stores.
+//
+// Grouped form (GROUP): the same staging and LePE, but each query column
+// meets only the keys its own region is routed to.  The four query regions
+// of a block each bring their routed key rows (read at the routed positions
+// in LDS); S^T for 16 routed keys is the sum of four MFMAs whose Q operand
+// keeps only the columns of one region (the other columns are zero), so
+// every column ends with the logits of its own region's keys, and O^T and
+// the row sums are built the same way from V^T rows gathered per region and
+// P^T operands keeping one region's columns.  A query then takes 4 TOPK
+// softmax values instead of one per key of the image (st3: 64 against 224),
+// at four MFMAs per 16 keys; the exponentials are what the masked form is
+// bound by.
 // ---------------------------------------------------------------------------
-template <int TOPK_, int NW_, int NKB2_>
+template <int TOPK_, int NW_, int NKB2_, bool GROUP_ = false>
 struct Im {
   // TOPK routed regions, NW wavefronts a workgroup, NKB2 steps of 32 keys
   // (the image's keys padded to a multiple of 32)
   static constexpr int HS = 2, WS = 2, n = 4, TOPK = TOPK_, KS = 5, NW = NW_, NKB2 = NKB2_;
+  static constexpr bool GROUP = GROUP_;
+  static constexpr int KB = TOPK / 4;                 // (GROUP) 16-key blocks of a region's keys
+  // (GROUP) byte offset of the V rows: right after the K rows at offset 0;
+  // they are kept as two arrays of 16-channel halves [pos][16], VH bytes
+  // each, so a transposing read of either half is one address apart
+  static constexpr int VS_OFF = 32 * NKB2 * kHd * 2;
+  static constexpr int VH = 32 * NKB2 * 16 * 2;
   static constexpr int NKB = 2 * NKB2;                // 16-key blocks
   static constexpr int NT = NW * 64, P = KS / 2, KK = KS * KS, LSW = kHd + 4;
   static constexpr int NBS = (128 * NKB2 + NT - 1) / NT;   // K (and V) chunks a thread stages
   static constexpr int NES = (64 * TOPK + NT - 1) / NT;    // routing entries a thread (R <= 64)
   static_assert(KS == 5 && NT >= KS * 3 * kHd, "LePE weights: one tap-pair entry a thread");
+  static_assert(!GROUP || (TOPK % 8 == 0 && TOPK * 4 <= 64),
+                "grouped form: whole 32-key steps, a routing row within a table row");
 };
 
 struct MaskArgs {
@@ -538,10 +559,14 @@ __global__ __launch_bounds__(G::NT) void attend_image_mask_kernel(MaskArgs A) {
       ent[i] = __builtin_amdgcn_raw_buffer_load_b32(Ir, e < nent ? (uint32_t)e * 4 : kOob, 0, 0);
     }
     // cleared areas: key rows past the last key (their multiplicity is zero
-    // too), the zero border of the V image, the multiplicity table
-    for (int e = nkeys * 4 + tid; e < 32 * NKB2 * 4; e += NT) {
-      *(uint4*)(Ks + e * 8) = make_uint4(0, 0, 0, 0);
-      *(uint4*)(Vs + e * 8) = make_uint4(0, 0, 0, 0);
+    // too; the grouped form never reads them), the zero border of the V
+    // image, the multiplicity table (the grouped form writes every entry of
+    // its routing table)
+    if constexpr (!G::GROUP) {
+      for (int e = nkeys * 4 + tid; e < 32 * NKB2 * 4; e += NT) {
+        *(uint4*)(Ks + e * 8) = make_uint4(0, 0, 0, 0);
+        *(uint4*)(Vs + e * 8) = make_uint4(0, 0, 0, 0);
+      }
     }
     for (int e = tid; e < HP * WP * 4; e += NT) {
       const int pc = fdiv(e, A.f_wp4);
@@ -549,7 +574,8 @@ __global__ __launch_bounds__(G::NT) void attend_image_mask_kernel(MaskArgs A) {
       if ((unsigned)(pc - P) >= (unsigned)H || (unsigned)(px - P) >= (unsigned)W)
         *(uint4*)(Vi + e * 8) = make_uint4(0, 0, 0, 0);
     }
-    for (int e = tid; e < nqr * 4; e += NT) *(uint4*)(ct + e * 16) = make_uint4(0, 0, 0, 0);
+    if constexpr (!G::GROUP)
+      for (int e = tid; e < nqr * 4; e += NT) *(uint4*)(ct + e * 16) = make_uint4(0, 0, 0, 0);
     // per region (padded to whole query blocks, clamped into [0, R)): the
     // byte offset in the V image of its top-left pixel, with bit 5 carrying
     // the parity of its region column (the swizzle of its pixel pairs)
@@ -568,7 +594,10 @@ __global__ __launch_bounds__(G::NT) void attend_image_mask_kernel(MaskArgs A) {
         const int ry = y >> 1, rx = x >> 1;
         const int pos = (ry * S + rx) * n + (y & 1) * 2 + (x & 1);
         *(uint4*)(Ks + pos * kHd + ((g ^ kswz(pos)) << 3)) = kr[i];
-        *(uint4*)(Vs + pos * kHd + ((g ^ vrswz(pos)) << 3)) = vr[i];
+        if constexpr (G::GROUP)
+          *(uint4*)(lds + G::VS_OFF + (g >> 1) * G::VH + pos * 32 + (g & 1) * 16) = vr[i];
+        else
+          *(uint4*)(Vs + pos * kHd + ((g ^ vrswz(pos)) << 3)) = vr[i];
         const int py = y + P, px = x + P;
         *(uint4*)(Vi + (py * WP + px) * kHd + ((g ^ vmswz(px)) << 3)) = vr[i];
       }
@@ -583,17 +612,39 @@ __global__ __launch_bounds__(G::NT) void attend_image_mask_kernel(MaskArgs A) {
               : kk == 1 ? make_uint2(pack_bf16x2(wt[2], wt[3]), pack_bf16x2(wt[1], wt[2]))
                         : make_uint2(pack_bf16x2(wt[4], 0.f), pack_bf16x2(wt[3], wt[4]));
     }
-    // multiplicities: routed key region kr of query region rl counts at
-    // byte (kr % 4) * 16 + kr / 4 of row rl (indices clamped into [0, R));
-    // byte counts stay below 256 (at most TOPK entries a row)
+    if constexpr (G::GROUP) {
+      // routing tables: entry j = 4m + s of query region rl at int
+      // rl * TOPK + s * KB + m, so the KB entries a lane needs (s = its
+      // row's region slot) are contiguous.  K table: the byte offset of the
+      // routed region's first K row, kr * 256, with the region's parity in
+      // bit 5 (the parity part of the K rows' chunk swizzle); V table
+      // (nqr * TOPK ints further): the byte offset of its first row in the
+      // low V half-array (indices clamped into [0, R))
+      int* tab = (int*)ct;
 #pragma unroll
-    for (int i = 0; i < NES; ++i) {
-      const int e = i * NT + tid;
-      if (e < nent) {
-        const int kr = min(max(ent[i], 0), R - 1);
-        const int slot = (kr & 3) * 16 + (kr >> 2);
-        __atomic_fetch_add((uint32_t*)(ct + (e / TOPK) * 64 + (slot & ~3)),
-                           1u << (8 * (slot & 3)), __ATOMIC_RELAXED);
+      for (int i = 0; i < NES; ++i) {
+        const int e = i * NT + tid;
+        if (e < nent) {
+          const int kr = min(max(ent[i], 0), R - 1);
+          const int rl = e / TOPK, j = e - rl * TOPK;
+          const int o = rl * TOPK + (j & 3) * G::KB + (j >> 2);
+          tab[o] = kr * 256 | ((kr & 1) << 5);
+          tab[nent + o] = G::VS_OFF + kr * 128;
+        }
+      }
+    } else {
+      // multiplicities: routed key region kr of query region rl counts at
+      // byte (kr % 4) * 16 + kr / 4 of row rl (indices clamped into [0, R));
+      // byte counts stay below 256 (at most TOPK entries a row)
+#pragma unroll
+      for (int i = 0; i < NES; ++i) {
+        const int e = i * NT + tid;
+        if (e < nent) {
+          const int kr = min(max(ent[i], 0), R - 1);
+          const int slot = (kr & 3) * 16 + (kr >> 2);
+          __atomic_fetch_add((uint32_t*)(ct + (e / TOPK) * 64 + (slot & ~3)),
+                             1u << (8 * (slot & 3)), __ATOMIC_RELAXED);
+        }
       }
     }
   }
@@ -627,67 +678,154 @@ __global__ __launch_bounds__(G::NT) void attend_image_mask_kernel(MaskArgs A) {
     qn = bload16(Qr, qb + NW < qb1 ? q_off(qb + NW) : kOob);
     __builtin_amdgcn_sched_barrier(0);
     const int qr = 4 * qb + (lq >> 2);
-    const int qrl = min(qr, R - 1) - qr0;             // row of the multiplicity table
-    // multiplicities of key regions 4 kb + lg, kb = 0..15, for this column
-    const uint4 cnt = *(const uint4*)(ct + qrl * 64 + lg * 16);
-    const uint32_t cw4[4] = {cnt.x, cnt.y, cnt.z, cnt.w};
-
-    // ---- S^T = K Q^T over every key block; the largest routed logit ----
-    float x[NKB][4];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const int pos = 16 * kb + lq;
-      const bf16x8 ka = *(const bf16x8*)(Ks + pos * kHd + ((lg ^ kswz(pos)) << 3));
-      const f32x4 sv = mfma_bf16(ka, qop, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[kb][e] = sv[e];
-    }
-    bstore16(Or, pend_off, pend_v);
-    float m = -3.0e38f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const bool routed = (cw4[kb >> 2] >> (8 * (kb & 3))) & 0xff;
-      const float mk = fmaxf(fmaxf(x[kb][0], x[kb][1]), fmaxf(x[kb][2], x[kb][3]));
-      m = routed ? fmaxf(m, mk) : m;
-    }
-    m = fmaxf(m, xor16(m));
-    m = fmaxf(m, xor32(m));
-    const float mc = m * c;
-
-    // ---- numerators in P^T slot order; O^T += V^T P^T, 32 keys a step ----
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
     const int cc = 4 * (lq & 3);
     const int ga = cc >> 3, gb = (16 + cc) >> 3, wi = cc & 7;
+    if constexpr (G::GROUP) {
+      constexpr int KB = G::KB;
+      const int* tab = (const int*)ct;
+      const int own = lq >> 2;                        // this column's region of the block
+      // routing rows of the block's four query regions (regions past R read
+      // row R - 1; their outputs are not stored): the K entries of this
+      // lane's key-row slot, the V entries of its transposing-read slot
+      int tk[4][KB], tv[4][KB];
 #pragma unroll
-    for (int hh = 0; hh < NKB2; ++hh) {
-      uint32_t ph[4];
+      for (int a = 0; a < 4; ++a) {
+        const int* row = tab + (min(4 * qb + a, R - 1) - qr0) * TOPK;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int kb = 2 * hh + half;
-        const float cm = (float)((cw4[kb >> 2] >> (8 * (kb & 3))) & 0xff);
-        float pv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pv[e] = cm * __builtin_amdgcn_exp2f(fmaf(x[kb][e], c, -mc));
-        ph[2 * half] = pack_bf16x2(pv[0], pv[1]);
-        ph[2 * half + 1] = pack_bf16x2(pv[2], pv[3]);
+        for (int m2 = 0; m2 < KB; ++m2) {
+          tk[a][m2] = row[own * KB + m2];
+          tv[a][m2] = row[nqr * TOPK + lg * KB + m2];
+        }
       }
-      // V^T operands: lane (lq, lg) addresses key row 32hh + 4lg + lq/4 (+16),
-      // channels 4(lq % 4) .. +3 of each 16-channel half, and receives
-      // channel d0 + lq of rows 4lg + 0..3
-      const int vrow = 32 * hh + 4 * lg + (lq >> 2);
-      const uint16_t* r0p = Vs + vrow * kHd;
-      const uint16_t* r1p = r0p + 16 * kHd;
-      const int s0 = vrswz(vrow), s1 = vrswz(vrow + 16);
-      const uint2 a0 = lds_read_tr16(r0p + ((ga ^ s0) << 3) + wi);
-      const uint2 a1 = lds_read_tr16(r1p + ((ga ^ s1) << 3) + wi);
-      const uint2 d0 = lds_read_tr16(r0p + ((gb ^ s0) << 3) + wi);
-      const uint2 d1 = lds_read_tr16(r1p + ((gb ^ s1) << 3) + wi);
-      const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(d0.x, d0.y, d1.x, d1.y));
-      const bf16x8 phi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
-      acc0 = mfma_bf16(va, phi, acc0);
-      acc1 = mfma_bf16(vb, phi, acc1);
-      accl = mfma_bf16(ones, phi, accl);
+      // Q operands keeping only region a's columns
+      const bf16x8 zero = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
+      bf16x8 qa[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) qa[a] = own == a ? qop : zero;
+
+      // ---- S^T: key block kb holds routed slots 4kb .. 4kb+3 of every
+      // region; lane (lq, lg) supplies token lq % 4 of slot 4kb + lq / 4,
+      // chunk lg (the K rows' swizzle: lg ^ (token >> 1) ^ 2 (parity)) ----
+      const uint32_t tok = lq & 3;
+      const uint32_t lck = tok * 64 + (((uint32_t)lg ^ (tok >> 1)) << 4);
+      float x[KB][4];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const bf16x8 ka = *(const bf16x8*)(lds + ((uint32_t)tk[a][kb] ^ lck));
+          sv = mfma_bf16(ka, qa[a], sv);
+        }
+        // lane holds token e of slot 4kb + lg, for its own region and query lq
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[kb][e] = sv[e];
+      }
+      bstore16(Or, pend_off, pend_v);
+      float m = x[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = fmaxf(m, x[kb][e]);
+      m = fmaxf(m, xor16(m));
+      m = fmaxf(m, xor32(m));
+      const float mc = m * c;
+
+      // ---- numerators in P^T slot order (slots 0-3: slot 8h + lg, 4-7: slot
+      // 8h + 4 + lg); O^T += V^T P^T per region, 32 keys a step ----
+      uint32_t ph[2 * KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        ph[2 * kb] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(x[kb][0], c, -mc)),
+                                 __builtin_amdgcn_exp2f(fmaf(x[kb][1], c, -mc)));
+        ph[2 * kb + 1] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(x[kb][2], c, -mc)),
+                                     __builtin_amdgcn_exp2f(fmaf(x[kb][3], c, -mc)));
+      }
+      // V^T operands: lane (lq, lg) addresses token lq / 4 of slots 8h + lg
+      // and 8h + 4 + lg, channels 4(lq % 4) .. +3 of each 16-channel half
+      // (128 contiguous bytes for the 16 lanes of a row)
+      const uint32_t lv = (lq >> 2) * 32 + (lq & 3) * 8;
+#pragma unroll
+      for (int hh = 0; hh < KB / 2; ++hh) {
+        const bf16x8 phi = __builtin_bit_cast(
+            bf16x8, make_uint4(ph[4 * hh], ph[4 * hh + 1], ph[4 * hh + 2], ph[4 * hh + 3]));
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const unsigned char* r0 = lds + ((uint32_t)tv[a][2 * hh] + lv);
+          const unsigned char* r1 = lds + ((uint32_t)tv[a][2 * hh + 1] + lv);
+          const uint2 a0 = lds_read_tr16((const uint16_t*)r0);
+          const uint2 a1 = lds_read_tr16((const uint16_t*)r1);
+          const uint2 d0 = lds_read_tr16((const uint16_t*)(r0 + G::VH));
+          const uint2 d1 = lds_read_tr16((const uint16_t*)(r1 + G::VH));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
+          const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(d0.x, d0.y, d1.x, d1.y));
+          const bf16x8 pa = own == a ? phi : zero;
+          acc0 = mfma_bf16(va, pa, acc0);
+          acc1 = mfma_bf16(vb, pa, acc1);
+          accl = mfma_bf16(ones, pa, accl);
+        }
+      }
+    } else {
+      const int qrl = min(qr, R - 1) - qr0;             // row of the multiplicity table
+      // multiplicities of key regions 4 kb + lg, kb = 0..15, for this column
+      const uint4 cnt = *(const uint4*)(ct + qrl * 64 + lg * 16);
+      const uint32_t cw4[4] = {cnt.x, cnt.y, cnt.z, cnt.w};
+
+      // ---- S^T = K Q^T over every key block; the largest routed logit ----
+      float x[NKB][4];
+  #pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int pos = 16 * kb + lq;
+        const bf16x8 ka = *(const bf16x8*)(Ks + pos * kHd + ((lg ^ kswz(pos)) << 3));
+        const f32x4 sv = mfma_bf16(ka, qop, f32x4{0.f, 0.f, 0.f, 0.f});
+  #pragma unroll
+        for (int e = 0; e < 4; ++e) x[kb][e] = sv[e];
+      }
+      bstore16(Or, pend_off, pend_v);
+      float m = -3.0e38f;
+  #pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bool routed = (cw4[kb >> 2] >> (8 * (kb & 3))) & 0xff;
+        const float mk = fmaxf(fmaxf(x[kb][0], x[kb][1]), fmaxf(x[kb][2], x[kb][3]));
+        m = routed ? fmaxf(m, mk) : m;
+      }
+      m = fmaxf(m, xor16(m));
+      m = fmaxf(m, xor32(m));
+      const float mc = m * c;
+
+      // ---- numerators in P^T slot order; O^T += V^T P^T, 32 keys a step ----
+  #pragma unroll
+      for (int hh = 0; hh < NKB2; ++hh) {
+        uint32_t ph[4];
+  #pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int kb = 2 * hh + half;
+          const float cm = (float)((cw4[kb >> 2] >> (8 * (kb & 3))) & 0xff);
+          float pv[4];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) pv[e] = cm * __builtin_amdgcn_exp2f(fmaf(x[kb][e], c, -mc));
+          ph[2 * half] = pack_bf16x2(pv[0], pv[1]);
+          ph[2 * half + 1] = pack_bf16x2(pv[2], pv[3]);
+        }
+        // V^T operands: lane (lq, lg) addresses key row 32hh + 4lg + lq/4 (+16),
+        // channels 4(lq % 4) .. +3 of each 16-channel half, and receives
+        // channel d0 + lq of rows 4lg + 0..3
+        const int vrow = 32 * hh + 4 * lg + (lq >> 2);
+        const uint16_t* r0p = Vs + vrow * kHd;
+        const uint16_t* r1p = r0p + 16 * kHd;
+        const int s0 = vrswz(vrow), s1 = vrswz(vrow + 16);
+        const uint2 a0 = lds_read_tr16(r0p + ((ga ^ s0) << 3) + wi);
+        const uint2 a1 = lds_read_tr16(r1p + ((ga ^ s1) << 3) + wi);
+        const uint2 d0 = lds_read_tr16(r0p + ((gb ^ s0) << 3) + wi);
+        const uint2 d1 = lds_read_tr16(r1p + ((gb ^ s1) << 3) + wi);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y));
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, make_uint4(d0.x, d0.y, d1.x, d1.y));
+        const bf16x8 phi = __builtin_bit_cast(bf16x8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+        acc0 = mfma_bf16(va, phi, acc0);
+        acc1 = mfma_bf16(vb, phi, acc1);
+        accl = mfma_bf16(ones, phi, accl);
+      }
     }
 
     // ---- LePE of the block's 16 pixels: region j's pixel row grp, two columns ----
@@ -768,7 +906,7 @@ MaskLds<G> mask_lds(int H, int W, int nqr, int nqb) {
   l.vi_off = (int)off;
   off += ((size_t)HP * WP + WP) * kHd * 2;
   l.ct_off = (int)off;
-  off += (size_t)nqr * 64;
+  off += (size_t)nqr * (G::GROUP ? 2 * G::TOPK * 4 : 64);   // K and V tables / multiplicities
   off = (off + 15) / 16 * 16;
   l.rt_off = (int)off;
   off += (size_t)nqb * 4 * 4;
@@ -906,6 +1044,8 @@ using ImgSt3 = Ic<2, 2, 16, 5, BRA_IMAGE_NW3>;
 #endif
 template <int NKB2>
 using MaskSt3 = Im<16, BRA_MASK_NW, NKB2>;
+template <int NKB2>
+using GroupSt3 = Im<16, BRA_MASK_NW, NKB2, true>;
 
 }  // namespace
 
@@ -930,10 +1070,11 @@ hipError_t launch_attend_image(const void* q, const void* k, const void* v, cons
   a.f_wp4 = make_fastdiv((s.W + 4) * 4);
   const int rsplit = BRA_IMAGE_RSPLIT;                // 0: chosen from the batch
   auto is = [&](int hs, int ws, int topk) { return s.hs == hs && s.ws == ws && s.topk == topk; };
-  // 2x2 regions whose routed keys are at least a quarter of the image: the
-  // masked whole-image form (fewer MFMA and softmax operations than 16-column
-  // blocks padded from four queries)
-  if (s.hs == 2 && s.ws == 2 && s.topk == MaskSt3<1>::TOPK && 4 * s.topk >= s.R && s.R <= 64) {
+  // 2x2 regions, up to 64 of them: the grouped form (a query's softmax over
+  // its 4 topk routed keys) unless the image holds no more keys than that
+  // in whole 32-key steps, where the masked form (every key of the image,
+  // one MFMA per 16 keys, no per-region selects) is the cheaper one
+  if (s.hs == 2 && s.ws == 2 && s.topk == MaskSt3<1>::TOPK && s.R <= 64) {
     MaskArgs m;
     m.q = a.q; m.k = a.k; m.v = a.v; m.idx = a.idx; m.out = a.out; m.w = a.w; m.bias = a.bias;
     m.B = s.B; m.H = s.H; m.W = s.W; m.C = s.C; m.S = s.S; m.R = s.R; m.heads = s.heads;
@@ -942,14 +1083,14 @@ hipError_t launch_attend_image(const void* q, const void* k, const void* v, cons
     m.scale_log2 = a.scale_log2;
     m.f_S = a.f_S; m.f_W = a.f_W; m.f_heads = a.f_heads; m.f_wp4 = a.f_wp4;
     hipError_t e = hipErrorNotSupported;
-    switch ((s.R * 4 + 31) / 32) {          // 32-key steps
+    switch ((s.R * 4 + 31) / 32) {          // 32-key steps of the image
       case 2: e = mask_launch<MaskSt3<2>>(m, st); break;
-      case 3: e = mask_launch<MaskSt3<3>>(m, st); break;
-      case 4: e = mask_launch<MaskSt3<4>>(m, st); break;
-      case 5: e = mask_launch<MaskSt3<5>>(m, st); break;
-      case 6: e = mask_launch<MaskSt3<6>>(m, st); break;
-      case 7: e = mask_launch<MaskSt3<7>>(m, st); break;
-      case 8: e = mask_launch<MaskSt3<8>>(m, st); break;
+      case 3: e = mask_launch<GroupSt3<3>>(m, st); break;
+      case 4: e = mask_launch<GroupSt3<4>>(m, st); break;
+      case 5: e = mask_launch<GroupSt3<5>>(m, st); break;
+      case 6: e = mask_launch<GroupSt3<6>>(m, st); break;
+      case 7: e = mask_launch<GroupSt3<7>>(m, st); break;
+      case 8: e = mask_launch<GroupSt3<8>>(m, st); break;
       default: break;
     }
     if (e != hipErrorNotSupported) return e;
