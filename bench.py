@@ -137,15 +137,14 @@ def write_traffic(a) -> int:
 
 def attend_kernel_name(wl) -> str:
     """The attention kernel the library launches for this workload: the
-    masked whole-image kernel for bf16 2x2 / top-16 regions (up to 64 of
-    them, routed keys at least a quarter of the image), the whole-image
-    gather kernel for bf16 4x4 / top-4 regions, the per-region kernel for the
-    bf16 stage-1 and dense shapes, else the pipelined general kernel or, when
-    its routed keys or LePE halo do not fit that one, the chunked general
-    kernel."""
+    whole-image 2x2-region kernel (grouped or masked form) for bf16 2x2 /
+    top-16 regions (up to 64 of them), the whole-image gather kernel for
+    bf16 4x4 / top-4 regions, the per-region kernel for the bf16 stage-1 and
+    dense shapes, else the pipelined general kernel or, when its routed keys
+    or LePE halo do not fit that one, the chunked general kernel."""
     R = wl.S * wl.S
     if (wl.lepe_ks == 5 and wl.dtype == "bf16" and wl.C % 32 == 0 and wl.H // wl.S == 2
-            and wl.topk == 16 and 4 * wl.topk >= R and R <= 64):
+            and wl.topk == 16 and R <= 64):
         return "attend_image_mask_kernel"
     if wl.lepe_ks == 5 and (wl.dtype, wl.H // wl.S, wl.topk) == ("bf16", 4, 4) and wl.C % 32 == 0:
         return "attend_image_kernel"
@@ -703,11 +702,9 @@ def main() -> int:
 def measure_bra(a, wl, bra, headline: bool) -> dict:
     """The BRA forward pass of one workload: the whole pass over rotating
     input sets (mean over exactly a.steps steps, and the median of per-step
-    times), the attention launch inside each step (an event pair around it,
-    after the routing launch of the same step: the roofline's time), the
-    same steps on one input set left in the MALL (warm), and the two stages
-    alone (bra_route: pooling and routing; bra_attend: attention with LePE),
-    each between HIP events on the launch stream."""
+    times), the same steps on one input set left in the MALL (warm), and the
+    two stages alone (bra_route: pooling and routing; bra_attend: attention
+    with LePE), each between HIP events on the launch stream."""
     import numpy as np
     import torch
 
@@ -767,20 +764,6 @@ def measure_bra(a, wl, bra, headline: bool) -> dict:
     torch.cuda.synchronize()
     ms_median = float(np.median([e0.elapsed_time(e1) for e0, e1 in pairs]))
 
-    # the attention launch as it runs inside a step: the same steps as the
-    # routing launch (bra_route) then the attention launch (bra_attend) on one
-    # stream, with an event pair around the attention launch of each
-    trip = [(ev(), ev()) for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    for i, (e1, e2) in enumerate(trip):
-        b = bufs[i % sets]
-        ridx = bra.route(b["q"], b["k"], wl.S, wl.topk, workspace=b["ws"])
-        e1.record(stream)
-        bra.attend(b["q"], b["k"], b["v"], ridx, wl.heads, wl.S, lepe_w=w, out=b["out"])
-        e2.record(stream)
-    torch.cuda.synchronize()
-    t_attn_step = float(np.mean([e1.elapsed_time(e2) for e1, e2 in trip]))
-
     def loop_ms(fn):
         e0, e1 = ev(), ev()
         torch.cuda.synchronize()
@@ -802,23 +785,20 @@ def measure_bra(a, wl, bra, headline: bool) -> dict:
     t_attn_warm = loop_ms(lambda i: bra.attend(bufs[0]["q"], bufs[0]["k"], bufs[0]["v"],
                                                bufs[0]["idx"], wl.heads, wl.S, lepe_w=w,
                                                out=bufs[0]["out"]))
-    log(f"per stage (ms): pool+route {t_route:.4f}  attend+lepe {t_attn:.4f} alone, "
-        f"{t_attn_step:.4f} in the step (warm {t_attn_warm:.4f}); step median {ms_median:.4f}, "
-        f"warm {ms_warm:.4f}")
+    log(f"per stage (ms): pool+route {t_route:.4f}  attend+lepe {t_attn:.4f} "
+        f"(warm {t_attn_warm:.4f}); step median {ms_median:.4f}, warm {ms_warm:.4f}")
     del bufs
     torch.cuda.empty_cache()
 
     tokens = wl.tokens
     attn_bytes = 4 * wl.tensor_bytes           # Q, K, V read once + out written once
-    # rates of the attention launch as timed inside the step
-    attn_gbs = attn_bytes / (t_attn_step * 1e-3) / 1e9
-    attn_tflops = wl.attn_flops / (t_attn_step * 1e-3) / 1e12
+    attn_gbs = attn_bytes / (t_attn * 1e-3) / 1e9
+    attn_tflops = wl.attn_flops / (t_attn * 1e-3) / 1e12
     route_bytes = 2 * wl.tensor_bytes          # Q and K read once
     config = {"workload": f"{wl.name}: B={wl.B} H=W={wl.H} C={wl.C} heads={wl.heads} "
                           f"d={wl.d} S={wl.S} topk={wl.topk} LePE {wl.lepe_ks}x{wl.lepe_ks}",
               "tokens_per_step": tokens, "input_sets_rotated": sets}
-    attention = {"kernel": attend_kernel_name(wl), "ms": t_attn_step, "ms_alone": t_attn,
-                 "ms_warm": t_attn_warm,
+    attention = {"kernel": attend_kernel_name(wl), "ms": t_attn, "ms_warm": t_attn_warm,
                  "tflops": attn_tflops, "frac_bf16_peak": attn_tflops / BF16_PEAK_TFLOPS,
                  "gbs": attn_gbs, "frac_hbm": attn_gbs / HBM_PEAK_GBS}
     stages = {"pool_route": t_route, "attend_lepe": t_attn,
