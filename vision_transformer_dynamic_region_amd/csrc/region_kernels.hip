@@ -60,9 +60,16 @@ struct Rc {
   // of the unit's queries, routed keys and halo pixels is loaded in the MFMA
   // operand layout and multiplied by the unit block's rows of Wq, Wk, Wv
   static constexpr bool XP = XP_;
-  // more than 128 routed keys: S^T is computed twice (the maximum, then the
-  // numerators 32 keys a step) rather than held in 4 KC / 64 registers
+  // more than 128 routed keys: S^T is not held in 4 KC / 64 registers but
+  // taken 64 keys a step with a running maximum (the accumulators rescaled
+  // when it grows; BRA_TWO_PASS: computed twice instead, the maximum first,
+  // then the numerators 32 keys a step)
   static constexpr bool TWO_PASS = TOPK_ * HS_ * WS_ > 128;
+#ifndef BRA_TWO_PASS
+  static constexpr bool ONLINE = TWO_PASS;
+#else
+  static constexpr bool ONLINE = false;
+#endif
   static constexpr int OCC = OCC_;                 // workgroups per CU to allow for
   // output stores non-temporal (written through, so the end-of-kernel
   // write-back is short; each 16-byte store then costs more HBM writes)
@@ -581,6 +588,56 @@ __global__ __launch_bounds__(kThreads, G::OCC) void attend_region_kernel(RegionA
       // ---- phase 3: O^T += V^T P^T, row sums += ones P^T ----
 #pragma unroll
       for (int h = 0; h < KC / 32; ++h) pv_step(h, ph + 4 * h);
+    } else if constexpr (G::ONLINE) {
+      // ---- many routed keys, 64 a step: S^T of the step, the running row
+      // maximum, the accumulators (O and the row sums alike) rescaled by
+      // 2^((m_old - m_new) c) when it grows, numerators against the new
+      // maximum (so every weight is at most 1), O^T += V^T P^T ----
+      float m = -3.0e38f;
+      auto chunk = [&](int ch) {
+        float xx[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 sv = mfma_bf16(kop(4 * ch + q), qop, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xx[4 * q + e] = sv[e];
+        }
+        float mk = xx[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mk = fmaxf(mk, xx[e]);
+        mk = fmaxf(mk, xor16(mk));
+        mk = fmaxf(mk, xor32(mk));
+        const float mn = fmaxf(m, mk);
+        if (ch > 0) {
+          const float alpha = __builtin_amdgcn_exp2f((m - mn) * c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc0[e] *= alpha;
+            acc1[e] *= alpha;
+            accl[e] *= alpha;
+          }
+        }
+        m = mn;
+        const float mc = m * c;
+        uint32_t p8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          p8[e] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(xx[2 * e], c, -mc)),
+                              __builtin_amdgcn_exp2f(fmaf(xx[2 * e + 1], c, -mc)));
+        pv_step(2 * ch, p8);
+        pv_step(2 * ch + 1, p8 + 4);
+      };
+      static_assert(KC % 64 == 0 && KC / 64 >= 2, "online steps: whole 64-key steps, at least two");
+      chunk(0);
+      __builtin_amdgcn_sched_barrier(0);
+      conv_rows(0, NR / 3);
+      __builtin_amdgcn_sched_barrier(0);
+      chunk(1);
+      __builtin_amdgcn_sched_barrier(0);
+      conv_rows(NR / 3, 2 * NR / 3);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ch = 2; ch < KC / 64; ++ch) chunk(ch);
     } else {
       // ---- many routed keys: phase 1 keeps only the row maximum; phase 2
       // computes S^T again, 32 keys a step, into numerators and O ----
