@@ -57,7 +57,7 @@ struct Ic {
   static constexpr int NXG = WS / XG;
   static constexpr int TYW = QR * NXG / 2;
   static constexpr int LSW = kHd + 4;                  // L tile row stride (floats)
-  static constexpr int NB = 8;                         // staging vectors in flight a thread
+  static constexpr int NB = 4;                         // staging vectors in flight a thread (K and V each)
   static_assert(KC % 32 == 0 && KC <= 256, "routed keys: a multiple of 32, one softmax step");
   static_assert(n >= 16 ? 16 % WS == 0 : n % WS == 0, "query blocks are whole pixel rows");
   static_assert(KS == 5 && (XG == 4 || XG == 2) && TYW >= 1 && (QR * NXG) % 2 == 0,
@@ -157,7 +157,28 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
   const auto Or = image_rsrc(A.out + img, img_elems * 2);
   const int c0 = h * kHd;
 
-  // ---- stage: K region-major, V into the padded image, routing rows ----
+  const int cw = lane & 31;
+  const int ntask = (r1 - r0) * NQB;
+  auto q_off = [&](int task) -> uint32_t {
+    const int rl = task / NQB, qb = task - rl * NQB;
+    const int r = r0 + rl;
+    const int ry = fdiv(r, A.f_S), rx = r - ry * S;
+    const int q = qb * 16 + lq;
+    const uint32_t off = ((ry * HS + q / WS) * W + rx * WS + q % WS) * C + c0 + 8 * lg;
+    return q < n ? off * 2 : kOob;
+  };
+  int task = wave;
+  uint4 qn;
+
+  // ---- stage: K region-major, V into the padded image, routing rows.  The
+  // routing entries, this lane's LePE weights and the first task's Q are
+  // issued while the first round of K and V chunks is in flight, and the
+  // zero border of the V image is written meanwhile, so the staging waits
+  // on one round trip to memory, not three ----
+  const int nent = (r1 - r0) * TOPK;
+  const int32_t* irow = A.idx + ((size_t)b * A.R + r0) * TOPK;
+  int ent0 = 0;
+  float wt[KK];
   {
     const int total = H * W * 4;                     // 16-byte chunks of this head
     for (int e0 = 0; e0 < total; e0 += NB * NT) {
@@ -169,6 +190,20 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
         const uint32_t off = e < total ? (uint32_t)(p * C + c0 + g * 8) * 2 : kOob;
         kr[i] = bload16(Kr, off);
         vr[i] = bload16(Vr, off);
+      }
+      if (e0 == 0) {
+        ent0 = tid < nent ? irow[tid] : 0;
+        const float* wp = A.w + (size_t)(c0 + cw) * KK;
+#pragma unroll
+        for (int t = 0; t < KK; ++t) wt[t] = wp[t];
+        qn = bload16(Qr, task < ntask ? q_off(task) : kOob);
+        // the zero border of the V image (position within a pixel does not matter)
+        for (int e = tid; e < HP * WP * 4; e += NT) {
+          const int pc = fdiv(e, A.f_wp4);             // padded row
+          const int px = (e - pc * WP * 4) >> 2;
+          if ((unsigned)(pc - P) >= (unsigned)H || (unsigned)(px - P) >= (unsigned)W)
+            *(uint4*)(Vs + e * 8) = make_uint4(0, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
@@ -184,18 +219,11 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
         }
       }
     }
-    // the zero border of the V image (position within a pixel does not matter)
-    for (int e = tid; e < HP * WP * 4; e += NT) {
-      const int pc = fdiv(e, A.f_wp4);               // padded row
-      const int px = (e - pc * WP * 4) >> 2;
-      if ((unsigned)(pc - P) >= (unsigned)H || (unsigned)(px - P) >= (unsigned)W)
-        *(uint4*)(Vs + e * 8) = make_uint4(0, 0, 0, 0);
-    }
     // routing rows of this workgroup's query regions: the routed region's
     // first key position and the padded image coordinates of its top-left
-    // pixel (indices clamped into [0, R))
-    for (int e = tid; e < (r1 - r0) * TOPK; e += NT) {
-      const int reg = min(max(A.idx[((size_t)b * A.R + r0) * TOPK + e], 0), A.R - 1);
+    // pixel (indices clamped into [0, R)); entry tid came with the staging
+    for (int e = tid; e < nent; e += NT) {
+      const int reg = min(max(e == tid ? ent0 : irow[e], 0), A.R - 1);
       const int sy = fdiv(reg, A.f_S), sx = reg - sy * S;
       itab[e] = make_int2(reg * n, ((sy * HS + P) << 16) | (sx * WS + P));
     }
@@ -205,21 +233,17 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
   // even output column the tap pairs (w0,w1) (w2,w3) (w4,0) over pixel pairs
   // (x,x+1) (x+2,x+3) (x+4,x+5); for the odd column after it (0,w0) (w1,w2)
   // (w3,w4) over the same pairs
-  const int cw = lane & 31;
   uint32_t we[KS][3], wo[KS][3];
-  {
-    const float* wp = A.w + (size_t)(c0 + cw) * KK;
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      const float t0 = wp[i * KS], t1 = wp[i * KS + 1], t2 = wp[i * KS + 2];
-      const float t3 = wp[i * KS + 3], t4 = wp[i * KS + 4];
-      we[i][0] = pack_bf16x2(t0, t1);
-      we[i][1] = pack_bf16x2(t2, t3);
-      we[i][2] = pack_bf16x2(t4, 0.f);
-      wo[i][0] = pack_bf16x2(0.f, t0);
-      wo[i][1] = pack_bf16x2(t1, t2);
-      wo[i][2] = pack_bf16x2(t3, t4);
-    }
+  for (int i = 0; i < KS; ++i) {
+    const float t0 = wt[i * KS], t1 = wt[i * KS + 1], t2 = wt[i * KS + 2];
+    const float t3 = wt[i * KS + 3], t4 = wt[i * KS + 4];
+    we[i][0] = pack_bf16x2(t0, t1);
+    we[i][1] = pack_bf16x2(t2, t3);
+    we[i][2] = pack_bf16x2(t4, 0.f);
+    wo[i][0] = pack_bf16x2(0.f, t0);
+    wo[i][1] = pack_bf16x2(t1, t2);
+    wo[i][2] = pack_bf16x2(t3, t4);
   }
   const float b0 = A.bias ? A.bias[c0 + cw] : 0.f;
   __syncthreads();
@@ -231,17 +255,6 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
   const int grp = lane >> 5;
   const int xw = (grp % NXG) * XG, yl = (grp / NXG) * TYW;
 
-  const int ntask = (r1 - r0) * NQB;
-  auto q_off = [&](int task) -> uint32_t {
-    const int rl = task / NQB, qb = task - rl * NQB;
-    const int r = r0 + rl;
-    const int ry = fdiv(r, A.f_S), rx = r - ry * S;
-    const int q = qb * 16 + lq;
-    const uint32_t off = ((ry * HS + q / WS) * W + rx * WS + q % WS) * C + c0 + 8 * lg;
-    return q < n ? off * 2 : kOob;
-  };
-  int task = wave;
-  uint4 qn = bload16(Qr, task < ntask ? q_off(task) : kOob);
   for (; task < ntask; task += NW) {
     const bf16x8 qop = __builtin_bit_cast(bf16x8, qn);
     // the next task's Q, always issued (past the range it reads zeros)
