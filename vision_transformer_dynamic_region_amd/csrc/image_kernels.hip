@@ -691,6 +691,37 @@ __global__ __launch_bounds__(G::NT) void attend_image_mask_kernel(MaskArgs A) {
     qn = bload16(Qr, qb + NW < qb1 ? q_off(qb + NW) : kOob);
     __builtin_amdgcn_sched_barrier(0);
     const int qr = 4 * qb + (lq >> 2);
+    // ---- LePE of the block's 16 pixels: region j's pixel row grp, two
+    // columns, one kernel row dy a step (the grouped form spreads the rows
+    // over the attention phases, to fill their latency) ----
+    float lw[4][2];
+    uint32_t va[4];
+    {
+      const int4 tb = *(const int4*)(rtab + 4 * qb);
+      const int tj[4] = {tb.x, tb.y, tb.z, tb.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lw[j][0] = lw[j][1] = b0;
+        va[j] = ((uint32_t)tj[j] ^ lx) + lbase;
+      }
+    }
+    auto lepe_rows = [&](int dy0, int dy1) {
+#pragma unroll
+      for (int dy = 0; dy < KS; ++dy) {
+        if (dy < dy0 || dy >= dy1) continue;
+        const uint2 w0 = wpr[(dy * 3 + 0) * kHd + cw];
+        const uint2 w1 = wpr[(dy * 3 + 1) * kHd + cw];
+        const uint2 w2 = wpr[(dy * 3 + 2) * kHd + cw];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint16_t* pa = (const uint16_t*)(lds + va[j] + dy * rs);
+          const uint2 a = lds_read_tr16(pa);
+          const uint2 bb = lds_read_tr16(pa + 4 * kHd);
+          lw[j][0] = dot2(w2.x, bb.x, dot2(w1.x, a.y, dot2(w0.x, a.x, lw[j][0])));
+          lw[j][1] = dot2(w2.y, bb.x, dot2(w1.y, a.y, dot2(w0.y, a.x, lw[j][1])));
+        }
+      }
+    };
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
     const int cc = 4 * (lq & 3);
     const int ga = cc >> 3, gb = (16 + cc) >> 3, wi = cc & 7;
@@ -735,6 +766,9 @@ __global__ __launch_bounds__(G::NT) void attend_image_mask_kernel(MaskArgs A) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[kb][e] = sv[e];
       }
+      __builtin_amdgcn_sched_barrier(0);
+      lepe_rows(0, 2);
+      __builtin_amdgcn_sched_barrier(0);
       bstore16(Or, pend_off, pend_v);
       float m = x[0][0];
 #pragma unroll
@@ -759,6 +793,9 @@ __global__ __launch_bounds__(G::NT) void attend_image_mask_kernel(MaskArgs A) {
       // and 8h + 4 + lg, channels 4(lq % 4) .. +3 of each 16-channel half
       // (128 contiguous bytes for the 16 lanes of a row)
       const uint32_t lv = (lq >> 2) * 32 + (lq & 3) * 8;
+      __builtin_amdgcn_sched_barrier(0);
+      lepe_rows(2, 4);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int hh = 0; hh < KB / 2; ++hh) {
         const bf16x8 phi = __builtin_bit_cast(
@@ -779,6 +816,8 @@ __global__ __launch_bounds__(G::NT) void attend_image_mask_kernel(MaskArgs A) {
           accl = mfma_bf16(ones, pa, accl);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      lepe_rows(4, KS);
     } else {
       const int qrl = min(qr, R - 1) - qr0;             // row of the multiplicity table
       // multiplicities of key regions 4 kb + lg, kb = 0..15, for this column
@@ -839,34 +878,9 @@ __global__ __launch_bounds__(G::NT) void attend_image_mask_kernel(MaskArgs A) {
         acc1 = mfma_bf16(vb, phi, acc1);
         accl = mfma_bf16(ones, phi, accl);
       }
+      lepe_rows(0, KS);
     }
 
-    // ---- LePE of the block's 16 pixels: region j's pixel row grp, two columns ----
-    float lw[4][2];
-    {
-      const int4 tb = *(const int4*)(rtab + 4 * qb);
-      const int tj[4] = {tb.x, tb.y, tb.z, tb.w};
-      uint32_t va[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lw[j][0] = lw[j][1] = b0;
-        va[j] = ((uint32_t)tj[j] ^ lx) + lbase;
-      }
-#pragma unroll
-      for (int dy = 0; dy < KS; ++dy) {
-        const uint2 w0 = wpr[(dy * 3 + 0) * kHd + cw];
-        const uint2 w1 = wpr[(dy * 3 + 1) * kHd + cw];
-        const uint2 w2 = wpr[(dy * 3 + 2) * kHd + cw];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint16_t* pa = (const uint16_t*)(lds + va[j] + dy * rs);
-          const uint2 a = lds_read_tr16(pa);
-          const uint2 bb = lds_read_tr16(pa + 4 * kHd);
-          lw[j][0] = dot2(w2.x, bb.x, dot2(w1.x, a.y, dot2(w0.x, a.x, lw[j][0])));
-          lw[j][1] = dot2(w2.y, bb.x, dot2(w1.y, a.y, dot2(w0.y, a.x, lw[j][1])));
-        }
-      }
-    }
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
