@@ -76,7 +76,7 @@ struct ImageArgs {
   int rsplit;           // workgroups per (image, head), each a range of query regions
   int rper;             // query regions per workgroup
   float scale_log2;     // attn_scale * log2(e)
-  int ks_off, vs_off, it_off, lw_off;   // LDS byte offsets
+  int ks_off, vs_off, it_off, lw_off, wt_off;   // LDS byte offsets
   FastDiv f_S, f_W, f_rsplit, f_heads, f_wp4;   // f_wp4: (W + 2P) * 4 (padded pixel chunks)
 };
 
@@ -178,7 +178,11 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
   const int nent = (r1 - r0) * TOPK;
   const int32_t* irow = A.idx + ((size_t)b * A.R + r0) * TOPK;
   int ent0 = 0;
-  float wt[KK];
+  // this head's LePE weights ([32 channels][KK] floats, one contiguous run
+  // of memory) are read in order by the workgroup and kept in LDS
+  constexpr int NWT = (KK * kHd + NT - 1) / NT;
+  float wv[NWT];
+  float* wtab = (float*)(lds + A.wt_off);
   {
     const int total = H * W * 4;                     // 16-byte chunks of this head
     for (int e0 = 0; e0 < total; e0 += NB * NT) {
@@ -193,9 +197,12 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
       }
       if (e0 == 0) {
         ent0 = tid < nent ? irow[tid] : 0;
-        const float* wp = A.w + (size_t)(c0 + cw) * KK;
+        const float* wsrc = A.w + (size_t)c0 * KK;
 #pragma unroll
-        for (int t = 0; t < KK; ++t) wt[t] = wp[t];
+        for (int i = 0; i < NWT; ++i) {
+          const int e = i * NT + tid;
+          wv[i] = e < KK * kHd ? wsrc[e] : 0.f;
+        }
         qn = bload16(Qr, task < ntask ? q_off(task) : kOob);
         // the zero border of the V image (position within a pixel does not matter)
         for (int e = tid; e < HP * WP * 4; e += NT) {
@@ -219,6 +226,11 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < NWT; ++i) {
+      const int e = i * NT + tid;
+      if (e < KK * kHd) wtab[e] = wv[i];
+    }
     // routing rows of this workgroup's query regions: the routed region's
     // first key position and the padded image coordinates of its top-left
     // pixel (indices clamped into [0, R)); entry tid came with the staging
@@ -229,24 +241,27 @@ __global__ __launch_bounds__(G::NT) void attend_image_kernel(ImageArgs A) {
     }
   }
 
+  const float b0 = A.bias ? A.bias[c0 + cw] : 0.f;
+  __syncthreads();
   // this channel lane's LePE weights as bf16 pairs per kernel row i: for an
   // even output column the tap pairs (w0,w1) (w2,w3) (w4,0) over pixel pairs
   // (x,x+1) (x+2,x+3) (x+4,x+5); for the odd column after it (0,w0) (w1,w2)
   // (w3,w4) over the same pairs
   uint32_t we[KS][3], wo[KS][3];
+  {
+    const float* wt = wtab + cw * KK;               // KK odd: lanes hit distinct banks
 #pragma unroll
-  for (int i = 0; i < KS; ++i) {
-    const float t0 = wt[i * KS], t1 = wt[i * KS + 1], t2 = wt[i * KS + 2];
-    const float t3 = wt[i * KS + 3], t4 = wt[i * KS + 4];
-    we[i][0] = pack_bf16x2(t0, t1);
-    we[i][1] = pack_bf16x2(t2, t3);
-    we[i][2] = pack_bf16x2(t4, 0.f);
-    wo[i][0] = pack_bf16x2(0.f, t0);
-    wo[i][1] = pack_bf16x2(t1, t2);
-    wo[i][2] = pack_bf16x2(t3, t4);
+    for (int i = 0; i < KS; ++i) {
+      const float t0 = wt[i * KS], t1 = wt[i * KS + 1], t2 = wt[i * KS + 2];
+      const float t3 = wt[i * KS + 3], t4 = wt[i * KS + 4];
+      we[i][0] = pack_bf16x2(t0, t1);
+      we[i][1] = pack_bf16x2(t2, t3);
+      we[i][2] = pack_bf16x2(t4, 0.f);
+      wo[i][0] = pack_bf16x2(0.f, t0);
+      wo[i][1] = pack_bf16x2(t1, t2);
+      wo[i][2] = pack_bf16x2(t3, t4);
+    }
   }
-  const float b0 = A.bias ? A.bias[c0 + cw] : 0.f;
-  __syncthreads();
 
   const float c = A.scale_log2;
   const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u,
@@ -991,7 +1006,7 @@ hipError_t mask_launch(MaskArgs a, hipStream_t st) {
 // the wavefronts' L tiles.
 template <class G>
 struct ImageLds {
-  int ks_off, vs_off, it_off, lw_off;
+  int ks_off, vs_off, it_off, lw_off, wt_off;
   size_t bytes;
 };
 
@@ -1009,6 +1024,8 @@ ImageLds<G> image_lds(int H, int W, int rper) {
   off = (off + 15) / 16 * 16;
   l.lw_off = (int)off;
   off += (size_t)G::NW * 16 * G::LSW * 4;
+  l.wt_off = (int)off;
+  off += (size_t)G::KK * kHd * 4;
   l.bytes = off;
   return l;
 }
@@ -1047,6 +1064,7 @@ hipError_t image_launch(ImageArgs a, int rsplit, hipStream_t st) {
   const ImageLds<G> l = image_lds<G>(a.H, a.W, a.rper);
   if (l.bytes > (size_t)lds_max) return hipErrorNotSupported;
   a.ks_off = l.ks_off; a.vs_off = l.vs_off; a.it_off = l.it_off; a.lw_off = l.lw_off;
+  a.wt_off = l.wt_off;
   e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)l.bytes);
   if (e != hipSuccess) return e;
   const long long groups = (long long)(a.B + kXcds - 1) / kXcds * a.heads * a.rsplit * kXcds;
