@@ -738,8 +738,6 @@ __global__ __launch_bounds__(G::NT) void attend_image_mask_kernel(MaskArgs A) {
       }
     };
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
-    const int cc = 4 * (lq & 3);
-    const int ga = cc >> 3, gb = (16 + cc) >> 3, wi = cc & 7;
     if constexpr (G::GROUP) {
       constexpr int KB = G::KB;
       const int* tab = (const int*)ct;
@@ -834,6 +832,8 @@ __global__ __launch_bounds__(G::NT) void attend_image_mask_kernel(MaskArgs A) {
       __builtin_amdgcn_sched_barrier(0);
       lepe_rows(4, KS);
     } else {
+      const int cc = 4 * (lq & 3);
+      const int ga = cc >> 3, gb = (16 + cc) >> 3, wi = cc & 7;
       const int qrl = min(qr, R - 1) - qr0;             // row of the multiplicity table
       // multiplicities of key regions 4 kb + lg, kb = 0..15, for this column
       const uint4 cnt = *(const uint4*)(ct + qrl * 64 + lg * 16);
