@@ -139,8 +139,9 @@ def attend_kernel_name(wl) -> str:
     """The attention kernel the library launches for this workload: the
     whole-image 2x2-region kernel (grouped or masked form) for bf16 2x2 /
     top-16 regions (up to 64 of them), the whole-image gather kernel for
-    bf16 4x4 / top-4 regions, the per-region kernel for the bf16 stage-1 and
-    dense shapes, else the pipelined general kernel or, when its routed keys
+    bf16 4x4 / top-4 regions, the per-region kernel for bf16 8x8 regions
+    (C 32..128 in heads of 32, top-1, 2 or 4: the stage-1 and dense shapes
+    among them), else the pipelined general kernel or, when its routed keys
     or LePE halo do not fit that one, the chunked general kernel."""
     R = wl.S * wl.S
     if (wl.lepe_ks == 5 and wl.dtype == "bf16" and wl.C % 32 == 0 and wl.H // wl.S == 2
@@ -148,9 +149,9 @@ def attend_kernel_name(wl) -> str:
         return "attend_image_mask_kernel"
     if wl.lepe_ks == 5 and (wl.dtype, wl.H // wl.S, wl.topk) == ("bf16", 4, 4) and wl.C % 32 == 0:
         return "attend_image_kernel"
-    region = {("bf16", 64, 8, 1), ("bf16", 64, 8, 4)}
-    key = (wl.dtype, wl.C, wl.H // wl.S, wl.topk)
-    return "attend_region_kernel" if key in region and wl.lepe_ks == 5 \
+    region = (wl.dtype == "bf16" and wl.H // wl.S == 8 and wl.C in (32, 64, 96, 128)
+              and wl.C == 32 * wl.heads and wl.topk in (1, 2, 4))
+    return "attend_region_kernel" if region and wl.lepe_ks == 5 \
         else "attend_stream_kernel|attend_kernel"
 
 

@@ -782,6 +782,13 @@ using St1 = Rc<64, 32, 8, 8, 1, 5, BRA_DB_ST1, 4>;
 using St2 = Rc<128, 128, 4, 4, 4, 5, false>;
 using St3 = Rc<256, 128, 2, 2, 16, 5, false>;
 using Dense = Rc<64, 32, 8, 8, 4, 5, BRA_DB_DENSE, 3, true>;
+// the rest of the 8x8-region family (C = 32..128 in heads of 32, top-1, 2
+// or 4): units of one head, so only the image stride changes with C; top-1
+// as St1 (four workgroups a CU), top-2 (128 keys, S^T held) and top-4 (the
+// one-pass softmax) at three, top-4 with the dense shape's non-temporal
+// stores
+template <int C, int TOPK>
+using Rc8 = Rc<C, 32, 8, 8, TOPK, 5, false, TOPK == 1 ? 4 : 3, TOPK == 4>;
 // the module's fused form of St1: Q and K projected from x in the kernel
 using StX1 = Rc<64, 32, 8, 8, 1, 5, false, 3, false, true>;
 
@@ -819,6 +826,16 @@ hipError_t launch_attend_region(const void* q, const void* k, const void* v, con
   }
   if (is(Dense::C, Dense::HS, Dense::WS, Dense::TOPK, Dense::KS)) {
     return region_launch<Dense>(a, s.B, st);
+  }
+  if (s.hs == 8 && s.ws == 8 && ks == 5) {
+#define BRA_RC8(CC)                                                  \
+    if (s.C == CC) {                                                 \
+      if (s.topk == 1) return region_launch<Rc8<CC, 1>>(a, s.B, st); \
+      if (s.topk == 2) return region_launch<Rc8<CC, 2>>(a, s.B, st); \
+      if (s.topk == 4) return region_launch<Rc8<CC, 4>>(a, s.B, st); \
+    }
+    BRA_RC8(32) BRA_RC8(64) BRA_RC8(96) BRA_RC8(128)
+#undef BRA_RC8
   }
   return hipErrorNotSupported;
 }
