@@ -139,7 +139,7 @@ def attend_kernel_name(wl) -> str:
     """The attention kernel the library launches for this workload: the
     whole-image 2x2-region kernel (grouped or masked form) for bf16 2x2 /
     top-16 regions (up to 64 of them), the whole-image gather kernel for
-    bf16 4x4 / top-4 regions, the per-region kernel for bf16 8x8 regions
+    bf16 4x4 regions with top-2, 4 or 8, the per-region kernel for bf16 8x8 regions
     (C 32..128 in heads of 32, top-1, 2 or 4: the stage-1 and dense shapes
     among them), else the pipelined general kernel or, when its routed keys
     or LePE halo do not fit that one, the chunked general kernel."""
@@ -147,7 +147,8 @@ def attend_kernel_name(wl) -> str:
     if (wl.lepe_ks == 5 and wl.dtype == "bf16" and wl.C % 32 == 0 and wl.H // wl.S == 2
             and wl.topk == 16 and R <= 64):
         return "attend_image_mask_kernel"
-    if wl.lepe_ks == 5 and (wl.dtype, wl.H // wl.S, wl.topk) == ("bf16", 4, 4) and wl.C % 32 == 0:
+    if (wl.lepe_ks == 5 and wl.dtype == "bf16" and wl.H // wl.S == 4 and wl.topk in (2, 4, 8)
+            and wl.C % 32 == 0):
         return "attend_image_kernel"
     region = (wl.dtype == "bf16" and wl.H // wl.S == 8 and wl.C in (32, 64, 96, 128)
               and wl.C == 32 * wl.heads and wl.topk in (1, 2, 4))

@@ -22,6 +22,9 @@ pytestmark = pytest.mark.gpu
 CASES = {
     # name: (B, H, W, C, heads, S, topk)
     "st2_B3": (3, 28, 28, 128, 4, 7, 4),
+    # 4x4 regions routed to 8 or to 2 (128 or 32 keys a query)
+    "st2_top8_B3": (3, 28, 28, 128, 4, 7, 8),
+    "img4_top2_C64": (2, 16, 16, 64, 2, 4, 2),
     "st3_B9": (9, 14, 14, 256, 8, 7, 16),
     # 16 regions of 2x2 routed to all 16: no more keys than the routed ones,
     # so the masked form runs (the grouped form takes the larger grids)

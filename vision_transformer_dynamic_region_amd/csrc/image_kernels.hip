@@ -1084,6 +1084,10 @@ hipError_t image_launch(ImageArgs a, int rsplit, hipStream_t st) {
 #endif
 using ImgSt2 = Ic<4, 4, 4, 5, BRA_IMAGE_NW2>;
 using ImgSt3 = Ic<2, 2, 16, 5, BRA_IMAGE_NW3>;
+// 4x4 regions with top-2 or top-8 (32 or 128 routed keys; top-16 would
+// spill at sixteen wavefronts a workgroup)
+template <int TOPK>
+using Img4 = Ic<4, 4, TOPK, 5, BRA_IMAGE_NW2>;
 #ifndef BRA_MASK_NW
 #define BRA_MASK_NW 8
 #endif
@@ -1141,6 +1145,8 @@ hipError_t launch_attend_image(const void* q, const void* k, const void* v, cons
     if (e != hipErrorNotSupported) return e;
   }
   if (is(ImgSt2::HS, ImgSt2::WS, ImgSt2::TOPK)) return image_launch<ImgSt2>(a, rsplit, st);
+  if (is(4, 4, 2)) return image_launch<Img4<2>>(a, rsplit, st);
+  if (is(4, 4, 8)) return image_launch<Img4<8>>(a, rsplit, st);
   if (is(ImgSt3::HS, ImgSt3::WS, ImgSt3::TOPK)) return image_launch<ImgSt3>(a, rsplit, st);
   return hipErrorNotSupported;
 }
