@@ -52,6 +52,10 @@ EDGE = {
     "rc8_C128_top4": (1, 64, 64, 128, 4, 8, 4, "bf16", 5),
     "rc8_C96_top4": (1, 48, 48, 96, 3, 6, 4, "bf16", 5),
     "rc8_C32_top2_S2": (3, 16, 16, 32, 1, 2, 2, "bf16", 5),
+    # pixels of 24 and 48 16-byte groups (BiFormer-B's stage-2 and stage-3
+    # widths): the fused pooling and routing on 32 and 64 lanes a pixel
+    "groups24_C192": (2, 28, 28, 192, 6, 7, 4, "bf16", 5),
+    "groups48_C384": (2, 14, 14, 384, 12, 7, 16, "bf16", 5),
 }
 
 

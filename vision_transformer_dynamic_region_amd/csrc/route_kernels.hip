@@ -702,6 +702,7 @@ struct PoolRouteArgs {
   double scale;
   int nrb;          // 16-row strips per image
   int ldm;          // LDS row stride of the means (doubles)
+  int gr;           // 16-byte groups of a pixel (G, or fewer: the lanes of g >= gr idle)
   FastDiv f_ws, f_S;
 };
 
@@ -733,9 +734,13 @@ __global__ __launch_bounds__(kSmallWaves * 64) void pool_route_kernel(PoolRouteA
 
   // ---- pool ----
   {
+    // a pixel's gr groups on G lanes (G the power of two at or above gr):
+    // the lanes of g >= gr load nothing and keep nothing
     const int g = lane % G, p = lane / G;
-    const uint32_t img_bytes = (uint32_t)s.H * s.W * G * 16;
-    const size_t img = (size_t)b * s.H * s.W * G;
+    const int gr = A.gr;
+    const bool gok = g < gr;
+    const uint32_t img_bytes = (uint32_t)s.H * s.W * gr * 16;
+    const size_t img = (size_t)b * s.H * s.W * gr;
     const auto Qr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(A.q + img), (short)0,
                                                       (int)img_bytes, 0x00020000);
     const auto Kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(A.k + img), (short)0,
@@ -745,7 +750,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void pool_route_kernel(PoolRouteA
     for (int u = 0; u < NP; ++u) {
       const int t = p + u * PP;
       const int ty = fdiv(t, A.f_ws), tx = t - ty * s.ws;
-      toff[u] = t < s.n ? (uint32_t)(((ty * s.W + tx) * G + g) * 16) : 0x80000000u;
+      toff[u] = t < s.n && gok ? (uint32_t)(((ty * s.W + tx) * gr + g) * 16) : 0x80000000u;
     }
     const int U = R + rows;
     const int nj = wave < U ? (U - wave + kSmallWaves - 1) / kSmallWaves : 0;
@@ -753,7 +758,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void pool_route_kernel(PoolRouteA
     auto issue = [&](int slot, int item) {
       const int reg = item < R ? item : r0 + item - R;
       const int ry = fdiv(reg, A.f_S), rx = reg - ry * s.S;
-      const uint32_t base = (uint32_t)(((ry * s.hs) * s.W + rx * s.ws) * G * 16);
+      const uint32_t base = (uint32_t)(((ry * s.hs) * s.W + rx * s.ws) * gr * 16);
       const auto rs = item < R ? Kr : Qr;       // uniform over the wavefront
 #pragma unroll
       for (int u = 0; u < NP; ++u) {
@@ -791,12 +796,14 @@ __global__ __launch_bounds__(kSmallWaves * 64) void pool_route_kernel(PoolRouteA
         double* gdst = !A.qm ? nullptr
                      : item < R ? (strip == 0 ? A.km + ((size_t)b * R + item) * C : nullptr)
                                 : A.qm + ((size_t)b * R + r0 + item - R) * C;
+        if (gok) {
 #pragma unroll
-        for (int jj = 0; jj < KEEP; ++jj) {
-          const int c = g * VEC + p * KEEP + jj;
-          const double m = v[jj] * inv_n;
-          means[row * A.ldm + c] = m;
-          if (gdst) gdst[c] = m;
+          for (int jj = 0; jj < KEEP; ++jj) {
+            const int c = g * VEC + p * KEEP + jj;
+            const double m = v[jj] * inv_n;
+            means[row * A.ldm + c] = m;
+            if (gdst) gdst[c] = m;
+          }
         }
       }
     }
@@ -996,13 +1003,17 @@ hipError_t launch_pool_route(const void* q, const void* k, double* qm, double* k
                              hipStream_t st) {
   const int vec = bf16 ? 8 : 4;
   if (s.R > 64 || s.C % vec) return hipErrorNotSupported;
-  const int G = s.C / vec;
-  if (G != 8 && G != 16 && G != 32 && G != 64) return hipErrorNotSupported;
+  const int gr = s.C / vec;
+  // lanes a pixel: the power of two at or above its 16-byte groups (a
+  // quarter of them idle at C = 96 in bf16)
+  int G = 8;
+  while (G < gr) G *= 2;
+  if (G > 64) return hipErrorNotSupported;
   const int PP = 64 / G;
   if (vec < PP) return hipErrorNotSupported;                 // a value a lane after the scatter
   const int passes = (s.n + PP - 1) / PP;
   if (passes > 8) return hipErrorNotSupported;
-  if ((long long)s.H * s.W * G * 16 >= 0x80000000LL) return hipErrorNotSupported;
+  if ((long long)s.H * s.W * gr * 16 >= 0x80000000LL) return hipErrorNotSupported;
   int dev = 0, lds_max = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -1013,6 +1024,7 @@ hipError_t launch_pool_route(const void* q, const void* k, double* qm, double* k
   a.idx = idx; a.logits = logits; a.s = s; a.scale = route_scale;
   a.nrb = (s.R + kRouteRows - 1) / kRouteRows;
   a.ldm = s.C + 2;              // 16 bytes of padding: the 16 rows' reads spread over the banks
+  a.gr = gr;
   a.f_ws = make_fastdiv(s.ws);
   a.f_S = make_fastdiv(s.S);
   size_t lds = (size_t)(s.R + kRouteRows) * a.ldm * sizeof(double);
