@@ -56,6 +56,9 @@ EDGE = {
     # widths): the fused pooling and routing on 32 and 64 lanes a pixel
     "groups24_C192": (2, 28, 28, 192, 6, 7, 4, "bf16", 5),
     "groups48_C384": (2, 14, 14, 384, 12, 7, 16, "bf16", 5),
+    # 32 lanes a pixel at 8x8 regions, in bf16 and f32 (64 passes a region)
+    "lanes32_C256_8x8": (1, 32, 32, 256, 8, 4, 3, "bf16", 5),
+    "lanes32_f32_C96_8x8": (1, 24, 24, 96, 3, 3, 2, "f32", 3),
 }
 
 
@@ -186,3 +189,40 @@ def test_region_means(cuda, name):
     for got, t in ((means[0], x["q"]), (means[1], x["k"])):
         want = oracle.region_mean(t, S)
         assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, float(np.abs(want).max())), name
+
+
+# The fused pooling and routing with each region in 2 or 4 runs of 8 passes
+# (more than 8 passes a region): taken only when the launch has a workgroup
+# for every CU, so these run at that size.  (B, H, W, C, S, topk, dtype)
+RUNS = {
+    "runs2_C96_st1": (64, 56, 56, 96, 7, 1, "bf16"),      # BiFormer-B stage 1
+    "runs4_C256_S2": (256, 16, 16, 256, 2, 2, "bf16"),
+    "runs4_f32_C96_S2": (256, 16, 16, 96, 2, 3, "f32"),
+}
+
+
+@pytest.mark.parametrize("name", list(RUNS))
+def test_route_in_runs(cuda, name):
+    """Region means (bra_route's workspace) and indices against the oracle;
+    the forward pass (which keeps the means on chip) gives the same indices."""
+    import torch
+    import vision_transformer_dynamic_region_amd as bra
+    B, H, W, C, S, topk, dtype = RUNS[name]
+    print(f"[edge] runs {name} {RUNS[name]}", flush=True)
+    heads = C // 32
+    wl = Workload(name, 600, dtype, B, H, W, C, heads, S, topk)
+    x = make_inputs(wl)
+    q, k, v = (to_dev(x[n], dtype) for n in ("q", "k", "v"))
+    ws = torch.full((bra.workspace_bytes(B, S, C),), 0xFF, dtype=torch.uint8, device=cuda)
+    idx = bra.route(q, k, S, topk, workspace=ws)
+    torch.cuda.synchronize()
+    means = ws.view(torch.float64).cpu().numpy().reshape(2, B, S * S, C)
+    q_r, k_r = oracle.region_mean(x["q"], S), oracle.region_mean(x["k"], S)
+    for got, want in ((means[0], q_r), (means[1], k_r)):
+        assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, float(np.abs(want).max())), name
+    A = oracle.region_affinity(q_r, k_r, C ** -0.5)
+    check_idx(idx.cpu().numpy(), oracle.topk_route(A, topk), A)
+    w = torch.from_numpy(x["w"]).to(cuda)
+    _, idx_f = bra.forward(q, k, v, heads, S, topk, w)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_f, idx), name

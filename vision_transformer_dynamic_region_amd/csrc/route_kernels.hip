@@ -703,6 +703,8 @@ struct PoolRouteArgs {
   int nrb;          // 16-row strips per image
   int ldm;          // LDS row stride of the means (doubles)
   int gr;           // 16-byte groups of a pixel (G, or fewer: the lanes of g >= gr idle)
+  int parts_log2;   // a region's pixels in 2^parts_log2 runs of NP passes (one ring slot each)
+  uint32_t part_off;  // bytes from one run to the next (whole pixel rows)
   FastDiv f_ws, f_S;
 };
 
@@ -752,13 +754,18 @@ __global__ __launch_bounds__(kSmallWaves * 64) void pool_route_kernel(PoolRouteA
       const int ty = fdiv(t, A.f_ws), tx = t - ty * s.ws;
       toff[u] = t < s.n && gok ? (uint32_t)(((ty * s.W + tx) * gr + g) * 16) : 0x80000000u;
     }
+    // ring entry j is run j % 2^ps of the wavefront's item j / 2^ps
+    const int ps = A.parts_log2, H = 1 << ps;
     const int U = R + rows;
-    const int nj = wave < U ? (U - wave + kSmallWaves - 1) / kSmallWaves : 0;
+    const int ni = wave < U ? (U - wave + kSmallWaves - 1) / kSmallWaves : 0;
+    const int nj = ni << ps;
     uint4 buf[IB][NP];
-    auto issue = [&](int slot, int item) {
+    auto issue = [&](int slot, int j) {
+      const int item = wave + kSmallWaves * (j >> ps);
       const int reg = item < R ? item : r0 + item - R;
       const int ry = fdiv(reg, A.f_S), rx = reg - ry * s.S;
-      const uint32_t base = (uint32_t)(((ry * s.hs) * s.W + rx * s.ws) * gr * 16);
+      const uint32_t base = (uint32_t)(((ry * s.hs) * s.W + rx * s.ws) * gr * 16) +
+                            (uint32_t)(j & (H - 1)) * A.part_off;
       const auto rs = item < R ? Kr : Qr;       // uniform over the wavefront
 #pragma unroll
       for (int u = 0; u < NP; ++u) {
@@ -769,17 +776,19 @@ __global__ __launch_bounds__(kSmallWaves * 64) void pool_route_kernel(PoolRouteA
     };
 #pragma unroll
     for (int sl = 0; sl < IB; ++sl)
-      if (sl < nj) issue(sl, wave + kSmallWaves * sl);
+      if (sl < nj) issue(sl, sl);
     const double inv_n = 1.0 / (double)s.n;
+    double v[VEC];                               // an item's sums, over its runs
     for (int j0 = 0; j0 < nj; j0 += IB) {
 #pragma unroll
       for (int sl = 0; sl < IB; ++sl) {
         const int j = j0 + sl;
         if (j >= nj) break;                      // uniform
-        const int item = wave + kSmallWaves * j;
-        double v[VEC];
+        const int item = wave + kSmallWaves * (j >> ps);
+        if ((j & (H - 1)) == 0) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) v[e] = 0.0;
+          for (int e = 0; e < VEC; ++e) v[e] = 0.0;
+        }
 #pragma unroll
         for (int u = 0; u < NP; ++u) {
           float f[VEC];
@@ -787,7 +796,8 @@ __global__ __launch_bounds__(kSmallWaves * 64) void pool_route_kernel(PoolRouteA
 #pragma unroll
           for (int e = 0; e < VEC; ++e) v[e] += (double)f[e];
         }
-        if (j + IB < nj) issue(sl, item + kSmallWaves * IB);
+        if (j + IB < nj) issue(sl, j + IB);
+        if ((j & (H - 1)) != H - 1) continue;   // uniform: more runs of this item to come
         if constexpr (PP >= 2) scatter_step<5, VEC>(v);
         if constexpr (PP >= 4) scatter_step<4, VEC / 2>(v);
         if constexpr (PP >= 8) scatter_step<3, VEC / 4>(v);
@@ -1012,7 +1022,17 @@ hipError_t launch_pool_route(const void* q, const void* k, double* qm, double* k
   const int PP = 64 / G;
   if (vec < PP) return hipErrorNotSupported;                 // a value a lane after the scatter
   const int passes = (s.n + PP - 1) / PP;
-  if (passes > 8) return hipErrorNotSupported;
+  // more than 8 passes: the region in 2 or 4 runs of 8 passes (whole rows
+  // of the region each), one ring slot a run, so that a lane holds no more
+  // than 32 VGPRs of loads (C = 96 and 128 at 8x8-pixel regions: 2 runs)
+  int parts_log2 = 0;
+  if (passes > 8) {
+    const int run = 8 * PP;                    // pixels a run
+    if (s.n % run || run % s.ws) return hipErrorNotSupported;
+    const int parts = s.n / run;
+    if (parts != 2 && parts != 4) return hipErrorNotSupported;
+    parts_log2 = parts == 2 ? 1 : 2;
+  }
   if ((long long)s.H * s.W * gr * 16 >= 0x80000000LL) return hipErrorNotSupported;
   int dev = 0, lds_max = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1023,8 +1043,20 @@ hipError_t launch_pool_route(const void* q, const void* k, double* qm, double* k
   a.q = (const uint4*)q; a.k = (const uint4*)k; a.qm = qm; a.km = km;
   a.idx = idx; a.logits = logits; a.s = s; a.scale = route_scale;
   a.nrb = (s.R + kRouteRows - 1) / kRouteRows;
+  if (parts_log2) {
+    // runs double a workgroup's round trips to memory: worth it only while
+    // the launch has a workgroup for every CU (64 images of 56x56 at C = 96:
+    // forward 77.6-81.3 -> 70.2-71.8 us; 16 images of 64x64 at C = 128, 64
+    // workgroups: 53.1-55.4 -> 67.8-70.0 us, so the two launches stay there)
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if ((long long)s.B * a.nrb < cus) return hipErrorNotSupported;
+  }
   a.ldm = s.C + 2;              // 16 bytes of padding: the 16 rows' reads spread over the banks
   a.gr = gr;
+  a.parts_log2 = parts_log2;
+  a.part_off = parts_log2 ? (uint32_t)((8 * PP / s.ws) * s.W * gr * 16) : 0u;
   a.f_ws = make_fastdiv(s.ws);
   a.f_S = make_fastdiv(s.S);
   size_t lds = (size_t)(s.R + kRouteRows) * a.ldm * sizeof(double);
