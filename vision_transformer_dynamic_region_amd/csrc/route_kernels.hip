@@ -687,7 +687,9 @@ __global__ __launch_bounds__(kSmallWaves * 64) void route_small_kernel(RouteArgs
 // Pooling: wavefront w takes items w, w + 16, ... (K regions 0..R-1, then
 // the strip's Q regions); lane (p, g) = (lane / G, lane % G) owns 16-byte
 // channel group g of pixels p, p + 64/G, ...; IB items' loads are in flight
-// at once in a ring of registers, refilled as each item is added; the
+// at once in a ring of registers, refilled as each item is added (a region
+// of more than 8 passes takes 2 or 4 slots in turn, one band of its pixel
+// rows each, its sums carried from one to the next); the
 // float64 partial sums of the 64/G lanes sharing g are combined by the
 // reduce-scatter of pool_pipe_kernel, in a fixed order.
 // ---------------------------------------------------------------------------
