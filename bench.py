@@ -150,7 +150,7 @@ def attend_kernel_name(wl) -> str:
     if (wl.lepe_ks == 5 and wl.dtype == "bf16" and wl.H // wl.S == 4 and wl.topk in (2, 4, 8)
             and wl.C % 32 == 0):
         return "attend_image_kernel"
-    region = (wl.dtype == "bf16" and wl.H // wl.S == 8 and wl.C in (32, 64, 96, 128)
+    region = (wl.dtype == "bf16" and wl.H // wl.S == 8 and wl.C in (32, 64, 96, 128, 192, 256)
               and wl.C == 32 * wl.heads and wl.topk in (1, 2, 4))
     return "attend_region_kernel" if region and wl.lepe_ks == 5 \
         else "attend_stream_kernel|attend_kernel"

@@ -26,9 +26,10 @@
  *   - LePE weights are float32 [C, ks, ks] (PyTorch depthwise Conv2d weight
  *     without its singleton axis); bias is float32 [C] or NULL.  In bf16
  *     with ks = 5 and d = 32, the attention kernels of 8x8-pixel regions
- *     (C of 32 to 128, top-1, 2 or 4), 4x4 (top-2, 4 or 8) and 2x2
- *     (top-16) fuse the LePE on v_dot2_f32_bf16: the weights are rounded
- *     once to bf16 (relative error at most 2^-9 each), the products
+ *     (C of 32, 64, 96, 128, 192 or 256, top-1, 2 or 4), 4x4 (top-2, 4
+ *     or 8) and 2x2 (top-16) fuse the LePE on v_dot2_f32_bf16: the
+ *     weights are rounded once to bf16 (relative error at most 2^-9
+ *     each), the products
  *     with the bf16 pixels are exact and the sums float32.  Every other path
  *     (float32 data, other ks, other shapes, bra_lepe) uses the float32
  *     weights as given.

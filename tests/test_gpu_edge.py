@@ -2,7 +2,7 @@
 ragged regions and key tails, non-square regions, topk = 1 and S*S, S = 1,
 one pixel per region, many tasks per region, the largest region grid, wide
 channels, float32, LePE kernel sizes and bias, the shapes with a dedicated
-kernel at small batch, the 8x8-region family (C 32..128, top-1/2/4) on the
+kernel at small batch, the 8x8-region family (C 32..256, top-1/2/4) on the
 per-region kernel, exact ties, identity routing, out-of-range indices,
 determinism and a non-default stream."""
 
@@ -46,12 +46,15 @@ EDGE = {
     "st3_shape_B1": (1, 14, 14, 256, 8, 7, 16, "bf16", 5),
     "dense_shape_B1": (1, 128, 128, 64, 2, 16, 4, "bf16", 5),
     # the rest of the 8x8-region family on the per-region kernel: C of 32 to
-    # 128 in heads of 32, top-1, 2 or 4 (BiFormer-B's stage-1 width is 96)
+    # 256 in heads of 32, top-1, 2 or 4 (BiFormer-B's stage-1 width is 96)
     "rc8_C96_top1": (2, 56, 56, 96, 3, 7, 1, "bf16", 5),
     "rc8_C64_top2": (2, 56, 56, 64, 2, 7, 2, "bf16", 5),
     "rc8_C128_top4": (1, 64, 64, 128, 4, 8, 4, "bf16", 5),
     "rc8_C96_top4": (1, 48, 48, 96, 3, 6, 4, "bf16", 5),
     "rc8_C32_top2_S2": (3, 16, 16, 32, 1, 2, 2, "bf16", 5),
+    "rc8_C256_top1": (2, 56, 56, 256, 8, 7, 1, "bf16", 5),
+    "rc8_C192_top2": (1, 32, 32, 192, 6, 4, 2, "bf16", 5),
+    "rc8_C256_top4": (1, 32, 32, 256, 8, 4, 4, "bf16", 5),
     # pixels of 24 and 48 16-byte groups (BiFormer-B's stage-2 and stage-3
     # widths): the fused pooling and routing on 32 and 64 lanes a pixel
     "groups24_C192": (2, 28, 28, 192, 6, 7, 4, "bf16", 5),

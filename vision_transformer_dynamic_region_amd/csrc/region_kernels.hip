@@ -834,7 +834,7 @@ hipError_t launch_attend_region(const void* q, const void* k, const void* v, con
       if (s.topk == 2) return region_launch<Rc8<CC, 2>>(a, s.B, st); \
       if (s.topk == 4) return region_launch<Rc8<CC, 4>>(a, s.B, st); \
     }
-    BRA_RC8(32) BRA_RC8(64) BRA_RC8(96) BRA_RC8(128)
+    BRA_RC8(32) BRA_RC8(64) BRA_RC8(96) BRA_RC8(128) BRA_RC8(192) BRA_RC8(256)
 #undef BRA_RC8
   }
   return hipErrorNotSupported;
